@@ -1,0 +1,760 @@
+// C ABI of the routed MoE-layer library: context, workspace carving, the
+// decode path through the slot cache and the double-buffered prefill
+// streamer.  Kernels live in the .hip files; this file only orchestrates
+// HIP streams, events, copies and the host thread pool.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <chrono>
+#include <cmath>
+#include <cstdio>
+#include <cstring>
+#include <string>
+#include <thread>
+#include <vector>
+
+#include "moe.h"
+#include "common.h"
+#include "host_ffn.h"
+
+extern "C" {
+hipError_t moe_launch_router(const uint16_t* x, const float* R, const float* bias, int T, int E, int H, float* z,
+                             hipStream_t s);
+hipError_t moe_launch_topk(const float* z, int T, int E, int k, int32_t* ids, float* w, hipStream_t s);
+hipError_t moe_launch_group(const int32_t* ids, int T, int k, int E, const uint32_t* miss_mask,
+                            const int32_t* slot_row, int mb, int32_t* counts, int32_t* offsets, int32_t* pos,
+                            int32_t* perm_tok, int32_t* hist, WorkList* wl, int* err, hipStream_t s);
+hipError_t moe_launch_gemm_dec(int fmt, int gated, int grid, const WorkList* wl, const int32_t* counts,
+                               const int32_t* offsets, const uint8_t* pool, size_t S, size_t woff0, size_t woff1,
+                               size_t soff0, size_t soff1, const void* X, const void* Xs, const int32_t* row_tok,
+                               int K, int N, void* out, hipStream_t s);
+hipError_t moe_launch_combine(const uint16_t* Z, const int32_t* ids, const float* w, const int32_t* pos,
+                              const uint32_t* miss_mask, const int32_t* slot_row, const float* hp, int T, int k,
+                              int H, uint16_t* out, hipStream_t s);
+hipError_t moe_launch_quant(int fmt, int src_bf16, const void* src, int rows, const int32_t* nrows_dev, int cols,
+                            uint8_t* q, void* scale, hipStream_t s);
+hipError_t moe_launch_plan(const int32_t* ids, int n_assign, int layer, int E, int n_slots, int32_t* slot_table,
+                           int32_t* owner, uint32_t* last_use, uint32_t tick, int policy, double BP, double BH,
+                           uint32_t* miss_mask, void* plan, hipStream_t s);
+hipError_t moe_launch_evict(const int32_t* experts, int n, int layer, int E, int32_t* slot_table, int32_t* owner,
+                            uint32_t* last_use, hipStream_t s);
+hipError_t moe_launch_install_layer(int layer, int base, int E, uint32_t tick, int32_t* slot_table, int32_t* owner,
+                                    uint32_t* last_use, hipStream_t s);
+hipError_t moe_launch_free_slots(const int32_t* slots, int n, int32_t* slot_table, int32_t* owner,
+                                 uint32_t* last_use, hipStream_t s);
+hipError_t moe_launch_reset(int n_table, int n_slots, int32_t* slot_table, int32_t* owner, uint32_t* last_use,
+                            int* err, hipStream_t s);
+}
+
+namespace {
+
+thread_local std::string g_err;
+
+size_t align256(size_t x) { return (x + 255) & ~(size_t)255; }
+
+// Byte offsets of gate/up/down and of their scale arrays inside one blob.
+struct BlobLayout {
+  size_t w[3];
+  size_t s[3];
+  size_t S;
+};
+
+BlobLayout blob_layout(const moe_config& c) {
+  const size_t n = (size_t)c.H * c.I;
+  BlobLayout b{};
+  if (c.wfmt == MOE_W_BF16) {
+    for (int i = 0; i < 3; ++i) { b.w[i] = i * n * 2; b.s[i] = 0; }
+    b.S = 3 * n * 2;
+  } else if (c.wfmt == MOE_W_FP8_E4M3_B128) {
+    const size_t ns = n / (128 * 128);
+    for (int i = 0; i < 3; ++i) { b.w[i] = i * n; b.s[i] = 3 * n + i * ns * 4; }
+    b.S = 3 * n + 3 * ns * 4;
+  } else {
+    for (int i = 0; i < 3; ++i) { b.w[i] = i * (n / 2); b.s[i] = 3 * (n / 2) + i * (n / 32); }
+    b.S = 3 * (n / 2) + 3 * (n / 32);
+  }
+  return b;
+}
+
+// Workspace carving (all offsets 256-byte aligned).
+struct WsLayout {
+  size_t slot_table, owner, last_use, err, logits, ids, w, pos, perm_tok, counts, offsets, hist, wl, mask, plan, A,
+      Aq, As, Z, Xq, Xs, hp, total;
+};
+
+WsLayout ws_layout(const moe_config& c) {
+  WsLayout L{};
+  const size_t Tm = (size_t)std::max(c.max_tokens, 1);
+  const size_t R = Tm * c.k;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o += align256(std::max<size_t>(bytes, 1));
+    return at;
+  };
+  L.slot_table = take((size_t)c.L * c.E * 4);
+  L.owner = take((size_t)c.n_slots * 4);
+  L.last_use = take((size_t)c.n_slots * 4);
+  L.err = take(64);
+  L.logits = take(Tm * c.E * 4);
+  L.ids = take(R * 4);
+  L.w = take(R * 4);
+  L.pos = take(R * 4);
+  L.perm_tok = take(R * 4);
+  L.counts = take((size_t)c.E * 4);
+  L.offsets = take((size_t)(c.E + 1) * 4);
+  L.hist = take(((Tm + 255) / 256) * c.E * 4);
+  L.wl = take(sizeof(WorkList));
+  L.mask = take(64);
+  L.plan = take(sizeof(PlanOut));
+  const bool q8 = c.wfmt != MOE_W_BF16;
+  L.A = take(R * c.I * (q8 ? 4 : 2));
+  L.Aq = take(q8 ? R * c.I : 0);
+  L.As = take(c.wfmt == MOE_W_FP8_E4M3_B128 ? R * (c.I / 128) * 4 : (q8 ? R * (c.I / 32) : 0));
+  L.Z = take(R * c.H * 2);
+  L.Xq = take(q8 ? Tm * c.H : 0);
+  L.Xs = take(c.wfmt == MOE_W_FP8_E4M3_B128 ? Tm * (c.H / 128) * 4 : (q8 ? Tm * (c.H / 32) : 0));
+  L.hp = take(Tm * c.H * 4);
+  L.total = o;
+  return L;
+}
+
+}  // namespace
+
+struct moe_ctx {
+  moe_config cfg;
+  BlobLayout bl;
+  WsLayout wsl;
+  uint8_t* host_pool = nullptr;
+  uint8_t* slot_pool = nullptr;
+  uint8_t* ws = nullptr;
+  int device = 0;
+  int n_cu = 256;
+  // device buffers (carved)
+  int32_t* slot_table;
+  int32_t* owner;
+  uint32_t* last_use;
+  int* err;
+  float* logits;
+  int32_t* ids;
+  float* w;
+  int32_t* pos;
+  int32_t* perm_tok;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* hist;
+  WorkList* wl;
+  uint32_t* mask;
+  PlanOut* plan_dev;
+  void* A;
+  uint8_t* Aq;
+  void* As;
+  uint16_t* Z;
+  uint8_t* Xq;
+  void* Xs;
+  float* hp;
+  // pinned host staging
+  PlanOut* plan_host = nullptr;
+  uint16_t* hidden_host = nullptr;
+  int32_t* ids_host = nullptr;
+  float* w_host = nullptr;
+  float* hp_host = nullptr;
+  int32_t* list_dev_stage = nullptr;   // pinned staging for small int lists sent to the device
+  // policy
+  int policy = MOE_POLICY_OFFLOAD;
+  double BP = 1.0, BH = 1.0;
+  uint32_t tick = 0;
+  // events
+  hipEvent_t plan_evt = nullptr, fill_evt = nullptr, ready[2] = {nullptr, nullptr}, done[2] = {nullptr, nullptr};
+  int pf_next = -1;
+  HostPool* pool = nullptr;
+  std::string err_msg;
+};
+
+namespace {
+
+int fail(moe_ctx* c, int code, const std::string& m) {
+  if (c) c->err_msg = m;
+  g_err = m;
+  return code;
+}
+
+#define HIPCHK(ctx, expr)                                                                  \
+  do {                                                                                     \
+    hipError_t _e = (expr);                                                                \
+    if (_e != hipSuccess)                                                                  \
+      return fail(ctx, MOE_E_HIP, std::string(#expr) + ": " + hipGetErrorString(_e));      \
+  } while (0)
+
+hipStream_t as_stream(void* s) { return (hipStream_t)s; }
+
+int check_cfg(const moe_config* c) {
+  if (!c) return fail(nullptr, MOE_E_INVAL, "null config");
+  if (c->L < 1 || c->E < 1 || c->E > 256 || c->k < 1 || c->k > 8 || c->k > c->E)
+    return fail(nullptr, MOE_E_INVAL, "need 1 <= k <= 8, k <= E <= 256, L >= 1");
+  if (c->H < 256 || c->H % 256 || c->I < 128 || c->I % 128)
+    return fail(nullptr, MOE_E_INVAL, "need H % 256 == 0 and I % 128 == 0");
+  if (c->wfmt < 0 || c->wfmt > 2) return fail(nullptr, MOE_E_INVAL, "unknown weight format");
+  if (c->n_slots < 0 || c->n_slots > 8192) return fail(nullptr, MOE_E_UNSUPPORTED, "n_slots must be in [0, 8192]");
+  if (c->max_tokens < 1) return fail(nullptr, MOE_E_INVAL, "max_tokens must be >= 1");
+  return MOE_OK;
+}
+
+int nthreads_of(const moe_config& c) {
+  if (c.host_threads > 0) return c.host_threads;
+  const unsigned h = std::thread::hardware_concurrency();
+  return h ? (int)h : 1;
+}
+
+HostFfnShape host_shape(const moe_config& c, size_t S) { return HostFfnShape{c.wfmt, c.E, c.k, c.H, c.I, S}; }
+
+int grid_dec(const moe_ctx* c) { return c->n_cu * 4; }
+
+// Grouping, quantisation and both grouped GEMMs for a routed batch (ids/w in
+// the workspace).  slot_row: this layer's device row of the residency table.
+int forward_experts(moe_ctx* c, const void* hidden, int T, const int32_t* slot_row, const uint32_t* mask,
+                    hipStream_t s) {
+  const moe_config& g = c->cfg;
+  HIPCHK(c, hipStreamWaitEvent(s, c->fill_evt, 0));
+  HIPCHK(c, moe_launch_group(c->ids, T, g.k, g.E, mask, slot_row, DEC_MB, c->counts, c->offsets, c->pos, c->perm_tok,
+                             c->hist, c->wl, c->err, s));
+  const int grid = grid_dec(c);
+  const BlobLayout& b = c->bl;
+  if (g.wfmt == MOE_W_BF16) {
+    HIPCHK(c, moe_launch_gemm_dec(g.wfmt, 1, grid, c->wl, c->counts, c->offsets, c->slot_pool, b.S, b.w[0], b.w[1], 0,
+                                  0, hidden, nullptr, c->perm_tok, g.H, g.I, c->A, s));
+    HIPCHK(c, moe_launch_gemm_dec(g.wfmt, 0, grid, c->wl, c->counts, c->offsets, c->slot_pool, b.S, b.w[2], 0, 0, 0,
+                                  c->A, nullptr, nullptr, g.I, g.H, c->Z, s));
+  } else {
+    HIPCHK(c, moe_launch_quant(g.wfmt, 1, hidden, T, nullptr, g.H, c->Xq, c->Xs, s));
+    HIPCHK(c, moe_launch_gemm_dec(g.wfmt, 1, grid, c->wl, c->counts, c->offsets, c->slot_pool, b.S, b.w[0], b.w[1],
+                                  b.s[0], b.s[1], c->Xq, c->Xs, c->perm_tok, g.H, g.I, c->A, s));
+    HIPCHK(c, moe_launch_quant(g.wfmt, 0, c->A, T * g.k, c->offsets + g.E, g.I, c->Aq, c->As, s));
+    HIPCHK(c, moe_launch_gemm_dec(g.wfmt, 0, grid, c->wl, c->counts, c->offsets, c->slot_pool, b.S, b.w[2], 0, b.s[2],
+                                  0, c->Aq, c->As, nullptr, g.I, g.H, c->Z, s));
+  }
+  return MOE_OK;
+}
+
+int route_only(moe_ctx* c, const void* hidden, const float* R, const float* bias, int T, hipStream_t s) {
+  const moe_config& g = c->cfg;
+  HIPCHK(c, moe_launch_router((const uint16_t*)hidden, R, bias, T, g.E, g.H, c->logits, s));
+  HIPCHK(c, moe_launch_topk(c->logits, T, g.E, g.k, c->ids, c->w, s));
+  return MOE_OK;
+}
+
+int check_T(moe_ctx* c, int T) {
+  if (T < 0 || T > c->cfg.max_tokens) return fail(c, MOE_E_INVAL, "T outside [0, max_tokens]");
+  return MOE_OK;
+}
+
+int plan_sync(moe_ctx* c, int layer, const int32_t* ids_dev, int T, uint32_t* mask_dev, int policy, hipStream_t s) {
+  const moe_config& g = c->cfg;
+  const uint32_t tick = ++c->tick;
+  HIPCHK(c, moe_launch_plan(ids_dev, T * g.k, layer, g.E, g.n_slots, c->slot_table, c->owner, c->last_use, tick,
+                            policy, c->BP, c->BH, mask_dev, c->plan_dev, s));
+  HIPCHK(c, hipMemcpyAsync(c->plan_host, c->plan_dev, sizeof(PlanOut), hipMemcpyDeviceToHost, s));
+  return MOE_OK;
+}
+
+void fill_info(moe_ctx* c, moe_plan_info* info) {
+  if (!info) return;
+  const PlanOut& p = *c->plan_host;
+  info->n_unique = p.n_unique;
+  info->n_hit = p.n_hit;
+  info->m = p.m;
+  info->q = p.q;
+  info->n_host = p.n_host;
+  info->n_evict = p.n_evict;
+  const double S = (double)c->bl.S;
+  info->t_fill_pred_us = p.q * S / (c->BP * 1e9) * 1e6;
+  const double BR = c->BH - c->BP;
+  info->t_host_pred_us = p.n_host == 0 ? 0.0 : (BR > 0 ? p.n_host * S / (BR * 1e9) * 1e6 : INFINITY);
+}
+
+int issue_fills(moe_ctx* c, int layer, const int* experts, const int* slots, int n, hipStream_t copy) {
+  const size_t S = c->bl.S;
+  for (int i = 0; i < n; ++i) {
+    const size_t g = (size_t)layer * c->cfg.E + experts[i];
+    HIPCHK(c, hipMemcpyAsync(c->slot_pool + (size_t)slots[i] * S, c->host_pool + g * S, S, hipMemcpyHostToDevice,
+                             copy));
+  }
+  HIPCHK(c, hipEventRecord(c->fill_evt, copy));
+  return MOE_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t moe_expert_bytes(const moe_config* cfg) {
+  if (!cfg) return 0;
+  return blob_layout(*cfg).S;
+}
+
+size_t moe_workspace_bytes(const moe_config* cfg) {
+  if (check_cfg(cfg) != MOE_OK) return 0;
+  return ws_layout(*cfg).total;
+}
+
+const char* moe_last_error(moe_ctx* ctx) { return ctx ? ctx->err_msg.c_str() : g_err.c_str(); }
+
+int moe_host_alloc(size_t bytes, void** out) {
+  if (!out) return fail(nullptr, MOE_E_INVAL, "null out");
+  *out = nullptr;
+  void* p = nullptr;
+  hipError_t e = hipHostMalloc(&p, bytes, hipHostMallocDefault);
+  if (e != hipSuccess) return fail(nullptr, MOE_E_PIN, std::string("hipHostMalloc: ") + hipGetErrorString(e));
+  *out = p;
+  return MOE_OK;
+}
+
+int moe_host_free(void* p) {
+  if (!p) return MOE_OK;
+  hipError_t e = hipHostFree(p);
+  if (e != hipSuccess) return fail(nullptr, MOE_E_HIP, std::string("hipHostFree: ") + hipGetErrorString(e));
+  return MOE_OK;
+}
+
+int moe_create(const moe_config* cfg, void* host_pool, size_t host_bytes, void* d_slot_pool, size_t slot_bytes,
+               void* d_workspace, size_t ws_bytes, moe_ctx** out) {
+  if (!out) return fail(nullptr, MOE_E_INVAL, "null out");
+  *out = nullptr;
+  int rc = check_cfg(cfg);
+  if (rc != MOE_OK) return rc;
+  moe_ctx* c = new moe_ctx();
+  c->cfg = *cfg;
+  c->bl = blob_layout(*cfg);
+  c->wsl = ws_layout(*cfg);
+  const size_t S = c->bl.S;
+  auto bad = [&](int code, const std::string& m) {
+    delete c;
+    return fail(nullptr, code, m);
+  };
+  if (!host_pool || host_bytes < (size_t)cfg->L * cfg->E * S) return bad(MOE_E_INVAL, "host pool smaller than L*E*S");
+  if ((cfg->n_slots > 0 && !d_slot_pool) || slot_bytes < (size_t)cfg->n_slots * S)
+    return bad(MOE_E_INVAL, "slot pool smaller than n_slots*S");
+  if (!d_workspace || ws_bytes < c->wsl.total) return bad(MOE_E_INVAL, "workspace smaller than moe_workspace_bytes");
+  c->host_pool = (uint8_t*)host_pool;
+  c->slot_pool = (uint8_t*)d_slot_pool;
+  c->ws = (uint8_t*)d_workspace;
+  if (hipGetDevice(&c->device) != hipSuccess) return bad(MOE_E_HIP, "hipGetDevice failed");
+  int ncu = 0;
+  if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, c->device) == hipSuccess && ncu > 0)
+    c->n_cu = ncu;
+  const WsLayout& L = c->wsl;
+  uint8_t* w = c->ws;
+  c->slot_table = (int32_t*)(w + L.slot_table);
+  c->owner = (int32_t*)(w + L.owner);
+  c->last_use = (uint32_t*)(w + L.last_use);
+  c->err = (int*)(w + L.err);
+  c->logits = (float*)(w + L.logits);
+  c->ids = (int32_t*)(w + L.ids);
+  c->w = (float*)(w + L.w);
+  c->pos = (int32_t*)(w + L.pos);
+  c->perm_tok = (int32_t*)(w + L.perm_tok);
+  c->counts = (int32_t*)(w + L.counts);
+  c->offsets = (int32_t*)(w + L.offsets);
+  c->hist = (int32_t*)(w + L.hist);
+  c->wl = (WorkList*)(w + L.wl);
+  c->mask = (uint32_t*)(w + L.mask);
+  c->plan_dev = (PlanOut*)(w + L.plan);
+  c->A = w + L.A;
+  c->Aq = w + L.Aq;
+  c->As = w + L.As;
+  c->Z = (uint16_t*)(w + L.Z);
+  c->Xq = w + L.Xq;
+  c->Xs = w + L.Xs;
+  c->hp = (float*)(w + L.hp);
+  const size_t Tm = cfg->max_tokens;
+  const size_t R = Tm * cfg->k;
+  void* p;
+  if (hipHostMalloc(&p, sizeof(PlanOut), hipHostMallocDefault) != hipSuccess) return bad(MOE_E_PIN, "staging");
+  c->plan_host = (PlanOut*)p;
+  if (hipHostMalloc(&p, Tm * cfg->H * 2, hipHostMallocDefault) != hipSuccess) return bad(MOE_E_PIN, "staging");
+  c->hidden_host = (uint16_t*)p;
+  if (hipHostMalloc(&p, R * 4, hipHostMallocDefault) != hipSuccess) return bad(MOE_E_PIN, "staging");
+  c->ids_host = (int32_t*)p;
+  if (hipHostMalloc(&p, R * 4, hipHostMallocDefault) != hipSuccess) return bad(MOE_E_PIN, "staging");
+  c->w_host = (float*)p;
+  if (hipHostMalloc(&p, Tm * cfg->H * 4, hipHostMallocDefault) != hipSuccess) return bad(MOE_E_PIN, "staging");
+  c->hp_host = (float*)p;
+  if (hipHostMalloc(&p, 2 * 8192 * 4, hipHostMallocDefault) != hipSuccess) return bad(MOE_E_PIN, "staging");
+  c->list_dev_stage = (int32_t*)p;
+  if (hipEventCreateWithFlags(&c->plan_evt, hipEventDisableTiming) != hipSuccess ||
+      hipEventCreateWithFlags(&c->fill_evt, hipEventDisableTiming) != hipSuccess)
+    return bad(MOE_E_HIP, "event create");
+  for (int i = 0; i < 2; ++i)
+    if (hipEventCreateWithFlags(&c->ready[i], hipEventDisableTiming) != hipSuccess ||
+        hipEventCreateWithFlags(&c->done[i], hipEventDisableTiming) != hipSuccess)
+      return bad(MOE_E_HIP, "event create");
+  if (moe_launch_reset(cfg->L * cfg->E, cfg->n_slots, c->slot_table, c->owner, c->last_use, c->err, nullptr) !=
+      hipSuccess)
+    return bad(MOE_E_HIP, "reset kernel launch");
+  if (hipEventRecord(c->fill_evt, nullptr) != hipSuccess) return bad(MOE_E_HIP, "event record");
+  for (int i = 0; i < 2; ++i)
+    if (hipEventRecord(c->done[i], nullptr) != hipSuccess || hipEventRecord(c->ready[i], nullptr) != hipSuccess)
+      return bad(MOE_E_HIP, "event record");
+  if (hipDeviceSynchronize() != hipSuccess) return bad(MOE_E_HIP, "init sync");
+  c->pool = host_pool_create(nthreads_of(*cfg));
+  *out = c;
+  return MOE_OK;
+}
+
+int moe_destroy(moe_ctx* c) {
+  if (!c) return MOE_OK;
+  (void)hipDeviceSynchronize();
+  if (c->pool) host_pool_destroy(c->pool);
+  if (c->plan_host) (void)hipHostFree(c->plan_host);
+  if (c->hidden_host) (void)hipHostFree(c->hidden_host);
+  if (c->ids_host) (void)hipHostFree(c->ids_host);
+  if (c->w_host) (void)hipHostFree(c->w_host);
+  if (c->hp_host) (void)hipHostFree(c->hp_host);
+  if (c->list_dev_stage) (void)hipHostFree(c->list_dev_stage);
+  for (hipEvent_t e : {c->plan_evt, c->fill_evt, c->ready[0], c->ready[1], c->done[0], c->done[1]})
+    if (e) (void)hipEventDestroy(e);
+  delete c;
+  return MOE_OK;
+}
+
+int moe_set_policy(moe_ctx* c, int policy, double B_P, double B_H) {
+  if (!c) return fail(nullptr, MOE_E_INVAL, "null ctx");
+  if (policy < 0 || policy > 2) return fail(c, MOE_E_INVAL, "unknown policy");
+  if (!(B_P > 0) || !(B_H > 0)) return fail(c, MOE_E_INVAL, "bandwidths must be positive");
+  c->policy = policy;
+  c->BP = B_P;
+  c->BH = B_H;
+  return MOE_OK;
+}
+
+int32_t* moe_slot_table(moe_ctx* c) { return c ? c->slot_table : nullptr; }
+
+int moe_reset_cache(moe_ctx* c, void* stream) {
+  if (!c) return fail(nullptr, MOE_E_INVAL, "null ctx");
+  HIPCHK(c, moe_launch_reset(c->cfg.L * c->cfg.E, c->cfg.n_slots, c->slot_table, c->owner, c->last_use, c->err,
+                             as_stream(stream)));
+  c->pf_next = -1;
+  return MOE_OK;
+}
+
+int moe_route(moe_ctx* c, const void* hidden, const float* R, const float* bias, int T, int32_t* topk_ids,
+              float* topk_w, void* stream) {
+  if (!c) return fail(nullptr, MOE_E_INVAL, "null ctx");
+  int rc = check_T(c, T);
+  if (rc) return rc;
+  if (T == 0) return MOE_OK;
+  hipStream_t s = as_stream(stream);
+  HIPCHK(c, moe_launch_router((const uint16_t*)hidden, R, bias, T, c->cfg.E, c->cfg.H, c->logits, s));
+  HIPCHK(c, moe_launch_topk(c->logits, T, c->cfg.E, c->cfg.k, topk_ids, topk_w, s));
+  return MOE_OK;
+}
+
+int moe_route_from_logits(moe_ctx* c, const float* logits, int T, int32_t* topk_ids, float* topk_w, int32_t* counts,
+                          int32_t* offsets, int32_t* perm_tok, int32_t* pos, void* stream) {
+  if (!c) return fail(nullptr, MOE_E_INVAL, "null ctx");
+  int rc = check_T(c, T);
+  if (rc) return rc;
+  if (T == 0) return MOE_OK;
+  hipStream_t s = as_stream(stream);
+  const moe_config& g = c->cfg;
+  HIPCHK(c, moe_launch_topk(logits, T, g.E, g.k, topk_ids, topk_w, s));
+  HIPCHK(c, moe_launch_group(topk_ids, T, g.k, g.E, nullptr, nullptr, DEC_MB, counts, offsets, pos, perm_tok,
+                             c->hist, c->wl, c->err, s));
+  return MOE_OK;
+}
+
+int moe_plan(moe_ctx* c, int layer, const int32_t* topk_ids, int T, uint32_t* miss_mask_out, moe_plan_info* info,
+             int32_t* fill_experts, int32_t* fill_slots, void* stream) {
+  if (!c) return fail(nullptr, MOE_E_INVAL, "null ctx");
+  if (layer < 0 || layer >= c->cfg.L) return fail(c, MOE_E_INVAL, "layer out of range");
+  int rc = check_T(c, T);
+  if (rc) return rc;
+  hipStream_t s = as_stream(stream);
+  rc = plan_sync(c, layer, topk_ids, T, miss_mask_out ? miss_mask_out : c->mask, c->policy, s);
+  if (rc) return rc;
+  HIPCHK(c, hipEventRecord(c->plan_evt, s));
+  HIPCHK(c, hipEventSynchronize(c->plan_evt));
+  fill_info(c, info);
+  const PlanOut& p = *c->plan_host;
+  for (int i = 0; i < p.q; ++i) {
+    if (fill_experts) fill_experts[i] = p.F[i];
+    if (fill_slots) fill_slots[i] = p.F_slot[i];
+  }
+  return MOE_OK;
+}
+
+int slot_pool_fill(moe_ctx* c, int layer, const int32_t* experts, const int32_t* slots, int n, void* copy_stream) {
+  if (!c) return fail(nullptr, MOE_E_INVAL, "null ctx");
+  if (layer < 0 || layer >= c->cfg.L || n < 0) return fail(c, MOE_E_INVAL, "bad layer or count");
+  for (int i = 0; i < n; ++i)
+    if (experts[i] < 0 || experts[i] >= c->cfg.E || slots[i] < 0 || slots[i] >= c->cfg.n_slots)
+      return fail(c, MOE_E_INVAL, "expert or slot out of range");
+  return issue_fills(c, layer, experts, slots, n, as_stream(copy_stream));
+}
+
+int slot_pool_admit(moe_ctx* c, int layer, const int32_t* experts, int n, void* copy_stream) {
+  if (!c) return fail(nullptr, MOE_E_INVAL, "null ctx");
+  const moe_config& g = c->cfg;
+  if (layer < 0 || layer >= g.L || n < 0 || n > 8192) return fail(c, MOE_E_INVAL, "bad layer or count");
+  for (int i = 0; i < n; ++i)
+    if (experts[i] < 0 || experts[i] >= g.E) return fail(c, MOE_E_INVAL, "expert out of range");
+  if (n == 0) return MOE_OK;
+  hipStream_t s = as_stream(copy_stream);
+  // the plan kernel reads the list as routed ids: stage it into the workspace
+  std::memcpy(c->list_dev_stage, experts, (size_t)n * 4);
+  HIPCHK(c, hipMemcpyAsync(c->ids, c->list_dev_stage, (size_t)n * 4, hipMemcpyHostToDevice, s));
+  const uint32_t tick = ++c->tick;
+  HIPCHK(c, moe_launch_plan(c->ids, n, layer, g.E, g.n_slots, c->slot_table, c->owner, c->last_use, tick,
+                            MOE_POLICY_OFFLOAD, 1.0, 1.0, c->mask, c->plan_dev, s));
+  HIPCHK(c, hipMemcpyAsync(c->plan_host, c->plan_dev, sizeof(PlanOut), hipMemcpyDeviceToHost, s));
+  HIPCHK(c, hipEventRecord(c->plan_evt, s));
+  HIPCHK(c, hipEventSynchronize(c->plan_evt));
+  const PlanOut& p = *c->plan_host;
+  // the experts the plan installed must be copied even when some did not fit
+  const int rc = issue_fills(c, layer, p.F, p.F_slot, p.q, s);
+  if (rc) return rc;
+  if (p.q < p.m) return fail(c, MOE_E_NOSLOTS, "not enough evictable slots to admit every expert");
+  return MOE_OK;
+}
+
+int slot_pool_evict(moe_ctx* c, int layer, const int32_t* experts, int n) {
+  if (!c) return fail(nullptr, MOE_E_INVAL, "null ctx");
+  const moe_config& g = c->cfg;
+  if (layer < 0 || layer >= g.L || n < 0 || n > 8192) return fail(c, MOE_E_INVAL, "bad layer or count");
+  for (int i = 0; i < n; ++i)
+    if (experts[i] < 0 || experts[i] >= g.E) return fail(c, MOE_E_INVAL, "expert out of range");
+  if (n == 0) return MOE_OK;
+  std::memcpy(c->list_dev_stage, experts, (size_t)n * 4);
+  HIPCHK(c, hipMemcpyAsync(c->ids, c->list_dev_stage, (size_t)n * 4, hipMemcpyHostToDevice, nullptr));
+  HIPCHK(c, moe_launch_evict(c->ids, n, layer, g.E, c->slot_table, c->owner, c->last_use, nullptr));
+  HIPCHK(c, hipStreamSynchronize(nullptr));
+  return MOE_OK;
+}
+
+int moe_host_partial(moe_ctx* c, int layer, const void* hidden, const int32_t* topk_ids, const float* topk_w, int T,
+                     const uint32_t* miss_mask, float* out) {
+  if (!c) return fail(nullptr, MOE_E_INVAL, "null ctx");
+  const moe_config& g = c->cfg;
+  if (layer < 0 || layer >= g.L) return fail(c, MOE_E_INVAL, "layer out of range");
+  int rc = check_T(c, T);
+  if (rc) return rc;
+  std::vector<int32_t> C;
+  for (int e = 0; e < g.E; ++e)
+    if ((miss_mask[e >> 5] >> (e & 31)) & 1u) C.push_back(e);
+  HostFfnHandle* h = host_ffn_start(c->pool, host_shape(g, c->bl.S), c->host_pool, layer, T, (const uint16_t*)hidden,
+                                    topk_ids, topk_w, C.data(), (int)C.size(), out);
+  host_ffn_wait(c->pool, h);
+  return MOE_OK;
+}
+
+int moe_host_ffn(const moe_config* cfg, const void* host_pool, int layer, const void* hidden, const int32_t* topk_ids,
+                 const float* topk_w, int T, const uint32_t* miss_mask, float* out) {
+  if (!cfg || !host_pool || !hidden || !topk_ids || !topk_w || !miss_mask || !out)
+    return fail(nullptr, MOE_E_INVAL, "null argument");
+  if (cfg->E < 1 || cfg->E > 256 || cfg->k < 1 || cfg->k > cfg->E || cfg->H < 1 || cfg->I < 1 || layer < 0 ||
+      layer >= cfg->L || T < 0 || cfg->wfmt < 0 || cfg->wfmt > 2)
+    return fail(nullptr, MOE_E_INVAL, "bad shape");
+  if ((cfg->wfmt == 1 && (cfg->H % 128 || cfg->I % 128)) || (cfg->wfmt == 2 && (cfg->H % 32 || cfg->I % 32)))
+    return fail(nullptr, MOE_E_INVAL, "H and I must be multiples of the scale block");
+  std::vector<int32_t> C;
+  for (int e = 0; e < cfg->E; ++e)
+    if ((miss_mask[e >> 5] >> (e & 31)) & 1u) C.push_back(e);
+  HostPool* P = host_pool_create(nthreads_of(*cfg));
+  HostFfnHandle* h = host_ffn_start(P, host_shape(*cfg, blob_layout(*cfg).S), (const uint8_t*)host_pool, layer, T,
+                                    (const uint16_t*)hidden, topk_ids, topk_w, C.data(), (int)C.size(), out);
+  host_ffn_wait(P, h);
+  host_pool_destroy(P);
+  return MOE_OK;
+}
+
+int moe_layer_forward(moe_ctx* c, int layer, const void* hidden, const float* R, const float* bias, int T,
+                      const int32_t* slot_row, const uint32_t* miss_mask, const float* host_partial, void* out,
+                      void* stream) {
+  if (!c) return fail(nullptr, MOE_E_INVAL, "null ctx");
+  if (layer < 0 || layer >= c->cfg.L) return fail(c, MOE_E_INVAL, "layer out of range");
+  if (!slot_row && c->cfg.n_slots > 0) return fail(c, MOE_E_INVAL, "null slot table");
+  int rc = check_T(c, T);
+  if (rc) return rc;
+  if (T == 0) return MOE_OK;
+  hipStream_t s = as_stream(stream);
+  rc = route_only(c, hidden, R, bias, T, s);
+  if (rc) return rc;
+  rc = forward_experts(c, hidden, T, slot_row, miss_mask, s);
+  if (rc) return rc;
+  HIPCHK(c, moe_launch_combine(c->Z, c->ids, c->w, c->pos, miss_mask, slot_row, host_partial, T, c->cfg.k, c->cfg.H,
+                               (uint16_t*)out, s));
+  return MOE_OK;
+}
+
+int moe_decode_layer(moe_ctx* c, int layer, const void* hidden, const float* R, const float* bias, int T, void* out,
+                     moe_plan_info* info, void* compute_stream, void* copy_stream) {
+  if (!c) return fail(nullptr, MOE_E_INVAL, "null ctx");
+  const moe_config& g = c->cfg;
+  if (layer < 0 || layer >= g.L) return fail(c, MOE_E_INVAL, "layer out of range");
+  int rc = check_T(c, T);
+  if (rc) return rc;
+  if (T == 0) return MOE_OK;
+  hipStream_t s = as_stream(compute_stream), cs = as_stream(copy_stream);
+  rc = route_only(c, hidden, R, bias, T, s);
+  if (rc) return rc;
+  rc = plan_sync(c, layer, c->ids, T, c->mask, c->policy, s);
+  if (rc) return rc;
+  const bool may_host = c->policy != MOE_POLICY_OFFLOAD || g.n_slots < g.E;
+  if (may_host) {
+    HIPCHK(c, hipMemcpyAsync(c->ids_host, c->ids, (size_t)T * g.k * 4, hipMemcpyDeviceToHost, s));
+    HIPCHK(c, hipMemcpyAsync(c->w_host, c->w, (size_t)T * g.k * 4, hipMemcpyDeviceToHost, s));
+    HIPCHK(c, hipMemcpyAsync(c->hidden_host, hidden, (size_t)T * g.H * 2, hipMemcpyDeviceToHost, s));
+  }
+  HIPCHK(c, hipEventRecord(c->plan_evt, s));
+  HIPCHK(c, hipEventSynchronize(c->plan_evt));
+  const PlanOut& p = *c->plan_host;
+  fill_info(c, info);
+  // host branch first (section 2.5: the CPU branch is launched before the GPU miss path)
+  HostFfnHandle* h = nullptr;
+  if (p.n_host > 0) {
+    if (!may_host) return fail(c, MOE_E_INVAL, "host work planned without staged inputs");
+    h = host_ffn_start(c->pool, host_shape(g, c->bl.S), c->host_pool, layer, T, c->hidden_host, c->ids_host,
+                       c->w_host, p.C, p.n_host, c->hp_host);
+  }
+  if (p.q > 0) {
+    rc = issue_fills(c, layer, p.F, p.F_slot, p.q, cs);
+    if (rc) {
+      if (h) host_ffn_wait(c->pool, h);
+      return rc;
+    }
+  }
+  const int32_t* row = c->slot_table + (size_t)layer * g.E;
+  rc = forward_experts(c, hidden, T, row, c->mask, s);
+  if (h) host_ffn_wait(c->pool, h);
+  if (rc) return rc;
+  const float* hp = nullptr;
+  if (p.n_host > 0) {
+    HIPCHK(c, hipMemcpyAsync(c->hp, c->hp_host, (size_t)T * g.H * 4, hipMemcpyHostToDevice, s));
+    hp = c->hp;
+  }
+  HIPCHK(c, moe_launch_combine(c->Z, c->ids, c->w, c->pos, c->mask, row, hp, T, g.k, g.H, (uint16_t*)out, s));
+  return MOE_OK;
+}
+
+int prefill_stream_layer(moe_ctx* c, int layer, const void* hidden, const float* R, const float* bias, int T,
+                         void* out, void* compute_stream, void* copy_stream, int double_buffer) {
+  if (!c) return fail(nullptr, MOE_E_INVAL, "null ctx");
+  const moe_config& g = c->cfg;
+  if (layer < 0 || layer >= g.L) return fail(c, MOE_E_INVAL, "layer out of range");
+  int rc = check_T(c, T);
+  if (rc) return rc;
+  hipStream_t s = as_stream(compute_stream), cs = as_stream(copy_stream);
+  const size_t S = c->bl.S;
+  const size_t layer_bytes = (size_t)g.E * S;
+  if (g.n_slots < 2 * g.E) {
+    // not enough room for two full layers: on-demand loading of what is routed
+    const int saved = c->policy;
+    c->policy = MOE_POLICY_OFFLOAD;
+    rc = moe_decode_layer(c, layer, hidden, R, bias, T, out, nullptr, compute_stream, copy_stream);
+    c->policy = saved;
+    return rc ? rc : MOE_I_FALLBACK_ONDEMAND;
+  }
+  auto base_of = [&](int l) { return double_buffer ? (l & 1) * g.E : 0; };
+  auto buf_of = [&](int l) { return double_buffer ? (l & 1) : 0; };
+  auto issue_copy = [&](int l) -> int {
+    const int b = buf_of(l);
+    HIPCHK(c, hipStreamWaitEvent(cs, c->done[b], 0));
+    HIPCHK(c, moe_launch_install_layer(l, base_of(l), g.E, ++c->tick, c->slot_table, c->owner, c->last_use, cs));
+    HIPCHK(c, hipMemcpyAsync(c->slot_pool + (size_t)base_of(l) * S, c->host_pool + (size_t)l * layer_bytes,
+                             layer_bytes, hipMemcpyHostToDevice, cs));
+    HIPCHK(c, hipEventRecord(c->ready[b], cs));
+    return MOE_OK;
+  };
+  if (c->pf_next != layer) {
+    rc = issue_copy(layer);
+    if (rc) return rc;
+  }
+  if (double_buffer && layer + 1 < g.L) {
+    rc = issue_copy(layer + 1);
+    if (rc) return rc;
+  }
+  HIPCHK(c, hipStreamWaitEvent(s, c->ready[buf_of(layer)], 0));
+  if (T > 0) {
+    rc = route_only(c, hidden, R, bias, T, s);
+    if (rc) return rc;
+    const int32_t* row = c->slot_table + (size_t)layer * g.E;
+    rc = forward_experts(c, hidden, T, row, nullptr, s);
+    if (rc) return rc;
+    HIPCHK(c, moe_launch_combine(c->Z, c->ids, c->w, c->pos, nullptr, row, nullptr, T, g.k, g.H, (uint16_t*)out, s));
+  }
+  HIPCHK(c, hipEventRecord(c->done[buf_of(layer)], s));
+  if (!double_buffer && layer + 1 < g.L) {
+    rc = issue_copy(layer + 1);
+    if (rc) return rc;
+  }
+  c->pf_next = layer + 1 < g.L ? layer + 1 : -1;
+  return MOE_OK;
+}
+
+int moe_calibrate(moe_ctx* c, double* B_P, double* B_H) {
+  if (!c) return fail(nullptr, MOE_E_INVAL, "null ctx");
+  const moe_config& g = c->cfg;
+  const size_t S = c->bl.S;
+  // B_P: whole-expert copies into the highest-numbered slots (freed afterwards)
+  double bp = 0.0;
+  const int n = std::min(std::min(8, g.n_slots), g.L * g.E);
+  if (n > 0) {
+    hipStream_t s;
+    HIPCHK(c, hipStreamCreateWithFlags(&s, hipStreamNonBlocking));
+    hipEvent_t t0, t1;
+    HIPCHK(c, hipEventCreate(&t0));
+    HIPCHK(c, hipEventCreate(&t1));
+    for (int i = 0; i < n; ++i) c->list_dev_stage[i] = g.n_slots - 1 - i;
+    HIPCHK(c, hipMemcpyAsync(c->ids, c->list_dev_stage, (size_t)n * 4, hipMemcpyHostToDevice, s));
+    HIPCHK(c, moe_launch_free_slots(c->ids, n, c->slot_table, c->owner, c->last_use, s));
+    float best = 1e30f;
+    for (int rep = 0; rep < 4; ++rep) {
+      HIPCHK(c, hipEventRecord(t0, s));
+      for (int i = 0; i < n; ++i)
+        HIPCHK(c, hipMemcpyAsync(c->slot_pool + (size_t)(g.n_slots - 1 - i) * S, c->host_pool + (size_t)i * S, S,
+                                 hipMemcpyHostToDevice, s));
+      HIPCHK(c, hipEventRecord(t1, s));
+      HIPCHK(c, hipEventSynchronize(t1));
+      float ms = 0.f;
+      HIPCHK(c, hipEventElapsedTime(&ms, t0, t1));
+      if (rep > 0) best = std::min(best, ms);
+    }
+    bp = (double)n * S / (best * 1e-3) / 1e9;
+    (void)hipEventDestroy(t0);
+    (void)hipEventDestroy(t1);
+    (void)hipStreamDestroy(s);
+  }
+  // B_H: host FFN over k experts of layer 0 for one token
+  std::vector<uint16_t> hid((size_t)g.H, 0x3f80);
+  std::vector<int32_t> ids(g.k);
+  std::vector<float> w(g.k, 1.0f / g.k);
+  std::vector<float> outv((size_t)g.H);
+  std::vector<int32_t> C(g.k);
+  for (int j = 0; j < g.k; ++j) ids[j] = C[j] = j;
+  double best_h = 1e30;
+  for (int rep = 0; rep < 4; ++rep) {
+    auto a = std::chrono::steady_clock::now();
+    HostFfnHandle* h = host_ffn_start(c->pool, host_shape(g, S), c->host_pool, 0, 1, hid.data(), ids.data(), w.data(),
+                                      C.data(), g.k, outv.data());
+    host_ffn_wait(c->pool, h);
+    const double dt = std::chrono::duration<double>(std::chrono::steady_clock::now() - a).count();
+    if (rep > 0) best_h = std::min(best_h, dt);
+  }
+  const double bh = (double)g.k * S / best_h / 1e9;
+  if (B_P) *B_P = bp;
+  if (B_H) *B_H = bh;
+  return MOE_OK;
+}
+
+int moe_check_device_error(moe_ctx* c) {
+  if (!c) return fail(nullptr, MOE_E_INVAL, "null ctx");
+  int v = 0;
+  HIPCHK(c, hipDeviceSynchronize());
+  HIPCHK(c, hipMemcpy(&v, c->err, sizeof(int), hipMemcpyDeviceToHost));
+  HIPCHK(c, hipMemset(c->err, 0, sizeof(int)));
+  HIPCHK(c, hipDeviceSynchronize());
+  if (v) return fail(c, MOE_E_NOT_RESIDENT, "a routed expert was neither resident nor in the host miss set");
+  return MOE_OK;
+}
+
+}  // extern "C"

@@ -1,0 +1,132 @@
+// Weighted unpermute-combine and activation quantisation.
+//
+// Combine (paper.oopus.info review of FreeToken, section 2.5: the GPU and the
+// host each compute the partial sum of their own experts and the two are
+// added, leaving the MoE output unchanged):
+//   out[t] = bf16( sum_{j<k, e_tj on the GPU} w_tj * Z[pos[t,j]]  + host_partial[t] )
+// summed in fp32 in the order j = 0..k-1, then the host partial.
+//
+// Quantisation of GEMM inputs for the 8-bit weight formats (the pages only
+// say the kernels dequantise in-kernel; these are the declared readings):
+//   * fp8 path: per (row, 128 columns): scale = amax/448, code = E4M3(v*(448/amax));
+//   * mxfp4 path: OCP MX rule, E4M3 elements per 32 columns with E8M0 scale
+//     2^(floor(log2 amax) - 8).
+#include "common.h"
+
+__global__ void __launch_bounds__(256)
+combine_kernel(const uint16_t* __restrict__ Z, const int32_t* __restrict__ ids, const float* __restrict__ w,
+               const int32_t* __restrict__ pos, const uint32_t* __restrict__ miss_mask,
+               const int32_t* __restrict__ slot_row, const float* __restrict__ hp, int T, int k, int H,
+               uint16_t* __restrict__ out) {
+  const int t = blockIdx.y;
+  const int h = (blockIdx.x * 256 + threadIdx.x) * 8;
+  if (t >= T || h >= H) return;
+  float acc[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
+  for (int j = 0; j < k; ++j) {
+    const int e = ids[(size_t)t * k + j];
+    if (miss_mask && ((miss_mask[e >> 5] >> (e & 31)) & 1u)) continue;   // computed by the host
+    if (slot_row[e] < 0) continue;                                        // not resident: error flagged
+    const float wj = w[(size_t)t * k + j];
+    const i32x4_t zv = ld16(Z + (size_t)pos[(size_t)t * k + j] * H + h);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint32_t u = (uint32_t)zv[i];
+      acc[2 * i] += wj * bf16_bits_to_f32(u & 0xffffu);
+      acc[2 * i + 1] += wj * bf16_bits_to_f32(u >> 16);
+    }
+  }
+  if (hp) {
+    const float4 a = *(const float4*)(hp + (size_t)t * H + h);
+    const float4 b = *(const float4*)(hp + (size_t)t * H + h + 4);
+    acc[0] += a.x; acc[1] += a.y; acc[2] += a.z; acc[3] += a.w;
+    acc[4] += b.x; acc[5] += b.y; acc[6] += b.z; acc[7] += b.w;
+  }
+  i32x4_t o;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    o[i] = (int)((uint32_t)f32_to_bf16_bits(acc[2 * i]) | ((uint32_t)f32_to_bf16_bits(acc[2 * i + 1]) << 16));
+  *(i32x4_t*)(out + (size_t)t * H + h) = o;
+}
+
+template <bool SRC_BF16>
+DEV float load_src(const void* src, size_t i) {
+  if (SRC_BF16) return bf16_bits_to_f32(((const uint16_t*)src)[i]);
+  return ((const float*)src)[i];
+}
+
+// One wave per (row, 128-column group); rows from *nrows_dev when given.
+template <bool SRC_BF16>
+__global__ void __launch_bounds__(256)
+quant_fp8_kernel(const void* __restrict__ src, int rows, const int32_t* __restrict__ nrows_dev, int cols,
+                 uint8_t* __restrict__ q, float* __restrict__ scale) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int ng = cols / 128;
+  const int g = blockIdx.x * 4 + wave;
+  const int nrows = nrows_dev ? *nrows_dev : rows;
+  const int r = g / ng, c0 = (g - r * ng) * 128;
+  if (r >= nrows) return;
+  const size_t base = (size_t)r * cols + c0 + lane * 2;
+  const float v0 = load_src<SRC_BF16>(src, base), v1 = load_src<SRC_BF16>(src, base + 1);
+  const float amax = wave_max(fmaxf(fabsf(v0), fabsf(v1)));
+  const float inv = amax > 0.0f ? 448.0f / amax : 1.0f;
+  const float sc = amax > 0.0f ? amax / 448.0f : 1.0f;
+  const uint32_t q0 = f32_to_e4m3(v0 * inv), q1 = f32_to_e4m3(v1 * inv);
+  *(uint16_t*)(q + base) = (uint16_t)(q0 | (q1 << 8));
+  if (lane == 0) scale[(size_t)r * ng + c0 / 128] = sc;
+}
+
+// One wave per (row, 64 columns) = two 32-column MX blocks (lanes 0-31, 32-63).
+template <bool SRC_BF16>
+__global__ void __launch_bounds__(256)
+quant_mxfp8_kernel(const void* __restrict__ src, int rows, const int32_t* __restrict__ nrows_dev, int cols,
+                   uint8_t* __restrict__ q, uint8_t* __restrict__ scale) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int ng = cols / 64;
+  const int g = blockIdx.x * 4 + wave;
+  const int nrows = nrows_dev ? *nrows_dev : rows;
+  const int r = g / ng, c0 = (g - r * ng) * 64;
+  if (r >= nrows) return;
+  const size_t i = (size_t)r * cols + c0 + lane;
+  const float v = load_src<SRC_BF16>(src, i);
+  float amax = fabsf(v);
+#pragma unroll
+  for (int off = 16; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
+  int x = 0;
+  if (amax > 0.0f) {
+    int e;
+    frexpf(amax, &e);                    // amax = m * 2^e, m in [0.5, 1)
+    x = min(127, max(-127, (e - 1) - 8));
+  }
+  q[i] = (uint8_t)f32_to_e4m3(ldexpf(v, -x));
+  if ((lane & 31) == 0) scale[(size_t)r * (cols / 32) + (c0 + lane) / 32] = (uint8_t)(x + 127);
+}
+
+extern "C" hipError_t moe_launch_combine(const uint16_t* Z, const int32_t* ids, const float* w, const int32_t* pos,
+                                         const uint32_t* miss_mask, const int32_t* slot_row, const float* hp, int T,
+                                         int k, int H, uint16_t* out, hipStream_t s) {
+  if (T == 0) return hipSuccess;
+  dim3 g((H / 8 + 255) / 256, T);
+  combine_kernel<<<g, 256, 0, s>>>(Z, ids, w, pos, miss_mask, slot_row, hp, T, k, H, out);
+  return hipGetLastError();
+}
+
+extern "C" hipError_t moe_launch_quant(int fmt, int src_bf16, const void* src, int rows, const int32_t* nrows_dev,
+                                       int cols, uint8_t* q, void* scale, hipStream_t s) {
+  if (rows == 0) return hipSuccess;
+  if (fmt == WFMT_FP8) {
+    const int groups = rows * (cols / 128);
+    if (src_bf16)
+      quant_fp8_kernel<true><<<(groups + 3) / 4, 256, 0, s>>>(src, rows, nrows_dev, cols, q, (float*)scale);
+    else
+      quant_fp8_kernel<false><<<(groups + 3) / 4, 256, 0, s>>>(src, rows, nrows_dev, cols, q, (float*)scale);
+  } else {
+    const int groups = rows * (cols / 64);
+    if (src_bf16)
+      quant_mxfp8_kernel<true><<<(groups + 3) / 4, 256, 0, s>>>(src, rows, nrows_dev, cols, q, (uint8_t*)scale);
+    else
+      quant_mxfp8_kernel<false><<<(groups + 3) / 4, 256, 0, s>>>(src, rows, nrows_dev, cols, q, (uint8_t*)scale);
+  }
+  return hipGetLastError();
+}

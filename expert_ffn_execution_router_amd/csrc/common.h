@@ -1,0 +1,95 @@
+// Shared device-side definitions of the MoE layer library (gfx950 only).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+#include <stddef.h>
+
+typedef __bf16 bf16x8_t __attribute__((__vector_size__(8 * sizeof(__bf16))));
+typedef float f32x4_t __attribute__((__vector_size__(4 * sizeof(float))));
+typedef int i32x4_t __attribute__((__vector_size__(4 * sizeof(int))));
+typedef int i32x8_t __attribute__((__vector_size__(8 * sizeof(int))));
+
+#define DEV __device__ __forceinline__
+
+enum { WFMT_BF16 = 0, WFMT_FP8 = 1, WFMT_MXFP4 = 2 };
+
+// Tokens per m-block of the small-batch grouped GEMM (one wave covers 16
+// tokens per MFMA; a work item carries up to four such sub-tiles).
+constexpr int DEC_MB = 64;
+// Rows of weights per work item of the small-batch grouped GEMM.
+constexpr int DEC_NT = 16;
+
+// Device-resident description of one forward's grouped work, written by the
+// grouping kernels and read by the GEMM kernels (no host round trip).
+struct WorkList {
+  int n_act;          // experts that run on the GPU this call
+  int n_mblk;         // total m-blocks over those experts
+  int mb;             // tokens per m-block used to build mblk_prefix
+  int pad;
+  int act_e[256];     // expert id of active expert a (ascending ids)
+  int act_slot[256];  // slot holding it
+  int mblk_prefix[257];
+};
+
+// Result of the per-layer cache-control kernel, copied to the host.
+struct PlanOut {
+  int n_unique, n_hit, m, q, n_host, n_evict, eligible, tick;
+  int F[256];       // experts filled over the link, ascending
+  int F_slot[256];  // their slots
+  int C[256];       // experts executed on the host, ascending
+};
+
+DEV float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
+
+DEV uint16_t f32_to_bf16_bits(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (uint16_t)((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return (uint16_t)(u >> 16);
+}
+
+// OCP E4M3FN code of v, round to nearest even, saturating at +-448.
+DEV uint32_t f32_to_e4m3(float v) {
+  uint32_t u = __float_as_uint(v);
+  uint32_t s = (u >> 24) & 0x80u;
+  uint32_t a = u & 0x7fffffffu;
+  float af = __uint_as_float(a);
+  if (af >= 448.0f) return s | 0x7Eu;
+  if (af < 0.015625f) {                      // below 2^-6: subnormal step 2^-9
+    float q = rintf(af * 512.0f);            // exact scaling, RNE
+    return s | (uint32_t)q;                  // q == 8 is the smallest normal code
+  }
+  int E = (int)(a >> 23) - 127;
+  uint32_t m = a & 0x7fffffu;
+  uint32_t r = m >> 20, rem = m & 0xfffffu;
+  if (rem > 0x80000u || (rem == 0x80000u && (r & 1u))) ++r;
+  if (r == 8u) { r = 0u; ++E; }
+  uint32_t code = ((uint32_t)(E + 7) << 3) | r;
+  if (code > 0x7Eu) code = 0x7Eu;
+  return s | code;
+}
+
+DEV float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+DEV float wave_max(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v = fmaxf(v, __shfl_xor(v, off, 64));
+  return v;
+}
+
+DEV i32x4_t ld16(const void* p) { return *(const i32x4_t*)p; }
+DEV void st8(void* p, uint2 v) { *(uint2*)p = v; }
+
+// Locate active expert a holding global m-block p (mblk_prefix ascending).
+DEV int find_active(const WorkList* wl, int p) {
+  int lo = 0, hi = wl->n_act - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (wl->mblk_prefix[mid] <= p) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}

@@ -1,0 +1,278 @@
+// Host-side expert execution for the miss set C.
+//
+// Method (paper.oopus.info review of FreeToken, sections 2.5-2.6): experts in
+// C run on the CPU straight from the host expert pool, on a resident thread
+// pool, with dequantisation inside the kernel so the path stays bound by host
+// memory bandwidth; it returns the gate-weighted per-token partial output,
+// which the GPU adds to its own partial sum.
+//
+// Arithmetic: fp32 throughout (x widened exactly from bf16, weights
+// dequantised exactly, g, u, a = silu(g)*u and the down projection in fp32),
+// no intermediate rounding.  Experts are processed in ascending id order and
+// each output element is owned by one thread, so the result is deterministic.
+#include <atomic>
+#include <cmath>
+#include <cstdint>
+#include <cstring>
+#include <thread>
+#include <vector>
+#include <mutex>
+#include <condition_variable>
+#include <functional>
+
+#include "host_ffn.h"
+
+namespace {
+
+// E4M3FN value of each code, from the bit fields (bias 7, S.1111.111 = NaN).
+struct Tables {
+  float e4m3[256];
+  float e2m1[16];
+  Tables() {
+    for (int c = 0; c < 256; ++c) {
+      const int s = c >> 7, e = (c >> 3) & 15, m = c & 7;
+      float v;
+      if (e == 15 && m == 7) v = NAN;
+      else if (e == 0) v = std::ldexp((float)m, -9);
+      else v = std::ldexp(1.0f + m / 8.0f, e - 7);
+      e4m3[c] = s ? -v : v;
+    }
+    for (int c = 0; c < 16; ++c) {
+      const int s = c >> 3, e = (c >> 1) & 3, m = c & 1;
+      const float v = e == 0 ? 0.5f * m : std::ldexp(1.0f + 0.5f * m, e - 1);
+      e2m1[c] = s ? -v : v;
+    }
+  }
+};
+const Tables& tables() {
+  static Tables t;
+  return t;
+}
+
+// Dequantise row `r` of matrix `mat` (0 gate, 1 up, 2 down) into dst[cols].
+void load_row(const HostFfnShape& sh, const uint8_t* blob, int mat, int r, float* dst) {
+  const int rows = mat < 2 ? sh.I : sh.H;
+  const int cols = mat < 2 ? sh.H : sh.I;
+  const size_t n = (size_t)sh.H * sh.I;
+  const Tables& tb = tables();
+  if (sh.fmt == 0) {
+    const uint16_t* w = (const uint16_t*)blob + mat * n + (size_t)r * cols;
+    for (int c = 0; c < cols; ++c) {
+      const uint32_t u = (uint32_t)w[c] << 16;
+      float f;
+      std::memcpy(&f, &u, 4);
+      dst[c] = f;
+    }
+  } else if (sh.fmt == 1) {
+    const uint8_t* q = blob + mat * n + (size_t)r * cols;
+    const float* sc = (const float*)(blob + 3 * n) + mat * (n / 16384) + (size_t)(r / 128) * (cols / 128);
+    for (int c = 0; c < cols; ++c) dst[c] = tb.e4m3[q[c]] * sc[c / 128];
+  } else {
+    const uint8_t* p = blob + mat * (n / 2) + (size_t)r * (cols / 2);
+    const uint8_t* sc = blob + 3 * (n / 2) + mat * (n / 32) + (size_t)r * (cols / 32);
+    for (int b = 0; b < cols / 32; ++b) {
+      const float s = std::ldexp(1.0f, (int)sc[b] - 127);
+      for (int c = 0; c < 32; c += 2) {
+        const uint8_t v = p[(b * 32 + c) / 2];
+        dst[b * 32 + c] = tb.e2m1[v & 15] * s;
+        dst[b * 32 + c + 1] = tb.e2m1[v >> 4] * s;
+      }
+    }
+  }
+  (void)rows;
+}
+
+inline float dot(const float* a, const float* b, int n) {
+  float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f, s4 = 0.f, s5 = 0.f, s6 = 0.f, s7 = 0.f;
+  int i = 0;
+  for (; i + 8 <= n; i += 8) {
+    s0 += a[i] * b[i]; s1 += a[i + 1] * b[i + 1]; s2 += a[i + 2] * b[i + 2]; s3 += a[i + 3] * b[i + 3];
+    s4 += a[i + 4] * b[i + 4]; s5 += a[i + 5] * b[i + 5]; s6 += a[i + 6] * b[i + 6]; s7 += a[i + 7] * b[i + 7];
+  }
+  for (; i < n; ++i) s0 += a[i] * b[i];
+  return ((s0 + s1) + (s2 + s3)) + ((s4 + s5) + (s6 + s7));
+}
+
+}  // namespace
+
+// ---------------------------------------------------------------------------
+// resident thread pool with a phase barrier
+// ---------------------------------------------------------------------------
+struct HostPool {
+  int n;
+  std::vector<std::thread> th;
+  std::mutex mu;
+  std::condition_variable cv, done_cv;
+  std::function<void(int)> job;
+  uint64_t gen = 0;
+  int running = 0;
+  bool stop = false;
+  // spin barrier for phases inside a job
+  std::atomic<int> bar_count{0};
+  std::atomic<int> bar_gen{0};
+
+  explicit HostPool(int nthreads) : n(nthreads < 1 ? 1 : nthreads) {
+    for (int i = 0; i < n; ++i) th.emplace_back([this, i] { loop(i); });
+  }
+  ~HostPool() {
+    {
+      std::lock_guard<std::mutex> g(mu);
+      stop = true;
+    }
+    cv.notify_all();
+    for (auto& t : th) t.join();
+  }
+  void loop(int id) {
+    uint64_t seen = 0;
+    for (;;) {
+      std::function<void(int)> f;
+      {
+        std::unique_lock<std::mutex> g(mu);
+        cv.wait(g, [&] { return stop || gen != seen; });
+        if (stop) return;
+        seen = gen;
+        f = job;
+      }
+      f(id);
+      {
+        std::lock_guard<std::mutex> g(mu);
+        if (--running == 0) done_cv.notify_all();
+      }
+    }
+  }
+  void start(std::function<void(int)> f) {
+    {
+      std::lock_guard<std::mutex> g(mu);
+      job = std::move(f);
+      running = n;
+      ++gen;
+    }
+    cv.notify_all();
+  }
+  void wait() {
+    std::unique_lock<std::mutex> g(mu);
+    done_cv.wait(g, [&] { return running == 0; });
+  }
+  void barrier() {
+    const int g = bar_gen.load(std::memory_order_acquire);
+    if (bar_count.fetch_add(1, std::memory_order_acq_rel) == n - 1) {
+      bar_count.store(0, std::memory_order_relaxed);
+      bar_gen.fetch_add(1, std::memory_order_acq_rel);
+    } else {
+      while (bar_gen.load(std::memory_order_acquire) == g) std::this_thread::yield();
+    }
+  }
+};
+
+HostPool* host_pool_create(int nthreads) { return new HostPool(nthreads); }
+void host_pool_destroy(HostPool* p) { delete p; }
+int host_pool_threads(const HostPool* p) { return p->n; }
+
+// Body of the host FFN for worker `id` of `nt`.  Shared scratch lives in `ws`.
+struct HostFfnWork {
+  HostFfnShape sh;
+  const uint8_t* pool;
+  int layer, T;
+  const uint16_t* hidden;
+  const int32_t* ids;
+  const float* w;
+  const int32_t* C;
+  int nC;
+  float* out;
+  // scratch
+  std::vector<int> tok, jj;
+  std::vector<float> X, A;   // [n_e, H], [n_e, I]
+};
+
+static void host_ffn_worker(HostPool* P, HostFfnWork* W, int id) {
+  const HostFfnShape& sh = W->sh;
+  const int nt = P->n, H = sh.H, I = sh.I, k = sh.k;
+  const size_t S = sh.S;
+  std::vector<float> row((size_t)(H > I ? H : I)), row2((size_t)H);
+  // zero own slice of out
+  {
+    const size_t tot = (size_t)W->T * H;
+    const size_t a = tot * id / nt, b = tot * (id + 1) / nt;
+    std::memset(W->out + a, 0, (b - a) * sizeof(float));
+  }
+  P->barrier();
+  for (int ci = 0; ci < W->nC; ++ci) {
+    const int e = W->C[ci];
+    const uint8_t* blob = W->pool + ((size_t)W->layer * sh.E + e) * S;
+    if (id == 0) {
+      W->tok.clear();
+      W->jj.clear();
+      for (int t = 0; t < W->T; ++t)
+        for (int j = 0; j < k; ++j)
+          if (W->ids[(size_t)t * k + j] == e) { W->tok.push_back(t); W->jj.push_back(j); }
+      const int ne = (int)W->tok.size();
+      W->X.resize((size_t)ne * H);
+      W->A.resize((size_t)ne * I);
+      for (int r = 0; r < ne; ++r)
+        for (int h = 0; h < H; ++h) {
+          const uint32_t u = (uint32_t)W->hidden[(size_t)W->tok[r] * H + h] << 16;
+          float f;
+          std::memcpy(&f, &u, 4);
+          W->X[(size_t)r * H + h] = f;
+        }
+    }
+    P->barrier();
+    const int ne = (int)W->tok.size();
+    if (ne > 0) {
+      // gate / up rows [i0, i1)
+      const int i0 = (int)((long)I * id / nt), i1 = (int)((long)I * (id + 1) / nt);
+      for (int i = i0; i < i1; ++i) {
+        load_row(sh, blob, 0, i, row.data());
+        load_row(sh, blob, 1, i, row2.data());
+        for (int r = 0; r < ne; ++r) {
+          const float* x = &W->X[(size_t)r * H];
+          const float g = dot(row.data(), x, H);
+          const float u = dot(row2.data(), x, H);
+          W->A[(size_t)r * I + i] = g / (1.0f + std::exp(-g)) * u;
+        }
+      }
+    }
+    P->barrier();
+    if (ne > 0) {
+      const int h0 = (int)((long)H * id / nt), h1 = (int)((long)H * (id + 1) / nt);
+      for (int h = h0; h < h1; ++h) {
+        load_row(sh, blob, 2, h, row.data());
+        for (int r = 0; r < ne; ++r) {
+          const float y = dot(row.data(), &W->A[(size_t)r * I], I);
+          const int t = W->tok[r];
+          W->out[(size_t)t * H + h] += W->w[(size_t)t * k + W->jj[r]] * y;
+        }
+      }
+    }
+    P->barrier();
+  }
+}
+
+struct HostFfnHandle {
+  HostFfnWork work;
+};
+
+HostFfnHandle* host_ffn_start(HostPool* P, const HostFfnShape& sh, const uint8_t* pool, int layer, int T,
+                              const uint16_t* hidden, const int32_t* ids, const float* w, const int32_t* C, int nC,
+                              float* out) {
+  HostFfnHandle* h = new HostFfnHandle();
+  HostFfnWork& W = h->work;
+  W.sh = sh;
+  W.pool = pool;
+  W.layer = layer;
+  W.T = T;
+  W.hidden = hidden;
+  W.ids = ids;
+  W.w = w;
+  W.C = C;
+  W.nC = nC;
+  W.out = out;
+  HostFfnWork* wp = &W;
+  P->start([P, wp](int id) { host_ffn_worker(P, wp, id); });
+  return h;
+}
+
+void host_ffn_wait(HostPool* P, HostFfnHandle* h) {
+  P->wait();
+  delete h;
+}

@@ -1,0 +1,23 @@
+// Host FFN path: resident thread pool evaluating the host miss set C.
+#pragma once
+#include <cstddef>
+#include <cstdint>
+
+struct HostFfnShape {
+  int fmt, E, k, H, I;
+  size_t S;
+};
+
+struct HostPool;
+struct HostFfnHandle;
+
+HostPool* host_pool_create(int nthreads);
+void host_pool_destroy(HostPool* p);
+int host_pool_threads(const HostPool* p);
+
+// Starts the job on the pool and returns at once; out[T*H] is overwritten
+// with sum over (t, j) with ids[t,j] in C of w[t,j] * FFN_e(x_t).
+HostFfnHandle* host_ffn_start(HostPool* P, const HostFfnShape& sh, const uint8_t* pool, int layer, int T,
+                              const uint16_t* hidden, const int32_t* ids, const float* w, const int32_t* C, int nC,
+                              float* out);
+void host_ffn_wait(HostPool* P, HostFfnHandle* h);

@@ -1,0 +1,342 @@
+// Routing and grouping kernels: router logits, top-k with renormalised gate
+// weights, per-expert histogram, exclusive scan and stable token permutation.
+//
+// Method (paper.oopus.info review of FreeToken, sections 1-2; gpts24
+// analysis "FreeToken 重写本地 MoE 推理"): a gate network picks a few experts
+// per token.  The gate is softmax over E router logits; selection uses the
+// logits (larger first, equal values -> lower expert index) and the k chosen
+// weights are the softmax over the chosen logits, i.e. the full softmax
+// renormalised over them.  Grouping sorts the (token, choice) assignments by
+// expert, tokens ascending inside an expert (a stable counting sort, so the
+// result is a deterministic function of the routing).
+#include "common.h"
+
+// ---------------------------------------------------------------------------
+// router logits z[t,e] = sum_h x[t,h] R[e,h] + b[e]  (x bf16, R fp32, fp32 sums)
+// ---------------------------------------------------------------------------
+
+// Small batches: one wave per expert streams its row of R once; H % 256 == 0.
+__global__ void __launch_bounds__(256)
+router_small_kernel(const uint16_t* __restrict__ x, const float* __restrict__ R,
+                    const float* __restrict__ bias, int T, int E, int H, float* __restrict__ z) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int e = blockIdx.x * 4 + wave;
+  if (e >= E) return;
+  const float* r = R + (size_t)e * H;
+  const float b = bias ? bias[e] : 0.0f;
+  for (int t0 = 0; t0 < T; t0 += 16) {
+    const int nt = min(16, T - t0);
+    float acc[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
+    for (int h = lane * 4; h < H; h += 256) {
+      const float4 rv = *(const float4*)(r + h);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        if (i < nt) {
+          const uint2 xv = *(const uint2*)(x + (size_t)(t0 + i) * H + h);
+          acc[i] += bf16_bits_to_f32(xv.x & 0xffffu) * rv.x;
+          acc[i] += bf16_bits_to_f32(xv.x >> 16) * rv.y;
+          acc[i] += bf16_bits_to_f32(xv.y & 0xffffu) * rv.z;
+          acc[i] += bf16_bits_to_f32(xv.y >> 16) * rv.w;
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const float v = wave_sum(acc[i]);
+      if (lane == 0 && i < nt) z[(size_t)(t0 + i) * E + e] = v + b;
+    }
+  }
+}
+
+// Large batches: 64 tokens x 64 experts per workgroup, K staged through LDS.
+__global__ void __launch_bounds__(256)
+router_tiled_kernel(const uint16_t* __restrict__ x, const float* __restrict__ R,
+                    const float* __restrict__ bias, int T, int E, int H, float* __restrict__ z) {
+  __shared__ float xs[32][65];
+  __shared__ float rs[32][65];
+  const int t0 = blockIdx.x * 64, e0 = blockIdx.y * 64;
+  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
+  float acc[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) acc[i][j] = 0.0f;
+  for (int k0 = 0; k0 < H; k0 += 32) {
+    for (int i = tid; i < 64 * 32; i += 256) {
+      const int tt = i >> 5, kk = i & 31;
+      const int t = t0 + tt, e = e0 + tt;
+      xs[kk][tt] = t < T ? bf16_bits_to_f32(x[(size_t)t * H + k0 + kk]) : 0.0f;
+      rs[kk][tt] = e < E ? R[(size_t)e * H + k0 + kk] : 0.0f;
+    }
+    __syncthreads();
+#pragma unroll 8
+    for (int kk = 0; kk < 32; ++kk) {
+      float a[4], b[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) { a[i] = xs[kk][ty * 4 + i]; b[i] = rs[kk][tx * 4 + i]; }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) acc[i][j] += a[i] * b[j];
+    }
+    __syncthreads();
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int t = t0 + ty * 4 + i;
+    if (t >= T) continue;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int e = e0 + tx * 4 + j;
+      if (e < E) z[(size_t)t * E + e] = acc[i][j] + (bias ? bias[e] : 0.0f);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// top-k (one wave per token, E <= 256) and renormalised weights
+// ---------------------------------------------------------------------------
+__global__ void __launch_bounds__(256)
+topk_kernel(const float* __restrict__ z, int T, int E, int k, int32_t* __restrict__ ids,
+            float* __restrict__ w) {
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int t = blockIdx.x * 4 + wave;
+  if (t >= T) return;
+  const float* zr = z + (size_t)t * E;
+  float v[4];
+  bool taken[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = lane + 64 * i;
+    v[i] = e < E ? zr[e] : 0.0f;
+    taken[i] = e >= E;
+  }
+  float selv[8];
+  int sele[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    if (j >= k) break;
+    float bv = 0.0f;
+    int be = 0x7fffffff;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int e = lane + 64 * i;
+      if (!taken[i] && (be == 0x7fffffff || v[i] > bv)) { bv = v[i]; be = e; }
+    }
+#pragma unroll
+    for (int off = 32; off >= 1; off >>= 1) {
+      const float ov = __shfl_xor(bv, off, 64);
+      const int oe = __shfl_xor(be, off, 64);
+      const bool better = (oe != 0x7fffffff) &&
+                          (be == 0x7fffffff || ov > bv || (ov == bv && oe < be));
+      if (better) { bv = ov; be = oe; }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      if (be == lane + 64 * i) taken[i] = true;
+    selv[j] = bv;
+    sele[j] = be;
+  }
+  // softmax over the chosen logits (max is the first one)
+  float ex[8], s = 0.0f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    if (j >= k) break;
+    ex[j] = expf(selv[j] - selv[0]);
+    s += ex[j];
+  }
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    if (j >= k) break;
+    if (lane == j) {
+      ids[(size_t)t * k + j] = sele[j];
+      w[(size_t)t * k + j] = ex[j] / s;
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// grouping: histogram -> exclusive scan -> stable scatter
+// ---------------------------------------------------------------------------
+constexpr int GROUP_TOK = 256;   // tokens per grouping block
+
+// Exclusive scan of one value per thread over a 256-thread block.
+__device__ int block_exclusive_scan256(int v, int* tmp /* >= 4 ints of LDS */, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  int incl = v;
+#pragma unroll
+  for (int off = 1; off < 64; off <<= 1) {
+    const int o = __shfl_up(incl, off, 64);
+    if (lane >= off) incl += o;
+  }
+  if (lane == 63) tmp[wave] = incl;
+  __syncthreads();
+  int base = 0;
+  for (int i = 0; i < wave; ++i) base += tmp[i];
+  *total = tmp[0] + tmp[1] + tmp[2] + tmp[3];
+  __syncthreads();
+  return base + incl - v;
+}
+
+// From per-expert counts (thread e holds counts[e]), write offsets, the list
+// of experts that run on the GPU (routed, not in the host miss mask) with
+// their slots and m-block prefix.  A routed, unmasked expert without a slot
+// raises the device error flag and is skipped.
+__device__ void finish_grouping(int cnt, int E, const uint32_t* miss_mask, const int32_t* slot_row,
+                                int32_t* counts, int32_t* offsets, WorkList* wl, int mb, int* err,
+                                int* tmp) {
+  const int e = threadIdx.x;
+  const int c = e < E ? cnt : 0;
+  int total;
+  const int off = block_exclusive_scan256(c, tmp, &total);
+  if (e < E) { counts[e] = c; offsets[e] = off; }
+  if (e == 0) offsets[E] = total;
+  bool act = false;
+  int slot = -1;
+  if (e < E && c > 0) {
+    const bool masked = miss_mask && ((miss_mask[e >> 5] >> (e & 31)) & 1u);
+    if (!masked) {
+      slot = slot_row ? slot_row[e] : 0;     // no table: grouping only
+      if (slot < 0) atomicOr(err, 1);
+      else act = true;
+    }
+  }
+  int nact;
+  const int a = block_exclusive_scan256(act ? 1 : 0, tmp, &nact);
+  const int nb = act ? (c + mb - 1) / mb : 0;
+  int nmblk;
+  const int pb = block_exclusive_scan256(nb, tmp, &nmblk);
+  if (act) { wl->act_e[a] = e; wl->act_slot[a] = slot; wl->mblk_prefix[a] = pb; }
+  if (e == 0) { wl->n_act = nact; wl->n_mblk = nmblk; wl->mb = mb; wl->mblk_prefix[nact] = nmblk; }
+}
+
+// Stable scatter of one block of tokens given per-expert bases for the block.
+// bits: LDS [E][8] words, token-major presence bits of the block.
+__device__ void scatter_block(const int32_t* __restrict__ ids, int t0, int T, int k, int E,
+                              const int* base /* per expert, may be LDS or global */, uint32_t* bits,
+                              int32_t* __restrict__ pos, int32_t* __restrict__ perm_tok) {
+  const int tl = threadIdx.x, t = t0 + tl;
+  const int wi = tl >> 5;
+  const uint32_t below = (1u << (tl & 31)) - 1u;
+  if (t < T) {
+    for (int j = 0; j < k; ++j) {
+      const int e = ids[(size_t)t * k + j];
+      int r = __popc(bits[e * 8 + wi] & below);
+      for (int q = 0; q < wi; ++q) r += __popc(bits[e * 8 + q]);
+      const int p = base[e] + r;
+      pos[(size_t)t * k + j] = p;
+      perm_tok[p] = t;
+    }
+  }
+}
+
+__device__ void mark_block(const int32_t* __restrict__ ids, int t0, int T, int k, int E, uint32_t* bits) {
+  for (int i = threadIdx.x; i < E * 8; i += blockDim.x) bits[i] = 0u;
+  __syncthreads();
+  const int tl = threadIdx.x, t = t0 + tl;
+  if (t < T)
+    for (int j = 0; j < k; ++j) {
+      const int e = ids[(size_t)t * k + j];
+      atomicOr(&bits[e * 8 + (tl >> 5)], 1u << (tl & 31));
+    }
+  __syncthreads();
+}
+
+// T <= 256: histogram, scan, work list and scatter in one workgroup.
+__global__ void __launch_bounds__(256)
+group_single_kernel(const int32_t* __restrict__ ids, int T, int k, int E, const uint32_t* miss_mask,
+                    const int32_t* slot_row, int mb, int32_t* counts, int32_t* offsets,
+                    int32_t* __restrict__ pos, int32_t* __restrict__ perm_tok, WorkList* wl, int* err) {
+  __shared__ uint32_t bits[256 * 8];
+  __shared__ int base[256];
+  __shared__ int tmp[4];
+  mark_block(ids, 0, T, k, E, bits);
+  int cnt = 0;
+  if ((int)threadIdx.x < E)
+    for (int q = 0; q < 8; ++q) cnt += __popc(bits[threadIdx.x * 8 + q]);
+  finish_grouping(cnt, E, miss_mask, slot_row, counts, offsets, wl, mb, err, tmp);
+  if ((int)threadIdx.x < E) base[threadIdx.x] = offsets[threadIdx.x];
+  __syncthreads();
+  scatter_block(ids, 0, T, k, E, base, bits, pos, perm_tok);
+}
+
+// General path, pass 1: per-block histograms hist[b][e].
+__global__ void __launch_bounds__(256)
+group_count_kernel(const int32_t* __restrict__ ids, int T, int k, int E, int32_t* __restrict__ hist) {
+  __shared__ uint32_t bits[256 * 8];
+  const int t0 = blockIdx.x * GROUP_TOK;
+  mark_block(ids, t0, T, k, E, bits);
+  if ((int)threadIdx.x < E) {
+    int c = 0;
+    for (int q = 0; q < 8; ++q) c += __popc(bits[threadIdx.x * 8 + q]);
+    hist[(size_t)blockIdx.x * E + threadIdx.x] = c;
+  }
+}
+
+// General path, pass 2: counts, offsets, work list; hist[b][e] becomes the
+// block's base row for expert e.
+__global__ void __launch_bounds__(256)
+group_scan_kernel(int nblk, int E, const uint32_t* miss_mask, const int32_t* slot_row, int mb,
+                  int32_t* __restrict__ hist, int32_t* counts, int32_t* offsets, WorkList* wl, int* err) {
+  __shared__ int tmp[4];
+  const int e = threadIdx.x;
+  int cnt = 0;
+  if (e < E)
+    for (int b = 0; b < nblk; ++b) cnt += hist[(size_t)b * E + e];
+  finish_grouping(cnt, E, miss_mask, slot_row, counts, offsets, wl, mb, err, tmp);
+  if (e < E) {
+    int run = offsets[e];
+    for (int b = 0; b < nblk; ++b) {
+      const int h = hist[(size_t)b * E + e];
+      hist[(size_t)b * E + e] = run;
+      run += h;
+    }
+  }
+}
+
+// General path, pass 3: stable scatter per block.
+__global__ void __launch_bounds__(256)
+group_scatter_kernel(const int32_t* __restrict__ ids, int T, int k, int E, const int32_t* __restrict__ hist,
+                     int32_t* __restrict__ pos, int32_t* __restrict__ perm_tok) {
+  __shared__ uint32_t bits[256 * 8];
+  const int t0 = blockIdx.x * GROUP_TOK;
+  mark_block(ids, t0, T, k, E, bits);
+  scatter_block(ids, t0, T, k, E, hist + (size_t)blockIdx.x * E, bits, pos, perm_tok);
+}
+
+// ---------------------------------------------------------------------------
+// launchers
+// ---------------------------------------------------------------------------
+extern "C" hipError_t moe_launch_router(const uint16_t* x, const float* R, const float* bias, int T, int E, int H,
+                                        float* z, hipStream_t s) {
+  if (T <= 64) {
+    router_small_kernel<<<(E + 3) / 4, 256, 0, s>>>(x, R, bias, T, E, H, z);
+  } else {
+    dim3 g((T + 63) / 64, (E + 63) / 64);
+    router_tiled_kernel<<<g, 256, 0, s>>>(x, R, bias, T, E, H, z);
+  }
+  return hipGetLastError();
+}
+
+extern "C" hipError_t moe_launch_topk(const float* z, int T, int E, int k, int32_t* ids, float* w, hipStream_t s) {
+  topk_kernel<<<(T + 3) / 4, 256, 0, s>>>(z, T, E, k, ids, w);
+  return hipGetLastError();
+}
+
+extern "C" hipError_t moe_launch_group(const int32_t* ids, int T, int k, int E, const uint32_t* miss_mask,
+                                       const int32_t* slot_row, int mb, int32_t* counts, int32_t* offsets,
+                                       int32_t* pos, int32_t* perm_tok, int32_t* hist, WorkList* wl, int* err,
+                                       hipStream_t s) {
+  if (T <= GROUP_TOK) {
+    group_single_kernel<<<1, 256, 0, s>>>(ids, T, k, E, miss_mask, slot_row, mb, counts, offsets, pos, perm_tok,
+                                          wl, err);
+  } else {
+    const int nblk = (T + GROUP_TOK - 1) / GROUP_TOK;
+    group_count_kernel<<<nblk, 256, 0, s>>>(ids, T, k, E, hist);
+    group_scan_kernel<<<1, 256, 0, s>>>(nblk, E, miss_mask, slot_row, mb, hist, counts, offsets, wl, err);
+    group_scatter_kernel<<<nblk, 256, 0, s>>>(ids, T, k, E, hist, pos, perm_tok);
+  }
+  return hipGetLastError();
+}

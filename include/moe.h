@@ -1,0 +1,230 @@
+/*
+ * moe.h - C ABI of the routed MoE-layer library for MI355X (gfx950).
+ *
+ * One routed MoE layer forward whose expert weights sit in a shared HBM slot
+ * pool keyed by (layer, expert), with the full expert pool in pinned host
+ * memory as the source of truth.  The method follows the paper.oopus.info
+ * review of FreeToken ("论文综述：FreeToken 让个人电脑跑起前沿 MoE 大模型的边缘原生
+ * 服务系统"):
+ *   section 2    two-level expert memory; one slot holds every tensor of one
+ *                (layer, expert); the cache affects speed, never the output;
+ *   section 2.2  full-layer double buffering during prefill;
+ *   section 2.4  one global LRU over all layers' experts;
+ *   section 2.5  the miss set splits into fills (q of m) and host execution,
+ *                q* = m B_P / B_H; the two partial sums are added exactly;
+ *   section 2.6  device-side cache control in one kernel per layer; the host
+ *                branch returns gate-weighted per-token partial outputs;
+ *   section 2.7  expert banks indexed by the flattened id l*E + e.
+ *
+ * Conventions for every call:
+ *   - "device" pointers are HIP device memory, "host" pointers are host
+ *     memory (pinned where stated).  The caller owns every buffer it passes;
+ *     the library keeps no reference beyond the call except for the buffers
+ *     given to moe_create (host pool, slot pool, workspace), which must stay
+ *     alive until moe_destroy.
+ *   - The library allocates no device memory.  It allocates pinned host
+ *     staging buffers and a host thread pool inside the context.
+ *   - `stream` arguments are hipStream_t values passed as void* (NULL = the
+ *     null stream).  Calls taking a stream enqueue their GPU work on it and
+ *     return without waiting unless stated otherwise.
+ *   - Returns 0 on success, a negative MOE_E_* code on error (message in
+ *     moe_last_error), or a positive informational code.  No C++ exception
+ *     crosses this interface.  One context must not be used from two host
+ *     threads at once.
+ *
+ * Data layout:
+ *   hidden      bf16 [T, H] row-major (device)
+ *   router_w    fp32 [E, H] row-major (device); router_bias fp32 [E] or NULL
+ *   expert blob (S = moe_expert_bytes bytes; host pool row l*E+e, one slot):
+ *     gate [I, H], up [I, H], down [H, I], row-major [out, in], then
+ *     - fp8:   fp32 scale per 128x128 block of each matrix ([rows/128][cols/128],
+ *              gate, up, down), weight = E4M3FN code * scale;
+ *     - mxfp4: E8M0 scale per 32 consecutive inputs of each row ([rows][cols/32],
+ *              gate, up, down); two E2M1 codes per byte, even input in the low
+ *              nibble; weight = E2M1 value * 2^(scale - 127).
+ *   out         bf16 [T, H] (device)
+ */
+#ifndef MOE_H
+#define MOE_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct moe_ctx moe_ctx;
+
+enum {
+  MOE_OK = 0,
+  MOE_E_INVAL = -1,          /* bad shape or argument */
+  MOE_E_HIP = -2,            /* HIP runtime error (detail in moe_last_error) */
+  MOE_E_NOSLOTS = -3,        /* slot pool too small for the request */
+  MOE_E_PIN = -4,            /* pinned host allocation failed */
+  MOE_E_NOT_RESIDENT = -5,   /* a routed expert neither resident nor masked (device flag) */
+  MOE_E_UNSUPPORTED = -6,    /* shape outside the supported range */
+  MOE_I_FALLBACK_ONDEMAND = 1 /* prefill ran on demand: fewer than 2E slots */
+};
+
+enum { MOE_W_BF16 = 0, MOE_W_FP8_E4M3_B128 = 1, MOE_W_MXFP4 = 2 };
+
+/* Miss policy (paper.oopus.info review, section 5 lists the backend switch
+ * offload / cpu / hybrid): OFFLOAD fills every miss (q = m), HOST executes
+ * every miss on the host (q = 0), HYBRID uses q* = round(m B_P / B_H),
+ * at least 1 (section 2.5). */
+enum { MOE_POLICY_OFFLOAD = 0, MOE_POLICY_HOST = 1, MOE_POLICY_HYBRID = 2 };
+
+typedef struct {
+  int L, E, k, H, I;   /* layers, experts per layer (<= 256), top-k (<= 8), hidden, expert intermediate */
+  int wfmt;            /* MOE_W_* */
+  int n_slots;         /* slots in the device slot pool (<= 8192) */
+  int max_tokens;      /* largest T of any call */
+  int host_threads;    /* host FFN threads (0: hardware concurrency) */
+} moe_config;
+
+/* Outcome of one planning call (section 2.5 quantities). */
+typedef struct {
+  int n_unique;        /* distinct experts routed in this layer */
+  int n_hit;           /* resident ones (H) */
+  int m;               /* misses */
+  int q;               /* filled over the link (F) */
+  int n_host;          /* executed on the host (C = m - q) */
+  int n_evict;         /* occupied slots overwritten */
+  double t_fill_pred_us, t_host_pred_us;  /* qS/B_P and (m-q)S/(B_H-B_P) */
+} moe_plan_info;
+
+/* Bytes of one expert blob S for the configuration (layout above). */
+size_t moe_expert_bytes(const moe_config* cfg);
+
+/* Bytes of device workspace moe_create needs for this configuration. */
+size_t moe_workspace_bytes(const moe_config* cfg);
+
+/* Creates a context.  host_pool: host [L*E][S] bytes, pinned (moe_host_alloc)
+ * for the copy engines, row l*E+e = expert e of layer l (section 2.7 banks);
+ * d_slot_pool: device, n_slots*S bytes; d_workspace: device,
+ * moe_workspace_bytes bytes.  Starts with an empty cache (section 2.7: cold
+ * start, no warm-up).  Errors: INVAL (shapes: H, I multiples of 128 and H of
+ * 256, E <= 256, k <= 8, k <= E, n_slots <= 8192, sizes too small), HIP,
+ * PIN (staging), UNSUPPORTED. */
+int moe_create(const moe_config* cfg, void* host_pool, size_t host_bytes, void* d_slot_pool, size_t slot_bytes,
+               void* d_workspace, size_t ws_bytes, moe_ctx** out);
+int moe_destroy(moe_ctx* ctx);
+
+/* Last error message of ctx, or of the calling thread when ctx is NULL. */
+const char* moe_last_error(moe_ctx* ctx);
+
+/* Pinned host memory for the host expert pool (hipHostMalloc); the caller
+ * fills it and frees it with moe_host_free after moe_destroy. */
+int moe_host_alloc(size_t bytes, void** out);
+int moe_host_free(void* p);
+
+/* Miss policy and the bandwidths (GB/s) q* uses (section 2.5). */
+int moe_set_policy(moe_ctx* ctx, int policy, double B_P, double B_H);
+
+/* Startup calibration on the deployed shapes (section 2.5, section 3 Table 1):
+ * B_P = pinned-host -> slot copy rate of whole experts, B_H = effective
+ * weight-byte rate of the host FFN with the configured threads, both GB/s.
+ * Uses the least recently used slots as copy targets and leaves them empty.
+ * Synchronous. */
+int moe_calibrate(moe_ctx* ctx, double* B_P, double* B_H);
+
+/* Device int32 [L*E] residency table: slot of (l, e) or -1. */
+int32_t* moe_slot_table(moe_ctx* ctx);
+
+/* Empties the cache (every slot free, table -1) and clears the device error
+ * flag; enqueued on stream. */
+int moe_reset_cache(moe_ctx* ctx, void* stream);
+
+/* Router: logits z = hidden router_w^T + bias (fp32), top-k by logit (larger
+ * first, ties to the lower expert id), weights = softmax over the chosen
+ * logits.  topk_ids int32 [T, k], topk_w fp32 [T, k] (device). */
+int moe_route(moe_ctx* ctx, const void* hidden, const float* router_w, const float* router_bias, int T,
+              int32_t* topk_ids, float* topk_w, void* stream);
+
+/* Same selection from given fp32 logits [T, E] (device), plus the grouping:
+ * counts int32 [E], offsets int32 [E+1] (exclusive scan), perm_tok int32 [T*k]
+ * (token of each grouped row: experts ascending, tokens ascending within an
+ * expert), pos int32 [T, k] (grouped row of each choice).  All device. */
+int moe_route_from_logits(moe_ctx* ctx, const float* logits, int T, int32_t* topk_ids, float* topk_w,
+                          int32_t* counts, int32_t* offsets, int32_t* perm_tok, int32_t* pos, void* stream);
+
+/* Device-side cache control for one layer (section 2.6): de-duplicate the
+ * routed experts in topk_ids (device [T, k]), classify hits and misses,
+ * choose q by the policy, pick victims by LRU, rewrite the residency table
+ * and write the host-set bits into miss_mask_out (device uint32 [8], bit e
+ * set = expert e runs on the host).  Does NOT copy weights: slot_pool_fill
+ * or moe_decode_layer does.  Blocks the calling thread until the plan is
+ * known; info may be NULL.  The fills it decided are returned through
+ * fill_experts / fill_slots (host int32 [E] each, may be NULL). */
+int moe_plan(moe_ctx* ctx, int layer, const int32_t* topk_ids, int T, uint32_t* miss_mask_out,
+             moe_plan_info* info, int32_t* fill_experts, int32_t* fill_slots, void* stream);
+
+/* Copies expert (layer, experts[i]) from the host pool into slots[i] on
+ * copy_stream (n whole-expert DMAs of S bytes) and records the context's
+ * fill event, which the next forward on any stream waits for. */
+int slot_pool_fill(moe_ctx* ctx, int layer, const int32_t* experts, const int32_t* slots, int n, void* copy_stream);
+
+/* LRU admission of the given experts of a layer (host int32 [n]): already
+ * resident ones are refreshed, the others take the least recently used
+ * slots and are copied from the host pool on copy_stream.  Blocks until the
+ * admission plan is known (not until the copies end). */
+int slot_pool_admit(moe_ctx* ctx, int layer, const int32_t* experts, int n, void* copy_stream);
+
+/* Drops the given experts of a layer (host int32 [n]) from the cache. */
+int slot_pool_evict(moe_ctx* ctx, int layer, const int32_t* experts, int n);
+
+/* Host branch (section 2.6): host_partial_out[t] = sum over j with
+ * topk_ids[t,j] in the mask of topk_w[t,j] * FFN_e(hidden[t]), fp32, computed
+ * from the host pool by the context's thread pool.  All pointers host:
+ * hidden bf16 [T,H], topk_ids [T,k], topk_w [T,k], miss_mask uint32 [8],
+ * host_partial_out fp32 [T,H].  Synchronous. */
+int moe_host_partial(moe_ctx* ctx, int layer, const void* hidden, const int32_t* topk_ids, const float* topk_w,
+                     int T, const uint32_t* miss_mask, float* host_partial_out);
+
+/* The same computation without a context or GPU: host_pool as in
+ * moe_create, host_threads as in moe_config.  Synchronous. */
+int moe_host_ffn(const moe_config* cfg, const void* host_pool, int layer, const void* hidden,
+                 const int32_t* topk_ids, const float* topk_w, int T, const uint32_t* miss_mask,
+                 float* host_partial_out);
+
+/* The routed MoE layer forward on the GPU:
+ *   out[t] = bf16( sum_{j: e_tj not in mask} w_tj * FFN_e(hidden[t]) + host_partial[t] )
+ * routing as moe_route; experts found through slot_table (device int32 [E],
+ * this layer's row: slot or -1) in the context's slot pool; miss_mask
+ * (device uint32 [8] or NULL) marks experts whose contribution is already in
+ * host_partial (device fp32 [T, H] or NULL).  A routed, unmasked expert
+ * without a slot sets the device error flag (moe_check_device_error) and is
+ * left out.  T <= max_tokens.  Waits for pending fills. */
+int moe_layer_forward(moe_ctx* ctx, int layer, const void* hidden, const float* router_w, const float* router_bias,
+                      int T, const int32_t* slot_table, const uint32_t* miss_mask, const float* host_partial,
+                      void* out, void* stream);
+
+/* One decode-time layer through the cache (sections 2.4-2.6): route, plan
+ * (host sync once), start the host branch on C, fill F on copy_stream,
+ * grouped GPU evaluation of H u F on compute_stream, add the host partial.
+ * Returns after the work is enqueued and the host branch has finished; info
+ * may be NULL. */
+int moe_decode_layer(moe_ctx* ctx, int layer, const void* hidden, const float* router_w, const float* router_bias,
+                     int T, void* out, moe_plan_info* info, void* compute_stream, void* copy_stream);
+
+/* Prefill with full-layer double buffering (section 2.2): layer l computes
+ * from one E-slot buffer while layer l+1's complete expert set is copied into
+ * the other on copy_stream.  Buffers are slots [0, E) and [E, 2E) of the
+ * pool, entered into the LRU table (survivors warm decode).  Call for
+ * l = 0..L-1 in order; layer 0 also issues its own copy.  With fewer than 2E
+ * slots it runs on demand and returns MOE_I_FALLBACK_ONDEMAND.
+ * double_buffer = 0 serialises copy and compute (ablation). */
+int prefill_stream_layer(moe_ctx* ctx, int layer, const void* hidden, const float* router_w,
+                         const float* router_bias, int T, void* out, void* compute_stream, void* copy_stream,
+                         int double_buffer);
+
+/* Reads and clears the device error flag (synchronous): MOE_OK or
+ * MOE_E_NOT_RESIDENT. */
+int moe_check_device_error(moe_ctx* ctx);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_H */
