@@ -41,6 +41,18 @@ class moe_plan_info(ctypes.Structure):
         return {f: getattr(self, f) for f, _ in self._fields_}
 
 
+MOE_N_STAGES = 9
+STAGES = ["route", "topk", "group", "quant_x", "gemm1", "quant_a", "gemm2", "combine", "plan"]
+
+
+class moe_profile(ctypes.Structure):
+    _fields_ = [("launches", ctypes.c_int * MOE_N_STAGES), ("ms", ctypes.c_double * MOE_N_STAGES),
+                ("dropped", ctypes.c_int)]
+
+    def as_dict(self):
+        return {name: {"launches": self.launches[i], "ms": self.ms[i]} for i, name in enumerate(STAGES)}
+
+
 _vp, _i, _sz, _d = ctypes.c_void_p, ctypes.c_int, ctypes.c_size_t, ctypes.c_double
 _P = ctypes.POINTER
 
@@ -69,6 +81,8 @@ SIGNATURES = {
     "moe_decode_layer": (_i, [_vp, _i, _vp, _vp, _vp, _i, _vp, _P(moe_plan_info), _vp, _vp]),
     "prefill_stream_layer": (_i, [_vp, _i, _vp, _vp, _vp, _i, _vp, _vp, _vp, _i]),
     "moe_check_device_error": (_i, [_vp]),
+    "moe_profile_begin": (_i, [_vp, _i]),
+    "moe_profile_end": (_i, [_vp, _P(moe_profile)]),
 }
 
 _lib = None
@@ -136,6 +150,8 @@ moe_layer_forward = _fn("moe_layer_forward")
 moe_decode_layer = _fn("moe_decode_layer")
 prefill_stream_layer = _fn("prefill_stream_layer")
 moe_check_device_error = _fn("moe_check_device_error")
+moe_profile_begin = _fn("moe_profile_begin")
+moe_profile_end = _fn("moe_profile_end")
 
 
 def make_config(L, E, k, H, I, wfmt, n_slots, max_tokens, host_threads=0) -> moe_config:

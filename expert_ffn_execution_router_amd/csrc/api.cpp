@@ -169,6 +169,11 @@ struct moe_ctx {
   int pf_next = -1;
   HostPool* pool = nullptr;
   std::string err_msg;
+  // optional per-stage timing (moe_profile_begin / moe_profile_end)
+  bool prof_on = false;
+  std::vector<hipEvent_t> prof_ev;      // 2 per record
+  std::vector<int> prof_stage;
+  size_t prof_used = 0;
 };
 
 namespace {
@@ -187,6 +192,27 @@ int fail(moe_ctx* c, int code, const std::string& m) {
   } while (0)
 
 hipStream_t as_stream(void* s) { return (hipStream_t)s; }
+
+// Opens a timed record for one launch of `stage` on stream s (-1 when off).
+int prof_open(moe_ctx* c, int stage, hipStream_t s) {
+  if (!c->prof_on || c->prof_used >= c->prof_stage.size()) return -1;
+  const int i = (int)c->prof_used++;
+  c->prof_stage[i] = stage;
+  if (hipEventRecord(c->prof_ev[2 * i], s) != hipSuccess) return -1;
+  return i;
+}
+
+void prof_close(moe_ctx* c, int i, hipStream_t s) {
+  if (i >= 0) (void)hipEventRecord(c->prof_ev[2 * i + 1], s);
+}
+
+// HIP launch `expr` on stream s, timed as `stage` when profiling is on.
+#define STAGE(ctx, stage, s, expr)                 \
+  do {                                             \
+    const int _pi = prof_open(ctx, stage, s);      \
+    HIPCHK(ctx, expr);                             \
+    prof_close(ctx, _pi, s);                       \
+  } while (0)
 
 int check_cfg(const moe_config* c) {
   if (!c) return fail(nullptr, MOE_E_INVAL, "null config");
@@ -216,30 +242,42 @@ int forward_experts(moe_ctx* c, const void* hidden, int T, const int32_t* slot_r
                     hipStream_t s) {
   const moe_config& g = c->cfg;
   HIPCHK(c, hipStreamWaitEvent(s, c->fill_evt, 0));
-  HIPCHK(c, moe_launch_group(c->ids, T, g.k, g.E, mask, slot_row, DEC_MB, c->counts, c->offsets, c->pos, c->perm_tok,
-                             c->hist, c->wl, c->err, s));
+  STAGE(c, MOE_STAGE_GROUP, s,
+        moe_launch_group(c->ids, T, g.k, g.E, mask, slot_row, DEC_MB, c->counts, c->offsets, c->pos, c->perm_tok,
+                         c->hist, c->wl, c->err, s));
   const int grid = grid_dec(c);
   const BlobLayout& b = c->bl;
   if (g.wfmt == MOE_W_BF16) {
-    HIPCHK(c, moe_launch_gemm_dec(g.wfmt, 1, grid, c->wl, c->counts, c->offsets, c->slot_pool, b.S, b.w[0], b.w[1], 0,
-                                  0, hidden, nullptr, c->perm_tok, g.H, g.I, c->A, s));
-    HIPCHK(c, moe_launch_gemm_dec(g.wfmt, 0, grid, c->wl, c->counts, c->offsets, c->slot_pool, b.S, b.w[2], 0, 0, 0,
-                                  c->A, nullptr, nullptr, g.I, g.H, c->Z, s));
+    STAGE(c, MOE_STAGE_GEMM1, s,
+          moe_launch_gemm_dec(g.wfmt, 1, grid, c->wl, c->counts, c->offsets, c->slot_pool, b.S, b.w[0], b.w[1], 0, 0,
+                              hidden, nullptr, c->perm_tok, g.H, g.I, c->A, s));
+    STAGE(c, MOE_STAGE_GEMM2, s,
+          moe_launch_gemm_dec(g.wfmt, 0, grid, c->wl, c->counts, c->offsets, c->slot_pool, b.S, b.w[2], 0, 0, 0, c->A,
+                              nullptr, nullptr, g.I, g.H, c->Z, s));
   } else {
-    HIPCHK(c, moe_launch_quant(g.wfmt, 1, hidden, T, nullptr, g.H, c->Xq, c->Xs, s));
-    HIPCHK(c, moe_launch_gemm_dec(g.wfmt, 1, grid, c->wl, c->counts, c->offsets, c->slot_pool, b.S, b.w[0], b.w[1],
-                                  b.s[0], b.s[1], c->Xq, c->Xs, c->perm_tok, g.H, g.I, c->A, s));
-    HIPCHK(c, moe_launch_quant(g.wfmt, 0, c->A, T * g.k, c->offsets + g.E, g.I, c->Aq, c->As, s));
-    HIPCHK(c, moe_launch_gemm_dec(g.wfmt, 0, grid, c->wl, c->counts, c->offsets, c->slot_pool, b.S, b.w[2], 0, b.s[2],
-                                  0, c->Aq, c->As, nullptr, g.I, g.H, c->Z, s));
+    STAGE(c, MOE_STAGE_QUANT_X, s, moe_launch_quant(g.wfmt, 1, hidden, T, nullptr, g.H, c->Xq, c->Xs, s));
+    STAGE(c, MOE_STAGE_GEMM1, s,
+          moe_launch_gemm_dec(g.wfmt, 1, grid, c->wl, c->counts, c->offsets, c->slot_pool, b.S, b.w[0], b.w[1],
+                              b.s[0], b.s[1], c->Xq, c->Xs, c->perm_tok, g.H, g.I, c->A, s));
+    STAGE(c, MOE_STAGE_QUANT_A, s,
+          moe_launch_quant(g.wfmt, 0, c->A, T * g.k, c->offsets + g.E, g.I, c->Aq, c->As, s));
+    STAGE(c, MOE_STAGE_GEMM2, s,
+          moe_launch_gemm_dec(g.wfmt, 0, grid, c->wl, c->counts, c->offsets, c->slot_pool, b.S, b.w[2], 0, b.s[2], 0,
+                              c->Aq, c->As, nullptr, g.I, g.H, c->Z, s));
   }
   return MOE_OK;
 }
 
 int route_only(moe_ctx* c, const void* hidden, const float* R, const float* bias, int T, hipStream_t s) {
   const moe_config& g = c->cfg;
-  HIPCHK(c, moe_launch_router((const uint16_t*)hidden, R, bias, T, g.E, g.H, c->logits, s));
-  HIPCHK(c, moe_launch_topk(c->logits, T, g.E, g.k, c->ids, c->w, s));
+  STAGE(c, MOE_STAGE_ROUTE, s, moe_launch_router((const uint16_t*)hidden, R, bias, T, g.E, g.H, c->logits, s));
+  STAGE(c, MOE_STAGE_TOPK, s, moe_launch_topk(c->logits, T, g.E, g.k, c->ids, c->w, s));
+  return MOE_OK;
+}
+
+int combine(moe_ctx* c, const uint32_t* mask, const int32_t* row, const float* hp, int T, void* out, hipStream_t s) {
+  STAGE(c, MOE_STAGE_COMBINE, s,
+        moe_launch_combine(c->Z, c->ids, c->w, c->pos, mask, row, hp, T, c->cfg.k, c->cfg.H, (uint16_t*)out, s));
   return MOE_OK;
 }
 
@@ -251,8 +289,9 @@ int check_T(moe_ctx* c, int T) {
 int plan_sync(moe_ctx* c, int layer, const int32_t* ids_dev, int T, uint32_t* mask_dev, int policy, hipStream_t s) {
   const moe_config& g = c->cfg;
   const uint32_t tick = ++c->tick;
-  HIPCHK(c, moe_launch_plan(ids_dev, T * g.k, layer, g.E, g.n_slots, c->slot_table, c->owner, c->last_use, tick,
-                            policy, c->BP, c->BH, mask_dev, c->plan_dev, s));
+  STAGE(c, MOE_STAGE_PLAN, s,
+        moe_launch_plan(ids_dev, T * g.k, layer, g.E, g.n_slots, c->slot_table, c->owner, c->last_use, tick, policy,
+                        c->BP, c->BH, mask_dev, c->plan_dev, s));
   HIPCHK(c, hipMemcpyAsync(c->plan_host, c->plan_dev, sizeof(PlanOut), hipMemcpyDeviceToHost, s));
   return MOE_OK;
 }
@@ -581,9 +620,7 @@ int moe_layer_forward(moe_ctx* c, int layer, const void* hidden, const float* R,
   if (rc) return rc;
   rc = forward_experts(c, hidden, T, slot_row, miss_mask, s);
   if (rc) return rc;
-  HIPCHK(c, moe_launch_combine(c->Z, c->ids, c->w, c->pos, miss_mask, slot_row, host_partial, T, c->cfg.k, c->cfg.H,
-                               (uint16_t*)out, s));
-  return MOE_OK;
+  return combine(c, miss_mask, slot_row, host_partial, T, out, s);
 }
 
 int moe_decode_layer(moe_ctx* c, int layer, const void* hidden, const float* R, const float* bias, int T, void* out,
@@ -632,8 +669,7 @@ int moe_decode_layer(moe_ctx* c, int layer, const void* hidden, const float* R, 
     HIPCHK(c, hipMemcpyAsync(c->hp, c->hp_host, (size_t)T * g.H * 4, hipMemcpyHostToDevice, s));
     hp = c->hp;
   }
-  HIPCHK(c, moe_launch_combine(c->Z, c->ids, c->w, c->pos, c->mask, row, hp, T, g.k, g.H, (uint16_t*)out, s));
-  return MOE_OK;
+  return combine(c, c->mask, row, hp, T, out, s);
 }
 
 int prefill_stream_layer(moe_ctx* c, int layer, const void* hidden, const float* R, const float* bias, int T,
@@ -680,7 +716,8 @@ int prefill_stream_layer(moe_ctx* c, int layer, const void* hidden, const float*
     const int32_t* row = c->slot_table + (size_t)layer * g.E;
     rc = forward_experts(c, hidden, T, row, nullptr, s);
     if (rc) return rc;
-    HIPCHK(c, moe_launch_combine(c->Z, c->ids, c->w, c->pos, nullptr, row, nullptr, T, g.k, g.H, (uint16_t*)out, s));
+    rc = combine(c, nullptr, row, nullptr, T, out, s);
+    if (rc) return rc;
   }
   HIPCHK(c, hipEventRecord(c->done[buf_of(layer)], s));
   if (!double_buffer && layer + 1 < g.L) {
@@ -754,6 +791,43 @@ int moe_check_device_error(moe_ctx* c) {
   HIPCHK(c, hipMemset(c->err, 0, sizeof(int)));
   HIPCHK(c, hipDeviceSynchronize());
   if (v) return fail(c, MOE_E_NOT_RESIDENT, "a routed expert was neither resident nor in the host miss set");
+  return MOE_OK;
+}
+
+int moe_profile_begin(moe_ctx* c, int max_launches) {
+  if (!c) return fail(nullptr, MOE_E_INVAL, "null ctx");
+  if (max_launches < 1 || max_launches > (1 << 20)) return fail(c, MOE_E_INVAL, "max_launches out of range");
+  for (hipEvent_t e : c->prof_ev) (void)hipEventDestroy(e);
+  c->prof_ev.assign(2 * (size_t)max_launches, nullptr);
+  for (auto& e : c->prof_ev) HIPCHK(c, hipEventCreate(&e));
+  c->prof_stage.assign(max_launches, -1);
+  c->prof_used = 0;
+  c->prof_on = true;
+  return MOE_OK;
+}
+
+int moe_profile_end(moe_ctx* c, moe_profile* out) {
+  if (!c) return fail(nullptr, MOE_E_INVAL, "null ctx");
+  if (!c->prof_on) return fail(c, MOE_E_INVAL, "profiling was not started");
+  c->prof_on = false;
+  HIPCHK(c, hipDeviceSynchronize());
+  moe_profile p;
+  std::memset(&p, 0, sizeof(p));
+  for (size_t i = 0; i < c->prof_used; ++i) {
+    float ms = 0.f;
+    HIPCHK(c, hipEventElapsedTime(&ms, c->prof_ev[2 * i], c->prof_ev[2 * i + 1]));
+    const int st = c->prof_stage[i];
+    if (st >= 0 && st < MOE_N_STAGES) {
+      p.launches[st] += 1;
+      p.ms[st] += ms;
+    }
+  }
+  p.dropped = c->prof_used >= c->prof_stage.size() ? 1 : 0;
+  for (hipEvent_t e : c->prof_ev) (void)hipEventDestroy(e);
+  c->prof_ev.clear();
+  c->prof_stage.clear();
+  c->prof_used = 0;
+  if (out) *out = p;
   return MOE_OK;
 }
 

@@ -15,7 +15,9 @@
 // router logits z[t,e] = sum_h x[t,h] R[e,h] + b[e]  (x bf16, R fp32, fp32 sums)
 // ---------------------------------------------------------------------------
 
-// Small batches: one wave per expert streams its row of R once; H % 256 == 0.
+// Small batches: one wave per (expert, 16 tokens); grid (E/4, T/16) so every
+// CU takes part; the expert's row of R is read from L2 by each token group.
+// H % 256 == 0.
 __global__ void __launch_bounds__(256)
 router_small_kernel(const uint16_t* __restrict__ x, const float* __restrict__ R,
                     const float* __restrict__ bias, int T, int E, int H, float* __restrict__ z) {
@@ -24,7 +26,8 @@ router_small_kernel(const uint16_t* __restrict__ x, const float* __restrict__ R,
   if (e >= E) return;
   const float* r = R + (size_t)e * H;
   const float b = bias ? bias[e] : 0.0f;
-  for (int t0 = 0; t0 < T; t0 += 16) {
+  {
+    const int t0 = blockIdx.y * 16;
     const int nt = min(16, T - t0);
     float acc[16];
 #pragma unroll
@@ -312,7 +315,7 @@ group_scatter_kernel(const int32_t* __restrict__ ids, int T, int k, int E, const
 extern "C" hipError_t moe_launch_router(const uint16_t* x, const float* R, const float* bias, int T, int E, int H,
                                         float* z, hipStream_t s) {
   if (T <= 64) {
-    router_small_kernel<<<(E + 3) / 4, 256, 0, s>>>(x, R, bias, T, E, H, z);
+    router_small_kernel<<<dim3((E + 3) / 4, (T + 15) / 16), 256, 0, s>>>(x, R, bias, T, E, H, z);
   } else {
     dim3 g((T + 63) / 64, (E + 63) / 64);
     router_tiled_kernel<<<g, 256, 0, s>>>(x, R, bias, T, E, H, z);

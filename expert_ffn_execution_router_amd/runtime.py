@@ -172,5 +172,15 @@ class MoeRuntime:
                                                 self.stream_ptr(copy_stream) if copy_stream is not None
                                                 else self.stream_ptr(stream), 1 if double_buffer else 0))
 
+    def profile_begin(self, max_launches=100000):
+        self._chk(B.moe_profile_begin(self.ctx, max_launches))
+
+    def profile_end(self):
+        p = B.moe_profile()
+        self._chk(B.moe_profile_end(self.ctx, ctypes.byref(p)))
+        d = p.as_dict()
+        d["dropped"] = p.dropped
+        return d
+
     def check_device_error(self):
         return B.moe_check_device_error(self.ctx)

@@ -223,6 +223,33 @@ int prefill_stream_layer(moe_ctx* ctx, int layer, const void* hidden, const floa
  * MOE_E_NOT_RESIDENT. */
 int moe_check_device_error(moe_ctx* ctx);
 
+/* Per-stage GPU timing (the pages time stages by wall clock only; this hook
+ * brackets each of the context's launches with HIP events on the stream the
+ * launch goes to).  Stages: */
+enum {
+  MOE_STAGE_ROUTE = 0,    /* router logits */
+  MOE_STAGE_TOPK = 1,     /* top-k and gate weights */
+  MOE_STAGE_GROUP = 2,    /* histogram, scan, permutation, work list */
+  MOE_STAGE_QUANT_X = 3,  /* activation quantisation before GEMM 1 (8-bit formats) */
+  MOE_STAGE_GEMM1 = 4,    /* grouped gate/up GEMM with SwiGLU */
+  MOE_STAGE_QUANT_A = 5,  /* quantisation of A before GEMM 2 (8-bit formats) */
+  MOE_STAGE_GEMM2 = 6,    /* grouped down GEMM */
+  MOE_STAGE_COMBINE = 7,  /* weighted unpermute-combine */
+  MOE_STAGE_PLAN = 8,     /* cache-control kernel */
+  MOE_N_STAGES = 9
+};
+
+typedef struct {
+  int launches[MOE_N_STAGES];  /* timed launches per stage */
+  double ms[MOE_N_STAGES];     /* summed event time per stage, ms */
+  int dropped;                 /* 1 if more than max_launches launches happened */
+} moe_profile;
+
+/* Starts timing up to max_launches launches (allocates 2*max_launches events). */
+int moe_profile_begin(moe_ctx* ctx, int max_launches);
+/* Synchronises the device, sums the records into out and stops timing. */
+int moe_profile_end(moe_ctx* ctx, moe_profile* out);
+
 #ifdef __cplusplus
 }
 #endif

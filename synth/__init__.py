@@ -124,6 +124,8 @@ def lib():
         L.synth_expert_blob.argtypes = [vp, ctypes.c_int, ctypes.c_int, ctypes.c_int, u64, vp, ctypes.c_float]
         L.synth_pool.argtypes = [vp, sz, ctypes.c_long, ctypes.c_long, ctypes.c_int, ctypes.c_int, ctypes.c_int,
                                  u64, vp, ctypes.c_float]
+        L.synth_keys.argtypes = [vp, sz, u64, u64]
+        L.synth_rows_bf16.argtypes = [vp, vp, sz, ctypes.c_int, vp, ctypes.c_float]
         _lib = L
     return _lib
 
@@ -221,18 +223,21 @@ def router_bias(cfg: MoeShape, seed: int, layer: int) -> np.ndarray | None:
 
 def hidden_rows(cfg: MoeShape, row_keys: np.ndarray) -> np.ndarray:
     """bf16 bit patterns [len(row_keys), H], one N(0,1) row per key."""
-    out = np.empty((len(row_keys), cfg.H), dtype=np.uint16)
-    t = normal_table()
-    for i, rk in enumerate(row_keys):
-        lib().synth_normal_bf16(out[i].ctypes.data, cfg.H, int(rk), _ptr(t), cfg.x_sigma)
+    keys = np.ascontiguousarray(row_keys, dtype=np.uint64).reshape(-1)
+    out = np.empty((len(keys), cfg.H), dtype=np.uint16)
+    lib().synth_rows_bf16(_ptr(out), _ptr(keys), len(keys), cfg.H, _ptr(normal_table()), cfg.x_sigma)
+    return out
+
+
+def keys_range(base: int, first: int, n: int) -> np.ndarray:
+    out = np.empty(n, dtype=np.uint64)
+    lib().synth_keys(_ptr(out), n, base, first)
     return out
 
 
 def hidden(cfg: MoeShape, seed: int, T: int, tag: int = 0) -> np.ndarray:
     """Fresh activations [T, H] as bf16 bit patterns."""
-    base = key(seed, cfg.config_id, _K_HIDDEN, tag)
-    keys = np.array([lib().synth_key(base, t) for t in range(T)], dtype=np.uint64)
-    return hidden_rows(cfg, keys)
+    return hidden_rows(cfg, keys_range(key(seed, cfg.config_id, _K_HIDDEN, tag), 0, T))
 
 
 def decode_row_keys(cfg: MoeShape, seed: int, steps: int, T: int, layers: int | None = None) -> np.ndarray:
@@ -246,12 +251,11 @@ def decode_row_keys(cfg: MoeShape, seed: int, steps: int, T: int, layers: int | 
     base = key(seed, cfg.config_id, _K_HIDDEN, 0xDEC0DE, T)
     reuse_base = key(seed, cfg.config_id, _K_REUSE, T)
     for s in range(steps):
-        u = uniform_f64(L * T, lib().synth_key(reuse_base, s)).reshape(L, T)
-        for l in range(L):
-            for t in range(T):
-                if s > 0 and u[l, t] < cfg.reuse_p:
-                    keys[s, l, t] = keys[s - 1, l, t]
-                else:
-                    keys[s, l, t] = lib().synth_key(base, (s * L + l) * 65536 + t)
+        fresh = keys_range(base, s * L * 65536, L * 65536).reshape(L, 65536)[:, :T]
+        if s == 0:
+            keys[s] = fresh
+        else:
+            u = uniform_f64(L * T, lib().synth_key(reuse_base, s)).reshape(L, T)
+            keys[s] = np.where(u < cfg.reuse_p, keys[s - 1], fresh)
     return keys
 

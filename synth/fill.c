@@ -97,6 +97,18 @@ void synth_normal_f32(float* out, size_t n, uint64_t key, const float* table, fl
   for (size_t i = 0; i < n; ++i) out[i] = table[uniform16(key, i)] * sigma;
 }
 
+/* keys[i] = synth_key(base, first + i). */
+void synth_keys(uint64_t* out, size_t n, uint64_t base, uint64_t first) {
+#pragma omp parallel for schedule(static)
+  for (long i = 0; i < (long)n; ++i) out[i] = synth_key(base, first + (uint64_t)i);
+}
+
+/* n rows of H bf16 values, row i drawn from stream keys[i]. */
+void synth_rows_bf16(uint16_t* out, const uint64_t* keys, size_t n, int H, const float* table, float sigma) {
+#pragma omp parallel for schedule(static)
+  for (long i = 0; i < (long)n; ++i) synth_normal_bf16(out + (size_t)i * H, (size_t)H, keys[i], table, sigma);
+}
+
 /* n uniforms in [0,1) with 53 bits. */
 void synth_uniform_f64(double* out, size_t n, uint64_t key) {
   for (size_t i = 0; i < n; ++i) out[i] = (double)(synth_word(key, i) >> 11) * (1.0 / 9007199254740992.0);
