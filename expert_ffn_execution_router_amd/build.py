@@ -15,7 +15,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
 
-HIP_SOURCES = ["route.hip", "gemm_dec.hip", "combine.hip", "slots.hip"]
+HIP_SOURCES = ["route.hip", "gemm_dec.hip", "gemm_pf.hip", "combine.hip", "slots.hip"]
 HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
              "-I" + CSRC, "-I" + os.path.join(ROOT, "include")]

@@ -28,6 +28,10 @@ hipError_t moe_launch_gemm_dec(int fmt, int gated, int grid, const WorkList* wl,
                                const int32_t* offsets, const uint8_t* pool, size_t S, size_t woff0, size_t woff1,
                                size_t soff0, size_t soff1, const void* X, const void* Xs, const int32_t* row_tok,
                                int K, int N, void* out, hipStream_t s);
+int moe_pf_tile_tokens();
+hipError_t moe_launch_gemm_pf(int fmt, int gated, int grid, const WorkList* wl, const int32_t* counts,
+                              const int32_t* offsets, const uint8_t* pool, size_t S, size_t woff0, size_t woff1,
+                              const void* X, const int32_t* row_tok, int K, int N, void* out, hipStream_t s);
 hipError_t moe_launch_combine(const uint16_t* Z, const int32_t* ids, const float* w, const int32_t* pos,
                               const uint32_t* miss_mask, const int32_t* slot_row, const float* hp, int T, int k,
                               int H, uint16_t* out, hipStream_t s);
@@ -242,12 +246,21 @@ int forward_experts(moe_ctx* c, const void* hidden, int T, const int32_t* slot_r
                     hipStream_t s) {
   const moe_config& g = c->cfg;
   HIPCHK(c, hipStreamWaitEvent(s, c->fill_evt, 0));
+  // many tokens per expert: LDS-tiled MFMA kernels; otherwise weight streaming
+  const bool tiled = g.wfmt == MOE_W_BF16 && T > 64 && (long)T * g.k >= 48L * g.E;
   STAGE(c, MOE_STAGE_GROUP, s,
-        moe_launch_group(c->ids, T, g.k, g.E, mask, slot_row, DEC_MB, c->counts, c->offsets, c->pos, c->perm_tok,
-                         c->hist, c->wl, c->err, s));
+        moe_launch_group(c->ids, T, g.k, g.E, mask, slot_row, tiled ? moe_pf_tile_tokens() : DEC_MB, c->counts,
+                         c->offsets, c->pos, c->perm_tok, c->hist, c->wl, c->err, s));
   const int grid = grid_dec(c);
   const BlobLayout& b = c->bl;
-  if (g.wfmt == MOE_W_BF16) {
+  if (tiled) {
+    STAGE(c, MOE_STAGE_GEMM1, s,
+          moe_launch_gemm_pf(g.wfmt, 1, c->n_cu, c->wl, c->counts, c->offsets, c->slot_pool, b.S, b.w[0], b.w[1],
+                             hidden, c->perm_tok, g.H, g.I, c->A, s));
+    STAGE(c, MOE_STAGE_GEMM2, s,
+          moe_launch_gemm_pf(g.wfmt, 0, c->n_cu, c->wl, c->counts, c->offsets, c->slot_pool, b.S, b.w[2], 0, c->A,
+                             nullptr, g.I, g.H, c->Z, s));
+  } else if (g.wfmt == MOE_W_BF16) {
     STAGE(c, MOE_STAGE_GEMM1, s,
           moe_launch_gemm_dec(g.wfmt, 1, grid, c->wl, c->counts, c->offsets, c->slot_pool, b.S, b.w[0], b.w[1], 0, 0,
                               hidden, nullptr, c->perm_tok, g.H, g.I, c->A, s));

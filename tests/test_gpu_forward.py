@@ -29,14 +29,14 @@ def _get(setups, name):
     if name not in setups:
         kw = dict(CASES[name])
         cfg = shape(kw.pop("base"), **kw)
-        s = Setup(cfg, seed=11, max_tokens=320)
+        s = Setup(cfg, seed=11, max_tokens=1024)
         s.admit_all(0)
         setups[name] = s
     return setups[name]
 
 
 @pytest.mark.parametrize("name", list(CASES))
-@pytest.mark.parametrize("T", [1, 16, 100, 300])
+@pytest.mark.parametrize("T", [1, 16, 100, 300, 1000])
 def test_forward_matches_oracle(setups, name, T):
     print(f"forward {name} T={T}", flush=True)
     s = _get(setups, name)
