@@ -50,11 +50,30 @@ def parse():
     ap.add_argument("--prefill-T", type=int, default=8192)
     ap.add_argument("--cpu-layers", type=int, default=3)
     ap.add_argument("--host-threads", type=int, default=16)
+    ap.add_argument("--copy-probe", action="store_true",
+                    help="only copy 1 GiB device->device 3 times (calibrates HBM byte counters)")
     return ap.parse_args()
+
+
+def copy_probe():
+    """A plain copy kernel of known size, for scaling FETCH_SIZE / WRITE_SIZE."""
+    import torch
+    n = 1 << 30
+    a = torch.ones(n, dtype=torch.uint8, device="cuda")
+    b = torch.empty_like(a)
+    torch.cuda.synchronize()
+    for _ in range(3):
+        t0 = time.perf_counter()
+        b.copy_(a)
+        torch.cuda.synchronize()
+        log(f"copy {n} bytes: {2 * n / (time.perf_counter() - t0) / 1e9:.0f} GB/s (read+write)")
 
 
 def main():
     args = parse()
+    if args.copy_probe:
+        copy_probe()
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the path has no multi-GPU mode",
               file=sys.stderr)

@@ -24,7 +24,7 @@ hipError_t moe_launch_topk(const float* z, int T, int E, int k, int32_t* ids, fl
 hipError_t moe_launch_group(const int32_t* ids, int T, int k, int E, const uint32_t* miss_mask,
                             const int32_t* slot_row, int mb, int32_t* counts, int32_t* offsets, int32_t* pos,
                             int32_t* perm_tok, int32_t* hist, WorkList* wl, int* err, hipStream_t s);
-hipError_t moe_launch_gemm_dec(int fmt, int gated, int grid, const WorkList* wl, const int32_t* counts,
+hipError_t moe_launch_gemm_dec(int fmt, int gated, int split, int n_cu, const WorkList* wl, const int32_t* counts,
                                const int32_t* offsets, const uint8_t* pool, size_t S, size_t woff0, size_t woff1,
                                size_t soff0, size_t soff1, const void* X, const void* Xs, const int32_t* row_tok,
                                int K, int N, void* out, hipStream_t s);
@@ -238,7 +238,6 @@ int nthreads_of(const moe_config& c) {
 
 HostFfnShape host_shape(const moe_config& c, size_t S) { return HostFfnShape{c.wfmt, c.E, c.k, c.H, c.I, S}; }
 
-int grid_dec(const moe_ctx* c) { return c->n_cu * 4; }
 
 // Grouping, quantisation and both grouped GEMMs for a routed batch (ids/w in
 // the workspace).  slot_row: this layer's device row of the residency table.
@@ -251,7 +250,9 @@ int forward_experts(moe_ctx* c, const void* hidden, int T, const int32_t* slot_r
   STAGE(c, MOE_STAGE_GROUP, s,
         moe_launch_group(c->ids, T, g.k, g.E, mask, slot_row, tiled ? moe_pf_tile_tokens() : DEC_MB, c->counts,
                          c->offsets, c->pos, c->perm_tok, c->hist, c->wl, c->err, s));
-  const int grid = grid_dec(c);
+  // waves sharing one 16-row tile's K: more when few experts are active
+  const int sp1 = T <= 8 ? 4 : 2, sp2 = T <= 8 ? 4 : 1;
+  const int ncu = c->n_cu;
   const BlobLayout& b = c->bl;
   if (tiled) {
     STAGE(c, MOE_STAGE_GEMM1, s,
@@ -262,21 +263,21 @@ int forward_experts(moe_ctx* c, const void* hidden, int T, const int32_t* slot_r
                              nullptr, g.I, g.H, c->Z, s));
   } else if (g.wfmt == MOE_W_BF16) {
     STAGE(c, MOE_STAGE_GEMM1, s,
-          moe_launch_gemm_dec(g.wfmt, 1, grid, c->wl, c->counts, c->offsets, c->slot_pool, b.S, b.w[0], b.w[1], 0, 0,
-                              hidden, nullptr, c->perm_tok, g.H, g.I, c->A, s));
+          moe_launch_gemm_dec(g.wfmt, 1, sp1, ncu, c->wl, c->counts, c->offsets, c->slot_pool, b.S, b.w[0], b.w[1],
+                              0, 0, hidden, nullptr, c->perm_tok, g.H, g.I, c->A, s));
     STAGE(c, MOE_STAGE_GEMM2, s,
-          moe_launch_gemm_dec(g.wfmt, 0, grid, c->wl, c->counts, c->offsets, c->slot_pool, b.S, b.w[2], 0, 0, 0, c->A,
-                              nullptr, nullptr, g.I, g.H, c->Z, s));
+          moe_launch_gemm_dec(g.wfmt, 0, sp2, ncu, c->wl, c->counts, c->offsets, c->slot_pool, b.S, b.w[2], 0, 0, 0,
+                              c->A, nullptr, nullptr, g.I, g.H, c->Z, s));
   } else {
     STAGE(c, MOE_STAGE_QUANT_X, s, moe_launch_quant(g.wfmt, 1, hidden, T, nullptr, g.H, c->Xq, c->Xs, s));
     STAGE(c, MOE_STAGE_GEMM1, s,
-          moe_launch_gemm_dec(g.wfmt, 1, grid, c->wl, c->counts, c->offsets, c->slot_pool, b.S, b.w[0], b.w[1],
+          moe_launch_gemm_dec(g.wfmt, 1, sp1, ncu, c->wl, c->counts, c->offsets, c->slot_pool, b.S, b.w[0], b.w[1],
                               b.s[0], b.s[1], c->Xq, c->Xs, c->perm_tok, g.H, g.I, c->A, s));
     STAGE(c, MOE_STAGE_QUANT_A, s,
           moe_launch_quant(g.wfmt, 0, c->A, T * g.k, c->offsets + g.E, g.I, c->Aq, c->As, s));
     STAGE(c, MOE_STAGE_GEMM2, s,
-          moe_launch_gemm_dec(g.wfmt, 0, grid, c->wl, c->counts, c->offsets, c->slot_pool, b.S, b.w[2], 0, b.s[2], 0,
-                              c->Aq, c->As, nullptr, g.I, g.H, c->Z, s));
+          moe_launch_gemm_dec(g.wfmt, 0, sp2, ncu, c->wl, c->counts, c->offsets, c->slot_pool, b.S, b.w[2], 0, b.s[2],
+                              0, c->Aq, c->As, nullptr, g.I, g.H, c->Z, s));
   }
   return MOE_OK;
 }

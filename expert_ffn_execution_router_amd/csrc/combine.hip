@@ -24,17 +24,32 @@ combine_kernel(const uint16_t* __restrict__ Z, const int32_t* __restrict__ ids, 
   float acc[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) acc[i] = 0.0f;
-  for (int j = 0; j < k; ++j) {
-    const int e = ids[(size_t)t * k + j];
-    if (miss_mask && ((miss_mask[e >> 5] >> (e & 31)) & 1u)) continue;   // computed by the host
-    if (slot_row[e] < 0) continue;                                        // not resident: error flagged
-    const float wj = w[(size_t)t * k + j];
-    const i32x4_t zv = ld16(Z + (size_t)pos[(size_t)t * k + j] * H + h);
+  // all loads unconditional (choices past k repeat choice k-1 and are not
+  // used); excluded choices are dropped with a select, never multiplied,
+  // because their Z rows were not written
+  int p[8];
+  bool use[8];
+  float wj[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    const size_t a = (size_t)t * k + min(j, k - 1);
+    const int e = ids[a];
+    const bool host = miss_mask && ((miss_mask[e >> 5] >> (e & 31)) & 1u);   // computed by the host
+    use[j] = j < k && !host && slot_row[e] >= 0;                            // not resident: error flagged
+    p[j] = pos[a];
+    wj[j] = w[a];
+  }
+  i32x4_t zv[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) zv[j] = ld16(Z + (size_t)p[j] * H + h);
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const uint32_t u = (uint32_t)zv[i];
-      acc[2 * i] += wj * bf16_bits_to_f32(u & 0xffffu);
-      acc[2 * i + 1] += wj * bf16_bits_to_f32(u >> 16);
+      const uint32_t u = (uint32_t)zv[j][i];
+      const float lo = wj[j] * bf16_bits_to_f32(u & 0xffffu), hi = wj[j] * bf16_bits_to_f32(u >> 16);
+      acc[2 * i] += use[j] ? lo : 0.0f;
+      acc[2 * i + 1] += use[j] ? hi : 0.0f;
     }
   }
   if (hp) {

@@ -32,17 +32,22 @@ router_small_kernel(const uint16_t* __restrict__ x, const float* __restrict__ R,
     float acc[16];
 #pragma unroll
     for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
+    // loads are unconditional (rows past T re-read row T-1 and are not stored)
+    // so the compiler can keep every load of an iteration in flight at once
+    const uint16_t* xr[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) xr[i] = x + (size_t)min(t0 + i, T - 1) * H;
     for (int h = lane * 4; h < H; h += 256) {
       const float4 rv = *(const float4*)(r + h);
+      uint2 xv[16];
+#pragma unroll
+      for (int i = 0; i < 16; ++i) xv[i] = *(const uint2*)(xr[i] + h);
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        if (i < nt) {
-          const uint2 xv = *(const uint2*)(x + (size_t)(t0 + i) * H + h);
-          acc[i] += bf16_bits_to_f32(xv.x & 0xffffu) * rv.x;
-          acc[i] += bf16_bits_to_f32(xv.x >> 16) * rv.y;
-          acc[i] += bf16_bits_to_f32(xv.y & 0xffffu) * rv.z;
-          acc[i] += bf16_bits_to_f32(xv.y >> 16) * rv.w;
-        }
+        acc[i] += bf16_bits_to_f32(xv[i].x & 0xffffu) * rv.x;
+        acc[i] += bf16_bits_to_f32(xv[i].x >> 16) * rv.y;
+        acc[i] += bf16_bits_to_f32(xv[i].y & 0xffffu) * rv.z;
+        acc[i] += bf16_bits_to_f32(xv[i].y >> 16) * rv.w;
       }
     }
 #pragma unroll
@@ -113,7 +118,7 @@ topk_kernel(const float* __restrict__ z, int T, int E, int k, int32_t* __restric
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int e = lane + 64 * i;
-    v[i] = e < E ? zr[e] : 0.0f;
+    v[i] = zr[min(e, E - 1)];          // unconditional load; entries past E are marked taken
     taken[i] = e >= E;
   }
   float selv[8];
@@ -212,7 +217,9 @@ __device__ void finish_grouping(int cnt, int E, const uint32_t* miss_mask, const
   int nmblk;
   const int pb = block_exclusive_scan256(nb, tmp, &nmblk);
   if (act) { wl->act_e[a] = e; wl->act_slot[a] = slot; wl->mblk_prefix[a] = pb; }
-  if (e == 0) { wl->n_act = nact; wl->n_mblk = nmblk; wl->mb = mb; wl->mblk_prefix[nact] = nmblk; }
+  if (e == 0) {
+    wl->n_act = nact; wl->n_mblk = nmblk; wl->mb = mb; wl->mblk_prefix[nact] = nmblk;
+  }
 }
 
 // Stable scatter of one block of tokens given per-expert bases for the block.
