@@ -55,6 +55,27 @@ def parse():
     return ap.parse_args()
 
 
+def counted_traffic(kernel: str):
+    """HBM bytes per launch of `kernel` from the committed rocprofv3 counter
+    summary, or None when the kernel source changed since it was taken."""
+    import hashlib
+    root = os.path.dirname(os.path.abspath(__file__))
+    path = os.path.join(root, "profiles", "decode_T64_bf16_gemm_hbm_counters.md")
+    src = os.path.join(root, "expert_ffn_execution_router_amd", "csrc", "gemm_dec.hip")
+    if not os.path.exists(path):
+        return None
+    vals = {}
+    for line in open(path):
+        if "=" in line and line[0] not in "|#`":
+            k, v = line.strip().split("=", 1)
+            vals[k] = v
+    cur = hashlib.sha256(open(src, "rb").read()).hexdigest()[:16]
+    if vals.get("source_sha256_16[gemm_dec.hip]") != cur:
+        return None
+    v = vals.get(f"traffic_bytes[{kernel}]")
+    return None if v is None else float(v)
+
+
 def copy_probe():
     """A plain copy kernel of known size, for scaling FETCH_SIZE / WRITE_SIZE."""
     import torch
@@ -159,7 +180,9 @@ def main():
     result["roofline"] = {
         "bound": "hbm", "kernel": "gemm_dec_bf16 (grouped gate/up + SwiGLU)",
         "achieved": g1_achieved / 1e9, "peak": HBM_PEAK / 1e9, "unit": "GB/s",
-        "frac": g1_achieved / HBM_PEAK, "traffic": None,
+        "frac": g1_achieved / HBM_PEAK,
+        "traffic": counted_traffic("void gemm_dec<0, true, 2>") if T > 8 else None,
+        "traffic_unit": "HBM bytes per launch (rocprofv3 FETCH_SIZE+WRITE_SIZE, copy-calibrated)",
         "bytes_per_launch": float(g1_bytes / n_calls), "avg_launch_us": g1_ms * 1e3,
     }
     result["decode_resident"] = {
