@@ -58,50 +58,65 @@ router_small_kernel(const uint16_t* __restrict__ x, const float* __restrict__ R,
   }
 }
 
-// Large batches: 64 tokens x 64 experts per workgroup, K staged through LDS.
+// Large batches on fp32 MFMA: 64 tokens x 64 experts per workgroup, each wave
+// 16 tokens x 64 experts with v_mfma_f32_16x16x4f32 (x widened exactly from
+// bf16; R fp32; fp32 accumulation).  K is staged through LDS in chunks of 64
+// with rows padded to 65 floats so the 16 rows an MFMA operand read touches
+// fall in different banks.
 __global__ void __launch_bounds__(256)
-router_tiled_kernel(const uint16_t* __restrict__ x, const float* __restrict__ R,
-                    const float* __restrict__ bias, int T, int E, int H, float* __restrict__ z) {
-  __shared__ float xs[32][65];
-  __shared__ float rs[32][65];
+router_mfma_kernel(const uint16_t* __restrict__ x, const float* __restrict__ R, const float* __restrict__ bias,
+                   int T, int E, int H, float* __restrict__ z) {
+  __shared__ float xs[64][65];
+  __shared__ float rs[64][65];
   const int t0 = blockIdx.x * 64, e0 = blockIdx.y * 64;
-  const int tid = threadIdx.x, tx = tid & 15, ty = tid >> 4;
-  float acc[4][4];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int lr = lane & 15, lg = lane >> 4;
+  f32x4_t acc[4];
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
+  for (int n = 0; n < 4; ++n) acc[n] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  // staging: thread loads 16 bf16 of one token row and 16 floats of one expert row
+  const int sr = tid >> 2, sc = (tid & 3) * 16;
+  const uint16_t* xrow = x + (size_t)min(t0 + sr, T - 1) * H + sc;
+  const float* rrow = R + (size_t)min(e0 + sr, E - 1) * H + sc;
+  for (int k0 = 0; k0 < H; k0 += 64) {
+    const i32x4_t xa = ld16(xrow + k0), xb = ld16(xrow + k0 + 8);
+    i32x4_t rv[4];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) acc[i][j] = 0.0f;
-  for (int k0 = 0; k0 < H; k0 += 32) {
-    for (int i = tid; i < 64 * 32; i += 256) {
-      const int tt = i >> 5, kk = i & 31;
-      const int t = t0 + tt, e = e0 + tt;
-      xs[kk][tt] = t < T ? bf16_bits_to_f32(x[(size_t)t * H + k0 + kk]) : 0.0f;
-      rs[kk][tt] = e < E ? R[(size_t)e * H + k0 + kk] : 0.0f;
+    for (int q = 0; q < 4; ++q) rv[q] = ld16(rrow + k0 + q * 4);
+    __syncthreads();                     // previous chunk's reads are done
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t a = (uint32_t)xa[q], b = (uint32_t)xb[q];
+      xs[sr][sc + 2 * q] = bf16_bits_to_f32(a & 0xffffu);
+      xs[sr][sc + 2 * q + 1] = bf16_bits_to_f32(a >> 16);
+      xs[sr][sc + 8 + 2 * q] = bf16_bits_to_f32(b & 0xffffu);
+      xs[sr][sc + 8 + 2 * q + 1] = bf16_bits_to_f32(b >> 16);
+#pragma unroll
+      for (int u = 0; u < 4; ++u) rs[sr][sc + 4 * q + u] = __int_as_float(rv[q][u]);
     }
     __syncthreads();
-#pragma unroll 8
-    for (int kk = 0; kk < 32; ++kk) {
-      float a[4], b[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) { a[i] = xs[kk][ty * 4 + i]; b[i] = rs[kk][tx * 4 + i]; }
+    for (int ks = 0; ks < 16; ++ks) {
+      const float av = xs[wave * 16 + lr][ks * 4 + lg];
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) acc[i][j] += a[i] * b[j];
+      for (int n = 0; n < 4; ++n)
+        acc[n] = __builtin_amdgcn_mfma_f32_16x16x4f32(av, rs[n * 16 + lr][ks * 4 + lg], acc[n], 0, 0, 0);
     }
-    __syncthreads();
   }
+  // lane holds expert column lr of tile n, tokens 4*lg..4*lg+3 of the wave's 16
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int t = t0 + ty * 4 + i;
-    if (t >= T) continue;
+  for (int n = 0; n < 4; ++n) {
+    const int e = e0 + n * 16 + lr;
+    if (e >= E) continue;
+    const float b = bias ? bias[e] : 0.0f;
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const int e = e0 + tx * 4 + j;
-      if (e < E) z[(size_t)t * E + e] = acc[i][j] + (bias ? bias[e] : 0.0f);
+    for (int i = 0; i < 4; ++i) {
+      const int t = t0 + wave * 16 + lg * 4 + i;
+      if (t < T) z[(size_t)t * E + e] = acc[n][i] + b;
     }
   }
 }
+
 
 // ---------------------------------------------------------------------------
 // top-k (one wave per token, E <= 256) and renormalised weights
@@ -325,7 +340,7 @@ extern "C" hipError_t moe_launch_router(const uint16_t* x, const float* R, const
     router_small_kernel<<<dim3((E + 3) / 4, (T + 15) / 16), 256, 0, s>>>(x, R, bias, T, E, H, z);
   } else {
     dim3 g((T + 63) / 64, (E + 63) / 64);
-    router_tiled_kernel<<<g, 256, 0, s>>>(x, R, bias, T, E, H, z);
+    router_mfma_kernel<<<g, 256, 0, s>>>(x, R, bias, T, E, H, z);
   }
   return hipGetLastError();
 }
