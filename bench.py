@@ -56,6 +56,7 @@ def parse():
     ap.add_argument("--prefill-runs", type=int, default=2, help="double-buffered chunks timed (best is kept)")
     ap.add_argument("--cpu-layers", type=int, default=3)
     ap.add_argument("--host-threads", type=int, default=16)
+    ap.add_argument("--eager", action="store_true", help="time eager launches instead of one graph per step")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only copy 1 GiB device->device 3 times (calibrates HBM byte counters)")
     a = ap.parse_args()
@@ -163,25 +164,59 @@ def phase_decode(w: Workload):
     for s in range(W):
         step(s)
     torch.cuda.synchronize()
+    # per-stage breakdown: one eager pass over the timed steps with every stage timed (not the value)
     rt.profile_begin(K * L * 8 + 16)
+    for s in range(K):
+        step(W + s)
+    prof_all = rt.profile_end()
+    # eager timed pass: GEMM 1 bracketed by HIP events on its stream (the
+    # roofline's kernel duration); events inside a captured graph cannot be timed
+    rt.profile_begin(K * L + 16, stages=["gemm1"])
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(K):
         step(W + s)
     torch.cuda.synchronize()
-    elapsed = time.perf_counter() - t0
+    elapsed_eager = time.perf_counter() - t0
     prof = rt.profile_end()
+    # graph timed pass (the value): one HIP graph per step (48 layers of
+    # launches), as the pages replay a captured decode step
+    use_graph = not args.eager
+    graphs = []
+    if use_graph:
+        try:
+            cap = torch.cuda.Stream()
+            for s in range(K):
+                g = torch.cuda.CUDAGraph()
+                with torch.cuda.graph(g, stream=cap):
+                    step(W + s)
+                graphs.append(g)
+        except Exception as ex:       # capture unavailable: the eager pass is the value
+            log(f"graph capture failed ({ex}); the value is the eager pass")
+            use_graph = False
+    torch.cuda.synchronize()
+    elapsed = elapsed_eager
+    if use_graph:
+        graphs[0].replay()            # first replay uploads the graph
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        for s in range(K):
+            graphs[s].replay()
+        torch.cuda.synchronize()
+        elapsed = time.perf_counter() - t0
     assert rt.check_device_error() == 0
     value = K * L * T / elapsed
-    log(f"decode resident: {elapsed / K * 1e3:.3f} ms/step, {value:.0f} MoE-layer tokens/s")
+    log(f"decode resident: eager {elapsed_eager / K * 1e3:.3f} ms/step, "
+        f"{'graph' if use_graph else 'eager'} {elapsed / K * 1e3:.3f} ms/step, {value:.0f} MoE-layer tokens/s")
     # algorithmic bytes (each active expert's weights read once; routed rows and outputs once)
     tk = T * k
     g1_bytes = (n_active * 2 * I * H * 2 + tk * H * 2 + tk * I * 2).sum()
     g2_bytes = (n_active * H * I * 2 + tk * I * 2 + tk * H * 2).sum()
     layer_bytes = (n_active * S + E * H * 4 + 2 * T * H * 2).sum()
     n_calls = K * L
-    stage_ms = {n: v["ms"] / v["launches"] for n, v in prof.items() if isinstance(v, dict) and v["launches"]}
-    g1_ms, g2_ms = stage_ms["gemm1"], stage_ms["gemm2"]
+    stage_ms = {n: v["ms"] / v["launches"] for n, v in prof_all.items() if isinstance(v, dict) and v["launches"]}
+    g1_ms = prof["gemm1"]["ms"] / max(prof["gemm1"]["launches"], 1)   # inside the timed region
+    g2_ms = stage_ms["gemm2"]
     gpu_layer_ms = sum(stage_ms.values())
     g1_achieved = g1_bytes / n_calls / (g1_ms * 1e-3)
     roofline = {
@@ -193,6 +228,9 @@ def phase_decode(w: Workload):
         "bytes_per_launch": float(g1_bytes / n_calls), "avg_launch_us": g1_ms * 1e3,
     }
     detail = {
+        "launch": "hip graph per step" if use_graph else "eager",
+        "eager_ms_per_step": elapsed_eager / K * 1e3,
+        "gemm1_launches_timed": prof["gemm1"]["launches"],
         "ms_per_step": elapsed / K * 1e3, "layer_wall_us": elapsed / n_calls * 1e6,
         "stage_us": {n: v * 1e3 for n, v in stage_ms.items()},
         "gpu_layer_us": gpu_layer_ms * 1e3,

@@ -81,7 +81,7 @@ SIGNATURES = {
     "moe_decode_layer": (_i, [_vp, _i, _vp, _vp, _vp, _i, _vp, _P(moe_plan_info), _vp, _vp]),
     "prefill_stream_layer": (_i, [_vp, _i, _vp, _vp, _vp, _i, _vp, _vp, _vp, _i]),
     "moe_check_device_error": (_i, [_vp]),
-    "moe_profile_begin": (_i, [_vp, _i]),
+    "moe_profile_begin": (_i, [_vp, _i, ctypes.c_uint]),
     "moe_profile_end": (_i, [_vp, _P(moe_profile)]),
 }
 

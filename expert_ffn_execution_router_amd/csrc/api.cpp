@@ -175,6 +175,8 @@ struct moe_ctx {
   std::string err_msg;
   // optional per-stage timing (moe_profile_begin / moe_profile_end)
   bool prof_on = false;
+  unsigned prof_mask = 0;               // stages timed (bit per MOE_STAGE_*)
+  bool fills_pending = false;           // fill_evt recorded since the last wait on it
   std::vector<hipEvent_t> prof_ev;      // 2 per record
   std::vector<int> prof_stage;
   size_t prof_used = 0;
@@ -199,7 +201,7 @@ hipStream_t as_stream(void* s) { return (hipStream_t)s; }
 
 // Opens a timed record for one launch of `stage` on stream s (-1 when off).
 int prof_open(moe_ctx* c, int stage, hipStream_t s) {
-  if (!c->prof_on || c->prof_used >= c->prof_stage.size()) return -1;
+  if (!c->prof_on || !((c->prof_mask >> stage) & 1u) || c->prof_used >= c->prof_stage.size()) return -1;
   const int i = (int)c->prof_used++;
   c->prof_stage[i] = stage;
   if (hipEventRecord(c->prof_ev[2 * i], s) != hipSuccess) return -1;
@@ -244,7 +246,10 @@ HostFfnShape host_shape(const moe_config& c, size_t S) { return HostFfnShape{c.w
 int forward_experts(moe_ctx* c, const void* hidden, int T, const int32_t* slot_row, const uint32_t* mask,
                     hipStream_t s) {
   const moe_config& g = c->cfg;
-  HIPCHK(c, hipStreamWaitEvent(s, c->fill_evt, 0));
+  if (c->fills_pending) {                 // weights copied by slot_pool_* / the decode plan
+    HIPCHK(c, hipStreamWaitEvent(s, c->fill_evt, 0));
+    c->fills_pending = false;
+  }
   // many tokens per expert: LDS-tiled MFMA kernels; otherwise weight streaming
   const bool tiled = g.wfmt == MOE_W_BF16 && T > 64 && (long)T * g.k >= 48L * g.E;
   STAGE(c, MOE_STAGE_GROUP, s,
@@ -333,6 +338,7 @@ int issue_fills(moe_ctx* c, int layer, const int* experts, const int* slots, int
                              copy));
   }
   HIPCHK(c, hipEventRecord(c->fill_evt, copy));
+  c->fills_pending = true;
   return MOE_OK;
 }
 
@@ -808,9 +814,10 @@ int moe_check_device_error(moe_ctx* c) {
   return MOE_OK;
 }
 
-int moe_profile_begin(moe_ctx* c, int max_launches) {
+int moe_profile_begin(moe_ctx* c, int max_launches, unsigned stage_mask) {
   if (!c) return fail(nullptr, MOE_E_INVAL, "null ctx");
   if (max_launches < 1 || max_launches > (1 << 20)) return fail(c, MOE_E_INVAL, "max_launches out of range");
+  c->prof_mask = stage_mask;
   for (hipEvent_t e : c->prof_ev) (void)hipEventDestroy(e);
   c->prof_ev.assign(2 * (size_t)max_launches, nullptr);
   for (auto& e : c->prof_ev) HIPCHK(c, hipEventCreate(&e));

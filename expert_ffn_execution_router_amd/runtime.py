@@ -172,8 +172,13 @@ class MoeRuntime:
                                                 self.stream_ptr(copy_stream) if copy_stream is not None
                                                 else self.stream_ptr(stream), 1 if double_buffer else 0))
 
-    def profile_begin(self, max_launches=100000):
-        self._chk(B.moe_profile_begin(self.ctx, max_launches))
+    def profile_begin(self, max_launches=100000, stages=None):
+        """Time launches of the named stages (all when None)."""
+        mask = 0
+        for i, name in enumerate(B.STAGES):
+            if stages is None or name in stages:
+                mask |= 1 << i
+        self._chk(B.moe_profile_begin(self.ctx, max_launches, mask))
 
     def profile_end(self):
         p = B.moe_profile()

@@ -245,8 +245,11 @@ typedef struct {
   int dropped;                 /* 1 if more than max_launches launches happened */
 } moe_profile;
 
-/* Starts timing up to max_launches launches (allocates 2*max_launches events). */
-int moe_profile_begin(moe_ctx* ctx, int max_launches);
+/* Starts timing up to max_launches launches of the stages whose bit is set in
+ * stage_mask (bit MOE_STAGE_x; allocates 2*max_launches events).  Event
+ * records issued while a stream is being captured become graph nodes and
+ * time each replay. */
+int moe_profile_begin(moe_ctx* ctx, int max_launches, unsigned stage_mask);
 /* Synchronises the device, sums the records into out and stops timing. */
 int moe_profile_end(moe_ctx* ctx, moe_profile* out);
 
