@@ -24,10 +24,12 @@ hipError_t moe_launch_topk(const float* z, int T, int E, int k, int32_t* ids, fl
 hipError_t moe_launch_group(const int32_t* ids, int T, int k, int E, const uint32_t* miss_mask,
                             const int32_t* slot_row, int mb, int32_t* counts, int32_t* offsets, int32_t* pos,
                             int32_t* perm_tok, int32_t* hist, WorkList* wl, int* err, hipStream_t s);
-hipError_t moe_launch_gemm_dec(int fmt, int gated, int split, int n_cu, const WorkList* wl, const int32_t* counts,
+hipError_t moe_launch_gemm_dec(int fmt, int gated, int ns, int n_cu, const WorkList* wl, const int32_t* counts,
                                const int32_t* offsets, const uint8_t* pool, size_t S, size_t woff0, size_t woff1,
                                size_t soff0, size_t soff1, const void* X, const void* Xs, const int32_t* row_tok,
-                               int K, int N, void* out, hipStream_t s);
+                               int K, int N, void* out, void* part, hipStream_t s);
+size_t moe_dec_part_bytes();
+int moe_dec_max_ns(int fmt);
 int moe_pf_tile_tokens();
 hipError_t moe_launch_gemm_pf(int fmt, int gated, int grid, const WorkList* wl, const int32_t* counts,
                               const int32_t* offsets, const uint8_t* pool, size_t S, size_t woff0, size_t woff1,
@@ -35,8 +37,8 @@ hipError_t moe_launch_gemm_pf(int fmt, int gated, int grid, const WorkList* wl, 
 hipError_t moe_launch_combine(const uint16_t* Z, const int32_t* ids, const float* w, const int32_t* pos,
                               const uint32_t* miss_mask, const int32_t* slot_row, const float* hp, int T, int k,
                               int H, uint16_t* out, hipStream_t s);
-hipError_t moe_launch_quant(int fmt, int src_bf16, const void* src, int rows, const int32_t* nrows_dev, int cols,
-                            uint8_t* q, void* scale, hipStream_t s);
+hipError_t moe_launch_quant(int fmt, int src_bf16, const void* src, int rows, const int32_t* nrows_dev,
+                            const int32_t* row_map, int cols, uint8_t* q, void* scale, hipStream_t s);
 hipError_t moe_launch_plan(const int32_t* ids, int n_assign, int layer, int E, int n_slots, int32_t* slot_table,
                            int32_t* owner, uint32_t* last_use, uint32_t tick, int policy, double BP, double BH,
                            uint32_t* miss_mask, void* plan, hipStream_t s);
@@ -83,7 +85,7 @@ BlobLayout blob_layout(const moe_config& c) {
 // Workspace carving (all offsets 256-byte aligned).
 struct WsLayout {
   size_t slot_table, owner, last_use, err, logits, ids, w, pos, perm_tok, counts, offsets, hist, wl, mask, plan, A,
-      Aq, As, Z, Xq, Xs, hp, total;
+      Aq, As, Z, Xq, Xs, hp, part, total;
 };
 
 WsLayout ws_layout(const moe_config& c) {
@@ -116,9 +118,12 @@ WsLayout ws_layout(const moe_config& c) {
   L.Aq = take(q8 ? R * c.I : 0);
   L.As = take(c.wfmt == MOE_W_FP8_E4M3_B128 ? R * (c.I / 128) * 4 : (q8 ? R * (c.I / 32) : 0));
   L.Z = take(R * c.H * 2);
-  L.Xq = take(q8 ? Tm * c.H : 0);
-  L.Xs = take(c.wfmt == MOE_W_FP8_E4M3_B128 ? Tm * (c.H / 128) * 4 : (q8 ? Tm * (c.H / 32) : 0));
+  // quantised activations in grouped order (one row per routed pair)
+  L.Xq = take(q8 ? R * c.H : 0);
+  L.Xs = take(c.wfmt == MOE_W_FP8_E4M3_B128 ? R * (c.H / 128) * 4 : (q8 ? R * (c.H / 32) : 0));
   L.hp = take(Tm * c.H * 4);
+  // small-batch GEMM: partial tiles of items cut between workgroups
+  L.part = take(moe_dec_part_bytes());
   L.total = o;
   return L;
 }
@@ -157,6 +162,7 @@ struct moe_ctx {
   uint8_t* Xq;
   void* Xs;
   float* hp;
+  void* part;
   // pinned host staging
   PlanOut* plan_host = nullptr;
   uint16_t* hidden_host = nullptr;
@@ -229,6 +235,10 @@ int check_cfg(const moe_config* c) {
   if (c->wfmt < 0 || c->wfmt > 2) return fail(nullptr, MOE_E_INVAL, "unknown weight format");
   if (c->n_slots < 0 || c->n_slots > 8192) return fail(nullptr, MOE_E_UNSUPPORTED, "n_slots must be in [0, 8192]");
   if (c->max_tokens < 1) return fail(nullptr, MOE_E_INVAL, "max_tokens must be >= 1");
+  // the small-batch GEMM numbers its (item, K-chunk) units with 32-bit ints
+  const double units = ((double)c->max_tokens * c->k / 16 + 1 + c->E) * (std::max(c->H, c->I) / 64) *
+                       (std::max(c->H, c->I) / 128);
+  if (units >= 2147483647.0) return fail(nullptr, MOE_E_UNSUPPORTED, "max_tokens * k too large for one call");
   return MOE_OK;
 }
 
@@ -252,11 +262,12 @@ int forward_experts(moe_ctx* c, const void* hidden, int T, const int32_t* slot_r
   }
   // many tokens per expert: LDS-tiled MFMA kernels; otherwise weight streaming
   const bool tiled = g.wfmt == MOE_W_BF16 && T > 64 && (long)T * g.k >= 48L * g.E;
+  // weight streaming: m-blocks of 16 * ns tokens (each m-block reads the
+  // expert's weights once; larger blocks cost LDS and idle MFMA rows)
+  const int ns = std::min(T <= 16 ? 1 : (T <= 64 ? 2 : 4), moe_dec_max_ns(g.wfmt));
   STAGE(c, MOE_STAGE_GROUP, s,
-        moe_launch_group(c->ids, T, g.k, g.E, mask, slot_row, tiled ? moe_pf_tile_tokens() : DEC_MB, c->counts,
+        moe_launch_group(c->ids, T, g.k, g.E, mask, slot_row, tiled ? moe_pf_tile_tokens() : 16 * ns, c->counts,
                          c->offsets, c->pos, c->perm_tok, c->hist, c->wl, c->err, s));
-  // waves sharing one 16-row tile's K: more when few experts are active
-  const int sp1 = T <= 8 ? 4 : 2, sp2 = T <= 8 ? 4 : 1;
   const int ncu = c->n_cu;
   const BlobLayout& b = c->bl;
   if (tiled) {
@@ -268,21 +279,23 @@ int forward_experts(moe_ctx* c, const void* hidden, int T, const int32_t* slot_r
                              nullptr, g.I, g.H, c->Z, s));
   } else if (g.wfmt == MOE_W_BF16) {
     STAGE(c, MOE_STAGE_GEMM1, s,
-          moe_launch_gemm_dec(g.wfmt, 1, sp1, ncu, c->wl, c->counts, c->offsets, c->slot_pool, b.S, b.w[0], b.w[1],
-                              0, 0, hidden, nullptr, c->perm_tok, g.H, g.I, c->A, s));
+          moe_launch_gemm_dec(g.wfmt, 1, ns, ncu, c->wl, c->counts, c->offsets, c->slot_pool, b.S, b.w[0], b.w[1],
+                              0, 0, hidden, nullptr, c->perm_tok, g.H, g.I, c->A, c->part, s));
     STAGE(c, MOE_STAGE_GEMM2, s,
-          moe_launch_gemm_dec(g.wfmt, 0, sp2, ncu, c->wl, c->counts, c->offsets, c->slot_pool, b.S, b.w[2], 0, 0, 0,
-                              c->A, nullptr, nullptr, g.I, g.H, c->Z, s));
+          moe_launch_gemm_dec(g.wfmt, 0, ns, ncu, c->wl, c->counts, c->offsets, c->slot_pool, b.S, b.w[2], 0, 0, 0,
+                              c->A, nullptr, nullptr, g.I, g.H, c->Z, c->part, s));
   } else {
-    STAGE(c, MOE_STAGE_QUANT_X, s, moe_launch_quant(g.wfmt, 1, hidden, T, nullptr, g.H, c->Xq, c->Xs, s));
+    // activations quantised straight into grouped order (row p <- token perm_tok[p])
+    STAGE(c, MOE_STAGE_QUANT_X, s,
+          moe_launch_quant(g.wfmt, 1, hidden, T * g.k, c->offsets + g.E, c->perm_tok, g.H, c->Xq, c->Xs, s));
     STAGE(c, MOE_STAGE_GEMM1, s,
-          moe_launch_gemm_dec(g.wfmt, 1, sp1, ncu, c->wl, c->counts, c->offsets, c->slot_pool, b.S, b.w[0], b.w[1],
-                              b.s[0], b.s[1], c->Xq, c->Xs, c->perm_tok, g.H, g.I, c->A, s));
+          moe_launch_gemm_dec(g.wfmt, 1, ns, ncu, c->wl, c->counts, c->offsets, c->slot_pool, b.S, b.w[0], b.w[1],
+                              b.s[0], b.s[1], c->Xq, c->Xs, nullptr, g.H, g.I, c->A, c->part, s));
     STAGE(c, MOE_STAGE_QUANT_A, s,
-          moe_launch_quant(g.wfmt, 0, c->A, T * g.k, c->offsets + g.E, g.I, c->Aq, c->As, s));
+          moe_launch_quant(g.wfmt, 0, c->A, T * g.k, c->offsets + g.E, nullptr, g.I, c->Aq, c->As, s));
     STAGE(c, MOE_STAGE_GEMM2, s,
-          moe_launch_gemm_dec(g.wfmt, 0, sp2, ncu, c->wl, c->counts, c->offsets, c->slot_pool, b.S, b.w[2], 0, b.s[2],
-                              0, c->Aq, c->As, nullptr, g.I, g.H, c->Z, s));
+          moe_launch_gemm_dec(g.wfmt, 0, ns, ncu, c->wl, c->counts, c->offsets, c->slot_pool, b.S, b.w[2], 0, b.s[2],
+                              0, c->Aq, c->As, nullptr, g.I, g.H, c->Z, c->part, s));
   }
   return MOE_OK;
 }
@@ -425,6 +438,7 @@ int moe_create(const moe_config* cfg, void* host_pool, size_t host_bytes, void* 
   c->Xq = w + L.Xq;
   c->Xs = w + L.Xs;
   c->hp = (float*)(w + L.hp);
+  c->part = w + L.part;
   const size_t Tm = cfg->max_tokens;
   const size_t R = Tm * cfg->k;
   void* p;

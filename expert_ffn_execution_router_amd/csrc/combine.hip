@@ -72,18 +72,20 @@ DEV float load_src(const void* src, size_t i) {
 }
 
 // One wave per (row, 128-column group); rows from *nrows_dev when given.
+// Output row r quantises source row row_map[r] (r itself without a map).
 template <bool SRC_BF16>
 __global__ void __launch_bounds__(256)
-quant_fp8_kernel(const void* __restrict__ src, int rows, const int32_t* __restrict__ nrows_dev, int cols,
-                 uint8_t* __restrict__ q, float* __restrict__ scale) {
+quant_fp8_kernel(const void* __restrict__ src, int rows, const int32_t* __restrict__ nrows_dev,
+                 const int32_t* __restrict__ row_map, int cols, uint8_t* __restrict__ q, float* __restrict__ scale) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int ng = cols / 128;
   const int g = blockIdx.x * 4 + wave;
   const int nrows = nrows_dev ? *nrows_dev : rows;
   const int r = g / ng, c0 = (g - r * ng) * 128;
   if (r >= nrows) return;
+  const size_t sbase = (size_t)(row_map ? row_map[r] : r) * cols + c0 + lane * 2;
   const size_t base = (size_t)r * cols + c0 + lane * 2;
-  const float v0 = load_src<SRC_BF16>(src, base), v1 = load_src<SRC_BF16>(src, base + 1);
+  const float v0 = load_src<SRC_BF16>(src, sbase), v1 = load_src<SRC_BF16>(src, sbase + 1);
   const float amax = wave_max(fmaxf(fabsf(v0), fabsf(v1)));
   const float inv = amax > 0.0f ? 448.0f / amax : 1.0f;
   const float sc = amax > 0.0f ? amax / 448.0f : 1.0f;
@@ -95,8 +97,9 @@ quant_fp8_kernel(const void* __restrict__ src, int rows, const int32_t* __restri
 // One wave per (row, 64 columns) = two 32-column MX blocks (lanes 0-31, 32-63).
 template <bool SRC_BF16>
 __global__ void __launch_bounds__(256)
-quant_mxfp8_kernel(const void* __restrict__ src, int rows, const int32_t* __restrict__ nrows_dev, int cols,
-                   uint8_t* __restrict__ q, uint8_t* __restrict__ scale) {
+quant_mxfp8_kernel(const void* __restrict__ src, int rows, const int32_t* __restrict__ nrows_dev,
+                   const int32_t* __restrict__ row_map, int cols, uint8_t* __restrict__ q,
+                   uint8_t* __restrict__ scale) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int ng = cols / 64;
   const int g = blockIdx.x * 4 + wave;
@@ -104,7 +107,7 @@ quant_mxfp8_kernel(const void* __restrict__ src, int rows, const int32_t* __rest
   const int r = g / ng, c0 = (g - r * ng) * 64;
   if (r >= nrows) return;
   const size_t i = (size_t)r * cols + c0 + lane;
-  const float v = load_src<SRC_BF16>(src, i);
+  const float v = load_src<SRC_BF16>(src, (size_t)(row_map ? row_map[r] : r) * cols + c0 + lane);
   float amax = fabsf(v);
 #pragma unroll
   for (int off = 16; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
@@ -128,20 +131,20 @@ extern "C" hipError_t moe_launch_combine(const uint16_t* Z, const int32_t* ids, 
 }
 
 extern "C" hipError_t moe_launch_quant(int fmt, int src_bf16, const void* src, int rows, const int32_t* nrows_dev,
-                                       int cols, uint8_t* q, void* scale, hipStream_t s) {
+                                       const int32_t* row_map, int cols, uint8_t* q, void* scale, hipStream_t s) {
   if (rows == 0) return hipSuccess;
   if (fmt == WFMT_FP8) {
     const int groups = rows * (cols / 128);
     if (src_bf16)
-      quant_fp8_kernel<true><<<(groups + 3) / 4, 256, 0, s>>>(src, rows, nrows_dev, cols, q, (float*)scale);
+      quant_fp8_kernel<true><<<(groups + 3) / 4, 256, 0, s>>>(src, rows, nrows_dev, row_map, cols, q, (float*)scale);
     else
-      quant_fp8_kernel<false><<<(groups + 3) / 4, 256, 0, s>>>(src, rows, nrows_dev, cols, q, (float*)scale);
+      quant_fp8_kernel<false><<<(groups + 3) / 4, 256, 0, s>>>(src, rows, nrows_dev, row_map, cols, q, (float*)scale);
   } else {
     const int groups = rows * (cols / 64);
     if (src_bf16)
-      quant_mxfp8_kernel<true><<<(groups + 3) / 4, 256, 0, s>>>(src, rows, nrows_dev, cols, q, (uint8_t*)scale);
+      quant_mxfp8_kernel<true><<<(groups + 3) / 4, 256, 0, s>>>(src, rows, nrows_dev, row_map, cols, q, (uint8_t*)scale);
     else
-      quant_mxfp8_kernel<false><<<(groups + 3) / 4, 256, 0, s>>>(src, rows, nrows_dev, cols, q, (uint8_t*)scale);
+      quant_mxfp8_kernel<false><<<(groups + 3) / 4, 256, 0, s>>>(src, rows, nrows_dev, row_map, cols, q, (uint8_t*)scale);
   }
   return hipGetLastError();
 }

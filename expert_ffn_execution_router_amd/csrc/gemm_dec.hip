@@ -9,179 +9,197 @@
 //   GEMM 2: Z = A W_down^T                    (fp32 accumulate)
 //
 // Small batches are bound by HBM: every weight byte of an active expert is
-// read once.  A work item is (expert, m-block of <= 64 tokens, 16*4/SPLIT
-// weight rows).  Each 16-row tile is streamed by SPLIT waves that split K
-// (chunks of 128 taken round-robin); weights go straight from HBM into MFMA
-// operand registers (each weight byte is used by one wave, so no LDS), the
-// next chunk's weights are in flight while the current chunk is multiplied,
-// and the SPLIT partial sums are added through LDS in a fixed wave order so
-// the result does not depend on scheduling.  The grid holds exactly the
-// resident workgroups and strides over the device work list, so no host
-// synchronisation is needed and no workgroup starts late.
+// read once, so the kernel is a weight stream with MFMAs riding on it.
 //
-// MFMA operand mapping (v_mfma_f32_16x16x32_bf16): lane l feeds row l%16 of
-// A (16 weight rows) and column l%16 of B (16 tokens), with the 8 K values of
-// lane group l/16.  Because a contraction is invariant under a common
-// permutation of K, lane group g takes the 32 consecutive K values
-// [chunk + 32g, chunk + 32g + 32) spread over four MFMAs (8 per MFMA): each
-// lane then reads 64 contiguous bytes of its weight row per 128-K chunk.
-// Result lane l holds rows 4*(l/16)..+3 (weight rows) of column l%16 (token).
+// Work.  An item is (expert, m-block of 16*NS tokens, 64 weight rows per
+// matrix); its K range is cut into chunks of 256 bytes per weight row (128
+// bf16, 256 fp8 or 512 E2M1 values).  The flat sequence of (item, chunk)
+// units is split into equal contiguous ranges, one per workgroup, so every
+// workgroup streams the same number of bytes whatever the expert sizes; the
+// ranges of consecutive workgroups of one XCD are contiguous.  An item cut by
+// a range boundary leaves fp32 partial tiles, one per workgroup that holds
+// part of it; a second small kernel adds them in workgroup order and applies
+// the epilogue, so the sum is deterministic for a given set of GPU experts
+// and no workgroup waits for another (cross-XCD visibility inside one kernel
+// would need an L2 write-back and invalidate per handoff, which costs more
+// than the launch).
 //
-// fp8 (E4M3, 128x128 fp32 block scales): v_mfma_scale_f32_16x16x128_f8f6f4
-// with unit E8M0 scales; one instruction covers one 128-K block, whose
-// partial sum is multiplied by w_scale[block] * x_scale[token, block].
-// MXFP4: the same instruction with E2M1 weights (A) and MXFP8 activations
-// (B).  Lane layout of that instruction (measured on gfx950 with one-hot
-// inputs): an E2M1 operand's lane group g = l/16 holds the 32 consecutive K
-// values [32g, 32g+32) in its low 16 bytes; an 8-bit operand's lane group g
-// holds K [16g, 16g+16) in bytes 0-15 and K [64+16g, 64+16g+16) in bytes
-// 16-31; the E8M0 scale of lane group g covers K block [32g, 32g+32) of
-// that lane's row (A) or column (B).  With uniform scales (the fp8 path)
-// the 8-bit layout only has to agree between A and B, so both take 32
-// consecutive bytes there.
+// Memory.  Each chunk goes from HBM into a ring of three LDS stages by
+// direct global->LDS loads (lane l's 16 bytes land at the instruction's LDS
+// base + 16*l) with the nontemporal hint: 16 consecutive lanes cover one
+// 256-byte row segment, the pattern that streams HBM at 7.0-7.3 TB/s on
+// MI355X (weights are read once and must not displace reused lines).  The
+// 16-byte pieces of a row are XOR-swizzled by the row index so the MFMA
+// operand reads of 16 rows hit distinct banks; the loads pick their source
+// piece so the swizzle comes out of the lane-linear placement.  The token
+// rows of the chunk, the scales of the 8-bit formats and the weight scales
+// go through the same ring, so one counter wait per chunk covers everything
+// the chunk needs: chunk c+2 is requested while chunk c is multiplied.
+//
+// MFMA.  Wave w owns weight rows 16w..16w+15 of the item (of each matrix);
+// weights are the A operand (16 rows) and tokens the B operand (16 tokens per
+// sub-tile).  Result lane l holds weight rows 4*(l/16)..+3 of token l%16.
+//  * bf16: v_mfma_f32_16x16x32_bf16; lane group g of MFMA q takes the K
+//    values [32q + 8g, 32q + 8g + 8) of the chunk, i.e. 16-byte piece 4q+g.
+//  * fp8 (E4M3, fp32 scale per 128x128 weight block, per token per 128-K
+//    activation group): v_mfma_scale_f32_16x16x128_f8f6f4 with unit E8M0
+//    scales per 128-K half of the chunk, its partial sum multiplied by
+//    w_scale * x_scale.  With uniform scales only the agreement of the A and
+//    B byte layouts matters, so lane group g takes 32 consecutive bytes.
+//  * MXFP4: the same instruction with E2M1 weights (A) and MXFP8 activations
+//    (B) and their E8M0 block scales.  Lane layout of that instruction
+//    (measured on gfx950 with one-hot inputs): an E2M1 operand's lane group
+//    g holds the 32 K values [32g, 32g+32) in its low 16 bytes; an 8-bit
+//    operand's lane group g holds K [16g, 16g+16) in bytes 0-15 and
+//    K [64+16g, 64+16g+16) in bytes 16-31; the E8M0 scale of lane group g
+//    covers K block [32g, 32g+32) of that lane's row (A) or column (B).
 #include "common.h"
 
 namespace {
 
-constexpr int NWAVE = 4;
+constexpr int NW = 4;                 // waves per workgroup
+constexpr int ROWS = 16 * NW;         // weight rows per item and matrix
+constexpr int NST = 3;                // ring stages
+constexpr int N_XCD = 8;
+constexpr int MAX_BLOCKS = 1024;      // capacity of the partial-tile buffer (workgroups)
+constexpr int CACHE_NT = 2;           // cache-policy bits of a nontemporal load (gfx94x/gfx950)
 
-// Gathered row of X for token sub-tile ms, lane column c: returns the source
-// row index or -1.
-DEV int src_row(const int32_t* row_tok, int row0, int nrows, int ms, int c) {
-  const int r = ms * 16 + c;
-  if (r >= nrows) return -1;
-  return row_tok ? row_tok[row0 + r] : row0 + r;
+template <int FMT, bool GATED, int NS>
+struct Cfg {
+  static constexpr int NMAT = GATED ? 2 : 1;
+  static constexpr int CK = FMT == WFMT_BF16 ? 128 : (FMT == WFMT_FP8 ? 256 : 512);   // K per chunk
+  static constexpr int XB = FMT == WFMT_MXFP4 ? 512 : 256;   // token bytes per chunk
+  static constexpr int MB = 16 * NS;                          // tokens per m-block
+  static constexpr int NXI = MB * XB / 1024 / NW;             // token loads per wave per chunk
+  static constexpr int W_OFF = 0;
+  static constexpr int X_OFF = NMAT * NW * 4096;
+  static constexpr int XS_OFF = X_OFF + MB * XB;
+  static constexpr int XS_BYTES = FMT == WFMT_BF16 ? 0 : NW * 256;
+  static constexpr int WS_OFF = XS_OFF + XS_BYTES;
+  static constexpr int WS_BYTES = FMT == WFMT_BF16 ? 0 : (FMT == WFMT_FP8 ? NW * 256 : NMAT * NW * 256);
+  static constexpr int STAGE = WS_OFF + WS_BYTES;
+  // loads per wave per chunk: weights, tokens, token scales, weight scales
+  static constexpr int NI = 4 * NMAT + NXI + (FMT == WFMT_BF16 ? 0 : 1) +
+                            (FMT == WFMT_BF16 ? 0 : (FMT == WFMT_FP8 ? 1 : NMAT));
+  static constexpr int NACC = NMAT * NS;
+  static_assert(NXI >= 1 && NXI * NW * 1024 == MB * XB, "token chunk must split evenly over the waves");
+  static_assert(FMT != WFMT_FP8 || 2 * MB <= NW * 64, "fp8 token scales: one dword per lane");
+  static_assert(FMT != WFMT_MXFP4 || 4 * MB <= NW * 64, "MX token scales: one dword per lane");
+};
+
+// weights: read once, streamed with the nontemporal hint
+DEV void dma16_nt(const void* src, lds_u8_t* dst) {
+  __builtin_amdgcn_global_load_lds((gbl_void_t*)src, (lds_void_t*)dst, 16, 0, CACHE_NT);
 }
+// token rows: re-read by every tile of the expert, kept in the caches
+DEV void dma16(const void* src, lds_u8_t* dst) {
+  __builtin_amdgcn_global_load_lds((gbl_void_t*)src, (lds_void_t*)dst, 16, 0, 0);
+}
+DEV void dma4(const void* src, lds_u8_t* dst) {
+  __builtin_amdgcn_global_load_lds((gbl_void_t*)src, (lds_void_t*)dst, 4, 0, 0);
+}
+
+DEV int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
 
 DEV float silu_mul(float g, float u) { return g / (1.0f + expf(-g)) * u; }
 
-DEV i32x8_t cat(i32x4_t lo, i32x4_t hi) { return i32x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]}; }
+DEV i32x4_t lds16(const uint8_t* p) { return *(const i32x4_t*)p; }
 
-// Per-format pieces: what one lane loads for one 128-K chunk of one weight
-// row, what it loads for one token row, and the MFMA(s) that combine them.
-struct Bf16 {
-  struct W { i32x4_t v[4]; };
-  struct X { i32x4_t v[4]; };
-  // row pointer at the weight row; kb = chunk K offset (elements)
-  static DEV void load_w(W& w, const uint8_t* row, size_t, int kb, int lg) {
-    const uint16_t* p = (const uint16_t*)row + kb + lg * 32;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) w.v[s] = ld16(p + s * 8);
-  }
-  static DEV void load_x(X& x, const void* base, const void*, int row, int K, int kb, int, int lg) {
-    const uint16_t* p = (const uint16_t*)base + (size_t)row * K + kb + lg * 32;
-#pragma unroll
-    for (int s = 0; s < 4; ++s) x.v[s] = ld16(p + s * 8);
-  }
-  static DEV void zero_x(X& x) {
-#pragma unroll
-    for (int s = 0; s < 4; ++s) x.v[s] = i32x4_t{0, 0, 0, 0};
-  }
-  static DEV void mma(f32x4_t& acc, const W& w, const X& x, float) {
-#pragma unroll
-    for (int s = 0; s < 4; ++s)
-      acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, w.v[s]),
-                                                    __builtin_bit_cast(bf16x8_t, x.v[s]), acc, 0, 0, 0);
-  }
+struct Item {
+  int slot, row0, nrows, n0;
 };
 
-struct Fp8 {
-  struct W { i32x8_t v; float s; };
-  struct X { i32x8_t v; float s; };
-  // scale row pointer is passed as `srow` (fp32 [N/128][K/128], row block of the tile)
-  static DEV void load_w(W& w, const uint8_t* row, size_t, int kb, int lg) {
-    const uint8_t* p = row + kb + lg * 32;
-    w.v = cat(ld16(p), ld16(p + 16));
-  }
-  static DEV void load_x(X& x, const void* base, const void* sbase, int row, int K, int kb, int c, int lg) {
-    const uint8_t* p = (const uint8_t*)base + (size_t)row * K + kb + lg * 32;
-    x.v = cat(ld16(p), ld16(p + 16));
-    x.s = ((const float*)sbase)[(size_t)row * (K / 128) + c];
-  }
-  static DEV void zero_x(X& x) {
-    x.v = i32x8_t{0, 0, 0, 0, 0, 0, 0, 0};
-    x.s = 0.0f;
-  }
-  static DEV void mma(f32x4_t& acc, const W& w, const X& x, float ws) {
-    const f32x4_t z4 = {0.f, 0.f, 0.f, 0.f};
-    const f32x4_t p = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(w.v, x.v, z4, 0, 0, 0, 127, 0, 127);
-    const float f = ws * x.s;
+// First unit of workgroup b when U units are split over G workgroups.
+DEV long range_start(long b, long U, long G) { return b * U / G; }
+// Workgroup whose range holds unit u (G <= U, so every range is non-empty).
+DEV long owner_of(long u, long U, long G) {
+  long b = ((u + 1) * G - 1) / U;
+  return b < G - 1 ? b : G - 1;
+}
+
+// Partial tile of workgroup bb for item i (its first item: slot 0, else 1),
+// [NW waves][NACC][64 lanes] f32x4.
+template <int NACC>
+DEV f32x4_t* part_tile(f32x4_t* part, long bb, int i, long U, long G, int KC, int wave) {
+  const int slot = (range_start(bb, U, G) / KC == i) ? 0 : 1;
+  return part + (((size_t)bb * 2 + slot) * NW + wave) * NACC * 64;
+}
+
+// Output values of one wave's accumulators of an item (SwiGLU for GEMM 1):
+// lane holds weight rows 4*lg..+3 (output columns) of token lr of each
+// 16-token sub-tile; gate in acc[ms], up in acc[NS + ms].
+template <bool GATED, int NS>
+DEV void activate(const f32x4_t* acc, f32x4_t* val) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) acc[i] += p[i] * f;
+  for (int ms = 0; ms < NS; ++ms) {
+    if (GATED) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) val[ms][i] = silu_mul(acc[ms][i], acc[NS + ms][i]);
+    } else {
+      val[ms] = acc[ms];
+    }
   }
-};
+}
 
-struct Mxfp4 {
-  struct W { i32x4_t v; int s; };
-  struct X { i32x8_t v; int s; };
-  static DEV void load_w(W& w, const uint8_t* row, size_t, int kb, int lg) { w.v = ld16(row + kb / 2 + lg * 16); }
-  static DEV void load_x(X& x, const void* base, const void* sbase, int row, int K, int kb, int c, int lg) {
-    // 8-bit operand: bytes 0-15 = K [16g, 16g+16), bytes 16-31 = K [64+16g, 64+16g+16)
-    const uint8_t* p = (const uint8_t*)base + (size_t)row * K + kb + lg * 16;
-    x.v = cat(ld16(p), ld16(p + 64));
-    x.s = ((const uint8_t*)sbase)[(size_t)row * (K / 32) + c * 4 + lg];
+// Store the output values (fp32 for GEMM 1 of the 8-bit formats, else bf16).
+template <int FMT, bool GATED, int NS>
+DEV void store_out(const f32x4_t* val, const Item& it, int wave, int lane, int N, void* out) {
+  const int lr = lane & 15, lg = lane >> 4;
+  const int col = it.n0 + 16 * wave + 4 * lg;
+#pragma unroll
+  for (int ms = 0; ms < NS; ++ms) {
+    const int t = ms * 16 + lr;
+    if (t >= it.nrows) continue;
+    const size_t o = (size_t)(it.row0 + t) * N + col;
+    if (GATED && FMT != WFMT_BF16) {
+      *(f32x4_t*)((float*)out + o) = val[ms];
+    } else {
+      uint2 pk;
+      pk.x = pack_bf16x2(val[ms][0], val[ms][1]);
+      pk.y = pack_bf16x2(val[ms][2], val[ms][3]);
+      st8((uint16_t*)out + o, pk);
+    }
   }
-  static DEV void zero_x(X& x) {
-    x.v = i32x8_t{0, 0, 0, 0, 0, 0, 0, 0};
-    x.s = 127;
-  }
-  static DEV void mma(f32x4_t& acc, const W& w, const X& x, float) {
-    const i32x8_t a = i32x8_t{w.v[0], w.v[1], w.v[2], w.v[3], 0, 0, 0, 0};
-    acc = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, x.v, acc, 4, 0, 0, w.s, 0, x.s);
-  }
-};
+}
 
-// Weight-side scale of chunk c for the lane's row.
-template <class F>
-DEV void load_wscale(typename F::W& w, const uint8_t* srow, int c, int lg);
-template <>
-DEV void load_wscale<Bf16>(Bf16::W&, const uint8_t*, int, int) {}
-template <>
-DEV void load_wscale<Fp8>(Fp8::W& w, const uint8_t* srow, int c, int) { w.s = ((const float*)srow)[c]; }
-template <>
-DEV void load_wscale<Mxfp4>(Mxfp4::W& w, const uint8_t* srow, int c, int lg) { w.s = srow[c * 4 + lg]; }
-
-template <class F>
-DEV float wscale(const typename F::W& w);
-template <>
-DEV float wscale<Bf16>(const Bf16::W&) { return 1.0f; }
-template <>
-DEV float wscale<Fp8>(const Fp8::W& w) { return w.s; }
-template <>
-DEV float wscale<Mxfp4>(const Mxfp4::W&) { return 1.0f; }
+// Item i of the work list (m-block p = i / ntiles, 64-row tile i % ntiles),
+// read from global memory.
+DEV void decode_global(const WorkList* wl, const int32_t* counts, const int32_t* offsets, int ntiles, int MB, int i,
+                       Item& it) {
+  const int p = i / ntiles, nt = i - p * ntiles;
+  const int a = find_active(wl, p);
+  const int e = wl->act_e[a];
+  const int mb = p - wl->mblk_prefix[a];
+  it.slot = wl->act_slot[a];
+  it.row0 = offsets[e] + mb * MB;
+  it.nrows = min(MB, counts[e] - mb * MB);
+  it.n0 = nt * ROWS;
+}
 
 }  // namespace
 
 // FMT: WFMT_*.  GATED: GEMM 1 (gate rows at woff0, up rows at woff1, SwiGLU
 // epilogue; out = A, bf16 for WFMT_BF16 else fp32 for the quantisation pass).
-// Otherwise GEMM 2 (weights at woff0; out = Z bf16).  X rows are gathered
-// through row_tok (GEMM 1) or taken in grouped order (GEMM 2); Xs holds the
-// activation scales of the 8-bit formats.  soff0/soff1: weight scale arrays.
-template <int FMT, bool GATED, int SPLIT>
-__global__ void __launch_bounds__(256)
+// Otherwise GEMM 2 (weights at woff0; out = Z bf16).  Token rows of X are
+// gathered through row_tok (bf16 GEMM 1) or taken in grouped order; Xs holds
+// the activation scales of the 8-bit formats; soff0/soff1 the weight scales.
+// part: partial tiles [MAX_BLOCKS][2][NW][NACC][64] of the items cut by a
+// range boundary, finished by gemm_dec_fix.
+template <int FMT, bool GATED, int NS>
+__global__ void __launch_bounds__(256, 1)
 gemm_dec(const WorkList* __restrict__ wl, const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
          const uint8_t* __restrict__ pool, size_t S, size_t woff0, size_t woff1, size_t soff0, size_t soff1,
-         const void* __restrict__ X, const void* __restrict__ Xs, const int32_t* __restrict__ row_tok, int K, int N,
-         void* __restrict__ out) {
-  using F = typename std::conditional<FMT == WFMT_BF16, Bf16,
-                                      typename std::conditional<FMT == WFMT_FP8, Fp8, Mxfp4>::type>::type;
-  constexpr int TILES = NWAVE / SPLIT;          // 16-row tiles per work item
-  constexpr int NACC = GATED ? 8 : 4;
-  __shared__ float red[(SPLIT > 1 ? (SPLIT - 1) * TILES : 1) * NACC * 4 * 64];
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int lr = lane & 15, lg = lane >> 4;
-  const int tw = wave / SPLIT, ks = wave - tw * SPLIT;
-  const int rows_item = 16 * TILES;
-  const int ntiles = N / rows_item;
-  const int nitems = wl->n_mblk * ntiles;
-  const int nchunk = K / 128;
-  // bytes per weight row and per scale row of one matrix
-  const size_t wrow_bytes = FMT == WFMT_BF16 ? (size_t)K * 2 : (FMT == WFMT_FP8 ? (size_t)K : (size_t)K / 2);
-  const int last = nchunk - 1 - ((nchunk - 1 - ks) % SPLIT);   // this wave's last chunk (if ks < nchunk)
-
-  // the work list in LDS: an item's expert is then found without a chain of
-  // dependent global loads in front of its first weight load
+         const uint8_t* __restrict__ X, const uint8_t* __restrict__ Xs, const int32_t* __restrict__ row_tok, int K,
+         int N, void* __restrict__ out, f32x4_t* __restrict__ part) {
+  using C = Cfg<FMT, GATED, NS>;
+  extern __shared__ __align__(16) uint8_t ring[];
   __shared__ int l_pref[257], l_slot[256], l_row0[256], l_cnt[256];
+  // token row of each grouped row this workgroup touches (bf16 GEMM 1)
+  constexpr int ROWTAB = (FMT == WFMT_BF16 && GATED) ? 2048 : 1;
+  __shared__ int l_rows[ROWTAB];
+  const int wave = uni(threadIdx.x >> 6), lane = threadIdx.x & 63;
+  const int lr = lane & 15, lg = lane >> 4;
+
   const int n_act = wl->n_act;
   for (int i = threadIdx.x; i <= n_act; i += blockDim.x) {
     l_pref[i] = wl->mblk_prefix[i];
@@ -194,168 +212,452 @@ gemm_dec(const WorkList* __restrict__ wl, const int32_t* __restrict__ counts, co
   }
   __syncthreads();
 
-  for (int it = blockIdx.x; it < nitems; it += gridDim.x) {
-    const int p = it / ntiles, nt = it - p * ntiles;
-    int a = 0;
-    {
-      int hi = n_act - 1;
-      while (a < hi) {
-        const int mid = (a + hi + 1) >> 1;
-        if (l_pref[mid] <= p) a = mid; else hi = mid - 1;
+  const int ntiles = N / ROWS;
+  const int KC = (K + C::CK - 1) / C::CK;
+  const long U = (long)wl->n_mblk * ntiles * KC;     // < 2^31 for any admissible shape (checked by the host)
+  if (U == 0) return;
+  const long G = U < (long)gridDim.x ? U : (long)gridDim.x;
+  long b = blockIdx.x;
+  if (G == gridDim.x && (gridDim.x % N_XCD) == 0)       // XCD x takes ranges x*G/8 .. (x+1)*G/8 - 1
+    b = (long)(blockIdx.x % N_XCD) * (gridDim.x / N_XCD) + blockIdx.x / N_XCD;
+  if (b >= G) return;
+  const long u0 = range_start(b, U, G), u1 = range_start(b + 1, U, G);
+
+  // bytes of one weight row and of one token row
+  const int wrow = FMT == WFMT_BF16 ? K * 2 : (FMT == WFMT_FP8 ? K : K / 2);
+  const int xrow = FMT == WFMT_BF16 ? K * 2 : K;
+
+  // Items are visited in order: a cursor (m-block p, tile nt, active expert
+  // a) moves to the next item without searching the work list.
+  struct Cur {
+    int p, nt, a;
+  };
+  auto cur_at = [&](int i) {
+    Cur c;
+    c.p = i / ntiles;
+    c.nt = i - c.p * ntiles;
+    int a = 0, hi = n_act - 1;
+    while (a < hi) {
+      const int mid = (a + hi + 1) >> 1;
+      if (l_pref[mid] <= c.p) a = mid; else hi = mid - 1;
+    }
+    c.a = uni(a);
+    return c;
+  };
+  auto cur_next = [&](Cur& c) {
+    if (++c.nt == ntiles) {
+      c.nt = 0;
+      ++c.p;
+      if (c.a + 1 < n_act && c.p == uni(l_pref[c.a + 1])) ++c.a;
+    }
+  };
+  auto item_of = [&](const Cur& c, Item& it) {
+    const int mb = c.p - uni(l_pref[c.a]);
+    it.slot = uni(l_slot[c.a]);
+    it.row0 = uni(l_row0[c.a]) + mb * C::MB;
+    it.nrows = min(C::MB, uni(l_cnt[c.a]) - mb * C::MB);
+    it.n0 = c.nt * ROWS;
+  };
+
+  const int i_first = (int)(u0 / KC), kc_first = (int)(u0 - (long)i_first * KC);
+  // gathered token rows of the workgroup's grouped-row span, when it fits
+  int rbase = 0;
+  bool tab = false;
+  if (row_tok) {
+    Item f, l;
+    item_of(cur_at(i_first), f);
+    item_of(cur_at((int)((u1 - 1) / KC)), l);
+    rbase = f.row0;
+    const int rspan = l.row0 + l.nrows - f.row0;
+    tab = rspan <= ROWTAB;
+    if (tab)
+      for (int r = threadIdx.x; r < rspan; r += blockDim.x) l_rows[r] = row_tok[rbase + r];
+    __syncthreads();
+  }
+
+  // ---- per-lane constants ---------------------------------------------------
+  // weight loads: instruction j covers rows 4j..4j+3 of the wave's 16; lane l
+  // fetches piece (l&15) ^ row so that the lane-linear LDS placement is the
+  // swizzled layout
+  uint32_t w_lane[4];
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int r = 4 * j + (lane >> 4);
+    w_lane[j] = (uint32_t)(16 * wave + r) * wrow + (((lane & 15) ^ r) << 4);
+  }
+  // token loads: instruction j of the wave covers tokens (wave*NXI + j)*per + ...
+  constexpr int XPER = C::XB == 256 ? 4 : 2;
+  const int x_tok_lane = C::XB == 256 ? (lane >> 4) : (lane >> 5);
+  const int x_pos = C::XB == 256 ? (lane & 15) : (lane & 31);
+  // operand reads (bytes inside a stage)
+  uint32_t w_rd[4];   // bf16 / MXFP4: piece 4q+lg of row lr; fp8: piece 2lg (+8h) of row lr
+  uint32_t x_rd[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int pw = FMT == WFMT_FP8 ? (8 * (q >> 1) + 2 * lg + (q & 1)) : (4 * q + lg);
+    w_rd[q] = C::W_OFF + wave * 4096 + lr * 256 + ((pw ^ lr) << 4);
+    const int px = FMT == WFMT_MXFP4 ? (8 * q + lg) : pw;
+    x_rd[q] = C::X_OFF + lr * C::XB + ((px ^ lr) << 4);
+  }
+
+  // ---- issue side: the loads of the next unit into one ring stage ----------
+  Cur icur = cur_at(i_first);
+  Item ii{};
+  int iss_kc = kc_first;
+  uint32_t x_lane[C::NXI];    // byte offset of this lane's token piece in X (less the chunk)
+  int x_tt[C::NXI];           // the lane's token inside the m-block (clamped to a real one)
+  auto set_issue_item = [&]() {
+    item_of(icur, ii);
+#pragma unroll
+    for (int j = 0; j < C::NXI; ++j) {
+      const int t0 = (wave * C::NXI + j) * XPER;
+      const int t = t0 + x_tok_lane;
+      const int tt = t < ii.nrows ? t : 0;
+      x_tt[j] = tt;
+      int row;
+      if (tab) {
+        row = l_rows[ii.row0 - rbase + tt];
+      } else if (row_tok) {
+        // uniform lookups of the instruction's tokens (scalar loads), then a per-lane pick
+        int r[4];
+#pragma unroll
+        for (int q = 0; q < XPER; ++q) r[q] = row_tok[ii.row0 + (t0 + q < ii.nrows ? t0 + q : 0)];
+        row = r[0];
+#pragma unroll
+        for (int q = 1; q < XPER; ++q) row = (x_tok_lane == q && t < ii.nrows) ? r[q] : row;
+      } else {
+        row = ii.row0 + tt;
+      }
+      x_lane[j] = (uint32_t)row * xrow + ((x_pos ^ (t & 15)) << 4);
+    }
+  };
+  set_issue_item();
+
+  auto issue = [&](int st) {
+    if (iss_kc == KC) {
+      iss_kc = 0;
+      cur_next(icur);
+      set_issue_item();
+    }
+    const int kc = iss_kc++;
+    lds_u8_t* sb = (lds_u8_t*)ring + st * C::STAGE;
+    const uint8_t* wb = pool + (size_t)ii.slot * S;
+    const bool wpart = kc * 256 + 256 > wrow;          // last chunk shorter than 256 bytes per row
+#pragma unroll
+    for (int m = 0; m < C::NMAT; ++m) {
+      const uint8_t* mat = wb + (m ? woff1 : woff0) + (size_t)ii.n0 * wrow + (size_t)kc * 256;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        uint32_t o = w_lane[j];
+        if (FMT != WFMT_BF16 && wpart) {
+          const int r = 4 * j + (lane >> 4), p16 = ((lane & 15) ^ r) << 4;
+          o = (uint32_t)(16 * wave + r) * wrow + (p16 < wrow - kc * 256 ? p16 : 0);
+        }
+        dma16_nt(mat + o, sb + C::W_OFF + (m * NW + wave) * 4096 + j * 1024);
       }
     }
-    const int slot = l_slot[a];
-    const int mb = p - l_pref[a];
-    const int row0 = l_row0[a] + mb * DEC_MB;
-    const int nrows = min(DEC_MB, l_cnt[a] - mb * DEC_MB);
-    const int n0 = nt * rows_item + tw * 16;
-    const uint8_t* wbase = pool + (size_t)slot * S;
-    const int wr = n0 + lr;                                   // this lane's weight row
-    const uint8_t* w0 = wbase + woff0 + (size_t)wr * wrow_bytes;
-    const uint8_t* w1 = wbase + woff1 + (size_t)wr * wrow_bytes;
-    const uint8_t* s0 = nullptr;
-    const uint8_t* s1 = nullptr;
+    const bool xpart = kc * C::XB + C::XB > xrow;
+    const uint8_t* xb = X + (size_t)kc * C::XB;
+#pragma unroll
+    for (int j = 0; j < C::NXI; ++j) {
+      uint32_t o = x_lane[j];
+      if (FMT != WFMT_BF16 && xpart) {
+        const int t = (wave * C::NXI + j) * XPER + x_tok_lane;
+        const int p16 = (x_pos ^ (t & 15)) << 4;
+        o = o - p16 + (p16 < xrow - kc * C::XB ? p16 : 0);
+      }
+      dma16(xb + o, sb + C::X_OFF + (wave * C::NXI + j) * 1024);
+    }
     if (FMT == WFMT_FP8) {
-      s0 = wbase + soff0 + (size_t)(n0 / 128) * (K / 128) * 4;
-      s1 = wbase + soff1 + (size_t)(n0 / 128) * (K / 128) * 4;
+      const int kb = K / 128;   // 128-K groups per row
+      {
+        // token scales: entry e = 64*wave + lane -> token e/2, half e%2 of the chunk
+        const int e = wave * 64 + lane, t = e >> 1, h = e & 1;
+        const int tt = t < ii.nrows ? t : 0;
+        const int g = min(kc * 2 + h, kb - 1);
+        dma4(Xs + ((size_t)(ii.row0 + tt) * kb + g) * 4, sb + C::XS_OFF + wave * 256);
+      }
+      {
+        // weight scales of this wave's 16 rows: lane (2m + h) -> matrix m, half h
+        const int m = (lane >> 1) & 1, h = lane & 1;
+        const size_t so = (m && GATED) ? soff1 : soff0;
+        const int g = min(kc * 2 + h, kb - 1);
+        dma4(wb + so + ((size_t)((ii.n0 + 16 * wave) / 128) * kb + g) * 4, sb + C::WS_OFF + wave * 256);
+      }
     } else if (FMT == WFMT_MXFP4) {
-      s0 = wbase + soff0 + (size_t)wr * (K / 32);
-      s1 = wbase + soff1 + (size_t)wr * (K / 32);
-    }
-    int xr[4];
-#pragma unroll
-    for (int ms = 0; ms < 4; ++ms) xr[ms] = src_row(row_tok, row0, nrows, ms, lr);
-    const int nms = (nrows + 15) >> 4;
-    f32x4_t acc[NACC];
-#pragma unroll
-    for (int q = 0; q < NACC; ++q) acc[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
-
-    // loads are unconditional: past the wave's last chunk they re-read that
-    // chunk (a cache hit, unused), so no branch drains the memory counter
-    auto loadw = [&](int c, typename F::W& ga, typename F::W& ua) {
-      const int cc = min(c, last);
-      F::load_w(ga, w0, wrow_bytes, cc * 128, lg);
-      load_wscale<F>(ga, s0, cc, lg);
-      if (GATED) {
-        F::load_w(ua, w1, wrow_bytes, cc * 128, lg);
-        load_wscale<F>(ua, s1, cc, lg);
+      const int kb = K / 32;    // 32-K blocks per row
+      {
+        // token scales: entry e -> token e/4, 4 bytes (blocks 4*(e%4)..+3 of the chunk)
+        const int e = wave * 64 + lane, t = e >> 2, qd = e & 3;
+        const int tt = t < ii.nrows ? t : 0;
+        const int g = min(kc * 16 + qd * 4, kb - 4);
+        dma4(Xs + (size_t)(ii.row0 + tt) * kb + g, sb + C::XS_OFF + wave * 256);
       }
-    };
-    auto compute = [&](int c, const typename F::W& ga, const typename F::W& ua) {
 #pragma unroll
-      for (int ms = 0; ms < 4; ++ms) {
+      for (int m = 0; m < C::NMAT; ++m) {
+        // weight scales: lane -> row lane/4 of the wave's 16, 4 bytes
+        const int r = lane >> 2, qd = lane & 3;
+        const int g = min(kc * 16 + qd * 4, kb - 4);
+        dma4(wb + (m ? soff1 : soff0) + (size_t)(ii.n0 + 16 * wave + r) * kb + g,
+             sb + C::WS_OFF + (m * NW + wave) * 256);
+      }
+    }
+  };
+
+  // ---- compute side ------------------------------------------------------
+  f32x4_t acc[C::NACC];
+#pragma unroll
+  for (int q = 0; q < C::NACC; ++q) acc[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  Cur ccur = cur_at(i_first);
+  Item ci{};
+  item_of(ccur, ci);
+
+  auto compute = [&](int kc, int st) {
+    const uint8_t* sb = ring + st * C::STAGE;
+    const int nms = (ci.nrows + 15) >> 4;
+    if (FMT == WFMT_BF16) {
+      i32x4_t wa[C::NMAT][4];
+#pragma unroll
+      for (int m = 0; m < C::NMAT; ++m)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) wa[m][q] = lds16(sb + w_rd[q] + m * NW * 4096);
+#pragma unroll
+      for (int ms = 0; ms < NS; ++ms) {
         if (ms >= nms) break;
-        typename F::X xb;
-        F::load_x(xb, X, Xs, max(xr[ms], 0), K, c * 128, c, lg);
-        if (xr[ms] < 0) F::zero_x(xb);
-        F::mma(acc[ms], ga, xb, wscale<F>(ga));
-        if (GATED) F::mma(acc[4 + ms], ua, xb, wscale<F>(ua));
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          const i32x4_t xv = lds16(sb + x_rd[q] + ms * 16 * C::XB);
+#pragma unroll
+          for (int m = 0; m < C::NMAT; ++m)
+            acc[m * NS + ms] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                __builtin_bit_cast(bf16x8_t, wa[m][q]), __builtin_bit_cast(bf16x8_t, xv), acc[m * NS + ms], 0, 0, 0);
+        }
       }
-    };
-    if (ks < nchunk) {
-      typename F::W g0, u0, g1, u1;
-      loadw(ks, g0, u0);
-      for (int c = ks; c <= last; c += 2 * SPLIT) {
-        loadw(c + SPLIT, g1, u1);
-        compute(c, g0, u0);
-        if (c + SPLIT > last) break;
-        loadw(c + 2 * SPLIT, g0, u0);
-        compute(c + SPLIT, g1, u1);
+    } else if (FMT == WFMT_FP8) {
+      const f32x4_t z4 = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        if (h == 1 && kc * 256 + 128 >= K) break;
+        i32x8_t wa[C::NMAT];
+        float ws[C::NMAT];
+#pragma unroll
+        for (int m = 0; m < C::NMAT; ++m) {
+          const i32x4_t lo = lds16(sb + w_rd[2 * h] + m * NW * 4096);
+          const i32x4_t hi = lds16(sb + w_rd[2 * h + 1] + m * NW * 4096);
+          wa[m] = i32x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          ws[m] = *(const float*)(sb + C::WS_OFF + wave * 256 + (2 * m + h) * 4);
+        }
+#pragma unroll
+        for (int ms = 0; ms < NS; ++ms) {
+          if (ms >= nms) break;
+          const int t = ms * 16 + lr;
+          const i32x4_t lo = lds16(sb + x_rd[2 * h] + ms * 16 * C::XB);
+          const i32x4_t hi = lds16(sb + x_rd[2 * h + 1] + ms * 16 * C::XB);
+          const i32x8_t xv = i32x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          const float xs = *(const float*)(sb + C::XS_OFF + (2 * t + h) * 4);
+#pragma unroll
+          for (int m = 0; m < C::NMAT; ++m) {
+            const f32x4_t pr = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wa[m], xv, z4, 0, 0, 0, 127, 0, 127);
+            acc[m * NS + ms] += pr * (ws[m] * xs);
+          }
+        }
       }
-    }
-
-    // partial sums of the SPLIT waves of a tile, added in wave order
-    if (SPLIT > 1) {
-      if (ks > 0) {
+    } else {
 #pragma unroll
-        for (int q = 0; q < NACC; ++q)
+      for (int q = 0; q < 4; ++q) {
+        if (q > 0 && kc * 512 + q * 128 >= K) break;
+        i32x8_t wa[C::NMAT];
+        int wsc[C::NMAT];
 #pragma unroll
-          for (int i = 0; i < 4; ++i) red[(((tw * (SPLIT - 1) + ks - 1) * NACC + q) * 4 + i) * 64 + lane] = acc[q][i];
-      }
-      __syncthreads();
-      if (ks == 0) {
+        for (int m = 0; m < C::NMAT; ++m) {
+          const i32x4_t v = lds16(sb + w_rd[q] + m * NW * 4096);
+          wa[m] = i32x8_t{v[0], v[1], v[2], v[3], 0, 0, 0, 0};
+          wsc[m] = sb[C::WS_OFF + (m * NW + wave) * 256 + lr * 16 + 4 * q + lg];
+        }
 #pragma unroll
-        for (int w = 1; w < SPLIT; ++w)
+        for (int ms = 0; ms < NS; ++ms) {
+          if (ms >= nms) break;
+          const int t = ms * 16 + lr;
+          // 8-bit operand: bytes 0-15 = K [16g, 16g+16), bytes 16-31 = K [64+16g, 64+16g+16)
+          const i32x4_t lo = lds16(sb + x_rd[q] + ms * 16 * C::XB);
+          const i32x4_t hi = lds16(sb + C::X_OFF + t * C::XB + (((8 * q + 4 + lg) ^ lr) << 4));
+          const i32x8_t xv = i32x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          const int xsc = sb[C::XS_OFF + t * 16 + 4 * q + lg];
 #pragma unroll
-          for (int q = 0; q < NACC; ++q)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) acc[q][i] += red[(((tw * (SPLIT - 1) + w - 1) * NACC + q) * 4 + i) * 64 + lane];
-      }
-      __syncthreads();
-    }
-    if (ks == 0) {
-#pragma unroll
-      for (int ms = 0; ms < 4; ++ms) {
-        const int r = ms * 16 + lr;
-        if (r >= nrows) continue;
-        const size_t o = (size_t)(row0 + r) * N + n0 + lg * 4;
-        if (GATED && FMT != WFMT_BF16) {
-          float4 v;
-          v.x = silu_mul(acc[ms][0], acc[4 + ms][0]);
-          v.y = silu_mul(acc[ms][1], acc[4 + ms][1]);
-          v.z = silu_mul(acc[ms][2], acc[4 + ms][2]);
-          v.w = silu_mul(acc[ms][3], acc[4 + ms][3]);
-          *(float4*)((float*)out + o) = v;
-        } else {
-          float v[4];
-#pragma unroll
-          for (int i = 0; i < 4; ++i) v[i] = GATED ? silu_mul(acc[ms][i], acc[4 + ms][i]) : acc[ms][i];
-          uint2 pk;
-          pk.x = (uint32_t)f32_to_bf16_bits(v[0]) | ((uint32_t)f32_to_bf16_bits(v[1]) << 16);
-          pk.y = (uint32_t)f32_to_bf16_bits(v[2]) | ((uint32_t)f32_to_bf16_bits(v[3]) << 16);
-          st8((uint16_t*)out + o, pk);
+          for (int m = 0; m < C::NMAT; ++m)
+            acc[m * NS + ms] =
+                __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wa[m], xv, acc[m * NS + ms], 4, 0, 0, wsc[m], 0, xsc);
         }
       }
     }
+  };
+
+  // A finished item's outputs (or, for an item cut by a range boundary, its
+  // partial tile) are stored at the start of the next iteration, before that
+  // iteration's loads: the memory counter also counts stores, so stores
+  // issued after a chunk's loads would make the next wait cover part of the
+  // chunk just requested.
+  f32x4_t pend[C::NACC];
+  Item pit{};
+  f32x4_t* pend_part = nullptr;
+  bool has_pend = false;
+  auto flush = [&]() {
+    if (has_pend) {
+      if (pend_part) {
+#pragma unroll
+        for (int q = 0; q < C::NACC; ++q) pend_part[q * 64 + lane] = pend[q];
+      } else {
+        store_out<FMT, GATED, NS>(pend, pit, wave, lane, N, out);
+      }
+    }
+    has_pend = false;
+  };
+  auto finish_item = [&](int i) {
+    if ((long)i * KC >= u0 && (long)(i + 1) * KC <= u1) {
+      activate<GATED, NS>(acc, pend);
+      pit = ci;
+      pend_part = nullptr;
+    } else {                      // cut by a range boundary: gemm_dec_fix adds the parts
+#pragma unroll
+      for (int q = 0; q < C::NACC; ++q) pend[q] = acc[q];
+      pend_part = part_tile<C::NACC>(part, b, i, U, G, KC, wave);
+    }
+    has_pend = true;
+  };
+
+  // ---- the stream ----------------------------------------------------------
+  const int n = (int)(u1 - u0);     // units of this workgroup
+#pragma unroll
+  for (int s = 0; s < NST - 1; ++s)
+    if (s < n) issue(s);
+  int st = 0, i = i_first, kc = kc_first;
+  for (int v = 0; v < n; ++v) {
+    if (v + NST - 2 < n) wait_vmcnt<C::NI * (NST - 2)>();   // this wave's loads of unit v have landed
+    else wait_vmcnt<0>();
+    barrier_keep_loads();                                   // everyone's have; the oldest stage is free
+    flush();
+    if (v + NST - 1 < n) issue(st == 0 ? NST - 1 : st - 1);
+    if (kc == KC) {
+      kc = 0;
+      ++i;
+      cur_next(ccur);
+      item_of(ccur, ci);
+    }
+    compute(kc, st);
+    if (kc == KC - 1 || v == n - 1) {
+      finish_item(i);
+#pragma unroll
+      for (int q = 0; q < C::NACC; ++q) acc[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    }
+    ++kc;
+    st = st + 1 == NST ? 0 : st + 1;
   }
+  flush();
+}
+
+// Items cut by range boundaries of a gemm_dec launch of `grid` workgroups:
+// workgroup j looks at the boundary between ranges j-1 and j; if it cuts an
+// item and is the first boundary inside it, the workgroup adds the item's
+// partial tiles in workgroup order and applies the epilogue.
+template <int FMT, bool GATED, int NS>
+__global__ void __launch_bounds__(256)
+gemm_dec_fix(const WorkList* __restrict__ wl, const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
+             int K, int N, int grid, void* __restrict__ out, const f32x4_t* __restrict__ part) {
+  using C = Cfg<FMT, GATED, NS>;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int ntiles = N / ROWS;
+  const int KC = (K + C::CK - 1) / C::CK;
+  const long U = (long)wl->n_mblk * ntiles * KC;
+  const long G = U < (long)grid ? U : (long)grid;
+  const long j = blockIdx.x;
+  if (j < 1 || j >= G) return;
+  const long ub = range_start(j, U, G);
+  const int i = (int)(ub / KC);
+  if (ub == (long)i * KC) return;                      // boundary between items
+  const long bf = owner_of((long)i * KC, U, G);
+  if (bf != j - 1) return;                             // an earlier boundary owns the item
+  const long bl = owner_of((long)(i + 1) * KC - 1, U, G);
+  f32x4_t acc[C::NACC];
+#pragma unroll
+  for (int q = 0; q < C::NACC; ++q) acc[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (long bb = bf; bb <= bl; ++bb) {
+    const f32x4_t* src = part_tile<C::NACC>((f32x4_t*)part, bb, i, U, G, KC, wave);
+#pragma unroll
+    for (int q = 0; q < C::NACC; ++q) acc[q] += src[q * 64 + lane];
+  }
+  Item it;
+  decode_global(wl, counts, offsets, ntiles, C::MB, i, it);
+  f32x4_t val[NS];
+  activate<GATED, NS>(acc, val);
+  store_out<FMT, GATED, NS>(val, it, wave, lane, N, out);
 }
 
 namespace {
 
-template <int FMT, bool GATED, int SPLIT>
+template <int FMT, bool GATED, int NS>
 hipError_t launch_dec(int n_cu, const WorkList* wl, const int32_t* counts, const int32_t* offsets,
                       const uint8_t* pool, size_t S, size_t woff0, size_t woff1, size_t soff0, size_t soff1,
-                      const void* X, const void* Xs, const int32_t* row_tok, int K, int N, void* out, hipStream_t s) {
+                      const void* X, const void* Xs, const int32_t* row_tok, int K, int N, void* out, f32x4_t* part,
+                      hipStream_t s) {
+  using C = Cfg<FMT, GATED, NS>;
   static int per_cu = 0;     // resident workgroups per CU for this instance
+  const size_t lds = (size_t)NST * C::STAGE;
   if (per_cu == 0) {
+    hipError_t e = hipFuncSetAttribute((const void*)gemm_dec<FMT, GATED, NS>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
     int nb = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, gemm_dec<FMT, GATED, SPLIT>, 256, 0) != hipSuccess ||
-        nb < 1)
-      nb = 2;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&nb, gemm_dec<FMT, GATED, NS>, 256, lds) != hipSuccess || nb < 1)
+      nb = 1;
     per_cu = nb;
   }
-  gemm_dec<FMT, GATED, SPLIT><<<n_cu * per_cu, 256, 0, s>>>(wl, counts, offsets, pool, S, woff0, woff1, soff0, soff1,
-                                                             X, Xs, row_tok, K, N, out);
+  int grid = n_cu * per_cu;
+  if (grid > MAX_BLOCKS) grid = MAX_BLOCKS - MAX_BLOCKS % N_XCD;
+  gemm_dec<FMT, GATED, NS><<<grid, 256, lds, s>>>(wl, counts, offsets, pool, S, woff0, woff1, soff0, soff1,
+                                                  (const uint8_t*)X, (const uint8_t*)Xs, row_tok, K, N, out, part);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  gemm_dec_fix<FMT, GATED, NS><<<grid, 256, 0, s>>>(wl, counts, offsets, K, N, grid, out, part);
   return hipGetLastError();
 }
 
 template <int FMT, bool GATED>
-hipError_t launch_split(int split, int n_cu, const WorkList* wl, const int32_t* counts, const int32_t* offsets,
-                        const uint8_t* pool, size_t S, size_t woff0, size_t woff1, size_t soff0, size_t soff1,
-                        const void* X, const void* Xs, const int32_t* row_tok, int K, int N, void* out,
-                        hipStream_t s) {
-  if (split == 1)
-    return launch_dec<FMT, GATED, 1>(n_cu, wl, counts, offsets, pool, S, woff0, woff1, soff0, soff1, X, Xs, row_tok,
-                                     K, N, out, s);
-  if (split == 2)
-    return launch_dec<FMT, GATED, 2>(n_cu, wl, counts, offsets, pool, S, woff0, woff1, soff0, soff1, X, Xs, row_tok,
-                                     K, N, out, s);
-  return launch_dec<FMT, GATED, 4>(n_cu, wl, counts, offsets, pool, S, woff0, woff1, soff0, soff1, X, Xs, row_tok, K,
-                                   N, out, s);
+hipError_t launch_ns(int ns, int n_cu, const WorkList* wl, const int32_t* counts, const int32_t* offsets,
+                     const uint8_t* pool, size_t S, size_t woff0, size_t woff1, size_t soff0, size_t soff1,
+                     const void* X, const void* Xs, const int32_t* row_tok, int K, int N, void* out, f32x4_t* part,
+                     hipStream_t s) {
+#define MOE_DEC_ARGS n_cu, wl, counts, offsets, pool, S, woff0, woff1, soff0, soff1, X, Xs, row_tok, K, N, out, part, s
+  if (ns == 1) return launch_dec<FMT, GATED, 1>(MOE_DEC_ARGS);
+  if (ns == 2) return launch_dec<FMT, GATED, 2>(MOE_DEC_ARGS);
+  if constexpr (FMT != WFMT_MXFP4) {
+    if (ns == 4) return launch_dec<FMT, GATED, 4>(MOE_DEC_ARGS);
+  }
+#undef MOE_DEC_ARGS
+  return hipErrorInvalidValue;
 }
 
 }  // namespace
 
-// split: waves sharing one 16-row tile's K (1, 2 or 4); N must be a multiple
-// of 16*4/split.
-extern "C" hipError_t moe_launch_gemm_dec(int fmt, int gated, int split, int n_cu, const WorkList* wl,
+// Bytes of the partial-tile buffer.
+extern "C" size_t moe_dec_part_bytes() { return (size_t)MAX_BLOCKS * 2 * NW * 8 * 64 * sizeof(f32x4_t); }
+// Largest tokens-per-m-block choice (16 * ns) for a weight format.
+extern "C" int moe_dec_max_ns(int fmt) { return fmt == WFMT_MXFP4 ? 2 : 4; }
+
+// ns: 16-token sub-tiles per m-block (1, 2 or 4; 1 or 2 for MXFP4); the work
+// list must have been built with m-blocks of 16*ns tokens.  N must be a
+// multiple of 64; K a multiple of 128.  For the 8-bit formats X holds the
+// quantised rows in grouped order (row_tok must be null).  Two launches: the
+// stream and the fix-up of items cut between workgroups.
+extern "C" hipError_t moe_launch_gemm_dec(int fmt, int gated, int ns, int n_cu, const WorkList* wl,
                                           const int32_t* counts, const int32_t* offsets, const uint8_t* pool,
                                           size_t S, size_t woff0, size_t woff1, size_t soff0, size_t soff1,
                                           const void* X, const void* Xs, const int32_t* row_tok, int K, int N,
-                                          void* out, hipStream_t s) {
-#define MOE_DEC_ARGS split, n_cu, wl, counts, offsets, pool, S, woff0, woff1, soff0, soff1, X, Xs, row_tok, K, N, out, s
-  if (fmt == WFMT_BF16) return gated ? launch_split<WFMT_BF16, true>(MOE_DEC_ARGS) : launch_split<WFMT_BF16, false>(MOE_DEC_ARGS);
-  if (fmt == WFMT_FP8) return gated ? launch_split<WFMT_FP8, true>(MOE_DEC_ARGS) : launch_split<WFMT_FP8, false>(MOE_DEC_ARGS);
-  return gated ? launch_split<WFMT_MXFP4, true>(MOE_DEC_ARGS) : launch_split<WFMT_MXFP4, false>(MOE_DEC_ARGS);
+                                          void* out, void* part, hipStream_t s) {
+  if (N % ROWS || K % 128 || (fmt != WFMT_BF16 && row_tok)) return hipErrorInvalidValue;
+  f32x4_t* p = (f32x4_t*)part;
+#define MOE_DEC_ARGS ns, n_cu, wl, counts, offsets, pool, S, woff0, woff1, soff0, soff1, X, Xs, row_tok, K, N, out, p, s
+  if (fmt == WFMT_BF16) return gated ? launch_ns<WFMT_BF16, true>(MOE_DEC_ARGS) : launch_ns<WFMT_BF16, false>(MOE_DEC_ARGS);
+  if (fmt == WFMT_FP8) return gated ? launch_ns<WFMT_FP8, true>(MOE_DEC_ARGS) : launch_ns<WFMT_FP8, false>(MOE_DEC_ARGS);
+  return gated ? launch_ns<WFMT_MXFP4, true>(MOE_DEC_ARGS) : launch_ns<WFMT_MXFP4, false>(MOE_DEC_ARGS);
 #undef MOE_DEC_ARGS
 }

@@ -44,17 +44,7 @@ constexpr int PF_BLK_PER_WAVE = PF_BLOCKS / 4;         // 6
 constexpr int N_XCD = 8;
 constexpr int PF_WG_PER_CU = 2;
 
-typedef __attribute__((address_space(3))) void lds_void_t;
-typedef __attribute__((address_space(1))) const void gbl_void_t;
-
 DEV int swz(int row, int piece) { return row * PF_ROWB + ((piece ^ ((row >> 1) & 3)) << 4); }
-
-// s_waitcnt with only the vector-memory counter constrained (gfx9 encoding:
-// vmcnt bits [3:0] and [15:14], expcnt [6:4] and lgkmcnt [11:8] left at max).
-template <int N>
-DEV void wait_vmcnt() {
-  __builtin_amdgcn_s_waitcnt((N & 0xF) | (0x7 << 4) | (0xF << 8) | ((N >> 4) << 14));
-}
 
 struct PfItem {
   int slot, row0, nrows, f0;

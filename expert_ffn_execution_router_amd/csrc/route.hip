@@ -15,46 +15,59 @@
 // router logits z[t,e] = sum_h x[t,h] R[e,h] + b[e]  (x bf16, R fp32, fp32 sums)
 // ---------------------------------------------------------------------------
 
-// Small batches: one wave per (expert, 16 tokens); grid (E/4, T/16) so every
-// CU takes part; the expert's row of R is read from L2 by each token group.
-// H % 256 == 0.
+// Small batches: one wave per (expert, 4 tokens), grid (E/4, T/4) so that
+// every CU takes part.  A lane covers 4 consecutive elements of each
+// 256-element chunk of H and issues the loads of 8 chunks (2048 elements) at
+// once, so a wave waits for memory once per 2048 elements instead of once
+// per chunk.  Loads and sums are unconditional (token rows past T re-read
+// row T-1 and are not stored; chunks past H re-read the last one and are
+// weighted by zero), so no branch splits the batch.  H % 256 == 0.
+constexpr int RT_TOK = 4;
 __global__ void __launch_bounds__(256)
 router_small_kernel(const uint16_t* __restrict__ x, const float* __restrict__ R,
                     const float* __restrict__ bias, int T, int E, int H, float* __restrict__ z) {
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int e = blockIdx.x * 4 + wave;
   if (e >= E) return;
+  const int t0 = blockIdx.y * RT_TOK;
   const float* r = R + (size_t)e * H;
-  const float b = bias ? bias[e] : 0.0f;
-  {
-    const int t0 = blockIdx.y * 16;
-    const int nt = min(16, T - t0);
-    float acc[16];
+  const uint16_t* xr[RT_TOK];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) acc[i] = 0.0f;
-    // loads are unconditional (rows past T re-read row T-1 and are not stored)
-    // so the compiler can keep every load of an iteration in flight at once
-    const uint16_t* xr[16];
+  for (int i = 0; i < RT_TOK; ++i) xr[i] = x + (size_t)min(t0 + i, T - 1) * H;
+  float acc[RT_TOK];
 #pragma unroll
-    for (int i = 0; i < 16; ++i) xr[i] = x + (size_t)min(t0 + i, T - 1) * H;
-    for (int h = lane * 4; h < H; h += 256) {
-      const float4 rv = *(const float4*)(r + h);
-      uint2 xv[16];
+  for (int i = 0; i < RT_TOK; ++i) acc[i] = 0.0f;
+  const int nchunk = H / 256;
+  for (int c0 = 0; c0 < nchunk; c0 += 8) {
+    float4 rv[8];
+    uint2 xv[8][RT_TOK];
 #pragma unroll
-      for (int i = 0; i < 16; ++i) xv[i] = *(const uint2*)(xr[i] + h);
+    for (int c = 0; c < 8; ++c) {
+      const int h = min(c0 + c, nchunk - 1) * 256 + lane * 4;
+      rv[c] = *(const float4*)(r + h);
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        acc[i] += bf16_bits_to_f32(xv[i].x & 0xffffu) * rv.x;
-        acc[i] += bf16_bits_to_f32(xv[i].x >> 16) * rv.y;
-        acc[i] += bf16_bits_to_f32(xv[i].y & 0xffffu) * rv.z;
-        acc[i] += bf16_bits_to_f32(xv[i].y >> 16) * rv.w;
+      for (int i = 0; i < RT_TOK; ++i) xv[c][i] = *(const uint2*)(xr[i] + h);
+    }
+    __builtin_amdgcn_sched_barrier(0);    // keep every load of the batch ahead of the sums
+#pragma unroll
+    for (int c = 0; c < 8; ++c) {
+      // padding chunks (past H) contribute exactly zero; no branch
+      const float f = c0 + c < nchunk ? 1.0f : 0.0f;
+      const float4 rw = make_float4(rv[c].x * f, rv[c].y * f, rv[c].z * f, rv[c].w * f);
+#pragma unroll
+      for (int i = 0; i < RT_TOK; ++i) {
+        acc[i] += bf16_bits_to_f32(xv[c][i].x & 0xffffu) * rw.x;
+        acc[i] += bf16_bits_to_f32(xv[c][i].x >> 16) * rw.y;
+        acc[i] += bf16_bits_to_f32(xv[c][i].y & 0xffffu) * rw.z;
+        acc[i] += bf16_bits_to_f32(xv[c][i].y >> 16) * rw.w;
       }
     }
+  }
+  const float b = bias ? bias[e] : 0.0f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const float v = wave_sum(acc[i]);
-      if (lane == 0 && i < nt) z[(size_t)(t0 + i) * E + e] = v + b;
-    }
+  for (int i = 0; i < RT_TOK; ++i) {
+    const float v = wave_sum(acc[i]);
+    if (lane == 0 && t0 + i < T) z[(size_t)(t0 + i) * E + e] = v + b;
   }
 }
 
@@ -337,7 +350,7 @@ group_scatter_kernel(const int32_t* __restrict__ ids, int T, int k, int E, const
 extern "C" hipError_t moe_launch_router(const uint16_t* x, const float* R, const float* bias, int T, int E, int H,
                                         float* z, hipStream_t s) {
   if (T <= 64) {
-    router_small_kernel<<<dim3((E + 3) / 4, (T + 15) / 16), 256, 0, s>>>(x, R, bias, T, E, H, z);
+    router_small_kernel<<<dim3((E + 3) / 4, (T + RT_TOK - 1) / RT_TOK), 256, 0, s>>>(x, R, bias, T, E, H, z);
   } else {
     dim3 g((T + 63) / 64, (E + 63) / 64);
     router_mfma_kernel<<<g, 256, 0, s>>>(x, R, bias, T, E, H, z);
