@@ -492,37 +492,37 @@ gemm_dec(const WorkList* __restrict__ wl, const int32_t* __restrict__ counts, co
     }
   };
 
-  // A finished item's outputs (or, for an item cut by a range boundary, its
-  // partial tile) are stored at the start of the next iteration, before that
-  // iteration's loads: the memory counter also counts stores, so stores
-  // issued after a chunk's loads would make the next wait cover part of the
-  // chunk just requested.
-  f32x4_t pend[C::NACC];
+  // Stores share the memory counter with the loads.  A finished item's
+  // outputs are stored at the start of the next iteration, before that
+  // iteration's loads, and the following wait allows for them (one store
+  // per 16-token sub-tile holding a token); the partial tiles of the (at
+  // most two) items cut by the range boundaries are kept in registers and
+  // stored after the stream.
+  f32x4_t pend[NS], first_part[C::NACC], last_part[C::NACC];
   Item pit{};
-  f32x4_t* pend_part = nullptr;
-  bool has_pend = false;
-  auto flush = [&]() {
-    if (has_pend) {
-      if (pend_part) {
-#pragma unroll
-        for (int q = 0; q < C::NACC; ++q) pend_part[q * 64 + lane] = pend[q];
-      } else {
-        store_out<FMT, GATED, NS>(pend, pit, wave, lane, N, out);
-      }
-    }
+  bool has_pend = false, has_first = false, has_last = false;
+  int last_i = 0;
+  auto flush = [&]() -> int {
+    if (!has_pend) return 0;
     has_pend = false;
+    store_out<FMT, GATED, NS>(pend, pit, wave, lane, N, out);
+    return min(NS, (pit.nrows + 15) >> 4);
   };
   auto finish_item = [&](int i) {
     if ((long)i * KC >= u0 && (long)(i + 1) * KC <= u1) {
       activate<GATED, NS>(acc, pend);
       pit = ci;
-      pend_part = nullptr;
-    } else {                      // cut by a range boundary: gemm_dec_fix adds the parts
+      has_pend = true;
+    } else if (i == i_first) {    // cut by a range boundary: gemm_dec_fix adds the parts
 #pragma unroll
-      for (int q = 0; q < C::NACC; ++q) pend[q] = acc[q];
-      pend_part = part_tile<C::NACC>(part, b, i, U, G, KC, wave);
+      for (int q = 0; q < C::NACC; ++q) first_part[q] = acc[q];
+      has_first = true;
+    } else {
+#pragma unroll
+      for (int q = 0; q < C::NACC; ++q) last_part[q] = acc[q];
+      has_last = true;
+      last_i = i;
     }
-    has_pend = true;
   };
 
   // ---- the stream ----------------------------------------------------------
@@ -530,12 +530,21 @@ gemm_dec(const WorkList* __restrict__ wl, const int32_t* __restrict__ counts, co
 #pragma unroll
   for (int s = 0; s < NST - 1; ++s)
     if (s < n) issue(s);
-  int st = 0, i = i_first, kc = kc_first;
+  int st = 0, i = i_first, kc = kc_first, nst = 0;
   for (int v = 0; v < n; ++v) {
-    if (v + NST - 2 < n) wait_vmcnt<C::NI * (NST - 2)>();   // this wave's loads of unit v have landed
-    else wait_vmcnt<0>();
+    // this wave's loads of unit v have landed (nst stores were issued after them)
+    if (v + NST - 2 < n) {
+      constexpr int W0 = C::NI * (NST - 2);
+      if (nst == 0) wait_vmcnt<W0>();
+      else if (nst == 1) wait_vmcnt<W0 + 1>();
+      else if (nst == 2) wait_vmcnt<W0 + 2>();
+      else if (nst == 3) wait_vmcnt<W0 + 3>();
+      else wait_vmcnt<W0 + 4>();
+    } else {
+      wait_vmcnt<0>();
+    }
     barrier_keep_loads();                                   // everyone's have; the oldest stage is free
-    flush();
+    nst = flush();
     if (v + NST - 1 < n) issue(st == 0 ? NST - 1 : st - 1);
     if (kc == KC) {
       kc = 0;
@@ -553,6 +562,16 @@ gemm_dec(const WorkList* __restrict__ wl, const int32_t* __restrict__ counts, co
     st = st + 1 == NST ? 0 : st + 1;
   }
   flush();
+  if (has_first) {
+    f32x4_t* p = part_tile<C::NACC>(part, b, i_first, U, G, KC, wave);
+#pragma unroll
+    for (int q = 0; q < C::NACC; ++q) p[q * 64 + lane] = first_part[q];
+  }
+  if (has_last) {
+    f32x4_t* p = part_tile<C::NACC>(part, b, last_i, U, G, KC, wave);
+#pragma unroll
+    for (int q = 0; q < C::NACC; ++q) p[q * 64 + lane] = last_part[q];
+  }
 }
 
 // Items cut by range boundaries of a gemm_dec launch of `grid` workgroups:
