@@ -41,8 +41,8 @@ class moe_plan_info(ctypes.Structure):
         return {f: getattr(self, f) for f, _ in self._fields_}
 
 
-MOE_N_STAGES = 9
-STAGES = ["route", "topk", "group", "quant_x", "gemm1", "quant_a", "gemm2", "combine", "plan"]
+MOE_N_STAGES = 10
+STAGES = ["route", "topk", "group", "quant_x", "gemm1", "quant_a", "gemm2", "combine", "plan", "fixup"]
 
 
 class moe_profile(ctypes.Structure):

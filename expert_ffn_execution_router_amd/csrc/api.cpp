@@ -27,7 +27,7 @@ hipError_t moe_launch_group(const int32_t* ids, int T, int k, int E, const uint3
 hipError_t moe_launch_gemm_dec(int fmt, int gated, int ns, int n_cu, const WorkList* wl, const int32_t* counts,
                                const int32_t* offsets, const uint8_t* pool, size_t S, size_t woff0, size_t woff1,
                                size_t soff0, size_t soff1, const void* X, const void* Xs, const int32_t* row_tok,
-                               int K, int N, void* out, void* part, hipStream_t s);
+                               int K, int N, void* out, void* part, int fix, hipStream_t s);
 size_t moe_dec_part_bytes();
 int moe_dec_max_ns(int fmt);
 int moe_pf_tile_tokens();
@@ -280,22 +280,34 @@ int forward_experts(moe_ctx* c, const void* hidden, int T, const int32_t* slot_r
   } else if (g.wfmt == MOE_W_BF16) {
     STAGE(c, MOE_STAGE_GEMM1, s,
           moe_launch_gemm_dec(g.wfmt, 1, ns, ncu, c->wl, c->counts, c->offsets, c->slot_pool, b.S, b.w[0], b.w[1],
-                              0, 0, hidden, nullptr, c->perm_tok, g.H, g.I, c->A, c->part, s));
+                              0, 0, hidden, nullptr, c->perm_tok, g.H, g.I, c->A, c->part, 0, s));
+    STAGE(c, MOE_STAGE_FIXUP, s,
+          moe_launch_gemm_dec(g.wfmt, 1, ns, ncu, c->wl, c->counts, c->offsets, c->slot_pool, b.S, b.w[0], b.w[1],
+                              0, 0, hidden, nullptr, c->perm_tok, g.H, g.I, c->A, c->part, 1, s));
     STAGE(c, MOE_STAGE_GEMM2, s,
           moe_launch_gemm_dec(g.wfmt, 0, ns, ncu, c->wl, c->counts, c->offsets, c->slot_pool, b.S, b.w[2], 0, 0, 0,
-                              c->A, nullptr, nullptr, g.I, g.H, c->Z, c->part, s));
+                              c->A, nullptr, nullptr, g.I, g.H, c->Z, c->part, 0, s));
+    STAGE(c, MOE_STAGE_FIXUP, s,
+          moe_launch_gemm_dec(g.wfmt, 0, ns, ncu, c->wl, c->counts, c->offsets, c->slot_pool, b.S, b.w[2], 0, 0, 0,
+                              c->A, nullptr, nullptr, g.I, g.H, c->Z, c->part, 1, s));
   } else {
     // activations quantised straight into grouped order (row p <- token perm_tok[p])
     STAGE(c, MOE_STAGE_QUANT_X, s,
           moe_launch_quant(g.wfmt, 1, hidden, T * g.k, c->offsets + g.E, c->perm_tok, g.H, c->Xq, c->Xs, s));
     STAGE(c, MOE_STAGE_GEMM1, s,
           moe_launch_gemm_dec(g.wfmt, 1, ns, ncu, c->wl, c->counts, c->offsets, c->slot_pool, b.S, b.w[0], b.w[1],
-                              b.s[0], b.s[1], c->Xq, c->Xs, nullptr, g.H, g.I, c->A, c->part, s));
+                              b.s[0], b.s[1], c->Xq, c->Xs, nullptr, g.H, g.I, c->A, c->part, 0, s));
+    STAGE(c, MOE_STAGE_FIXUP, s,
+          moe_launch_gemm_dec(g.wfmt, 1, ns, ncu, c->wl, c->counts, c->offsets, c->slot_pool, b.S, b.w[0], b.w[1],
+                              b.s[0], b.s[1], c->Xq, c->Xs, nullptr, g.H, g.I, c->A, c->part, 1, s));
     STAGE(c, MOE_STAGE_QUANT_A, s,
           moe_launch_quant(g.wfmt, 0, c->A, T * g.k, c->offsets + g.E, nullptr, g.I, c->Aq, c->As, s));
     STAGE(c, MOE_STAGE_GEMM2, s,
           moe_launch_gemm_dec(g.wfmt, 0, ns, ncu, c->wl, c->counts, c->offsets, c->slot_pool, b.S, b.w[2], 0, b.s[2],
-                              0, c->Aq, c->As, nullptr, g.I, g.H, c->Z, c->part, s));
+                              0, c->Aq, c->As, nullptr, g.I, g.H, c->Z, c->part, 0, s));
+    STAGE(c, MOE_STAGE_FIXUP, s,
+          moe_launch_gemm_dec(g.wfmt, 0, ns, ncu, c->wl, c->counts, c->offsets, c->slot_pool, b.S, b.w[2], 0, b.s[2],
+                              0, c->Aq, c->As, nullptr, g.I, g.H, c->Z, c->part, 1, s));
   }
   return MOE_OK;
 }

@@ -617,7 +617,7 @@ template <int FMT, bool GATED, int NS>
 hipError_t launch_dec(int n_cu, const WorkList* wl, const int32_t* counts, const int32_t* offsets,
                       const uint8_t* pool, size_t S, size_t woff0, size_t woff1, size_t soff0, size_t soff1,
                       const void* X, const void* Xs, const int32_t* row_tok, int K, int N, void* out, f32x4_t* part,
-                      hipStream_t s) {
+                      bool fix, hipStream_t s) {
   using C = Cfg<FMT, GATED, NS>;
   static int per_cu = 0;     // resident workgroups per CU for this instance
   const size_t lds = (size_t)NST * C::STAGE;
@@ -632,11 +632,11 @@ hipError_t launch_dec(int n_cu, const WorkList* wl, const int32_t* counts, const
   }
   int grid = n_cu * per_cu;
   if (grid > MAX_BLOCKS) grid = MAX_BLOCKS - MAX_BLOCKS % N_XCD;
-  gemm_dec<FMT, GATED, NS><<<grid, 256, lds, s>>>(wl, counts, offsets, pool, S, woff0, woff1, soff0, soff1,
-                                                  (const uint8_t*)X, (const uint8_t*)Xs, row_tok, K, N, out, part);
-  hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
-  gemm_dec_fix<FMT, GATED, NS><<<grid, 256, 0, s>>>(wl, counts, offsets, K, N, grid, out, part);
+  if (fix)
+    gemm_dec_fix<FMT, GATED, NS><<<grid, 256, 0, s>>>(wl, counts, offsets, K, N, grid, out, part);
+  else
+    gemm_dec<FMT, GATED, NS><<<grid, 256, lds, s>>>(wl, counts, offsets, pool, S, woff0, woff1, soff0, soff1,
+                                                    (const uint8_t*)X, (const uint8_t*)Xs, row_tok, K, N, out, part);
   return hipGetLastError();
 }
 
@@ -644,8 +644,8 @@ template <int FMT, bool GATED>
 hipError_t launch_ns(int ns, int n_cu, const WorkList* wl, const int32_t* counts, const int32_t* offsets,
                      const uint8_t* pool, size_t S, size_t woff0, size_t woff1, size_t soff0, size_t soff1,
                      const void* X, const void* Xs, const int32_t* row_tok, int K, int N, void* out, f32x4_t* part,
-                     hipStream_t s) {
-#define MOE_DEC_ARGS n_cu, wl, counts, offsets, pool, S, woff0, woff1, soff0, soff1, X, Xs, row_tok, K, N, out, part, s
+                     bool fix, hipStream_t s) {
+#define MOE_DEC_ARGS n_cu, wl, counts, offsets, pool, S, woff0, woff1, soff0, soff1, X, Xs, row_tok, K, N, out, part, fix, s
   if (ns == 1) return launch_dec<FMT, GATED, 1>(MOE_DEC_ARGS);
   if (ns == 2) return launch_dec<FMT, GATED, 2>(MOE_DEC_ARGS);
   if constexpr (FMT != WFMT_MXFP4) {
@@ -665,16 +665,18 @@ extern "C" int moe_dec_max_ns(int fmt) { return fmt == WFMT_MXFP4 ? 2 : 4; }
 // ns: 16-token sub-tiles per m-block (1, 2 or 4; 1 or 2 for MXFP4); the work
 // list must have been built with m-blocks of 16*ns tokens.  N must be a
 // multiple of 64; K a multiple of 128.  For the 8-bit formats X holds the
-// quantised rows in grouped order (row_tok must be null).  Two launches: the
-// stream and the fix-up of items cut between workgroups.
+// quantised rows in grouped order (row_tok must be null).  The stream leaves
+// the items cut between workgroups as partial tiles in `part`; the same call
+// with fix != 0 (same arguments, next on the stream) adds and stores them.
 extern "C" hipError_t moe_launch_gemm_dec(int fmt, int gated, int ns, int n_cu, const WorkList* wl,
                                           const int32_t* counts, const int32_t* offsets, const uint8_t* pool,
                                           size_t S, size_t woff0, size_t woff1, size_t soff0, size_t soff1,
                                           const void* X, const void* Xs, const int32_t* row_tok, int K, int N,
-                                          void* out, void* part, hipStream_t s) {
+                                          void* out, void* part, int fix, hipStream_t s) {
   if (N % ROWS || K % 128 || (fmt != WFMT_BF16 && row_tok)) return hipErrorInvalidValue;
   f32x4_t* p = (f32x4_t*)part;
-#define MOE_DEC_ARGS ns, n_cu, wl, counts, offsets, pool, S, woff0, woff1, soff0, soff1, X, Xs, row_tok, K, N, out, p, s
+  const bool f = fix != 0;
+#define MOE_DEC_ARGS ns, n_cu, wl, counts, offsets, pool, S, woff0, woff1, soff0, soff1, X, Xs, row_tok, K, N, out, p, f, s
   if (fmt == WFMT_BF16) return gated ? launch_ns<WFMT_BF16, true>(MOE_DEC_ARGS) : launch_ns<WFMT_BF16, false>(MOE_DEC_ARGS);
   if (fmt == WFMT_FP8) return gated ? launch_ns<WFMT_FP8, true>(MOE_DEC_ARGS) : launch_ns<WFMT_FP8, false>(MOE_DEC_ARGS);
   return gated ? launch_ns<WFMT_MXFP4, true>(MOE_DEC_ARGS) : launch_ns<WFMT_MXFP4, false>(MOE_DEC_ARGS);

@@ -236,7 +236,8 @@ enum {
   MOE_STAGE_GEMM2 = 6,    /* grouped down GEMM */
   MOE_STAGE_COMBINE = 7,  /* weighted unpermute-combine */
   MOE_STAGE_PLAN = 8,     /* cache-control kernel */
-  MOE_N_STAGES = 9
+  MOE_STAGE_FIXUP = 9,    /* small-batch GEMMs: sums of the items cut between workgroups */
+  MOE_N_STAGES = 10
 };
 
 typedef struct {
