@@ -52,6 +52,9 @@ def parse():
     ap.add_argument("--no-e2e", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--e2e-T", type=int, default=1, help="tokens per step through the slot cache")
+    ap.add_argument("--e2e-warmup", type=int, default=16)
+    ap.add_argument("--e2e-steps", type=int, default=32)
     ap.add_argument("--prefill-T", type=int, default=8192)
     ap.add_argument("--prefill-runs", type=int, default=2, help="double-buffered chunks timed (best is kept)")
     ap.add_argument("--cpu-layers", type=int, default=3)
@@ -249,29 +252,37 @@ def phase_decode(w: Workload):
 
 
 def phase_e2e(w: Workload):
-    """The same steps through the 40% slot cache: PCIe and host included."""
+    """Decode steps through the 40% slot cache (LRU, HYBRID miss split with the
+    bandwidths measured at startup), cold start: PCIe and host included."""
     import torch
+    import synth
     from expert_ffn_execution_router_amd import binding as B
     args, c = w.args, w.cfg
-    L, T, K, W = c.L, args.T, args.steps, args.warmup
+    L, T = c.L, args.e2e_T
+    W, K = args.e2e_warmup, args.e2e_steps
+    keys = synth.decode_row_keys(c, args.seed + 1, W + K, T)
+    hid = torch.from_numpy(synth.hidden_rows(c, keys.reshape(-1)).reshape(W + K, L, T, c.H).view(np.int16)).to(w.dev)
+    outs = torch.empty(L, T, c.H, dtype=torch.bfloat16, device=w.dev)
     rc = w.runtime(c.n_slots, max(T, 64))
     bp, bh = rc.calibrate()
     rc.set_policy(B.MOE_POLICY_HYBRID, bp, bh)
     copy = torch.cuda.Stream()
-    ke = max(2, K // 2)
     infos = []
 
     def e2e_step(s, record):
         for l in range(L):
-            info = rc.decode_layer(l, w.hidden[s % (W + K), l], w.R[l], w.bias[l], w.outs[l], copy_stream=copy)
+            info = rc.decode_layer(l, hid[s, l], w.R[l], w.bias[l], outs[l], copy_stream=copy)
             if record:
                 infos.append(info.as_dict())
 
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
     for s in range(W):
         e2e_step(s, False)
     torch.cuda.synchronize()
+    warm_el = time.perf_counter() - t0
     t0 = time.perf_counter()
-    for s in range(ke):
+    for s in range(K):
         e2e_step(W + s, True)
     torch.cuda.synchronize()
     el = time.perf_counter() - t0
@@ -279,9 +290,9 @@ def phase_e2e(w: Workload):
     uq = sum(i["n_unique"] for i in infos)
     res = {
         "note": "PCIe and host included; not the value",
-        "n_slots": c.n_slots, "policy": "hybrid", "B_P_GBps": bp, "B_H_GBps": bh,
-        "q_star_over_m": bp / bh, "steps": ke,
-        "moe_layer_tokens_per_s": ke * L * T / el, "ms_per_step": el / ke * 1e3,
+        "T": T, "n_slots": c.n_slots, "policy": "hybrid", "B_P_GBps": bp, "B_H_GBps": bh,
+        "q_star_over_m": bp / bh, "warmup_steps": W, "warmup_ms_per_step": warm_el / max(W, 1) * 1e3,
+        "steps": K, "moe_layer_tokens_per_s": K * L * T / el, "ms_per_step": el / K * 1e3,
         "hit_rate": sum(i["n_hit"] for i in infos) / max(uq, 1),
         "misses_per_layer": sum(i["m"] for i in infos) / len(infos),
         "fills_per_layer": sum(i["q"] for i in infos) / len(infos),
