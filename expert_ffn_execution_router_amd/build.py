@@ -16,6 +16,8 @@ BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
 
 HIP_SOURCES = ["route.hip", "gemm_dec.hip", "gemm_pf.hip", "combine.hip", "slots.hip"]
+# Per-source code-generation options (none at present).
+HIP_EXTRA = {}
 HIP_FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
              "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
              "-I" + CSRC, "-I" + os.path.join(ROOT, "include")]
@@ -40,7 +42,7 @@ def build(jobs: int = 8) -> str:
     for src in HIP_SOURCES:
         obj = os.path.join(BUILD, src.replace(".hip", ".o"))
         objs.append(obj)
-        procs.append(["hipcc", *HIP_FLAGS, "-c", os.path.join(CSRC, src), "-o", obj])
+        procs.append(["hipcc", *HIP_FLAGS, *HIP_EXTRA.get(src, []), "-c", os.path.join(CSRC, src), "-o", obj])
     api_obj = os.path.join(BUILD, "api.o")
     objs.append(api_obj)
     procs.append(["hipcc", *HIP_FLAGS, "-c", os.path.join(CSRC, "api.cpp"), "-o", api_obj])

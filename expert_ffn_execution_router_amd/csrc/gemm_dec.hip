@@ -492,21 +492,22 @@ gemm_dec(const WorkList* __restrict__ wl, const int32_t* __restrict__ counts, co
     }
   };
 
-  // Stores share the memory counter with the loads.  A finished item's
-  // outputs are stored at the start of the next iteration, before that
-  // iteration's loads, and the following wait allows for them (one store
-  // per 16-token sub-tile holding a token); the partial tiles of the (at
-  // most two) items cut by the range boundaries are kept in registers and
-  // stored after the stream.
+  // Stores share the memory counter with the loads and may complete before
+  // loads issued earlier, so a counter wait is only trusted when everything
+  // it leaves outstanding is a load issued after what it must cover.  A
+  // finished item's outputs are therefore stored at the start of the next
+  // iteration, ahead of that iteration's loads (a compiler and scheduling
+  // barrier keeps them there), and the partial tiles of the (at most two)
+  // items cut by the range boundaries are kept in registers and stored after
+  // the stream.
   f32x4_t pend[NS], first_part[C::NACC], last_part[C::NACC];
   Item pit{};
   bool has_pend = false, has_first = false, has_last = false;
   int last_i = 0;
-  auto flush = [&]() -> int {
-    if (!has_pend) return 0;
+  auto flush = [&]() {
+    if (!has_pend) return;
     has_pend = false;
     store_out<FMT, GATED, NS>(pend, pit, wave, lane, N, out);
-    return min(NS, (pit.nrows + 15) >> 4);
   };
   auto finish_item = [&](int i) {
     if ((long)i * KC >= u0 && (long)(i + 1) * KC <= u1) {
@@ -530,21 +531,16 @@ gemm_dec(const WorkList* __restrict__ wl, const int32_t* __restrict__ counts, co
 #pragma unroll
   for (int s = 0; s < NST - 1; ++s)
     if (s < n) issue(s);
-  int st = 0, i = i_first, kc = kc_first, nst = 0;
+  int st = 0, i = i_first, kc = kc_first;
   for (int v = 0; v < n; ++v) {
-    // this wave's loads of unit v have landed (nst stores were issued after them)
-    if (v + NST - 2 < n) {
-      constexpr int W0 = C::NI * (NST - 2);
-      if (nst == 0) wait_vmcnt<W0>();
-      else if (nst == 1) wait_vmcnt<W0 + 1>();
-      else if (nst == 2) wait_vmcnt<W0 + 2>();
-      else if (nst == 3) wait_vmcnt<W0 + 3>();
-      else wait_vmcnt<W0 + 4>();
-    } else {
-      wait_vmcnt<0>();
-    }
+    // this wave's loads of unit v have landed: what may still be outstanding
+    // is the NI loads of unit v+1, all issued after everything else
+    if (v + NST - 2 < n) wait_vmcnt<C::NI * (NST - 2)>();
+    else wait_vmcnt<0>();
     barrier_keep_loads();                                   // everyone's have; the oldest stage is free
-    nst = flush();
+    flush();
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);                // the stores stay ahead of the next loads
+    __builtin_amdgcn_sched_barrier(0);
     if (v + NST - 1 < n) issue(st == 0 ? NST - 1 : st - 1);
     if (kc == KC) {
       kc = 0;
