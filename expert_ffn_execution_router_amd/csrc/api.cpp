@@ -106,7 +106,7 @@ WsLayout ws_layout(const moe_config& c) {
   L.ids = take(R * 4);
   L.w = take(R * 4);
   L.pos = take(R * 4);
-  L.perm_tok = take(R * 4 + 256 * 4);      // + one tile of slack: the prefill GEMM reads 16-entry blocks
+  L.perm_tok = take((R + moe_pf_tile_tokens()) * 4);   // + one tile of slack: the prefill GEMM reads whole blocks
   L.counts = take((size_t)c.E * 4);
   L.offsets = take((size_t)(c.E + 1) * 4);
   L.hist = take(((Tm + 255) / 256) * c.E * 4);

@@ -6,9 +6,13 @@
 // tokens routed to it; SwiGLU expert), but here each expert sees hundreds of
 // tokens, so the contraction is MFMA-bound and both operands are reused
 // through LDS:
-//   * work item = (expert, 256-token m-tile, 256 weight rows); for GEMM 1 the
-//     256 rows are 128 gate and 128 up rows of the same 128 features,
-//     arranged so that each wave holds gate and up of the same 32 features;
+//   * work item = (expert, m-tile of up to 288 tokens, 256 weight rows); an
+//     expert's c tokens are cut into ceil(c/288) m-tiles of equal size (the
+//     weight tiles are streamed once per m-tile, so fewer, fuller m-tiles
+//     mean fewer bytes: c = 540 gives two tiles of 270, not 256+256+28); for
+//     GEMM 1 the 256 rows are 128 gate and 128 up rows of the same 128
+//     features, arranged so that each wave holds gate and up of the same 32
+//     features;
 //   * items are ordered expert, then weight tile, then m-tile (the m-tiles
 //     sharing a weight tile are neighbours); each XCD (workgroup b runs on
 //     XCD b mod 8) takes one eighth of the list and deals it round-robin to
@@ -16,10 +20,10 @@
 //     and share their weight and token tiles in its L2;
 //   * one workgroup of 8 waves per CU (two per SIMD, so one wave's LDS waits
 //     are covered by the other's MFMAs), in a 2 (tokens) x 4 (weight rows)
-//     grid, each computing 64 weight rows x 128 tokens with
-//     v_mfma_f32_16x16x32_bf16 (weights as the A operand, tokens as B): 64
-//     MFMAs per 64-deep K chunk, 128 accumulators per lane;
-//   * K advances in chunks of 64 through two 64 KiB LDS stages filled by
+//     grid, each computing 64 weight rows x 144 tokens with
+//     v_mfma_f32_16x16x32_bf16 (weights as the A operand, tokens as B): 72
+//     MFMAs per 64-deep K chunk, 144 accumulators per lane;
+//   * K advances in chunks of 64 through two 68 KiB LDS stages filled by
 //     direct global->LDS loads (global_load_lds_dwordx4: lane l's 16 bytes
 //     land at the instruction's LDS base + 16*l), chunk c+1 in flight while
 //     chunk c is multiplied; the stream runs on across item boundaries, so an
@@ -32,24 +36,28 @@
 //     ((row / 2) mod 8), so the operand reads of 16 consecutive rows cover all
 //     64 banks; the loads pick their source piece so that this layout comes
 //     out of the lane-linear placement;
-//   * padding rows of a ragged m-tile are loaded clamped to a real row (every
-//     chunk issues the same number of loads) and their results are not
-//     stored; a wave whose 128-token half holds no routed token skips its
-//     MFMAs;
+//   * 8-row blocks of an m-tile that hold no routed token are not loaded
+//     (their stale LDS rows only feed result columns that are not stored),
+//     padding rows of a partly filled block are loaded clamped to a real row,
+//     and a wave whose 144-token half holds no routed token skips its MFMAs;
 //   * the grid is persistent over the device work list, so the host never
 //     reads the routing.
 #include "common.h"
 
 namespace {
 
-constexpr int PF_BM = 256;    // tokens per tile
+constexpr int PF_BM = 288;    // most tokens per tile (two halves of 144)
+constexpr int PF_HALF = PF_BM / 2;
+constexpr int PF_SUB = PF_HALF / 16;                  // 16-token sub-tiles per half (9)
 constexpr int PF_BN = 256;    // weight rows per tile
 constexpr int PF_BK = 64;     // K per chunk
 constexpr int PF_ROWB = PF_BK * 2;                    // bytes per LDS row (128)
-constexpr int PF_STAGE = (PF_BM + PF_BN) * PF_ROWB;    // 64 KiB per stage
+constexpr int PF_STAGE = (PF_BM + PF_BN) * PF_ROWB;    // 68 KiB per stage
 constexpr int PF_NSTAGE = 2;
 constexpr int PF_WAVES = 8;
-constexpr int PF_LOADS = (PF_BM + PF_BN) / 8 / PF_WAVES;    // 1 KiB loads of 8 rows per wave per chunk (8)
+constexpr int PF_TLOADS = PF_BM / 8 / (PF_WAVES / 2);   // 8-row token blocks per loading wave (9)
+constexpr int PF_WLOADS = PF_BN / 8 / (PF_WAVES / 2);   // 8-row weight blocks per loading wave (8)
+constexpr int PF_LOADS = PF_TLOADS > PF_WLOADS ? PF_TLOADS : PF_WLOADS;
 constexpr int N_XCD = 8;
 
 // byte offset of (row, 16-byte piece) in a stage
@@ -65,6 +73,8 @@ struct PfItem {
 // and up at woff1 ([N, K] each).  Otherwise out = Z (bf16 [rows, N]) with
 // weights at woff0 ([N, K]).  X rows are gathered through row_tok (GEMM 1) or
 // taken in grouped order.  K % 64 == 0; N % 128 (gated) or 256 (not gated).
+// row_tok is read in 8-entry blocks up to 287 entries past a tile's first
+// row, so it must hold 288 entries of slack after the last routed row.
 template <bool GATED>
 __global__ void __launch_bounds__(64 * PF_WAVES, 1)
 gemm_pf_bf16(const WorkList* __restrict__ wl, const int32_t* __restrict__ counts,
@@ -75,7 +85,7 @@ gemm_pf_bf16(const WorkList* __restrict__ wl, const int32_t* __restrict__ counts
   __shared__ int l_pref[257], l_slot[256], l_row0[256], l_cnt[256];
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
   const int lr = lane & 15, lg = lane >> 4;
-  const int wm = wave & 1;        // token half (128 tokens)
+  const int wm = wave & 1;        // token half (144 tokens)
   const int wn = wave >> 1;       // weight-row quarter (64 rows)
 
   const int n_act = wl->n_act;
@@ -118,37 +128,43 @@ gemm_pf_bf16(const WorkList* __restrict__ wl, const int32_t* __restrict__ counts
     const int pre = l_pref[a], nm = l_pref[a + 1] - pre;
     const int q = it - pre * ntiles;
     const int nt = q / nm, mt = q - nt * nm;
+    // nm = ceil(c / 288) tiles of ts = ceil(c / nm) <= 288 tokens; the last
+    // one is not empty, since (nm - 1) * ts < c while c / nm > nm
+    const int c = l_cnt[a], ts = (c + nm - 1) / nm;
     o.slot = __builtin_amdgcn_readfirstlane(l_slot[a]);
-    o.row0 = __builtin_amdgcn_readfirstlane(l_row0[a] + mt * PF_BM);
-    o.nrows = __builtin_amdgcn_readfirstlane(min(PF_BM, l_cnt[a] - mt * PF_BM));
+    o.row0 = __builtin_amdgcn_readfirstlane(l_row0[a] + mt * ts);
+    o.nrows = __builtin_amdgcn_readfirstlane(min(ts, c - mt * ts));
     o.f0 = __builtin_amdgcn_readfirstlane(nt * feat);
   };
 
-  // ---- loads: this wave's 8 blocks of 8 stage rows ------------------------
-  // stage rows 0..255 are tokens, 256..511 weights; block q of the wave
-  // covers rows (8*wave + q)*8 ..+7; lane l writes row r = 8*(8*wave + q) +
-  // l/8, physical piece (l&7), so it fetches logical piece (l&7) ^ ((r/2)&7),
-  // where (r/2)&7 = 4*(q&1) + (l/8)/2 (waves 0-3 load token rows, waves 4-7
-  // weight rows; byte offsets from a uniform base: X, or the slot's blob)
+  // ---- loads: blocks of 8 stage rows, 1 KiB each ----------------------------
+  // stage rows 0..287 are tokens, 288..543 weights.  Waves 0-3 load token
+  // blocks 9*wave + q (q < 9), waves 4-7 weight blocks 8*(wave-4) + q (q < 8).
+  // Lane l writes row (l/8) of its block, physical piece (l&7), so it fetches
+  // logical piece (l&7) ^ ((row/2)&7) of that row.  Byte offsets are 32-bit,
+  // from a uniform base: X, or the slot's blob.
   const int brow = lane >> 3;
-  const int bpiece = (lane & 7) ^ (brow >> 1);           // even q; odd q: bpiece ^ 4
   const bool wtok = wave < PF_WAVES / 2;
+  const int blk0 = wtok ? wave * PF_TLOADS : PF_BM / 8 + (wave - PF_WAVES / 2) * PF_WLOADS;
   uint32_t src[PF_LOADS];
+  int tok_blocks = 0;                         // token blocks holding a routed token
   const uint8_t* sbase = (const uint8_t*)X;
   auto set_sources = [&](const PfItem& t) {
     sbase = wtok ? (const uint8_t*)X : pool + (size_t)t.slot * S;
+    tok_blocks = (t.nrows + 7) >> 3;
 #pragma unroll
     for (int q = 0; q < PF_LOADS; ++q) {
-      const int r = (wave * PF_LOADS + q) * 8 + brow;
+      const int srow = (blk0 + q) * 8 + brow;                     // stage row
+      const int piece = (lane & 7) ^ ((srow >> 1) & 7);
       if (wtok) {
-        const int rr = min(r, t.nrows - 1);                       // ragged tail: clamped, masked at store
-        int xrow = t.row0 + rr;
+        const int r = srow;                                       // token row of the tile
+        int xrow = t.row0 + min(r, t.nrows - 1);                  // padding: clamped, not stored
         if (row_tok) {
           // the block's 8 entries by scalar loads (they do not count on the
           // vector-memory counter the stream waits on), then a per-lane pick;
           // entries past the expert's rows are read but not used (the
           // workspace continues after the permutation)
-          const int r0 = (wave * PF_LOADS + q) * 8;
+          const int r0 = (blk0 + q) * 8;
           const int* rp = row_tok + __builtin_amdgcn_readfirstlane(t.row0 + r0);
           int v = __builtin_amdgcn_readfirstlane(row_tok[__builtin_amdgcn_readfirstlane(t.row0 + t.nrows - 1)]);
 #pragma unroll
@@ -158,17 +174,16 @@ gemm_pf_bf16(const WorkList* __restrict__ wl, const int32_t* __restrict__ counts
           }
           xrow = v;
         }
-        src[q] = (uint32_t)xrow * (uint32_t)(K * 2) + (bpiece ^ ((q & 1) << 2)) * 16;
-      } else {
-        const int wr = r - PF_BM;                                 // weight tile row 0..255
+        src[q] = (uint32_t)xrow * (uint32_t)(K * 2) + piece * 16;
+      } else if (q < PF_WLOADS) {
+        const int wr = srow - PF_BM;                              // weight tile row 0..255
         if (GATED) {
           // tile rows [64*h + 32*g + j]: h = weight quarter (wave column),
           // g = 0 gate / 1 up, feature f0 + 32*h + j
           const int h = wr >> 6, g = (wr >> 5) & 1, j = wr & 31;
-          src[q] = (uint32_t)((g ? woff1 : woff0) + (size_t)(t.f0 + h * 32 + j) * K * 2) +
-                   (bpiece ^ ((q & 1) << 2)) * 16;
+          src[q] = (uint32_t)((g ? woff1 : woff0) + (size_t)(t.f0 + h * 32 + j) * K * 2) + piece * 16;
         } else {
-          src[q] = (uint32_t)(woff0 + (size_t)(t.f0 + wr) * K * 2) + (bpiece ^ ((q & 1) << 2)) * 16;
+          src[q] = (uint32_t)(woff0 + (size_t)(t.f0 + wr) * K * 2) + piece * 16;
         }
       }
     }
@@ -190,32 +205,37 @@ gemm_pf_bf16(const WorkList* __restrict__ wl, const int32_t* __restrict__ counts
     }
     const uint8_t* base = sbase + iss_c * (PF_BK * 2);
     ++iss_c;
+    lds_u8_t* dst = (lds_u8_t*)lds + stage * PF_STAGE + blk0 * 1024;
+    if (wtok) {
 #pragma unroll
-    for (int q = 0; q < PF_LOADS; ++q)
-      __builtin_amdgcn_global_load_lds((gbl_void_t*)(base + src[q]),
-                                       (lds_void_t*)((lds_u8_t*)lds + stage * PF_STAGE +
-                                                     (wave * PF_LOADS + q) * 1024),
-                                       16, 0, 0);
+      for (int q = 0; q < PF_TLOADS; ++q)
+        if (blk0 + q < tok_blocks)            // blocks past the tile's rows are skipped
+          __builtin_amdgcn_global_load_lds((gbl_void_t*)(base + src[q]), (lds_void_t*)(dst + q * 1024), 16, 0, 0);
+    } else {
+#pragma unroll
+      for (int q = 0; q < PF_WLOADS; ++q)
+        __builtin_amdgcn_global_load_lds((gbl_void_t*)(base + src[q]), (lds_void_t*)(dst + q * 1024), 16, 0, 0);
+    }
   };
 
   // operand read offsets inside a stage (K steps 0 and 1 of the chunk): the
   // swizzle of row 16*j + lr depends on lr only, so sub-tile j is a constant
   // 2 KiB step
-  const int xoff[2] = {swz(wm * 128 + lr, lg), swz(wm * 128 + lr, 4 + lg)};
+  const int xoff[2] = {swz(wm * PF_HALF + lr, lg), swz(wm * PF_HALF + lr, 4 + lg)};
   const int woff[2] = {swz(PF_BM + wn * 64 + lr, lg), swz(PF_BM + wn * 64 + lr, 4 + lg)};
 
-  f32x4_t acc[4][8];
+  f32x4_t acc[4][PF_SUB];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int j = 0; j < 8; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+    for (int j = 0; j < PF_SUB; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
   // epilogue: lane holds weight rows 4*lg..+3 of each 16-row sub-tile i for
   // token column lr of each 16-token sub-tile j
   auto store_item = [&](const PfItem& t) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const int r = wm * 128 + j * 16 + lr;
+    for (int j = 0; j < PF_SUB; ++j) {
+      const int r = wm * PF_HALF + j * 16 + lr;
       if (r >= t.nrows) continue;
       uint16_t* orow = out + (size_t)(t.row0 + r) * N;
       if (GATED) {
@@ -268,23 +288,25 @@ gemm_pf_bf16(const WorkList* __restrict__ wl, const int32_t* __restrict__ counts
 #pragma unroll
       for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int j = 0; j < 8; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+        for (int j = 0; j < PF_SUB; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       pending = false;
     }
     if (v + PF_NSTAGE - 1 < n_units) issue(stage == 0 ? PF_NSTAGE - 1 : stage - 1);
     const uint8_t* cur = lds + stage * PF_STAGE;
-    if (ct.nrows > wm * 128) {                  // this wave's token half holds a routed token
+    if (ct.nrows > wm * PF_HALF) {              // this wave's token half holds a routed token
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
-        bf16x8_t bx[8];
+        bf16x8_t bx[PF_SUB], aw[4];
 #pragma unroll
-        for (int j = 0; j < 8; ++j) bx[j] = __builtin_bit_cast(bf16x8_t, *(const i32x4_t*)(cur + xoff[ks] + j * 2048));
+        for (int j = 0; j < PF_SUB; ++j)
+          bx[j] = __builtin_bit_cast(bf16x8_t, *(const i32x4_t*)(cur + xoff[ks] + j * 2048));
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const bf16x8_t aw = __builtin_bit_cast(bf16x8_t, *(const i32x4_t*)(cur + woff[ks] + i * 2048));
+        for (int i = 0; i < 4; ++i) aw[i] = __builtin_bit_cast(bf16x8_t, *(const i32x4_t*)(cur + woff[ks] + i * 2048));
 #pragma unroll
-          for (int j = 0; j < 8; ++j) acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw, bx[j], acc[i][j], 0, 0, 0);
-        }
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < PF_SUB; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(aw[i], bx[j], acc[i][j], 0, 0, 0);
       }
     }
     stage = stage + 1 == PF_NSTAGE ? 0 : stage + 1;

@@ -101,3 +101,56 @@ def test_host_partial_is_added_exactly(setups):
                  host_partial=torch.from_numpy(hp).cuda())
     torch.cuda.synchronize()
     compare(s, 0, x, out)
+
+
+def _bf16_bits(x32: np.ndarray) -> np.ndarray:
+    """fp32 -> bf16 bit patterns, round to nearest even (finite inputs)."""
+    u = x32.astype(np.float32).view(np.uint32).astype(np.uint64)
+    return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
+
+
+# Expert token counts at the edges of the large-batch kernel's m-tiling: an
+# expert's c tokens are cut into ceil(c/288) equal tiles of at most 288
+# (two halves of 144): one full tile, one token over it, two full tiles, one
+# over those, a single token, a ragged small tile, four tiles, and an expert
+# nobody routes to.
+EDGE_COUNTS = [288, 289, 576, 577, 1, 17, 900, 0]
+
+
+def test_tiled_forward_tile_edges():
+    """Routing forced to EDGE_COUNTS by a one-hot router: token t's hidden row
+    holds 4 at its first expert's dimension and 3 at its second's (noise
+    elsewhere), the router reads dimension e for expert e."""
+    cfg = shape(1)                                   # E=8, k=2, H=256, I=128, bf16
+    E, k, H = cfg.E, cfg.k, cfg.H
+    slots = np.repeat(np.arange(E), EDGE_COUNTS)
+    T = len(slots) // k
+    assert T * k == len(slots) and T > 64 and T * k >= 48 * E   # the tiled kernels run
+    first, second = slots[:T], slots[T:]
+    assert np.all(first != second)
+    rng = np.random.default_rng(7)
+    x32 = rng.normal(0.0, 0.05, size=(T, H)).astype(np.float32)
+    x32[np.arange(T), first] = 4.0
+    x32[np.arange(T), second] = 3.0
+    bits = _bf16_bits(x32)
+    R = np.zeros((E, H), np.float32)
+    R[np.arange(E), np.arange(E)] = 1.0
+    # the construction routes exactly as intended
+    xf = (bits.astype(np.uint32) << 16).view(np.float32)
+    top = np.argsort(-(xf @ R.T), axis=1, kind="stable")[:, :k]
+    assert np.array_equal(np.bincount(top.ravel(), minlength=E), np.array(EDGE_COUNTS))
+
+    s = Setup(cfg, seed=5, max_tokens=T)
+    try:
+        s.admit_all(0)
+        s.R[0], s.b[0] = R, None
+        xd = torch.from_numpy(bits.view(np.int16)).cuda()
+        out = torch.empty(T, H, dtype=torch.bfloat16, device="cuda")
+        s.rt.forward(0, xd, torch.from_numpy(R).cuda(), None, s.slot_row(0), out)
+        torch.cuda.synchronize()
+        assert s.rt.check_device_error() == 0
+        e_m, e_x, n = compare(s, 0, bits, out)
+        assert n == T
+        print(f"tile edges: err vs mirrored {e_m:.2e}, vs exact {e_x:.2e}")
+    finally:
+        s.close()
