@@ -37,6 +37,8 @@ def log(*a):
 METRIC = "MoE-layer tokens/s (decode T≤64, prefill 8k); % HBM BW / % MFMA peak"
 HBM_PEAK = 8.0e12
 BF16_PEAK = 2.5e15
+FP8_PEAK = 5.0e15
+FP4_PEAK = 10.1e15
 ROOT = os.path.dirname(os.path.abspath(__file__))
 
 
@@ -60,6 +62,8 @@ def parse():
     ap.add_argument("--cpu-layers", type=int, default=3)
     ap.add_argument("--host-threads", type=int, default=16)
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of one graph per step")
+    ap.add_argument("--format-layers", type=int, default=4,
+                    help="layers of the fp8 and MXFP4 pools in the formats phase")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only copy 1 GiB device->device 3 times (calibrates HBM byte counters)")
     a = ap.parse_args()
@@ -354,6 +358,106 @@ def phase_prefill(w: Workload):
     return res
 
 
+def phase_formats(args):
+    """The fp8 (43-layer E=256 top-6 H=4096 I=2048 shape) and MXFP4 (16-layer
+    E=256 top-8 H=6144 I=2048 shape) paths with every expert resident:
+    decode steps at the small token counts, and one prefill-shaped batch per
+    layer.  Layers are cut to --format-layers so the pools fit host memory;
+    per-layer work is unchanged."""
+    import torch
+    import synth
+    from expert_ffn_execution_router_amd.runtime import HostPool, MoeRuntime
+    out = {}
+    dev = torch.device("cuda:0")
+    for cid, dec_T, pf_T, pf_bound in ((4, (1, 32), 4096, "hbm"), (5, (1,), 16384, "mfma")):
+        c = synth.CONFIGS[cid].with_layers(args.format_layers)
+        L, E, k, H, I, S = c.L, c.E, c.k, c.H, c.I, c.expert_bytes
+        name = {4: "fp8_e4m3_b128", 5: "mxfp4"}[cid]
+        pool = HostPool(L * E * S)
+        synth.fill_pool(pool.ptr, c, args.seed)
+        R = [torch.from_numpy(synth.router_weights(c, args.seed, l)).to(dev) for l in range(L)]
+        bias = [None if b is None else torch.from_numpy(b).to(dev)
+                for b in (synth.router_bias(c, args.seed, l) for l in range(L))]
+        rt = MoeRuntime(L, E, k, H, I, c.fmt, L * E, max(max(dec_T), pf_T), pool, host_threads=args.host_threads)
+        for l in range(L):
+            rt.admit(l, list(range(E)))
+        torch.cuda.synchronize()
+        table = rt.slot_table()
+        rows = [table[l * E:(l + 1) * E] for l in range(L)]
+        res = {"workload": f"{name}: E={E} top-{k} H={H} I={I}, {L} layers resident", "expert_bytes": S}
+        wgu = 2 * S / 3                          # gate + up bytes of one expert (scales included)
+        for T in dec_T:
+            K, W = 16, 4
+            keys = synth.decode_row_keys(c, args.seed, W + K, T)
+            hid = torch.from_numpy(synth.hidden_rows(c, keys.reshape(-1)).reshape(W + K, L, T, H).view(np.int16)).to(dev)
+            o = torch.empty(T, H, dtype=torch.bfloat16, device=dev)
+            ids = torch.empty(T, k, dtype=torch.int32, device=dev)
+            wts = torch.empty(T, k, dtype=torch.float32, device=dev)
+            n_active = np.zeros((K, L))
+            for s in range(K):
+                for l in range(L):
+                    rt.route(hid[W + s, l], R[l], bias[l], ids, wts)
+                    n_active[s, l] = len(torch.unique(ids).cpu())
+            for s in range(W):
+                for l in range(L):
+                    rt.forward(l, hid[s, l], R[l], bias[l], rows[l], o)
+            torch.cuda.synchronize()
+            rt.profile_begin(K * L * 12 + 16)
+            for s in range(K):
+                for l in range(L):
+                    rt.forward(l, hid[W + s, l], R[l], bias[l], rows[l], o)
+            prof = rt.profile_end()
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            for s in range(K):
+                for l in range(L):
+                    rt.forward(l, hid[W + s, l], R[l], bias[l], rows[l], o)
+            torch.cuda.synchronize()
+            wall = (time.perf_counter() - t0) / (K * L)
+            assert rt.check_device_error() == 0
+            st = {n: v["ms"] / v["launches"] * 1e3 for n, v in prof.items() if isinstance(v, dict) and v["launches"]}
+            g1_bytes = float(n_active.mean() * wgu + T * k * H + T * k * I * 4)
+            layer_bytes = float(n_active.mean() * S + E * H * 4 + 2 * T * H * 2)
+            gpu_us = sum(st.values())
+            res[f"decode_T{T}"] = {
+                "tokens_per_s_eager": T / wall, "layer_wall_us": wall * 1e6, "gpu_layer_us": gpu_us,
+                "stage_us": st, "mean_active_experts": float(n_active.mean()),
+                "gemm1_GBps": g1_bytes / (st["gemm1"] * 1e-6) / 1e9,
+                "gemm1_hbm_frac": g1_bytes / (st["gemm1"] * 1e-6) / HBM_PEAK,
+                "layer_hbm_frac_of_gpu_time": layer_bytes / (gpu_us * 1e-6) / HBM_PEAK,
+            }
+            log(f"{name} decode T={T}: {json.dumps(res[f'decode_T{T}'])}")
+            del hid
+        # prefill-shaped batch: one forward per layer
+        hp = torch.from_numpy(synth.hidden(c, args.seed, pf_T, 7).view(np.int16)).to(dev)
+        op = torch.empty(pf_T, H, dtype=torch.bfloat16, device=dev)
+        rt.forward(0, hp, R[0], bias[0], rows[0], op)
+        torch.cuda.synchronize()
+        rt.profile_begin(L * 12 + 16)
+        for l in range(L):
+            rt.forward(l, hp, R[l], bias[l], rows[l], op)
+        prof = rt.profile_end()
+        torch.cuda.synchronize()
+        assert rt.check_device_error() == 0
+        st = {n: v["ms"] / v["launches"] * 1e3 for n, v in prof.items() if isinstance(v, dict) and v["launches"]}
+        gemm_us = st["gemm1"] + st["gemm2"] + st.get("fixup", 0.0) * 2
+        flops = 6.0 * pf_T * k * H * I
+        peak = {4: FP8_PEAK, 5: FP4_PEAK}[cid]
+        res[f"prefill_T{pf_T}"] = {
+            "bound": pf_bound, "gemm_us": gemm_us, "gpu_layer_us": sum(st.values()), "stage_us": st,
+            "weights_hbm_frac": E * S / (gemm_us * 1e-6) / HBM_PEAK,
+            "mfma_frac": flops / (gemm_us * 1e-6) / peak, "mfma_peak_TFLOPs": peak / 1e12,
+            "kernel": "gemm_dec (small-batch streaming GEMM; no tiled kernel for this format yet)",
+        }
+        log(f"{name} prefill T={pf_T}: {json.dumps(res[f'prefill_T{pf_T}'])}")
+        out[name] = res
+        rt.close()
+        del rt, hp, op
+        torch.cuda.empty_cache()
+        pool.free()
+    return out
+
+
 def phase_cpu(w: Workload):
     """The float64 oracle on a bounded sample of the decode workload."""
     from threadpoolctl import threadpool_info
@@ -399,8 +503,9 @@ def main():
     B.lib()   # fail loudly when the library is missing
     synth.lib()
     torch.cuda.init()
-    w = Workload(args)
-    c = w.cfg
+    needs_w = bool(args.phase_set & {"decode", "e2e", "prefill", "cpu"})
+    w = Workload(args) if needs_w else None
+    c = w.cfg if needs_w else synth.CONFIGS[2].with_layers(args.layers)
     line = {
         "metric": METRIC, "value": None, "unit": "MoE-layer tokens/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": None, "higher_is_better": True, "scaling": "weak",
@@ -422,8 +527,11 @@ def main():
         line["prefill_chunk"] = phase_prefill(w)
     if "cpu" in args.phase_set:
         line["cpu_baseline"] = phase_cpu(w)
+    if "formats" in args.phase_set:
+        line["formats_resident"] = phase_formats(args)
     print(json.dumps(line), flush=True)
-    w.pool.free()
+    if w is not None:
+        w.pool.free()
 
 
 if __name__ == "__main__":
