@@ -71,6 +71,7 @@ SIGNATURES = {
     "moe_reset_cache": (_i, [_vp, _vp]),
     "moe_route": (_i, [_vp, _vp, _vp, _vp, _i, _vp, _vp, _vp]),
     "moe_route_from_logits": (_i, [_vp, _vp, _i, _vp, _vp, _vp, _vp, _vp, _vp, _vp]),
+    "moe_quantize": (_i, [_i, _i, _vp, _i, _i, _vp, _vp, _vp, _vp]),
     "moe_plan": (_i, [_vp, _i, _vp, _i, _vp, _P(moe_plan_info), _vp, _vp, _vp]),
     "slot_pool_fill": (_i, [_vp, _i, _vp, _vp, _i, _vp]),
     "slot_pool_admit": (_i, [_vp, _i, _vp, _i, _vp]),
@@ -140,6 +141,7 @@ moe_slot_table = _fn("moe_slot_table")
 moe_reset_cache = _fn("moe_reset_cache")
 moe_route = _fn("moe_route")
 moe_route_from_logits = _fn("moe_route_from_logits")
+moe_quantize = _fn("moe_quantize")
 moe_plan = _fn("moe_plan")
 slot_pool_fill = _fn("slot_pool_fill")
 slot_pool_admit = _fn("slot_pool_admit")

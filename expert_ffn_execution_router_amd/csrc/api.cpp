@@ -534,6 +534,19 @@ int moe_route(moe_ctx* c, const void* hidden, const float* R, const float* bias,
   return MOE_OK;
 }
 
+int moe_quantize(int wfmt, int src_bf16, const void* src, int rows, int cols, const int32_t* row_map, uint8_t* q,
+                 void* scale, void* stream) {
+  if (wfmt != MOE_W_FP8_E4M3_B128 && wfmt != MOE_W_MXFP4) return fail(nullptr, MOE_E_INVAL, "format has no quantisation");
+  if (rows < 0 || cols <= 0 || cols % (wfmt == MOE_W_FP8_E4M3_B128 ? 128 : 32))
+    return fail(nullptr, MOE_E_INVAL, "bad shape");
+  if (rows == 0) return MOE_OK;
+  if (!src || !q || !scale) return fail(nullptr, MOE_E_INVAL, "null argument");
+  hipError_t e = moe_launch_quant(wfmt, src_bf16 ? 1 : 0, src, rows, nullptr, row_map, cols, q, scale,
+                                  as_stream(stream));
+  if (e != hipSuccess) return fail(nullptr, MOE_E_HIP, hipGetErrorString(e));
+  return MOE_OK;
+}
+
 int moe_route_from_logits(moe_ctx* c, const float* logits, int T, int32_t* topk_ids, float* topk_w, int32_t* counts,
                           int32_t* offsets, int32_t* perm_tok, int32_t* pos, void* stream) {
   if (!c) return fail(nullptr, MOE_E_INVAL, "null ctx");

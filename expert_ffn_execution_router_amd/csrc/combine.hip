@@ -65,60 +65,96 @@ combine_kernel(const uint16_t* __restrict__ Z, const int32_t* __restrict__ ids, 
   *(i32x4_t*)(out + (size_t)t * H + h) = o;
 }
 
+// 16 consecutive source values of one row as fp32 (bf16: two 16-byte loads;
+// fp32: four).
 template <bool SRC_BF16>
-DEV float load_src(const void* src, size_t i) {
-  if (SRC_BF16) return bf16_bits_to_f32(((const uint16_t*)src)[i]);
-  return ((const float*)src)[i];
+DEV void load16(const void* src, size_t i, float (&v)[16]) {
+  if (SRC_BF16) {
+    const i32x4_t a = ld16((const uint16_t*)src + i), b = ld16((const uint16_t*)src + i + 8);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      v[2 * k] = bf16_bits_to_f32((uint32_t)a[k] & 0xffffu);
+      v[2 * k + 1] = bf16_bits_to_f32((uint32_t)a[k] >> 16);
+      v[8 + 2 * k] = bf16_bits_to_f32((uint32_t)b[k] & 0xffffu);
+      v[8 + 2 * k + 1] = bf16_bits_to_f32((uint32_t)b[k] >> 16);
+    }
+  } else {
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const i32x4_t a = ld16((const float*)src + i + 4 * k);
+#pragma unroll
+      for (int m = 0; m < 4; ++m) v[4 * k + m] = __int_as_float(a[m]);
+    }
+  }
 }
 
-// One wave per (row, 128-column group); rows from *nrows_dev when given.
-// Output row r quantises source row row_map[r] (r itself without a map).
+// 16 E4M3 codes packed little-endian into 16 bytes.
+DEV i32x4_t pack_e4m3x16(const float (&v)[16], float mul) {
+  i32x4_t o;
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    o[k] = (int)(f32_to_e4m3(v[4 * k] * mul) | (f32_to_e4m3(v[4 * k + 1] * mul) << 8) |
+                 (f32_to_e4m3(v[4 * k + 2] * mul) << 16) | (f32_to_e4m3(v[4 * k + 3] * mul) << 24));
+  return o;
+}
+
+// One thread per (row, 16 columns); the 8 threads of a 128-column group are
+// consecutive lanes.  Rows from *nrows_dev when given.  Output row r
+// quantises source row row_map[r] (r itself without a map).
 template <bool SRC_BF16>
 __global__ void __launch_bounds__(256)
 quant_fp8_kernel(const void* __restrict__ src, int rows, const int32_t* __restrict__ nrows_dev,
                  const int32_t* __restrict__ row_map, int cols, uint8_t* __restrict__ q, float* __restrict__ scale) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int ng = cols / 128;
-  const int g = blockIdx.x * 4 + wave;
+  const long g = (long)blockIdx.x * 256 + threadIdx.x;
+  const int per_row = cols / 16;
   const int nrows = nrows_dev ? *nrows_dev : rows;
-  const int r = g / ng, c0 = (g - r * ng) * 128;
-  if (r >= nrows) return;
-  const size_t sbase = (size_t)(row_map ? row_map[r] : r) * cols + c0 + lane * 2;
-  const size_t base = (size_t)r * cols + c0 + lane * 2;
-  const float v0 = load_src<SRC_BF16>(src, sbase), v1 = load_src<SRC_BF16>(src, sbase + 1);
-  const float amax = wave_max(fmaxf(fabsf(v0), fabsf(v1)));
+  const long r = g / per_row;
+  const int c0 = (int)(g - r * per_row) * 16;
+  if (r >= nrows) return;                     // whole 8-lane groups leave together (cols % 128 == 0)
+  float v[16];
+  load16<SRC_BF16>(src, (size_t)(row_map ? row_map[r] : r) * cols + c0, v);
+  float amax = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 16; ++k) amax = fmaxf(amax, fabsf(v[k]));
+#pragma unroll
+  for (int off = 1; off < 8; off <<= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
   const float inv = amax > 0.0f ? 448.0f / amax : 1.0f;
   const float sc = amax > 0.0f ? amax / 448.0f : 1.0f;
-  const uint32_t q0 = f32_to_e4m3(v0 * inv), q1 = f32_to_e4m3(v1 * inv);
-  *(uint16_t*)(q + base) = (uint16_t)(q0 | (q1 << 8));
-  if (lane == 0) scale[(size_t)r * ng + c0 / 128] = sc;
+  *(i32x4_t*)(q + (size_t)r * cols + c0) = pack_e4m3x16(v, inv);
+  if ((c0 & 127) == 0) scale[(size_t)r * (cols / 128) + c0 / 128] = sc;
 }
 
-// One wave per (row, 64 columns) = two 32-column MX blocks (lanes 0-31, 32-63).
+// One thread per (row, 16 columns); two threads per 32-column MX block.
 template <bool SRC_BF16>
 __global__ void __launch_bounds__(256)
 quant_mxfp8_kernel(const void* __restrict__ src, int rows, const int32_t* __restrict__ nrows_dev,
                    const int32_t* __restrict__ row_map, int cols, uint8_t* __restrict__ q,
                    uint8_t* __restrict__ scale) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int ng = cols / 64;
-  const int g = blockIdx.x * 4 + wave;
+  const long g = (long)blockIdx.x * 256 + threadIdx.x;
+  const int per_row = cols / 16;
   const int nrows = nrows_dev ? *nrows_dev : rows;
-  const int r = g / ng, c0 = (g - r * ng) * 64;
-  if (r >= nrows) return;
-  const size_t i = (size_t)r * cols + c0 + lane;
-  const float v = load_src<SRC_BF16>(src, (size_t)(row_map ? row_map[r] : r) * cols + c0 + lane);
-  float amax = fabsf(v);
+  const long r = g / per_row;
+  const int c0 = (int)(g - r * per_row) * 16;
+  if (r >= nrows) return;                     // lane pairs leave together (cols % 32 == 0)
+  float v[16];
+  load16<SRC_BF16>(src, (size_t)(row_map ? row_map[r] : r) * cols + c0, v);
+  float amax = 0.0f;
 #pragma unroll
-  for (int off = 16; off >= 1; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off, 64));
+  for (int k = 0; k < 16; ++k) amax = fmaxf(amax, fabsf(v[k]));
+  amax = fmaxf(amax, __shfl_xor(amax, 1, 64));
   int x = 0;
   if (amax > 0.0f) {
     int e;
     frexpf(amax, &e);                    // amax = m * 2^e, m in [0.5, 1)
     x = min(127, max(-127, (e - 1) - 8));
   }
-  q[i] = (uint8_t)f32_to_e4m3(ldexpf(v, -x));
-  if ((lane & 31) == 0) scale[(size_t)r * (cols / 32) + (c0 + lane) / 32] = (uint8_t)(x + 127);
+  // ldexpf(v, -x) is exact scaling by a power of two (no overflow: |v| <
+  // 2^(x+9), and x >= -127 keeps results finite)
+  float w[16];
+#pragma unroll
+  for (int k = 0; k < 16; ++k) w[k] = ldexpf(v[k], -x);
+  *(i32x4_t*)(q + (size_t)r * cols + c0) = pack_e4m3x16(w, 1.0f);
+  if ((c0 & 31) == 0) scale[(size_t)r * (cols / 32) + c0 / 32] = (uint8_t)(x + 127);
 }
 
 extern "C" hipError_t moe_launch_combine(const uint16_t* Z, const int32_t* ids, const float* w, const int32_t* pos,
@@ -133,18 +169,20 @@ extern "C" hipError_t moe_launch_combine(const uint16_t* Z, const int32_t* ids, 
 extern "C" hipError_t moe_launch_quant(int fmt, int src_bf16, const void* src, int rows, const int32_t* nrows_dev,
                                        const int32_t* row_map, int cols, uint8_t* q, void* scale, hipStream_t s) {
   if (rows == 0) return hipSuccess;
+  const long threads = (long)rows * (cols / 16);
+  const unsigned blocks = (unsigned)((threads + 255) / 256);
   if (fmt == WFMT_FP8) {
-    const int groups = rows * (cols / 128);
+    if (cols % 128) return hipErrorInvalidValue;
     if (src_bf16)
-      quant_fp8_kernel<true><<<(groups + 3) / 4, 256, 0, s>>>(src, rows, nrows_dev, row_map, cols, q, (float*)scale);
+      quant_fp8_kernel<true><<<blocks, 256, 0, s>>>(src, rows, nrows_dev, row_map, cols, q, (float*)scale);
     else
-      quant_fp8_kernel<false><<<(groups + 3) / 4, 256, 0, s>>>(src, rows, nrows_dev, row_map, cols, q, (float*)scale);
+      quant_fp8_kernel<false><<<blocks, 256, 0, s>>>(src, rows, nrows_dev, row_map, cols, q, (float*)scale);
   } else {
-    const int groups = rows * (cols / 64);
+    if (cols % 32) return hipErrorInvalidValue;
     if (src_bf16)
-      quant_mxfp8_kernel<true><<<(groups + 3) / 4, 256, 0, s>>>(src, rows, nrows_dev, row_map, cols, q, (uint8_t*)scale);
+      quant_mxfp8_kernel<true><<<blocks, 256, 0, s>>>(src, rows, nrows_dev, row_map, cols, q, (uint8_t*)scale);
     else
-      quant_mxfp8_kernel<false><<<(groups + 3) / 4, 256, 0, s>>>(src, rows, nrows_dev, row_map, cols, q, (uint8_t*)scale);
+      quant_mxfp8_kernel<false><<<blocks, 256, 0, s>>>(src, rows, nrows_dev, row_map, cols, q, (uint8_t*)scale);
   }
   return hipGetLastError();
 }

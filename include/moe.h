@@ -142,6 +142,21 @@ int moe_reset_cache(moe_ctx* ctx, void* stream);
 int moe_route(moe_ctx* ctx, const void* hidden, const float* router_w, const float* router_bias, int T,
               int32_t* topk_ids, float* topk_w, void* stream);
 
+/* Test hook: the activation quantisation that precedes each grouped GEMM
+ * of the 8-bit paths (the pages say only that the kernels dequantise in
+ * kernel; the rule is a declared reading).  rows x cols values (device),
+ * bf16 (src_bf16 = 1) or fp32; output row r quantises source row
+ * row_map[r] (device int32 [rows], or NULL for r itself).
+ *   wfmt 1 (fp8): per (row, 128 columns) scale = amax/448, q = E4M3(v*448/amax);
+ *                 scale fp32 [rows, cols/128]; cols % 128 == 0.
+ *   wfmt 2 (mxfp4 weights, MXFP8 activations): per (row, 32 columns) E8M0
+ *                 scale 2^x, x = floor(log2 amax) - 8, q = E4M3(v*2^-x);
+ *                 scale uint8 [rows, cols/32]; cols % 32 == 0.
+ * q uint8 [rows, cols] (E4M3 codes), caller-owned.  Asynchronous on stream;
+ * MOE_E_INVAL for another format or a bad shape. */
+int moe_quantize(int wfmt, int src_bf16, const void* src, int rows, int cols, const int32_t* row_map, uint8_t* q,
+                 void* scale, void* stream);
+
 /* Same selection from given fp32 logits [T, E] (device), plus the grouping:
  * counts int32 [E], offsets int32 [E+1] (exclusive scan), perm_tok int32 [T*k]
  * (token of each grouped row: experts ascending, tokens ascending within an
