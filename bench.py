@@ -292,6 +292,16 @@ def phase_e2e(w: Workload):
     el = time.perf_counter() - t0
     assert rc.check_device_error() == 0
     uq = sum(i["n_unique"] for i in infos)
+    # per-stage GPU times over the timed steps' rows again (after the timed
+    # region, cache state carried on; not part of the step time)
+    n_rec = len(infos)
+    rc.profile_begin(K * L * 12 + 16)
+    for s in range(K):
+        e2e_step(W + s, False)
+    prof = rc.profile_end()
+    torch.cuda.synchronize()
+    stage_us = {n: v["ms"] / v["launches"] * 1e3 for n, v in prof.items() if isinstance(v, dict) and v["launches"]}
+    del infos[n_rec:]
     res = {
         "note": "PCIe and host included; not the value",
         "T": T, "n_slots": c.n_slots, "policy": "hybrid", "B_P_GBps": bp, "B_H_GBps": bh,
@@ -303,6 +313,7 @@ def phase_e2e(w: Workload):
         "host_per_layer": sum(i["n_host"] for i in infos) / len(infos),
         "t_fill_pred_us_per_layer": sum(i["t_fill_pred_us"] for i in infos) / len(infos),
         "t_host_pred_us_per_layer": sum(i["t_host_pred_us"] for i in infos) / len(infos),
+        "stage_us_per_launch": stage_us,
     }
     log(json.dumps(res))
     rc.close()

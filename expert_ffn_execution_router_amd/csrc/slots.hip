@@ -21,98 +21,138 @@
 
 constexpr int PLAN_MAX_SLOTS = 8192;
 
+// Exclusive rank of this lane's predicate among the block's threads, in
+// thread order (one call per thread of the block; all threads take part).
+// wtot: LDS scratch of one int per wave; returns the block total in *total.
+DEV int block_rank(bool pred, int* wtot, int* total) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  const uint64_t b = __ballot(pred);
+  if (lane == 0) wtot[wave] = __popcll(b);
+  __syncthreads();
+  int off = 0, all = 0;
+  for (int w = 0; w < nw; ++w) {
+    const int c = wtot[w];
+    off += w < wave ? c : 0;
+    all += c;
+  }
+  __syncthreads();                      // wtot may be reused by the next call
+  *total = all;
+  return off + __popcll(b & ((1ull << lane) - 1ull));
+}
+
 __global__ void __launch_bounds__(1024)
 plan_kernel(const int32_t* __restrict__ ids, int n_assign, int layer, int E, int n_slots,
             int32_t* __restrict__ slot_table, int32_t* __restrict__ owner, uint32_t* __restrict__ last_use,
             uint32_t tick, int policy, double BP, double BH, uint32_t* __restrict__ miss_mask,
             PlanOut* __restrict__ plan) {
-  __shared__ uint64_t keys[PLAN_MAX_SLOTS];
+  __shared__ uint32_t stamp[PLAN_MAX_SLOTS];
   __shared__ int flag[256];
   __shared__ int miss[256];
-  __shared__ int s_m, s_q, s_hit, s_uniq, s_npow, s_elig;
+  __shared__ int hist[256];
+  __shared__ int wtot[16];
+  __shared__ uint64_t vkey[256];
+  __shared__ int vict[256];
+  __shared__ int s_q, s_digit, s_need, s_nv;
   __shared__ uint32_t mask[8];
   const int tid = threadIdx.x;
   if (tid < 256) flag[tid] = 0;
   if (tid < 8) mask[tid] = 0u;
   // stamps before this call (read once; later updates are tracked in LDS)
-  for (int s = tid; s < n_slots; s += blockDim.x) keys[s] = last_use[s];
+  for (int s = tid; s < n_slots; s += blockDim.x) stamp[s] = last_use[s];
   __syncthreads();
   for (int i = tid; i < n_assign; i += blockDim.x) flag[ids[i]] = 1;
   __syncthreads();
+  // classify: thread e looks up expert e
+  const bool routed = tid < E && flag[tid];
   int my_slot = -1;
-  if (tid < E && flag[tid]) {
+  if (routed) {
     my_slot = slot_table[layer * E + tid];
     if (my_slot >= 0) {                 // hit: refresh recency
-      keys[my_slot] = tick;
+      stamp[my_slot] = tick;
       last_use[my_slot] = tick;
     }
   }
-  __syncthreads();
-  if (tid == 0) {
-    int m = 0, h = 0, u = 0;
-    for (int e = 0; e < E; ++e) {
-      if (!flag[e]) continue;
-      ++u;
-      if (slot_table[layer * E + e] >= 0) ++h; else miss[m++] = e;
-    }
-    int q;
-    if (m == 0 || policy == 1) q = 0;              // HOST: every miss on the host
-    else if (policy == 0 || BH <= BP) q = m;       // OFFLOAD, or no residual host bandwidth
-    else {
-      q = (int)floor((double)m * BP / BH + 0.5);
-      q = max(1, min(m, q));
-    }
-    int np = 1;
-    while (np < n_slots) np <<= 1;
-    s_m = m; s_q = q; s_hit = h; s_uniq = u; s_npow = np;
+  int m, h, u;
+  const int mrank = block_rank(routed && my_slot < 0, wtot, &m);   // misses in ascending expert id
+  block_rank(routed && my_slot >= 0, wtot, &h);
+  block_rank(routed, wtot, &u);
+  if (routed && my_slot < 0) miss[mrank] = tid;
+  int q;
+  if (m == 0 || policy == 1) q = 0;              // HOST: every miss on the host
+  else if (policy == 0 || BH <= BP) q = m;       // OFFLOAD, or no residual host bandwidth
+  else {
+    q = (int)floor((double)m * BP / BH + 0.5);
+    q = max(1, min(m, q));
   }
-  __syncthreads();
-  const int np = s_npow;
-  int q = s_q;
+  int elig = 0;
   if (q > 0) {
-    // keys: (stamp << 32 | slot); slots stamped this tick are not eligible
-    for (int s = tid; s < np; s += blockDim.x) {
-      uint64_t k;
-      if (s < n_slots) {
-        const uint32_t st = (uint32_t)keys[s];
-        k = (st == tick) ? ~0ull : (((uint64_t)st << 32) | (uint32_t)s);
-      } else {
-        k = ~0ull;
+    // Victims: the q eligible slots (stamp != tick) with the smallest
+    // (stamp, slot).  Radix select of the q-th smallest stamp, one byte per
+    // pass from the top, then the lowest-numbered slots holding that stamp.
+    int n_elig = 0;
+    for (int base = 0; base < n_slots; base += blockDim.x) {
+      int c;
+      block_rank(base + tid < n_slots && stamp[base + tid] != tick, wtot, &c);
+      n_elig += c;
+    }
+    elig = min(n_elig, 256);
+    q = min(q, elig);
+  }
+  if (q > 0) {
+    uint32_t prefix = 0, pmask = 0;
+    int need = q;                                 // rank (1-based) still sought among matching stamps
+    for (int shift = 24; shift >= 0; shift -= 8) {
+      if (tid < 256) hist[tid] = 0;
+      __syncthreads();
+      for (int s = tid; s < n_slots; s += blockDim.x) {
+        const uint32_t st = stamp[s];
+        if (st != tick && (st & pmask) == prefix) atomicAdd(&hist[(st >> shift) & 255u], 1);
       }
-      keys[s] = k;
+      __syncthreads();
+      if (tid == 0) {
+        int cum = 0, d = 0;
+        while (cum + hist[d] < need) cum += hist[d++];
+        s_digit = d;
+        s_need = need - cum;
+      }
+      __syncthreads();
+      prefix |= (uint32_t)s_digit << shift;
+      pmask |= 255u << shift;
+      need = s_need;
+    }
+    // prefix = the q-th smallest stamp; every eligible slot below it is a
+    // victim, plus the `need` lowest-numbered slots holding it
+    if (tid == 0) s_nv = 0;
+    __syncthreads();
+    int taken = 0;
+    for (int base = 0; base < n_slots; base += blockDim.x) {
+      const int s = base + tid;
+      const uint32_t st = s < n_slots ? stamp[s] : tick;
+      const bool below = st != tick && st < prefix;
+      const bool at = st != tick && st == prefix;
+      int n_at;
+      const int r = block_rank(at, wtot, &n_at);
+      if (below || (at && taken + r < need)) {
+        const int slot_i = atomicAdd(&s_nv, 1);
+        vkey[slot_i] = ((uint64_t)st << 32) | (uint32_t)s;
+      }
+      taken += n_at;
     }
     __syncthreads();
-    // bitonic sort, ascending
-    for (int kk = 2; kk <= np; kk <<= 1) {
-      for (int j = kk >> 1; j > 0; j >>= 1) {
-        for (int i = tid; i < np; i += blockDim.x) {
-          const int ixj = i ^ j;
-          if (ixj > i) {
-            const uint64_t a = keys[i], b = keys[ixj];
-            const bool up = (i & kk) == 0;
-            if ((a > b) == up) { keys[i] = b; keys[ixj] = a; }
-          }
-        }
-        __syncthreads();
-      }
-    }
-    if (tid == 0) {
-      int el = 0;
-      while (el < np && el < 256 && keys[el] != ~0ull) ++el;
-      if (el < q) q = el;
-      s_q = q;
-      s_elig = el;
+    // order the q victims by (stamp, slot)
+    if (tid < q) {
+      const uint64_t k = vkey[tid];
+      int r = 0;
+      for (int j = 0; j < q; ++j) r += vkey[j] < k ? 1 : 0;
+      vict[r] = (int)(uint32_t)(k & 0xffffffffull);
     }
     __syncthreads();
-    q = s_q;
-  } else if (tid == 0) {
-    s_elig = 0;
   }
   // evict victims' owners, install F
   __shared__ int ev_flag[256];
   if (tid < q) {
     const int e = miss[tid];
-    const int s = (int)(uint32_t)(keys[tid] & 0xffffffffull);
+    const int s = vict[tid];
     const int old = owner[s];
     ev_flag[tid] = old >= 0 ? 1 : 0;
     if (old >= 0) slot_table[old] = -1;
@@ -123,7 +163,6 @@ plan_kernel(const int32_t* __restrict__ ids, int n_assign, int layer, int E, int
     plan->F_slot[tid] = s;
   }
   __syncthreads();
-  const int m = s_m;
   if (tid >= q && tid < m) {
     const int e = miss[tid];
     atomicOr(&mask[e >> 5], 1u << (e & 31));
@@ -134,13 +173,13 @@ plan_kernel(const int32_t* __restrict__ ids, int n_assign, int layer, int E, int
   if (tid == 0) {
     int ne = 0;
     for (int i = 0; i < q; ++i) ne += ev_flag[i];
-    plan->n_unique = s_uniq;
-    plan->n_hit = s_hit;
+    plan->n_unique = u;
+    plan->n_hit = h;
     plan->m = m;
     plan->q = q;
     plan->n_host = m - q;
     plan->n_evict = ne;
-    plan->eligible = s_elig;
+    plan->eligible = elig;
     plan->tick = (int)tick;
   }
 }

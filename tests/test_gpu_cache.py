@@ -66,6 +66,39 @@ def test_plan_kernel_matches_slot_model(n_slots, policy):
         s.close()
 
 
+@pytest.mark.parametrize("policy", [B.MOE_POLICY_OFFLOAD, B.MOE_POLICY_HYBRID])
+def test_plan_kernel_many_slots(policy):
+    """More slots than the kernel has threads (victims and stamp ties across
+    1024-slot blocks) and up to ~128 misses per layer (q beyond one wave)."""
+    print(f"plan many slots policy={policy}", flush=True)
+    cfg = _cfg(L=24, E=128, k=8, H=256, I=128)
+    n_slots = 2500
+    s = Setup(cfg, seed=23, n_slots=n_slots, max_tokens=64)
+    try:
+        BP, BH = 30.0, 70.0
+        s.rt.set_policy(policy, BP, BH)
+        model = OC.SlotCache(cfg.L, cfg.E, n_slots)
+        rng = np.random.default_rng(3)
+        for step in range(4):
+            for layer in range(cfg.L):
+                T = int(rng.integers(8, 41))
+                x, xd = s.hidden(T, tag=step * 100 + layer)
+                ids = _route(s, layer, xd)
+                ids_d = torch.from_numpy(ids).cuda()
+                mask = torch.zeros(8, dtype=torch.int32, device="cuda")
+                info, fe, fs = s.rt.plan(layer, ids_d, mask)
+                ref = model.plan(layer, ids.reshape(-1), policy, BP, BH)
+                assert (info.m, info.q, info.n_hit, info.n_unique) == (ref["m"], ref["q"], len(ref["hits"]),
+                                                                       len(ref["unique"]))
+                assert fe == ref["F"] and fs == ref["victims"]
+                m = mask.cpu().numpy().view(np.uint32)
+                got_c = [e for e in range(cfg.E) if (m[e >> 5] >> (e & 31)) & 1]
+                assert got_c == ref["C"]
+        assert list(s.rt.slot_table().cpu().numpy()) == model.slot_of
+    finally:
+        s.close()
+
+
 def _decode_run(cfg, n_slots, policy, steps, T, seed=5, BP=30.0, BH=70.0, reverse_admit=False):
     s = Setup(cfg, seed=seed, n_slots=n_slots, max_tokens=64)
     outs = []
