@@ -458,7 +458,7 @@ def phase_formats(args):
             "bound": pf_bound, "gemm_us": gemm_us, "gpu_layer_us": sum(st.values()), "stage_us": st,
             "weights_hbm_frac": E * S / (gemm_us * 1e-6) / HBM_PEAK,
             "mfma_frac": flops / (gemm_us * 1e-6) / peak, "mfma_peak_TFLOPs": peak / 1e12,
-            "kernel": "gemm_dec (small-batch streaming GEMM; no tiled kernel for this format yet)",
+            "kernel": "gemm_pf_q8 (LDS-tiled scaled-MFMA grouped GEMM)",
         }
         log(f"{name} prefill T={pf_T}: {json.dumps(res[f'prefill_T{pf_T}'])}")
         out[name] = res

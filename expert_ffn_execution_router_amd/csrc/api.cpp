@@ -31,6 +31,11 @@ hipError_t moe_launch_gemm_dec(int fmt, int gated, int ns, int n_cu, const WorkL
 size_t moe_dec_part_bytes();
 int moe_dec_max_ns(int fmt);
 int moe_pf_tile_tokens();
+int moe_pf8_tile_tokens(int fmt);
+hipError_t moe_launch_gemm_pf8(int fmt, int gated, int n_cu, const WorkList* wl, const int32_t* counts,
+                               const int32_t* offsets, const uint8_t* pool, size_t S, size_t woff0, size_t woff1,
+                               size_t soff0, size_t soff1, const void* X, const void* Xs, int K, int N, void* out,
+                               int trash_row, hipStream_t s);
 hipError_t moe_launch_gemm_pf(int fmt, int gated, int grid, const WorkList* wl, const int32_t* counts,
                               const int32_t* offsets, const uint8_t* pool, size_t S, size_t woff0, size_t woff1,
                               const void* X, const int32_t* row_tok, int K, int N, void* out, hipStream_t s);
@@ -114,10 +119,10 @@ WsLayout ws_layout(const moe_config& c) {
   L.mask = take(64);
   L.plan = take(sizeof(PlanOut));
   const bool q8 = c.wfmt != MOE_W_BF16;
-  L.A = take(R * c.I * (q8 ? 4 : 2));
+  L.A = take((R + 1) * c.I * (q8 ? 4 : 2));   // + a spare row for the 8-bit large-batch GEMM's padding stores
   L.Aq = take(q8 ? R * c.I : 0);
   L.As = take(c.wfmt == MOE_W_FP8_E4M3_B128 ? R * (c.I / 128) * 4 : (q8 ? R * (c.I / 32) : 0));
-  L.Z = take(R * c.H * 2);
+  L.Z = take((R + 1) * c.H * 2);
   // quantised activations in grouped order (one row per routed pair)
   L.Xq = take(q8 ? R * c.H : 0);
   L.Xs = take(c.wfmt == MOE_W_FP8_E4M3_B128 ? R * (c.H / 128) * 4 : (q8 ? R * (c.H / 32) : 0));
@@ -261,16 +266,30 @@ int forward_experts(moe_ctx* c, const void* hidden, int T, const int32_t* slot_r
     c->fills_pending = false;
   }
   // many tokens per expert: LDS-tiled MFMA kernels; otherwise weight streaming
-  const bool tiled = g.wfmt == MOE_W_BF16 && T > 64 && (long)T * g.k >= 48L * g.E;
+  const bool tiled = T > 64 && (long)T * g.k >= 48L * g.E;
+  const int tile_mb = g.wfmt == MOE_W_BF16 ? moe_pf_tile_tokens() : moe_pf8_tile_tokens(g.wfmt);
   // weight streaming: m-blocks of 16 * ns tokens (each m-block reads the
   // expert's weights once; larger blocks cost LDS and idle MFMA rows)
   const int ns = std::min(T <= 16 ? 1 : (T <= 64 ? 2 : 4), moe_dec_max_ns(g.wfmt));
   STAGE(c, MOE_STAGE_GROUP, s,
-        moe_launch_group(c->ids, T, g.k, g.E, mask, slot_row, tiled ? moe_pf_tile_tokens() : 16 * ns, c->counts,
+        moe_launch_group(c->ids, T, g.k, g.E, mask, slot_row, tiled ? tile_mb : 16 * ns, c->counts,
                          c->offsets, c->pos, c->perm_tok, c->hist, c->wl, c->err, s));
   const int ncu = c->n_cu;
   const BlobLayout& b = c->bl;
-  if (tiled) {
+  if (tiled && g.wfmt != MOE_W_BF16) {
+    const int trash = g.max_tokens * g.k;       // the spare row of A and Z
+    // activations quantised straight into grouped order (row p <- token perm_tok[p])
+    STAGE(c, MOE_STAGE_QUANT_X, s,
+          moe_launch_quant(g.wfmt, 1, hidden, T * g.k, c->offsets + g.E, c->perm_tok, g.H, c->Xq, c->Xs, s));
+    STAGE(c, MOE_STAGE_GEMM1, s,
+          moe_launch_gemm_pf8(g.wfmt, 1, c->n_cu, c->wl, c->counts, c->offsets, c->slot_pool, b.S, b.w[0], b.w[1],
+                              b.s[0], b.s[1], c->Xq, c->Xs, g.H, g.I, c->A, trash, s));
+    STAGE(c, MOE_STAGE_QUANT_A, s,
+          moe_launch_quant(g.wfmt, 0, c->A, T * g.k, c->offsets + g.E, nullptr, g.I, c->Aq, c->As, s));
+    STAGE(c, MOE_STAGE_GEMM2, s,
+          moe_launch_gemm_pf8(g.wfmt, 0, c->n_cu, c->wl, c->counts, c->offsets, c->slot_pool, b.S, b.w[2], 0,
+                              b.s[2], 0, c->Aq, c->As, g.I, g.H, c->Z, trash, s));
+  } else if (tiled) {
     STAGE(c, MOE_STAGE_GEMM1, s,
           moe_launch_gemm_pf(g.wfmt, 1, c->n_cu, c->wl, c->counts, c->offsets, c->slot_pool, b.S, b.w[0], b.w[1],
                              hidden, c->perm_tok, g.H, g.I, c->A, s));

@@ -109,21 +109,25 @@ def _bf16_bits(x32: np.ndarray) -> np.ndarray:
     return ((u + 0x7FFF + ((u >> 16) & 1)) >> 16).astype(np.uint16)
 
 
-# Expert token counts at the edges of the large-batch kernel's m-tiling: an
-# expert's c tokens are cut into ceil(c/288) equal tiles of at most 288
-# (two halves of 144): one full tile, one token over it, two full tiles, one
-# over those, a single token, a ragged small tile, four tiles, and an expert
-# nobody routes to.
-EDGE_COUNTS = [288, 289, 576, 577, 1, 17, 900, 0]
+# Expert token counts at the edges of the large-batch kernels' m-tiling: an
+# expert's c tokens are cut into ceil(c/cap) equal tiles of at most cap (288
+# for bf16 and MXFP4, 256 for fp8): one full tile, one token over it, two
+# full tiles, one over those, a single token, a ragged small tile, four
+# tiles, and an expert nobody routes to.
+def edge_counts(cap):
+    return [cap, cap + 1, 2 * cap, 2 * cap + 1, 1, 17, 900, 0]
 
 
-def test_tiled_forward_tile_edges():
-    """Routing forced to EDGE_COUNTS by a one-hot router: token t's hidden row
+@pytest.mark.parametrize("fmt", [0, 1, 2])
+def test_tiled_forward_tile_edges(fmt):
+    """Routing forced to edge_counts by a one-hot router: token t's hidden row
     holds 4 at its first expert's dimension and 3 at its second's (noise
     elsewhere), the router reads dimension e for expert e."""
-    cfg = shape(1)                                   # E=8, k=2, H=256, I=128, bf16
+    print(f"tile edges fmt={fmt}", flush=True)
+    cfg = shape(1, fmt=fmt)                          # E=8, k=2, H=256, I=128
     E, k, H = cfg.E, cfg.k, cfg.H
-    slots = np.repeat(np.arange(E), EDGE_COUNTS)
+    counts = edge_counts(256 if fmt == 1 else 288)
+    slots = np.repeat(np.arange(E), counts)
     T = len(slots) // k
     assert T * k == len(slots) and T > 64 and T * k >= 48 * E   # the tiled kernels run
     first, second = slots[:T], slots[T:]
@@ -138,7 +142,7 @@ def test_tiled_forward_tile_edges():
     # the construction routes exactly as intended
     xf = (bits.astype(np.uint32) << 16).view(np.float32)
     top = np.argsort(-(xf @ R.T), axis=1, kind="stable")[:, :k]
-    assert np.array_equal(np.bincount(top.ravel(), minlength=E), np.array(EDGE_COUNTS))
+    assert np.array_equal(np.bincount(top.ravel(), minlength=E), np.array(counts))
 
     s = Setup(cfg, seed=5, max_tokens=T)
     try:

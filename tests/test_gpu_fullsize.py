@@ -81,7 +81,7 @@ def test_prefill_config3_shape(T):
         s.close()
 
 
-@pytest.mark.parametrize("T", [1, 32, 512])
+@pytest.mark.parametrize("T", [1, 32, 512, 4096])
 def test_fp8_config4_shape(T):
     print(f"fp8 config-4 shape T={T}", flush=True)
     cfg = _fullsize(4, L=1)
@@ -98,11 +98,11 @@ def test_fp8_config4_shape(T):
         s.close()
 
 
-@pytest.mark.parametrize("T", [1, 16])
+@pytest.mark.parametrize("T", [1, 16, 2048])
 def test_mxfp4_config5_shape(T):
     print(f"mxfp4 config-5 shape T={T}", flush=True)
     cfg = _fullsize(5, L=1)
-    s = Setup(cfg, seed=3, max_tokens=64, host_threads=8)
+    s = Setup(cfg, seed=3, max_tokens=max(T, 64), host_threads=8)
     try:
         s.admit_all(0)
         x, xd = s.hidden(T, tag=T)
