@@ -134,6 +134,14 @@ router_mfma_kernel(const uint16_t* __restrict__ x, const float* __restrict__ R, 
 // ---------------------------------------------------------------------------
 // top-k (one wave per token, E <= 256) and renormalised weights
 // ---------------------------------------------------------------------------
+// One wave per token (E <= 256: lane l holds experts l, l+64, l+128, l+192).
+// Selection works on an order-preserving 32-bit key of each logit (-0 taken
+// as +0, so equal logits have equal keys): the k-th largest key is found by
+// bisection on its bits with wave ballots (no data crosses lanes), the k
+// winners are the keys above it plus the lowest-numbered experts at it, and
+// each winner's output position is its rank among the winners (descending
+// logit, ties to the lower expert id).  The gate weights are the softmax of
+// the winners, summed in output order.
 __global__ void __launch_bounds__(256)
 topk_kernel(const float* __restrict__ z, int T, int E, int k, int32_t* __restrict__ ids,
             float* __restrict__ w) {
@@ -141,54 +149,76 @@ topk_kernel(const float* __restrict__ z, int T, int E, int k, int32_t* __restric
   const int t = blockIdx.x * 4 + wave;
   if (t >= T) return;
   const float* zr = z + (size_t)t * E;
+  const uint64_t below = (1ull << lane) - 1ull;
   float v[4];
-  bool taken[4];
+  uint32_t key[4];
+  bool valid[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int e = lane + 64 * i;
-    v[i] = zr[min(e, E - 1)];          // unconditional load; entries past E are marked taken
-    taken[i] = e >= E;
+    valid[i] = e < E;
+    const float x = zr[min(e, E - 1)];           // unconditional load; entries past E are not valid
+    v[i] = x == 0.0f ? 0.0f : x;
+    const uint32_t u = __float_as_uint(v[i]);
+    key[i] = (u >> 31) ? ~u : (u | 0x80000000u);
   }
-  float selv[8];
-  int sele[8];
+  // the k-th largest key
+  uint32_t kth = 0;
+  for (int b = 31; b >= 0; --b) {
+    const uint32_t cand = kth | (1u << b);
+    int cnt = 0;
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    if (j >= k) break;
-    float bv = 0.0f;
-    int be = 0x7fffffff;
+    for (int i = 0; i < 4; ++i) cnt += __popcll(__ballot(valid[i] && key[i] >= cand));
+    if (cnt >= k) kth = cand;
+  }
+  // winners: keys above kth, then the lowest-numbered experts at kth
+  int n_gt = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) n_gt += __popcll(__ballot(valid[i] && key[i] > kth));
+  const int need = k - n_gt;
+  bool sel[4];
+  int eq_before = 0;                            // experts at kth with a lower id (slots before i, then lanes)
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const bool eq = valid[i] && key[i] == kth;
+    const uint64_t m = __ballot(eq);
+    sel[i] = (valid[i] && key[i] > kth) || (eq && eq_before + __popcll(m & below) < need);
+    eq_before += __popcll(m);
+  }
+  // rank of each winner among the winners
+  int rank[4] = {0, 0, 0, 0};
+#pragma unroll
+  for (int i2 = 0; i2 < 4; ++i2) {
+    uint64_t m = __ballot(sel[i2]);
+    while (m) {
+      const int L = __builtin_ctzll(m);
+      m &= m - 1;
+      const uint32_t uk = (uint32_t)__builtin_amdgcn_readlane((int)key[i2], L);   // winner (L, i2)
+      const int ue = L + 64 * i2;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int e = lane + 64 * i;
+        rank[i] += (sel[i] && (uk > key[i] || (uk == key[i] && ue < e))) ? 1 : 0;
+      }
+    }
+  }
+  // softmax over the winners in output order (the first is the largest)
+  float top = 0.0f, ssum = 0.0f;
+  for (int j = 0; j < k; ++j) {
+    float vj = 0.0f;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
-      const int e = lane + 64 * i;
-      if (!taken[i] && (be == 0x7fffffff || v[i] > bv)) { bv = v[i]; be = e; }
+      const uint64_t m = __ballot(sel[i] && rank[i] == j);
+      if (m) vj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v[i]), __builtin_ctzll(m)));
     }
-#pragma unroll
-    for (int off = 32; off >= 1; off >>= 1) {
-      const float ov = __shfl_xor(bv, off, 64);
-      const int oe = __shfl_xor(be, off, 64);
-      const bool better = (oe != 0x7fffffff) &&
-                          (be == 0x7fffffff || ov > bv || (ov == bv && oe < be));
-      if (better) { bv = ov; be = oe; }
-    }
-#pragma unroll
-    for (int i = 0; i < 4; ++i)
-      if (be == lane + 64 * i) taken[i] = true;
-    selv[j] = bv;
-    sele[j] = be;
-  }
-  // softmax over the chosen logits (max is the first one)
-  float ex[8], s = 0.0f;
-#pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    if (j >= k) break;
-    ex[j] = expf(selv[j] - selv[0]);
-    s += ex[j];
+    if (j == 0) top = vj;
+    ssum += expf(vj - top);
   }
 #pragma unroll
-  for (int j = 0; j < 8; ++j) {
-    if (j >= k) break;
-    if (lane == j) {
-      ids[(size_t)t * k + j] = sele[j];
-      w[(size_t)t * k + j] = ex[j] / s;
+  for (int i = 0; i < 4; ++i) {
+    if (sel[i]) {
+      ids[(size_t)t * k + rank[i]] = lane + 64 * i;
+      w[(size_t)t * k + rank[i]] = expf(v[i] - top) / ssum;
     }
   }
 }
