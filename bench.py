@@ -59,7 +59,7 @@ def parse():
     ap.add_argument("--e2e-steps", type=int, default=32)
     ap.add_argument("--prefill-T", type=int, default=8192)
     ap.add_argument("--prefill-runs", type=int, default=2, help="double-buffered chunks timed (best is kept)")
-    ap.add_argument("--cpu-layers", type=int, default=3)
+    ap.add_argument("--cpu-layers", type=int, default=20, help="decode layers the oracle times (~0.5 s each)")
     ap.add_argument("--host-threads", type=int, default=16)
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of one graph per step")
     ap.add_argument("--format-layers", type=int, default=4,
@@ -494,6 +494,7 @@ def phase_cpu(w: Workload):
         "value": nl * T / el, "unit": "MoE-layer tokens/s", "cores": int(blas_threads), "kind": "oracle",
         "sample": f"layers 0-{nl - 1} of the first timed decode step (T={T}), float64 NumPy oracle, "
                   f"{cores} host cores visible",
+        "seconds": el,
     }
     log(json.dumps(res))
     return res
