@@ -15,7 +15,9 @@ through the 40% slot cache with the q* miss split (PCIe and host included,
 never the value), and one 8192-token prefill chunk streamed through the
 full-layer double buffer (with the ablation without it).
 
---phases selects a subset (decode, e2e, prefill, cpu) for profiling runs;
+--phases selects a subset (decode, e2e, prefill, cpu) for profiling runs, or
+adds the optional ones: formats (fp8 / MXFP4 shapes) and policies (miss rates
+of expert placements replayed over synthetic routing);
 --copy-probe only runs a 1 GiB device copy (calibrates the byte counters).
 """
 from __future__ import annotations
@@ -64,6 +66,7 @@ def parse():
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of one graph per step")
     ap.add_argument("--format-layers", type=int, default=4,
                     help="layers of the fp8 and MXFP4 pools in the formats phase")
+    ap.add_argument("--policy-steps", type=int, default=256, help="decode steps counted by the policies phase")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only copy 1 GiB device->device 3 times (calibrates HBM byte counters)")
     a = ap.parse_args()
@@ -469,6 +472,67 @@ def phase_formats(args):
     return out
 
 
+def phase_policies(args):
+    """Miss rates of three expert placements at matched slot counts, replayed
+    over synthetic decode routing (T=1, the 0.7-reuse locality model) of the
+    decode-shaped (48 layers, E=128 top-8, Zipf bias) and large-pool (43
+    layers, E=256 top-6, log-normal router scales) generators: the device
+    global LRU, a hot set frozen from a 2048-token prefill chunk's routing,
+    and a static layer split.  Routing runs through the library's router."""
+    import torch
+    import synth
+    from expert_ffn_execution_router_amd import policies as P
+    from expert_ffn_execution_router_amd.runtime import HostPool, MoeRuntime
+    dev = torch.device("cuda:0")
+    W, K, Tp = 16, args.policy_steps, 2048
+    caps = (0.11, 0.2, 0.3, 0.37, 0.4, 0.5, 0.578)
+    out = {}
+    for cid in (2, 4):
+        c = synth.CONFIGS[cid]
+        L, E, k, H = c.L, c.E, c.k, c.H
+        t0 = time.time()
+        # routing context: one layer's shapes, router weights passed per call
+        rpool = HostPool(E * synth.expert_bytes(0, H, 128))
+        rrt = MoeRuntime(1, E, k, H, 128, 0, 0, 4096, rpool)
+        keys = synth.decode_row_keys(c, args.seed, W + K, 1)
+        trace = np.empty((W + K, L, 1, k), dtype=np.int32)
+        prefill = np.empty((L, Tp, k), dtype=np.int32)
+        for l in range(L):
+            R = torch.from_numpy(synth.router_weights(c, args.seed, l)).to(dev)
+            b = synth.router_bias(c, args.seed, l)
+            b = None if b is None else torch.from_numpy(b).to(dev)
+            x = torch.from_numpy(synth.hidden_rows(c, keys[:, l].reshape(-1)).view(np.int16)).to(dev)
+            trace[:, l] = P.route_rows(rrt, x, R, b).reshape(W + K, 1, k)
+            xp = torch.from_numpy(synth.hidden(c, args.seed, Tp, 0x9F0000 + l).view(np.int16)).to(dev)
+            prefill[l] = P.route_rows(rrt, xp, R, b)
+        rrt.close()
+        rpool.free()
+        log(f"policies C{cid}: routed {W + K} decode steps and a {Tp}-token prefill in {time.time() - t0:.1f}s")
+        # LRU context: the same L, E, k; planning never touches expert bytes
+        S = synth.expert_bytes(0, 256, 128)
+        lpool = HostPool(L * E * S)
+        res = {"workload": f"{c.name}: {L} layers, E={E} top-{k}, decode T=1, {W} warm-up + {K} counted steps, "
+                           f"prefill chunk {Tp} tokens",
+               "mean_unique_per_layer": float(np.mean([len(np.unique(trace[s, l])) for s in range(W, W + K)
+                                                       for l in range(L)]))}
+        for cap in caps:
+            n = max(k, int(round(cap * L * E)))
+            lrt = MoeRuntime(L, E, k, 256, 128, 0, n, 64, lpool)
+            t1 = time.time()
+            lm, lu = P.lru_replay(lrt, trace, W)
+            lrt.close()
+            hm, hu = P.fixed_replay(P.prefill_hot_set(prefill, E, n), trace, W)
+            sm, su = P.fixed_replay(P.static_split(L, E, n), trace, W)
+            assert lu == hu == su
+            res[f"{cap:.3f}"] = {"n_slots": n, "lru": lm / lu, "prefill_hot_set": hm / hu, "static_split": sm / su}
+            log(f"policies C{cid} capacity {cap:.3f} ({n} slots): {json.dumps(res[f'{cap:.3f}'])} "
+                f"[{time.time() - t1:.1f}s]")
+        lpool.free()
+        out[f"config{cid}"] = res
+        torch.cuda.empty_cache()
+    return out
+
+
 def phase_cpu(w: Workload):
     """The float64 oracle on a bounded sample of the decode workload."""
     from threadpoolctl import threadpool_info
@@ -541,6 +605,8 @@ def main():
         line["cpu_baseline"] = phase_cpu(w)
     if "formats" in args.phase_set:
         line["formats_resident"] = phase_formats(args)
+    if "policies" in args.phase_set:
+        line["placement_miss_rates"] = phase_policies(args)
     print(json.dumps(line), flush=True)
     if w is not None:
         w.pool.free()
