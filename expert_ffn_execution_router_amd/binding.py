@@ -32,6 +32,14 @@ class moe_config(ctypes.Structure):
                 ("max_tokens", ctypes.c_int), ("host_threads", ctypes.c_int)]
 
 
+class moe_plan_totals(ctypes.Structure):
+    _fields_ = [(f, ctypes.c_longlong) for f in ("calls", "n_unique", "n_hit", "m", "q", "n_host", "n_evict")] + \
+        [("host_ms", ctypes.c_double)]
+
+    def as_dict(self):
+        return {f: getattr(self, f) for f, _ in self._fields_}
+
+
 class moe_plan_info(ctypes.Structure):
     _fields_ = [("n_unique", ctypes.c_int), ("n_hit", ctypes.c_int), ("m", ctypes.c_int), ("q", ctypes.c_int),
                 ("n_host", ctypes.c_int), ("n_evict", ctypes.c_int), ("t_fill_pred_us", ctypes.c_double),
@@ -41,8 +49,8 @@ class moe_plan_info(ctypes.Structure):
         return {f: getattr(self, f) for f, _ in self._fields_}
 
 
-MOE_N_STAGES = 10
-STAGES = ["route", "topk", "group", "quant_x", "gemm1", "quant_a", "gemm2", "combine", "plan", "fixup"]
+MOE_N_STAGES = 11
+STAGES = ["route", "topk", "group", "quant_x", "gemm1", "quant_a", "gemm2", "combine", "plan", "fixup", "fill"]
 
 
 class moe_profile(ctypes.Structure):
@@ -80,6 +88,8 @@ SIGNATURES = {
     "moe_host_ffn": (_i, [_P(moe_config), _vp, _i, _vp, _vp, _vp, _i, _vp, _vp]),
     "moe_layer_forward": (_i, [_vp, _i, _vp, _vp, _vp, _i, _vp, _vp, _vp, _vp, _vp]),
     "moe_decode_layer": (_i, [_vp, _i, _vp, _vp, _vp, _i, _vp, _P(moe_plan_info), _vp, _vp]),
+    "moe_decode_layer_async": (_i, [_vp, _i, _vp, _vp, _vp, _i, _vp, _vp, _vp]),
+    "moe_plan_stats": (_i, [_vp, _P(moe_plan_totals), _i]),
     "prefill_stream_layer": (_i, [_vp, _i, _vp, _vp, _vp, _i, _vp, _vp, _vp, _i]),
     "moe_check_device_error": (_i, [_vp]),
     "moe_profile_begin": (_i, [_vp, _i, ctypes.c_uint]),
@@ -150,6 +160,8 @@ moe_host_partial = _fn("moe_host_partial")
 moe_host_ffn = _fn("moe_host_ffn")
 moe_layer_forward = _fn("moe_layer_forward")
 moe_decode_layer = _fn("moe_decode_layer")
+moe_decode_layer_async = _fn("moe_decode_layer_async")
+moe_plan_stats = _fn("moe_plan_stats")
 prefill_stream_layer = _fn("prefill_stream_layer")
 moe_check_device_error = _fn("moe_check_device_error")
 moe_profile_begin = _fn("moe_profile_begin")

@@ -9,6 +9,8 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <map>
+#include <memory>
 #include <string>
 #include <thread>
 #include <vector>
@@ -40,16 +42,18 @@ hipError_t moe_launch_gemm_pf(int fmt, int gated, int grid, const WorkList* wl, 
                               const int32_t* offsets, const uint8_t* pool, size_t S, size_t woff0, size_t woff1,
                               const void* X, const int32_t* row_tok, int K, int N, void* out, hipStream_t s);
 hipError_t moe_launch_combine(const uint16_t* Z, const int32_t* ids, const float* w, const int32_t* pos,
-                              const uint32_t* miss_mask, const int32_t* slot_row, const float* hp, int T, int k,
-                              int H, uint16_t* out, hipStream_t s);
+                              const uint32_t* miss_mask, const int32_t* slot_row, const float* hp,
+                              const int32_t* hp_count, int T, int k, int H, uint16_t* out, hipStream_t s);
 hipError_t moe_launch_quant(int fmt, int src_bf16, const void* src, int rows, const int32_t* nrows_dev,
                             const int32_t* row_map, int cols, uint8_t* q, void* scale, hipStream_t s);
 hipError_t moe_launch_plan(const int32_t* ids, int n_assign, int layer, int E, int n_slots, int32_t* slot_table,
-                           int32_t* owner, uint32_t* last_use, uint32_t tick, int policy, double BP, double BH,
-                           uint32_t* miss_mask, void* plan, hipStream_t s);
+                           int32_t* owner, uint32_t* last_use, void* ctl, int policy, double BP, double BH,
+                           uint32_t* miss_mask, void* plan, const void* host_stage, hipStream_t s);
+hipError_t moe_launch_fill(const void* plan, const uint8_t* host_pool_dev, int layer, int E, size_t S,
+                           uint8_t* slot_pool, int grid, hipStream_t s);
 hipError_t moe_launch_evict(const int32_t* experts, int n, int layer, int E, int32_t* slot_table, int32_t* owner,
                             uint32_t* last_use, hipStream_t s);
-hipError_t moe_launch_install_layer(int layer, int base, int E, uint32_t tick, int32_t* slot_table, int32_t* owner,
+hipError_t moe_launch_install_layer(int layer, int base, int E, void* ctl, int32_t* slot_table, int32_t* owner,
                                     uint32_t* last_use, hipStream_t s);
 hipError_t moe_launch_free_slots(const int32_t* slots, int n, int32_t* slot_table, int32_t* owner,
                                  uint32_t* last_use, hipStream_t s);
@@ -89,7 +93,7 @@ BlobLayout blob_layout(const moe_config& c) {
 
 // Workspace carving (all offsets 256-byte aligned).
 struct WsLayout {
-  size_t slot_table, owner, last_use, err, logits, ids, w, pos, perm_tok, counts, offsets, hist, wl, mask, plan, A,
+  size_t slot_table, owner, last_use, ctl, err, logits, ids, w, pos, perm_tok, counts, offsets, hist, wl, mask, plan, A,
       Aq, As, Z, Xq, Xs, hp, part, total;
 };
 
@@ -106,6 +110,7 @@ WsLayout ws_layout(const moe_config& c) {
   L.slot_table = take((size_t)c.L * c.E * 4);
   L.owner = take((size_t)c.n_slots * 4);
   L.last_use = take((size_t)c.n_slots * 4);
+  L.ctl = take(sizeof(CacheCtl));
   L.err = take(64);
   L.logits = take(Tm * c.E * 4);
   L.ids = take(R * 4);
@@ -135,6 +140,12 @@ WsLayout ws_layout(const moe_config& c) {
 
 }  // namespace
 
+// Argument of one host-branch callback of the asynchronous decode path.
+struct AsyncArg {
+  moe_ctx* c;
+  int layer, T;
+};
+
 struct moe_ctx {
   moe_config cfg;
   BlobLayout bl;
@@ -148,6 +159,7 @@ struct moe_ctx {
   int32_t* slot_table;
   int32_t* owner;
   uint32_t* last_use;
+  CacheCtl* ctl;
   int* err;
   float* logits;
   int32_t* ids;
@@ -175,10 +187,18 @@ struct moe_ctx {
   float* w_host = nullptr;
   float* hp_host = nullptr;
   int32_t* list_dev_stage = nullptr;   // pinned staging for small int lists sent to the device
+  uint8_t* host_pool_dev = nullptr;    // device mapping of the pinned host pool (NULL: not mapped)
+  HostStage stage_dev{};                // device mappings of the staging buffers (plan NULL: not mapped)
+  float* hp_host_dev = nullptr;
   // policy
   int policy = MOE_POLICY_OFFLOAD;
   double BP = 1.0, BH = 1.0;
-  uint32_t tick = 0;
+  // asynchronous decode: host-branch callback arguments, one per (layer, T),
+  // alive until moe_destroy because captured graphs keep their addresses
+  std::map<std::pair<int, int>, std::unique_ptr<AsyncArg>> async_args;
+  hipEvent_t async_plan_evt = nullptr, async_host_evt = nullptr;
+  int async_err = 0;                    // set by a host-branch callback that failed
+  double async_host_ms = 0.0;           // wall time spent in host-branch callbacks
   // events
   hipEvent_t plan_evt = nullptr, fill_evt = nullptr, ready[2] = {nullptr, nullptr}, done[2] = {nullptr, nullptr};
   int pf_next = -1;
@@ -338,9 +358,11 @@ int route_only(moe_ctx* c, const void* hidden, const float* R, const float* bias
   return MOE_OK;
 }
 
-int combine(moe_ctx* c, const uint32_t* mask, const int32_t* row, const float* hp, int T, void* out, hipStream_t s) {
+int combine(moe_ctx* c, const uint32_t* mask, const int32_t* row, const float* hp, int T, void* out, hipStream_t s,
+            const int32_t* hp_count = nullptr) {
   STAGE(c, MOE_STAGE_COMBINE, s,
-        moe_launch_combine(c->Z, c->ids, c->w, c->pos, mask, row, hp, T, c->cfg.k, c->cfg.H, (uint16_t*)out, s));
+        moe_launch_combine(c->Z, c->ids, c->w, c->pos, mask, row, hp, hp_count, T, c->cfg.k, c->cfg.H,
+                           (uint16_t*)out, s));
   return MOE_OK;
 }
 
@@ -351,10 +373,9 @@ int check_T(moe_ctx* c, int T) {
 
 int plan_sync(moe_ctx* c, int layer, const int32_t* ids_dev, int T, uint32_t* mask_dev, int policy, hipStream_t s) {
   const moe_config& g = c->cfg;
-  const uint32_t tick = ++c->tick;
   STAGE(c, MOE_STAGE_PLAN, s,
-        moe_launch_plan(ids_dev, T * g.k, layer, g.E, g.n_slots, c->slot_table, c->owner, c->last_use, tick, policy,
-                        c->BP, c->BH, mask_dev, c->plan_dev, s));
+        moe_launch_plan(ids_dev, T * g.k, layer, g.E, g.n_slots, c->slot_table, c->owner, c->last_use, c->ctl, policy,
+                        c->BP, c->BH, mask_dev, c->plan_dev, nullptr, s));
   HIPCHK(c, hipMemcpyAsync(c->plan_host, c->plan_dev, sizeof(PlanOut), hipMemcpyDeviceToHost, s));
   return MOE_OK;
 }
@@ -384,6 +405,26 @@ int issue_fills(moe_ctx* c, int layer, const int* experts, const int* slots, int
   HIPCHK(c, hipEventRecord(c->fill_evt, copy));
   c->fills_pending = true;
   return MOE_OK;
+}
+
+// Host branch of the asynchronous decode path, run by the HIP runtime when
+// the host stream reaches it: the plan and the routed inputs have just been
+// copied into the pinned staging buffers; the host set C runs on the thread
+// pool into hp_host.  Calls no HIP function.
+void host_branch_cb(void* p) {
+  const AsyncArg* a = (const AsyncArg*)p;
+  moe_ctx* c = a->c;
+  const PlanOut& pl = *c->plan_host;
+  if (pl.n_host <= 0) return;
+  if (pl.n_host > c->cfg.E) {
+    c->async_err = 1;
+    return;
+  }
+  const auto t0 = std::chrono::steady_clock::now();
+  HostFfnHandle* h = host_ffn_start(c->pool, host_shape(c->cfg, c->bl.S), c->host_pool, a->layer, a->T,
+                                    c->hidden_host, c->ids_host, c->w_host, pl.C, pl.n_host, c->hp_host);
+  host_ffn_wait(c->pool, h);
+  c->async_host_ms += std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t0).count();
 }
 
 }  // namespace
@@ -450,6 +491,7 @@ int moe_create(const moe_config* cfg, void* host_pool, size_t host_bytes, void* 
   c->slot_table = (int32_t*)(w + L.slot_table);
   c->owner = (int32_t*)(w + L.owner);
   c->last_use = (uint32_t*)(w + L.last_use);
+  c->ctl = (CacheCtl*)(w + L.ctl);
   c->err = (int*)(w + L.err);
   c->logits = (float*)(w + L.logits);
   c->ids = (int32_t*)(w + L.ids);
@@ -473,21 +515,50 @@ int moe_create(const moe_config* cfg, void* host_pool, size_t host_bytes, void* 
   const size_t Tm = cfg->max_tokens;
   const size_t R = Tm * cfg->k;
   void* p;
-  if (hipHostMalloc(&p, sizeof(PlanOut), hipHostMallocDefault) != hipSuccess) return bad(MOE_E_PIN, "staging");
+  // staging shared with kernels of the asynchronous path: coherent, so the
+  // device's stores and loads through the mappings bypass its caches
+  const unsigned coh = hipHostMallocCoherent;
+  if (hipHostMalloc(&p, sizeof(PlanOut), coh) != hipSuccess) return bad(MOE_E_PIN, "staging");
   c->plan_host = (PlanOut*)p;
-  if (hipHostMalloc(&p, Tm * cfg->H * 2, hipHostMallocDefault) != hipSuccess) return bad(MOE_E_PIN, "staging");
+  if (hipHostMalloc(&p, Tm * cfg->H * 2, coh) != hipSuccess) return bad(MOE_E_PIN, "staging");
   c->hidden_host = (uint16_t*)p;
-  if (hipHostMalloc(&p, R * 4, hipHostMallocDefault) != hipSuccess) return bad(MOE_E_PIN, "staging");
+  if (hipHostMalloc(&p, R * 4, coh) != hipSuccess) return bad(MOE_E_PIN, "staging");
   c->ids_host = (int32_t*)p;
-  if (hipHostMalloc(&p, R * 4, hipHostMallocDefault) != hipSuccess) return bad(MOE_E_PIN, "staging");
+  if (hipHostMalloc(&p, R * 4, coh) != hipSuccess) return bad(MOE_E_PIN, "staging");
   c->w_host = (float*)p;
-  if (hipHostMalloc(&p, Tm * cfg->H * 4, hipHostMallocDefault) != hipSuccess) return bad(MOE_E_PIN, "staging");
+  if (hipHostMalloc(&p, Tm * cfg->H * 4, coh) != hipSuccess) return bad(MOE_E_PIN, "staging");
   c->hp_host = (float*)p;
   if (hipHostMalloc(&p, 2 * 8192 * 4, hipHostMallocDefault) != hipSuccess) return bad(MOE_E_PIN, "staging");
   c->list_dev_stage = (int32_t*)p;
   if (hipEventCreateWithFlags(&c->plan_evt, hipEventDisableTiming) != hipSuccess ||
-      hipEventCreateWithFlags(&c->fill_evt, hipEventDisableTiming) != hipSuccess)
+      hipEventCreateWithFlags(&c->fill_evt, hipEventDisableTiming) != hipSuccess ||
+      hipEventCreateWithFlags(&c->async_plan_evt, hipEventDisableTiming) != hipSuccess ||
+      hipEventCreateWithFlags(&c->async_host_evt, hipEventDisableTiming) != hipSuccess)
     return bad(MOE_E_HIP, "event create");
+  // the indexed fill kernel reads the host pool through its device mapping
+  // (pinned memory from hipHostMalloc has one; other memory leaves the
+  // asynchronous decode path unavailable)
+  void* hdev = nullptr;
+  if (hipHostGetDevicePointer(&hdev, host_pool, 0) == hipSuccess) c->host_pool_dev = (uint8_t*)hdev;
+  (void)hipGetLastError();
+  {
+    void *a = nullptr, *b = nullptr, *d = nullptr, *e = nullptr, *f = nullptr;
+    if (hipHostGetDevicePointer(&a, c->plan_host, 0) == hipSuccess &&
+        hipHostGetDevicePointer(&b, c->ids_host, 0) == hipSuccess &&
+        hipHostGetDevicePointer(&d, c->w_host, 0) == hipSuccess &&
+        hipHostGetDevicePointer(&e, c->hidden_host, 0) == hipSuccess &&
+        hipHostGetDevicePointer(&f, c->hp_host, 0) == hipSuccess) {
+      c->stage_dev.plan = (PlanOut*)a;
+      c->stage_dev.ids = (int32_t*)b;
+      c->stage_dev.w = (float*)d;
+      c->stage_dev.hidden = (uint16_t*)e;
+      c->hp_host_dev = (float*)f;
+    } else {
+      c->host_pool_dev = nullptr;      // the asynchronous path needs every mapping
+    }
+    (void)hipGetLastError();
+  }
+  if (hipMemset(c->ctl, 0, sizeof(CacheCtl)) != hipSuccess) return bad(MOE_E_HIP, "control block clear");
   for (int i = 0; i < 2; ++i)
     if (hipEventCreateWithFlags(&c->ready[i], hipEventDisableTiming) != hipSuccess ||
         hipEventCreateWithFlags(&c->done[i], hipEventDisableTiming) != hipSuccess)
@@ -515,7 +586,8 @@ int moe_destroy(moe_ctx* c) {
   if (c->w_host) (void)hipHostFree(c->w_host);
   if (c->hp_host) (void)hipHostFree(c->hp_host);
   if (c->list_dev_stage) (void)hipHostFree(c->list_dev_stage);
-  for (hipEvent_t e : {c->plan_evt, c->fill_evt, c->ready[0], c->ready[1], c->done[0], c->done[1]})
+  for (hipEvent_t e : {c->plan_evt, c->fill_evt, c->ready[0], c->ready[1], c->done[0], c->done[1],
+                       c->async_plan_evt, c->async_host_evt})
     if (e) (void)hipEventDestroy(e);
   delete c;
   return MOE_OK;
@@ -620,9 +692,8 @@ int slot_pool_admit(moe_ctx* c, int layer, const int32_t* experts, int n, void* 
   // the plan kernel reads the list as routed ids: stage it into the workspace
   std::memcpy(c->list_dev_stage, experts, (size_t)n * 4);
   HIPCHK(c, hipMemcpyAsync(c->ids, c->list_dev_stage, (size_t)n * 4, hipMemcpyHostToDevice, s));
-  const uint32_t tick = ++c->tick;
-  HIPCHK(c, moe_launch_plan(c->ids, n, layer, g.E, g.n_slots, c->slot_table, c->owner, c->last_use, tick,
-                            MOE_POLICY_OFFLOAD, 1.0, 1.0, c->mask, c->plan_dev, s));
+  HIPCHK(c, moe_launch_plan(c->ids, n, layer, g.E, g.n_slots, c->slot_table, c->owner, c->last_use, c->ctl,
+                            MOE_POLICY_OFFLOAD, 1.0, 1.0, c->mask, c->plan_dev, nullptr, s));
   HIPCHK(c, hipMemcpyAsync(c->plan_host, c->plan_dev, sizeof(PlanOut), hipMemcpyDeviceToHost, s));
   HIPCHK(c, hipEventRecord(c->plan_evt, s));
   HIPCHK(c, hipEventSynchronize(c->plan_evt));
@@ -750,6 +821,79 @@ int moe_decode_layer(moe_ctx* c, int layer, const void* hidden, const float* R, 
   return combine(c, c->mask, row, hp, T, out, s);
 }
 
+int moe_decode_layer_async(moe_ctx* c, int layer, const void* hidden, const float* R, const float* bias, int T,
+                           void* out, void* compute_stream, void* host_stream) {
+  if (!c) return fail(nullptr, MOE_E_INVAL, "null ctx");
+  const moe_config& g = c->cfg;
+  if (layer < 0 || layer >= g.L) return fail(c, MOE_E_INVAL, "layer out of range");
+  int rc = check_T(c, T);
+  if (rc) return rc;
+  if (!c->host_pool_dev) return fail(c, MOE_E_UNSUPPORTED, "host pool has no device mapping (use moe_host_alloc)");
+  if (T == 0) return MOE_OK;
+  hipStream_t s = as_stream(compute_stream), hs = as_stream(host_stream);
+  rc = route_only(c, hidden, R, bias, T, s);
+  if (rc) return rc;
+  // host branch (section 2.5: started before the GPU miss path): the plan
+  // kernel writes the plan and the routed inputs into pinned staging; the
+  // host stream waits for it, runs C in a host callback into pinned hp, and
+  // the combine reads hp through its device mapping
+  const bool may_host = c->policy != MOE_POLICY_OFFLOAD || g.n_slots < g.E;
+  HostStage hst{};
+  if (may_host) {
+    hst = c->stage_dev;
+    hst.w_src = c->w;
+    hst.hidden_src = (const uint16_t*)hidden;
+    hst.n_hidden = T * g.H;
+  }
+  STAGE(c, MOE_STAGE_PLAN, s,
+        moe_launch_plan(c->ids, T * g.k, layer, g.E, g.n_slots, c->slot_table, c->owner, c->last_use, c->ctl,
+                        c->policy, c->BP, c->BH, c->mask, c->plan_dev, may_host ? &hst : nullptr, s));
+  if (may_host) {
+    auto& slot = c->async_args[{layer, T}];
+    if (!slot) slot.reset(new AsyncArg{c, layer, T});
+    HIPCHK(c, hipEventRecord(c->async_plan_evt, s));
+    HIPCHK(c, hipStreamWaitEvent(hs, c->async_plan_evt, 0));
+    HIPCHK(c, hipLaunchHostFunc(hs, host_branch_cb, slot.get()));
+    HIPCHK(c, hipEventRecord(c->async_host_evt, hs));
+  }
+  // the fill set in one launch, from the device plan (section 2.6)
+  if (g.n_slots > 0)
+    STAGE(c, MOE_STAGE_FILL, s,
+          moe_launch_fill(c->plan_dev, c->host_pool_dev, layer, g.E, c->bl.S, c->slot_pool, 64, s));
+  const int32_t* row = c->slot_table + (size_t)layer * g.E;
+  rc = forward_experts(c, hidden, T, row, c->mask, s);
+  if (rc) return rc;
+  if (!may_host) return combine(c, c->mask, row, nullptr, T, out, s);
+  HIPCHK(c, hipStreamWaitEvent(s, c->async_host_evt, 0));
+  return combine(c, c->mask, row, c->hp_host_dev, T, out, s, &c->plan_dev->n_host);
+}
+
+int moe_plan_stats(moe_ctx* c, moe_plan_totals* out, int reset) {
+  if (!c) return fail(nullptr, MOE_E_INVAL, "null ctx");
+  HIPCHK(c, hipDeviceSynchronize());
+  CacheCtl v;
+  HIPCHK(c, hipMemcpy(&v, c->ctl, sizeof(CacheCtl), hipMemcpyDeviceToHost));
+  if (out) {
+    out->calls = (long long)v.calls;
+    out->n_unique = (long long)v.n_unique;
+    out->n_hit = (long long)v.n_hit;
+    out->m = (long long)v.m;
+    out->q = (long long)v.q;
+    out->n_host = (long long)v.n_host;
+    out->n_evict = (long long)v.n_evict;
+    out->host_ms = c->async_host_ms;
+  }
+  if (reset) {
+    v.calls = v.n_unique = v.n_hit = v.m = v.q = v.n_host = v.n_evict = 0;
+    c->async_host_ms = 0.0;
+    HIPCHK(c, hipMemcpy(c->ctl, &v, sizeof(CacheCtl), hipMemcpyHostToDevice));
+  }
+  const int e = c->async_err;
+  c->async_err = 0;
+  if (e) return fail(c, MOE_E_INVAL, "a host-branch callback received an invalid plan");
+  return MOE_OK;
+}
+
 int prefill_stream_layer(moe_ctx* c, int layer, const void* hidden, const float* R, const float* bias, int T,
                          void* out, void* compute_stream, void* copy_stream, int double_buffer) {
   if (!c) return fail(nullptr, MOE_E_INVAL, "null ctx");
@@ -773,7 +917,7 @@ int prefill_stream_layer(moe_ctx* c, int layer, const void* hidden, const float*
   auto issue_copy = [&](int l) -> int {
     const int b = buf_of(l);
     HIPCHK(c, hipStreamWaitEvent(cs, c->done[b], 0));
-    HIPCHK(c, moe_launch_install_layer(l, base_of(l), g.E, ++c->tick, c->slot_table, c->owner, c->last_use, cs));
+    HIPCHK(c, moe_launch_install_layer(l, base_of(l), g.E, c->ctl, c->slot_table, c->owner, c->last_use, cs));
     HIPCHK(c, hipMemcpyAsync(c->slot_pool + (size_t)base_of(l) * S, c->host_pool + (size_t)l * layer_bytes,
                              layer_bytes, hipMemcpyHostToDevice, cs));
     HIPCHK(c, hipEventRecord(c->ready[b], cs));

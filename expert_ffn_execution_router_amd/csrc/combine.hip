@@ -16,8 +16,8 @@
 __global__ void __launch_bounds__(256)
 combine_kernel(const uint16_t* __restrict__ Z, const int32_t* __restrict__ ids, const float* __restrict__ w,
                const int32_t* __restrict__ pos, const uint32_t* __restrict__ miss_mask,
-               const int32_t* __restrict__ slot_row, const float* __restrict__ hp, int T, int k, int H,
-               uint16_t* __restrict__ out) {
+               const int32_t* __restrict__ slot_row, const float* __restrict__ hp,
+               const int32_t* __restrict__ hp_count, int T, int k, int H, uint16_t* __restrict__ out) {
   const int t = blockIdx.y;
   const int h = (blockIdx.x * 256 + threadIdx.x) * 8;
   if (t >= T || h >= H) return;
@@ -52,7 +52,9 @@ combine_kernel(const uint16_t* __restrict__ Z, const int32_t* __restrict__ ids, 
       acc[2 * i + 1] += use[j] ? hi : 0.0f;
     }
   }
-  if (hp) {
+  // hp_count (device, optional): the host partial is used only when the
+  // plan sent at least one expert to the host
+  if (hp && (!hp_count || *hp_count > 0)) {
     const float4 a = *(const float4*)(hp + (size_t)t * H + h);
     const float4 b = *(const float4*)(hp + (size_t)t * H + h + 4);
     acc[0] += a.x; acc[1] += a.y; acc[2] += a.z; acc[3] += a.w;
@@ -158,11 +160,12 @@ quant_mxfp8_kernel(const void* __restrict__ src, int rows, const int32_t* __rest
 }
 
 extern "C" hipError_t moe_launch_combine(const uint16_t* Z, const int32_t* ids, const float* w, const int32_t* pos,
-                                         const uint32_t* miss_mask, const int32_t* slot_row, const float* hp, int T,
-                                         int k, int H, uint16_t* out, hipStream_t s) {
+                                         const uint32_t* miss_mask, const int32_t* slot_row, const float* hp,
+                                         const int32_t* hp_count, int T, int k, int H, uint16_t* out,
+                                         hipStream_t s) {
   if (T == 0) return hipSuccess;
   dim3 g((H / 8 + 255) / 256, T);
-  combine_kernel<<<g, 256, 0, s>>>(Z, ids, w, pos, miss_mask, slot_row, hp, T, k, H, out);
+  combine_kernel<<<g, 256, 0, s>>>(Z, ids, w, pos, miss_mask, slot_row, hp, hp_count, T, k, H, out);
   return hipGetLastError();
 }
 

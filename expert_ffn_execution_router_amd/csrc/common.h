@@ -37,6 +37,28 @@ struct PlanOut {
   int C[256];       // experts executed on the host, ascending
 };
 
+// Device-resident cache-control state beside the residency table: the LRU
+// clock (one tick per planning or layer-install call, advanced by the kernel
+// itself so a captured graph replays with fresh ticks) and running plan
+// statistics.
+struct CacheCtl {
+  uint32_t tick;
+  uint32_t pad[3];
+  unsigned long long calls, n_unique, n_hit, m, q, n_host, n_evict, pad2;
+};
+
+// Pinned host staging (device mappings) that the cache-control kernel fills
+// for a host branch: the plan and the routed inputs.  plan == nullptr: none.
+struct HostStage {
+  PlanOut* plan;
+  int32_t* ids;
+  float* w;
+  uint16_t* hidden;
+  const float* w_src;
+  const uint16_t* hidden_src;
+  int n_hidden;                 // T * H
+};
+
 DEV float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
 
 DEV uint16_t f32_to_bf16_bits(float f) {

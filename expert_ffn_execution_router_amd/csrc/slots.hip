@@ -43,8 +43,8 @@ DEV int block_rank(bool pred, int* wtot, int* total) {
 __global__ void __launch_bounds__(1024)
 plan_kernel(const int32_t* __restrict__ ids, int n_assign, int layer, int E, int n_slots,
             int32_t* __restrict__ slot_table, int32_t* __restrict__ owner, uint32_t* __restrict__ last_use,
-            uint32_t tick, int policy, double BP, double BH, uint32_t* __restrict__ miss_mask,
-            PlanOut* __restrict__ plan) {
+            CacheCtl* __restrict__ ctl, int policy, double BP, double BH, uint32_t* __restrict__ miss_mask,
+            PlanOut* __restrict__ plan, HostStage hs) {
   __shared__ uint32_t stamp[PLAN_MAX_SLOTS];
   __shared__ int flag[256];
   __shared__ int miss[256];
@@ -52,9 +52,10 @@ plan_kernel(const int32_t* __restrict__ ids, int n_assign, int layer, int E, int
   __shared__ int wtot[16];
   __shared__ uint64_t vkey[256];
   __shared__ int vict[256];
-  __shared__ int s_q, s_digit, s_need, s_nv;
+  __shared__ int s_digit, s_need, s_nv;
   __shared__ uint32_t mask[8];
   const int tid = threadIdx.x;
+  const uint32_t tick = ctl->tick + 1u;   // written back by thread 0 after the last barrier
   if (tid < 256) flag[tid] = 0;
   if (tid < 8) mask[tid] = 0u;
   // stamps before this call (read once; later updates are tracked in LDS)
@@ -161,12 +162,17 @@ plan_kernel(const int32_t* __restrict__ ids, int n_assign, int layer, int E, int
     last_use[s] = tick;
     plan->F[tid] = e;
     plan->F_slot[tid] = s;
+    if (hs.plan) {
+      hs.plan->F[tid] = e;
+      hs.plan->F_slot[tid] = s;
+    }
   }
   __syncthreads();
   if (tid >= q && tid < m) {
     const int e = miss[tid];
     atomicOr(&mask[e >> 5], 1u << (e & 31));
     plan->C[tid - q] = e;
+    if (hs.plan) hs.plan->C[tid - q] = e;
   }
   __syncthreads();
   if (tid < 8) miss_mask[tid] = mask[tid];
@@ -181,6 +187,69 @@ plan_kernel(const int32_t* __restrict__ ids, int n_assign, int layer, int E, int
     plan->n_evict = ne;
     plan->eligible = elig;
     plan->tick = (int)tick;
+    ctl->tick = tick;
+    ctl->calls += 1;
+    ctl->n_unique += u;
+    ctl->n_hit += h;
+    ctl->m += m;
+    ctl->q += q;
+    ctl->n_host += m - q;
+    ctl->n_evict += ne;
+    if (hs.plan) {
+      hs.plan->n_unique = u;
+      hs.plan->n_hit = h;
+      hs.plan->m = m;
+      hs.plan->q = q;
+      hs.plan->n_host = m - q;
+      hs.plan->n_evict = ne;
+      hs.plan->eligible = elig;
+      hs.plan->tick = (int)tick;
+    }
+  }
+  // the host branch's inputs, written straight into pinned host memory
+  // (visible to the host once the kernel has completed)
+  if (hs.plan) {
+    for (int i = tid; i < n_assign; i += blockDim.x) {
+      hs.ids[i] = ids[i];
+      hs.w[i] = hs.w_src[i];
+    }
+    if ((((uintptr_t)hs.hidden_src | (uintptr_t)hs.hidden) & 15u) == 0 && (hs.n_hidden & 7) == 0) {
+      const i32x4_t* src = (const i32x4_t*)hs.hidden_src;
+      i32x4_t* dst = (i32x4_t*)hs.hidden;
+      for (int i = tid; i < hs.n_hidden / 8; i += blockDim.x) dst[i] = src[i];
+    } else {
+      for (int i = tid; i < hs.n_hidden; i += blockDim.x) hs.hidden[i] = hs.hidden_src[i];
+    }
+  }
+}
+
+// The fill set of the last plan in one launch (section 2.6: a device-resident
+// source/destination table shared by every bank, applied by one fixed-shape
+// launch, entries past the device valid count unused): expert F[j] of
+// `layer` is read from the pinned host pool through its device mapping and
+// written to slot F_slot[j].  Each expert blob is S contiguous bytes in both
+// pools, so one table entry moves one blob.  V is the copy word (16, 8 or 4
+// bytes, dividing S and both base addresses); four words per thread are in
+// flight so a few dozen workgroups keep the link busy.
+template <typename V>
+__global__ void __launch_bounds__(256)
+fill_kernel(const PlanOut* __restrict__ plan, const uint8_t* __restrict__ host_pool, int layer, int E, size_t S,
+            uint8_t* __restrict__ slot_pool) {
+  const int q = plan->q;
+  const size_t n = S / sizeof(V);
+  const size_t stride = (size_t)gridDim.x * blockDim.x;
+  for (int j = 0; j < q; ++j) {
+    const V* __restrict__ src = (const V*)(host_pool + ((size_t)layer * E + plan->F[j]) * S);
+    V* __restrict__ dst = (V*)(slot_pool + (size_t)plan->F_slot[j] * S);
+    size_t i = (size_t)blockIdx.x * blockDim.x + threadIdx.x;
+    for (; i + 3 * stride < n; i += 4 * stride) {
+      const V a = src[i], b = src[i + stride], c = src[i + 2 * stride], d = src[i + 3 * stride];
+      dst[i] = a;
+      dst[i + stride] = b;
+      dst[i + 2 * stride] = c;
+      dst[i + 3 * stride] = d;
+    }
+    for (; i < n; i += stride) dst[i] = src[i];
   }
 }
 
@@ -204,9 +273,10 @@ __global__ void evict_kernel(const int32_t* __restrict__ experts, int n, int lay
 // residency; slots previously holding this layer's experts elsewhere become
 // empty.  Two phases separated by a barrier so installs win.
 __global__ void __launch_bounds__(256)
-install_layer_kernel(int layer, int base, int E, uint32_t tick, int32_t* __restrict__ slot_table,
+install_layer_kernel(int layer, int base, int E, CacheCtl* __restrict__ ctl, int32_t* __restrict__ slot_table,
                      int32_t* __restrict__ owner, uint32_t* __restrict__ last_use) {
   const int e = threadIdx.x;
+  const uint32_t tick = ctl->tick + 1u;
   const int g = layer * E + e;
   const int s = base + e;
   if (e < E) {
@@ -225,6 +295,7 @@ install_layer_kernel(int layer, int base, int E, uint32_t tick, int32_t* __restr
     slot_table[g] = s;
     last_use[s] = tick;
   }
+  if (e == 0) ctl->tick = tick;
 }
 
 // Free the given slots (their owners lose residency).
@@ -251,11 +322,29 @@ __global__ void reset_kernel(int n_table, int n_slots, int32_t* slot_table, int3
 extern "C" size_t moe_plan_out_bytes() { return sizeof(PlanOut); }
 
 extern "C" hipError_t moe_launch_plan(const int32_t* ids, int n_assign, int layer, int E, int n_slots,
-                                      int32_t* slot_table, int32_t* owner, uint32_t* last_use, uint32_t tick,
+                                      int32_t* slot_table, int32_t* owner, uint32_t* last_use, void* ctl,
                                       int policy, double BP, double BH, uint32_t* miss_mask, void* plan,
-                                      hipStream_t s) {
-  plan_kernel<<<1, 1024, 0, s>>>(ids, n_assign, layer, E, n_slots, slot_table, owner, last_use, tick, policy, BP, BH,
-                                 miss_mask, (PlanOut*)plan);
+                                      const void* host_stage, hipStream_t s) {
+  HostStage hs{};
+  if (host_stage) hs = *(const HostStage*)host_stage;
+  plan_kernel<<<1, 1024, 0, s>>>(ids, n_assign, layer, E, n_slots, slot_table, owner, last_use, (CacheCtl*)ctl,
+                                 policy, BP, BH, miss_mask, (PlanOut*)plan, hs);
+  return hipGetLastError();
+}
+
+// grid: workgroups of the fill launch (the link saturates near 64).
+extern "C" hipError_t moe_launch_fill(const void* plan, const uint8_t* host_pool_dev, int layer, int E, size_t S,
+                                      uint8_t* slot_pool, int grid, hipStream_t s) {
+  const uintptr_t a = (uintptr_t)host_pool_dev | (uintptr_t)slot_pool | (uintptr_t)S;
+  const PlanOut* p = (const PlanOut*)plan;
+  if ((a & 15u) == 0)
+    fill_kernel<i32x4_t><<<grid, 256, 0, s>>>(p, host_pool_dev, layer, E, S, slot_pool);
+  else if ((a & 7u) == 0)
+    fill_kernel<unsigned long long><<<grid, 256, 0, s>>>(p, host_pool_dev, layer, E, S, slot_pool);
+  else if ((a & 3u) == 0)
+    fill_kernel<unsigned int><<<grid, 256, 0, s>>>(p, host_pool_dev, layer, E, S, slot_pool);
+  else
+    return hipErrorInvalidValue;
   return hipGetLastError();
 }
 
@@ -266,9 +355,9 @@ extern "C" hipError_t moe_launch_evict(const int32_t* experts, int n, int layer,
   return hipGetLastError();
 }
 
-extern "C" hipError_t moe_launch_install_layer(int layer, int base, int E, uint32_t tick, int32_t* slot_table,
+extern "C" hipError_t moe_launch_install_layer(int layer, int base, int E, void* ctl, int32_t* slot_table,
                                                int32_t* owner, uint32_t* last_use, hipStream_t s) {
-  install_layer_kernel<<<1, 256, 0, s>>>(layer, base, E, tick, slot_table, owner, last_use);
+  install_layer_kernel<<<1, 256, 0, s>>>(layer, base, E, (CacheCtl*)ctl, slot_table, owner, last_use);
   return hipGetLastError();
 }
 

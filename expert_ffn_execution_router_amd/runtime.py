@@ -164,6 +164,24 @@ class MoeRuntime:
                                      else self.stream_ptr(stream)))
         return info
 
+    def decode_layer_async(self, layer, hidden, router_w, bias, out, stream=None, host_stream=None):
+        """Enqueues the layer with no host read of the plan (capturable)."""
+        T = hidden.shape[0]
+        hs = host_stream if host_stream is not None else self._host_stream()
+        self._chk(B.moe_decode_layer_async(self.ctx, layer, hidden.data_ptr(), router_w.data_ptr(),
+                                           None if bias is None else bias.data_ptr(), T, out.data_ptr(),
+                                           self.stream_ptr(stream), self.stream_ptr(hs)))
+
+    def _host_stream(self):
+        if getattr(self, "_hs", None) is None:
+            self._hs = torch.cuda.Stream(device=self.device)
+        return self._hs
+
+    def plan_stats(self, reset=False):
+        out = B.moe_plan_totals()
+        self._chk(B.moe_plan_stats(self.ctx, ctypes.byref(out), 1 if reset else 0))
+        return out.as_dict()
+
     def prefill_layer(self, layer, hidden, router_w, bias, out, stream=None, copy_stream=None, double_buffer=True):
         T = hidden.shape[0]
         return self._chk(B.prefill_stream_layer(self.ctx, layer, hidden.data_ptr(), router_w.data_ptr(),

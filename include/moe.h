@@ -223,6 +223,44 @@ int moe_layer_forward(moe_ctx* ctx, int layer, const void* hidden, const float* 
 int moe_decode_layer(moe_ctx* ctx, int layer, const void* hidden, const float* router_w, const float* router_bias,
                      int T, void* out, moe_plan_info* info, void* compute_stream, void* copy_stream);
 
+/* The same layer with no host read of the plan (section 2.6: device-resident
+ * cache control, the fill set moved by one fixed-shape launch from a device
+ * table with a device valid count, the host branch as a node of the step):
+ * every step is enqueued and the call returns at once.
+ *   compute_stream: route, plan (the LRU clock advances on the device), the
+ *     indexed fill kernel (F from the device plan; reads the pinned host pool
+ *     through its device mapping at link speed), grouped GEMMs over H u F,
+ *     then, after the host branch, the combine;
+ *   host_stream: waits for the plan, copies it and the routed inputs to
+ *     pinned staging, runs the host set C on the thread pool in a
+ *     hipLaunchHostFunc callback, sends the fp32 partial back.  Used only
+ *     when the policy can route misses to the host (not OFFLOAD, or fewer
+ *     slots than E); the combine adds the partial only when C is not empty.
+ * Both streams may be captured into one HIP graph (fork/join through the
+ * context's events; the callback becomes a host node): replays plan afresh.
+ * Consecutive calls of one context are ordered through the streams; the
+ * staging buffers are shared, so a context runs one asynchronous step
+ * sequence at a time and makes no other host-pool call meanwhile.  Results
+ * equal moe_decode_layer's.  Errors: INVAL (layer, T), UNSUPPORTED (host pool
+ * without a device mapping: allocate it with moe_host_alloc), HIP.  Plan
+ * statistics: moe_plan_stats. */
+int moe_decode_layer_async(moe_ctx* ctx, int layer, const void* hidden, const float* router_w,
+                           const float* router_bias, int T, void* out, void* compute_stream, void* host_stream);
+
+/* Running totals of every plan of the context (device counters, summed by
+ * the cache-control kernel): planning calls, routed distinct experts, hits,
+ * misses m, fills q, host executions m - q, evictions of a resident expert;
+ * host_ms: wall time of the asynchronous path's host-branch callbacks. */
+typedef struct moe_plan_totals {
+  long long calls, n_unique, n_hit, m, q, n_host, n_evict;
+  double host_ms;
+} moe_plan_totals;
+
+/* Synchronises the device, reads the totals into out (may be NULL) and clears
+ * them when reset != 0.  Also reports (INVAL) a host-branch callback that saw
+ * an invalid plan since the last call. */
+int moe_plan_stats(moe_ctx* ctx, moe_plan_totals* out, int reset);
+
 /* Prefill with full-layer double buffering (section 2.2): layer l computes
  * from one E-slot buffer while layer l+1's complete expert set is copied into
  * the other on copy_stream.  Buffers are slots [0, E) and [E, 2E) of the
@@ -252,7 +290,8 @@ enum {
   MOE_STAGE_COMBINE = 7,  /* weighted unpermute-combine */
   MOE_STAGE_PLAN = 8,     /* cache-control kernel */
   MOE_STAGE_FIXUP = 9,    /* small-batch GEMMs: sums of the items cut between workgroups */
-  MOE_N_STAGES = 10
+  MOE_STAGE_FILL = 10,    /* indexed host-pool -> slot copy of the fill set (asynchronous decode) */
+  MOE_N_STAGES = 11
 };
 
 typedef struct {

@@ -228,3 +228,22 @@ def test_admit_evict_api():
             s.rt.admit(0, list(range(cfg.E)))      # more than the 10 slots
     finally:
         s.close()
+
+
+def test_calibrate_bandwidths():
+    """Both rates positive; the copy targets are left empty and the table
+    stays consistent."""
+    print("calibrate", flush=True)
+    cfg = _cfg(L=2)
+    s = Setup(cfg, seed=6, n_slots=10)
+    try:
+        bp, bh = s.rt.calibrate()
+        assert bp > 0.1 and bh > 0.1
+        tab = s.rt.slot_table().cpu().numpy()
+        assert (tab == -1).all()
+        s.rt.admit(0, list(range(8)))
+        torch.cuda.synchronize()
+        assert (s.rt.slot_table().cpu().numpy()[:8] >= 0).all()
+        assert s.rt.check_device_error() == 0
+    finally:
+        s.close()
