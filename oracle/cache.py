@@ -19,7 +19,10 @@ Sources (paper.oopus.info review of FreeToken):
     misses enter F is left to the replacement policy; C does not change
     residency;
   * section 2.6: one pass finds K least-recently-used candidate slots and the
-    miss path takes the first q of them.
+    miss path takes the first q of them;
+  * section 2.7: at a scheduler safe point the GPU expert cache is rebuilt
+    under a revised memory budget without restarting or reloading the host
+    pool; the output never depends on the cache size (section 2).
 Readings where the pages leave a step open:
   * "rounded to the nearest integer" = floor(x + 0.5) (round half up);
   * B_H <= B_P leaves no residual host bandwidth, so q = m;
@@ -29,7 +32,11 @@ Readings where the pages leave a step open:
     first; the i-th smallest expert of F goes to the i-th victim;
   * one tick per planning call; hits and fills are stamped with it;
   * if fewer slots are eligible than q, q shrinks to the eligible count and
-    the rest of M joins C (capacity cap).
+    the rest of M joins C (capacity cap);
+  * a rebuild to n' slots keeps the n' most recently used residents (last-use
+    stamp descending, ties to the lower slot), with their stamps; survivors
+    are packed into slots 0, 1, ... in the order of their old slots; the
+    clock keeps running.
 """
 from __future__ import annotations
 
@@ -133,6 +140,23 @@ class SlotCache:
         victims = elig[:len(need)]
         self._install(layer, need, victims)
         return victims
+
+    def resize(self, n_slots: int) -> list:
+        """Rebuild with n_slots slots; returns the (old slot, new slot) moves."""
+        used = [s for s in range(self.n_slots) if self.owner[s] >= 0]
+        keep = sorted(used, key=lambda s: (-self.last_use[s], s))[:n_slots]
+        keep.sort()
+        owner = [-1] * n_slots
+        last_use = [0] * n_slots
+        self.slot_of = [-1] * (self.L * self.E)
+        moves = []
+        for new, old in enumerate(keep):
+            owner[new] = self.owner[old]
+            last_use[new] = self.last_use[old]
+            self.slot_of[self.owner[old]] = new
+            moves.append((old, new))
+        self.owner, self.last_use, self.n_slots = owner, last_use, n_slots
+        return moves
 
     def evict(self, layer: int, experts) -> None:
         for e in experts:

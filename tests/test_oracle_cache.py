@@ -4,6 +4,8 @@ import math
 import os
 import random
 
+import numpy as np
+
 import pytest
 
 from oracle import cache as C
@@ -129,3 +131,50 @@ def test_admit_evict():
     assert sc.slot_of[8 + 3] == -1 and sc.owner[0] == -1 and sc.last_use[0] == 0
     v = sc.admit(0, [0, 1, 2])
     assert v == [0, 2, 3]         # empty slots (stamp 0) first, lower slot first
+
+
+def test_resize_keeps_most_recent():
+    """Shrinking keeps the most recently used residents (review section 2.7
+    rebuild under a smaller budget, LRU order of section 2.4)."""
+    sc = C.SlotCache(1, 32, 8)
+    for e in range(8):
+        sc.plan(0, [e], C.POLICY_OFFLOAD)
+    sc.resize(3)
+    assert sorted(e for e in range(32) if sc.slot_of[e] >= 0) == [5, 6, 7]
+    assert sc.plan(0, [7], C.POLICY_OFFLOAD)["m"] == 0
+    assert sc.plan(0, [4], C.POLICY_OFFLOAD)["m"] == 1
+    # growing keeps everything and adds empty slots
+    sc.resize(10)
+    assert sorted(e for e in range(32) if sc.slot_of[e] >= 0) == [4, 6, 7]
+    assert sc.owner[3:] == [-1] * 7
+
+
+def test_resize_matches_recency_list():
+    """One expert per planning call (every stamp distinct): the slot cache
+    with random rebuilds equals a plain recency-ordered list, miss for miss
+    and resident set for resident set."""
+    from collections import OrderedDict
+    rng = np.random.default_rng(12)
+    L, E = 3, 10
+    n = 7
+    sc = C.SlotCache(L, E, n)
+    lru = OrderedDict()
+    for step in range(600):
+        if step % 50 == 49:
+            n = int(rng.integers(1, 20))
+            moves = sc.resize(n)
+            while len(lru) > n:
+                lru.popitem(last=False)
+            assert all(new <= old for old, new in moves)
+        l, e = int(rng.integers(0, L)), int(rng.integers(0, E))
+        miss = (l, e) not in lru
+        if not miss:
+            lru.move_to_end((l, e))
+        else:
+            if len(lru) >= n:
+                lru.popitem(last=False)
+            lru[(l, e)] = True
+        p = sc.plan(l, [e], C.POLICY_OFFLOAD)
+        assert p["m"] == int(miss)
+        got = {(g // E, g % E) for g in range(L * E) if sc.slot_of[g] >= 0}
+        assert got == set(lru.keys())
