@@ -16,8 +16,9 @@ never the value), and one 8192-token prefill chunk streamed through the
 full-layer double buffer (with the ablation without it).
 
 --phases selects a subset (decode, e2e, prefill, cpu) for profiling runs, or
-adds the optional ones: formats (fp8 / MXFP4 shapes) and policies (miss rates
-of expert placements replayed over synthetic routing);
+adds the optional ones: formats (fp8 / MXFP4 shapes), policies (miss rates
+of expert placements replayed over synthetic routing) and elastic (cache
+rebuilds between decode steps);
 --copy-probe only runs a 1 GiB device copy (calibrates the byte counters).
 """
 from __future__ import annotations
@@ -402,6 +403,66 @@ def e2e_async(w: Workload, rc, hid, outs):
     return out
 
 
+def phase_elastic(w: Workload):
+    """Rebuilds of the expert cache at step boundaries (decode T=1, HYBRID,
+    one captured graph per step, captured again after every rebuild): 40% of
+    the pool, shrink in place to 20%, grow into a new pool of 57.8%.  Reports
+    each rebuild's wall time and each segment's step time and hit rate."""
+    import torch
+    import synth
+    from expert_ffn_execution_router_amd import binding as B
+    args, c = w.args, w.cfg
+    L, T, E = c.L, 1, c.E
+    W, K = 8, 16
+    segs = [("40%", 0.4, None), ("20% in place", 0.2, True), ("57.8% new pool", 0.578, False)]
+    keys = synth.decode_row_keys(c, args.seed + 2, len(segs) * (W + K), T)
+    hid = torch.from_numpy(synth.hidden_rows(c, keys.reshape(-1)).reshape(-1, L, T, c.H).view(np.int16)).to(w.dev)
+    outs = torch.empty(L, T, c.H, dtype=torch.bfloat16, device=w.dev)
+    rc = w.runtime(int(round(0.4 * L * E)), 64)
+    bp, bh = rc.calibrate()
+    rc.set_policy(B.MOE_POLICY_HYBRID, bp, bh)
+    hs, cap = torch.cuda.Stream(), torch.cuda.Stream()
+    xin = torch.empty_like(hid[0])
+    res = {"T": T, "policy": "hybrid", "steps_per_segment": K, "warmup_per_segment": W}
+    row = 0
+    for name, frac, in_place in segs:
+        n = int(round(frac * L * E))
+        if in_place is not None:
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            rc.resize(n, in_place=in_place)
+            dt = time.perf_counter() - t0
+        else:
+            dt = None
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cap):
+            for l in range(L):
+                rc.decode_layer_async(l, xin[l], w.R[l], w.bias[l], outs[l], stream=cap, host_stream=hs)
+        for s in range(W):
+            xin.copy_(hid[row])
+            row += 1
+            g.replay()
+        torch.cuda.synchronize()
+        rc.plan_stats(reset=True)
+        t0 = time.perf_counter()
+        for s in range(K):
+            xin.copy_(hid[row])
+            row += 1
+            g.replay()
+        torch.cuda.synchronize()
+        el = time.perf_counter() - t0
+        st = rc.plan_stats(reset=True)
+        res[name] = {"n_slots": n, "rebuild_s": dt, "ms_per_step": el / K * 1e3,
+                     "hit_rate": st["n_hit"] / max(st["n_unique"], 1), "misses_per_layer": st["m"] / max(st["calls"], 1)}
+        log(f"elastic {name}: {json.dumps(res[name])}")
+        del g
+    assert rc.check_device_error() == 0
+    rc.close()
+    del rc
+    torch.cuda.empty_cache()
+    return res
+
+
 def phase_prefill(w: Workload):
     """One prefill chunk through the full-layer double buffer, and without it."""
     import torch
@@ -656,7 +717,7 @@ def main():
     B.lib()   # fail loudly when the library is missing
     synth.lib()
     torch.cuda.init()
-    needs_w = bool(args.phase_set & {"decode", "e2e", "prefill", "cpu"})
+    needs_w = bool(args.phase_set & {"decode", "e2e", "prefill", "cpu", "elastic"})
     w = Workload(args) if needs_w else None
     c = w.cfg if needs_w else synth.CONFIGS[2].with_layers(args.layers)
     line = {
@@ -678,6 +739,8 @@ def main():
         line["decode_cache40_e2e"] = phase_e2e(w)
     if "prefill" in args.phase_set:
         line["prefill_chunk"] = phase_prefill(w)
+    if "elastic" in args.phase_set:
+        line["elastic_cache"] = phase_elastic(w)
     if "cpu" in args.phase_set:
         line["cpu_baseline"] = phase_cpu(w)
     if "formats" in args.phase_set:

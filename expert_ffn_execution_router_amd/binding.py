@@ -90,6 +90,7 @@ SIGNATURES = {
     "moe_decode_layer": (_i, [_vp, _i, _vp, _vp, _vp, _i, _vp, _P(moe_plan_info), _vp, _vp]),
     "moe_decode_layer_async": (_i, [_vp, _i, _vp, _vp, _vp, _i, _vp, _vp, _vp]),
     "moe_plan_stats": (_i, [_vp, _P(moe_plan_totals), _i]),
+    "slot_pool_resize": (_i, [_vp, _vp, ctypes.c_size_t, _i, _vp]),
     "prefill_stream_layer": (_i, [_vp, _i, _vp, _vp, _vp, _i, _vp, _vp, _vp, _i]),
     "moe_check_device_error": (_i, [_vp]),
     "moe_profile_begin": (_i, [_vp, _i, ctypes.c_uint]),
@@ -162,6 +163,7 @@ moe_layer_forward = _fn("moe_layer_forward")
 moe_decode_layer = _fn("moe_decode_layer")
 moe_decode_layer_async = _fn("moe_decode_layer_async")
 moe_plan_stats = _fn("moe_plan_stats")
+slot_pool_resize = _fn("slot_pool_resize")
 prefill_stream_layer = _fn("prefill_stream_layer")
 moe_check_device_error = _fn("moe_check_device_error")
 moe_profile_begin = _fn("moe_profile_begin")

@@ -108,8 +108,9 @@ WsLayout ws_layout(const moe_config& c) {
     return at;
   };
   L.slot_table = take((size_t)c.L * c.E * 4);
-  L.owner = take((size_t)c.n_slots * 4);
-  L.last_use = take((size_t)c.n_slots * 4);
+  // slot metadata sized for the largest pool, so a rebuild can grow it
+  L.owner = take((size_t)MOE_MAX_SLOTS * 4);
+  L.last_use = take((size_t)MOE_MAX_SLOTS * 4);
   L.ctl = take(sizeof(CacheCtl));
   L.err = take(64);
   L.logits = take(Tm * c.E * 4);
@@ -258,7 +259,8 @@ int check_cfg(const moe_config* c) {
   if (c->H < 256 || c->H % 256 || c->I < 128 || c->I % 128)
     return fail(nullptr, MOE_E_INVAL, "need H % 256 == 0 and I % 128 == 0");
   if (c->wfmt < 0 || c->wfmt > 2) return fail(nullptr, MOE_E_INVAL, "unknown weight format");
-  if (c->n_slots < 0 || c->n_slots > 8192) return fail(nullptr, MOE_E_UNSUPPORTED, "n_slots must be in [0, 8192]");
+  if (c->n_slots < 0 || c->n_slots > MOE_MAX_SLOTS)
+    return fail(nullptr, MOE_E_UNSUPPORTED, "n_slots must be in [0, 8192]");
   if (c->max_tokens < 1) return fail(nullptr, MOE_E_INVAL, "max_tokens must be >= 1");
   // the small-batch GEMM numbers its (item, K-chunk) units with 32-bit ints
   const double units = ((double)c->max_tokens * c->k / 16 + 1 + c->E) * (std::max(c->H, c->I) / 64) *
@@ -702,6 +704,55 @@ int slot_pool_admit(moe_ctx* c, int layer, const int32_t* experts, int n, void* 
   const int rc = issue_fills(c, layer, p.F, p.F_slot, p.q, s);
   if (rc) return rc;
   if (p.q < p.m) return fail(c, MOE_E_NOSLOTS, "not enough evictable slots to admit every expert");
+  return MOE_OK;
+}
+
+int slot_pool_resize(moe_ctx* c, void* d_slot_pool, size_t slot_bytes, int n_slots, void* stream) {
+  if (!c) return fail(nullptr, MOE_E_INVAL, "null ctx");
+  const moe_config& g = c->cfg;
+  const size_t S = c->bl.S;
+  if (n_slots < 0 || n_slots > MOE_MAX_SLOTS) return fail(c, MOE_E_INVAL, "n_slots outside [0, 8192]");
+  if ((n_slots > 0 && !d_slot_pool) || slot_bytes < (size_t)n_slots * S)
+    return fail(c, MOE_E_INVAL, "slot pool smaller than n_slots*S");
+  hipStream_t s = as_stream(stream);
+  HIPCHK(c, hipDeviceSynchronize());            // safe point: no work of the context in flight
+  const int n_old = g.n_slots;
+  std::vector<int32_t> owner(std::max(n_old, 1));
+  std::vector<uint32_t> last(std::max(n_old, 1));
+  if (n_old > 0) {
+    HIPCHK(c, hipMemcpy(owner.data(), c->owner, (size_t)n_old * 4, hipMemcpyDeviceToHost));
+    HIPCHK(c, hipMemcpy(last.data(), c->last_use, (size_t)n_old * 4, hipMemcpyDeviceToHost));
+  }
+  // survivors: the n_slots most recently used residents (stamp descending,
+  // ties to the lower slot), packed into slots 0, 1, ... in old-slot order
+  std::vector<int> keep;
+  for (int sl = 0; sl < n_old; ++sl)
+    if (owner[sl] >= 0) keep.push_back(sl);
+  std::stable_sort(keep.begin(), keep.end(), [&](int a, int b) { return last[a] > last[b]; });
+  if ((int)keep.size() > n_slots) keep.resize(n_slots);
+  std::sort(keep.begin(), keep.end());
+  std::vector<int32_t> table((size_t)g.L * g.E, -1), owner_n(std::max(n_slots, 1), -1);
+  std::vector<uint32_t> last_n(std::max(n_slots, 1), 0u);
+  uint8_t* dst = (uint8_t*)d_slot_pool;
+  for (int nw = 0; nw < (int)keep.size(); ++nw) {
+    const int old = keep[nw];
+    owner_n[nw] = owner[old];
+    last_n[nw] = last[old];
+    table[owner[old]] = nw;
+    // in place, nw <= old and every source above nw is still unmoved
+    if (dst != c->slot_pool || nw != old)
+      HIPCHK(c, hipMemcpyAsync(dst + (size_t)nw * S, c->slot_pool + (size_t)old * S, S, hipMemcpyDeviceToDevice, s));
+  }
+  HIPCHK(c, hipMemcpyAsync(c->slot_table, table.data(), table.size() * 4, hipMemcpyHostToDevice, s));
+  if (n_slots > 0) {
+    HIPCHK(c, hipMemcpyAsync(c->owner, owner_n.data(), (size_t)n_slots * 4, hipMemcpyHostToDevice, s));
+    HIPCHK(c, hipMemcpyAsync(c->last_use, last_n.data(), (size_t)n_slots * 4, hipMemcpyHostToDevice, s));
+  }
+  HIPCHK(c, hipStreamSynchronize(s));
+  c->slot_pool = dst;
+  c->cfg.n_slots = n_slots;
+  c->pf_next = -1;                              // the prefill streamer restarts its buffers
+  c->fills_pending = false;
   return MOE_OK;
 }
 

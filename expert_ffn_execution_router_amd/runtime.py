@@ -177,6 +177,21 @@ class MoeRuntime:
             self._hs = torch.cuda.Stream(device=self.device)
         return self._hs
 
+    def resize(self, n_slots, in_place=False, stream=None):
+        """Rebuilds the cache with n_slots slots (safe point).  in_place keeps
+        the current allocation (n_slots must fit it); otherwise a new pool is
+        allocated and the old one released after the call."""
+        need = max(n_slots, 1) * self.S
+        if in_place:
+            if need > self.slots.numel():
+                raise ValueError("in-place rebuild larger than the current slot pool")
+            pool = self.slots
+        else:
+            pool = torch.empty(need, dtype=torch.uint8, device=self.device)
+        self._chk(B.slot_pool_resize(self.ctx, pool.data_ptr(), pool.numel(), n_slots, self.stream_ptr(stream)))
+        self.slots = pool
+        self.cfg.n_slots = n_slots
+
     def plan_stats(self, reset=False):
         out = B.moe_plan_totals()
         self._chk(B.moe_plan_stats(self.ctx, ctypes.byref(out), 1 if reset else 0))

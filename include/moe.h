@@ -75,6 +75,9 @@ enum { MOE_W_BF16 = 0, MOE_W_FP8_E4M3_B128 = 1, MOE_W_MXFP4 = 2 };
  * at least 1 (section 2.5). */
 enum { MOE_POLICY_OFFLOAD = 0, MOE_POLICY_HOST = 1, MOE_POLICY_HYBRID = 2 };
 
+/* Largest slot pool a context can hold (also the bound of a rebuild). */
+enum { MOE_MAX_SLOTS = 8192 };
+
 typedef struct {
   int L, E, k, H, I;   /* layers, experts per layer (<= 256), top-k (<= 8), hidden, expert intermediate */
   int wfmt;            /* MOE_W_* */
@@ -188,6 +191,21 @@ int slot_pool_admit(moe_ctx* ctx, int layer, const int32_t* experts, int n, void
 
 /* Drops the given experts of a layer (host int32 [n]) from the cache. */
 int slot_pool_evict(moe_ctx* ctx, int layer, const int32_t* experts, int n);
+
+/* Rebuilds the expert cache under a new slot budget at a safe point (review
+ * section 2.7: no restart, the host pool is not reloaded; section 2: the
+ * cache size never changes outputs).  Synchronises the device first, so no
+ * work of the context may be in flight on other host threads.  The
+ * n_slots (<= MOE_MAX_SLOTS) most recently used residents survive with
+ * their recency (stamp descending, ties to the lower slot), packed into
+ * slots 0, 1, ... in the order of their old slots; their blobs are copied
+ * device-to-device on stream.  d_slot_pool (device, >= n_slots*S bytes,
+ * caller-owned) may be the current pool (in place: shrink, or grow within
+ * the caller's allocation) or a new one (the old pool may be freed once the
+ * call returns).  The prefill streamer restarts its buffers.  HIP graphs
+ * captured before the call hold the old pool and slot count and must be
+ * captured again.  Errors: INVAL (sizes), HIP. */
+int slot_pool_resize(moe_ctx* ctx, void* d_slot_pool, size_t slot_bytes, int n_slots, void* stream);
 
 /* Host branch (section 2.6): host_partial_out[t] = sum over j with
  * topk_ids[t,j] in the mask of topk_w[t,j] * FFN_e(hidden[t]), fp32, computed
