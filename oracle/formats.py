@@ -10,7 +10,10 @@ format definitions, not the pages:
   * OCP 8-bit floating point E4M3FN: bias 7, no infinities, S.1111.111 is NaN,
     max normal 448, subnormal step 2^-9;
   * OCP Microscaling v1.0: E2M1 elements (values 0, 0.5, 1, 1.5, 2, 3, 4, 6 with
-    a sign bit) and E8M0 scales 2^(e-127), 0xFF = NaN.
+    a sign bit) and E8M0 scales 2^(e-127), 0xFF = NaN;
+  * NVFP4 (NVIDIA's 4-bit format, named on the same pages): the same E2M1
+    elements, an E4M3 scale per 16 consecutive elements and one fp32 scale
+    per tensor; value = element * block scale * tensor scale.
 
 The encoders here serve the oracle's mirrored mode (the declared rounding
 points of the GPU path): they pick the nearest representable value by

@@ -24,7 +24,8 @@ Readings where the pages are silent (also listed in the design notes):
     * (W_up x)), silu(g) = g / (1 + exp(-g));
   * expert blob: gate, up, down row-major [out,in], then scale arrays in the
     same order (fp8: fp32 per 128x128 block; mxfp4: E8M0 per 32 inputs, two
-    E2M1 codes per byte, even element in the low nibble).
+    E2M1 codes per byte, even element in the low nibble; nvfp4: codes as
+    mxfp4, E4M3 per 16 inputs, then the three fp32 tensor scales).
 
 Two modes: "exact" (float64 throughout, weights dequantised exactly) and
 "mirrored" (float64 arithmetic with the GPU path's declared rounding and
@@ -41,7 +42,7 @@ import numpy as np
 from .formats import (bf16_to_f64, decode_e2m1, decode_e4m3, e8m0_to_f64, encode_e4m3,
                       round_to_bf16)
 
-FMT_BF16, FMT_FP8, FMT_MXFP4 = 0, 1, 2
+FMT_BF16, FMT_FP8, FMT_MXFP4, FMT_NVFP4 = 0, 1, 2, 3
 
 
 # ----------------------------------------------------------------------------
@@ -164,6 +165,22 @@ def dequant_expert(blob: np.ndarray, fmt: int, H: int, I: int):
         u = mat(b[npk:2 * npk], sc[ns:2 * ns], I, H)
         d = mat(b[2 * npk:3 * npk], sc[2 * ns:], H, I)
         return g, u, d
+    if fmt == FMT_NVFP4:
+        npk, ns = n // 2, n // 16
+        sc = b[3 * npk: 3 * npk + 3 * ns]
+        ts = b[3 * npk + 3 * ns: 3 * npk + 3 * ns + 12].view(np.float32).astype(np.float64)
+
+        def mat(p, s, t, rows, cols):
+            v = np.empty(rows * cols, dtype=np.float64)
+            v[0::2] = decode_e2m1(p & 0xF)
+            v[1::2] = decode_e2m1(p >> 4)
+            v = v.reshape(rows, cols // 16, 16) * decode_e4m3(s).reshape(rows, cols // 16, 1)
+            return v.reshape(rows, cols) * t
+
+        g = mat(b[:npk], sc[:ns], ts[0], I, H)
+        u = mat(b[npk:2 * npk], sc[ns:2 * ns], ts[1], I, H)
+        d = mat(b[2 * npk:3 * npk], sc[2 * ns:], ts[2], H, I)
+        return g, u, d
     raise ValueError(f"unknown weight format {fmt}")
 
 
@@ -213,8 +230,9 @@ def mirror_quant_mxfp8(v: np.ndarray) -> np.ndarray:
 
 def mirror_activation(v: np.ndarray, fmt: int) -> np.ndarray:
     """The GPU path's rounding of a GEMM input activation (x before GEMM 1,
-    A before GEMM 2): bf16 -> as is / bf16, fp8 -> per-128 E4M3, mxfp4 -> MXFP8."""
-    if fmt == FMT_BF16:
+    A before GEMM 2): bf16 and nvfp4 -> bf16, fp8 -> per-128 E4M3, mxfp4 ->
+    MXFP8."""
+    if fmt in (FMT_BF16, FMT_NVFP4):
         return round_to_bf16(v)
     if fmt == FMT_FP8:
         return mirror_quant_fp8_groups(v, 128)
@@ -223,8 +241,14 @@ def mirror_activation(v: np.ndarray, fmt: int) -> np.ndarray:
 
 def expert_ffn_mirrored(x: np.ndarray, Wg, Wu, Wd, fmt: int) -> np.ndarray:
     """Expert output Z with the GPU path's rounding points: x quantised (fp8,
-    mxfp4), A = silu(g)*u rounded to bf16 or quantised, Z rounded to bf16."""
-    xq = x if fmt == FMT_BF16 else mirror_activation(x, fmt)
+    mxfp4), A = silu(g)*u rounded to bf16 or quantised, Z rounded to bf16.
+    nvfp4 weights enter the bf16 MFMA as bf16 values of element * fp32(block
+    scale * tensor scale), within one bf16 rounding of the exact weights:
+    the mirror rounds the exact weights to bf16 (the two agree except where
+    the fp32 product rounds across a bf16 tie, a 2^-9 relative effect)."""
+    if fmt == FMT_NVFP4:
+        Wg, Wu, Wd = round_to_bf16(Wg), round_to_bf16(Wu), round_to_bf16(Wd)
+    xq = x if fmt in (FMT_BF16, FMT_NVFP4) else mirror_activation(x, fmt)
     g = xq @ Wg.T
     u = xq @ Wu.T
     a = silu(g) * u

@@ -33,8 +33,8 @@ _LIB_PATH = os.path.join(_HERE, "libsynth.so")
 _lib = None
 _table = None
 
-FMT_BF16, FMT_FP8, FMT_MXFP4 = 0, 1, 2
-FMT_NAMES = {FMT_BF16: "bf16", FMT_FP8: "fp8_e4m3_b128", FMT_MXFP4: "mxfp4"}
+FMT_BF16, FMT_FP8, FMT_MXFP4, FMT_NVFP4 = 0, 1, 2, 3
+FMT_NAMES = {FMT_BF16: "bf16", FMT_FP8: "fp8_e4m3_b128", FMT_MXFP4: "mxfp4", FMT_NVFP4: "nvfp4"}
 
 # tensor-kind tags mixed into the stream keys
 _K_POOL, _K_ROUTER, _K_BIAS, _K_HIDDEN, _K_REUSE, _K_LOGNORM = 1, 2, 3, 4, 5, 6
@@ -92,6 +92,8 @@ def expert_bytes(fmt: int, H: int, I: int) -> int:
         return 3 * n * 2
     if fmt == FMT_FP8:
         return 3 * n + 3 * (n // (128 * 128)) * 4
+    if fmt == FMT_NVFP4:
+        return 3 * n // 2 + 3 * n // 16 + 16
     return 3 * n // 2 + 3 * n // 32
 
 

@@ -18,6 +18,9 @@
  *   mxfp4: OCP E2M1 code of w*2^-x per 32 consecutive inputs, x =
  *          floor(log2 amax) - 2 stored as E8M0 (x+127); two codes per byte,
  *          the even element in the low nibble.
+ *   nvfp4: E2M1 code of w/(s_b*t) per 16 consecutive inputs, s_b = E4M3 of
+ *          amax_b/(6t), t = fp32 amax_matrix/(6*448) per matrix; codes as
+ *          mxfp4, then the E4M3 block scales, then the three t.
  */
 #include <stdint.h>
 #include <stddef.h>
@@ -168,12 +171,47 @@ static void fill_matrix_mxfp4(uint8_t* packed, uint8_t* e8m0, int rows, int cols
     }
 }
 
+static void fill_matrix_nvfp4(uint8_t* packed, uint8_t* e4m3, float* tensor_scale, int rows, int cols,
+                              uint64_t key, const float* table, float sigma) {
+  const size_t n = (size_t)rows * cols;
+  float amax = 0.0f;
+  for (size_t i = 0; i < n; ++i) {
+    const float a = fabsf(table[uniform16(key, i)] * sigma);
+    if (a > amax) amax = a;
+  }
+  const float t = amax > 0.0f ? amax / (6.0f * 448.0f) : 1.0f;
+  *tensor_scale = t;
+  const int nb = cols / 16;
+  for (int r = 0; r < rows; ++r)
+    for (int b = 0; b < nb; ++b) {
+      float w[16];
+      float bmax = 0.0f;
+      for (int c = 0; c < 16; ++c) {
+        w[c] = table[uniform16(key, (size_t)r * cols + b * 16 + c)] * sigma;
+        if (fabsf(w[c]) > bmax) bmax = fabsf(w[c]);
+      }
+      const uint8_t sc = enc_e4m3(bmax / (6.0f * t));
+      e4m3[(size_t)r * nb + b] = sc;
+      /* the decoded scale (E4M3: bias 7, subnormal step 2^-9) */
+      const int e = (sc >> 3) & 15, m = sc & 7;
+      const float sv = e == 0 ? ldexpf((float)m, -9) : ldexpf(1.0f + m / 8.0f, e - 7);
+      const float d = sv * t;
+      for (int c = 0; c < 16; c += 2) {
+        const uint8_t lo = d > 0.0f ? enc_e2m1(w[c] / d) : 0;
+        const uint8_t hi = d > 0.0f ? enc_e2m1(w[c + 1] / d) : 0;
+        packed[((size_t)r * cols + b * 16 + c) / 2] = (uint8_t)(lo | (hi << 4));
+      }
+    }
+}
+
 /* Bytes of one expert blob for format fmt (0 bf16, 1 fp8 e4m3 + 128x128 fp32
- * block scales, 2 mxfp4 + e8m0 per 32). */
+ * block scales, 2 mxfp4 + e8m0 per 32, 3 nvfp4 + e4m3 per 16 + 3 fp32
+ * tensor scales padded to 16 bytes). */
 size_t synth_expert_bytes(int fmt, int H, int I) {
   size_t n = (size_t)H * I;
   if (fmt == 0) return 3 * n * 2;
   if (fmt == 1) return 3 * n + 3 * (n / (128 * 128)) * 4;
+  if (fmt == 3) return 3 * n / 2 + 3 * n / 16 + 16;
   return 3 * n / 2 + 3 * n / 32;
 }
 
@@ -193,6 +231,14 @@ void synth_expert_blob(uint8_t* out, int fmt, int H, int I, uint64_t key, const 
     fill_matrix_fp8(out, sc, I, H, kg, table, sigma);
     fill_matrix_fp8(out + n, sc + ns, I, H, ku, table, sigma);
     fill_matrix_fp8(out + 2 * n, sc + 2 * ns, H, I, kd, table, sigma);
+  } else if (fmt == 3) {
+    size_t np = n / 2, ns = n / 16;
+    uint8_t* sc = out + 3 * np;
+    float ts[4] = {0.0f, 0.0f, 0.0f, 0.0f};
+    fill_matrix_nvfp4(out, sc, &ts[0], I, H, kg, table, sigma);
+    fill_matrix_nvfp4(out + np, sc + ns, &ts[1], I, H, ku, table, sigma);
+    fill_matrix_nvfp4(out + 2 * np, sc + 2 * ns, &ts[2], H, I, kd, table, sigma);
+    memcpy(out + 3 * np + 3 * ns, ts, sizeof(ts));
   } else {
     size_t np = n / 2, ns = n / 32;
     uint8_t* sc = out + 3 * np;

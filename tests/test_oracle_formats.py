@@ -80,3 +80,64 @@ def test_bf16_decode_exact():
     bits = np.array([0x3F80, 0xC000, 0x0000, 0x4049], dtype=np.uint16)
     v = F.bf16_to_f64(bits)
     assert v[0] == 1.0 and v[1] == -2.0 and v[2] == 0.0 and v[3] == 3.140625
+
+
+def _nvfp4_blob(H, I, codes, scales, ts):
+    """Blob bytes from per-matrix nibble arrays (row-major, element order),
+    E4M3 scale codes [rows, cols/16] and the three tensor scales."""
+    parts = []
+    for c in codes:
+        c = np.asarray(c, dtype=np.uint8).reshape(-1)
+        parts.append((c[0::2] | (c[1::2] << 4)).astype(np.uint8))
+    parts += [np.asarray(s, dtype=np.uint8).reshape(-1) for s in scales]
+    parts.append(np.array(list(ts) + [0.0], dtype=np.float32).view(np.uint8))
+    return np.concatenate(parts)
+
+
+def test_nvfp4_layout_hand_values():
+    """A hand-built NVFP4 expert (H=32, I=16): element codes, E4M3 block
+    scales (1.0, 2.0, 0.5 and the subnormal 2^-9) and tensor scales with the
+    values written out from the format's definition."""
+    from oracle import moe as M
+    H, I = 32, 16
+    cg = np.zeros((I, H), np.uint8)
+    cg[0, 0::2], cg[0, 1::2] = 0x2, 0xB                # 1.0, -1.5
+    cg[3, :] = 0x7                                      # 6.0
+    sg = np.full((I, H // 16), 0x38, np.uint8)          # 1.0
+    sg[0, 1] = 0x40                                     # 2.0
+    sg[3, 0] = 0x30                                     # 0.5
+    cu = np.full((I, H), 0x1, np.uint8)                 # 0.5
+    su = np.full((I, H // 16), 0x01, np.uint8)          # 2^-9
+    cd = np.zeros((H, I), np.uint8)
+    cd[5, 3] = 0xF                                      # -6.0
+    sd = np.full((H, I // 16), 0x38, np.uint8)
+    blob = _nvfp4_blob(H, I, [cg, cu, cd], [sg, su, sd], [0.5, 4.0, 0.25])
+    assert blob.size == 3 * H * I // 2 + 3 * H * I // 16 + 16
+    g, u, d = M.dequant_expert(blob, M.FMT_NVFP4, H, I)
+    want0 = np.array([1.0, -1.5] * 8 + [2.0, -3.0] * 8) * 0.5
+    assert np.array_equal(g[0], want0)
+    assert np.array_equal(g[3], np.array([1.5] * 16 + [3.0] * 16))
+    assert np.count_nonzero(g) == 2 * H
+    assert np.all(u == 0.5 * 2.0 ** -9 * 4.0)
+    assert d[5, 3] == -1.5 and np.count_nonzero(d) == 1
+
+
+def test_nvfp4_synth_weights_track_their_draws():
+    """The generator's NVFP4 blob, decoded by the oracle, stays within one
+    E2M1 step (at most 1.07 x block amax / 6, the block scale rounded to E4M3)
+    of the N(0, sigma) values it quantised, element by element."""
+    import dataclasses
+    import synth
+    from oracle import moe as M
+    cfg = dataclasses.replace(synth.CONFIGS[1], H=256, I=128, fmt=synth.FMT_NVFP4)
+    blob = synth.expert_blob(cfg, 3, 0, 5)
+    assert blob.size == cfg.expert_bytes
+    g, u, d = M.dequant_expert(blob, cfg.fmt, cfg.H, cfg.I)
+    k = synth.lib().synth_key(synth.pool_key(cfg, 3), 5)
+    for j, (w, rows, cols) in enumerate(((g, 128, 256), (u, 128, 256), (d, 256, 128))):
+        draw = synth.normal_f32(rows * cols, synth.lib().synth_key(k, j + 1), cfg.w_sigma).astype(np.float64)
+        draw = draw.reshape(rows, cols)
+        bmax = np.abs(draw.reshape(rows, cols // 16, 16)).max(axis=2)
+        err = np.abs(w - draw).reshape(rows, cols // 16, 16).max(axis=2)
+        assert np.all(err <= 1.07 * bmax / 6.0 + 1e-12)
+        assert np.corrcoef(w.ravel(), draw.ravel())[0, 1] > 0.99
