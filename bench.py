@@ -511,8 +511,9 @@ def phase_prefill(w: Workload):
 
 
 def phase_formats(args):
-    """The fp8 (43-layer E=256 top-6 H=4096 I=2048 shape) and MXFP4 (16-layer
-    E=256 top-8 H=6144 I=2048 shape) paths with every expert resident:
+    """The fp8 (43-layer E=256 top-6 H=4096 I=2048 shape), MXFP4 (16-layer
+    E=256 top-8 H=6144 I=2048 shape) and NVFP4 (the 48-layer E=128 top-8
+    H=2048 I=768 decode shape) paths with every expert resident:
     decode steps at the small token counts, and one prefill-shaped batch per
     layer.  Layers are cut to --format-layers so the pools fit host memory;
     per-layer work is unchanged."""
@@ -521,10 +522,16 @@ def phase_formats(args):
     from expert_ffn_execution_router_amd.runtime import HostPool, MoeRuntime
     out = {}
     dev = torch.device("cuda:0")
-    for cid, dec_T, pf_T, pf_bound in ((4, (1, 32), 4096, "hbm"), (5, (1,), 16384, "mfma")):
-        c = synth.CONFIGS[cid].with_layers(args.format_layers)
+    import dataclasses
+    for cid, dec_T, pf_T, pf_bound in ((4, (1, 32), 4096, "hbm"), (5, (1,), 16384, "mfma"),
+                                       (6, (1, 32, 64), 8192, "hbm")):
+        if cid == 6:       # the decode shape with NVFP4 experts (the pages' laptop build of that model)
+            c = dataclasses.replace(synth.CONFIGS[2], name="decode_nvfp4", fmt=synth.FMT_NVFP4)
+            c = c.with_layers(args.format_layers)
+        else:
+            c = synth.CONFIGS[cid].with_layers(args.format_layers)
         L, E, k, H, I, S = c.L, c.E, c.k, c.H, c.I, c.expert_bytes
-        name = {4: "fp8_e4m3_b128", 5: "mxfp4"}[cid]
+        name = {4: "fp8_e4m3_b128", 5: "mxfp4", 6: "nvfp4"}[cid]
         pool = HostPool(L * E * S)
         synth.fill_pool(pool.ptr, c, args.seed)
         R = [torch.from_numpy(synth.router_weights(c, args.seed, l)).to(dev) for l in range(L)]
@@ -568,7 +575,8 @@ def phase_formats(args):
             wall = (time.perf_counter() - t0) / (K * L)
             assert rt.check_device_error() == 0
             st = {n: v["ms"] / v["launches"] * 1e3 for n, v in prof.items() if isinstance(v, dict) and v["launches"]}
-            g1_bytes = float(n_active.mean() * wgu + T * k * H + T * k * I * 4)
+            xb, ab = (2, 2) if cid == 6 else (1, 4)        # token and A bytes per value
+            g1_bytes = float(n_active.mean() * wgu + T * k * H * xb + T * k * I * ab)
             layer_bytes = float(n_active.mean() * S + E * H * 4 + 2 * T * H * 2)
             gpu_us = sum(st.values())
             res[f"decode_T{T}"] = {
@@ -594,12 +602,13 @@ def phase_formats(args):
         st = {n: v["ms"] / v["launches"] * 1e3 for n, v in prof.items() if isinstance(v, dict) and v["launches"]}
         gemm_us = st["gemm1"] + st["gemm2"] + st.get("fixup", 0.0) * 2
         flops = 6.0 * pf_T * k * H * I
-        peak = {4: FP8_PEAK, 5: FP4_PEAK}[cid]
+        peak = {4: FP8_PEAK, 5: FP4_PEAK, 6: BF16_PEAK}[cid]
         res[f"prefill_T{pf_T}"] = {
             "bound": pf_bound, "gemm_us": gemm_us, "gpu_layer_us": sum(st.values()), "stage_us": st,
             "weights_hbm_frac": E * S / (gemm_us * 1e-6) / HBM_PEAK,
             "mfma_frac": flops / (gemm_us * 1e-6) / peak, "mfma_peak_TFLOPs": peak / 1e12,
-            "kernel": "gemm_pf_q8 (LDS-tiled scaled-MFMA grouped GEMM)",
+            "kernel": ("gemm_dec (weight stream, NVFP4 dequantised to bf16 in registers)" if cid == 6
+                       else "gemm_pf_q8 (LDS-tiled scaled-MFMA grouped GEMM)"),
         }
         log(f"{name} prefill T={pf_T}: {json.dumps(res[f'prefill_T{pf_T}'])}")
         out[name] = res

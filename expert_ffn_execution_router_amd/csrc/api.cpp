@@ -84,6 +84,10 @@ BlobLayout blob_layout(const moe_config& c) {
     const size_t ns = n / (128 * 128);
     for (int i = 0; i < 3; ++i) { b.w[i] = i * n; b.s[i] = 3 * n + i * ns * 4; }
     b.S = 3 * n + 3 * ns * 4;
+  } else if (c.wfmt == MOE_W_NVFP4) {
+    // E4M3 block scales per 16 inputs, then the three fp32 tensor scales (16 bytes)
+    for (int i = 0; i < 3; ++i) { b.w[i] = i * (n / 2); b.s[i] = 3 * (n / 2) + i * (n / 16); }
+    b.S = 3 * (n / 2) + 3 * (n / 16) + 16;
   } else {
     for (int i = 0; i < 3; ++i) { b.w[i] = i * (n / 2); b.s[i] = 3 * (n / 2) + i * (n / 32); }
     b.S = 3 * (n / 2) + 3 * (n / 32);
@@ -124,7 +128,7 @@ WsLayout ws_layout(const moe_config& c) {
   L.wl = take(sizeof(WorkList));
   L.mask = take(64);
   L.plan = take(sizeof(PlanOut));
-  const bool q8 = c.wfmt != MOE_W_BF16;
+  const bool q8 = c.wfmt == MOE_W_FP8_E4M3_B128 || c.wfmt == MOE_W_MXFP4;   // quantised activations
   L.A = take((R + 1) * c.I * (q8 ? 4 : 2));   // + a spare row for the 8-bit large-batch GEMM's padding stores
   L.Aq = take(q8 ? R * c.I : 0);
   L.As = take(c.wfmt == MOE_W_FP8_E4M3_B128 ? R * (c.I / 128) * 4 : (q8 ? R * (c.I / 32) : 0));
@@ -258,7 +262,7 @@ int check_cfg(const moe_config* c) {
     return fail(nullptr, MOE_E_INVAL, "need 1 <= k <= 8, k <= E <= 256, L >= 1");
   if (c->H < 256 || c->H % 256 || c->I < 128 || c->I % 128)
     return fail(nullptr, MOE_E_INVAL, "need H % 256 == 0 and I % 128 == 0");
-  if (c->wfmt < 0 || c->wfmt > 2) return fail(nullptr, MOE_E_INVAL, "unknown weight format");
+  if (c->wfmt < 0 || c->wfmt > 3) return fail(nullptr, MOE_E_INVAL, "unknown weight format");
   if (c->n_slots < 0 || c->n_slots > MOE_MAX_SLOTS)
     return fail(nullptr, MOE_E_UNSUPPORTED, "n_slots must be in [0, 8192]");
   if (c->max_tokens < 1) return fail(nullptr, MOE_E_INVAL, "max_tokens must be >= 1");
@@ -288,7 +292,8 @@ int forward_experts(moe_ctx* c, const void* hidden, int T, const int32_t* slot_r
     c->fills_pending = false;
   }
   // many tokens per expert: LDS-tiled MFMA kernels; otherwise weight streaming
-  const bool tiled = T > 64 && (long)T * g.k >= 48L * g.E;
+  // (NVFP4 has no large-batch kernel: its weights stream at every size)
+  const bool tiled = T > 64 && (long)T * g.k >= 48L * g.E && g.wfmt != MOE_W_NVFP4;
   const int tile_mb = g.wfmt == MOE_W_BF16 ? moe_pf_tile_tokens() : moe_pf8_tile_tokens(g.wfmt);
   // weight streaming: m-blocks of 16 * ns tokens (each m-block reads the
   // expert's weights once; larger blocks cost LDS and idle MFMA rows)
@@ -318,19 +323,21 @@ int forward_experts(moe_ctx* c, const void* hidden, int T, const int32_t* slot_r
     STAGE(c, MOE_STAGE_GEMM2, s,
           moe_launch_gemm_pf(g.wfmt, 0, c->n_cu, c->wl, c->counts, c->offsets, c->slot_pool, b.S, b.w[2], 0, c->A,
                              nullptr, g.I, g.H, c->Z, s));
-  } else if (g.wfmt == MOE_W_BF16) {
+  } else if (g.wfmt == MOE_W_BF16 || g.wfmt == MOE_W_NVFP4) {
+    // bf16 tokens (gathered through perm_tok for GEMM 1), bf16 A; NVFP4
+    // weights carry their block-scale offsets
     STAGE(c, MOE_STAGE_GEMM1, s,
           moe_launch_gemm_dec(g.wfmt, 1, ns, ncu, c->wl, c->counts, c->offsets, c->slot_pool, b.S, b.w[0], b.w[1],
-                              0, 0, hidden, nullptr, c->perm_tok, g.H, g.I, c->A, c->part, 0, s));
+                              b.s[0], b.s[1], hidden, nullptr, c->perm_tok, g.H, g.I, c->A, c->part, 0, s));
     STAGE(c, MOE_STAGE_FIXUP, s,
           moe_launch_gemm_dec(g.wfmt, 1, ns, ncu, c->wl, c->counts, c->offsets, c->slot_pool, b.S, b.w[0], b.w[1],
-                              0, 0, hidden, nullptr, c->perm_tok, g.H, g.I, c->A, c->part, 1, s));
+                              b.s[0], b.s[1], hidden, nullptr, c->perm_tok, g.H, g.I, c->A, c->part, 1, s));
     STAGE(c, MOE_STAGE_GEMM2, s,
-          moe_launch_gemm_dec(g.wfmt, 0, ns, ncu, c->wl, c->counts, c->offsets, c->slot_pool, b.S, b.w[2], 0, 0, 0,
-                              c->A, nullptr, nullptr, g.I, g.H, c->Z, c->part, 0, s));
+          moe_launch_gemm_dec(g.wfmt, 0, ns, ncu, c->wl, c->counts, c->offsets, c->slot_pool, b.S, b.w[2], 0, b.s[2],
+                              0, c->A, nullptr, nullptr, g.I, g.H, c->Z, c->part, 0, s));
     STAGE(c, MOE_STAGE_FIXUP, s,
-          moe_launch_gemm_dec(g.wfmt, 0, ns, ncu, c->wl, c->counts, c->offsets, c->slot_pool, b.S, b.w[2], 0, 0, 0,
-                              c->A, nullptr, nullptr, g.I, g.H, c->Z, c->part, 1, s));
+          moe_launch_gemm_dec(g.wfmt, 0, ns, ncu, c->wl, c->counts, c->offsets, c->slot_pool, b.S, b.w[2], 0, b.s[2],
+                              0, c->A, nullptr, nullptr, g.I, g.H, c->Z, c->part, 1, s));
   } else {
     // activations quantised straight into grouped order (row p <- token perm_tok[p])
     STAGE(c, MOE_STAGE_QUANT_X, s,
@@ -791,9 +798,10 @@ int moe_host_ffn(const moe_config* cfg, const void* host_pool, int layer, const 
   if (!cfg || !host_pool || !hidden || !topk_ids || !topk_w || !miss_mask || !out)
     return fail(nullptr, MOE_E_INVAL, "null argument");
   if (cfg->E < 1 || cfg->E > 256 || cfg->k < 1 || cfg->k > cfg->E || cfg->H < 1 || cfg->I < 1 || layer < 0 ||
-      layer >= cfg->L || T < 0 || cfg->wfmt < 0 || cfg->wfmt > 2)
+      layer >= cfg->L || T < 0 || cfg->wfmt < 0 || cfg->wfmt > 3)
     return fail(nullptr, MOE_E_INVAL, "bad shape");
-  if ((cfg->wfmt == 1 && (cfg->H % 128 || cfg->I % 128)) || (cfg->wfmt == 2 && (cfg->H % 32 || cfg->I % 32)))
+  if ((cfg->wfmt == 1 && (cfg->H % 128 || cfg->I % 128)) || (cfg->wfmt == 2 && (cfg->H % 32 || cfg->I % 32)) ||
+      (cfg->wfmt == 3 && (cfg->H % 16 || cfg->I % 16)))
     return fail(nullptr, MOE_E_INVAL, "H and I must be multiples of the scale block");
   std::vector<int32_t> C;
   for (int e = 0; e < cfg->E; ++e)

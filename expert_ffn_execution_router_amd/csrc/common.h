@@ -12,7 +12,7 @@ typedef int i32x8_t __attribute__((__vector_size__(8 * sizeof(int))));
 
 #define DEV __device__ __forceinline__
 
-enum { WFMT_BF16 = 0, WFMT_FP8 = 1, WFMT_MXFP4 = 2 };
+enum { WFMT_BF16 = 0, WFMT_FP8 = 1, WFMT_MXFP4 = 2, WFMT_NVFP4 = 3 };
 
 // m-block size used when only the grouping (not a GEMM) reads the work list.
 constexpr int DEC_MB = 64;

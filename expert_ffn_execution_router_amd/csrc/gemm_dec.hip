@@ -53,6 +53,15 @@
 //    operand's lane group g holds K [16g, 16g+16) in bytes 0-15 and
 //    K [64+16g, 64+16g+16) in bytes 16-31; the E8M0 scale of lane group g
 //    covers K block [32g, 32g+32) of that lane's row (A) or column (B).
+//  * NVFP4 (E2M1 elements, E4M3 scale per 16 inputs, fp32 scale per
+//    matrix): gfx950's scaled MFMA takes only power-of-two block scales, so
+//    the weights are dequantised in registers to bf16 (element * block
+//    scale, exact: at most two and four significant bits) and go through the
+//    bf16 MFMA with bf16 tokens; the matrix's fp32 scale multiplies the fp32
+//    sums in the epilogue (gate and up before SwiGLU, down on Z).  Chunks
+//    are 256 K values: 128 bytes of codes and 16 scale bytes per weight row
+//    (8 lanes per row segment, pieces XOR-swizzled by row & 7), 512 bytes
+//    per token row.
 #include "common.h"
 
 namespace {
@@ -67,19 +76,24 @@ constexpr int CACHE_NT = 2;           // cache-policy bits of a nontemporal load
 template <int FMT, bool GATED, int NS>
 struct Cfg {
   static constexpr int NMAT = GATED ? 2 : 1;
-  static constexpr int CK = FMT == WFMT_BF16 ? 128 : (FMT == WFMT_FP8 ? 256 : 512);   // K per chunk
-  static constexpr int XB = FMT == WFMT_MXFP4 ? 512 : 256;   // token bytes per chunk
+  static constexpr bool NV = FMT == WFMT_NVFP4;
+  static constexpr bool BF_X = FMT == WFMT_BF16 || NV;       // bf16 tokens
+  static constexpr int CK = FMT == WFMT_BF16 ? 128 : (FMT == WFMT_MXFP4 ? 512 : 256);   // K per chunk
+  static constexpr int WB = NV ? 128 : 256;                   // weight bytes per row per chunk
+  static constexpr int WSZ = 16 * WB;                         // one wave's rows of one matrix
+  static constexpr int NWL = WSZ / 1024;                      // weight loads per wave and matrix
+  static constexpr int XB = (FMT == WFMT_MXFP4 || NV) ? 512 : 256;   // token bytes per chunk
   static constexpr int MB = 16 * NS;                          // tokens per m-block
   static constexpr int NXI = MB * XB / 1024 / NW;             // token loads per wave per chunk
   static constexpr int W_OFF = 0;
-  static constexpr int X_OFF = NMAT * NW * 4096;
+  static constexpr int X_OFF = NMAT * NW * WSZ;
   static constexpr int XS_OFF = X_OFF + MB * XB;
-  static constexpr int XS_BYTES = FMT == WFMT_BF16 ? 0 : NW * 256;
+  static constexpr int XS_BYTES = BF_X ? 0 : NW * 256;
   static constexpr int WS_OFF = XS_OFF + XS_BYTES;
   static constexpr int WS_BYTES = FMT == WFMT_BF16 ? 0 : (FMT == WFMT_FP8 ? NW * 256 : NMAT * NW * 256);
   static constexpr int STAGE = WS_OFF + WS_BYTES;
   // loads per wave per chunk: weights, tokens, token scales, weight scales
-  static constexpr int NI = 4 * NMAT + NXI + (FMT == WFMT_BF16 ? 0 : 1) +
+  static constexpr int NI = NWL * NMAT + NXI + (BF_X ? 0 : 1) +
                             (FMT == WFMT_BF16 ? 0 : (FMT == WFMT_FP8 ? 1 : NMAT));
   static constexpr int NACC = NMAT * NS;
   static_assert(NXI >= 1 && NXI * NW * 1024 == MB * XB, "token chunk must split evenly over the waves");
@@ -127,18 +141,29 @@ DEV f32x4_t* part_tile(f32x4_t* part, long bb, int i, long U, long G, int KC, in
 
 // Output values of one wave's accumulators of an item (SwiGLU for GEMM 1):
 // lane holds weight rows 4*lg..+3 (output columns) of token lr of each
-// 16-token sub-tile; gate in acc[ms], up in acc[NS + ms].
-template <bool GATED, int NS>
-DEV void activate(const f32x4_t* acc, f32x4_t* val) {
+// 16-token sub-tile; gate in acc[ms], up in acc[NS + ms].  SCALED: the
+// matrices' fp32 scales s0 (gate, or down) and s1 (up) multiply the sums.
+template <bool GATED, int NS, bool SCALED = false>
+DEV void activate(const f32x4_t* acc, f32x4_t* val, float s0 = 1.0f, float s1 = 1.0f) {
 #pragma unroll
   for (int ms = 0; ms < NS; ++ms) {
     if (GATED) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) val[ms][i] = silu_mul(acc[ms][i], acc[NS + ms][i]);
+      for (int i = 0; i < 4; ++i)
+        val[ms][i] = SCALED ? silu_mul(acc[ms][i] * s0, acc[NS + ms][i] * s1) : silu_mul(acc[ms][i], acc[NS + ms][i]);
     } else {
-      val[ms] = acc[ms];
+      val[ms] = SCALED ? acc[ms] * s0 : acc[ms];
     }
   }
+}
+
+// NVFP4: the fp32 scales of an expert's matrices, after its block scales
+// (gate, up, down); n = K * N elements per matrix.
+DEV void nv_tensor_scales(const uint8_t* pool, size_t S, int slot, int K, int N, bool gated, float& s0, float& s1) {
+  const size_t n = (size_t)K * N;
+  const float* t = (const float*)(pool + (size_t)slot * S + 3 * (n / 2) + 3 * (n / 16));
+  s0 = gated ? t[0] : t[2];
+  s1 = gated ? t[1] : 1.0f;
 }
 
 // Store the output values (fp32 for GEMM 1 of the 8-bit formats, else bf16).
@@ -151,7 +176,7 @@ DEV void store_out(const f32x4_t* val, const Item& it, int wave, int lane, int N
     const int t = ms * 16 + lr;
     if (t >= it.nrows) continue;
     const size_t o = (size_t)(it.row0 + t) * N + col;
-    if (GATED && FMT != WFMT_BF16) {
+    if (GATED && (FMT == WFMT_FP8 || FMT == WFMT_MXFP4)) {
       *(f32x4_t*)((float*)out + o) = val[ms];
     } else {
       uint2 pk;
@@ -195,7 +220,7 @@ gemm_dec(const WorkList* __restrict__ wl, const int32_t* __restrict__ counts, co
   extern __shared__ __align__(16) uint8_t ring[];
   __shared__ int l_pref[257], l_slot[256], l_row0[256], l_cnt[256];
   // token row of each grouped row this workgroup touches (bf16 GEMM 1)
-  constexpr int ROWTAB = (FMT == WFMT_BF16 && GATED) ? 2048 : 1;
+  constexpr int ROWTAB = (FMT == WFMT_BF16 && GATED) ? 2048 : ((C::NV && GATED) ? 1024 : 1);
   __shared__ int l_rows[ROWTAB];
   const int wave = uni(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int lr = lane & 15, lg = lane >> 4;
@@ -225,7 +250,7 @@ gemm_dec(const WorkList* __restrict__ wl, const int32_t* __restrict__ counts, co
 
   // bytes of one weight row and of one token row
   const int wrow = FMT == WFMT_BF16 ? K * 2 : (FMT == WFMT_FP8 ? K : K / 2);
-  const int xrow = FMT == WFMT_BF16 ? K * 2 : K;
+  const int xrow = C::BF_X ? K * 2 : K;
 
   // Items are visited in order: a cursor (m-block p, tile nt, active expert
   // a) moves to the next item without searching the work list.
@@ -279,11 +304,17 @@ gemm_dec(const WorkList* __restrict__ wl, const int32_t* __restrict__ counts, co
   // weight loads: instruction j covers rows 4j..4j+3 of the wave's 16; lane l
   // fetches piece (l&15) ^ row so that the lane-linear LDS placement is the
   // swizzled layout
+  // (NVFP4: instruction j covers rows 8j..8j+7, lane l piece (l&7) ^ (row&7))
   uint32_t w_lane[4];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int r = 4 * j + (lane >> 4);
-    w_lane[j] = (uint32_t)(16 * wave + r) * wrow + (((lane & 15) ^ r) << 4);
+  for (int j = 0; j < C::NWL; ++j) {
+    if (C::NV) {
+      const int r = 8 * j + (lane >> 3);
+      w_lane[j] = (uint32_t)(16 * wave + r) * wrow + (((lane & 7) ^ (r & 7)) << 4);
+    } else {
+      const int r = 4 * j + (lane >> 4);
+      w_lane[j] = (uint32_t)(16 * wave + r) * wrow + (((lane & 15) ^ r) << 4);
+    }
   }
   // token loads: instruction j of the wave covers tokens (wave*NXI + j)*per + ...
   constexpr int XPER = C::XB == 256 ? 4 : 2;
@@ -342,18 +373,19 @@ gemm_dec(const WorkList* __restrict__ wl, const int32_t* __restrict__ counts, co
     const int kc = iss_kc++;
     lds_u8_t* sb = (lds_u8_t*)ring + st * C::STAGE;
     const uint8_t* wb = pool + (size_t)ii.slot * S;
-    const bool wpart = kc * 256 + 256 > wrow;          // last chunk shorter than 256 bytes per row
+    const bool wpart = kc * C::WB + C::WB > wrow;      // last chunk shorter than WB bytes per row
 #pragma unroll
     for (int m = 0; m < C::NMAT; ++m) {
-      const uint8_t* mat = wb + (m ? woff1 : woff0) + (size_t)ii.n0 * wrow + (size_t)kc * 256;
+      const uint8_t* mat = wb + (m ? woff1 : woff0) + (size_t)ii.n0 * wrow + (size_t)kc * C::WB;
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
+      for (int j = 0; j < C::NWL; ++j) {
         uint32_t o = w_lane[j];
         if (FMT != WFMT_BF16 && wpart) {
-          const int r = 4 * j + (lane >> 4), p16 = ((lane & 15) ^ r) << 4;
-          o = (uint32_t)(16 * wave + r) * wrow + (p16 < wrow - kc * 256 ? p16 : 0);
+          const int r = C::NV ? 8 * j + (lane >> 3) : 4 * j + (lane >> 4);
+          const int p16 = (C::NV ? ((lane & 7) ^ (r & 7)) : ((lane & 15) ^ r)) << 4;
+          o = (uint32_t)(16 * wave + r) * wrow + (p16 < wrow - kc * C::WB ? p16 : 0);
         }
-        dma16_nt(mat + o, sb + C::W_OFF + (m * NW + wave) * 4096 + j * 1024);
+        dma16_nt(mat + o, sb + C::W_OFF + (m * NW + wave) * C::WSZ + j * 1024);
       }
     }
     const bool xpart = kc * C::XB + C::XB > xrow;
@@ -384,6 +416,16 @@ gemm_dec(const WorkList* __restrict__ wl, const int32_t* __restrict__ counts, co
         const int g = min(kc * 2 + h, kb - 1);
         dma4(wb + so + ((size_t)((ii.n0 + 16 * wave) / 128) * kb + g) * 4, sb + C::WS_OFF + wave * 256);
       }
+    } else if (C::NV) {
+      const int kb = K / 16;    // 16-K blocks per row
+#pragma unroll
+      for (int m = 0; m < C::NMAT; ++m) {
+        // weight scales: lane -> row lane/4 of the wave's 16, 4 bytes (16 per row per chunk)
+        const int r = lane >> 2, qd = lane & 3;
+        const int g = min(kc * 16 + qd * 4, kb - 4);
+        dma4(wb + (m ? soff1 : soff0) + (size_t)(ii.n0 + 16 * wave + r) * kb + g,
+             sb + C::WS_OFF + (m * NW + wave) * 256);
+      }
     } else if (FMT == WFMT_MXFP4) {
       const int kb = K / 32;    // 32-K blocks per row
       {
@@ -411,6 +453,8 @@ gemm_dec(const WorkList* __restrict__ wl, const int32_t* __restrict__ counts, co
   Cur ccur = cur_at(i_first);
   Item ci{};
   item_of(ccur, ci);
+  float ts0 = 1.0f, ts1 = 1.0f;             // NVFP4 matrix scales of the current item (epilogue)
+  if (C::NV) nv_tensor_scales(pool, S, ci.slot, K, N, GATED, ts0, ts1);
 
   auto compute = [&](int kc, int st) {
     const uint8_t* sb = ring + st * C::STAGE;
@@ -462,6 +506,61 @@ gemm_dec(const WorkList* __restrict__ wl, const int32_t* __restrict__ counts, co
           }
         }
       }
+    } else if (C::NV) {
+      // the 16 block-scale bytes of row lr of each matrix for this chunk
+      i32x4_t scv[C::NMAT];
+#pragma unroll
+      for (int m = 0; m < C::NMAT; ++m) scv[m] = lds16(sb + C::WS_OFF + (m * NW + wave) * 256 + lr * 16);
+      // K is a multiple of 128: a chunk holds 4 or 8 MFMA steps of 32; each
+      // half is converted in one batch (independent conversions back to
+      // back), then multiplied
+      const bool full = kc * 256 + 256 <= K;
+#pragma unroll
+      for (int hq = 0; hq < 2; ++hq) {
+        if (hq == 1 && !full) break;
+        // lane (row lr, group lg): K [32q + 8lg, +8) = 4 code bytes of piece q, one block scale
+        uint32_t cw[4][C::NMAT];
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+          for (int m = 0; m < C::NMAT; ++m)
+            cw[j][m] = *(const uint32_t*)(sb + C::W_OFF + (m * NW + wave) * C::WSZ + lr * C::WB +
+                                          (((4 * hq + j) ^ (lr & 7)) << 4) + 4 * lg);
+        i32x4_t wa[4][C::NMAT];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int q = 4 * hq + j;
+#pragma unroll
+          for (int m = 0; m < C::NMAT; ++m) {
+            // block 2q + lg/2 of the chunk: byte 2(q&1) + lg/2 of dword q/2
+            const int scw = (int)((uint32_t)scv[m][q >> 1] >> (8 * (2 * (q & 1) + (lg >> 1))));
+            const float sc = __builtin_amdgcn_cvt_f32_fp8(scw, 0);
+            const auto f0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw[j][m], 1.0f, 0);
+            const auto f1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw[j][m], 1.0f, 1);
+            const auto f2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw[j][m], 1.0f, 2);
+            const auto f3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw[j][m], 1.0f, 3);
+            wa[j][m][0] = (int)pack_bf16x2(f0[0] * sc, f0[1] * sc);
+            wa[j][m][1] = (int)pack_bf16x2(f1[0] * sc, f1[1] * sc);
+            wa[j][m][2] = (int)pack_bf16x2(f2[0] * sc, f2[1] * sc);
+            wa[j][m][3] = (int)pack_bf16x2(f3[0] * sc, f3[1] * sc);
+          }
+        }
+#pragma unroll
+        for (int ms = 0; ms < NS; ++ms) {
+          if (ms >= nms) break;
+          i32x4_t xv[4];
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            xv[j] = lds16(sb + C::X_OFF + (ms * 16 + lr) * C::XB + (((4 * (4 * hq + j) + lg) ^ lr) << 4));
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int m = 0; m < C::NMAT; ++m)
+              acc[m * NS + ms] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, wa[j][m]),
+                                                                        __builtin_bit_cast(bf16x8_t, xv[j]),
+                                                                        acc[m * NS + ms], 0, 0, 0);
+        }
+      }
     } else {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
@@ -511,7 +610,7 @@ gemm_dec(const WorkList* __restrict__ wl, const int32_t* __restrict__ counts, co
   };
   auto finish_item = [&](int i) {
     if ((long)i * KC >= u0 && (long)(i + 1) * KC <= u1) {
-      activate<GATED, NS>(acc, pend);
+      activate<GATED, NS, C::NV>(acc, pend, ts0, ts1);
       pit = ci;
       has_pend = true;
     } else if (i == i_first) {    // cut by a range boundary: gemm_dec_fix adds the parts
@@ -547,6 +646,7 @@ gemm_dec(const WorkList* __restrict__ wl, const int32_t* __restrict__ counts, co
       ++i;
       cur_next(ccur);
       item_of(ccur, ci);
+      if (C::NV) nv_tensor_scales(pool, S, ci.slot, K, N, GATED, ts0, ts1);
     }
     compute(kc, st);
     if (kc == KC - 1 || v == n - 1) {
@@ -577,7 +677,8 @@ gemm_dec(const WorkList* __restrict__ wl, const int32_t* __restrict__ counts, co
 template <int FMT, bool GATED, int NS>
 __global__ void __launch_bounds__(256)
 gemm_dec_fix(const WorkList* __restrict__ wl, const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
-             int K, int N, int grid, void* __restrict__ out, const f32x4_t* __restrict__ part) {
+             const uint8_t* __restrict__ pool, size_t S, int K, int N, int grid, void* __restrict__ out,
+             const f32x4_t* __restrict__ part) {
   using C = Cfg<FMT, GATED, NS>;
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int ntiles = N / ROWS;
@@ -602,8 +703,10 @@ gemm_dec_fix(const WorkList* __restrict__ wl, const int32_t* __restrict__ counts
   }
   Item it;
   decode_global(wl, counts, offsets, ntiles, C::MB, i, it);
+  float ts0 = 1.0f, ts1 = 1.0f;
+  if (C::NV) nv_tensor_scales(pool, S, it.slot, K, N, GATED, ts0, ts1);
   f32x4_t val[NS];
-  activate<GATED, NS>(acc, val);
+  activate<GATED, NS, C::NV>(acc, val, ts0, ts1);
   store_out<FMT, GATED, NS>(val, it, wave, lane, N, out);
 }
 
@@ -629,7 +732,7 @@ hipError_t launch_dec(int n_cu, const WorkList* wl, const int32_t* counts, const
   int grid = n_cu * per_cu;
   if (grid > MAX_BLOCKS) grid = MAX_BLOCKS - MAX_BLOCKS % N_XCD;
   if (fix)
-    gemm_dec_fix<FMT, GATED, NS><<<grid, 256, 0, s>>>(wl, counts, offsets, K, N, grid, out, part);
+    gemm_dec_fix<FMT, GATED, NS><<<grid, 256, 0, s>>>(wl, counts, offsets, pool, S, K, N, grid, out, part);
   else
     gemm_dec<FMT, GATED, NS><<<grid, 256, lds, s>>>(wl, counts, offsets, pool, S, woff0, woff1, soff0, soff1,
                                                     (const uint8_t*)X, (const uint8_t*)Xs, row_tok, K, N, out, part);
@@ -669,12 +772,15 @@ extern "C" hipError_t moe_launch_gemm_dec(int fmt, int gated, int ns, int n_cu, 
                                           size_t S, size_t woff0, size_t woff1, size_t soff0, size_t soff1,
                                           const void* X, const void* Xs, const int32_t* row_tok, int K, int N,
                                           void* out, void* part, int fix, hipStream_t s) {
-  if (N % ROWS || K % 128 || (fmt != WFMT_BF16 && row_tok)) return hipErrorInvalidValue;
+  if (N % ROWS || K % 128 || (fmt != WFMT_BF16 && fmt != WFMT_NVFP4 && row_tok)) return hipErrorInvalidValue;
   f32x4_t* p = (f32x4_t*)part;
   const bool f = fix != 0;
 #define MOE_DEC_ARGS ns, n_cu, wl, counts, offsets, pool, S, woff0, woff1, soff0, soff1, X, Xs, row_tok, K, N, out, p, f, s
   if (fmt == WFMT_BF16) return gated ? launch_ns<WFMT_BF16, true>(MOE_DEC_ARGS) : launch_ns<WFMT_BF16, false>(MOE_DEC_ARGS);
   if (fmt == WFMT_FP8) return gated ? launch_ns<WFMT_FP8, true>(MOE_DEC_ARGS) : launch_ns<WFMT_FP8, false>(MOE_DEC_ARGS);
+  if (fmt == WFMT_NVFP4)
+    return gated ? launch_ns<WFMT_NVFP4, true>(MOE_DEC_ARGS) : launch_ns<WFMT_NVFP4, false>(MOE_DEC_ARGS);
+  if (fmt != WFMT_MXFP4) return hipErrorInvalidValue;
   return gated ? launch_ns<WFMT_MXFP4, true>(MOE_DEC_ARGS) : launch_ns<WFMT_MXFP4, false>(MOE_DEC_ARGS);
 #undef MOE_DEC_ARGS
 }

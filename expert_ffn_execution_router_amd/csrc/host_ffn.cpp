@@ -67,6 +67,20 @@ void load_row(const HostFfnShape& sh, const uint8_t* blob, int mat, int r, float
     const uint8_t* q = blob + mat * n + (size_t)r * cols;
     const float* sc = (const float*)(blob + 3 * n) + mat * (n / 16384) + (size_t)(r / 128) * (cols / 128);
     for (int c = 0; c < cols; ++c) dst[c] = tb.e4m3[q[c]] * sc[c / 128];
+  } else if (sh.fmt == 3) {
+    // NVFP4: E4M3 block scale per 16 inputs and one fp32 scale per matrix
+    const uint8_t* p = blob + mat * (n / 2) + (size_t)r * (cols / 2);
+    const uint8_t* sc = blob + 3 * (n / 2) + mat * (n / 16) + (size_t)r * (cols / 16);
+    float t;
+    std::memcpy(&t, blob + 3 * (n / 2) + 3 * (n / 16) + 4 * mat, 4);
+    for (int b = 0; b < cols / 16; ++b) {
+      const float s = tb.e4m3[sc[b]] * t;
+      for (int c = 0; c < 16; c += 2) {
+        const uint8_t v = p[(b * 16 + c) / 2];
+        dst[b * 16 + c] = tb.e2m1[v & 15] * s;
+        dst[b * 16 + c + 1] = tb.e2m1[v >> 4] * s;
+      }
+    }
   } else {
     const uint8_t* p = blob + mat * (n / 2) + (size_t)r * (cols / 2);
     const uint8_t* sc = blob + 3 * (n / 2) + mat * (n / 32) + (size_t)r * (cols / 32);

@@ -42,6 +42,11 @@
  *     - mxfp4: E8M0 scale per 32 consecutive inputs of each row ([rows][cols/32],
  *              gate, up, down); two E2M1 codes per byte, even input in the low
  *              nibble; weight = E2M1 value * 2^(scale - 127).
+ *     - nvfp4: codes as mxfp4, then an E4M3FN scale per 16 consecutive inputs
+ *              of each row ([rows][cols/16], gate, up, down), then three fp32
+ *              tensor scales (gate, up, down) and 4 bytes of padding; weight =
+ *              E2M1 value * block scale * tensor scale.  Activations stay bf16
+ *              (the large-batch path streams weights as the small one does).
  *   out         bf16 [T, H] (device)
  */
 #ifndef MOE_H
@@ -67,7 +72,7 @@ enum {
   MOE_I_FALLBACK_ONDEMAND = 1 /* prefill ran on demand: fewer than 2E slots */
 };
 
-enum { MOE_W_BF16 = 0, MOE_W_FP8_E4M3_B128 = 1, MOE_W_MXFP4 = 2 };
+enum { MOE_W_BF16 = 0, MOE_W_FP8_E4M3_B128 = 1, MOE_W_MXFP4 = 2, MOE_W_NVFP4 = 3 };
 
 /* Miss policy (paper.oopus.info review, section 5 lists the backend switch
  * offload / cpu / hybrid): OFFLOAD fills every miss (q = m), HOST executes

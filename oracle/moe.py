@@ -242,12 +242,9 @@ def mirror_activation(v: np.ndarray, fmt: int) -> np.ndarray:
 def expert_ffn_mirrored(x: np.ndarray, Wg, Wu, Wd, fmt: int) -> np.ndarray:
     """Expert output Z with the GPU path's rounding points: x quantised (fp8,
     mxfp4), A = silu(g)*u rounded to bf16 or quantised, Z rounded to bf16.
-    nvfp4 weights enter the bf16 MFMA as bf16 values of element * fp32(block
-    scale * tensor scale), within one bf16 rounding of the exact weights:
-    the mirror rounds the exact weights to bf16 (the two agree except where
-    the fp32 product rounds across a bf16 tie, a 2^-9 relative effect)."""
-    if fmt == FMT_NVFP4:
-        Wg, Wu, Wd = round_to_bf16(Wg), round_to_bf16(Wu), round_to_bf16(Wd)
+    nvfp4 weights enter the bf16 MFMA as element * block scale (exact in
+    bf16) and the tensor scale multiplies the fp32 sums, so the weights are
+    not rounded here."""
     xq = x if fmt in (FMT_BF16, FMT_NVFP4) else mirror_activation(x, fmt)
     g = xq @ Wg.T
     u = xq @ Wu.T

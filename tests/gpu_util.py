@@ -10,7 +10,7 @@ import torch
 import synth
 from oracle import moe as M
 
-TOL = {0: 1e-2, 1: 3e-2, 2: 5e-2}      # max|diff| / max|ref| per weight format
+TOL = {0: 1e-2, 1: 3e-2, 2: 5e-2, 3: 1e-2}   # max|diff| / max|ref| per weight format
 MARGIN = 1e-4                         # tokens closer to a top-k tie are excluded
 
 

@@ -50,7 +50,8 @@ def _check_oracle(s, layer, x, out, host_set):
 
 @pytest.mark.parametrize("fmt,n_slots,policy,T", [(0, 12, B.MOE_POLICY_HYBRID, 5), (0, 12, B.MOE_POLICY_OFFLOAD, 3),
                                                   (0, 20, B.MOE_POLICY_OFFLOAD, 1), (0, 12, B.MOE_POLICY_HOST, 4),
-                                                  (1, 10, B.MOE_POLICY_HYBRID, 2), (2, 10, B.MOE_POLICY_OFFLOAD, 6)])
+                                                  (1, 10, B.MOE_POLICY_HYBRID, 2), (2, 10, B.MOE_POLICY_OFFLOAD, 6),
+                                                  (3, 10, B.MOE_POLICY_HYBRID, 3)])
 def test_async_equals_sync_decode(fmt, n_slots, policy, T):
     print(f"async decode fmt={fmt} n_slots={n_slots} policy={policy} T={T}", flush=True)
     cfg = shape(1, L=3, E=16, k=4, H=256, I=128, fmt=fmt)

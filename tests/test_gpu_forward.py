@@ -1,6 +1,6 @@
 """GPU parity of the MoE layer forward (router -> grouping -> grouped SwiGLU
 GEMMs -> combine) with every routed expert resident, against the mirrored
-oracle on the same bytes, for the three weight formats."""
+oracle on the same bytes, for the four weight formats."""
 import numpy as np
 import pytest
 import torch
@@ -14,6 +14,8 @@ CASES = {
     "fp8_small": dict(base=1, fmt=1, H=512, I=256),
     "mxfp4_small": dict(base=1, fmt=2, H=512, I=256),
     "bf16_mid": dict(base=1, E=32, k=4, H=1024, I=384),
+    "nvfp4_small": dict(base=1, fmt=3, H=512, I=256),
+    "nvfp4_mid": dict(base=1, fmt=3, E=32, k=4, H=1024, I=384),
 }
 
 
@@ -49,7 +51,7 @@ def test_forward_matches_oracle(setups, name, T):
     print(f"  err vs mirrored {e_m:.2e}, vs exact {e_x:.2e}, rows {n}")
 
 
-@pytest.mark.parametrize("name", ["bf16_tiny", "fp8_small", "mxfp4_small"])
+@pytest.mark.parametrize("name", ["bf16_tiny", "fp8_small", "mxfp4_small", "nvfp4_small"])
 def test_forward_is_deterministic(setups, name):
     s = _get(setups, name)
     x, xd = s.hidden(100, tag=5)

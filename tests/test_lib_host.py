@@ -73,7 +73,7 @@ def _run_host(B, cfg_s, seed, T, C, threads):
     return out, ref
 
 
-@pytest.mark.parametrize("fmt", [0, 1, 2])
+@pytest.mark.parametrize("fmt", [0, 1, 2, 3])
 @pytest.mark.parametrize("threads", [1, 3])
 def test_host_ffn_matches_oracle(B, fmt, threads):
     c = synth.CONFIGS[1]
