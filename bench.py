@@ -17,8 +17,9 @@ full-layer double buffer (with the ablation without it).
 
 --phases selects a subset (decode, e2e, prefill, cpu) for profiling runs, or
 adds the optional ones: formats (fp8 / MXFP4 shapes), policies (miss rates
-of expert placements replayed over synthetic routing) and elastic (cache
-rebuilds between decode steps);
+of expert placements replayed over synthetic routing), elastic (cache
+rebuilds between decode steps) and fallback (prefill with fewer than two
+layers of slots, and the prefill-to-decode hand-off);
 --copy-probe only runs a 1 GiB device copy (calibrates the byte counters).
 """
 from __future__ import annotations
@@ -510,6 +511,83 @@ def phase_prefill(w: Workload):
     return res
 
 
+def phase_fallback(w: Workload):
+    """The prefill regimes below two full layers of slots, and the hand-off
+    from a prefill chunk to decode: (a) 8192-token chunk with 1.5 layers of
+    slots (full layers through one buffer), (b) with half a layer of slots
+    (on demand, capacity overflow on the host; two layers only), (c) decode
+    T=1 steps right after a double-buffered chunk against the same steps
+    from a cold cache (40% of the pool, HYBRID)."""
+    import torch
+    import synth
+    from expert_ffn_execution_router_amd import binding as B
+    args, c = w.args, w.cfg
+    L, E, H = c.L, c.E, c.H
+    Tp = args.prefill_T
+    pcfg = synth.CONFIGS[3].with_layers(L)
+    hp = torch.empty(Tp, H, dtype=torch.int16, device=w.dev)
+    pk = synth.keys_range(synth.key(args.seed, pcfg.config_id, 4, 0xF111), 0, Tp)
+    hp.copy_(torch.from_numpy(synth.hidden_rows(pcfg, pk).view(np.int16)))
+    out_p = torch.empty(Tp, H, dtype=torch.bfloat16, device=w.dev)
+    comp, copy = torch.cuda.Stream(), torch.cuda.Stream()
+    res = {"T": Tp}
+
+    def chunk(rt, layers):
+        rcs = []
+        torch.cuda.synchronize()
+        t0 = time.perf_counter()
+        with torch.cuda.stream(comp):
+            for l in range(layers):
+                rcs.append(rt.prefill_layer(l, hp, w.R[l], None, out_p, stream=comp, copy_stream=copy))
+        torch.cuda.synchronize()
+        return time.perf_counter() - t0, rcs
+
+    rt = w.runtime(E + E // 2, Tp)
+    el, rcs = chunk(rt, L)
+    res["single_buffer"] = {"n_slots": E + E // 2, "chunk_s": el, "status": sorted(set(rcs)),
+                            "h2d_GBps": L * E * c.expert_bytes / el / 1e9}
+    log(f"fallback single buffer: {json.dumps(res['single_buffer'])}")
+    rt.close()
+    rt = w.runtime(E // 2, Tp)
+    rt.set_policy(B.MOE_POLICY_OFFLOAD)
+    el, rcs = chunk(rt, 2)
+    res["on_demand"] = {"n_slots": E // 2, "layers": 2, "s_per_layer": el / 2, "status": sorted(set(rcs))}
+    log(f"fallback on demand: {json.dumps(res['on_demand'])}")
+    rt.close()
+    # hand-off
+    rt = w.runtime(pcfg.n_slots, Tp)
+    bp, bh = rt.calibrate()
+    rt.set_policy(B.MOE_POLICY_HYBRID, bp, bh)
+    K = 4
+    keys = synth.decode_row_keys(c, args.seed + 3, K, 1)
+    hid = torch.from_numpy(synth.hidden_rows(c, keys.reshape(-1)).reshape(K, L, 1, H).view(np.int16)).to(w.dev)
+    o1 = torch.empty(1, H, dtype=torch.bfloat16, device=w.dev)
+
+    def decode_steps():
+        out = []
+        for s_ in range(K):
+            torch.cuda.synchronize()
+            t0 = time.perf_counter()
+            infos = [rt.decode_layer(l, hid[s_, l], w.R[l], w.bias[l], o1, copy_stream=copy) for l in range(L)]
+            torch.cuda.synchronize()
+            out.append({"ms": (time.perf_counter() - t0) * 1e3,
+                        "hit_rate": sum(i.n_hit for i in infos) / max(sum(i.n_unique for i in infos), 1)})
+        return out
+
+    rt.reset_cache()
+    chunk(rt, L)
+    warm = decode_steps()
+    rt.reset_cache()
+    torch.cuda.synchronize()
+    cold = decode_steps()
+    res["handoff"] = {"n_slots": pcfg.n_slots, "after_prefill": warm, "cold": cold}
+    log(f"hand-off: {json.dumps(res['handoff'])}")
+    assert rt.check_device_error() == 0
+    rt.close()
+    torch.cuda.empty_cache()
+    return res
+
+
 def phase_formats(args):
     """The fp8 (43-layer E=256 top-6 H=4096 I=2048 shape), MXFP4 (16-layer
     E=256 top-8 H=6144 I=2048 shape) and NVFP4 (the 48-layer E=128 top-8
@@ -726,7 +804,7 @@ def main():
     B.lib()   # fail loudly when the library is missing
     synth.lib()
     torch.cuda.init()
-    needs_w = bool(args.phase_set & {"decode", "e2e", "prefill", "cpu", "elastic"})
+    needs_w = bool(args.phase_set & {"decode", "e2e", "prefill", "cpu", "elastic", "fallback"})
     w = Workload(args) if needs_w else None
     c = w.cfg if needs_w else synth.CONFIGS[2].with_layers(args.layers)
     line = {
@@ -750,6 +828,8 @@ def main():
         line["prefill_chunk"] = phase_prefill(w)
     if "elastic" in args.phase_set:
         line["elastic_cache"] = phase_elastic(w)
+    if "fallback" in args.phase_set:
+        line["prefill_fallback_and_handoff"] = phase_fallback(w)
     if "cpu" in args.phase_set:
         line["cpu_baseline"] = phase_cpu(w)
     if "formats" in args.phase_set:

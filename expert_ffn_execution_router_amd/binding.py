@@ -21,6 +21,7 @@ MOE_E_PIN = -4
 MOE_E_NOT_RESIDENT = -5
 MOE_E_UNSUPPORTED = -6
 MOE_I_FALLBACK_ONDEMAND = 1
+MOE_I_SINGLE_BUFFER = 2
 
 MOE_W_BF16, MOE_W_FP8_E4M3_B128, MOE_W_MXFP4 = 0, 1, 2
 MOE_POLICY_OFFLOAD, MOE_POLICY_HOST, MOE_POLICY_HYBRID = 0, 1, 2

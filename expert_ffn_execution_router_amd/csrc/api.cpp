@@ -43,7 +43,9 @@ hipError_t moe_launch_gemm_pf(int fmt, int gated, int grid, const WorkList* wl, 
                               const void* X, const int32_t* row_tok, int K, int N, void* out, hipStream_t s);
 hipError_t moe_launch_combine(const uint16_t* Z, const int32_t* ids, const float* w, const int32_t* pos,
                               const uint32_t* miss_mask, const int32_t* slot_row, const float* hp,
-                              const int32_t* hp_count, int T, int k, int H, uint16_t* out, hipStream_t s);
+                              const int32_t* hp_count, int T, int k, int H, uint16_t* out, float* out_f32,
+                              hipStream_t s);
+hipError_t moe_launch_range_mask(int lo, int hi, int E, uint32_t* mask, hipStream_t s);
 hipError_t moe_launch_quant(int fmt, int src_bf16, const void* src, int rows, const int32_t* nrows_dev,
                             const int32_t* row_map, int cols, uint8_t* q, void* scale, hipStream_t s);
 hipError_t moe_launch_plan(const int32_t* ids, int n_assign, int layer, int E, int n_slots, int32_t* slot_table,
@@ -368,10 +370,10 @@ int route_only(moe_ctx* c, const void* hidden, const float* R, const float* bias
 }
 
 int combine(moe_ctx* c, const uint32_t* mask, const int32_t* row, const float* hp, int T, void* out, hipStream_t s,
-            const int32_t* hp_count = nullptr) {
+            const int32_t* hp_count = nullptr, float* out_f32 = nullptr) {
   STAGE(c, MOE_STAGE_COMBINE, s,
         moe_launch_combine(c->Z, c->ids, c->w, c->pos, mask, row, hp, hp_count, T, c->cfg.k, c->cfg.H,
-                           (uint16_t*)out, s));
+                           (uint16_t*)out, out_f32, s));
   return MOE_OK;
 }
 
@@ -963,14 +965,46 @@ int prefill_stream_layer(moe_ctx* c, int layer, const void* hidden, const float*
   hipStream_t s = as_stream(compute_stream), cs = as_stream(copy_stream);
   const size_t S = c->bl.S;
   const size_t layer_bytes = (size_t)g.E * S;
-  if (g.n_slots < 2 * g.E) {
-    // not enough room for two full layers: on-demand loading of what is routed
+  if (g.n_slots < g.E && g.n_slots > 0) {
+    // not even one full layer fits: the layer in expert ranges of n_slots,
+    // each copied in (LRU admission) and evaluated on the GPU; the ranges'
+    // weighted sums accumulate unrounded in hp and the last is rounded once
+    if (T == 0) return MOE_I_FALLBACK_ONDEMAND;
+    const int n = g.n_slots;
+    const int32_t* row = c->slot_table + (size_t)layer * g.E;
+    std::vector<int32_t> ex((size_t)n);
+    for (int lo = 0; lo < g.E; lo += n) {
+      const int hi = std::min(g.E, lo + n);
+      // the copies overwrite slots the previous range's kernels read
+      HIPCHK(c, hipEventRecord(c->done[0], s));
+      HIPCHK(c, hipStreamWaitEvent(cs, c->done[0], 0));
+      for (int e = lo; e < hi; ++e) ex[e - lo] = e;
+      rc = slot_pool_admit(c, layer, ex.data(), hi - lo, cs);
+      if (rc) return rc;
+      rc = route_only(c, hidden, R, bias, T, s);      // the admission staged its list in the ids buffer
+      if (rc) return rc;
+      HIPCHK(c, moe_launch_range_mask(lo, hi, g.E, c->mask, s));
+      rc = forward_experts(c, hidden, T, row, c->mask, s);
+      if (rc) return rc;
+      const bool first = lo == 0, last = hi == g.E;
+      rc = combine(c, c->mask, row, first ? nullptr : c->hp, T, out, s, nullptr, last ? nullptr : c->hp);
+      if (rc) return rc;
+    }
+    c->pf_next = -1;
+    return MOE_I_FALLBACK_ONDEMAND;
+  }
+  if (g.n_slots == 0) {
+    // no slots: every routed expert on the host
     const int saved = c->policy;
     c->policy = MOE_POLICY_OFFLOAD;
     rc = moe_decode_layer(c, layer, hidden, R, bias, T, out, nullptr, compute_stream, copy_stream);
     c->policy = saved;
     return rc ? rc : MOE_I_FALLBACK_ONDEMAND;
   }
+  // one full layer fits but not two: the same full-layer copies through a
+  // single buffer (copy, then compute; the next copy waits for the compute)
+  const bool single = g.n_slots < 2 * g.E;
+  if (single) double_buffer = 0;
   auto base_of = [&](int l) { return double_buffer ? (l & 1) * g.E : 0; };
   auto buf_of = [&](int l) { return double_buffer ? (l & 1) : 0; };
   auto issue_copy = [&](int l) -> int {
@@ -1006,7 +1040,7 @@ int prefill_stream_layer(moe_ctx* c, int layer, const void* hidden, const float*
     if (rc) return rc;
   }
   c->pf_next = layer + 1 < g.L ? layer + 1 : -1;
-  return MOE_OK;
+  return single ? MOE_I_SINGLE_BUFFER : MOE_OK;
 }
 
 int moe_calibrate(moe_ctx* c, double* B_P, double* B_H) {

@@ -16,8 +16,8 @@
 __global__ void __launch_bounds__(256)
 combine_kernel(const uint16_t* __restrict__ Z, const int32_t* __restrict__ ids, const float* __restrict__ w,
                const int32_t* __restrict__ pos, const uint32_t* __restrict__ miss_mask,
-               const int32_t* __restrict__ slot_row, const float* __restrict__ hp,
-               const int32_t* __restrict__ hp_count, int T, int k, int H, uint16_t* __restrict__ out) {
+               const int32_t* __restrict__ slot_row, const float* hp, const int32_t* __restrict__ hp_count, int T,
+               int k, int H, uint16_t* __restrict__ out, float* out_f32) {
   const int t = blockIdx.y;
   const int h = (blockIdx.x * 256 + threadIdx.x) * 8;
   if (t >= T || h >= H) return;
@@ -59,6 +59,11 @@ combine_kernel(const uint16_t* __restrict__ Z, const int32_t* __restrict__ ids, 
     const float4 b = *(const float4*)(hp + (size_t)t * H + h + 4);
     acc[0] += a.x; acc[1] += a.y; acc[2] += a.z; acc[3] += a.w;
     acc[4] += b.x; acc[5] += b.y; acc[6] += b.z; acc[7] += b.w;
+  }
+  if (out_f32) {            // unrounded partial sum (may overwrite hp in place: same thread, read first)
+    *(float4*)(out_f32 + (size_t)t * H + h) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    *(float4*)(out_f32 + (size_t)t * H + h + 4) = make_float4(acc[4], acc[5], acc[6], acc[7]);
+    return;
   }
   i32x4_t o;
 #pragma unroll
@@ -162,10 +167,10 @@ quant_mxfp8_kernel(const void* __restrict__ src, int rows, const int32_t* __rest
 extern "C" hipError_t moe_launch_combine(const uint16_t* Z, const int32_t* ids, const float* w, const int32_t* pos,
                                          const uint32_t* miss_mask, const int32_t* slot_row, const float* hp,
                                          const int32_t* hp_count, int T, int k, int H, uint16_t* out,
-                                         hipStream_t s) {
+                                         float* out_f32, hipStream_t s) {
   if (T == 0) return hipSuccess;
   dim3 g((H / 8 + 255) / 256, T);
-  combine_kernel<<<g, 256, 0, s>>>(Z, ids, w, pos, miss_mask, slot_row, hp, hp_count, T, k, H, out);
+  combine_kernel<<<g, 256, 0, s>>>(Z, ids, w, pos, miss_mask, slot_row, hp, hp_count, T, k, H, out, out_f32);
   return hipGetLastError();
 }
 

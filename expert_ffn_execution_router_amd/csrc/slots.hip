@@ -310,6 +310,18 @@ __global__ void free_slots_kernel(const int32_t* __restrict__ slots, int n, int3
   last_use[s] = 0u;
 }
 
+// Host-set bits of every expert outside [lo, hi) (one round of a layer
+// evaluated in expert ranges).
+__global__ void range_mask_kernel(int lo, int hi, int E, uint32_t* __restrict__ mask) {
+  const int wd = threadIdx.x;           // 8 threads, one 32-expert word each
+  uint32_t m = 0u;
+  for (int b = 0; b < 32; ++b) {
+    const int e = wd * 32 + b;
+    if (e < E && (e < lo || e >= hi)) m |= 1u << b;
+  }
+  mask[wd] = m;
+}
+
 // Empty every slot and the whole table.
 __global__ void reset_kernel(int n_table, int n_slots, int32_t* slot_table, int32_t* owner, uint32_t* last_use,
                              int* err) {
@@ -345,6 +357,11 @@ extern "C" hipError_t moe_launch_fill(const void* plan, const uint8_t* host_pool
     fill_kernel<unsigned int><<<grid, 256, 0, s>>>(p, host_pool_dev, layer, E, S, slot_pool);
   else
     return hipErrorInvalidValue;
+  return hipGetLastError();
+}
+
+extern "C" hipError_t moe_launch_range_mask(int lo, int hi, int E, uint32_t* mask, hipStream_t s) {
+  range_mask_kernel<<<1, 8, 0, s>>>(lo, hi, E, mask);
   return hipGetLastError();
 }
 

@@ -69,7 +69,8 @@ enum {
   MOE_E_PIN = -4,            /* pinned host allocation failed */
   MOE_E_NOT_RESIDENT = -5,   /* a routed expert neither resident nor masked (device flag) */
   MOE_E_UNSUPPORTED = -6,    /* shape outside the supported range */
-  MOE_I_FALLBACK_ONDEMAND = 1 /* prefill ran on demand: fewer than 2E slots */
+  MOE_I_FALLBACK_ONDEMAND = 1, /* prefill ran on demand: fewer than E slots */
+  MOE_I_SINGLE_BUFFER = 2      /* prefill streamed full layers through one buffer: E <= slots < 2E */
 };
 
 enum { MOE_W_BF16 = 0, MOE_W_FP8_E4M3_B128 = 1, MOE_W_MXFP4 = 2, MOE_W_NVFP4 = 3 };
@@ -288,8 +289,11 @@ int moe_plan_stats(moe_ctx* ctx, moe_plan_totals* out, int reset);
  * from one E-slot buffer while layer l+1's complete expert set is copied into
  * the other on copy_stream.  Buffers are slots [0, E) and [E, 2E) of the
  * pool, entered into the LRU table (survivors warm decode).  Call for
- * l = 0..L-1 in order; layer 0 also issues its own copy.  With fewer than 2E
- * slots it runs on demand and returns MOE_I_FALLBACK_ONDEMAND.
+ * l = 0..L-1 in order; layer 0 also issues its own copy.  With E to 2E-1
+ * slots the full layers go through one buffer (copy, then compute) and the
+ * call returns MOE_I_SINGLE_BUFFER; with fewer than E slots it runs on
+ * demand (section 2.2's fallback: the routed experts through the cache,
+ * capacity overflow on the host) and returns MOE_I_FALLBACK_ONDEMAND.
  * double_buffer = 0 serialises copy and compute (ablation). */
 int prefill_stream_layer(moe_ctx* ctx, int layer, const void* hidden, const float* router_w,
                          const float* router_bias, int T, void* out, void* compute_stream, void* copy_stream,

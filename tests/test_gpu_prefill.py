@@ -50,13 +50,27 @@ def test_prefill_matches_oracle_and_is_buffer_invariant(fmt):
         assert (t[cfg.L - 1] >= 0).all() and (t[cfg.L - 2] >= 0).all()
     finally:
         s.close()
-    for n_slots, dbuf, want_rc in [(2 * cfg.E, False, 0), (cfg.L * cfg.E, True, 0), (cfg.E, True, 1)]:
+    for n_slots, dbuf, want_rc in [(2 * cfg.E, False, 0), (cfg.L * cfg.E, True, 0), (cfg.E, True, 2),
+                                   (2 * cfg.E - 1, True, 2)]:
         print(f"  variant n_slots={n_slots} double_buffer={dbuf}", flush=True)
         s, outs, xs, rcs = _prefill(cfg, n_slots, T, double_buffer=dbuf)
         try:
             assert rcs == [want_rc] * cfg.L
             for a, b in zip(ref, outs):
                 assert np.array_equal(a, b.view(torch.int16).cpu().numpy())
+        finally:
+            s.close()
+    # fewer than E slots: the layer in expert ranges of n_slots on the GPU
+    # (the ranges' sums add in a different order: within tolerance, not bit
+    # for bit); 3 slots leave a short last range
+    for n_slots in (cfg.E // 2, 3):
+        print(f"  variant in ranges n_slots={n_slots}", flush=True)
+        s, outs, xs, rcs = _prefill(cfg, n_slots, T)
+        try:
+            assert rcs == [1] * cfg.L
+            assert s.rt.check_device_error() == 0
+            for layer in range(cfg.L):
+                compare(s, layer, xs[layer], outs[layer])
         finally:
             s.close()
 
