@@ -16,6 +16,7 @@
 #include <cstring>
 #include <thread>
 #include <vector>
+#include <immintrin.h>
 #include <mutex>
 #include <condition_variable>
 #include <functional>
@@ -28,6 +29,7 @@ namespace {
 struct Tables {
   float e4m3[256];
   float e2m1[16];
+  float e8m0[256];                    // 2^(c-127); 255 (NaN) is never stored
   Tables() {
     for (int c = 0; c < 256; ++c) {
       const int s = c >> 7, e = (c >> 3) & 15, m = c & 7;
@@ -37,6 +39,7 @@ struct Tables {
       else v = std::ldexp(1.0f + m / 8.0f, e - 7);
       e4m3[c] = s ? -v : v;
     }
+    for (int c = 0; c < 256; ++c) e8m0[c] = std::ldexp(1.0f, c - 127);
     for (int c = 0; c < 16; ++c) {
       const int s = c >> 3, e = (c >> 1) & 3, m = c & 1;
       const float v = e == 0 ? 0.5f * m : std::ldexp(1.0f + 0.5f * m, e - 1);
@@ -49,62 +52,94 @@ const Tables& tables() {
   return t;
 }
 
-// Dequantise row `r` of matrix `mat` (0 gate, 1 up, 2 down) into dst[cols].
+// Eight E2M1 codes (one per byte of the low 8 bytes of c8) as floats times
+// s: magnitude from a register table, sign bit moved to bit 31.
+inline __m256 e2m1x8(__m128i c8, __m256 lut, __m256 s) {
+  const __m256i idx = _mm256_cvtepu8_epi32(c8);
+  const __m256 mag = _mm256_permutevar8x32_ps(lut, idx);               // low 3 bits select
+  const __m256i sgn = _mm256_slli_epi32(_mm256_and_si256(idx, _mm256_set1_epi32(8)), 28);
+  return _mm256_mul_ps(_mm256_xor_ps(mag, _mm256_castsi256_ps(sgn)), s);
+}
+
+// 16 packed bytes = 32 E2M1 codes (even element in the low nibble), in
+// element order, into dst[0..32): codes 0-15 times s0, 16-31 times s1.
+inline void e2m1x32(const uint8_t* p, __m256 lut, __m256 s0, __m256 s1, float* dst) {
+  const __m128i b = _mm_loadu_si128((const __m128i*)p);
+  const __m128i m = _mm_set1_epi8(0x0F);
+  const __m128i lo = _mm_and_si128(b, m), hi = _mm_and_si128(_mm_srli_epi16(b, 4), m);
+  const __m128i e0 = _mm_unpacklo_epi8(lo, hi), e1 = _mm_unpackhi_epi8(lo, hi);   // codes 0-15, 16-31
+  _mm256_storeu_ps(dst, e2m1x8(e0, lut, s0));
+  _mm256_storeu_ps(dst + 8, e2m1x8(_mm_srli_si128(e0, 8), lut, s0));
+  _mm256_storeu_ps(dst + 16, e2m1x8(e1, lut, s1));
+  _mm256_storeu_ps(dst + 24, e2m1x8(_mm_srli_si128(e1, 8), lut, s1));
+}
+
+// Eight E4M3FN codes as floats times s: the 7 magnitude bits placed at the
+// top of an fp32 mantissa/exponent give value * 2^-120 (subnormal codes
+// land on fp32 subnormals, exact), so s carries the 2^120; sign to bit 31.
+// (The NaN code S.1111.111 is not decoded as NaN; stored pools never hold it.)
+inline __m256 e4m3x8(const uint8_t* p, __m256 s120) {
+  const __m256i v = _mm256_cvtepu8_epi32(_mm_loadl_epi64((const __m128i*)p));
+  const __m256i mag = _mm256_slli_epi32(_mm256_and_si256(v, _mm256_set1_epi32(0x7F)), 20);
+  const __m256i sgn = _mm256_slli_epi32(_mm256_and_si256(v, _mm256_set1_epi32(0x80)), 24);
+  return _mm256_mul_ps(_mm256_castsi256_ps(_mm256_or_si256(mag, sgn)), s120);
+}
+
+// Dequantise row `r` of matrix `mat` (0 gate, 1 up, 2 down) into dst[cols]
+// (AVX2; cols is a multiple of 128 for every format the library accepts).
 void load_row(const HostFfnShape& sh, const uint8_t* blob, int mat, int r, float* dst) {
-  const int rows = mat < 2 ? sh.I : sh.H;
   const int cols = mat < 2 ? sh.H : sh.I;
   const size_t n = (size_t)sh.H * sh.I;
   const Tables& tb = tables();
   if (sh.fmt == 0) {
     const uint16_t* w = (const uint16_t*)blob + mat * n + (size_t)r * cols;
-    for (int c = 0; c < cols; ++c) {
-      const uint32_t u = (uint32_t)w[c] << 16;
-      float f;
-      std::memcpy(&f, &u, 4);
-      dst[c] = f;
+    for (int c = 0; c < cols; c += 8) {
+      const __m256i v = _mm256_cvtepu16_epi32(_mm_loadu_si128((const __m128i*)(w + c)));
+      _mm256_storeu_ps(dst + c, _mm256_castsi256_ps(_mm256_slli_epi32(v, 16)));
     }
   } else if (sh.fmt == 1) {
     const uint8_t* q = blob + mat * n + (size_t)r * cols;
     const float* sc = (const float*)(blob + 3 * n) + mat * (n / 16384) + (size_t)(r / 128) * (cols / 128);
-    for (int c = 0; c < cols; ++c) dst[c] = tb.e4m3[q[c]] * sc[c / 128];
-  } else if (sh.fmt == 3) {
-    // NVFP4: E4M3 block scale per 16 inputs and one fp32 scale per matrix
-    const uint8_t* p = blob + mat * (n / 2) + (size_t)r * (cols / 2);
-    const uint8_t* sc = blob + 3 * (n / 2) + mat * (n / 16) + (size_t)r * (cols / 16);
-    float t;
-    std::memcpy(&t, blob + 3 * (n / 2) + 3 * (n / 16) + 4 * mat, 4);
-    for (int b = 0; b < cols / 16; ++b) {
-      const float s = tb.e4m3[sc[b]] * t;
-      for (int c = 0; c < 16; c += 2) {
-        const uint8_t v = p[(b * 16 + c) / 2];
-        dst[b * 16 + c] = tb.e2m1[v & 15] * s;
-        dst[b * 16 + c + 1] = tb.e2m1[v >> 4] * s;
-      }
+    const float p120 = std::ldexp(1.0f, 120);
+    for (int b = 0; b < cols / 128; ++b) {
+      const __m256 s = _mm256_set1_ps(sc[b] * p120);      // exact: a power-of-two factor
+      for (int c = b * 128; c < b * 128 + 128; c += 8) _mm256_storeu_ps(dst + c, e4m3x8(q + c, s));
     }
   } else {
+    // E2M1 magnitudes for codes 0..7
+    const __m256 lut = _mm256_setr_ps(0.0f, 0.5f, 1.0f, 1.5f, 2.0f, 3.0f, 4.0f, 6.0f);
     const uint8_t* p = blob + mat * (n / 2) + (size_t)r * (cols / 2);
-    const uint8_t* sc = blob + 3 * (n / 2) + mat * (n / 32) + (size_t)r * (cols / 32);
-    for (int b = 0; b < cols / 32; ++b) {
-      const float s = std::ldexp(1.0f, (int)sc[b] - 127);
-      for (int c = 0; c < 32; c += 2) {
-        const uint8_t v = p[(b * 32 + c) / 2];
-        dst[b * 32 + c] = tb.e2m1[v & 15] * s;
-        dst[b * 32 + c + 1] = tb.e2m1[v >> 4] * s;
+    if (sh.fmt == 3) {
+      // NVFP4: E4M3 block scale per 16 inputs and one fp32 scale per matrix
+      const uint8_t* sc = blob + 3 * (n / 2) + mat * (n / 16) + (size_t)r * (cols / 16);
+      float t;
+      std::memcpy(&t, blob + 3 * (n / 2) + 3 * (n / 16) + 4 * mat, 4);
+      for (int b = 0; b < cols / 32; ++b)
+        e2m1x32(p + b * 16, lut, _mm256_set1_ps(tb.e4m3[sc[2 * b]] * t), _mm256_set1_ps(tb.e4m3[sc[2 * b + 1]] * t),
+                dst + b * 32);
+    } else {
+      const uint8_t* sc = blob + 3 * (n / 2) + mat * (n / 32) + (size_t)r * (cols / 32);
+      for (int b = 0; b < cols / 32; ++b) {
+        const __m256 s = _mm256_set1_ps(tb.e8m0[sc[b]]);
+        e2m1x32(p + b * 16, lut, s, s, dst + b * 32);
       }
     }
   }
-  (void)rows;
 }
 
 inline float dot(const float* a, const float* b, int n) {
-  float s0 = 0.f, s1 = 0.f, s2 = 0.f, s3 = 0.f, s4 = 0.f, s5 = 0.f, s6 = 0.f, s7 = 0.f;
-  int i = 0;
-  for (; i + 8 <= n; i += 8) {
-    s0 += a[i] * b[i]; s1 += a[i + 1] * b[i + 1]; s2 += a[i + 2] * b[i + 2]; s3 += a[i + 3] * b[i + 3];
-    s4 += a[i + 4] * b[i + 4]; s5 += a[i + 5] * b[i + 5]; s6 += a[i + 6] * b[i + 6]; s7 += a[i + 7] * b[i + 7];
+  // n is a multiple of 128 (checked shapes): four independent 8-wide sums
+  __m256 s0 = _mm256_setzero_ps(), s1 = _mm256_setzero_ps(), s2 = _mm256_setzero_ps(), s3 = _mm256_setzero_ps();
+  for (int i = 0; i < n; i += 32) {
+    s0 = _mm256_fmadd_ps(_mm256_loadu_ps(a + i), _mm256_loadu_ps(b + i), s0);
+    s1 = _mm256_fmadd_ps(_mm256_loadu_ps(a + i + 8), _mm256_loadu_ps(b + i + 8), s1);
+    s2 = _mm256_fmadd_ps(_mm256_loadu_ps(a + i + 16), _mm256_loadu_ps(b + i + 16), s2);
+    s3 = _mm256_fmadd_ps(_mm256_loadu_ps(a + i + 24), _mm256_loadu_ps(b + i + 24), s3);
   }
-  for (; i < n; ++i) s0 += a[i] * b[i];
-  return ((s0 + s1) + (s2 + s3)) + ((s4 + s5) + (s6 + s7));
+  const __m256 s = _mm256_add_ps(_mm256_add_ps(s0, s1), _mm256_add_ps(s2, s3));
+  const __m128 h = _mm_add_ps(_mm256_castps256_ps128(s), _mm256_extractf128_ps(s, 1));
+  const __m128 q = _mm_add_ps(h, _mm_movehl_ps(h, h));
+  return _mm_cvtss_f32(_mm_add_ss(q, _mm_shuffle_ps(q, q, 1)));
 }
 
 }  // namespace
