@@ -33,8 +33,8 @@ hipError_t moe_launch_gemm_dec(int fmt, int gated, int ns, int n_cu, const WorkL
 size_t moe_dec_part_bytes();
 int moe_dec_max_ns(int fmt);
 int moe_pf_tile_tokens();
-int moe_pf8_tile_tokens(int fmt);
-hipError_t moe_launch_gemm_pf8(int fmt, int gated, int n_cu, const WorkList* wl, const int32_t* counts,
+int moe_pf8_tile_tokens(int fmt, int small);
+hipError_t moe_launch_gemm_pf8(int fmt, int gated, int small, int n_cu, const WorkList* wl, const int32_t* counts,
                                const int32_t* offsets, const uint8_t* pool, size_t S, size_t woff0, size_t woff1,
                                size_t soff0, size_t soff1, const void* X, const void* Xs, int K, int N, void* out,
                                int trash_row, hipStream_t s);
@@ -296,7 +296,10 @@ int forward_experts(moe_ctx* c, const void* hidden, int T, const int32_t* slot_r
   // many tokens per expert: LDS-tiled MFMA kernels; otherwise weight streaming
   // (NVFP4 has no large-batch kernel: its weights stream at every size)
   const bool tiled = T > 64 && (long)T * g.k >= 48L * g.E && g.wfmt != MOE_W_NVFP4;
-  const int tile_mb = g.wfmt == MOE_W_BF16 ? moe_pf_tile_tokens() : moe_pf8_tile_tokens(g.wfmt);
+  // 8-bit formats with few tokens per expert (at most 160 on average): the
+  // 128-token, three-stage variant (a weight stream more than a GEMM)
+  const int small8 = (long)T * g.k <= 160L * g.E ? 1 : 0;
+  const int tile_mb = g.wfmt == MOE_W_BF16 ? moe_pf_tile_tokens() : moe_pf8_tile_tokens(g.wfmt, small8);
   // weight streaming: m-blocks of 16 * ns tokens (each m-block reads the
   // expert's weights once; larger blocks cost LDS and idle MFMA rows)
   const int ns = std::min(T <= 16 ? 1 : (T <= 64 ? 2 : 4), moe_dec_max_ns(g.wfmt));
@@ -311,12 +314,13 @@ int forward_experts(moe_ctx* c, const void* hidden, int T, const int32_t* slot_r
     STAGE(c, MOE_STAGE_QUANT_X, s,
           moe_launch_quant(g.wfmt, 1, hidden, T * g.k, c->offsets + g.E, c->perm_tok, g.H, c->Xq, c->Xs, s));
     STAGE(c, MOE_STAGE_GEMM1, s,
-          moe_launch_gemm_pf8(g.wfmt, 1, c->n_cu, c->wl, c->counts, c->offsets, c->slot_pool, b.S, b.w[0], b.w[1],
+          moe_launch_gemm_pf8(g.wfmt, 1, small8, c->n_cu, c->wl, c->counts, c->offsets, c->slot_pool, b.S, b.w[0],
+                              b.w[1],
                               b.s[0], b.s[1], c->Xq, c->Xs, g.H, g.I, c->A, trash, s));
     STAGE(c, MOE_STAGE_QUANT_A, s,
           moe_launch_quant(g.wfmt, 0, c->A, T * g.k, c->offsets + g.E, nullptr, g.I, c->Aq, c->As, s));
     STAGE(c, MOE_STAGE_GEMM2, s,
-          moe_launch_gemm_pf8(g.wfmt, 0, c->n_cu, c->wl, c->counts, c->offsets, c->slot_pool, b.S, b.w[2], 0,
+          moe_launch_gemm_pf8(g.wfmt, 0, small8, c->n_cu, c->wl, c->counts, c->offsets, c->slot_pool, b.S, b.w[2], 0,
                               b.s[2], 0, c->Aq, c->As, g.I, g.H, c->Z, trash, s));
   } else if (tiled) {
     STAGE(c, MOE_STAGE_GEMM1, s,

@@ -40,7 +40,13 @@
 //     stored (to a spare trash row), a wave whose token half is empty skips
 //     its MFMAs;
 //   * GEMM 1 stores silu(g)*u in fp32 (the next pass quantises it), GEMM 2
-//     stores bf16.
+//     stores bf16;
+//   * few tokens per expert (a weight stream more than a GEMM): tiles of 128
+//     tokens and three LDS stages, so two chunks are in flight while one is
+//     multiplied; the wait before a chunk counts only loads (the ones this
+//     wave issued for the next chunk; loads complete in order, so nothing
+//     older can still be outstanding when that many remain), and a finished
+//     item's stores go out before the next chunk's loads.
 #include "common.h"
 
 namespace {
@@ -50,12 +56,13 @@ constexpr int Q_BK = 128;                       // K per chunk
 constexpr int Q_WAVES = 8;
 constexpr int N_XCD = 8;
 
-template <int FMT>
+template <int FMT, bool SMALL>
 struct QCfg {
   // most tokens per tile: fp8 keeps 32-byte A operands and a scaled partial
   // sum per MFMA, so its tile is 256 tokens (128 accumulators) to stay within
-  // 256 registers; MXFP4 takes 288 (144 accumulators)
-  static constexpr int BM = FMT == WFMT_MXFP4 ? 288 : 256;
+  // 256 registers; MXFP4 takes 288 (144 accumulators); SMALL: 128 tokens
+  static constexpr int BM = SMALL ? 128 : (FMT == WFMT_MXFP4 ? 288 : 256);
+  static constexpr int NST = SMALL ? 3 : 2;                       // LDS stages
   static constexpr int HALF = BM / 2;
   static constexpr int SUB = HALF / 16;                           // 16-token sub-tiles per half
   static constexpr int TLOADS = BM / 8 / (Q_WAVES / 2);           // 8-row token blocks per token wave
@@ -102,13 +109,13 @@ DEV void dma4(const void* src, lds_u8_t* dst) {
 // in grouped order ([rows, K] E4M3 codes) with scales Xs (fp8: fp32
 // [rows, K/128]; MXFP4: E8M0 [rows, K/32]).  K % 128 == 0; N % 128 (gated)
 // or 256 (not gated).  trash_row: a spare row of out for padding stores.
-template <int FMT, bool GATED>
+template <int FMT, bool GATED, bool SMALL>
 __global__ void __launch_bounds__(64 * Q_WAVES, 1)
 gemm_pf_q8(const WorkList* __restrict__ wl, const int32_t* __restrict__ counts,
            const int32_t* __restrict__ offsets, const uint8_t* __restrict__ pool, size_t S, size_t woff0,
            size_t woff1, size_t soff0, size_t soff1, const uint8_t* __restrict__ X, const uint8_t* __restrict__ Xs,
            int K, int N, void* __restrict__ out, int trash_row) {
-  using C = QCfg<FMT>;
+  using C = QCfg<FMT, SMALL>;
   extern __shared__ __align__(16) uint8_t lds[];
   __shared__ int l_pref[257], l_slot[256], l_row0[256], l_cnt[256];
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
@@ -230,6 +237,7 @@ gemm_pf_q8(const WorkList* __restrict__ wl, const int32_t* __restrict__ counts,
     decode(iss_it, t);
     set_sources(t);
   }
+  // returns the number of loads this wave issued (uniform per wave)
   auto issue = [&](int stage) __attribute__((always_inline)) {
     if (iss_c == nchunk) {
       iss_c = 0;
@@ -240,26 +248,37 @@ gemm_pf_q8(const WorkList* __restrict__ wl, const int32_t* __restrict__ counts,
     }
     const int kc = iss_c++;
     lds_u8_t* sb = (lds_u8_t*)lds + stage * C::STAGE;
+    int n = 0;
     if (wtok) {
       const uint8_t* xb_ = X + kc * 128;
 #pragma unroll
       for (int q = 0; q < C::TLOADS; ++q)
-        if (wave * C::TLOADS + q < tok_blocks) dma16(xb_ + src[q], sb + C::T_OFF + (wave * C::TLOADS + q) * 1024);
+        if (wave * C::TLOADS + q < tok_blocks) {
+          dma16(xb_ + src[q], sb + C::T_OFF + (wave * C::TLOADS + q) * 1024);
+          ++n;
+        }
       const uint8_t* xsb = Xs + kc * 4;         // fp32 scale kc, or E8M0 bytes 4kc..4kc+3
 #pragma unroll
       for (int i = 0; i < 2; ++i)
-        if (wave + 4 * i < C::NXS) dma4(xsb + xs_src[i], sb + C::XS_OFF + (wave + 4 * i) * 256);
+        if (wave + 4 * i < C::NXS) {
+          dma4(xsb + xs_src[i], sb + C::XS_OFF + (wave + 4 * i) * 256);
+          ++n;
+        }
     } else {
       const int wv = wave - Q_WAVES / 2;
       const uint8_t* wb_ = wbase + kc * C::WROWB;
 #pragma unroll
       for (int q = 0; q < C::WLOADS; ++q) dma16(wb_ + src[q], sb + C::W_OFF + (wv * C::WLOADS + q) * 1024);
+      n = C::WLOADS;
       if (FMT == WFMT_MXFP4) {
         dma4(wbase + ws_src + kc * 4, sb + C::WS_OFF + wv * 256);
+        ++n;
       } else if (wv == 0) {
         dma4(wbase + ws_src + kc * 4, sb + C::WS_OFF);
+        ++n;
       }
     }
+    return n;
   };
 
   // ---- operand reads (bytes inside a stage) -----------------------------------
@@ -371,17 +390,37 @@ gemm_pf_q8(const WorkList* __restrict__ wl, const int32_t* __restrict__ counts,
 
   // ---- the stream -------------------------------------------------------------
   // A finished item is stored at the start of the next iteration, ahead of
-  // that iteration's loads; with two stages every wait is vmcnt(0), which
-  // also covers stores that complete out of order with the loads.
-  issue(0);
+  // that iteration's loads.  Two stages: every wait is vmcnt(0), which also
+  // covers stores that complete out of order with the loads.  Three stages:
+  // the wait leaves outstanding only the loads issued for unit v+1 (the last
+  // issue, `last_n` of them); the stores went out before those loads.
+  (void)issue(0);
+  int last_n = 0;
+  if (C::NST == 3 && n_units > 1) last_n = issue(1);
   QItem ct;
   decode(it0, ct);
   QItem done{};
   bool pending = false;
   int c = 0, stage = 0;
   for (long v = 0; v < n_units; ++v) {
-    wait_vmcnt<0>();                            // this wave's loads of unit v have landed
-    barrier_keep_loads();                       // everyone's have; the other stage is free
+    if (C::NST == 3 && v + 1 < n_units) {
+      switch (last_n) {                         // this wave's loads of unit v have landed
+        case 0: wait_vmcnt<0>(); break;
+        case 1: wait_vmcnt<1>(); break;
+        case 2: wait_vmcnt<2>(); break;
+        case 3: wait_vmcnt<3>(); break;
+        case 4: wait_vmcnt<4>(); break;
+        case 5: wait_vmcnt<5>(); break;
+        case 6: wait_vmcnt<6>(); break;
+        case 7: wait_vmcnt<7>(); break;
+        case 8: wait_vmcnt<8>(); break;
+        case 9: wait_vmcnt<9>(); break;
+        default: wait_vmcnt<0>(); break;
+      }
+    } else {
+      wait_vmcnt<0>();
+    }
+    barrier_keep_loads();                       // everyone's have; the oldest stage is free
     if (pending) {
       store_item(done);
 #pragma unroll
@@ -390,9 +429,15 @@ gemm_pf_q8(const WorkList* __restrict__ wl, const int32_t* __restrict__ counts,
         for (int j = 0; j < C::SUB; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
       pending = false;
     }
-    if (v + 1 < n_units) issue(stage ^ 1);
+    __atomic_signal_fence(__ATOMIC_SEQ_CST);    // the stores stay ahead of the next loads
+    __builtin_amdgcn_sched_barrier(0);
+    if (C::NST == 2) {
+      if (v + 1 < n_units) (void)issue(stage ^ 1);
+    } else {
+      if (v + 2 < n_units) last_n = issue(stage == 0 ? 2 : stage - 1);
+    }
     if (ct.nrows > wm * C::HALF) compute(lds + stage * C::STAGE);
-    stage ^= 1;
+    stage = stage + 1 == C::NST ? 0 : stage + 1;
     if (++c == nchunk) {
       done = ct;
       pending = true;
@@ -403,47 +448,58 @@ gemm_pf_q8(const WorkList* __restrict__ wl, const int32_t* __restrict__ counts,
   if (pending) store_item(done);
 }
 
-extern "C" size_t moe_pf8_lds_bytes(int fmt) {
-  return 2 * (fmt == WFMT_MXFP4 ? QCfg<WFMT_MXFP4>::STAGE : QCfg<WFMT_FP8>::STAGE);
-}
-extern "C" int moe_pf8_tile_tokens(int fmt) { return fmt == WFMT_MXFP4 ? QCfg<WFMT_MXFP4>::BM : QCfg<WFMT_FP8>::BM; }
+template <int FMT, bool SMALL>
+static size_t lds_of() { return (size_t)QCfg<FMT, SMALL>::NST * QCfg<FMT, SMALL>::STAGE; }
 
-template <int FMT, bool GATED>
+extern "C" size_t moe_pf8_lds_bytes(int fmt, int small) {
+  if (fmt == WFMT_MXFP4) return small ? lds_of<WFMT_MXFP4, true>() : lds_of<WFMT_MXFP4, false>();
+  return small ? lds_of<WFMT_FP8, true>() : lds_of<WFMT_FP8, false>();
+}
+// Tokens per m-tile of the large-batch 8-bit kernel; small != 0: the variant
+// for few tokens per expert.
+extern "C" int moe_pf8_tile_tokens(int fmt, int small) {
+  if (small) return QCfg<WFMT_FP8, true>::BM;
+  return fmt == WFMT_MXFP4 ? QCfg<WFMT_MXFP4, false>::BM : QCfg<WFMT_FP8, false>::BM;
+}
+
+template <int FMT, bool GATED, bool SMALL>
 static hipError_t launch_q8(int n_cu, const WorkList* wl, const int32_t* counts, const int32_t* offsets,
                             const uint8_t* pool, size_t S, size_t woff0, size_t woff1, size_t soff0, size_t soff1,
                             const uint8_t* X, const uint8_t* Xs, int K, int N, void* out, int trash_row,
                             hipStream_t s) {
-  const size_t lds = 2 * QCfg<FMT>::STAGE;
+  const size_t lds = lds_of<FMT, SMALL>();
   static bool attr = false;
   if (!attr) {
-    hipError_t e =
-        hipFuncSetAttribute((const void*)gemm_pf_q8<FMT, GATED>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    hipError_t e = hipFuncSetAttribute((const void*)gemm_pf_q8<FMT, GATED, SMALL>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     attr = true;
   }
-  gemm_pf_q8<FMT, GATED><<<n_cu, 64 * Q_WAVES, lds, s>>>(wl, counts, offsets, pool, S, woff0, woff1, soff0, soff1, X,
-                                                          Xs, K, N, out, trash_row);
+  gemm_pf_q8<FMT, GATED, SMALL><<<n_cu, 64 * Q_WAVES, lds, s>>>(wl, counts, offsets, pool, S, woff0, woff1, soff0,
+                                                                 soff1, X, Xs, K, N, out, trash_row);
   return hipGetLastError();
 }
 
 // n_cu: CUs (one workgroup each).  The work list must have been built with
-// m-blocks of moe_pf8_tile_tokens(fmt) tokens.
-extern "C" hipError_t moe_launch_gemm_pf8(int fmt, int gated, int n_cu, const WorkList* wl, const int32_t* counts,
-                                          const int32_t* offsets, const uint8_t* pool, size_t S, size_t woff0,
-                                          size_t woff1, size_t soff0, size_t soff1, const void* X, const void* Xs,
-                                          int K, int N, void* out, int trash_row, hipStream_t s) {
+// m-blocks of moe_pf8_tile_tokens(fmt, small) tokens.
+extern "C" hipError_t moe_launch_gemm_pf8(int fmt, int gated, int small, int n_cu, const WorkList* wl,
+                                          const int32_t* counts, const int32_t* offsets, const uint8_t* pool,
+                                          size_t S, size_t woff0, size_t woff1, size_t soff0, size_t soff1,
+                                          const void* X, const void* Xs, int K, int N, void* out, int trash_row,
+                                          hipStream_t s) {
   if (K % Q_BK || N % (gated ? Q_BN / 2 : Q_BN)) return hipErrorInvalidValue;
   const uint8_t* x = (const uint8_t*)X;
   const uint8_t* xs = (const uint8_t*)Xs;
-  if (fmt == WFMT_FP8)
-    return gated ? launch_q8<WFMT_FP8, true>(n_cu, wl, counts, offsets, pool, S, woff0, woff1, soff0, soff1, x, xs,
-                                             K, N, out, trash_row, s)
-                 : launch_q8<WFMT_FP8, false>(n_cu, wl, counts, offsets, pool, S, woff0, woff1, soff0, soff1, x, xs,
-                                              K, N, out, trash_row, s);
-  if (fmt == WFMT_MXFP4)
-    return gated ? launch_q8<WFMT_MXFP4, true>(n_cu, wl, counts, offsets, pool, S, woff0, woff1, soff0, soff1, x,
-                                               xs, K, N, out, trash_row, s)
-                 : launch_q8<WFMT_MXFP4, false>(n_cu, wl, counts, offsets, pool, S, woff0, woff1, soff0, soff1, x,
-                                                xs, K, N, out, trash_row, s);
+#define MOE_Q8_ARGS n_cu, wl, counts, offsets, pool, S, woff0, woff1, soff0, soff1, x, xs, K, N, out, trash_row, s
+  if (fmt == WFMT_FP8) {
+    if (small) return gated ? launch_q8<WFMT_FP8, true, true>(MOE_Q8_ARGS) : launch_q8<WFMT_FP8, false, true>(MOE_Q8_ARGS);
+    return gated ? launch_q8<WFMT_FP8, true, false>(MOE_Q8_ARGS) : launch_q8<WFMT_FP8, false, false>(MOE_Q8_ARGS);
+  }
+  if (fmt == WFMT_MXFP4) {
+    if (small)
+      return gated ? launch_q8<WFMT_MXFP4, true, true>(MOE_Q8_ARGS) : launch_q8<WFMT_MXFP4, false, true>(MOE_Q8_ARGS);
+    return gated ? launch_q8<WFMT_MXFP4, true, false>(MOE_Q8_ARGS) : launch_q8<WFMT_MXFP4, false, false>(MOE_Q8_ARGS);
+  }
+#undef MOE_Q8_ARGS
   return hipErrorInvalidValue;
 }

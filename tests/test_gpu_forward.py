@@ -120,18 +120,22 @@ def edge_counts(cap):
     return [cap, cap + 1, 2 * cap, 2 * cap + 1, 1, 17, 900, 0]
 
 
-@pytest.mark.parametrize("fmt", [0, 1, 2])
-def test_tiled_forward_tile_edges(fmt):
+@pytest.mark.parametrize("fmt,cap", [(0, 288), (1, 256), (2, 288), (1, 128), (2, 128)])
+def test_tiled_forward_tile_edges(fmt, cap):
     """Routing forced to edge_counts by a one-hot router: token t's hidden row
     holds 4 at its first expert's dimension and 3 at its second's (noise
-    elsewhere), the router reads dimension e for expert e."""
-    print(f"tile edges fmt={fmt}", flush=True)
+    elsewhere), the router reads dimension e for expert e.  cap 128: the
+    8-bit formats' variant for few tokens per expert (128-token tiles)."""
+    print(f"tile edges fmt={fmt} cap={cap}", flush=True)
     cfg = shape(1, fmt=fmt)                          # E=8, k=2, H=256, I=128
     E, k, H = cfg.E, cfg.k, cfg.H
-    counts = edge_counts(256 if fmt == 1 else 288)
+    counts = edge_counts(cap)
+    if cap == 128:
+        counts[6] = 100                              # keep T*k within the small-tile regime
     slots = np.repeat(np.arange(E), counts)
     T = len(slots) // k
     assert T * k == len(slots) and T > 64 and T * k >= 48 * E   # the tiled kernels run
+    assert (T * k <= 160 * E) == (cap == 128)                  # which 8-bit variant
     first, second = slots[:T], slots[T:]
     assert np.all(first != second)
     rng = np.random.default_rng(7)

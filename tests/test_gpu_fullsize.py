@@ -113,3 +113,23 @@ def test_mxfp4_config5_shape(T):
         _check_rows(s, 0, x, out, 3, T)
     finally:
         s.close()
+
+
+@pytest.mark.parametrize("T", [1, 64, 1024])
+def test_nvfp4_decode_shape(T):
+    """The decode shape with NVFP4 experts at the sizes the formats bench
+    times (T=1 and 64) and a large batch through the same weight stream."""
+    import dataclasses
+    print(f"nvfp4 decode shape T={T}", flush=True)
+    cfg = dataclasses.replace(_fullsize(2, L=1), fmt=synth.FMT_NVFP4)
+    s = Setup(cfg, seed=4, max_tokens=max(T, 64), host_threads=8)
+    try:
+        s.admit_all(0)
+        x, xd = s.hidden(T, tag=T)
+        out = torch.empty(T, cfg.H, dtype=torch.bfloat16, device="cuda")
+        s.rt.forward(0, xd, s.R_d[0], s.b_d[0], s.slot_row(0), out)
+        torch.cuda.synchronize()
+        assert s.rt.check_device_error() == 0
+        _check_rows(s, 0, x, out, 6, T)
+    finally:
+        s.close()
