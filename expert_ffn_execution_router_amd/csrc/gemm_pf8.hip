@@ -56,13 +56,15 @@ constexpr int Q_BK = 128;                       // K per chunk
 constexpr int Q_WAVES = 8;
 constexpr int N_XCD = 8;
 
-template <int FMT, bool SMALL>
+// VAR 0: the largest tiles, two stages; 1: 128-token tiles, three stages
+// (few tokens per expert).
+template <int FMT, int VAR>
 struct QCfg {
   // most tokens per tile: fp8 keeps 32-byte A operands and a scaled partial
   // sum per MFMA, so its tile is 256 tokens (128 accumulators) to stay within
-  // 256 registers; MXFP4 takes 288 (144 accumulators); SMALL: 128 tokens
-  static constexpr int BM = SMALL ? 128 : (FMT == WFMT_MXFP4 ? 288 : 256);
-  static constexpr int NST = SMALL ? 3 : 2;                       // LDS stages
+  // 256 registers; MXFP4 takes 288 (144 accumulators)
+  static constexpr int BM = VAR == 1 ? 128 : (FMT == WFMT_MXFP4 ? 288 : 256);
+  static constexpr int NST = VAR ? 3 : 2;                         // LDS stages
   static constexpr int HALF = BM / 2;
   static constexpr int SUB = HALF / 16;                           // 16-token sub-tiles per half
   static constexpr int TLOADS = BM / 8 / (Q_WAVES / 2);           // 8-row token blocks per token wave
@@ -109,13 +111,14 @@ DEV void dma4(const void* src, lds_u8_t* dst) {
 // in grouped order ([rows, K] E4M3 codes) with scales Xs (fp8: fp32
 // [rows, K/128]; MXFP4: E8M0 [rows, K/32]).  K % 128 == 0; N % 128 (gated)
 // or 256 (not gated).  trash_row: a spare row of out for padding stores.
-template <int FMT, bool GATED, bool SMALL>
+template <int FMT, bool GATED, int VAR>
 __global__ void __launch_bounds__(64 * Q_WAVES, 1)
 gemm_pf_q8(const WorkList* __restrict__ wl, const int32_t* __restrict__ counts,
            const int32_t* __restrict__ offsets, const uint8_t* __restrict__ pool, size_t S, size_t woff0,
            size_t woff1, size_t soff0, size_t soff1, const uint8_t* __restrict__ X, const uint8_t* __restrict__ Xs,
            int K, int N, void* __restrict__ out, int trash_row) {
-  using C = QCfg<FMT, SMALL>;
+  using C = QCfg<FMT, VAR>;
+  static_assert(C::NST * C::STAGE + 4200 <= 160 * 1024, "LDS budget");
   extern __shared__ __align__(16) uint8_t lds[];
   __shared__ int l_pref[257], l_slot[256], l_row0[256], l_cnt[256];
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
@@ -448,34 +451,34 @@ gemm_pf_q8(const WorkList* __restrict__ wl, const int32_t* __restrict__ counts,
   if (pending) store_item(done);
 }
 
-template <int FMT, bool SMALL>
-static size_t lds_of() { return (size_t)QCfg<FMT, SMALL>::NST * QCfg<FMT, SMALL>::STAGE; }
+template <int FMT, int VAR>
+static size_t lds_of() { return (size_t)QCfg<FMT, VAR>::NST * QCfg<FMT, VAR>::STAGE; }
 
 extern "C" size_t moe_pf8_lds_bytes(int fmt, int small) {
-  if (fmt == WFMT_MXFP4) return small ? lds_of<WFMT_MXFP4, true>() : lds_of<WFMT_MXFP4, false>();
-  return small ? lds_of<WFMT_FP8, true>() : lds_of<WFMT_FP8, false>();
+  if (fmt == WFMT_MXFP4) return small ? lds_of<WFMT_MXFP4, 1>() : lds_of<WFMT_MXFP4, 0>();
+  return small ? lds_of<WFMT_FP8, 1>() : lds_of<WFMT_FP8, 0>();
 }
 // Tokens per m-tile of the large-batch 8-bit kernel; small != 0: the variant
 // for few tokens per expert.
 extern "C" int moe_pf8_tile_tokens(int fmt, int small) {
-  if (small) return QCfg<WFMT_FP8, true>::BM;
-  return fmt == WFMT_MXFP4 ? QCfg<WFMT_MXFP4, false>::BM : QCfg<WFMT_FP8, false>::BM;
+  if (small) return QCfg<WFMT_FP8, 1>::BM;
+  return fmt == WFMT_MXFP4 ? QCfg<WFMT_MXFP4, 0>::BM : QCfg<WFMT_FP8, 0>::BM;
 }
 
-template <int FMT, bool GATED, bool SMALL>
+template <int FMT, bool GATED, int VAR>
 static hipError_t launch_q8(int n_cu, const WorkList* wl, const int32_t* counts, const int32_t* offsets,
                             const uint8_t* pool, size_t S, size_t woff0, size_t woff1, size_t soff0, size_t soff1,
                             const uint8_t* X, const uint8_t* Xs, int K, int N, void* out, int trash_row,
                             hipStream_t s) {
-  const size_t lds = lds_of<FMT, SMALL>();
+  const size_t lds = lds_of<FMT, VAR>();
   static bool attr = false;
   if (!attr) {
-    hipError_t e = hipFuncSetAttribute((const void*)gemm_pf_q8<FMT, GATED, SMALL>,
+    hipError_t e = hipFuncSetAttribute((const void*)gemm_pf_q8<FMT, GATED, VAR>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     attr = true;
   }
-  gemm_pf_q8<FMT, GATED, SMALL><<<n_cu, 64 * Q_WAVES, lds, s>>>(wl, counts, offsets, pool, S, woff0, woff1, soff0,
+  gemm_pf_q8<FMT, GATED, VAR><<<n_cu, 64 * Q_WAVES, lds, s>>>(wl, counts, offsets, pool, S, woff0, woff1, soff0,
                                                                  soff1, X, Xs, K, N, out, trash_row);
   return hipGetLastError();
 }
@@ -492,13 +495,12 @@ extern "C" hipError_t moe_launch_gemm_pf8(int fmt, int gated, int small, int n_c
   const uint8_t* xs = (const uint8_t*)Xs;
 #define MOE_Q8_ARGS n_cu, wl, counts, offsets, pool, S, woff0, woff1, soff0, soff1, x, xs, K, N, out, trash_row, s
   if (fmt == WFMT_FP8) {
-    if (small) return gated ? launch_q8<WFMT_FP8, true, true>(MOE_Q8_ARGS) : launch_q8<WFMT_FP8, false, true>(MOE_Q8_ARGS);
-    return gated ? launch_q8<WFMT_FP8, true, false>(MOE_Q8_ARGS) : launch_q8<WFMT_FP8, false, false>(MOE_Q8_ARGS);
+    if (small) return gated ? launch_q8<WFMT_FP8, true, 1>(MOE_Q8_ARGS) : launch_q8<WFMT_FP8, false, 1>(MOE_Q8_ARGS);
+    return gated ? launch_q8<WFMT_FP8, true, 0>(MOE_Q8_ARGS) : launch_q8<WFMT_FP8, false, 0>(MOE_Q8_ARGS);
   }
   if (fmt == WFMT_MXFP4) {
-    if (small)
-      return gated ? launch_q8<WFMT_MXFP4, true, true>(MOE_Q8_ARGS) : launch_q8<WFMT_MXFP4, false, true>(MOE_Q8_ARGS);
-    return gated ? launch_q8<WFMT_MXFP4, true, false>(MOE_Q8_ARGS) : launch_q8<WFMT_MXFP4, false, false>(MOE_Q8_ARGS);
+    if (small) return gated ? launch_q8<WFMT_MXFP4, true, 1>(MOE_Q8_ARGS) : launch_q8<WFMT_MXFP4, false, 1>(MOE_Q8_ARGS);
+    return gated ? launch_q8<WFMT_MXFP4, true, 0>(MOE_Q8_ARGS) : launch_q8<WFMT_MXFP4, false, 0>(MOE_Q8_ARGS);
   }
 #undef MOE_Q8_ARGS
   return hipErrorInvalidValue;
