@@ -11,6 +11,9 @@ format definitions, not the pages:
     max normal 448, subnormal step 2^-9;
   * OCP Microscaling v1.0: E2M1 elements (values 0, 0.5, 1, 1.5, 2, 3, 4, 6 with
     a sign bit) and E8M0 scales 2^(e-127), 0xFF = NaN;
+  * OCP Microscaling v1.0 FP6 E2M3 (activations of the MXFP6 variant): 1
+    sign, 2 exponent bits with bias 1, 3 mantissa bits, no infinities or NaN,
+    max 7.5, subnormal step 1/8;
   * NVFP4 (NVIDIA's 4-bit format, named on the same pages): the same E2M1
     elements, an E4M3 scale per 16 consecutive elements and one fp32 scale
     per tensor; value = element * block scale * tensor scale.
@@ -96,3 +99,36 @@ def decode_e4m3(codes: np.ndarray) -> np.ndarray:
 
 def decode_e2m1(nibbles: np.ndarray) -> np.ndarray:
     return E2M1_TABLE[np.asarray(nibbles, dtype=np.uint8) & 0xF]
+
+
+def _e2m3_value(code: int) -> float:
+    s = -1.0 if code & 0x20 else 1.0
+    e = (code >> 3) & 0x3
+    m = code & 0x7
+    if e == 0:
+        return s * (m / 8.0)
+    return s * (1.0 + m / 8.0) * 2.0 ** (e - 1)
+
+
+E2M3_TABLE = np.array([_e2m3_value(c) for c in range(64)], dtype=np.float64)
+_E2M3_POS = E2M3_TABLE[:0x20]
+
+
+def encode_e2m3(v: np.ndarray) -> np.ndarray:
+    """Nearest E2M3 code (6 bits) for each value, ties to the even code,
+    saturating at 7.5; the sign bit follows v except for a zero result."""
+    v = np.asarray(v, dtype=np.float64)
+    a = np.minimum(np.abs(v), 7.5)
+    idx = np.clip(np.searchsorted(_E2M3_POS, a), 1, 0x1F)
+    lo, hi = idx - 1, idx
+    dlo = a - _E2M3_POS[lo]
+    dhi = _E2M3_POS[hi] - a
+    pick_hi = (dhi < dlo) | ((dhi == dlo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo)
+    code = np.where(a == 0.0, 0, code)
+    sign = np.signbit(v) & (code != 0)
+    return (code | (sign.astype(np.int64) << 5)).astype(np.uint8)
+
+
+def decode_e2m3(codes: np.ndarray) -> np.ndarray:
+    return E2M3_TABLE[np.asarray(codes, dtype=np.uint8) & 0x3F]

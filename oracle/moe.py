@@ -39,8 +39,8 @@ from __future__ import annotations
 
 import numpy as np
 
-from .formats import (bf16_to_f64, decode_e2m1, decode_e4m3, e8m0_to_f64, encode_e4m3,
-                      round_to_bf16)
+from .formats import (bf16_to_f64, decode_e2m1, decode_e2m3, decode_e4m3, e8m0_to_f64, encode_e2m3,
+                      encode_e4m3, round_to_bf16)
 
 FMT_BF16, FMT_FP8, FMT_MXFP4, FMT_NVFP4 = 0, 1, 2, 3
 
@@ -228,28 +228,45 @@ def mirror_quant_mxfp8(v: np.ndarray) -> np.ndarray:
     return np.ldexp(decode_e4m3(codes), x).reshape(rows, cols)
 
 
-def mirror_activation(v: np.ndarray, fmt: int) -> np.ndarray:
+def mirror_quant_mxfp6(v: np.ndarray) -> np.ndarray:
+    """OCP MX rule with FP6 E2M3 elements per 32 columns: x = floor(log2 amax)
+    - 2 (2 = exponent of E2M3's largest normal; clamped to [-127,127], amax
+    = 0 -> x = 0), code = E2M3(v * 2^-x) saturating at 7.5, value = code *
+    2^x."""
+    v32 = np.asarray(v, dtype=np.float64).astype(np.float32).astype(np.float64)
+    rows, cols = v32.shape
+    g = v32.reshape(rows, cols // 32, 32)
+    amax = np.abs(g).max(axis=2, keepdims=True)
+    _, ex = np.frexp(np.where(amax > 0, amax, 1.0))
+    x = np.where(amax > 0, np.clip(ex - 1 - 2, -127, 127), 0)
+    codes = encode_e2m3(np.ldexp(g, -x))
+    return np.ldexp(decode_e2m3(codes), x).reshape(rows, cols)
+
+
+def mirror_activation(v: np.ndarray, fmt: int, act: str | None = None) -> np.ndarray:
     """The GPU path's rounding of a GEMM input activation (x before GEMM 1,
     A before GEMM 2): bf16 and nvfp4 -> bf16, fp8 -> per-128 E4M3, mxfp4 ->
-    MXFP8."""
+    MXFP8, or MXFP6 with act="mxfp6" (the large-batch MXFP6 variant)."""
     if fmt in (FMT_BF16, FMT_NVFP4):
         return round_to_bf16(v)
     if fmt == FMT_FP8:
         return mirror_quant_fp8_groups(v, 128)
+    if act == "mxfp6":
+        return mirror_quant_mxfp6(v)
     return mirror_quant_mxfp8(v)
 
 
-def expert_ffn_mirrored(x: np.ndarray, Wg, Wu, Wd, fmt: int) -> np.ndarray:
+def expert_ffn_mirrored(x: np.ndarray, Wg, Wu, Wd, fmt: int, act: str | None = None) -> np.ndarray:
     """Expert output Z with the GPU path's rounding points: x quantised (fp8,
     mxfp4), A = silu(g)*u rounded to bf16 or quantised, Z rounded to bf16.
     nvfp4 weights enter the bf16 MFMA as element * block scale (exact in
     bf16) and the tensor scale multiplies the fp32 sums, so the weights are
-    not rounded here."""
-    xq = x if fmt in (FMT_BF16, FMT_NVFP4) else mirror_activation(x, fmt)
+    not rounded here.  act: activation variant of mxfp4 (None or "mxfp6")."""
+    xq = x if fmt in (FMT_BF16, FMT_NVFP4) else mirror_activation(x, fmt, act)
     g = xq @ Wg.T
     u = xq @ Wu.T
     a = silu(g) * u
-    aq = mirror_activation(a, fmt)
+    aq = mirror_activation(a, fmt, act)
     return round_to_bf16(aq @ Wd.T)
 
 
@@ -258,7 +275,7 @@ def expert_ffn_mirrored(x: np.ndarray, Wg, Wu, Wd, fmt: int) -> np.ndarray:
 # ----------------------------------------------------------------------------
 
 def moe_layer(x_bits, router_w, bias, k, expert_weights, fmt=FMT_BF16, mode="exact",
-              host_set=None, logits=None):
+              host_set=None, logits=None, act=None):
     """One routed MoE layer.
 
     x_bits: bf16 bit patterns [T,H]; router_w [E,H] fp32; bias [E] or None;
@@ -266,7 +283,8 @@ def moe_layer(x_bits, router_w, bias, k, expert_weights, fmt=FMT_BF16, mode="exa
     host_set: experts whose contribution is computed by the host branch.  In
     "mirrored" mode those are evaluated exactly (the host branch keeps fp32,
     without the GPU's intermediate rounding) and added before the final bf16
-    rounding.  logits: optional precomputed [T,E] logits.
+    rounding.  logits: optional precomputed [T,E] logits.  act: mxfp4's
+    activation variant in "mirrored" mode (None: MXFP8, "mxfp6": MXFP6).
     Returns dict(out [T,H] float64, ids, w, z, margin).
     """
     x = bf16_to_f64(x_bits)
@@ -283,7 +301,7 @@ def moe_layer(x_bits, router_w, bias, k, expert_weights, fmt=FMT_BF16, mode="exa
         if mode == "exact" or e in host_set:
             ye = expert_ffn(xe, Wg, Wu, Wd)
         else:
-            ye = expert_ffn_mirrored(xe, Wg, Wu, Wd, fmt)
+            ye = expert_ffn_mirrored(xe, Wg, Wu, Wd, fmt, act)
         out[rows] += w[rows, js][:, None] * ye
     if mode == "mirrored":
         out = round_to_bf16(out)

@@ -163,14 +163,15 @@ def test_split_is_exact_sum_of_partials():
 # Sanity bound only: the mirrored mode adds the GPU path's activation rounding
 # (bf16: 2^-9 relative; E4M3: 2^-4 relative per element), so it sits a
 # quantisation step away from the exact layer.
-@pytest.mark.parametrize("fmt,tol", [(M.FMT_BF16, 1e-2), (M.FMT_FP8, 0.1), (M.FMT_MXFP4, 0.1)])
-def test_mirrored_mode_close_to_exact(fmt, tol):
+@pytest.mark.parametrize("fmt,tol,act", [(M.FMT_BF16, 1e-2, None), (M.FMT_FP8, 0.1, None),
+                                         (M.FMT_MXFP4, 0.1, None), (M.FMT_MXFP4, 0.1, "mxfp6")])
+def test_mirrored_mode_close_to_exact(fmt, tol, act):
     cfg = _tiny(fmt)
     x = synth.hidden(cfg, 4, 16)
     R = synth.router_weights(cfg, 4, 0)
     wf = _weights_fn(cfg, 4)
     ex = M.moe_layer(x, R, None, cfg.k, wf, fmt=fmt, mode="exact")["out"]
-    mi = M.moe_layer(x, R, None, cfg.k, wf, fmt=fmt, mode="mirrored")["out"]
+    mi = M.moe_layer(x, R, None, cfg.k, wf, fmt=fmt, mode="mirrored", act=act)["out"]
     err = np.abs(mi - ex).max() / np.abs(ex).max()
     assert 0 < err <= tol
 
@@ -197,3 +198,35 @@ def test_mxfp8_scale_rule():
     # amax 1.9 -> exponent still -8; 1.9*256 = 486.4 saturates to 448
     v[0, 0] = 1.9
     assert M.mirror_quant_mxfp8(v)[0, 0] == 448.0 / 256.0
+
+
+def test_mxfp6_scale_rule():
+    # amax 1.0 -> shared exponent floor(log2 1) - 2 = -2 (E2M3's largest normal
+    # is 1.875 * 2^2): elements are scaled by 4 onto the E2M3 grid
+    v = np.zeros((2, 64)); v[0, 0] = 1.0; v[0, 1] = 0.1; v[0, 2] = -0.75
+    q = M.mirror_quant_mxfp6(v)
+    assert q[0, 0] == 1.0 and q[0, 2] == -0.75
+    # 0.1 * 4 = 0.4 -> nearest E2M3 subnormal 3/8 -> 3/32
+    assert q[0, 1] == 3.0 / 32.0
+    # amax 1.9 -> exponent -2; 1.9 * 4 = 7.6 saturates to 7.5 -> 1.875
+    v[0, 0] = 1.9
+    assert M.mirror_quant_mxfp6(v)[0, 0] == 1.875
+    # an all-zero block stays zero, blocks are independent
+    v[1, 32:] = 1000.0
+    q = M.mirror_quant_mxfp6(v)
+    assert (q[1, :32] == 0).all() and (q[1, 32:] == 1024.0 * 7.5 / 8.0).all()
+
+
+def test_mxfp6_relative_error_bound():
+    """Elements within a binade of their block's amax keep E2M3's 3-bit
+    mantissa: relative error <= 2^-4."""
+    rng = np.random.default_rng(8)
+    v = rng.normal(0, 1, size=(64, 256))
+    q = M.mirror_quant_mxfp6(v)
+    g = np.abs(v).reshape(64, 8, 32)
+    amax = g.max(axis=2, keepdims=True)
+    _, ex = np.frexp(amax)
+    near = (g >= np.ldexp(1.0, ex - 1)).reshape(64, 256)   # same binade as amax
+    rel = np.abs(q - v)[near] / np.abs(v)[near]
+    assert rel.max() <= 2.0 ** -4 + 1e-12
+    assert np.abs(q - v).max() <= np.abs(v).max() * 2.0 ** -3

@@ -60,6 +60,42 @@ def test_e2m1_from_bit_fields():
         assert F.decode_e2m1(np.array([c]))[0] == val
 
 
+def test_e2m3_values_pinned_by_e4m3():
+    """E2M3 (OCP MX FP6) against what the standard fixes without retyping its
+    formula: 64 finite codes (no inf/NaN), positive codes strictly increasing
+    from 0 to the 7.5 maximum with 0.125 the smallest subnormal and 1.0 the
+    smallest normal, negative codes the mirror image, and every value exactly
+    an E4M3 value (3 mantissa bits, narrower exponent range; torch's table)."""
+    t = F.E2M3_TABLE
+    assert t.shape == (64,) and np.isfinite(t).all()
+    pos = t[:32]
+    assert (np.diff(pos) > 0).all()
+    assert pos[0] == 0.0 and pos[1] == 0.125 and pos[8] == 1.0 and pos[31] == 7.5
+    assert np.array_equal(t[32:], -pos)
+    e4 = torch.arange(256, dtype=torch.int32).to(torch.uint8).view(torch.float8_e4m3fn).to(torch.float64).numpy()
+    assert np.isin(pos, e4).all()
+    # the step doubles with each binade: 1/8 below 2, 1/4 in [2, 4), 1/2 in [4, 7.5]
+    assert set(np.diff(pos[:17])) == {0.125} and set(np.diff(pos[16:25])) == {0.25}
+    assert set(np.diff(pos[24:])) == {0.5}
+
+
+def test_e2m3_encoder_against_torch_grids():
+    """Nearest-even rounding checked against torch: in [1, 7.5] E2M3 has E4M3's
+    3-bit mantissa, so both round alike (E4M3 reaches 8 where E2M3 saturates);
+    below 1 the step is 1/8, i.e. torch.round(8 v) / 8 (ties to even)."""
+    rng = np.random.default_rng(3)
+    hi = np.concatenate([rng.uniform(1.0, 7.75, 20000), (F.E2M3_TABLE[8:31] + F.E2M3_TABLE[9:32]) / 2])
+    ref = torch.from_numpy(hi).to(torch.float8_e4m3fn).to(torch.float64).numpy()
+    ref = np.minimum(ref, 7.5)
+    assert np.array_equal(F.decode_e2m3(F.encode_e2m3(hi)), ref)
+    assert np.array_equal(F.decode_e2m3(F.encode_e2m3(-hi)), -ref)
+    lo = np.concatenate([rng.uniform(0.0, 1.0, 20000), (np.arange(8) + 0.5) / 8])
+    ref = torch.round(torch.from_numpy(lo) * 8).numpy() / 8
+    assert np.array_equal(F.decode_e2m3(F.encode_e2m3(lo)), ref)
+    big = np.array([7.5, 7.74, 7.76, 100.0, -1e9])
+    assert list(F.encode_e2m3(big)) == [0x1F, 0x1F, 0x1F, 0x1F, 0x3F]
+
+
 def test_e8m0():
     v = F.e8m0_to_f64(np.array([127, 0, 254, 128, 120, 255]))
     assert v[0] == 1.0 and v[1] == 2.0 ** -127 and v[2] == 2.0 ** 127 and v[3] == 2.0 and v[4] == 2.0 ** -7
