@@ -748,26 +748,34 @@ def phase_formats(args):
         # prefill-shaped batch: one forward per layer
         hp = torch.from_numpy(synth.hidden(c, args.seed, pf_T, 7).view(np.int16)).to(dev)
         op = torch.empty(pf_T, H, dtype=torch.bfloat16, device=dev)
-        rt.forward(0, hp, R[0], bias[0], rows[0], op)
-        torch.cuda.synchronize()
-        rt.profile_begin(L * 12 + 16)
-        for l in range(L):
-            rt.forward(l, hp, R[l], bias[l], rows[l], op)
-        prof = rt.profile_end()
-        torch.cuda.synchronize()
-        assert rt.check_device_error() == 0
-        st = {n: v["ms"] / v["launches"] * 1e3 for n, v in prof.items() if isinstance(v, dict) and v["launches"]}
-        gemm_us = st["gemm1"] + st["gemm2"] + st.get("fixup", 0.0) * 2
-        flops = 6.0 * pf_T * k * H * I
+
+        def prefill_pass(key, kernel, peak):
+            rt.forward(0, hp, R[0], bias[0], rows[0], op)
+            torch.cuda.synchronize()
+            rt.profile_begin(L * 12 + 16)
+            for l in range(L):
+                rt.forward(l, hp, R[l], bias[l], rows[l], op)
+            prof = rt.profile_end()
+            torch.cuda.synchronize()
+            assert rt.check_device_error() == 0
+            st = {n: v["ms"] / v["launches"] * 1e3 for n, v in prof.items() if isinstance(v, dict) and v["launches"]}
+            gemm_us = st["gemm1"] + st["gemm2"] + st.get("fixup", 0.0) * 2
+            flops = 6.0 * pf_T * k * H * I
+            res[key] = {
+                "bound": pf_bound, "gemm_us": gemm_us, "gpu_layer_us": sum(st.values()), "stage_us": st,
+                "weights_hbm_frac": E * S / (gemm_us * 1e-6) / HBM_PEAK,
+                "mfma_frac": flops / (gemm_us * 1e-6) / peak, "mfma_peak_TFLOPs": peak / 1e12, "kernel": kernel,
+            }
+            log(f"{name} {key}: {json.dumps(res[key])}")
+
         peak = {4: FP8_PEAK, 5: FP4_PEAK, 6: BF16_PEAK}[cid]
-        res[f"prefill_T{pf_T}"] = {
-            "bound": pf_bound, "gemm_us": gemm_us, "gpu_layer_us": sum(st.values()), "stage_us": st,
-            "weights_hbm_frac": E * S / (gemm_us * 1e-6) / HBM_PEAK,
-            "mfma_frac": flops / (gemm_us * 1e-6) / peak, "mfma_peak_TFLOPs": peak / 1e12,
-            "kernel": ("gemm_dec (weight stream, NVFP4 dequantised to bf16 in registers)" if cid == 6
-                       else "gemm_pf_q8 (LDS-tiled scaled-MFMA grouped GEMM)"),
-        }
-        log(f"{name} prefill T={pf_T}: {json.dumps(res[f'prefill_T{pf_T}'])}")
+        prefill_pass(f"prefill_T{pf_T}", "gemm_dec (weight stream, NVFP4 dequantised to bf16 in registers)"
+                     if cid == 6 else "gemm_pf_q8 (LDS-tiled scaled-MFMA grouped GEMM)", peak)
+        if cid == 5:     # MXFP6 activations: E2M1 x E2M3 at the 6/4-bit MFMA rate
+            from expert_ffn_execution_router_amd import binding as B
+            rt.set_activations(B.MOE_ACT_MXFP6)
+            prefill_pass(f"prefill_T{pf_T}_mxfp6", "gemm_pf_q8 (E2M1 weights x MXFP6 activations)", FP4_PEAK)
+            rt.set_activations(B.MOE_ACT_DEFAULT)
         out[name] = res
         rt.close()
         del rt, hp, op

@@ -23,7 +23,9 @@ MOE_E_UNSUPPORTED = -6
 MOE_I_FALLBACK_ONDEMAND = 1
 MOE_I_SINGLE_BUFFER = 2
 
-MOE_W_BF16, MOE_W_FP8_E4M3_B128, MOE_W_MXFP4 = 0, 1, 2
+MOE_W_BF16, MOE_W_FP8_E4M3_B128, MOE_W_MXFP4, MOE_W_NVFP4 = 0, 1, 2, 3
+MOE_ACT_DEFAULT, MOE_ACT_MXFP6 = 0, 1
+MOE_QUANT_MXFP6 = 64
 MOE_POLICY_OFFLOAD, MOE_POLICY_HOST, MOE_POLICY_HYBRID = 0, 1, 2
 
 
@@ -75,6 +77,7 @@ SIGNATURES = {
     "moe_host_alloc": (_i, [_sz, _P(_vp)]),
     "moe_host_free": (_i, [_vp]),
     "moe_set_policy": (_i, [_vp, _i, _d, _d]),
+    "moe_set_activations": (_i, [_vp, _i]),
     "moe_calibrate": (_i, [_vp, _P(_d), _P(_d)]),
     "moe_slot_table": (_vp, [_vp]),
     "moe_reset_cache": (_i, [_vp, _vp]),
@@ -148,6 +151,7 @@ moe_destroy = _fn("moe_destroy")
 moe_host_alloc = _fn("moe_host_alloc")
 moe_host_free = _fn("moe_host_free")
 moe_set_policy = _fn("moe_set_policy")
+moe_set_activations = _fn("moe_set_activations")
 moe_calibrate = _fn("moe_calibrate")
 moe_slot_table = _fn("moe_slot_table")
 moe_reset_cache = _fn("moe_reset_cache")

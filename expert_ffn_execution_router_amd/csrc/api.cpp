@@ -36,8 +36,8 @@ int moe_pf_tile_tokens();
 int moe_pf8_tile_tokens(int fmt, int small);
 hipError_t moe_launch_gemm_pf8(int fmt, int gated, int small, int n_cu, const WorkList* wl, const int32_t* counts,
                                const int32_t* offsets, const uint8_t* pool, size_t S, size_t woff0, size_t woff1,
-                               size_t soff0, size_t soff1, const void* X, const void* Xs, int K, int N, void* out,
-                               int trash_row, hipStream_t s);
+                               size_t soff0, size_t soff1, const void* X, const void* Xs, int xcap, int K,
+                               int N, void* out, int trash_row, hipStream_t s);
 hipError_t moe_launch_gemm_pf(int fmt, int gated, int grid, const WorkList* wl, const int32_t* counts,
                               const int32_t* offsets, const uint8_t* pool, size_t S, size_t woff0, size_t woff1,
                               const void* X, const int32_t* row_tok, int K, int N, void* out, hipStream_t s);
@@ -47,7 +47,8 @@ hipError_t moe_launch_combine(const uint16_t* Z, const int32_t* ids, const float
                               hipStream_t s);
 hipError_t moe_launch_range_mask(int lo, int hi, int E, uint32_t* mask, hipStream_t s);
 hipError_t moe_launch_quant(int fmt, int src_bf16, const void* src, int rows, const int32_t* nrows_dev,
-                            const int32_t* row_map, int cols, uint8_t* q, void* scale, hipStream_t s);
+                            const int32_t* row_map, int cols, uint8_t* q, void* scale, int cap,
+                            hipStream_t s);
 hipError_t moe_launch_plan(const int32_t* ids, int n_assign, int layer, int E, int n_slots, int32_t* slot_table,
                            int32_t* owner, uint32_t* last_use, void* ctl, int policy, double BP, double BH,
                            uint32_t* miss_mask, void* plan, const void* host_stage, hipStream_t s);
@@ -131,12 +132,16 @@ WsLayout ws_layout(const moe_config& c) {
   L.mask = take(64);
   L.plan = take(sizeof(PlanOut));
   const bool q8 = c.wfmt == MOE_W_FP8_E4M3_B128 || c.wfmt == MOE_W_MXFP4;   // quantised activations
+  // MXFP4 may take MXFP6 activations: 128-column planes of x6_plane_bytes(R) bytes
+  auto qbytes = [&](size_t cols) {
+    return c.wfmt == MOE_W_MXFP4 ? std::max(R * cols, cols / 128 * x6_plane_bytes(R)) : (q8 ? R * cols : 0);
+  };
   L.A = take((R + 1) * c.I * (q8 ? 4 : 2));   // + a spare row for the 8-bit large-batch GEMM's padding stores
-  L.Aq = take(q8 ? R * c.I : 0);
+  L.Aq = take(qbytes(c.I));
   L.As = take(c.wfmt == MOE_W_FP8_E4M3_B128 ? R * (c.I / 128) * 4 : (q8 ? R * (c.I / 32) : 0));
   L.Z = take((R + 1) * c.H * 2);
   // quantised activations in grouped order (one row per routed pair)
-  L.Xq = take(q8 ? R * c.H : 0);
+  L.Xq = take(qbytes(c.H));
   L.Xs = take(c.wfmt == MOE_W_FP8_E4M3_B128 ? R * (c.H / 128) * 4 : (q8 ? R * (c.H / 32) : 0));
   L.hp = take(Tm * c.H * 4);
   // small-batch GEMM: partial tiles of items cut between workgroups
@@ -200,6 +205,7 @@ struct moe_ctx {
   // policy
   int policy = MOE_POLICY_OFFLOAD;
   double BP = 1.0, BH = 1.0;
+  int act = MOE_ACT_DEFAULT;              // MXFP4's large-batch activation format
   // asynchronous decode: host-branch callback arguments, one per (layer, T),
   // alive until moe_destroy because captured graphs keep their addresses
   std::map<std::pair<int, int>, std::unique_ptr<AsyncArg>> async_args;
@@ -310,18 +316,19 @@ int forward_experts(moe_ctx* c, const void* hidden, int T, const int32_t* slot_r
   const BlobLayout& b = c->bl;
   if (tiled && g.wfmt != MOE_W_BF16) {
     const int trash = g.max_tokens * g.k;       // the spare row of A and Z
+    // MXFP4 weights with MXFP6 activations when selected
+    const int qf = g.wfmt == MOE_W_MXFP4 && c->act == MOE_ACT_MXFP6 ? WFMT_MXFP4_A6 : g.wfmt;
     // activations quantised straight into grouped order (row p <- token perm_tok[p])
     STAGE(c, MOE_STAGE_QUANT_X, s,
-          moe_launch_quant(g.wfmt, 1, hidden, T * g.k, c->offsets + g.E, c->perm_tok, g.H, c->Xq, c->Xs, s));
+          moe_launch_quant(qf, 1, hidden, T * g.k, c->offsets + g.E, c->perm_tok, g.H, c->Xq, c->Xs, trash, s));
     STAGE(c, MOE_STAGE_GEMM1, s,
-          moe_launch_gemm_pf8(g.wfmt, 1, small8, c->n_cu, c->wl, c->counts, c->offsets, c->slot_pool, b.S, b.w[0],
-                              b.w[1],
-                              b.s[0], b.s[1], c->Xq, c->Xs, g.H, g.I, c->A, trash, s));
+          moe_launch_gemm_pf8(qf, 1, small8, c->n_cu, c->wl, c->counts, c->offsets, c->slot_pool, b.S, b.w[0],
+                              b.w[1], b.s[0], b.s[1], c->Xq, c->Xs, trash, g.H, g.I, c->A, trash, s));
     STAGE(c, MOE_STAGE_QUANT_A, s,
-          moe_launch_quant(g.wfmt, 0, c->A, T * g.k, c->offsets + g.E, nullptr, g.I, c->Aq, c->As, s));
+          moe_launch_quant(qf, 0, c->A, T * g.k, c->offsets + g.E, nullptr, g.I, c->Aq, c->As, trash, s));
     STAGE(c, MOE_STAGE_GEMM2, s,
-          moe_launch_gemm_pf8(g.wfmt, 0, small8, c->n_cu, c->wl, c->counts, c->offsets, c->slot_pool, b.S, b.w[2], 0,
-                              b.s[2], 0, c->Aq, c->As, g.I, g.H, c->Z, trash, s));
+          moe_launch_gemm_pf8(qf, 0, small8, c->n_cu, c->wl, c->counts, c->offsets, c->slot_pool, b.S, b.w[2], 0,
+                              b.s[2], 0, c->Aq, c->As, trash, g.I, g.H, c->Z, trash, s));
   } else if (tiled) {
     STAGE(c, MOE_STAGE_GEMM1, s,
           moe_launch_gemm_pf(g.wfmt, 1, c->n_cu, c->wl, c->counts, c->offsets, c->slot_pool, b.S, b.w[0], b.w[1],
@@ -347,7 +354,7 @@ int forward_experts(moe_ctx* c, const void* hidden, int T, const int32_t* slot_r
   } else {
     // activations quantised straight into grouped order (row p <- token perm_tok[p])
     STAGE(c, MOE_STAGE_QUANT_X, s,
-          moe_launch_quant(g.wfmt, 1, hidden, T * g.k, c->offsets + g.E, c->perm_tok, g.H, c->Xq, c->Xs, s));
+          moe_launch_quant(g.wfmt, 1, hidden, T * g.k, c->offsets + g.E, c->perm_tok, g.H, c->Xq, c->Xs, 0, s));
     STAGE(c, MOE_STAGE_GEMM1, s,
           moe_launch_gemm_dec(g.wfmt, 1, ns, ncu, c->wl, c->counts, c->offsets, c->slot_pool, b.S, b.w[0], b.w[1],
                               b.s[0], b.s[1], c->Xq, c->Xs, nullptr, g.H, g.I, c->A, c->part, 0, s));
@@ -355,7 +362,7 @@ int forward_experts(moe_ctx* c, const void* hidden, int T, const int32_t* slot_r
           moe_launch_gemm_dec(g.wfmt, 1, ns, ncu, c->wl, c->counts, c->offsets, c->slot_pool, b.S, b.w[0], b.w[1],
                               b.s[0], b.s[1], c->Xq, c->Xs, nullptr, g.H, g.I, c->A, c->part, 1, s));
     STAGE(c, MOE_STAGE_QUANT_A, s,
-          moe_launch_quant(g.wfmt, 0, c->A, T * g.k, c->offsets + g.E, nullptr, g.I, c->Aq, c->As, s));
+          moe_launch_quant(g.wfmt, 0, c->A, T * g.k, c->offsets + g.E, nullptr, g.I, c->Aq, c->As, 0, s));
     STAGE(c, MOE_STAGE_GEMM2, s,
           moe_launch_gemm_dec(g.wfmt, 0, ns, ncu, c->wl, c->counts, c->offsets, c->slot_pool, b.S, b.w[2], 0, b.s[2],
                               0, c->Aq, c->As, nullptr, g.I, g.H, c->Z, c->part, 0, s));
@@ -608,6 +615,15 @@ int moe_destroy(moe_ctx* c) {
   return MOE_OK;
 }
 
+int moe_set_activations(moe_ctx* c, int act) {
+  if (!c) return fail(nullptr, MOE_E_INVAL, "null ctx");
+  if (act != MOE_ACT_DEFAULT && act != MOE_ACT_MXFP6) return fail(c, MOE_E_INVAL, "unknown activation format");
+  if (act == MOE_ACT_MXFP6 && c->cfg.wfmt != MOE_W_MXFP4)
+    return fail(c, MOE_E_INVAL, "MXFP6 activations need MXFP4 weights");
+  c->act = act;
+  return MOE_OK;
+}
+
 int moe_set_policy(moe_ctx* c, int policy, double B_P, double B_H) {
   if (!c) return fail(nullptr, MOE_E_INVAL, "null ctx");
   if (policy < 0 || policy > 2) return fail(c, MOE_E_INVAL, "unknown policy");
@@ -642,13 +658,14 @@ int moe_route(moe_ctx* c, const void* hidden, const float* R, const float* bias,
 
 int moe_quantize(int wfmt, int src_bf16, const void* src, int rows, int cols, const int32_t* row_map, uint8_t* q,
                  void* scale, void* stream) {
-  if (wfmt != MOE_W_FP8_E4M3_B128 && wfmt != MOE_W_MXFP4) return fail(nullptr, MOE_E_INVAL, "format has no quantisation");
-  if (rows < 0 || cols <= 0 || cols % (wfmt == MOE_W_FP8_E4M3_B128 ? 128 : 32))
-    return fail(nullptr, MOE_E_INVAL, "bad shape");
+  if (wfmt != MOE_W_FP8_E4M3_B128 && wfmt != MOE_W_MXFP4 && wfmt != MOE_QUANT_MXFP6)
+    return fail(nullptr, MOE_E_INVAL, "format has no quantisation");
+  if (rows < 0 || cols <= 0 || cols % (wfmt == MOE_W_MXFP4 ? 32 : 128)) return fail(nullptr, MOE_E_INVAL, "bad shape");
   if (rows == 0) return MOE_OK;
   if (!src || !q || !scale) return fail(nullptr, MOE_E_INVAL, "null argument");
-  hipError_t e = moe_launch_quant(wfmt, src_bf16 ? 1 : 0, src, rows, nullptr, row_map, cols, q, scale,
-                                  as_stream(stream));
+  const int qf = wfmt == MOE_QUANT_MXFP6 ? WFMT_MXFP4_A6 : wfmt;
+  hipError_t e = moe_launch_quant(qf, src_bf16 ? 1 : 0, src, rows, nullptr, row_map, cols, q, scale,
+                                  rows, as_stream(stream));
   if (e != hipSuccess) return fail(nullptr, MOE_E_HIP, hipGetErrorString(e));
   return MOE_OK;
 }

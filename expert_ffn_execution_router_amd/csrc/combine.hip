@@ -10,7 +10,9 @@
 // say the kernels dequantise in-kernel; these are the declared readings):
 //   * fp8 path: per (row, 128 columns): scale = amax/448, code = E4M3(v*(448/amax));
 //   * mxfp4 path: OCP MX rule, E4M3 elements per 32 columns with E8M0 scale
-//     2^(floor(log2 amax) - 8).
+//     2^(floor(log2 amax) - 8);
+//   * its MXFP6 variant: OCP MX rule, E2M3 elements per 32 columns with E8M0
+//     scale 2^(floor(log2 amax) - 2), round to nearest even, saturating at 7.5.
 #include "common.h"
 
 __global__ void __launch_bounds__(256)
@@ -164,6 +166,61 @@ quant_mxfp8_kernel(const void* __restrict__ src, int rows, const int32_t* __rest
   if ((c0 & 31) == 0) scale[(size_t)r * (cols / 32) + c0 / 32] = (uint8_t)(x + 127);
 }
 
+// E2M3 code of w (OCP MX FP6: bias 1, max 7.5, subnormal step 1/8), round to
+// nearest even, saturating.  The step is 1/8 below 2, 1/4 in [2, 4) and 1/2
+// above, and the codes count up through the binades without a gap, so the
+// code is an offset plus w divided by its binade's step, rounded (ties to the
+// even integer, which is the even code).
+DEV uint32_t f32_to_e2m3(float w) {
+  const float a = fabsf(w);
+  uint32_t c;
+  if (a < 2.0f) c = (uint32_t)rintf(a * 8.0f);
+  else if (a < 4.0f) c = 8u + (uint32_t)rintf(a * 4.0f);
+  else c = min(16u + (uint32_t)rintf(fminf(a, 8.0f) * 2.0f), 31u);
+  return c ? (c | ((__float_as_uint(w) >> 26) & 0x20u)) : 0u;
+}
+
+// One thread per (row, 32-column block).  Rows from *nrows_dev when given;
+// output row r quantises source row row_map[r] (r itself without a map).
+template <bool SRC_BF16>
+__global__ void __launch_bounds__(256)
+quant_mxfp6_kernel(const void* __restrict__ src, int rows, const int32_t* __restrict__ nrows_dev,
+                   const int32_t* __restrict__ row_map, int cols, int cap, uint8_t* __restrict__ q,
+                   uint8_t* __restrict__ scale) {
+  const long gi = (long)blockIdx.x * 256 + threadIdx.x;
+  const int per_row = cols / 32;
+  const int nrows = nrows_dev ? *nrows_dev : rows;
+  const long r = gi / per_row;
+  const int b = (int)(gi - r * per_row);
+  if (r >= nrows) return;
+  float v[2][16];
+  const size_t at = (size_t)(row_map ? row_map[r] : r) * cols + b * 32;
+  load16<SRC_BF16>(src, at, v[0]);
+  load16<SRC_BF16>(src, at + 16, v[1]);
+  float amax = 0.0f;
+#pragma unroll
+  for (int k = 0; k < 32; ++k) amax = fmaxf(amax, fabsf(v[k >> 4][k & 15]));
+  int x = 0;
+  if (amax > 0.0f) {
+    int e;
+    frexpf(amax, &e);                    // amax = m * 2^e, m in [0.5, 1)
+    x = min(127, max(-127, (e - 1) - 2));
+  }
+  unsigned long long pc[3] = {0ull, 0ull, 0ull};
+#pragma unroll
+  for (int j = 0; j < 32; ++j) {
+    const unsigned long long c = f32_to_e2m3(ldexpf(v[j >> 4][j & 15], -x));   // exact power-of-two scaling
+    const int bit = 6 * j, wd = bit >> 6, off = bit & 63;
+    pc[wd] |= c << off;
+    if (off > 58) pc[wd + 1] |= c >> (64 - off);
+  }
+  uint8_t* row = q + (size_t)(b >> 2) * x6_plane_bytes(cap) + (size_t)r * X6_ROWB;
+  const int g = b & 3;
+  *(i32x4_t*)(row + x6_off16(g)) = i32x4_t{(int)pc[0], (int)(pc[0] >> 32), (int)pc[1], (int)(pc[1] >> 32)};
+  st8(row + x6_off8(g), make_uint2((uint32_t)pc[2], (uint32_t)(pc[2] >> 32)));
+  scale[(size_t)(b >> 2) * cap * 4 + r * 4 + (b & 3)] = (uint8_t)(x + 127);
+}
+
 extern "C" hipError_t moe_launch_combine(const uint16_t* Z, const int32_t* ids, const float* w, const int32_t* pos,
                                          const uint32_t* miss_mask, const int32_t* slot_row, const float* hp,
                                          const int32_t* hp_count, int T, int k, int H, uint16_t* out,
@@ -174,9 +231,22 @@ extern "C" hipError_t moe_launch_combine(const uint16_t* Z, const int32_t* ids, 
   return hipGetLastError();
 }
 
+// fmt WFMT_MXFP4_A6: MXFP6 codes and scales in 128-column planes sized for
+// cap rows (x6_plane_bytes); cols % 128 == 0, rows <= cap.
 extern "C" hipError_t moe_launch_quant(int fmt, int src_bf16, const void* src, int rows, const int32_t* nrows_dev,
-                                       const int32_t* row_map, int cols, uint8_t* q, void* scale, hipStream_t s) {
+                                       const int32_t* row_map, int cols, uint8_t* q, void* scale, int cap,
+                                       hipStream_t s) {
   if (rows == 0) return hipSuccess;
+  if (fmt == WFMT_MXFP4_A6) {
+    if (cols % 128 || cap < rows) return hipErrorInvalidValue;
+    const unsigned blocks = (unsigned)(((long)rows * (cols / 32) + 255) / 256);
+    if (src_bf16)
+      quant_mxfp6_kernel<true><<<blocks, 256, 0, s>>>(src, rows, nrows_dev, row_map, cols, cap, q, (uint8_t*)scale);
+    else
+      quant_mxfp6_kernel<false><<<blocks, 256, 0, s>>>(src, rows, nrows_dev, row_map, cols, cap, q,
+                                                       (uint8_t*)scale);
+    return hipGetLastError();
+  }
   const long threads = (long)rows * (cols / 16);
   const unsigned blocks = (unsigned)((threads + 255) / 256);
   if (fmt == WFMT_FP8) {

@@ -13,6 +13,28 @@ typedef int i32x8_t __attribute__((__vector_size__(8 * sizeof(int))));
 #define DEV __device__ __forceinline__
 
 enum { WFMT_BF16 = 0, WFMT_FP8 = 1, WFMT_MXFP4 = 2, WFMT_NVFP4 = 3 };
+// Internal to the large-batch path: MXFP4 weights with MXFP6 (E2M3)
+// activations.
+enum { WFMT_MXFP4_A6 = 4 };
+
+// MXFP6 activation rows: per 128-column chunk c a plane of 112-byte rows;
+// the 32 six-bit codes of column block 4c + g form a 24-byte little-endian
+// string (code j at bits 6j..6j+5) at bytes [24g, 24g+24) of the row, its
+// bytes 0-15 at the 16-byte aligned offset x6_off16(g) and bytes 16-23 at
+// x6_off8(g); bytes 96-111 are padding.  At a 112-byte stride any 16
+// consecutive rows read at one offset, 16 bytes a lane (or 8 bytes, two lane
+// groups at a time), cover the 64 LDS banks once.
+// Their E8M0 scales are chunk-major too: plane c holds 4 bytes per row (the
+// scales of column blocks 4c..4c+3), so a tile's scales of one chunk are one
+// contiguous range.  Planes are sized for a row capacity: x6_plane_bytes(cap)
+// for the codes (plus the 1 KiB the large-batch GEMM may read past the last
+// row) and 4 * cap for the scales.
+constexpr int X6_ROWB = 112;
+DEV int x6_off16(int g) { return 24 * g + ((g & 1) << 3); }
+DEV int x6_off8(int g) { return 24 * g + ((g & 1) ? 0 : 16); }
+__host__ __device__ inline size_t x6_plane_bytes(size_t cap) {
+  return (cap * X6_ROWB + 1024 + 255) / 256 * 256;
+}
 
 // m-block size used when only the grouping (not a GEMM) reads the work list.
 constexpr int DEC_MB = 64;

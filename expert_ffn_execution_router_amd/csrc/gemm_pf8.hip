@@ -1,7 +1,7 @@
 // Slot-indexed grouped expert GEMMs for large token counts per expert in the
 // 8-bit weight formats: fp8 E4M3 weights with an fp32 scale per 128x128
 // block and per-(token, 128 K) fp8 activations, or MXFP4 (E2M1 weights with
-// an E8M0 scale per 32 K) with MXFP8 activations.
+// an E8M0 scale per 32 K) with MXFP8 or MXFP6 (E2M3) activations.
 //
 // Same computation as the small-batch kernels (paper.oopus.info review of
 // FreeToken, section 2.5: grouped evaluation of every expert of G for the
@@ -41,6 +41,14 @@
 //     its MFMAs;
 //   * GEMM 1 stores silu(g)*u in fp32 (the next pass quantises it), GEMM 2
 //     stores bf16;
+//   * MXFP6 activations: the quantisation pass writes each 128-K chunk of
+//     the grouped rows as one plane of 112-byte rows (96 bytes of codes), so
+//     a tile's rows of a chunk are one contiguous range, moved in 1 KiB
+//     blocks; at that stride 16 consecutive rows read at one offset are
+//     bank-conflict free wherever the tile starts; the E2M3 operand of lane
+//     group g is the 24 bytes of K [32g, 32g+32), one 16-byte and one 8-byte
+//     aligned read (x6_off16, x6_off8), and E2M1 x E2M3 issues at the 6/4-bit
+//     rate (1.7x the E2M1 x E4M3 rate, measured);
 //   * few tokens per expert (a weight stream more than a GEMM): tiles of 128
 //     tokens and three LDS stages, so two chunks are in flight while one is
 //     multiplied; the wait before a chunk counts only loads (the ones this
@@ -60,25 +68,30 @@ constexpr int N_XCD = 8;
 // (few tokens per expert).
 template <int FMT, int VAR>
 struct QCfg {
+  static constexpr bool X6 = FMT == WFMT_MXFP4_A6;                // E2M3 token rows
+  static constexpr bool W4 = FMT == WFMT_MXFP4 || X6;             // E2M1 weights, E8M0 scales
   // most tokens per tile: fp8 keeps 32-byte A operands and a scaled partial
   // sum per MFMA, so its tile is 256 tokens (128 accumulators) to stay within
   // 256 registers; MXFP4 takes 288 (144 accumulators)
-  static constexpr int BM = VAR == 1 ? 128 : (FMT == WFMT_MXFP4 ? 288 : 256);
+  static constexpr int BM = VAR == 1 ? 128 : (W4 ? 288 : 256);
   static constexpr int NST = VAR ? 3 : 2;                         // LDS stages
   static constexpr int HALF = BM / 2;
   static constexpr int SUB = HALF / 16;                           // 16-token sub-tiles per half
-  static constexpr int TLOADS = BM / 8 / (Q_WAVES / 2);           // 8-row token blocks per token wave
+  // token loads per token wave: 8-row blocks of 128-byte rows, or (E2M3) the
+  // 1 KiB blocks of up to BM rows of X6_ROWB bytes
+  static constexpr int X6_BLOCKS = (BM * X6_ROWB + 1023) / 1024;
+  static constexpr int TLOADS = X6 ? (X6_BLOCKS + 3) / 4 : BM / 8 / (Q_WAVES / 2);
   static constexpr int NXS = (BM + 63) / 64;                      // 4-byte loads of 64 token-scale rows
-  static constexpr int WROWB = FMT == WFMT_MXFP4 ? 64 : 128;      // weight row bytes per chunk
+  static constexpr int WROWB = W4 ? 64 : 128;                     // weight row bytes per chunk
   static constexpr int WRPB = 1024 / WROWB;                       // weight rows per 1 KiB load
   static constexpr int WLOADS = Q_BN / WRPB / (Q_WAVES / 2);      // weight loads per weight wave
   static constexpr int LOADS = TLOADS > WLOADS ? TLOADS : WLOADS;
   static constexpr int T_OFF = 0;
-  static constexpr int W_OFF = BM * 128;
+  static constexpr int W_OFF = X6 ? TLOADS * 4 * 1024 : BM * 128;
   static constexpr int XS_OFF = W_OFF + Q_BN * WROWB;
   static constexpr int XS_BYTES = NXS * 256;                      // row r's scale dword at XS_OFF + 4r
   static constexpr int WS_OFF = XS_OFF + XS_BYTES;
-  static constexpr int WS_BYTES = FMT == WFMT_MXFP4 ? Q_BN * 4 : 256;
+  static constexpr int WS_BYTES = W4 ? Q_BN * 4 : 256;
   static constexpr int STAGE = WS_OFF + WS_BYTES;
 };
 
@@ -108,15 +121,16 @@ DEV void dma4(const void* src, lds_u8_t* dst) {
 // GATED: out = A (fp32 [rows, N], N = I features), weights gate at woff0 and
 // up at woff1 ([N, K] codes), their scales at soff0 / soff1.  Otherwise out =
 // Z (bf16 [rows, N]), weights at woff0, scales at soff0.  X: quantised rows
-// in grouped order ([rows, K] E4M3 codes) with scales Xs (fp8: fp32
-// [rows, K/128]; MXFP4: E8M0 [rows, K/32]).  K % 128 == 0; N % 128 (gated)
-// or 256 (not gated).  trash_row: a spare row of out for padding stores.
+// in grouped order ([rows, K] E4M3 codes, or MXFP6 planes sized for xcap
+// rows) with scales Xs (fp8: fp32 [rows, K/128]; MXFP4: E8M0 [rows, K/32];
+// MXFP6: E8M0 planes [K/128][xcap][4]).  K % 128 == 0; N % 128 (gated) or
+// 256 (not gated).  trash_row: a spare row of out for padding stores.
 template <int FMT, bool GATED, int VAR>
 __global__ void __launch_bounds__(64 * Q_WAVES, 1)
 gemm_pf_q8(const WorkList* __restrict__ wl, const int32_t* __restrict__ counts,
            const int32_t* __restrict__ offsets, const uint8_t* __restrict__ pool, size_t S, size_t woff0,
            size_t woff1, size_t soff0, size_t soff1, const uint8_t* __restrict__ X, const uint8_t* __restrict__ Xs,
-           int K, int N, void* __restrict__ out, int trash_row) {
+           int xcap, int K, int N, void* __restrict__ out, int trash_row) {
   using C = QCfg<FMT, VAR>;
   static_assert(C::NST * C::STAGE + 4200 <= 160 * 1024, "LDS budget");
   extern __shared__ __align__(16) uint8_t lds[];
@@ -176,7 +190,7 @@ gemm_pf_q8(const WorkList* __restrict__ wl, const int32_t* __restrict__ counts,
   const bool wtok = wave < Q_WAVES / 2;
   const int kb128 = K / 128, kb32 = K / 32;
   const int xrowb = K;                                    // bytes of a quantised token row
-  const int wrowb = FMT == WFMT_MXFP4 ? K / 2 : K;        // bytes of a weight row
+  const int wrowb = C::W4 ? K / 2 : K;                    // bytes of a weight row
   uint32_t src[C::LOADS];
   uint32_t xs_src[2];
   uint32_t ws_src = 0;
@@ -186,24 +200,32 @@ gemm_pf_q8(const WorkList* __restrict__ wl, const int32_t* __restrict__ counts,
     wbase = pool + (size_t)t.slot * S;
     tok_blocks = (t.nrows + 7) >> 3;
     if (wtok) {
+      if (C::X6) {
+        // rows row0 .. row0 + nrows - 1 of the chunk's plane, whole 1 KiB blocks
+        tok_blocks = (t.nrows * X6_ROWB + 1023) >> 10;
 #pragma unroll
-      for (int q = 0; q < C::TLOADS; ++q) {
-        const int r = (wave * C::TLOADS + q) * 8 + (lane >> 3);
-        const int piece = (lane & 7) ^ ((r >> 1) & 7);
-        src[q] = (uint32_t)(t.row0 + min(r, t.nrows - 1)) * (uint32_t)xrowb + piece * 16;
+        for (int q = 0; q < C::TLOADS; ++q)
+          src[q] = (uint32_t)t.row0 * (uint32_t)X6_ROWB + (uint32_t)((wave * C::TLOADS + q) * 1024 + lane * 16);
+      } else {
+#pragma unroll
+        for (int q = 0; q < C::TLOADS; ++q) {
+          const int r = (wave * C::TLOADS + q) * 8 + (lane >> 3);
+          const int piece = (lane & 7) ^ ((r >> 1) & 7);
+          src[q] = (uint32_t)(t.row0 + min(r, t.nrows - 1)) * (uint32_t)xrowb + piece * 16;
+        }
       }
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         const int r = min(64 * (wave + 4 * i) + lane, C::BM - 1);
         const uint32_t xr = (uint32_t)(t.row0 + min(r, t.nrows - 1));
-        xs_src[i] = FMT == WFMT_MXFP4 ? xr * (uint32_t)kb32 : xr * (uint32_t)kb128 * 4u;
+        xs_src[i] = C::X6 ? xr * 4u : (C::W4 ? xr * (uint32_t)kb32 : xr * (uint32_t)kb128 * 4u);
       }
     } else {
       const int wv = wave - Q_WAVES / 2;
 #pragma unroll
       for (int q = 0; q < C::WLOADS; ++q) {
         const int wr = (wv * C::WLOADS + q) * C::WRPB + lane / (64 / C::WRPB);   // weight tile row
-        const int piece = FMT == WFMT_MXFP4 ? ((lane & 3) ^ ((wr >> 2) & 3)) : ((lane & 7) ^ ((wr >> 1) & 7));
+        const int piece = C::W4 ? ((lane & 3) ^ ((wr >> 2) & 3)) : ((lane & 7) ^ ((wr >> 1) & 7));
         size_t off;
         if (GATED) {
           const int h = wr >> 6, g = (wr >> 5) & 1, j = wr & 31;
@@ -213,7 +235,7 @@ gemm_pf_q8(const WorkList* __restrict__ wl, const int32_t* __restrict__ counts,
         }
         src[q] = (uint32_t)off + piece * 16;
       }
-      if (FMT == WFMT_MXFP4) {
+      if (C::W4) {
         // E8M0 dword (4 blocks of 32) of weight tile row 64*wv + lane
         const int wr = 64 * wv + lane;
         size_t off;
@@ -253,14 +275,15 @@ gemm_pf_q8(const WorkList* __restrict__ wl, const int32_t* __restrict__ counts,
     lds_u8_t* sb = (lds_u8_t*)lds + stage * C::STAGE;
     int n = 0;
     if (wtok) {
-      const uint8_t* xb_ = X + kc * 128;
+      const uint8_t* xb_ = C::X6 ? X + (size_t)kc * x6_plane_bytes(xcap) : X + kc * 128;
 #pragma unroll
       for (int q = 0; q < C::TLOADS; ++q)
         if (wave * C::TLOADS + q < tok_blocks) {
           dma16(xb_ + src[q], sb + C::T_OFF + (wave * C::TLOADS + q) * 1024);
           ++n;
         }
-      const uint8_t* xsb = Xs + kc * 4;         // fp32 scale kc, or E8M0 bytes 4kc..4kc+3
+      // fp32 scale kc, or E8M0 bytes 4kc..4kc+3 (MXFP6: scale plane kc)
+      const uint8_t* xsb = C::X6 ? Xs + (size_t)kc * xcap * 4 : Xs + kc * 4;
 #pragma unroll
       for (int i = 0; i < 2; ++i)
         if (wave + 4 * i < C::NXS) {
@@ -273,7 +296,7 @@ gemm_pf_q8(const WorkList* __restrict__ wl, const int32_t* __restrict__ counts,
 #pragma unroll
       for (int q = 0; q < C::WLOADS; ++q) dma16(wb_ + src[q], sb + C::W_OFF + (wv * C::WLOADS + q) * 1024);
       n = C::WLOADS;
-      if (FMT == WFMT_MXFP4) {
+      if (C::W4) {
         dma4(wbase + ws_src + kc * 4, sb + C::WS_OFF + wv * 256);
         ++n;
       } else if (wv == 0) {
@@ -289,7 +312,7 @@ gemm_pf_q8(const WorkList* __restrict__ wl, const int32_t* __restrict__ counts,
   // 16i + lr of the weight region; the swizzle of such a row depends on lr only
   const int trow = C::HALF * wm + lr, wrow = 64 * wn + lr;
   int x_rd[2], w_rd[2];
-  if (FMT == WFMT_MXFP4) {
+  if (C::W4) {
     x_rd[0] = C::T_OFF + qswz<128>(trow, lg);
     x_rd[1] = C::T_OFF + qswz<128>(trow, 4 + lg);
     w_rd[0] = C::W_OFF + qswz<64>(wrow, lg);
@@ -314,14 +337,31 @@ gemm_pf_q8(const WorkList* __restrict__ wl, const int32_t* __restrict__ counts,
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       const i32x4_t lo = lds16(sb + w_rd[0] + i * 16 * C::WROWB);
-      if (FMT == WFMT_MXFP4) {
+      if (C::W4) {
         wa[i] = i32x8_t{lo[0], lo[1], lo[2], lo[3], 0, 0, 0, 0};
       } else {
         const i32x4_t hi = lds16(sb + w_rd[1] + i * 16 * C::WROWB);
         wa[i] = i32x8_t{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
       }
     }
-    if (FMT == WFMT_MXFP4) {
+    if (C::X6) {
+      int wsc[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) wsc[i] = sb[C::WS_OFF + (wrow + 16 * i) * 4 + lg];
+      const uint8_t* rb = sb + C::T_OFF + trow * X6_ROWB;
+      const int o16 = x6_off16(lg), o8 = x6_off8(lg);
+#pragma unroll
+      for (int j = 0; j < C::SUB; ++j) {
+        const uint8_t* p = rb + j * 16 * X6_ROWB;
+        const i32x4_t a = lds16(p + o16);
+        const uint2 b = *(const uint2*)(p + o8);
+        const i32x8_t xv = i32x8_t{a[0], a[1], a[2], a[3], (int)b.x, (int)b.y, 0, 0};
+        const int xsc = sb[xs_at(trow + 16 * j) + lg];
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+          acc[i][j] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wa[i], xv, acc[i][j], 4, 2, 0, wsc[i], 0, xsc);
+      }
+    } else if (C::W4) {
       int wsc[4];
 #pragma unroll
       for (int i = 0; i < 4; ++i) wsc[i] = sb[C::WS_OFF + (wrow + 16 * i) * 4 + lg];
@@ -455,21 +495,22 @@ template <int FMT, int VAR>
 static size_t lds_of() { return (size_t)QCfg<FMT, VAR>::NST * QCfg<FMT, VAR>::STAGE; }
 
 extern "C" size_t moe_pf8_lds_bytes(int fmt, int small) {
+  if (fmt == WFMT_MXFP4_A6) return small ? lds_of<WFMT_MXFP4_A6, 1>() : lds_of<WFMT_MXFP4_A6, 0>();
   if (fmt == WFMT_MXFP4) return small ? lds_of<WFMT_MXFP4, 1>() : lds_of<WFMT_MXFP4, 0>();
   return small ? lds_of<WFMT_FP8, 1>() : lds_of<WFMT_FP8, 0>();
 }
-// Tokens per m-tile of the large-batch 8-bit kernel; small != 0: the variant
-// for few tokens per expert.
+// Tokens per m-tile of the large-batch 8-bit kernel (fmt WFMT_MXFP4_A6: MXFP6
+// activations); small != 0: the variant for few tokens per expert.
 extern "C" int moe_pf8_tile_tokens(int fmt, int small) {
   if (small) return QCfg<WFMT_FP8, 1>::BM;
-  return fmt == WFMT_MXFP4 ? QCfg<WFMT_MXFP4, 0>::BM : QCfg<WFMT_FP8, 0>::BM;
+  return fmt == WFMT_FP8 ? QCfg<WFMT_FP8, 0>::BM : QCfg<WFMT_MXFP4, 0>::BM;
 }
 
 template <int FMT, bool GATED, int VAR>
 static hipError_t launch_q8(int n_cu, const WorkList* wl, const int32_t* counts, const int32_t* offsets,
                             const uint8_t* pool, size_t S, size_t woff0, size_t woff1, size_t soff0, size_t soff1,
-                            const uint8_t* X, const uint8_t* Xs, int K, int N, void* out, int trash_row,
-                            hipStream_t s) {
+                            const uint8_t* X, const uint8_t* Xs, int xcap, int K, int N, void* out,
+                            int trash_row, hipStream_t s) {
   const size_t lds = lds_of<FMT, VAR>();
   static bool attr = false;
   if (!attr) {
@@ -479,21 +520,24 @@ static hipError_t launch_q8(int n_cu, const WorkList* wl, const int32_t* counts,
     attr = true;
   }
   gemm_pf_q8<FMT, GATED, VAR><<<n_cu, 64 * Q_WAVES, lds, s>>>(wl, counts, offsets, pool, S, woff0, woff1, soff0,
-                                                                 soff1, X, Xs, K, N, out, trash_row);
+                                                                 soff1, X, Xs, xcap, K, N, out, trash_row);
   return hipGetLastError();
 }
 
 // n_cu: CUs (one workgroup each).  The work list must have been built with
-// m-blocks of moe_pf8_tile_tokens(fmt, small) tokens.
+// m-blocks of moe_pf8_tile_tokens(fmt, small) tokens.  xcap: the row
+// capacity the MXFP6 planes are sized for (fmt WFMT_MXFP4_A6; ignored
+// otherwise).
 extern "C" hipError_t moe_launch_gemm_pf8(int fmt, int gated, int small, int n_cu, const WorkList* wl,
                                           const int32_t* counts, const int32_t* offsets, const uint8_t* pool,
                                           size_t S, size_t woff0, size_t woff1, size_t soff0, size_t soff1,
-                                          const void* X, const void* Xs, int K, int N, void* out, int trash_row,
-                                          hipStream_t s) {
+                                          const void* X, const void* Xs, int xcap, int K, int N, void* out,
+                                          int trash_row, hipStream_t s) {
   if (K % Q_BK || N % (gated ? Q_BN / 2 : Q_BN)) return hipErrorInvalidValue;
   const uint8_t* x = (const uint8_t*)X;
   const uint8_t* xs = (const uint8_t*)Xs;
-#define MOE_Q8_ARGS n_cu, wl, counts, offsets, pool, S, woff0, woff1, soff0, soff1, x, xs, K, N, out, trash_row, s
+#define MOE_Q8_ARGS n_cu, wl, counts, offsets, pool, S, woff0, woff1, soff0, soff1, x, xs, xcap, K, N, out, \
+                    trash_row, s
   if (fmt == WFMT_FP8) {
     if (small) return gated ? launch_q8<WFMT_FP8, true, 1>(MOE_Q8_ARGS) : launch_q8<WFMT_FP8, false, 1>(MOE_Q8_ARGS);
     return gated ? launch_q8<WFMT_FP8, true, 0>(MOE_Q8_ARGS) : launch_q8<WFMT_FP8, false, 0>(MOE_Q8_ARGS);
@@ -501,6 +545,11 @@ extern "C" hipError_t moe_launch_gemm_pf8(int fmt, int gated, int small, int n_c
   if (fmt == WFMT_MXFP4) {
     if (small) return gated ? launch_q8<WFMT_MXFP4, true, 1>(MOE_Q8_ARGS) : launch_q8<WFMT_MXFP4, false, 1>(MOE_Q8_ARGS);
     return gated ? launch_q8<WFMT_MXFP4, true, 0>(MOE_Q8_ARGS) : launch_q8<WFMT_MXFP4, false, 0>(MOE_Q8_ARGS);
+  }
+  if (fmt == WFMT_MXFP4_A6) {
+    if (small)
+      return gated ? launch_q8<WFMT_MXFP4_A6, true, 1>(MOE_Q8_ARGS) : launch_q8<WFMT_MXFP4_A6, false, 1>(MOE_Q8_ARGS);
+    return gated ? launch_q8<WFMT_MXFP4_A6, true, 0>(MOE_Q8_ARGS) : launch_q8<WFMT_MXFP4_A6, false, 0>(MOE_Q8_ARGS);
   }
 #undef MOE_Q8_ARGS
   return hipErrorInvalidValue;

@@ -88,6 +88,10 @@ class MoeRuntime:
     def set_policy(self, policy, B_P=1.0, B_H=1.0):
         self._chk(B.moe_set_policy(self.ctx, policy, B_P, B_H))
 
+    def set_activations(self, act):
+        """MOE_ACT_DEFAULT or MOE_ACT_MXFP6 (MXFP4 weights' large-batch path)."""
+        self._chk(B.moe_set_activations(self.ctx, act))
+
     def calibrate(self):
         bp, bh = ctypes.c_double(), ctypes.c_double()
         self._chk(B.moe_calibrate(self.ctx, ctypes.byref(bp), ctypes.byref(bh)))

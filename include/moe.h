@@ -74,6 +74,8 @@ enum {
 };
 
 enum { MOE_W_BF16 = 0, MOE_W_FP8_E4M3_B128 = 1, MOE_W_MXFP4 = 2, MOE_W_NVFP4 = 3 };
+enum { MOE_ACT_DEFAULT = 0, MOE_ACT_MXFP6 = 1 };   /* moe_set_activations */
+enum { MOE_QUANT_MXFP6 = 64 };                      /* moe_quantize format code */
 
 /* Miss policy (paper.oopus.info review, section 5 lists the backend switch
  * offload / cpu / hybrid): OFFLOAD fills every miss (q = m), HOST executes
@@ -128,6 +130,16 @@ const char* moe_last_error(moe_ctx* ctx);
 int moe_host_alloc(size_t bytes, void** out);
 int moe_host_free(void* p);
 
+/* Activation format of the MXFP4 weight path's large-batch GEMMs (the
+ * tiled kernels, used when T > 64 and T*k >= 48*E): MOE_ACT_DEFAULT keeps
+ * MXFP8 (E4M3 per 32 with an E8M0 scale), MOE_ACT_MXFP6 quantises both GEMM
+ * inputs to MXFP6 (E2M3 per 32, see moe_quantize), which the scaled MFMA
+ * multiplies with the E2M1 weights at the 6/4-bit rate.  The pages list
+ * MXFP4 among the served formats; the activation format is a declared
+ * reading.  MOE_E_INVAL for an unknown value or MXFP6 without MXFP4
+ * weights.  Small batches keep MXFP8 activations. */
+int moe_set_activations(moe_ctx* ctx, int act);
+
 /* Miss policy and the bandwidths (GB/s) q* uses (section 2.5). */
 int moe_set_policy(moe_ctx* ctx, int policy, double B_P, double B_H);
 
@@ -161,8 +173,20 @@ int moe_route(moe_ctx* ctx, const void* hidden, const float* router_w, const flo
  *   wfmt 2 (mxfp4 weights, MXFP8 activations): per (row, 32 columns) E8M0
  *                 scale 2^x, x = floor(log2 amax) - 8, q = E4M3(v*2^-x);
  *                 scale uint8 [rows, cols/32]; cols % 32 == 0.
- * q uint8 [rows, cols] (E4M3 codes), caller-owned.  Asynchronous on stream;
- * MOE_E_INVAL for another format or a bad shape. */
+ *   MOE_QUANT_MXFP6 (mxfp4 weights, MXFP6 activations): per (row, 32
+ *                 columns) E8M0 scale 2^x, x = floor(log2 amax) - 2, codes
+ *                 E2M3(v*2^-x) (OCP MX FP6, nearest even, saturating at 7.5);
+ *                 cols % 128 == 0.  Chunk-major: q holds cols/128 planes of
+ *                 P = round_up(rows*112 + 1024, 256) bytes, rows of 112
+ *                 bytes (the last 16 unused); the codes of columns
+ *                 128c+32g .. +31 are a 24-byte little-endian string (code
+ *                 j at bits 6j..6j+5) whose bytes 0-15 are at
+ *                 c*P + r*112 + 24g + 8*(g odd) and bytes 16-23 at
+ *                 c*P + r*112 + 24g + 16*(g even); scale uint8
+ *                 [cols/128][rows][4], byte g of (c, r) for columns
+ *                 128c+32g .. +31.
+ * q uint8 [rows, cols] (E4M3 codes) otherwise, caller-owned.  Asynchronous
+ * on stream; MOE_E_INVAL for another format or a bad shape. */
 int moe_quantize(int wfmt, int src_bf16, const void* src, int rows, int cols, const int32_t* row_map, uint8_t* q,
                  void* scale, void* stream);
 

@@ -38,6 +38,18 @@ class Setup:
         self.R_d = [torch.from_numpy(r).cuda() for r in self.R]
         self.b_d = [None if b is None else torch.from_numpy(b).cuda() for b in self.b]
         self._w = {}
+        self.act = None
+
+    def set_act(self, act):
+        """MXFP4 activation variant: None (MXFP8) or "mxfp6" (large-batch GEMMs)."""
+        from expert_ffn_execution_router_amd import binding as B
+        self.rt.set_activations(B.MOE_ACT_MXFP6 if act == "mxfp6" else B.MOE_ACT_DEFAULT)
+        self.act = act
+
+    def tiled(self, T):
+        """Whether a forward of T tokens runs the large-batch GEMMs."""
+        c = self.cfg
+        return T > 64 and T * c.k >= 48 * c.E and c.fmt != 3
 
     def weights(self, layer):
         def get(e):
@@ -52,10 +64,14 @@ class Setup:
         x = synth.hidden(self.cfg, self.seed, T, tag)
         return x, torch.from_numpy(x.view(np.int16)).cuda()
 
-    def oracle(self, layer, x_bits, mode="mirrored", rows=None):
+    def oracle(self, layer, x_bits, mode="mirrored", rows=None, T=None):
+        """T: tokens of the GPU call (default len(x_bits)); the MXFP6 variant
+        applies only where that call ran the large-batch GEMMs."""
         xs = x_bits if rows is None else x_bits[rows]
+        T = len(x_bits) if T is None else T
+        act = self.act if self.tiled(T) else None
         return M.moe_layer(xs, self.R[layer], self.b[layer], self.cfg.k, self.weights(layer), fmt=self.cfg.fmt,
-                           mode=mode)
+                           mode=mode, act=act)
 
     def admit_all(self, layer):
         self.rt.admit(layer, list(range(self.cfg.E)))

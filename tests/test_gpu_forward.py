@@ -5,7 +5,8 @@ import numpy as np
 import pytest
 import torch
 
-from gpu_util import TOL, Setup, bf16_to_np, compare, shape
+from gpu_util import MARGIN, TOL, Setup, bf16_to_np, compare, rel_err, shape
+from oracle import moe as M
 
 pytestmark = pytest.mark.gpu
 
@@ -16,6 +17,8 @@ CASES = {
     "bf16_mid": dict(base=1, E=32, k=4, H=1024, I=384),
     "nvfp4_small": dict(base=1, fmt=3, H=512, I=256),
     "nvfp4_mid": dict(base=1, fmt=3, E=32, k=4, H=1024, I=384),
+    "mxfp4_x6_small": dict(base=1, fmt=2, H=512, I=256, act="mxfp6"),
+    "mxfp4_x6_mid": dict(base=1, fmt=2, E=32, k=4, H=1024, I=384, act="mxfp6"),
 }
 
 
@@ -30,9 +33,12 @@ def setups():
 def _get(setups, name):
     if name not in setups:
         kw = dict(CASES[name])
+        act = kw.pop("act", None)
         cfg = shape(kw.pop("base"), **kw)
         s = Setup(cfg, seed=11, max_tokens=1024)
         s.admit_all(0)
+        if act:
+            s.set_act(act)
         setups[name] = s
     return setups[name]
 
@@ -51,18 +57,51 @@ def test_forward_matches_oracle(setups, name, T):
     print(f"  err vs mirrored {e_m:.2e}, vs exact {e_x:.2e}, rows {n}")
 
 
-@pytest.mark.parametrize("name", ["bf16_tiny", "fp8_small", "mxfp4_small", "nvfp4_small"])
+@pytest.mark.parametrize("name", ["bf16_tiny", "fp8_small", "mxfp4_small", "nvfp4_small", "mxfp4_x6_small"])
 def test_forward_is_deterministic(setups, name):
     s = _get(setups, name)
-    x, xd = s.hidden(100, tag=5)
+    T = 400 if s.act else 100                  # MXFP6 only in the large-batch GEMMs
+    x, xd = s.hidden(T, tag=5)
     outs = []
     for _ in range(3):
-        out = torch.empty(100, s.cfg.H, dtype=torch.bfloat16, device="cuda")
+        out = torch.empty(T, s.cfg.H, dtype=torch.bfloat16, device="cuda")
         s.rt.forward(0, xd, s.R_d[0], s.b_d[0], s.slot_row(0), out)
         outs.append(out)
     torch.cuda.synchronize()
     assert torch.equal(outs[0].view(torch.int16), outs[1].view(torch.int16))
     assert torch.equal(outs[0].view(torch.int16), outs[2].view(torch.int16))
+
+
+def test_mxfp6_activations_in_effect(setups):
+    """The MXFP6 variant is what runs: at a large batch the output sits much
+    closer to the oracle mirroring MXFP6 than to the one mirroring MXFP8, and
+    switching back to the default gives the MXFP8 result; MXFP6 needs MXFP4
+    weights."""
+    from expert_ffn_execution_router_amd import binding as B
+    s = _get(setups, "mxfp4_x6_small")
+    T = 1000
+    x, xd = s.hidden(T, tag=77)
+    out = torch.empty(T, s.cfg.H, dtype=torch.bfloat16, device="cuda")
+    s.rt.forward(0, xd, s.R_d[0], s.b_d[0], s.slot_row(0), out)
+    torch.cuda.synchronize()
+    r6 = M.moe_layer(x, s.R[0], s.b[0], s.cfg.k, s.weights(0), fmt=2, mode="mirrored", act="mxfp6")
+    r8 = M.moe_layer(x, s.R[0], s.b[0], s.cfg.k, s.weights(0), fmt=2, mode="mirrored")
+    rows = np.nonzero(r6["margin"] >= MARGIN)[0]
+    got = bf16_to_np(out)
+    e6, e8 = rel_err(got, r6["out"], rows), rel_err(got, r8["out"], rows)
+    print(f"mxfp6 run: err vs mxfp6 mirror {e6:.2e}, vs mxfp8 mirror {e8:.2e}")
+    assert e6 * 3 < e8
+    try:
+        s.set_act(None)
+        s.rt.forward(0, xd, s.R_d[0], s.b_d[0], s.slot_row(0), out)
+        torch.cuda.synchronize()
+        got = bf16_to_np(out)
+        assert rel_err(got, r8["out"], rows) * 3 < rel_err(got, r6["out"], rows)
+    finally:
+        s.set_act("mxfp6")
+    bf = _get(setups, "bf16_tiny")
+    assert B.moe_set_activations(bf.rt.ctx, B.MOE_ACT_MXFP6) == B.MOE_E_INVAL
+    assert B.moe_set_activations(s.rt.ctx, 7) == B.MOE_E_INVAL
 
 
 def test_forward_empty_batch(setups):
@@ -120,13 +159,16 @@ def edge_counts(cap):
     return [cap, cap + 1, 2 * cap, 2 * cap + 1, 1, 17, 900, 0]
 
 
-@pytest.mark.parametrize("fmt,cap", [(0, 288), (1, 256), (2, 288), (1, 128), (2, 128)])
-def test_tiled_forward_tile_edges(fmt, cap):
+@pytest.mark.parametrize("fmt,cap,act", [(0, 288, None), (1, 256, None), (2, 288, None), (1, 128, None),
+                                         (2, 128, None), (2, 288, "mxfp6"), (2, 128, "mxfp6")])
+def test_tiled_forward_tile_edges(fmt, cap, act):
     """Routing forced to edge_counts by a one-hot router: token t's hidden row
     holds 4 at its first expert's dimension and 3 at its second's (noise
     elsewhere), the router reads dimension e for expert e.  cap 128: the
-    8-bit formats' variant for few tokens per expert (128-token tiles)."""
-    print(f"tile edges fmt={fmt} cap={cap}", flush=True)
+    8-bit formats' variant for few tokens per expert (128-token tiles).
+    act "mxfp6": MXFP6 activations (tiles start at any row of the 16-row
+    blocks their operand loads are aligned to)."""
+    print(f"tile edges fmt={fmt} cap={cap} act={act}", flush=True)
     cfg = shape(1, fmt=fmt)                          # E=8, k=2, H=256, I=128
     E, k, H = cfg.E, cfg.k, cfg.H
     counts = edge_counts(cap)
@@ -153,6 +195,8 @@ def test_tiled_forward_tile_edges(fmt, cap):
     s = Setup(cfg, seed=5, max_tokens=T)
     try:
         s.admit_all(0)
+        if act:
+            s.set_act(act)
         s.R[0], s.b[0] = R, None
         xd = torch.from_numpy(bits.view(np.int16)).cuda()
         out = torch.empty(T, H, dtype=torch.bfloat16, device="cuda")

@@ -23,7 +23,8 @@ def _check_rows(s, layer, x, out_t, n_sample, seed):
 
     def wf(e):   # no caching: one expert's float64 weights at a time
         return M.dequant_expert(s.pool_np[layer * cfg.E + e], cfg.fmt, cfg.H, cfg.I)
-    ref = M.moe_layer(x[rows], s.R[layer], s.b[layer], cfg.k, wf, fmt=cfg.fmt, mode="mirrored")
+    act = s.act if s.tiled(len(x)) else None
+    ref = M.moe_layer(x[rows], s.R[layer], s.b[layer], cfg.k, wf, fmt=cfg.fmt, mode="mirrored", act=act)
     got = bf16_to_np(out_t)[rows]
     err = rel_err(got, ref["out"])
     print(f"  sampled rows {list(rows)} err vs mirrored {err:.2e}")
@@ -106,6 +107,26 @@ def test_mxfp4_config5_shape(T):
     try:
         s.admit_all(0)
         x, xd = s.hidden(T, tag=T)
+        out = torch.empty(T, cfg.H, dtype=torch.bfloat16, device="cuda")
+        s.rt.forward(0, xd, s.R_d[0], s.b_d[0], s.slot_row(0), out)
+        torch.cuda.synchronize()
+        assert s.rt.check_device_error() == 0
+        _check_rows(s, 0, x, out, 3, T)
+    finally:
+        s.close()
+
+
+@pytest.mark.parametrize("T", [2048, 16384])
+def test_mxfp4_config5_shape_mxfp6(T):
+    """MXFP6 activations on the MXFP4 shape, up to the prefill chunk the bench
+    times (16384 tokens, ~512 rows per expert)."""
+    print(f"mxfp4 config-5 shape, MXFP6 activations, T={T}", flush=True)
+    cfg = _fullsize(5, L=1)
+    s = Setup(cfg, seed=3, max_tokens=T, host_threads=8)
+    try:
+        s.admit_all(0)
+        s.set_act("mxfp6")
+        x, xd = s.hidden(T, tag=T + 1)
         out = torch.empty(T, cfg.H, dtype=torch.bfloat16, device="cuda")
         s.rt.forward(0, xd, s.R_d[0], s.b_d[0], s.slot_row(0), out)
         torch.cuda.synchronize()

@@ -17,8 +17,10 @@ def _cfg(fmt=0):
     return shape(1, L=3, E=8, k=2, H=512, I=256, fmt=fmt)
 
 
-def _prefill(cfg, n_slots, T, double_buffer=True, seed=2):
+def _prefill(cfg, n_slots, T, double_buffer=True, seed=2, act=None):
     s = Setup(cfg, seed=seed, n_slots=n_slots, max_tokens=T)
+    if act:
+        s.set_act(act)
     outs, xs, rcs = [], [], []
     comp, copy = torch.cuda.Stream(), torch.cuda.Stream()
     with torch.cuda.stream(comp):
@@ -33,12 +35,12 @@ def _prefill(cfg, n_slots, T, double_buffer=True, seed=2):
     return s, outs, xs, rcs
 
 
-@pytest.mark.parametrize("fmt", [0, 1, 2])
-def test_prefill_matches_oracle_and_is_buffer_invariant(fmt):
-    print(f"prefill fmt={fmt}", flush=True)
+@pytest.mark.parametrize("fmt,act", [(0, None), (1, None), (2, None), (2, "mxfp6")])
+def test_prefill_matches_oracle_and_is_buffer_invariant(fmt, act):
+    print(f"prefill fmt={fmt} act={act}", flush=True)
     cfg = _cfg(fmt)
     T = 300
-    s, outs, xs, rcs = _prefill(cfg, 2 * cfg.E, T)
+    s, outs, xs, rcs = _prefill(cfg, 2 * cfg.E, T, act=act)
     try:
         assert rcs == [0] * cfg.L
         assert s.rt.check_device_error() == 0
@@ -53,7 +55,7 @@ def test_prefill_matches_oracle_and_is_buffer_invariant(fmt):
     for n_slots, dbuf, want_rc in [(2 * cfg.E, False, 0), (cfg.L * cfg.E, True, 0), (cfg.E, True, 2),
                                    (2 * cfg.E - 1, True, 2)]:
         print(f"  variant n_slots={n_slots} double_buffer={dbuf}", flush=True)
-        s, outs, xs, rcs = _prefill(cfg, n_slots, T, double_buffer=dbuf)
+        s, outs, xs, rcs = _prefill(cfg, n_slots, T, double_buffer=dbuf, act=act)
         try:
             assert rcs == [want_rc] * cfg.L
             for a, b in zip(ref, outs):
@@ -65,7 +67,7 @@ def test_prefill_matches_oracle_and_is_buffer_invariant(fmt):
     # for bit); 3 slots leave a short last range
     for n_slots in (cfg.E // 2, 3):
         print(f"  variant in ranges n_slots={n_slots}", flush=True)
-        s, outs, xs, rcs = _prefill(cfg, n_slots, T)
+        s, outs, xs, rcs = _prefill(cfg, n_slots, T, act=act)
         try:
             assert rcs == [1] * cfg.L
             assert s.rt.check_device_error() == 0
