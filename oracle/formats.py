@@ -49,6 +49,13 @@ def round_to_bf16(x: np.ndarray) -> np.ndarray:
     return out
 
 
+def round_to_f16(x: np.ndarray) -> np.ndarray:
+    """Round float64 values to IEEE binary16 (ties to even, overflow to
+    infinity, subnormals kept), returned as float64.  Like round_to_bf16 the
+    value passes through binary32 first (the GPU holds it in fp32)."""
+    return np.asarray(x, dtype=np.float64).astype(np.float32).astype(np.float16).astype(np.float64)
+
+
 def _e4m3_value(code: int) -> float:
     s = -1.0 if code & 0x80 else 1.0
     e = (code >> 3) & 0xF

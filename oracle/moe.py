@@ -40,7 +40,7 @@ from __future__ import annotations
 import numpy as np
 
 from .formats import (bf16_to_f64, decode_e2m1, decode_e2m3, decode_e4m3, e8m0_to_f64, encode_e2m3,
-                      encode_e4m3, round_to_bf16)
+                      encode_e4m3, round_to_bf16, round_to_f16)
 
 FMT_BF16, FMT_FP8, FMT_MXFP4, FMT_NVFP4 = 0, 1, 2, 3
 
@@ -245,10 +245,13 @@ def mirror_quant_mxfp6(v: np.ndarray) -> np.ndarray:
 
 def mirror_activation(v: np.ndarray, fmt: int, act: str | None = None) -> np.ndarray:
     """The GPU path's rounding of a GEMM input activation (x before GEMM 1,
-    A before GEMM 2): bf16 and nvfp4 -> bf16, fp8 -> per-128 E4M3, mxfp4 ->
-    MXFP8, or MXFP6 with act="mxfp6" (the large-batch MXFP6 variant)."""
-    if fmt in (FMT_BF16, FMT_NVFP4):
+    A before GEMM 2): bf16 -> bf16, nvfp4 -> fp16 (its dequantised weights
+    and the activations meet in the fp16 MFMA), fp8 -> per-128 E4M3, mxfp4
+    -> MXFP8, or MXFP6 with act="mxfp6" (the large-batch MXFP6 variant)."""
+    if fmt == FMT_BF16:
         return round_to_bf16(v)
+    if fmt == FMT_NVFP4:
+        return round_to_f16(v)
     if fmt == FMT_FP8:
         return mirror_quant_fp8_groups(v, 128)
     if act == "mxfp6":
@@ -258,11 +261,12 @@ def mirror_activation(v: np.ndarray, fmt: int, act: str | None = None) -> np.nda
 
 def expert_ffn_mirrored(x: np.ndarray, Wg, Wu, Wd, fmt: int, act: str | None = None) -> np.ndarray:
     """Expert output Z with the GPU path's rounding points: x quantised (fp8,
-    mxfp4), A = silu(g)*u rounded to bf16 or quantised, Z rounded to bf16.
-    nvfp4 weights enter the bf16 MFMA as element * block scale (exact in
-    bf16) and the tensor scale multiplies the fp32 sums, so the weights are
-    not rounded here.  act: activation variant of mxfp4 (None or "mxfp6")."""
-    xq = x if fmt in (FMT_BF16, FMT_NVFP4) else mirror_activation(x, fmt, act)
+    mxfp4) or rounded to fp16 (nvfp4), A = silu(g)*u rounded to bf16 or fp16
+    or quantised, Z rounded to bf16.  nvfp4 weights enter the fp16 MFMA as
+    element * block scale (exact in fp16) and the tensor scale multiplies
+    the fp32 sums, so the weights are not rounded here.  act: activation
+    variant of mxfp4 (None or "mxfp6")."""
+    xq = x if fmt == FMT_BF16 else mirror_activation(x, fmt, act)
     g = xq @ Wg.T
     u = xq @ Wu.T
     a = silu(g) * u

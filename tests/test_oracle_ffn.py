@@ -164,7 +164,8 @@ def test_split_is_exact_sum_of_partials():
 # (bf16: 2^-9 relative; E4M3: 2^-4 relative per element), so it sits a
 # quantisation step away from the exact layer.
 @pytest.mark.parametrize("fmt,tol,act", [(M.FMT_BF16, 1e-2, None), (M.FMT_FP8, 0.1, None),
-                                         (M.FMT_MXFP4, 0.1, None), (M.FMT_MXFP4, 0.1, "mxfp6")])
+                                         (M.FMT_MXFP4, 0.1, None), (M.FMT_MXFP4, 0.1, "mxfp6"),
+                                         (M.FMT_NVFP4, 1e-2, None)])
 def test_mirrored_mode_close_to_exact(fmt, tol, act):
     cfg = _tiny(fmt)
     x = synth.hidden(cfg, 4, 16)

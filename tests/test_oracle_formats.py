@@ -112,6 +112,17 @@ def test_bf16_round_matches_torch():
     assert np.array_equal(F.round_to_bf16(f.astype(np.float64)), ref)
 
 
+def test_f16_round_matches_torch():
+    rng = np.random.default_rng(4)
+    v = np.concatenate([rng.normal(0, 1, 20000), rng.normal(0, 1e-5, 5000), rng.normal(0, 3e4, 5000),
+                        np.array([65504.0, 65519.0, 65520.0, 1e6, -1e6, 2.0 ** -24, 2.0 ** -25, 3 * 2.0 ** -26, 0.0])])
+    ref = torch.from_numpy(v.astype(np.float32)).to(torch.float16).to(torch.float64).numpy()
+    got = F.round_to_f16(v)
+    assert np.array_equal(np.isinf(got), np.isinf(ref)) and np.array_equal(got[~np.isinf(got)], ref[~np.isinf(ref)])
+    assert got[-6] == np.inf and got[-5] == -np.inf and got[-7] == np.inf and got[-8] == 65504.0
+    assert got[-4] == 2.0 ** -24 and got[-3] == 0.0 and got[-2] == 2.0 ** -24     # ties to even at the bottom
+
+
 def test_bf16_decode_exact():
     bits = np.array([0x3F80, 0xC000, 0x0000, 0x4049], dtype=np.uint16)
     v = F.bf16_to_f64(bits)
