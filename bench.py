@@ -769,7 +769,7 @@ def phase_formats(args):
             log(f"{name} {key}: {json.dumps(res[key])}")
 
         peak = {4: FP8_PEAK, 5: FP4_PEAK, 6: BF16_PEAK}[cid]
-        prefill_pass(f"prefill_T{pf_T}", "gemm_dec (weight stream, NVFP4 dequantised to bf16 in registers)"
+        prefill_pass(f"prefill_T{pf_T}", "gemm_dec (weight stream, NVFP4 dequantised to fp16 in registers)"
                      if cid == 6 else "gemm_pf_q8 (LDS-tiled scaled-MFMA grouped GEMM)", peak)
         if cid == 5:     # MXFP6 activations: E2M1 x E2M3 at the 6/4-bit MFMA rate
             from expert_ffn_execution_router_amd import binding as B

@@ -46,6 +46,7 @@ hipError_t moe_launch_combine(const uint16_t* Z, const int32_t* ids, const float
                               const int32_t* hp_count, int T, int k, int H, uint16_t* out, float* out_f32,
                               hipStream_t s);
 hipError_t moe_launch_range_mask(int lo, int hi, int E, uint32_t* mask, hipStream_t s);
+hipError_t moe_launch_cvt_f16(const void* src, long n, void* dst, hipStream_t s);
 hipError_t moe_launch_quant(int fmt, int src_bf16, const void* src, int rows, const int32_t* nrows_dev,
                             const int32_t* row_map, int cols, uint8_t* q, void* scale, int cap,
                             hipStream_t s);
@@ -141,7 +142,7 @@ WsLayout ws_layout(const moe_config& c) {
   L.As = take(c.wfmt == MOE_W_FP8_E4M3_B128 ? R * (c.I / 128) * 4 : (q8 ? R * (c.I / 32) : 0));
   L.Z = take((R + 1) * c.H * 2);
   // quantised activations in grouped order (one row per routed pair)
-  L.Xq = take(qbytes(c.H));
+  L.Xq = take(c.wfmt == MOE_W_NVFP4 ? Tm * c.H * 2 : qbytes(c.H));   // NVFP4: the hidden rows in fp16
   L.Xs = take(c.wfmt == MOE_W_FP8_E4M3_B128 ? R * (c.H / 128) * 4 : (q8 ? R * (c.H / 32) : 0));
   L.hp = take(Tm * c.H * 4);
   // small-batch GEMM: partial tiles of items cut between workgroups
@@ -337,14 +338,20 @@ int forward_experts(moe_ctx* c, const void* hidden, int T, const int32_t* slot_r
           moe_launch_gemm_pf(g.wfmt, 0, c->n_cu, c->wl, c->counts, c->offsets, c->slot_pool, b.S, b.w[2], 0, c->A,
                              nullptr, g.I, g.H, c->Z, s));
   } else if (g.wfmt == MOE_W_BF16 || g.wfmt == MOE_W_NVFP4) {
-    // bf16 tokens (gathered through perm_tok for GEMM 1), bf16 A; NVFP4
-    // weights carry their block-scale offsets
+    // 16-bit tokens gathered through perm_tok for GEMM 1 (bf16, or the
+    // hidden rows converted to fp16 for NVFP4's fp16 MFMA), A in the same
+    // type; NVFP4 weights carry their block-scale offsets
+    const void* x16 = hidden;
+    if (g.wfmt == MOE_W_NVFP4) {
+      STAGE(c, MOE_STAGE_QUANT_X, s, moe_launch_cvt_f16(hidden, (long)T * g.H, c->Xq, s));
+      x16 = c->Xq;
+    }
     STAGE(c, MOE_STAGE_GEMM1, s,
           moe_launch_gemm_dec(g.wfmt, 1, ns, ncu, c->wl, c->counts, c->offsets, c->slot_pool, b.S, b.w[0], b.w[1],
-                              b.s[0], b.s[1], hidden, nullptr, c->perm_tok, g.H, g.I, c->A, c->part, 0, s));
+                              b.s[0], b.s[1], x16, nullptr, c->perm_tok, g.H, g.I, c->A, c->part, 0, s));
     STAGE(c, MOE_STAGE_FIXUP, s,
           moe_launch_gemm_dec(g.wfmt, 1, ns, ncu, c->wl, c->counts, c->offsets, c->slot_pool, b.S, b.w[0], b.w[1],
-                              b.s[0], b.s[1], hidden, nullptr, c->perm_tok, g.H, g.I, c->A, c->part, 1, s));
+                              b.s[0], b.s[1], x16, nullptr, c->perm_tok, g.H, g.I, c->A, c->part, 1, s));
     STAGE(c, MOE_STAGE_GEMM2, s,
           moe_launch_gemm_dec(g.wfmt, 0, ns, ncu, c->wl, c->counts, c->offsets, c->slot_pool, b.S, b.w[2], 0, b.s[2],
                               0, c->A, nullptr, nullptr, g.I, g.H, c->Z, c->part, 0, s));

@@ -221,6 +221,27 @@ quant_mxfp6_kernel(const void* __restrict__ src, int rows, const int32_t* __rest
   scale[(size_t)(b >> 2) * cap * 4 + r * 4 + (b & 3)] = (uint8_t)(x + 127);
 }
 
+// bf16 -> IEEE binary16, 8 values a thread (round to nearest even; the NVFP4
+// path's fp16 MFMA takes fp16 tokens).  n % 8 == 0.
+__global__ void __launch_bounds__(256) cvt_f16_kernel(const uint16_t* __restrict__ src, long n,
+                                                      uint16_t* __restrict__ dst) {
+  const long i = ((long)blockIdx.x * 256 + threadIdx.x) * 8;
+  if (i >= n) return;
+  const i32x4_t v = ld16(src + i);
+  i32x4_t o;
+#pragma unroll
+  for (int k = 0; k < 4; ++k)
+    o[k] = (int)pack_f16x2(bf16_bits_to_f32((uint32_t)v[k] & 0xffffu), bf16_bits_to_f32((uint32_t)v[k] >> 16));
+  *(i32x4_t*)(dst + i) = o;
+}
+
+extern "C" hipError_t moe_launch_cvt_f16(const void* src, long n, void* dst, hipStream_t s) {
+  if (n == 0) return hipSuccess;
+  if (n % 8) return hipErrorInvalidValue;
+  cvt_f16_kernel<<<(unsigned)((n / 8 + 255) / 256), 256, 0, s>>>((const uint16_t*)src, n, (uint16_t*)dst);
+  return hipGetLastError();
+}
+
 extern "C" hipError_t moe_launch_combine(const uint16_t* Z, const int32_t* ids, const float* w, const int32_t* pos,
                                          const uint32_t* miss_mask, const int32_t* slot_row, const float* hp,
                                          const int32_t* hp_count, int T, int k, int H, uint16_t* out,

@@ -98,6 +98,14 @@ DEV uint32_t pack_bf16x2(float a, float b) {
   return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, bf16x2_t));
 }
 
+// Two floats to packed IEEE binary16 (low half = a), round to nearest even,
+// overflow to infinity.
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+typedef _Float16 f16x8_t __attribute__((__vector_size__(8 * sizeof(_Float16))));
+DEV uint32_t pack_f16x2(float a, float b) {
+  return __builtin_bit_cast(uint32_t, __builtin_convertvector((f32x2_t){a, b}, f16x2_t));
+}
+
 // OCP E4M3FN code of v, round to nearest even, saturating at +-448.
 DEV uint32_t f32_to_e4m3(float v) {
   uint32_t u = __float_as_uint(v);

@@ -55,20 +55,22 @@
 //    covers K block [32g, 32g+32) of that lane's row (A) or column (B).
 //  * NVFP4 (E2M1 elements, E4M3 scale per 16 inputs, fp32 scale per
 //    matrix): gfx950's scaled MFMA takes only power-of-two block scales, so
-//    the weights are dequantised in registers to bf16 (element * block
-//    scale, exact: at most two and four significant bits) and go through the
-//    bf16 MFMA with bf16 tokens; the matrix's fp32 scale multiplies the fp32
-//    sums in the epilogue (gate and up before SwiGLU, down on Z).  Chunks
-//    are 256 K values: 128 bytes of codes and 16 scale bytes per weight row
-//    (8 lanes per row segment, pieces XOR-swizzled by row & 7), 512 bytes
-//    per token row.
+//    the weights are dequantised in registers to fp16 (element * block
+//    scale, exact: at most six significant bits within 2^-10 .. 2688): one
+//    scaled fp4 -> fp16 pair conversion and one packed fp16 multiply per
+//    two weights (a bf16 product would need fp32 multiplies and packs:
+//    gfx950 has no packed bf16 multiply); they meet fp16 tokens (the hidden
+//    rows converted once per call, A stored in fp16 by GEMM 1) in the fp16
+//    MFMA; the matrix's fp32 scale multiplies the fp32 sums in the epilogue
+//    (gate and up before SwiGLU, down on Z).  Chunks are 256 K values: 128
+//    bytes of codes and 16 scale bytes per weight row (8 lanes per row
+//    segment, pieces XOR-swizzled by row & 7), 512 bytes per token row.
 #include "common.h"
 
 namespace {
 
 constexpr int NW = 4;                 // waves per workgroup
 constexpr int ROWS = 16 * NW;         // weight rows per item and matrix
-constexpr int NST = 3;                // ring stages
 constexpr int N_XCD = 8;
 constexpr int MAX_BLOCKS = 1024;      // capacity of the partial-tile buffer (workgroups)
 constexpr int CACHE_NT = 2;           // cache-policy bits of a nontemporal load (gfx94x/gfx950)
@@ -77,7 +79,7 @@ template <int FMT, bool GATED, int NS>
 struct Cfg {
   static constexpr int NMAT = GATED ? 2 : 1;
   static constexpr bool NV = FMT == WFMT_NVFP4;
-  static constexpr bool BF_X = FMT == WFMT_BF16 || NV;       // bf16 tokens
+  static constexpr bool BF_X = FMT == WFMT_BF16 || NV;       // 16-bit tokens (bf16, or fp16 for NVFP4)
   static constexpr int CK = FMT == WFMT_BF16 ? 128 : (FMT == WFMT_MXFP4 ? 512 : 256);   // K per chunk
   static constexpr int WB = NV ? 128 : 256;                   // weight bytes per row per chunk
   static constexpr int WSZ = 16 * WB;                         // one wave's rows of one matrix
@@ -92,6 +94,8 @@ struct Cfg {
   static constexpr int WS_OFF = XS_OFF + XS_BYTES;
   static constexpr int WS_BYTES = FMT == WFMT_BF16 ? 0 : (FMT == WFMT_FP8 ? NW * 256 : NMAT * NW * 256);
   static constexpr int STAGE = WS_OFF + WS_BYTES;
+  // ring stages: NVFP4 with two stages fits more workgroups per CU
+  static constexpr int NST = (NV && NS <= 2) ? 2 : 3;
   // loads per wave per chunk: weights, tokens, token scales, weight scales
   static constexpr int NI = NWL * NMAT + NXI + (BF_X ? 0 : 1) +
                             (FMT == WFMT_BF16 ? 0 : (FMT == WFMT_FP8 ? 1 : NMAT));
@@ -166,7 +170,8 @@ DEV void nv_tensor_scales(const uint8_t* pool, size_t S, int slot, int K, int N,
   s1 = gated ? t[1] : 1.0f;
 }
 
-// Store the output values (fp32 for GEMM 1 of the 8-bit formats, else bf16).
+// Store the output values (fp32 for GEMM 1 of the 8-bit formats, fp16 for
+// GEMM 1 of NVFP4, else bf16).
 template <int FMT, bool GATED, int NS>
 DEV void store_out(const f32x4_t* val, const Item& it, int wave, int lane, int N, void* out) {
   const int lr = lane & 15, lg = lane >> 4;
@@ -178,6 +183,11 @@ DEV void store_out(const f32x4_t* val, const Item& it, int wave, int lane, int N
     const size_t o = (size_t)(it.row0 + t) * N + col;
     if (GATED && (FMT == WFMT_FP8 || FMT == WFMT_MXFP4)) {
       *(f32x4_t*)((float*)out + o) = val[ms];
+    } else if (GATED && FMT == WFMT_NVFP4) {
+      uint2 pk;
+      pk.x = pack_f16x2(val[ms][0], val[ms][1]);
+      pk.y = pack_f16x2(val[ms][2], val[ms][3]);
+      st8((uint16_t*)out + o, pk);
     } else {
       uint2 pk;
       pk.x = pack_bf16x2(val[ms][0], val[ms][1]);
@@ -534,15 +544,12 @@ gemm_dec(const WorkList* __restrict__ wl, const int32_t* __restrict__ counts, co
           for (int m = 0; m < C::NMAT; ++m) {
             // block 2q + lg/2 of the chunk: byte 2(q&1) + lg/2 of dword q/2
             const int scw = (int)((uint32_t)scv[m][q >> 1] >> (8 * (2 * (q & 1) + (lg >> 1))));
-            const float sc = __builtin_amdgcn_cvt_f32_fp8(scw, 0);
-            const auto f0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw[j][m], 1.0f, 0);
-            const auto f1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw[j][m], 1.0f, 1);
-            const auto f2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw[j][m], 1.0f, 2);
-            const auto f3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(cw[j][m], 1.0f, 3);
-            wa[j][m][0] = (int)pack_bf16x2(f0[0] * sc, f0[1] * sc);
-            wa[j][m][1] = (int)pack_bf16x2(f1[0] * sc, f1[1] * sc);
-            wa[j][m][2] = (int)pack_bf16x2(f2[0] * sc, f2[1] * sc);
-            wa[j][m][3] = (int)pack_bf16x2(f3[0] * sc, f3[1] * sc);
+            const _Float16 sh = (_Float16)__builtin_amdgcn_cvt_f32_fp8(scw, 0);   // E4M3 is exact in fp16
+            const f16x2_t s2 = {sh, sh};
+            wa[j][m][0] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw[j][m], 1.0f, 0) * s2);
+            wa[j][m][1] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw[j][m], 1.0f, 1) * s2);
+            wa[j][m][2] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw[j][m], 1.0f, 2) * s2);
+            wa[j][m][3] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw[j][m], 1.0f, 3) * s2);
           }
         }
 #pragma unroll
@@ -556,9 +563,9 @@ gemm_dec(const WorkList* __restrict__ wl, const int32_t* __restrict__ counts, co
           for (int j = 0; j < 4; ++j)
 #pragma unroll
             for (int m = 0; m < C::NMAT; ++m)
-              acc[m * NS + ms] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, wa[j][m]),
-                                                                        __builtin_bit_cast(bf16x8_t, xv[j]),
-                                                                        acc[m * NS + ms], 0, 0, 0);
+              acc[m * NS + ms] = __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(f16x8_t, wa[j][m]),
+                                                                       __builtin_bit_cast(f16x8_t, xv[j]),
+                                                                       acc[m * NS + ms], 0, 0, 0);
         }
       }
     } else {
@@ -627,13 +634,16 @@ gemm_dec(const WorkList* __restrict__ wl, const int32_t* __restrict__ counts, co
 
   // ---- the stream ----------------------------------------------------------
   const int n = (int)(u1 - u0);     // units of this workgroup
+  constexpr int NST = C::NST;
+  static_assert(NST * C::STAGE + 4 * (257 + 3 * 256 + ROWTAB) <= 160 * 1024, "LDS budget");
 #pragma unroll
   for (int s = 0; s < NST - 1; ++s)
     if (s < n) issue(s);
   int st = 0, i = i_first, kc = kc_first;
   for (int v = 0; v < n; ++v) {
     // this wave's loads of unit v have landed: what may still be outstanding
-    // is the NI loads of unit v+1, all issued after everything else
+    // is the NI loads each of units v+1 .. v+NST-2, all issued after
+    // everything else (loads complete in order)
     if (v + NST - 2 < n) wait_vmcnt<C::NI * (NST - 2)>();
     else wait_vmcnt<0>();
     barrier_keep_loads();                                   // everyone's have; the oldest stage is free
@@ -719,7 +729,7 @@ hipError_t launch_dec(int n_cu, const WorkList* wl, const int32_t* counts, const
                       bool fix, hipStream_t s) {
   using C = Cfg<FMT, GATED, NS>;
   static int per_cu = 0;     // resident workgroups per CU for this instance
-  const size_t lds = (size_t)NST * C::STAGE;
+  const size_t lds = (size_t)C::NST * C::STAGE;
   if (per_cu == 0) {
     hipError_t e = hipFuncSetAttribute((const void*)gemm_dec<FMT, GATED, NS>,
                                        hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);

@@ -45,8 +45,10 @@
  *     - nvfp4: codes as mxfp4, then an E4M3FN scale per 16 consecutive inputs
  *              of each row ([rows][cols/16], gate, up, down), then three fp32
  *              tensor scales (gate, up, down) and 4 bytes of padding; weight =
- *              E2M1 value * block scale * tensor scale.  Activations stay bf16
- *              (the large-batch path streams weights as the small one does).
+ *              E2M1 value * block scale * tensor scale.  The GEMM inputs
+ *              (hidden rows, A) are rounded to fp16 and meet the weights,
+ *              dequantised exactly to fp16, in the fp16 MFMA (the
+ *              large-batch path streams weights as the small one does).
  *   out         bf16 [T, H] (device)
  */
 #ifndef MOE_H
