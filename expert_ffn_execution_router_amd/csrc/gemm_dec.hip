@@ -13,7 +13,8 @@
 //
 // Work.  An item is (expert, m-block of 16*NS tokens, 64 weight rows per
 // matrix); its K range is cut into chunks of 256 bytes per weight row (128
-// bf16, 256 fp8 or 512 E2M1 values).  The flat sequence of (item, chunk)
+// bf16, 256 fp8 or 512 E2M1 values; NVFP4: 128 bytes, 256 values).  The flat
+// sequence of (item, chunk)
 // units is split into equal contiguous ranges, one per workgroup, so every
 // workgroup streams the same number of bytes whatever the expert sizes; the
 // ranges of consecutive workgroups of one XCD are contiguous.  An item cut by
@@ -24,7 +25,8 @@
 // would need an L2 write-back and invalidate per handoff, which costs more
 // than the launch).
 //
-// Memory.  Each chunk goes from HBM into a ring of three LDS stages by
+// Memory.  Each chunk goes from HBM into a ring of three LDS stages (two for
+// NVFP4 with up to 32 tokens per m-block, which fits more workgroups per CU) by
 // direct global->LDS loads (lane l's 16 bytes land at the instruction's LDS
 // base + 16*l) with the nontemporal hint: 16 consecutive lanes cover one
 // 256-byte row segment, the pattern that streams HBM at 7.0-7.3 TB/s on
@@ -34,7 +36,7 @@
 // piece so the swizzle comes out of the lane-linear placement.  The token
 // rows of the chunk, the scales of the 8-bit formats and the weight scales
 // go through the same ring, so one counter wait per chunk covers everything
-// the chunk needs: chunk c+2 is requested while chunk c is multiplied.
+// the chunk needs: chunk c+NST-1 is requested while chunk c is multiplied.
 //
 // MFMA.  Wave w owns weight rows 16w..16w+15 of the item (of each matrix);
 // weights are the A operand (16 rows) and tokens the B operand (16 tokens per
@@ -214,10 +216,11 @@ DEV void decode_global(const WorkList* wl, const int32_t* counts, const int32_t*
 }  // namespace
 
 // FMT: WFMT_*.  GATED: GEMM 1 (gate rows at woff0, up rows at woff1, SwiGLU
-// epilogue; out = A, bf16 for WFMT_BF16 else fp32 for the quantisation pass).
-// Otherwise GEMM 2 (weights at woff0; out = Z bf16).  Token rows of X are
-// gathered through row_tok (bf16 GEMM 1) or taken in grouped order; Xs holds
-// the activation scales of the 8-bit formats; soff0/soff1 the weight scales.
+// epilogue; out = A: bf16 for WFMT_BF16, fp16 for WFMT_NVFP4, else fp32 for
+// the quantisation pass).  Otherwise GEMM 2 (weights at woff0; out = Z
+// bf16).  Token rows of X are gathered through row_tok (16-bit GEMM 1: bf16,
+// or fp16 for NVFP4) or taken in grouped order; Xs holds the activation
+// scales of the 8-bit formats; soff0/soff1 the weight scales.
 // part: partial tiles [MAX_BLOCKS][2][NW][NACC][64] of the items cut by a
 // range boundary, finished by gemm_dec_fix.
 template <int FMT, bool GATED, int NS>
@@ -229,7 +232,7 @@ gemm_dec(const WorkList* __restrict__ wl, const int32_t* __restrict__ counts, co
   using C = Cfg<FMT, GATED, NS>;
   extern __shared__ __align__(16) uint8_t ring[];
   __shared__ int l_pref[257], l_slot[256], l_row0[256], l_cnt[256];
-  // token row of each grouped row this workgroup touches (bf16 GEMM 1)
+  // token row of each grouped row this workgroup touches (16-bit GEMM 1)
   constexpr int ROWTAB = (FMT == WFMT_BF16 && GATED) ? 2048 : ((C::NV && GATED) ? 1024 : 1);
   __shared__ int l_rows[ROWTAB];
   const int wave = uni(threadIdx.x >> 6), lane = threadIdx.x & 63;
