@@ -498,7 +498,8 @@ def phase_prefill(w: Workload):
     el_on, pprof = min(runs[True], key=lambda r: r[0])
     el_off = runs[False][0][0]
     flops = 6.0 * Tp * k * H * I * L
-    gemm_ms = pprof["gemm1"]["ms"] + pprof["gemm2"]["ms"]
+    # the overflow rows' small-batch GEMMs (and their sums) count as GEMM time
+    gemm_ms = pprof["gemm1"]["ms"] + pprof["gemm2"]["ms"] + pprof["tail"]["ms"]
     res = {
         "T": Tp, "layers": L, "chunk_s": el_on, "tokens_per_s": Tp / el_on,
         "h2d_GBps": L * E * S / el_on / 1e9,
@@ -758,8 +759,10 @@ def phase_formats(args):
             prof = rt.profile_end()
             torch.cuda.synchronize()
             assert rt.check_device_error() == 0
-            st = {n: v["ms"] / v["launches"] * 1e3 for n, v in prof.items() if isinstance(v, dict) and v["launches"]}
-            gemm_us = st["gemm1"] + st["gemm2"] + st.get("fixup", 0.0) * 2
+            # per layer (one forward each): the tiled GEMMs, the streaming
+            # kernels' sums and the overflow rows' GEMMs
+            st = {n: v["ms"] / L * 1e3 for n, v in prof.items() if isinstance(v, dict) and v["launches"]}
+            gemm_us = st["gemm1"] + st["gemm2"] + st.get("fixup", 0.0) + st.get("tail", 0.0)
             flops = 6.0 * pf_T * k * H * I
             res[key] = {
                 "bound": pf_bound, "gemm_us": gemm_us, "gpu_layer_us": sum(st.values()), "stage_us": st,

@@ -52,8 +52,9 @@ class moe_plan_info(ctypes.Structure):
         return {f: getattr(self, f) for f, _ in self._fields_}
 
 
-MOE_N_STAGES = 11
-STAGES = ["route", "topk", "group", "quant_x", "gemm1", "quant_a", "gemm2", "combine", "plan", "fixup", "fill"]
+MOE_N_STAGES = 12
+STAGES = ["route", "topk", "group", "quant_x", "gemm1", "quant_a", "gemm2", "combine", "plan", "fixup", "fill",
+          "tail"]
 
 
 class moe_profile(ctypes.Structure):

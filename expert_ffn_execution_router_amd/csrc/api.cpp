@@ -25,7 +25,8 @@ hipError_t moe_launch_router(const uint16_t* x, const float* R, const float* bia
 hipError_t moe_launch_topk(const float* z, int T, int E, int k, int32_t* ids, float* w, hipStream_t s);
 hipError_t moe_launch_group(const int32_t* ids, int T, int k, int E, const uint32_t* miss_mask,
                             const int32_t* slot_row, int mb, int32_t* counts, int32_t* offsets, int32_t* pos,
-                            int32_t* perm_tok, int32_t* hist, WorkList* wl, int* err, hipStream_t s);
+                            int32_t* perm_tok, int32_t* hist, WorkList* wl, int* err, const TailSplit* tail,
+                            hipStream_t s);
 hipError_t moe_launch_gemm_dec(int fmt, int gated, int ns, int n_cu, const WorkList* wl, const int32_t* counts,
                                const int32_t* offsets, const uint8_t* pool, size_t S, size_t woff0, size_t woff1,
                                size_t soff0, size_t soff1, const void* X, const void* Xs, const int32_t* row_tok,
@@ -101,7 +102,8 @@ BlobLayout blob_layout(const moe_config& c) {
 
 // Workspace carving (all offsets 256-byte aligned).
 struct WsLayout {
-  size_t slot_table, owner, last_use, ctl, err, logits, ids, w, pos, perm_tok, counts, offsets, hist, wl, mask, plan, A,
+  size_t slot_table, owner, last_use, ctl, err, logits, ids, w, pos, perm_tok, counts, offsets, hist, wl, wl_tail,
+      tail_rows, mask, plan, A,
       Aq, As, Z, Xq, Xs, hp, part, total;
 };
 
@@ -130,6 +132,9 @@ WsLayout ws_layout(const moe_config& c) {
   L.offsets = take((size_t)(c.E + 1) * 4);
   L.hist = take(((Tm + 255) / 256) * c.E * 4);
   L.wl = take(sizeof(WorkList));
+  // large batches: the overflow rows' work list and per-expert row splits
+  L.wl_tail = take(sizeof(WorkList));
+  L.tail_rows = take((size_t)3 * c.E * 4);
   L.mask = take(64);
   L.plan = take(sizeof(PlanOut));
   const bool q8 = c.wfmt == MOE_W_FP8_E4M3_B128 || c.wfmt == MOE_W_MXFP4;   // quantised activations
@@ -183,6 +188,8 @@ struct moe_ctx {
   int32_t* offsets;
   int32_t* hist;
   WorkList* wl;
+  WorkList* wl_tail;
+  int32_t* tail_rows;       // [3][E]: main rows, overflow rows, first overflow row
   uint32_t* mask;
   PlanOut* plan_dev;
   void* A;
@@ -310,33 +317,67 @@ int forward_experts(moe_ctx* c, const void* hidden, int T, const int32_t* slot_r
   // weight streaming: m-blocks of 16 * ns tokens (each m-block reads the
   // expert's weights once; larger blocks cost LDS and idle MFMA rows)
   const int ns = std::min(T <= 16 ? 1 : (T <= 64 ? 2 : 4), moe_dec_max_ns(g.wfmt));
+  // MXFP4 weights with MXFP6 activations when selected (large batches)
+  const int qf = g.wfmt == MOE_W_MXFP4 && c->act == MOE_ACT_MXFP6 ? WFMT_MXFP4_A6 : g.wfmt;
+  // Large batches: an expert whose last m-tile would hold at most one
+  // small-batch m-block of rows keeps one tile fewer and its overflow rows
+  // run through the small-batch kernel, so a few such tiles do not add a
+  // round of items to the persistent grid (not for MXFP6 rows, which only
+  // the tiled kernel reads).
+  const bool split = tiled && qf != WFMT_MXFP4_A6;
+  const int ns_tail = std::min(4, moe_dec_max_ns(g.wfmt));
+  int32_t* mcounts = c->tail_rows;
+  int32_t* tcounts = c->tail_rows + g.E;
+  int32_t* toffsets = c->tail_rows + 2 * g.E;
+  // items per m-tile of GEMM 1: the tiled kernels' 256 weight rows are 128 gate and 128 up rows
+  const int ntiles1 = g.I / 128;
+  const TailSplit tail{c->wl_tail, mcounts, tcounts, toffsets, 16 * ns_tail, 16 * ns_tail, c->n_cu, ntiles1};
   STAGE(c, MOE_STAGE_GROUP, s,
         moe_launch_group(c->ids, T, g.k, g.E, mask, slot_row, tiled ? tile_mb : 16 * ns, c->counts,
-                         c->offsets, c->pos, c->perm_tok, c->hist, c->wl, c->err, s));
+                         c->offsets, c->pos, c->perm_tok, c->hist, c->wl, c->err, split ? &tail : nullptr, s));
   const int ncu = c->n_cu;
   const BlobLayout& b = c->bl;
+  const int32_t* tile_counts = split ? mcounts : c->counts;
+  // the overflow rows of GEMM 1 (gated) or GEMM 2 through the small-batch
+  // kernel and its sums, after the tiled launch on the same stream (running
+  // them beside the tiled kernels on a second stream was slower: they take
+  // CUs from the persistent grid's next launch)
+  auto tail_gemm = [&](int gated, const void* X, const void* Xs, const int32_t* row_tok, void* out) -> int {
+    if (!split) return MOE_OK;
+    for (int fix = 0; fix < 2; ++fix)
+      STAGE(c, MOE_STAGE_TAIL, s,
+            moe_launch_gemm_dec(g.wfmt, gated, ns_tail, ncu, c->wl_tail, tcounts, toffsets, c->slot_pool, b.S,
+                                gated ? b.w[0] : b.w[2], gated ? b.w[1] : 0, gated ? b.s[0] : b.s[2],
+                                gated ? b.s[1] : 0, X, Xs, row_tok, gated ? g.H : g.I, gated ? g.I : g.H, out,
+                                c->part, fix, s));
+    return MOE_OK;
+  };
   if (tiled && g.wfmt != MOE_W_BF16) {
     const int trash = g.max_tokens * g.k;       // the spare row of A and Z
-    // MXFP4 weights with MXFP6 activations when selected
-    const int qf = g.wfmt == MOE_W_MXFP4 && c->act == MOE_ACT_MXFP6 ? WFMT_MXFP4_A6 : g.wfmt;
     // activations quantised straight into grouped order (row p <- token perm_tok[p])
     STAGE(c, MOE_STAGE_QUANT_X, s,
           moe_launch_quant(qf, 1, hidden, T * g.k, c->offsets + g.E, c->perm_tok, g.H, c->Xq, c->Xs, trash, s));
     STAGE(c, MOE_STAGE_GEMM1, s,
-          moe_launch_gemm_pf8(qf, 1, small8, c->n_cu, c->wl, c->counts, c->offsets, c->slot_pool, b.S, b.w[0],
+          moe_launch_gemm_pf8(qf, 1, small8, c->n_cu, c->wl, tile_counts, c->offsets, c->slot_pool, b.S, b.w[0],
                               b.w[1], b.s[0], b.s[1], c->Xq, c->Xs, trash, g.H, g.I, c->A, trash, s));
+    int rc = tail_gemm(1, c->Xq, c->Xs, nullptr, c->A);
+    if (rc) return rc;
     STAGE(c, MOE_STAGE_QUANT_A, s,
           moe_launch_quant(qf, 0, c->A, T * g.k, c->offsets + g.E, nullptr, g.I, c->Aq, c->As, trash, s));
     STAGE(c, MOE_STAGE_GEMM2, s,
-          moe_launch_gemm_pf8(qf, 0, small8, c->n_cu, c->wl, c->counts, c->offsets, c->slot_pool, b.S, b.w[2], 0,
+          moe_launch_gemm_pf8(qf, 0, small8, c->n_cu, c->wl, tile_counts, c->offsets, c->slot_pool, b.S, b.w[2], 0,
                               b.s[2], 0, c->Aq, c->As, trash, g.I, g.H, c->Z, trash, s));
+    if ((rc = tail_gemm(0, c->Aq, c->As, nullptr, c->Z))) return rc;
   } else if (tiled) {
     STAGE(c, MOE_STAGE_GEMM1, s,
-          moe_launch_gemm_pf(g.wfmt, 1, c->n_cu, c->wl, c->counts, c->offsets, c->slot_pool, b.S, b.w[0], b.w[1],
-                             hidden, c->perm_tok, g.H, g.I, c->A, s));
+          moe_launch_gemm_pf(g.wfmt, 1, c->n_cu, c->wl, tile_counts, c->offsets, c->slot_pool, b.S, b.w[0],
+                             b.w[1], hidden, c->perm_tok, g.H, g.I, c->A, s));
+    int rc = tail_gemm(1, hidden, nullptr, c->perm_tok, c->A);
+    if (rc) return rc;
     STAGE(c, MOE_STAGE_GEMM2, s,
-          moe_launch_gemm_pf(g.wfmt, 0, c->n_cu, c->wl, c->counts, c->offsets, c->slot_pool, b.S, b.w[2], 0, c->A,
+          moe_launch_gemm_pf(g.wfmt, 0, c->n_cu, c->wl, tile_counts, c->offsets, c->slot_pool, b.S, b.w[2], 0, c->A,
                              nullptr, g.I, g.H, c->Z, s));
+    if ((rc = tail_gemm(0, c->A, nullptr, nullptr, c->Z))) return rc;
   } else if (g.wfmt == MOE_W_BF16 || g.wfmt == MOE_W_NVFP4) {
     // 16-bit tokens gathered through perm_tok for GEMM 1 (bf16, or the
     // hidden rows converted to fp16 for NVFP4's fp16 MFMA), A in the same
@@ -531,6 +572,8 @@ int moe_create(const moe_config* cfg, void* host_pool, size_t host_bytes, void* 
   c->offsets = (int32_t*)(w + L.offsets);
   c->hist = (int32_t*)(w + L.hist);
   c->wl = (WorkList*)(w + L.wl);
+  c->wl_tail = (WorkList*)(w + L.wl_tail);
+  c->tail_rows = (int32_t*)(w + L.tail_rows);
   c->mask = (uint32_t*)(w + L.mask);
   c->plan_dev = (PlanOut*)(w + L.plan);
   c->A = w + L.A;
@@ -687,7 +730,7 @@ int moe_route_from_logits(moe_ctx* c, const float* logits, int T, int32_t* topk_
   const moe_config& g = c->cfg;
   HIPCHK(c, moe_launch_topk(logits, T, g.E, g.k, topk_ids, topk_w, s));
   HIPCHK(c, moe_launch_group(topk_ids, T, g.k, g.E, nullptr, nullptr, DEC_MB, counts, offsets, pos, perm_tok,
-                             c->hist, c->wl, c->err, s));
+                             c->hist, c->wl, c->err, nullptr, s));
   return MOE_OK;
 }
 

@@ -51,6 +51,23 @@ struct WorkList {
   int mblk_prefix[257];
 };
 
+// Optional split of the large-batch work: an expert whose last m-tile would
+// hold at most tau rows keeps one tile fewer, its main rows (mcounts) going
+// to the tiled kernels through the main work list and the overflow rows
+// (tcounts rows from toffsets) to the small-batch kernel through wl, built
+// with m-blocks of mb rows.  The split is taken only when it removes a round
+// of the persistent tiled grid (n_cu workgroups, ntiles items per m-tile)
+// and its overflow items are few (at most n_cu / 4): re-streaming many
+// experts' weights for their overflow rows costs more than the round.
+// wl == nullptr: no split.
+struct TailSplit {
+  WorkList* wl;
+  int32_t* mcounts;
+  int32_t* tcounts;
+  int32_t* toffsets;
+  int mb, tau, n_cu, ntiles;
+};
+
 // Result of the per-layer cache-control kernel, copied to the host.
 struct PlanOut {
   int n_unique, n_hit, m, q, n_host, n_evict, eligible, tick;

@@ -252,7 +252,7 @@ __device__ int block_exclusive_scan256(int v, int* tmp /* >= 4 ints of LDS */, i
 // raises the device error flag and is skipped.
 __device__ void finish_grouping(int cnt, int E, const uint32_t* miss_mask, const int32_t* slot_row,
                                 int32_t* counts, int32_t* offsets, WorkList* wl, int mb, int* err,
-                                int* tmp) {
+                                int* tmp, const TailSplit& ts) {
   const int e = threadIdx.x;
   const int c = e < E ? cnt : 0;
   int total;
@@ -271,12 +271,40 @@ __device__ void finish_grouping(int cnt, int E, const uint32_t* miss_mask, const
   }
   int nact;
   const int a = block_exclusive_scan256(act ? 1 : 0, tmp, &nact);
-  const int nb = act ? (c + mb - 1) / mb : 0;
+  int nb = act ? (c + mb - 1) / mb : 0;
+  // overflow rows of a last tile of at most tau rows go to the tail list
+  // when that removes a round of the tiled grid and the tail items are few
+  int tl = 0;
+  if (ts.wl) {
+    const bool cand = nb >= 2 && c - (nb - 1) * mb <= ts.tau;
+    int n0, ncand;
+    (void)block_exclusive_scan256(nb, tmp, &n0);
+    (void)block_exclusive_scan256(cand ? 1 : 0, tmp, &ncand);
+    const long it0 = (long)n0 * ts.ntiles, it1 = (long)(n0 - ncand) * ts.ntiles;
+    const bool split = ncand > 0 && (it1 + ts.n_cu - 1) / ts.n_cu < (it0 + ts.n_cu - 1) / ts.n_cu &&
+                       (long)ncand * ts.ntiles * 4 <= ts.n_cu;
+    if (split && cand) {
+      --nb;
+      tl = c - nb * mb;
+    }
+  }
   int nmblk;
   const int pb = block_exclusive_scan256(nb, tmp, &nmblk);
   if (act) { wl->act_e[a] = e; wl->act_slot[a] = slot; wl->mblk_prefix[a] = pb; }
   if (e == 0) {
     wl->n_act = nact; wl->n_mblk = nmblk; wl->mb = mb; wl->mblk_prefix[nact] = nmblk;
+  }
+  if (ts.wl) {
+    if (e < E) { ts.mcounts[e] = c - tl; ts.tcounts[e] = tl; ts.toffsets[e] = off + c - tl; }
+    int ntact;
+    const int ta = block_exclusive_scan256(tl > 0 ? 1 : 0, tmp, &ntact);
+    const int tnb = tl > 0 ? (tl + ts.mb - 1) / ts.mb : 0;
+    int tnm;
+    const int tpb = block_exclusive_scan256(tnb, tmp, &tnm);
+    if (tl > 0) { ts.wl->act_e[ta] = e; ts.wl->act_slot[ta] = slot; ts.wl->mblk_prefix[ta] = tpb; }
+    if (e == 0) {
+      ts.wl->n_act = ntact; ts.wl->n_mblk = tnm; ts.wl->mb = ts.mb; ts.wl->mblk_prefix[ntact] = tnm;
+    }
   }
 }
 
@@ -316,7 +344,8 @@ __device__ void mark_block(const int32_t* __restrict__ ids, int t0, int T, int k
 __global__ void __launch_bounds__(256)
 group_single_kernel(const int32_t* __restrict__ ids, int T, int k, int E, const uint32_t* miss_mask,
                     const int32_t* slot_row, int mb, int32_t* counts, int32_t* offsets,
-                    int32_t* __restrict__ pos, int32_t* __restrict__ perm_tok, WorkList* wl, int* err) {
+                    int32_t* __restrict__ pos, int32_t* __restrict__ perm_tok, WorkList* wl, int* err,
+                    TailSplit ts) {
   __shared__ uint32_t bits[256 * 8];
   __shared__ int base[256];
   __shared__ int tmp[4];
@@ -324,7 +353,7 @@ group_single_kernel(const int32_t* __restrict__ ids, int T, int k, int E, const 
   int cnt = 0;
   if ((int)threadIdx.x < E)
     for (int q = 0; q < 8; ++q) cnt += __popc(bits[threadIdx.x * 8 + q]);
-  finish_grouping(cnt, E, miss_mask, slot_row, counts, offsets, wl, mb, err, tmp);
+  finish_grouping(cnt, E, miss_mask, slot_row, counts, offsets, wl, mb, err, tmp, ts);
   if ((int)threadIdx.x < E) base[threadIdx.x] = offsets[threadIdx.x];
   __syncthreads();
   scatter_block(ids, 0, T, k, E, base, bits, pos, perm_tok);
@@ -347,13 +376,14 @@ group_count_kernel(const int32_t* __restrict__ ids, int T, int k, int E, int32_t
 // block's base row for expert e.
 __global__ void __launch_bounds__(256)
 group_scan_kernel(int nblk, int E, const uint32_t* miss_mask, const int32_t* slot_row, int mb,
-                  int32_t* __restrict__ hist, int32_t* counts, int32_t* offsets, WorkList* wl, int* err) {
+                  int32_t* __restrict__ hist, int32_t* counts, int32_t* offsets, WorkList* wl, int* err,
+                  TailSplit ts) {
   __shared__ int tmp[4];
   const int e = threadIdx.x;
   int cnt = 0;
   if (e < E)
     for (int b = 0; b < nblk; ++b) cnt += hist[(size_t)b * E + e];
-  finish_grouping(cnt, E, miss_mask, slot_row, counts, offsets, wl, mb, err, tmp);
+  finish_grouping(cnt, E, miss_mask, slot_row, counts, offsets, wl, mb, err, tmp, ts);
   if (e < E) {
     int run = offsets[e];
     for (int b = 0; b < nblk; ++b) {
@@ -393,17 +423,19 @@ extern "C" hipError_t moe_launch_topk(const float* z, int T, int E, int k, int32
   return hipGetLastError();
 }
 
+// tail: optional split of the large-batch work (TailSplit); nullptr: none.
 extern "C" hipError_t moe_launch_group(const int32_t* ids, int T, int k, int E, const uint32_t* miss_mask,
                                        const int32_t* slot_row, int mb, int32_t* counts, int32_t* offsets,
                                        int32_t* pos, int32_t* perm_tok, int32_t* hist, WorkList* wl, int* err,
-                                       hipStream_t s) {
+                                       const TailSplit* tail, hipStream_t s) {
+  const TailSplit ts = tail ? *tail : TailSplit{nullptr, nullptr, nullptr, nullptr, 1, 0};
   if (T <= GROUP_TOK) {
     group_single_kernel<<<1, 256, 0, s>>>(ids, T, k, E, miss_mask, slot_row, mb, counts, offsets, pos, perm_tok,
-                                          wl, err);
+                                          wl, err, ts);
   } else {
     const int nblk = (T + GROUP_TOK - 1) / GROUP_TOK;
     group_count_kernel<<<nblk, 256, 0, s>>>(ids, T, k, E, hist);
-    group_scan_kernel<<<1, 256, 0, s>>>(nblk, E, miss_mask, slot_row, mb, hist, counts, offsets, wl, err);
+    group_scan_kernel<<<1, 256, 0, s>>>(nblk, E, miss_mask, slot_row, mb, hist, counts, offsets, wl, err, ts);
     group_scatter_kernel<<<nblk, 256, 0, s>>>(ids, T, k, E, hist, pos, perm_tok);
   }
   return hipGetLastError();

@@ -344,7 +344,8 @@ enum {
   MOE_STAGE_PLAN = 8,     /* cache-control kernel */
   MOE_STAGE_FIXUP = 9,    /* small-batch GEMMs: sums of the items cut between workgroups */
   MOE_STAGE_FILL = 10,    /* indexed host-pool -> slot copy of the fill set (asynchronous decode) */
-  MOE_N_STAGES = 11
+  MOE_STAGE_TAIL = 11,    /* large batches: the overflow rows' small-batch GEMMs and their sums */
+  MOE_N_STAGES = 12
 };
 
 typedef struct {

@@ -208,3 +208,54 @@ def test_tiled_forward_tile_edges(fmt, cap, act):
         print(f"tile edges: err vs mirrored {e_m:.2e}, vs exact {e_x:.2e}")
     finally:
         s.close()
+
+
+@pytest.mark.parametrize("fmt,cap", [(0, 288), (1, 256), (2, 288)])
+def test_tiled_forward_overflow_rows(fmt, cap):
+    """Routing that makes the large-batch kernels send overflow rows to the
+    small-batch kernel: every one of E=256 experts fills one m-tile of cap
+    rows and 8 of them hold 5 rows more, so their second tiles would add a
+    round of items to a grid of one workgroup per CU (264 m-tiles of one item
+    each against 256 CUs); the 8 x 5 overflow rows run through the
+    small-batch kernel instead.  Checked against the oracle row by row (the
+    round the split removes exists only on a device of 256 CUs, which the
+    construction assumes)."""
+    n_cu = torch.cuda.get_device_properties(0).multi_processor_count
+    if n_cu != 256:
+        pytest.skip(f"construction assumes 256 CUs, device has {n_cu}")
+    print(f"overflow rows fmt={fmt} cap={cap}", flush=True)
+    cfg = shape(1, fmt=fmt, E=256, k=2, H=256, I=128)
+    E, k, H = cfg.E, cfg.k, cfg.H
+    counts = np.full(E, cap)
+    over = np.arange(0, E, E // 8)[:8]
+    counts[over] += 5
+    slots = np.repeat(np.arange(E), counts)
+    T = len(slots) // k
+    assert T * k == len(slots) and T * k > 160 * E          # the full-size tiles of the 8-bit kernels
+    first, second = slots[:T], slots[T:]
+    assert np.all(first != second)
+    rng = np.random.default_rng(9)
+    x32 = rng.normal(0.0, 0.05, size=(T, H)).astype(np.float32)
+    x32[np.arange(T), first] = 4.0
+    x32[np.arange(T), second] = 3.0
+    bits = _bf16_bits(x32)
+    R = np.zeros((E, H), np.float32)
+    R[np.arange(E), np.arange(E)] = 1.0
+    s = Setup(cfg, seed=6, max_tokens=T)
+    try:
+        s.admit_all(0)
+        s.R[0], s.b[0] = R, None
+        xd = torch.from_numpy(bits.view(np.int16)).cuda()
+        out = torch.empty(T, H, dtype=torch.bfloat16, device="cuda")
+        s.rt.forward(0, xd, torch.from_numpy(R).cuda(), None, s.slot_row(0), out)
+        torch.cuda.synchronize()
+        assert s.rt.check_device_error() == 0
+        ids = torch.empty(T, k, dtype=torch.int32, device="cuda")
+        w = torch.empty(T, k, dtype=torch.float32, device="cuda")
+        s.rt.route(xd, torch.from_numpy(R).cuda(), None, ids, w)
+        assert np.array_equal(np.bincount(ids.cpu().numpy().ravel(), minlength=E), counts)
+        e_m, e_x, n = compare(s, 0, bits, out)
+        assert n == T
+        print(f"overflow rows: err vs mirrored {e_m:.2e}, vs exact {e_x:.2e}")
+    finally:
+        s.close()
