@@ -36,6 +36,15 @@ import time
 import numpy as np
 
 
+def profile_end(rt):
+    """Stage timings of a profiled region; every launch must have been timed
+    (a region that outgrew its event capacity would undercount)."""
+    prof = rt.profile_end()
+    if prof["dropped"]:
+        raise RuntimeError("profiling dropped launches: raise the event capacity of profile_begin")
+    return prof
+
+
 def log(*a):
     print(*a, file=sys.stderr, flush=True)
 
@@ -184,7 +193,7 @@ def phase_decode(w: Workload):
     rt.profile_begin(K * L * 8 + 16)
     for s in range(K):
         step(W + s)
-    prof_all = rt.profile_end()
+    prof_all = profile_end(rt)
     # eager timed pass: GEMM 1 bracketed by HIP events on its stream (the
     # roofline's kernel duration); events inside a captured graph cannot be timed
     rt.profile_begin(K * L + 16, stages=["gemm1"])
@@ -194,7 +203,7 @@ def phase_decode(w: Workload):
         step(W + s)
     torch.cuda.synchronize()
     elapsed_eager = time.perf_counter() - t0
-    prof = rt.profile_end()
+    prof = profile_end(rt)
     # graph timed pass (the value): one HIP graph per step (48 layers of
     # launches), as the pages replay a captured decode step
     use_graph = not args.eager
@@ -307,7 +316,7 @@ def phase_e2e(w: Workload):
     rc.profile_begin(K * L * 12 + 16)
     for s in range(K):
         e2e_step(W + s, False)
-    prof = rc.profile_end()
+    prof = profile_end(rc)
     torch.cuda.synchronize()
     stage_us = {n: v["ms"] / v["launches"] * 1e3 for n, v in prof.items() if isinstance(v, dict) and v["launches"]}
     del infos[n_rec:]
@@ -371,7 +380,7 @@ def e2e_async(w: Workload, rc, hid, outs):
     for s in range(K):
         for l in range(L):
             rc.decode_layer_async(l, hid[W + s, l], w.R[l], w.bias[l], outs[l], host_stream=hs)
-    prof = rc.profile_end()
+    prof = profile_end(rc)
     out["eager"]["stage_us_per_launch"] = {n: v["ms"] / v["launches"] * 1e3 for n, v in prof.items()
                                            if isinstance(v, dict) and v["launches"]}
     fl = prof.get("fill", {"launches": 0})
@@ -487,14 +496,14 @@ def phase_prefill(w: Workload):
     for dbuf in [True] * max(1, args.prefill_runs - 1) + [False, True]:
         rp.reset_cache()
         torch.cuda.synchronize()
-        rp.profile_begin(L * 8 + 16)
+        rp.profile_begin(L * 16 + 16)
         t0 = time.perf_counter()
         with torch.cuda.stream(comp):
             for l in range(L):
                 rp.prefill_layer(l, hp, w.R[l], None, out_p, stream=comp, copy_stream=copy, double_buffer=dbuf)
         torch.cuda.synchronize()
         el = time.perf_counter() - t0
-        runs.setdefault(dbuf, []).append((el, rp.profile_end()))
+        runs.setdefault(dbuf, []).append((el, profile_end(rp)))
     el_on, pprof = min(runs[True], key=lambda r: r[0])
     el_off = runs[False][0][0]
     flops = 6.0 * Tp * k * H * I * L
@@ -723,7 +732,7 @@ def phase_formats(args):
             for s in range(K):
                 for l in range(L):
                     rt.forward(l, hid[W + s, l], R[l], bias[l], rows[l], o)
-            prof = rt.profile_end()
+            prof = profile_end(rt)
             torch.cuda.synchronize()
             t0 = time.perf_counter()
             for s in range(K):
@@ -753,10 +762,10 @@ def phase_formats(args):
         def prefill_pass(key, kernel, peak):
             rt.forward(0, hp, R[0], bias[0], rows[0], op)
             torch.cuda.synchronize()
-            rt.profile_begin(L * 12 + 16)
+            rt.profile_begin(L * 16 + 16)
             for l in range(L):
                 rt.forward(l, hp, R[l], bias[l], rows[l], op)
-            prof = rt.profile_end()
+            prof = profile_end(rt)
             torch.cuda.synchronize()
             assert rt.check_device_error() == 0
             # per layer (one forward each): the tiled GEMMs, the streaming
