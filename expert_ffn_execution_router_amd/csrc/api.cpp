@@ -339,17 +339,19 @@ int forward_experts(moe_ctx* c, const void* hidden, int T, const int32_t* slot_r
   const BlobLayout& b = c->bl;
   const int32_t* tile_counts = split ? mcounts : c->counts;
   // the overflow rows of GEMM 1 (gated) or GEMM 2 through the small-batch
-  // kernel and its sums, after the tiled launch on the same stream (running
-  // them beside the tiled kernels on a second stream was slower: they take
-  // CUs from the persistent grid's next launch)
+  // kernel, one workgroup per item (an overflow is at most one m-block, so
+  // there are at most E times the weight tiles items), after the tiled
+  // launch on the same stream (running them beside the tiled kernels on a
+  // second stream was slower: they take CUs from the persistent grid's next
+  // launch)
   auto tail_gemm = [&](int gated, const void* X, const void* Xs, const int32_t* row_tok, void* out) -> int {
     if (!split) return MOE_OK;
-    for (int fix = 0; fix < 2; ++fix)
-      STAGE(c, MOE_STAGE_TAIL, s,
-            moe_launch_gemm_dec(g.wfmt, gated, ns_tail, ncu, c->wl_tail, tcounts, toffsets, c->slot_pool, b.S,
-                                gated ? b.w[0] : b.w[2], gated ? b.w[1] : 0, gated ? b.s[0] : b.s[2],
-                                gated ? b.s[1] : 0, X, Xs, row_tok, gated ? g.H : g.I, gated ? g.I : g.H, out,
-                                c->part, fix, s));
+    const int N = gated ? g.I : g.H;
+    STAGE(c, MOE_STAGE_TAIL, s,
+          moe_launch_gemm_dec(g.wfmt, gated, ns_tail, ncu, c->wl_tail, tcounts, toffsets, c->slot_pool, b.S,
+                              gated ? b.w[0] : b.w[2], gated ? b.w[1] : 0, gated ? b.s[0] : b.s[2],
+                              gated ? b.s[1] : 0, X, Xs, row_tok, gated ? g.H : g.I, N, out, nullptr,
+                              -(g.E * (N / 64)), s));
     return MOE_OK;
   };
   if (tiled && g.wfmt != MOE_W_BF16) {

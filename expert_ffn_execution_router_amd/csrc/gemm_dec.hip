@@ -254,7 +254,10 @@ gemm_dec(const WorkList* __restrict__ wl, const int32_t* __restrict__ counts, co
   const int KC = (K + C::CK - 1) / C::CK;
   const long U = (long)wl->n_mblk * ntiles * KC;     // < 2^31 for any admissible shape (checked by the host)
   if (U == 0) return;
-  const long G = U < (long)gridDim.x ? U : (long)gridDim.x;
+  // part == nullptr: one workgroup per item (the grid covers every item),
+  // so no item is cut and nothing needs summing afterwards
+  if (!part && U / KC > (long)gridDim.x) return;
+  const long G = !part ? U / KC : (U < (long)gridDim.x ? U : (long)gridDim.x);
   long b = blockIdx.x;
   if (G == gridDim.x && (gridDim.x % N_XCD) == 0)       // XCD x takes ranges x*G/8 .. (x+1)*G/8 - 1
     b = (long)(blockIdx.x % N_XCD) * (gridDim.x / N_XCD) + blockIdx.x / N_XCD;
@@ -729,7 +732,7 @@ template <int FMT, bool GATED, int NS>
 hipError_t launch_dec(int n_cu, const WorkList* wl, const int32_t* counts, const int32_t* offsets,
                       const uint8_t* pool, size_t S, size_t woff0, size_t woff1, size_t soff0, size_t soff1,
                       const void* X, const void* Xs, const int32_t* row_tok, int K, int N, void* out, f32x4_t* part,
-                      bool fix, hipStream_t s) {
+                      int fix, hipStream_t s) {
   using C = Cfg<FMT, GATED, NS>;
   static int per_cu = 0;     // resident workgroups per CU for this instance
   const size_t lds = (size_t)C::NST * C::STAGE;
@@ -744,7 +747,11 @@ hipError_t launch_dec(int n_cu, const WorkList* wl, const int32_t* counts, const
   }
   int grid = n_cu * per_cu;
   if (grid > MAX_BLOCKS) grid = MAX_BLOCKS - MAX_BLOCKS % N_XCD;
-  if (fix)
+  if (fix < 0)      // one workgroup per item: a grid of -fix workgroups, no partial tiles
+    gemm_dec<FMT, GATED, NS><<<-fix, 256, lds, s>>>(wl, counts, offsets, pool, S, woff0, woff1, soff0, soff1,
+                                                    (const uint8_t*)X, (const uint8_t*)Xs, row_tok, K, N, out,
+                                                    nullptr);
+  else if (fix)
     gemm_dec_fix<FMT, GATED, NS><<<grid, 256, 0, s>>>(wl, counts, offsets, pool, S, K, N, grid, out, part);
   else
     gemm_dec<FMT, GATED, NS><<<grid, 256, lds, s>>>(wl, counts, offsets, pool, S, woff0, woff1, soff0, soff1,
@@ -756,7 +763,7 @@ template <int FMT, bool GATED>
 hipError_t launch_ns(int ns, int n_cu, const WorkList* wl, const int32_t* counts, const int32_t* offsets,
                      const uint8_t* pool, size_t S, size_t woff0, size_t woff1, size_t soff0, size_t soff1,
                      const void* X, const void* Xs, const int32_t* row_tok, int K, int N, void* out, f32x4_t* part,
-                     bool fix, hipStream_t s) {
+                     int fix, hipStream_t s) {
 #define MOE_DEC_ARGS n_cu, wl, counts, offsets, pool, S, woff0, woff1, soff0, soff1, X, Xs, row_tok, K, N, out, part, fix, s
   if (ns == 1) return launch_dec<FMT, GATED, 1>(MOE_DEC_ARGS);
   if (ns == 2) return launch_dec<FMT, GATED, 2>(MOE_DEC_ARGS);
@@ -779,7 +786,9 @@ extern "C" int moe_dec_max_ns(int fmt) { return fmt == WFMT_MXFP4 ? 2 : 4; }
 // multiple of 64; K a multiple of 128.  For the 8-bit formats X holds the
 // quantised rows in grouped order (row_tok must be null).  The stream leaves
 // the items cut between workgroups as partial tiles in `part`; the same call
-// with fix != 0 (same arguments, next on the stream) adds and stores them.
+// with fix = 1 (same arguments, next on the stream) adds and stores them.
+// fix = -n: one workgroup per item on a grid of n workgroups (n at least the
+// number of items), no partial tiles and no second call.
 extern "C" hipError_t moe_launch_gemm_dec(int fmt, int gated, int ns, int n_cu, const WorkList* wl,
                                           const int32_t* counts, const int32_t* offsets, const uint8_t* pool,
                                           size_t S, size_t woff0, size_t woff1, size_t soff0, size_t soff1,
@@ -787,7 +796,7 @@ extern "C" hipError_t moe_launch_gemm_dec(int fmt, int gated, int ns, int n_cu, 
                                           void* out, void* part, int fix, hipStream_t s) {
   if (N % ROWS || K % 128 || (fmt != WFMT_BF16 && fmt != WFMT_NVFP4 && row_tok)) return hipErrorInvalidValue;
   f32x4_t* p = (f32x4_t*)part;
-  const bool f = fix != 0;
+  const int f = fix;
 #define MOE_DEC_ARGS ns, n_cu, wl, counts, offsets, pool, S, woff0, woff1, soff0, soff1, X, Xs, row_tok, K, N, out, p, f, s
   if (fmt == WFMT_BF16) return gated ? launch_ns<WFMT_BF16, true>(MOE_DEC_ARGS) : launch_ns<WFMT_BF16, false>(MOE_DEC_ARGS);
   if (fmt == WFMT_FP8) return gated ? launch_ns<WFMT_FP8, true>(MOE_DEC_ARGS) : launch_ns<WFMT_FP8, false>(MOE_DEC_ARGS);
