@@ -100,8 +100,22 @@ def encode_e4m3(v: np.ndarray) -> np.ndarray:
     return (code | (sign.astype(np.int64) << 7)).astype(np.uint8)
 
 
+def lookup(table: np.ndarray, codes: np.ndarray) -> np.ndarray:
+    """table[codes] along the first axis (codes: uint8 array of any shape).
+    Large arrays go through torch's CPU index_select, which runs the same
+    gather on every core (numpy's fancy indexing is single-threaded and the
+    weight blobs hold tens of millions of codes)."""
+    c = np.asarray(codes, dtype=np.uint8)
+    if c.size < (1 << 16):
+        return table[c]
+    import torch
+    t = torch.from_numpy(np.ascontiguousarray(table))
+    out = torch.index_select(t, 0, torch.from_numpy(c.reshape(-1)).long()).numpy()
+    return out.reshape(c.shape + table.shape[1:])
+
+
 def decode_e4m3(codes: np.ndarray) -> np.ndarray:
-    return E4M3_TABLE[np.asarray(codes, dtype=np.uint8)]
+    return lookup(E4M3_TABLE, codes)
 
 
 def decode_e2m1(nibbles: np.ndarray) -> np.ndarray:

@@ -40,9 +40,12 @@ from __future__ import annotations
 import numpy as np
 
 from .formats import (bf16_to_f64, decode_e2m1, decode_e2m3, decode_e4m3, e8m0_to_f64, encode_e2m3,
-                      encode_e4m3, round_to_bf16, round_to_f16)
+                      encode_e4m3, lookup, round_to_bf16, round_to_f16)
 
 FMT_BF16, FMT_FP8, FMT_MXFP4, FMT_NVFP4 = 0, 1, 2, 3
+
+# the two E2M1 values packed in each byte value: [low nibble, high nibble]
+E2M1_PAIRS = np.stack([decode_e2m1(np.arange(256) & 0xF), decode_e2m1(np.arange(256) >> 4)], axis=1)
 
 
 # ----------------------------------------------------------------------------
@@ -140,9 +143,10 @@ def dequant_expert(blob: np.ndarray, fmt: int, H: int, I: int):
         sc = b[3 * n: 3 * n + 3 * ns * 4].view(np.float32).astype(np.float64)
 
         def mat(q, s, rows, cols):
-            v = decode_e4m3(q).reshape(rows, cols)
-            s = s.reshape(rows // 128, cols // 128)
-            return v * np.repeat(np.repeat(s, 128, axis=0), 128, axis=1)
+            # element (r, c) times the scale of block (r // 128, c // 128)
+            v = decode_e4m3(q).reshape(rows // 128, 128, cols // 128, 128)
+            v *= s.reshape(rows // 128, 1, cols // 128, 1)
+            return v.reshape(rows, cols)
 
         g = mat(b[:n], sc[:ns], I, H)
         u = mat(b[n:2 * n], sc[ns:2 * ns], I, H)
@@ -153,12 +157,9 @@ def dequant_expert(blob: np.ndarray, fmt: int, H: int, I: int):
         sc = b[3 * npk: 3 * npk + 3 * ns]
 
         def mat(p, s, rows, cols):
-            lo = decode_e2m1(p & 0xF)
-            hi = decode_e2m1(p >> 4)
-            v = np.empty(rows * cols, dtype=np.float64)
-            v[0::2] = lo
-            v[1::2] = hi
-            v = v.reshape(rows, cols // 32, 32) * e8m0_to_f64(s).reshape(rows, cols // 32, 1)
+            # byte -> (even element = low nibble, odd element = high nibble)
+            v = lookup(E2M1_PAIRS, p).reshape(rows, cols // 32, 32)
+            v *= e8m0_to_f64(s).reshape(rows, cols // 32, 1)
             return v.reshape(rows, cols)
 
         g = mat(b[:npk], sc[:ns], I, H)
@@ -171,11 +172,11 @@ def dequant_expert(blob: np.ndarray, fmt: int, H: int, I: int):
         ts = b[3 * npk + 3 * ns: 3 * npk + 3 * ns + 12].view(np.float32).astype(np.float64)
 
         def mat(p, s, t, rows, cols):
-            v = np.empty(rows * cols, dtype=np.float64)
-            v[0::2] = decode_e2m1(p & 0xF)
-            v[1::2] = decode_e2m1(p >> 4)
-            v = v.reshape(rows, cols // 16, 16) * decode_e4m3(s).reshape(rows, cols // 16, 1)
-            return v.reshape(rows, cols) * t
+            v = lookup(E2M1_PAIRS, p).reshape(rows, cols // 16, 16)
+            v *= decode_e4m3(s).reshape(rows, cols // 16, 1)
+            v = v.reshape(rows, cols)
+            v *= t
+            return v
 
         g = mat(b[:npk], sc[:ns], ts[0], I, H)
         u = mat(b[npk:2 * npk], sc[ns:2 * ns], ts[1], I, H)
@@ -245,10 +246,13 @@ def mirror_quant_mxfp6(v: np.ndarray) -> np.ndarray:
 
 def mirror_activation(v: np.ndarray, fmt: int, act: str | None = None) -> np.ndarray:
     """The GPU path's rounding of a GEMM input activation (x before GEMM 1,
-    A before GEMM 2): bf16 -> bf16, nvfp4 -> fp16 (its dequantised weights
-    and the activations meet in the fp16 MFMA), fp8 -> per-128 E4M3, mxfp4
-    -> MXFP8, or MXFP6 with act="mxfp6" (the large-batch MXFP6 variant)."""
-    if fmt == FMT_BF16:
+    A before GEMM 2).  act="bf16": rounded to bf16 whatever the weight
+    format (fp8 and mxfp4 weights dequantised exactly to bf16 meet bf16
+    activations: the small-batch kernels).  Otherwise by format: bf16 ->
+    bf16, nvfp4 -> fp16 (its dequantised weights and the activations meet in
+    the fp16 MFMA), fp8 -> per-128 E4M3, mxfp4 -> MXFP8, or MXFP6 with
+    act="mxfp6" (the large-batch kernels' 8-bit and 6-bit activations)."""
+    if fmt == FMT_BF16 or act == "bf16":
         return round_to_bf16(v)
     if fmt == FMT_NVFP4:
         return round_to_f16(v)
@@ -264,8 +268,11 @@ def expert_ffn_mirrored(x: np.ndarray, Wg, Wu, Wd, fmt: int, act: str | None = N
     mxfp4) or rounded to fp16 (nvfp4), A = silu(g)*u rounded to bf16 or fp16
     or quantised, Z rounded to bf16.  nvfp4 weights enter the fp16 MFMA as
     element * block scale (exact in fp16) and the tensor scale multiplies
-    the fp32 sums, so the weights are not rounded here.  act: activation
-    variant of mxfp4 (None or "mxfp6")."""
+    the fp32 sums, so the weights are not rounded here; fp8 and mxfp4
+    weights meeting bf16 activations are exact in bf16 as well (E4M3 codes,
+    and E2M1 codes times a power-of-two block scale; the fp8 block scale
+    multiplies fp32 partial sums).  act: "bf16" (16-bit activations for any
+    format), None (the format's rule above) or "mxfp6" (mxfp4 weights)."""
     xq = x if fmt == FMT_BF16 else mirror_activation(x, fmt, act)
     g = xq @ Wg.T
     u = xq @ Wu.T
@@ -283,12 +290,14 @@ def moe_layer(x_bits, router_w, bias, k, expert_weights, fmt=FMT_BF16, mode="exa
     """One routed MoE layer.
 
     x_bits: bf16 bit patterns [T,H]; router_w [E,H] fp32; bias [E] or None;
-    expert_weights(e) -> (Wg, Wu, Wd) float64; mode "exact" or "mirrored";
+    expert_weights(e) -> (Wg, Wu, Wd) float64; mode "exact", "mirrored" or
+    "both" (one pass over the experts, each dequantised once: out = the
+    mirrored output, out_exact = the exact one);
     host_set: experts whose contribution is computed by the host branch.  In
     "mirrored" mode those are evaluated exactly (the host branch keeps fp32,
     without the GPU's intermediate rounding) and added before the final bf16
-    rounding.  logits: optional precomputed [T,E] logits.  act: mxfp4's
-    activation variant in "mirrored" mode (None: MXFP8, "mxfp6": MXFP6).
+    rounding.  logits: optional precomputed [T,E] logits.  act: activation
+    rule in "mirrored" mode ("bf16", None: the format's own, "mxfp6").
     Returns dict(out [T,H] float64, ids, w, z, margin).
     """
     x = bf16_to_f64(x_bits)
@@ -298,18 +307,25 @@ def moe_layer(x_bits, router_w, bias, k, expert_weights, fmt=FMT_BF16, mode="exa
     w = gate_weights(z, ids)
     host_set = set() if host_set is None else set(int(e) for e in host_set)
     out = np.zeros_like(x)
+    out_x = np.zeros_like(x) if mode == "both" else None
     for e in sorted(set(ids.reshape(-1).tolist())):
         rows, js = np.nonzero(ids == e)
         Wg, Wu, Wd = expert_weights(e)
         xe = x[rows]
+        ye_x = expert_ffn(xe, Wg, Wu, Wd) if mode != "mirrored" or e in host_set else None
         if mode == "exact" or e in host_set:
-            ye = expert_ffn(xe, Wg, Wu, Wd)
+            ye = ye_x
         else:
             ye = expert_ffn_mirrored(xe, Wg, Wu, Wd, fmt, act)
         out[rows] += w[rows, js][:, None] * ye
-    if mode == "mirrored":
+        if out_x is not None:
+            out_x[rows] += w[rows, js][:, None] * ye_x
+    if mode in ("mirrored", "both"):
         out = round_to_bf16(out)
-    return dict(out=out, ids=ids, w=w, z=z, margin=topk_margin(z, k))
+    res = dict(out=out, ids=ids, w=w, z=z, margin=topk_margin(z, k))
+    if out_x is not None:
+        res["out_exact"] = out_x
+    return res
 
 
 def host_partial(x_bits, ids, w, host_set, expert_weights) -> np.ndarray:

@@ -231,3 +231,30 @@ def test_mxfp6_relative_error_bound():
     rel = np.abs(q - v)[near] / np.abs(v)[near]
     assert rel.max() <= 2.0 ** -4 + 1e-12
     assert np.abs(q - v).max() <= np.abs(v).max() * 2.0 ** -3
+
+
+@pytest.mark.parametrize("fmt,act", [(M.FMT_BF16, None), (M.FMT_FP8, None), (M.FMT_FP8, "bf16"),
+                                     (M.FMT_MXFP4, "mxfp6"), (M.FMT_NVFP4, None)])
+def test_both_modes_in_one_pass_equal_the_single_modes(fmt, act):
+    cfg = _tiny(fmt)
+    x = synth.hidden(cfg, 7, 16)
+    R = synth.router_weights(cfg, 7, 0)
+    wf = _weights_fn(cfg, 7)
+    both = M.moe_layer(x, R, None, cfg.k, wf, fmt=fmt, mode="both", act=act, host_set={2})
+    mi = M.moe_layer(x, R, None, cfg.k, wf, fmt=fmt, mode="mirrored", act=act, host_set={2})
+    ex = M.moe_layer(x, R, None, cfg.k, wf, fmt=fmt, mode="exact", act=act)
+    np.testing.assert_array_equal(both["out"], mi["out"])
+    np.testing.assert_array_equal(both["out_exact"], ex["out"])
+
+
+def test_bf16_activation_rule_applies_to_quantised_weights():
+    """act="bf16": fp8 / MXFP4 weights (dequantised exactly) meet bf16-rounded
+    activations, so the mirrored layer equals the bf16 rule applied to the
+    same float64 weights."""
+    cfg = _tiny(M.FMT_FP8)
+    x = synth.hidden(cfg, 8, 16)
+    R = synth.router_weights(cfg, 8, 0)
+    wf = _weights_fn(cfg, 8)
+    a = M.moe_layer(x, R, None, cfg.k, wf, fmt=M.FMT_FP8, mode="mirrored", act="bf16")["out"]
+    b = M.moe_layer(x, R, None, cfg.k, wf, fmt=M.FMT_BF16, mode="mirrored")["out"]
+    np.testing.assert_array_equal(a, b)
