@@ -69,10 +69,14 @@ def parse():
     ap.add_argument("--no-e2e", action="store_true")
     ap.add_argument("--no-prefill", action="store_true")
     ap.add_argument("--no-cpu", action="store_true")
+    ap.add_argument("--small-T", type=lambda v: [int(t) for t in v.split(",") if t], default=[1, 8, 32],
+                    help="extra resident decode batch sizes timed on the same runtime (comma list, empty: none)")
     ap.add_argument("--e2e-T", type=int, default=1, help="tokens per step through the slot cache")
     ap.add_argument("--e2e-warmup", type=int, default=16)
     ap.add_argument("--e2e-steps", type=int, default=32)
     ap.add_argument("--prefill-T", type=int, default=8192)
+    ap.add_argument("--prefill-Ts", type=lambda v: [int(t) for t in v.split(",") if t], default=[4096, 16384],
+                    help="further prefill chunk sizes timed with and without the second buffer (comma list)")
     ap.add_argument("--prefill-runs", type=int, default=2, help="double-buffered chunks timed (best is kept)")
     ap.add_argument("--cpu-layers", type=int, default=20, help="decode layers the oracle times (~0.5 s each)")
     ap.add_argument("--host-threads", type=int, default=16)
@@ -267,10 +271,74 @@ def phase_decode(w: Workload):
     }
     log(json.dumps(roofline))
     log(json.dumps(detail))
+    if args.small_T:
+        detail["small_T"] = {str(t): decode_resident_at(w, rt, rows, t) for t in args.small_T}
     rt.close()
     del rt
     torch.cuda.empty_cache()
     return value, elapsed, roofline, detail
+
+
+def decode_resident_at(w: Workload, rt, rows, T):
+    """Resident decode at a smaller batch on the same runtime: seeded rows of
+    the locality model, one HIP graph per 48-layer step (the value's launch
+    mode), then an eager pass with every launch timed for the stage split."""
+    import torch
+    import synth
+    args, c = w.args, w.cfg
+    L, E, k, H, I, S = c.L, c.E, c.k, c.H, c.I, c.expert_bytes
+    K, W = args.steps, args.warmup
+    keys = synth.decode_row_keys(c, args.seed + 100 + T, W + K, T)
+    hid = torch.from_numpy(synth.hidden_rows(c, keys.reshape(-1)).reshape(W + K, L, T, H).view(np.int16)).to(w.dev)
+    outs = torch.empty(L, T, H, dtype=torch.bfloat16, device=w.dev)
+    ids = torch.empty(T, k, dtype=torch.int32, device=w.dev)
+    wts = torch.empty(T, k, dtype=torch.float32, device=w.dev)
+    n_active = np.zeros((K, L), dtype=np.int64)
+    for s in range(K):
+        for l in range(L):
+            rt.route(hid[W + s, l], w.R[l], w.bias[l], ids, wts)
+            n_active[s, l] = len(torch.unique(ids).cpu())
+
+    def step(s):
+        for l in range(L):
+            rt.forward(l, hid[s, l], w.R[l], w.bias[l], rows[l], outs[l])
+
+    for s in range(W):
+        step(s)
+    torch.cuda.synchronize()
+    cap = torch.cuda.Stream()
+    graphs = []
+    for s in range(K):
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cap):
+            step(W + s)
+        graphs.append(g)
+    graphs[0].replay()
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(K):
+        graphs[s].replay()
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    rt.profile_begin(K * L * 10 + 16)
+    for s in range(K):
+        step(W + s)
+    prof = profile_end(rt)
+    assert rt.check_device_error() == 0
+    stage_us = {n: v["ms"] / v["launches"] * 1e3 for n, v in prof.items() if isinstance(v, dict) and v["launches"]}
+    launches = {n: v["launches"] / (K * L) for n, v in prof.items() if isinstance(v, dict) and v["launches"]}
+    gpu_layer_us = sum(stage_us[n] * launches[n] for n in stage_us)
+    layer_bytes = float((n_active * S + E * H * 4 + 2 * T * H * 2).sum() / (K * L))
+    res = {
+        "T": T, "launch": "hip graph per step", "ms_per_step": el / K * 1e3,
+        "moe_layer_tokens_per_s": K * L * T / el, "layer_wall_us": el / (K * L) * 1e6,
+        "layer_bytes_MB": layer_bytes / 1e6, "mean_active_experts": float(n_active.mean()),
+        "layer_hbm_frac_of_wall": layer_bytes / (el / (K * L)) / HBM_PEAK,
+        "gpu_layer_us": gpu_layer_us, "layer_hbm_frac_of_gpu_time": layer_bytes / (gpu_layer_us * 1e-6) / HBM_PEAK,
+        "launches_per_layer": launches, "stage_us": stage_us,
+    }
+    log(f"decode resident T={T}: {json.dumps(res)}")
+    return res
 
 
 def phase_e2e(w: Workload):
@@ -286,7 +354,9 @@ def phase_e2e(w: Workload):
     hid = torch.from_numpy(synth.hidden_rows(c, keys.reshape(-1)).reshape(W + K, L, T, c.H).view(np.int16)).to(w.dev)
     outs = torch.empty(L, T, c.H, dtype=torch.bfloat16, device=w.dev)
     rc = w.runtime(c.n_slots, max(T, 64))
-    bp, bh = rc.calibrate()
+    cal = rc.calibrate_ex(T)
+    bp, bh = cal["B_P"], cal["B_H"]
+    log(f"calibration: {json.dumps(cal)}")
     rc.set_policy(B.MOE_POLICY_HYBRID, bp, bh)
     copy = torch.cuda.Stream()
     infos = []
@@ -303,11 +373,13 @@ def phase_e2e(w: Workload):
         e2e_step(s, False)
     torch.cuda.synchronize()
     warm_el = time.perf_counter() - t0
+    rc.plan_stats(reset=True)
     t0 = time.perf_counter()
     for s in range(K):
         e2e_step(W + s, True)
     torch.cuda.synchronize()
     el = time.perf_counter() - t0
+    tot = rc.plan_stats(reset=True)           # host-branch time of the timed steps, from the pool
     assert rc.check_device_error() == 0
     uq = sum(i["n_unique"] for i in infos)
     # per-stage GPU times over the timed steps' rows again (after the timed
@@ -323,6 +395,7 @@ def phase_e2e(w: Workload):
     res = {
         "note": "PCIe and host included; not the value",
         "T": T, "n_slots": c.n_slots, "policy": "hybrid", "B_P_GBps": bp, "B_H_GBps": bh,
+        "B_R_GBps": bh - bp, "calibration": cal,
         "q_star_over_m": bp / bh, "warmup_steps": W, "warmup_ms_per_step": warm_el / max(W, 1) * 1e3,
         "steps": K, "moe_layer_tokens_per_s": K * L * T / el, "ms_per_step": el / K * 1e3,
         "hit_rate": sum(i["n_hit"] for i in infos) / max(uq, 1),
@@ -331,8 +404,12 @@ def phase_e2e(w: Workload):
         "host_per_layer": sum(i["n_host"] for i in infos) / len(infos),
         "t_fill_pred_us_per_layer": sum(i["t_fill_pred_us"] for i in infos) / len(infos),
         "t_host_pred_us_per_layer": sum(i["t_host_pred_us"] for i in infos) / len(infos),
+        # the host branches as they ran (pool time, timed steps), against the prediction above
+        "host_branch_us_per_layer": tot["host_ms"] * 1e3 / len(infos),
+        "host_branch_GBps": tot["n_host"] * c.expert_bytes / max(tot["host_ms"] * 1e-3, 1e-12) / 1e9,
         "stage_us_per_launch": stage_us,
     }
+    res["host_pred_over_measured"] = res["t_host_pred_us_per_layer"] / max(res["host_branch_us_per_layer"], 1e-9)
     res["device_cache_control"] = e2e_async(w, rc, hid, outs)
     log(json.dumps(res))
     rc.close()
@@ -478,14 +555,32 @@ def phase_elastic(w: Workload):
 
 
 def phase_prefill(w: Workload):
-    """One prefill chunk through the full-layer double buffer, and without it."""
+    """Prefill chunks through the full-layer double buffer, and without it,
+    at each chunk size of --prefill-Ts (the 8192-token chunk is the headline
+    prefill figure; the others are listed under by_T)."""
+    import torch
+    import synth
+    args, c = w.args, w.cfg
+    L = c.L
+    Ts = sorted(set(args.prefill_Ts + [args.prefill_T]))
+    pcfg = synth.CONFIGS[3].with_layers(L)
+    rp = w.runtime(pcfg.n_slots, max(Ts))
+    by_T = {Tp: prefill_at(w, rp, pcfg, Tp) for Tp in Ts}
+    rp.close()
+    del rp
+    torch.cuda.empty_cache()
+    res = dict(by_T[args.prefill_T])
+    res["by_T"] = {str(Tp): r for Tp, r in by_T.items() if Tp != args.prefill_T}
+    return res
+
+
+def prefill_at(w: Workload, rp, pcfg, Tp):
+    """One chunk of Tp tokens through the 48 layers: best of --prefill-runs
+    double-buffered runs, then one run with the second buffer off."""
     import torch
     import synth
     args, c = w.args, w.cfg
     L, E, k, H, I, S = c.L, c.E, c.k, c.H, c.I, c.expert_bytes
-    Tp = args.prefill_T
-    pcfg = synth.CONFIGS[3].with_layers(L)
-    rp = w.runtime(pcfg.n_slots, Tp)
     comp, copy = torch.cuda.Stream(), torch.cuda.Stream()
     hp = torch.empty(Tp, H, dtype=torch.int16, device=w.dev)
     out_p = torch.empty(Tp, H, dtype=torch.bfloat16, device=w.dev)
@@ -519,9 +614,6 @@ def phase_prefill(w: Workload):
         "loss_without_double_buffer": 1.0 - el_on / el_off,
     }
     log(json.dumps(res))
-    rp.close()
-    del rp
-    torch.cuda.empty_cache()
     return res
 
 
@@ -878,11 +970,28 @@ def phase_cpu(w: Workload):
         M.moe_layer(w.hid_np[args.warmup, l], w.R[l].cpu().numpy(), w.bias[l].cpu().numpy(), k, wf, fmt=c.fmt,
                     mode="exact")
     el = time.perf_counter() - t0
+    # the same oracle with its BLAS held to one thread, on fewer layers
+    from threadpoolctl import threadpool_limits
+    n1 = max(1, min(args.cpu_layers // 5, L))
+    with threadpool_limits(limits=1):
+        t0 = time.perf_counter()
+        for l in range(n1):
+            wcache = {}
+
+            def wf1(e, l=l):
+                if e not in wcache:
+                    wcache[e] = M.dequant_expert(pool_np[l * E + e], c.fmt, H, I)
+                return wcache[e]
+            M.moe_layer(w.hid_np[args.warmup, l], w.R[l].cpu().numpy(), w.bias[l].cpu().numpy(), k, wf1,
+                        fmt=c.fmt, mode="exact")
+        el1 = time.perf_counter() - t0
     res = {
         "value": nl * T / el, "unit": "MoE-layer tokens/s", "cores": int(blas_threads), "kind": "oracle",
         "sample": f"layers 0-{nl - 1} of the first timed decode step (T={T}), float64 NumPy oracle, "
                   f"{cores} host cores visible",
         "seconds": el,
+        "one_thread": {"value": n1 * T / el1, "cores": 1, "seconds": el1,
+                       "sample": f"layers 0-{n1 - 1} of the same step, BLAS limited to one thread"},
     }
     log(json.dumps(res))
     return res

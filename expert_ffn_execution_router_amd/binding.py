@@ -43,6 +43,15 @@ class moe_plan_totals(ctypes.Structure):
         return {f: getattr(self, f) for f, _ in self._fields_}
 
 
+class moe_calibration(ctypes.Structure):
+    _fields_ = [(f, ctypes.c_double) for f in ("B_P", "B_P_min", "B_P_max", "B_H", "host_alone", "host_alone_min",
+                                               "host_alone_max", "host_conc", "host_conc_min", "host_conc_max")] + \
+        [(f, ctypes.c_int) for f in ("n_copy", "n_host_alone", "n_host_conc")]
+
+    def as_dict(self):
+        return {f: getattr(self, f) for f, _ in self._fields_}
+
+
 class moe_plan_info(ctypes.Structure):
     _fields_ = [("n_unique", ctypes.c_int), ("n_hit", ctypes.c_int), ("m", ctypes.c_int), ("q", ctypes.c_int),
                 ("n_host", ctypes.c_int), ("n_evict", ctypes.c_int), ("t_fill_pred_us", ctypes.c_double),
@@ -79,6 +88,7 @@ SIGNATURES = {
     "moe_host_free": (_i, [_vp]),
     "moe_set_policy": (_i, [_vp, _i, _d, _d]),
     "moe_set_activations": (_i, [_vp, _i]),
+    "moe_calibrate_ex": (_i, [_vp, _i, _P(moe_calibration)]),
     "moe_calibrate": (_i, [_vp, _P(_d), _P(_d)]),
     "moe_slot_table": (_vp, [_vp]),
     "moe_reset_cache": (_i, [_vp, _vp]),
@@ -153,6 +163,7 @@ moe_host_alloc = _fn("moe_host_alloc")
 moe_host_free = _fn("moe_host_free")
 moe_set_policy = _fn("moe_set_policy")
 moe_set_activations = _fn("moe_set_activations")
+moe_calibrate_ex = _fn("moe_calibrate_ex")
 moe_calibrate = _fn("moe_calibrate")
 moe_slot_table = _fn("moe_slot_table")
 moe_reset_cache = _fn("moe_reset_cache")

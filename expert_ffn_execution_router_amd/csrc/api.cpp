@@ -17,6 +17,7 @@
 
 #include "moe.h"
 #include "common.h"
+#include "fwd_ws.h"
 #include "host_ffn.h"
 
 extern "C" {
@@ -30,7 +31,8 @@ hipError_t moe_launch_group(const int32_t* ids, int T, int k, int E, const uint3
 hipError_t moe_launch_gemm_dec(int fmt, int gated, int ns, int n_cu, const WorkList* wl, const int32_t* counts,
                                const int32_t* offsets, const uint8_t* pool, size_t S, size_t woff0, size_t woff1,
                                size_t soff0, size_t soff1, const void* X, const void* Xs, const int32_t* row_tok,
-                               int K, int N, void* out, void* part, int fix, hipStream_t s);
+                               int K, int N, void* out, void* part, size_t part_bytes, int fix, int* err,
+                               hipStream_t s);
 size_t moe_dec_part_bytes();
 int moe_dec_max_ns(int fmt);
 int moe_pf_tile_tokens();
@@ -107,7 +109,9 @@ struct WsLayout {
       Aq, As, Z, Xq, Xs, hp, part, total;
 };
 
-WsLayout ws_layout(const moe_config& c) {
+// fwd_only: the buffers of a forward alone (no residency table, cache
+// state, plan or host partial), with `part_bytes` of partial tiles last.
+WsLayout ws_layout(const moe_config& c, bool fwd_only = false, size_t part_bytes = 0) {
   WsLayout L{};
   const size_t Tm = (size_t)std::max(c.max_tokens, 1);
   const size_t R = Tm * c.k;
@@ -117,11 +121,13 @@ WsLayout ws_layout(const moe_config& c) {
     o += align256(std::max<size_t>(bytes, 1));
     return at;
   };
-  L.slot_table = take((size_t)c.L * c.E * 4);
-  // slot metadata sized for the largest pool, so a rebuild can grow it
-  L.owner = take((size_t)MOE_MAX_SLOTS * 4);
-  L.last_use = take((size_t)MOE_MAX_SLOTS * 4);
-  L.ctl = take(sizeof(CacheCtl));
+  if (!fwd_only) {
+    L.slot_table = take((size_t)c.L * c.E * 4);
+    // slot metadata sized for the largest pool, so a rebuild can grow it
+    L.owner = take((size_t)MOE_MAX_SLOTS * 4);
+    L.last_use = take((size_t)MOE_MAX_SLOTS * 4);
+    L.ctl = take(sizeof(CacheCtl));
+  }
   L.err = take(64);
   L.logits = take(Tm * c.E * 4);
   L.ids = take(R * 4);
@@ -136,7 +142,7 @@ WsLayout ws_layout(const moe_config& c) {
   L.wl_tail = take(sizeof(WorkList));
   L.tail_rows = take((size_t)3 * c.E * 4);
   L.mask = take(64);
-  L.plan = take(sizeof(PlanOut));
+  if (!fwd_only) L.plan = take(sizeof(PlanOut));
   const bool q8 = c.wfmt == MOE_W_FP8_E4M3_B128 || c.wfmt == MOE_W_MXFP4;   // quantised activations
   // MXFP4 may take MXFP6 activations: 128-column planes of x6_plane_bytes(R) bytes
   auto qbytes = [&](size_t cols) {
@@ -149,9 +155,9 @@ WsLayout ws_layout(const moe_config& c) {
   // quantised activations in grouped order (one row per routed pair)
   L.Xq = take(c.wfmt == MOE_W_NVFP4 ? Tm * c.H * 2 : qbytes(c.H));   // NVFP4: the hidden rows in fp16
   L.Xs = take(c.wfmt == MOE_W_FP8_E4M3_B128 ? R * (c.H / 128) * 4 : (q8 ? R * (c.H / 32) : 0));
-  L.hp = take(Tm * c.H * 4);
+  if (!fwd_only) L.hp = take(Tm * c.H * 4);
   // small-batch GEMM: partial tiles of items cut between workgroups
-  L.part = take(moe_dec_part_bytes());
+  L.part = take(fwd_only ? part_bytes : moe_dec_part_bytes());
   L.total = o;
   return L;
 }
@@ -200,6 +206,7 @@ struct moe_ctx {
   void* Xs;
   float* hp;
   void* part;
+  size_t part_bytes = 0;
   // pinned host staging
   PlanOut* plan_host = nullptr;
   uint16_t* hidden_host = nullptr;
@@ -219,7 +226,7 @@ struct moe_ctx {
   std::map<std::pair<int, int>, std::unique_ptr<AsyncArg>> async_args;
   hipEvent_t async_plan_evt = nullptr, async_host_evt = nullptr;
   int async_err = 0;                    // set by a host-branch callback that failed
-  double async_host_ms = 0.0;           // wall time spent in host-branch callbacks
+  double host_ms = 0.0;                 // time of the host branches (both decode paths), from the pool
   // events
   hipEvent_t plan_evt = nullptr, fill_evt = nullptr, ready[2] = {nullptr, nullptr}, done[2] = {nullptr, nullptr};
   int pf_next = -1;
@@ -235,6 +242,39 @@ struct moe_ctx {
 };
 
 namespace {
+
+// Device buffers of a context carved out of its workspace w (layout c->wsl;
+// the forward-only layout leaves the cache-control buffers null).
+void carve(moe_ctx* c, uint8_t* w, bool fwd_only) {
+  const WsLayout& L = c->wsl;
+  c->ws = w;
+  c->slot_table = fwd_only ? nullptr : (int32_t*)(w + L.slot_table);
+  c->owner = fwd_only ? nullptr : (int32_t*)(w + L.owner);
+  c->last_use = fwd_only ? nullptr : (uint32_t*)(w + L.last_use);
+  c->ctl = fwd_only ? nullptr : (CacheCtl*)(w + L.ctl);
+  c->err = (int*)(w + L.err);
+  c->logits = (float*)(w + L.logits);
+  c->ids = (int32_t*)(w + L.ids);
+  c->w = (float*)(w + L.w);
+  c->pos = (int32_t*)(w + L.pos);
+  c->perm_tok = (int32_t*)(w + L.perm_tok);
+  c->counts = (int32_t*)(w + L.counts);
+  c->offsets = (int32_t*)(w + L.offsets);
+  c->hist = (int32_t*)(w + L.hist);
+  c->wl = (WorkList*)(w + L.wl);
+  c->wl_tail = (WorkList*)(w + L.wl_tail);
+  c->tail_rows = (int32_t*)(w + L.tail_rows);
+  c->mask = (uint32_t*)(w + L.mask);
+  c->plan_dev = fwd_only ? nullptr : (PlanOut*)(w + L.plan);
+  c->A = w + L.A;
+  c->Aq = w + L.Aq;
+  c->As = w + L.As;
+  c->Z = (uint16_t*)(w + L.Z);
+  c->Xq = w + L.Xq;
+  c->Xs = w + L.Xs;
+  c->hp = fwd_only ? nullptr : (float*)(w + L.hp);
+  c->part = w + L.part;
+}
 
 int fail(moe_ctx* c, int code, const std::string& m) {
   if (c) c->err_msg = m;
@@ -314,9 +354,13 @@ int forward_experts(moe_ctx* c, const void* hidden, int T, const int32_t* slot_r
   // 128-token, three-stage variant (a weight stream more than a GEMM)
   const int small8 = (long)T * g.k <= 160L * g.E ? 1 : 0;
   const int tile_mb = g.wfmt == MOE_W_BF16 ? moe_pf_tile_tokens() : moe_pf8_tile_tokens(g.wfmt, small8);
-  // weight streaming: m-blocks of 16 * ns tokens (each m-block reads the
-  // expert's weights once; larger blocks cost LDS and idle MFMA rows)
-  const int ns = std::min(T <= 16 ? 1 : (T <= 64 ? 2 : 4), moe_dec_max_ns(g.wfmt));
+  // weight streaming with 16-bit activations: fp8 and MXFP4 weights are
+  // dequantised to bf16 in registers (the small-batch kernels are bound by
+  // the weight bytes, so unrounded activations cost nothing)
+  const int dfmt = g.wfmt == MOE_W_FP8_E4M3_B128 ? WFMT_FP8_A16 : (g.wfmt == MOE_W_MXFP4 ? WFMT_MXFP4_A16 : g.wfmt);
+  // m-blocks of 16 * ns tokens (each m-block reads the expert's weights
+  // once; larger blocks cost LDS and idle MFMA rows)
+  const int ns = std::min(T <= 16 ? 1 : (T <= 64 ? 2 : 4), moe_dec_max_ns(dfmt));
   // MXFP4 weights with MXFP6 activations when selected (large batches)
   const int qf = g.wfmt == MOE_W_MXFP4 && c->act == MOE_ACT_MXFP6 ? WFMT_MXFP4_A6 : g.wfmt;
   // Large batches: an expert whose last m-tile would hold at most one
@@ -344,6 +388,10 @@ int forward_experts(moe_ctx* c, const void* hidden, int T, const int32_t* slot_r
   // launch on the same stream (running them beside the tiled kernels on a
   // second stream was slower: they take CUs from the persistent grid's next
   // launch)
+  // the grouping splits at most n_cu / (4 * ntiles1) experts, each with at
+  // most one m-block of overflow rows, so that many experts times the 64-row
+  // weight tiles bound the overflow items
+  const int max_split = std::max(1, std::min(g.E, c->n_cu / (4 * ntiles1)));
   auto tail_gemm = [&](int gated, const void* X, const void* Xs, const int32_t* row_tok, void* out) -> int {
     if (!split) return MOE_OK;
     const int N = gated ? g.I : g.H;
@@ -351,7 +399,7 @@ int forward_experts(moe_ctx* c, const void* hidden, int T, const int32_t* slot_r
           moe_launch_gemm_dec(g.wfmt, gated, ns_tail, ncu, c->wl_tail, tcounts, toffsets, c->slot_pool, b.S,
                               gated ? b.w[0] : b.w[2], gated ? b.w[1] : 0, gated ? b.s[0] : b.s[2],
                               gated ? b.s[1] : 0, X, Xs, row_tok, gated ? g.H : g.I, N, out, nullptr,
-                              -(g.E * (N / 64)), s));
+                              0, -(max_split * (N / 64)), c->err, s));
     return MOE_OK;
   };
   if (tiled && g.wfmt != MOE_W_BF16) {
@@ -380,45 +428,29 @@ int forward_experts(moe_ctx* c, const void* hidden, int T, const int32_t* slot_r
           moe_launch_gemm_pf(g.wfmt, 0, c->n_cu, c->wl, tile_counts, c->offsets, c->slot_pool, b.S, b.w[2], 0, c->A,
                              nullptr, g.I, g.H, c->Z, s));
     if ((rc = tail_gemm(0, c->A, nullptr, nullptr, c->Z))) return rc;
-  } else if (g.wfmt == MOE_W_BF16 || g.wfmt == MOE_W_NVFP4) {
+  } else {
     // 16-bit tokens gathered through perm_tok for GEMM 1 (bf16, or the
     // hidden rows converted to fp16 for NVFP4's fp16 MFMA), A in the same
-    // type; NVFP4 weights carry their block-scale offsets
+    // type; the quantised formats carry their scale offsets
     const void* x16 = hidden;
     if (g.wfmt == MOE_W_NVFP4) {
       STAGE(c, MOE_STAGE_QUANT_X, s, moe_launch_cvt_f16(hidden, (long)T * g.H, c->Xq, s));
       x16 = c->Xq;
     }
     STAGE(c, MOE_STAGE_GEMM1, s,
-          moe_launch_gemm_dec(g.wfmt, 1, ns, ncu, c->wl, c->counts, c->offsets, c->slot_pool, b.S, b.w[0], b.w[1],
-                              b.s[0], b.s[1], x16, nullptr, c->perm_tok, g.H, g.I, c->A, c->part, 0, s));
+          moe_launch_gemm_dec(dfmt, 1, ns, ncu, c->wl, c->counts, c->offsets, c->slot_pool, b.S, b.w[0], b.w[1],
+                              b.s[0], b.s[1], x16, nullptr, c->perm_tok, g.H, g.I, c->A, c->part, c->part_bytes, 0,
+                              c->err, s));
     STAGE(c, MOE_STAGE_FIXUP, s,
-          moe_launch_gemm_dec(g.wfmt, 1, ns, ncu, c->wl, c->counts, c->offsets, c->slot_pool, b.S, b.w[0], b.w[1],
-                              b.s[0], b.s[1], x16, nullptr, c->perm_tok, g.H, g.I, c->A, c->part, 1, s));
+          moe_launch_gemm_dec(dfmt, 1, ns, ncu, c->wl, c->counts, c->offsets, c->slot_pool, b.S, b.w[0], b.w[1],
+                              b.s[0], b.s[1], x16, nullptr, c->perm_tok, g.H, g.I, c->A, c->part, c->part_bytes, 1,
+                              c->err, s));
     STAGE(c, MOE_STAGE_GEMM2, s,
-          moe_launch_gemm_dec(g.wfmt, 0, ns, ncu, c->wl, c->counts, c->offsets, c->slot_pool, b.S, b.w[2], 0, b.s[2],
-                              0, c->A, nullptr, nullptr, g.I, g.H, c->Z, c->part, 0, s));
+          moe_launch_gemm_dec(dfmt, 0, ns, ncu, c->wl, c->counts, c->offsets, c->slot_pool, b.S, b.w[2], 0, b.s[2],
+                              0, c->A, nullptr, nullptr, g.I, g.H, c->Z, c->part, c->part_bytes, 0, c->err, s));
     STAGE(c, MOE_STAGE_FIXUP, s,
-          moe_launch_gemm_dec(g.wfmt, 0, ns, ncu, c->wl, c->counts, c->offsets, c->slot_pool, b.S, b.w[2], 0, b.s[2],
-                              0, c->A, nullptr, nullptr, g.I, g.H, c->Z, c->part, 1, s));
-  } else {
-    // activations quantised straight into grouped order (row p <- token perm_tok[p])
-    STAGE(c, MOE_STAGE_QUANT_X, s,
-          moe_launch_quant(g.wfmt, 1, hidden, T * g.k, c->offsets + g.E, c->perm_tok, g.H, c->Xq, c->Xs, 0, s));
-    STAGE(c, MOE_STAGE_GEMM1, s,
-          moe_launch_gemm_dec(g.wfmt, 1, ns, ncu, c->wl, c->counts, c->offsets, c->slot_pool, b.S, b.w[0], b.w[1],
-                              b.s[0], b.s[1], c->Xq, c->Xs, nullptr, g.H, g.I, c->A, c->part, 0, s));
-    STAGE(c, MOE_STAGE_FIXUP, s,
-          moe_launch_gemm_dec(g.wfmt, 1, ns, ncu, c->wl, c->counts, c->offsets, c->slot_pool, b.S, b.w[0], b.w[1],
-                              b.s[0], b.s[1], c->Xq, c->Xs, nullptr, g.H, g.I, c->A, c->part, 1, s));
-    STAGE(c, MOE_STAGE_QUANT_A, s,
-          moe_launch_quant(g.wfmt, 0, c->A, T * g.k, c->offsets + g.E, nullptr, g.I, c->Aq, c->As, 0, s));
-    STAGE(c, MOE_STAGE_GEMM2, s,
-          moe_launch_gemm_dec(g.wfmt, 0, ns, ncu, c->wl, c->counts, c->offsets, c->slot_pool, b.S, b.w[2], 0, b.s[2],
-                              0, c->Aq, c->As, nullptr, g.I, g.H, c->Z, c->part, 0, s));
-    STAGE(c, MOE_STAGE_FIXUP, s,
-          moe_launch_gemm_dec(g.wfmt, 0, ns, ncu, c->wl, c->counts, c->offsets, c->slot_pool, b.S, b.w[2], 0, b.s[2],
-                              0, c->Aq, c->As, nullptr, g.I, g.H, c->Z, c->part, 1, s));
+          moe_launch_gemm_dec(dfmt, 0, ns, ncu, c->wl, c->counts, c->offsets, c->slot_pool, b.S, b.w[2], 0, b.s[2],
+                              0, c->A, nullptr, nullptr, g.I, g.H, c->Z, c->part, c->part_bytes, 1, c->err, s));
   }
   return MOE_OK;
 }
@@ -492,11 +524,9 @@ void host_branch_cb(void* p) {
     c->async_err = 1;
     return;
   }
-  const auto t0 = std::chrono::steady_clock::now();
   HostFfnHandle* h = host_ffn_start(c->pool, host_shape(c->cfg, c->bl.S), c->host_pool, a->layer, a->T,
                                     c->hidden_host, c->ids_host, c->w_host, pl.C, pl.n_host, c->hp_host);
-  host_ffn_wait(c->pool, h);
-  c->async_host_ms += std::chrono::duration<double, std::milli>(std::chrono::steady_clock::now() - t0).count();
+  c->host_ms += host_ffn_wait(c->pool, h);
 }
 
 }  // namespace
@@ -553,39 +583,12 @@ int moe_create(const moe_config* cfg, void* host_pool, size_t host_bytes, void* 
   if (!d_workspace || ws_bytes < c->wsl.total) return bad(MOE_E_INVAL, "workspace smaller than moe_workspace_bytes");
   c->host_pool = (uint8_t*)host_pool;
   c->slot_pool = (uint8_t*)d_slot_pool;
-  c->ws = (uint8_t*)d_workspace;
   if (hipGetDevice(&c->device) != hipSuccess) return bad(MOE_E_HIP, "hipGetDevice failed");
   int ncu = 0;
   if (hipDeviceGetAttribute(&ncu, hipDeviceAttributeMultiprocessorCount, c->device) == hipSuccess && ncu > 0)
     c->n_cu = ncu;
-  const WsLayout& L = c->wsl;
-  uint8_t* w = c->ws;
-  c->slot_table = (int32_t*)(w + L.slot_table);
-  c->owner = (int32_t*)(w + L.owner);
-  c->last_use = (uint32_t*)(w + L.last_use);
-  c->ctl = (CacheCtl*)(w + L.ctl);
-  c->err = (int*)(w + L.err);
-  c->logits = (float*)(w + L.logits);
-  c->ids = (int32_t*)(w + L.ids);
-  c->w = (float*)(w + L.w);
-  c->pos = (int32_t*)(w + L.pos);
-  c->perm_tok = (int32_t*)(w + L.perm_tok);
-  c->counts = (int32_t*)(w + L.counts);
-  c->offsets = (int32_t*)(w + L.offsets);
-  c->hist = (int32_t*)(w + L.hist);
-  c->wl = (WorkList*)(w + L.wl);
-  c->wl_tail = (WorkList*)(w + L.wl_tail);
-  c->tail_rows = (int32_t*)(w + L.tail_rows);
-  c->mask = (uint32_t*)(w + L.mask);
-  c->plan_dev = (PlanOut*)(w + L.plan);
-  c->A = w + L.A;
-  c->Aq = w + L.Aq;
-  c->As = w + L.As;
-  c->Z = (uint16_t*)(w + L.Z);
-  c->Xq = w + L.Xq;
-  c->Xs = w + L.Xs;
-  c->hp = (float*)(w + L.hp);
-  c->part = w + L.part;
+  carve(c, (uint8_t*)d_workspace, false);
+  c->part_bytes = moe_dec_part_bytes();
   const size_t Tm = cfg->max_tokens;
   const size_t R = Tm * cfg->k;
   void* p;
@@ -906,6 +909,41 @@ int moe_layer_forward(moe_ctx* c, int layer, const void* hidden, const float* R,
   return combine(c, miss_mask, slot_row, host_partial, T, out, s);
 }
 
+}  // extern "C"
+
+void moe_set_thread_error(const char* msg) { g_err = msg; }
+
+size_t moe_fwd_ws_bytes(const moe_config* cfg, int max_T, size_t part_bytes) {
+  moe_config g = *cfg;
+  g.max_tokens = max_T;
+  return ws_layout(g, true, part_bytes).total;
+}
+
+int moe_fwd_on_ws(const moe_config* cfg, int max_T, uint8_t* ws, size_t part_bytes, int n_cu, const void* slot_pool,
+                  const int32_t* slot_row, const void* hidden, const float* R, const float* bias, int T,
+                  const uint32_t* miss_mask, const float* hp, void* out, int* err, hipStream_t s, const char** msg) {
+  // a context on the stack over the given workspace: its containers stay
+  // empty, so nothing is allocated
+  moe_ctx c;
+  c.cfg = *cfg;
+  c.cfg.max_tokens = max_T;
+  c.cfg.n_slots = 0;
+  c.bl = blob_layout(c.cfg);
+  c.wsl = ws_layout(c.cfg, true, part_bytes);
+  c.slot_pool = (uint8_t*)slot_pool;
+  c.n_cu = n_cu;
+  carve(&c, ws, true);
+  c.err = err;
+  c.part_bytes = part_bytes;
+  int rc = route_only(&c, hidden, R, bias, T, s);
+  if (!rc) rc = forward_experts(&c, hidden, T, slot_row, miss_mask, s);
+  if (!rc) rc = combine(&c, miss_mask, slot_row, hp, T, out, s);
+  if (rc && msg) *msg = "a kernel launch of the forward failed";
+  return rc;
+}
+
+extern "C" {
+
 int moe_decode_layer(moe_ctx* c, int layer, const void* hidden, const float* R, const float* bias, int T, void* out,
                      moe_plan_info* info, void* compute_stream, void* copy_stream) {
   if (!c) return fail(nullptr, MOE_E_INVAL, "null ctx");
@@ -945,7 +983,7 @@ int moe_decode_layer(moe_ctx* c, int layer, const void* hidden, const float* R, 
   }
   const int32_t* row = c->slot_table + (size_t)layer * g.E;
   rc = forward_experts(c, hidden, T, row, c->mask, s);
-  if (h) host_ffn_wait(c->pool, h);
+  if (h) c->host_ms += host_ffn_wait(c->pool, h);
   if (rc) return rc;
   const float* hp = nullptr;
   if (p.n_host > 0) {
@@ -1015,11 +1053,11 @@ int moe_plan_stats(moe_ctx* c, moe_plan_totals* out, int reset) {
     out->q = (long long)v.q;
     out->n_host = (long long)v.n_host;
     out->n_evict = (long long)v.n_evict;
-    out->host_ms = c->async_host_ms;
+    out->host_ms = c->host_ms;
   }
   if (reset) {
     v.calls = v.n_unique = v.n_hit = v.m = v.q = v.n_host = v.n_evict = 0;
-    c->async_host_ms = 0.0;
+    c->host_ms = 0.0;
     HIPCHK(c, hipMemcpy(c->ctl, &v, sizeof(CacheCtl), hipMemcpyHostToDevice));
   }
   const int e = c->async_err;
@@ -1116,58 +1154,122 @@ int prefill_stream_layer(moe_ctx* c, int layer, const void* hidden, const float*
   return single ? MOE_I_SINGLE_BUFFER : MOE_OK;
 }
 
-int moe_calibrate(moe_ctx* c, double* B_P, double* B_H) {
-  if (!c) return fail(nullptr, MOE_E_INVAL, "null ctx");
+int moe_calibrate_ex(moe_ctx* c, int T, moe_calibration* out) {
+  if (!c || !out) return fail(c, MOE_E_INVAL, "null argument");
   const moe_config& g = c->cfg;
+  if (T < 1 || T > c->cfg.max_tokens) return fail(c, MOE_E_INVAL, "T outside [1, max_tokens]");
+  std::memset(out, 0, sizeof(*out));
   const size_t S = c->bl.S;
-  // B_P: whole-expert copies into the highest-numbered slots (freed afterwards)
-  double bp = 0.0;
-  const int n = std::min(std::min(8, g.n_slots), g.L * g.E);
-  if (n > 0) {
-    hipStream_t s;
-    HIPCHK(c, hipStreamCreateWithFlags(&s, hipStreamNonBlocking));
+  const int n_rows = g.L * g.E;
+  // statistics of one series of rates: median, min, max
+  auto summarise = [](std::vector<double> v, double& med, double& lo, double& hi) {
+    if (v.empty()) return;
+    std::sort(v.begin(), v.end());
+    const size_t n = v.size();
+    med = n % 2 ? v[n / 2] : 0.5 * (v[n / 2 - 1] + v[n / 2]);
+    lo = v.front();
+    hi = v.back();
+  };
+  // the host branch on one expert for T tokens (every token routed to it),
+  // as the decode path calls it; distinct (layer, expert) pairs spread over
+  // the pool, so no call reads bytes a previous one left in the host caches
+  std::vector<uint16_t> hid((size_t)T * g.H, 0x3f80);
+  std::vector<int32_t> ids((size_t)T * g.k, -1);
+  std::vector<float> w((size_t)T * g.k, 1.0f);
+  std::vector<float> outv((size_t)T * g.H);
+  int pair = 0;
+  auto host_call = [&]() -> double {
+    const int i = pair++;
+    const int l = (int)(((long)i * 5 + 1) % g.L), e = (int)(((long)i * 37 + 3) % g.E);
+    for (int t = 0; t < T; ++t) ids[(size_t)t * g.k] = e;
+    HostFfnHandle* h = host_ffn_start(c->pool, host_shape(g, S), c->host_pool, l, T, hid.data(), ids.data(),
+                                      w.data(), &e, 1, outv.data());
+    const double ms = host_ffn_wait(c->pool, h);
+    return (double)S / (ms * 1e-3) / 1e9;
+  };
+  // warm-up until the pool's threads run at speed: at least 8 calls and
+  // 100 ms (right after a large pool fill the first tens of ms run up to a
+  // third slower); then 40 timed calls (single calls vary by tens of
+  // percent on a shared host, so the median needs many)
+  const int n_host = 40;
+  {
+    const auto w0 = std::chrono::steady_clock::now();
+    for (int i = 0; i < 8 || std::chrono::steady_clock::now() - w0 < std::chrono::milliseconds(100); ++i)
+      (void)host_call();
+  }
+  std::vector<double> alone;
+  for (int i = 0; i < n_host; ++i) alone.push_back(host_call());
+  summarise(alone, out->host_alone, out->host_alone_min, out->host_alone_max);
+  out->n_host_alone = (int)alone.size();
+
+  // B_P: whole-expert copies from distinct host rows into the highest slots
+  // (freed first, left empty), rounds of n_cp copies
+  const int n_cp = std::min(8, g.n_slots);
+  if (n_cp > 0) {
+    hipStream_t cs;
+    HIPCHK(c, hipStreamCreateWithFlags(&cs, hipStreamNonBlocking));
     hipEvent_t t0, t1;
     HIPCHK(c, hipEventCreate(&t0));
     HIPCHK(c, hipEventCreate(&t1));
-    for (int i = 0; i < n; ++i) c->list_dev_stage[i] = g.n_slots - 1 - i;
-    HIPCHK(c, hipMemcpyAsync(c->ids, c->list_dev_stage, (size_t)n * 4, hipMemcpyHostToDevice, s));
-    HIPCHK(c, moe_launch_free_slots(c->ids, n, c->slot_table, c->owner, c->last_use, s));
-    float best = 1e30f;
-    for (int rep = 0; rep < 4; ++rep) {
-      HIPCHK(c, hipEventRecord(t0, s));
-      for (int i = 0; i < n; ++i)
-        HIPCHK(c, hipMemcpyAsync(c->slot_pool + (size_t)(g.n_slots - 1 - i) * S, c->host_pool + (size_t)i * S, S,
-                                 hipMemcpyHostToDevice, s));
-      HIPCHK(c, hipEventRecord(t1, s));
+    for (int i = 0; i < n_cp; ++i) c->list_dev_stage[i] = g.n_slots - 1 - i;
+    HIPCHK(c, hipMemcpyAsync(c->ids, c->list_dev_stage, (size_t)n_cp * 4, hipMemcpyHostToDevice, cs));
+    HIPCHK(c, moe_launch_free_slots(c->ids, n_cp, c->slot_table, c->owner, c->last_use, cs));
+    HIPCHK(c, hipStreamSynchronize(cs));
+    int row = 0;
+    auto copy = [&](int i) -> hipError_t {
+      const size_t src = (size_t)(row++ % n_rows) * S;
+      return hipMemcpyAsync(c->slot_pool + (size_t)(g.n_slots - 1 - i % n_cp) * S, c->host_pool + src, S,
+                            hipMemcpyHostToDevice, cs);
+    };
+    std::vector<double> rates;
+    for (int rep = 0; rep < 6; ++rep) {
+      HIPCHK(c, hipEventRecord(t0, cs));
+      for (int i = 0; i < n_cp; ++i) HIPCHK(c, copy(i));
+      HIPCHK(c, hipEventRecord(t1, cs));
       HIPCHK(c, hipEventSynchronize(t1));
       float ms = 0.f;
       HIPCHK(c, hipEventElapsedTime(&ms, t0, t1));
-      if (rep > 0) best = std::min(best, ms);
+      if (rep > 0) rates.push_back((double)n_cp * S / (ms * 1e-3) / 1e9);   // the first round warms up
     }
-    bp = (double)n * S / (best * 1e-3) / 1e9;
+    summarise(rates, out->B_P, out->B_P_min, out->B_P_max);
+    out->n_copy = (int)rates.size();
+    // the host branch while the link copies: a train of copies long enough
+    // to cover the host calls (about three times their expected time); only
+    // calls that end before the train does count
+    const double host_s = (n_host + 1) * (double)S / (out->host_alone * 1e9);
+    const double copy_s = (double)S / (out->B_P * 1e9);
+    const int n_train = (int)std::min(512.0, std::max(4.0 * n_cp, std::ceil(3.0 * host_s / copy_s)));
+    for (int i = 0; i < n_train; ++i) HIPCHK(c, copy(i));
+    HIPCHK(c, hipEventRecord(t1, cs));
+    std::vector<double> conc;
+    for (int i = 0; i < n_host + 1; ++i) {
+      if (hipEventQuery(t1) != hipErrorNotReady) break;
+      const double r = host_call();
+      if (hipEventQuery(t1) != hipErrorNotReady) break;   // the train ended during the call
+      if (i > 0) conc.push_back(r);
+    }
+    HIPCHK(c, hipEventSynchronize(t1));
+    summarise(conc, out->host_conc, out->host_conc_min, out->host_conc_max);
+    out->n_host_conc = (int)conc.size();
     (void)hipEventDestroy(t0);
     (void)hipEventDestroy(t1);
-    (void)hipStreamDestroy(s);
+    (void)hipStreamDestroy(cs);
   }
-  // B_H: host FFN over k experts of layer 0 for one token
-  std::vector<uint16_t> hid((size_t)g.H, 0x3f80);
-  std::vector<int32_t> ids(g.k);
-  std::vector<float> w(g.k, 1.0f / g.k);
-  std::vector<float> outv((size_t)g.H);
-  std::vector<int32_t> C(g.k);
-  for (int j = 0; j < g.k; ++j) ids[j] = C[j] = j;
-  double best_h = 1e30;
-  for (int rep = 0; rep < 4; ++rep) {
-    auto a = std::chrono::steady_clock::now();
-    HostFfnHandle* h = host_ffn_start(c->pool, host_shape(g, S), c->host_pool, 0, 1, hid.data(), ids.data(), w.data(),
-                                      C.data(), g.k, outv.data());
-    host_ffn_wait(c->pool, h);
-    const double dt = std::chrono::duration<double>(std::chrono::steady_clock::now() - a).count();
-    if (rep > 0) best_h = std::min(best_h, dt);
-  }
-  const double bh = (double)g.k * S / best_h / 1e9;
-  if (B_P) *B_P = bp;
-  if (B_H) *B_H = bh;
+  // the residual bandwidth the q* split gives the host branch (review
+  // section 2.5: B_R = B_H - B_P): measured directly with the link busy when
+  // enough calls ran inside the copy train, else the standalone rate
+  const double BR = out->n_host_conc >= 3 ? out->host_conc : out->host_alone;
+  out->B_H = out->B_P + BR;
+  return MOE_OK;
+}
+
+int moe_calibrate(moe_ctx* c, double* B_P, double* B_H) {
+  if (!c) return fail(nullptr, MOE_E_INVAL, "null ctx");
+  moe_calibration m;
+  const int rc = moe_calibrate_ex(c, 1, &m);
+  if (rc) return rc;
+  if (B_P) *B_P = m.B_P;
+  if (B_H) *B_H = m.B_H;
   return MOE_OK;
 }
 
@@ -1178,7 +1280,8 @@ int moe_check_device_error(moe_ctx* c) {
   HIPCHK(c, hipMemcpy(&v, c->err, sizeof(int), hipMemcpyDeviceToHost));
   HIPCHK(c, hipMemset(c->err, 0, sizeof(int)));
   HIPCHK(c, hipDeviceSynchronize());
-  if (v) return fail(c, MOE_E_NOT_RESIDENT, "a routed expert was neither resident nor in the host miss set");
+  if (v & 1) return fail(c, MOE_E_NOT_RESIDENT, "a routed expert was neither resident nor in the host miss set");
+  if (v & 2) return fail(c, MOE_E_UNSUPPORTED, "a one-workgroup-per-item GEMM launch had fewer workgroups than items");
   return MOE_OK;
 }
 

@@ -16,6 +16,13 @@ enum { WFMT_BF16 = 0, WFMT_FP8 = 1, WFMT_MXFP4 = 2, WFMT_NVFP4 = 3 };
 // Internal to the large-batch path: MXFP4 weights with MXFP6 (E2M3)
 // activations.
 enum { WFMT_MXFP4_A6 = 4 };
+// Internal to the small-batch path: fp8 or MXFP4 weights met by bf16
+// activations, the weights dequantised to bf16 in registers.
+enum { WFMT_FP8_A16 = 5, WFMT_MXFP4_A16 = 6 };
+
+// fp32 value of an E8M0 scale byte, 2^(e - 127) (e = 0 is the fp32
+// subnormal 2^-127; 255, NaN, is never stored).
+DEV float e8m0_to_f32(uint32_t e) { return __uint_as_float(e ? e << 23 : 0x00400000u); }
 
 // MXFP6 activation rows: per 128-column chunk c a plane of 112-byte rows;
 // the 32 six-bit codes of column block 4c + g form a 24-byte little-endian

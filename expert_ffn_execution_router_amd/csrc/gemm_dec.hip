@@ -67,6 +67,19 @@
 //    (gate and up before SwiGLU, down on Z).  Chunks are 256 K values: 128
 //    bytes of codes and 16 scale bytes per weight row (8 lanes per row
 //    segment, pieces XOR-swizzled by row & 7), 512 bytes per token row.
+//  * fp8 and MXFP4 weights with bf16 activations (the small-batch default:
+//    the stream is bound by the weight bytes, so 16-bit activations cost
+//    nothing and keep the activations unrounded): the weights are
+//    dequantised in registers to bf16 for v_mfma_f32_16x16x32_bf16.  E4M3
+//    codes convert exactly (scale 1) and each 128-K block's partial sum is
+//    multiplied by its fp32 block scale; E2M1 codes convert with their E8M0
+//    block scale, exactly (a power of two times at most two significant
+//    bits).  Chunks are 256 K values: 256 (fp8) or 128 (E2M1) bytes per
+//    weight row, 512 bytes per token row.  Within a pair of MFMA steps lane
+//    group g takes the 16 consecutive K values [16g, 16g+16) of the pair's
+//    64 (8 for each step; the token operand uses the same assignment, so the
+//    products pair up), one 16-byte (fp8) or 8-byte (E2M1) weight read and
+//    one scale per pair.
 #include "common.h"
 
 namespace {
@@ -81,12 +94,15 @@ template <int FMT, bool GATED, int NS>
 struct Cfg {
   static constexpr int NMAT = GATED ? 2 : 1;
   static constexpr bool NV = FMT == WFMT_NVFP4;
-  static constexpr bool BF_X = FMT == WFMT_BF16 || NV;       // 16-bit tokens (bf16, or fp16 for NVFP4)
+  static constexpr bool A16 = FMT == WFMT_FP8_A16 || FMT == WFMT_MXFP4_A16;   // 8/4-bit weights, bf16 tokens
+  static constexpr bool F8S = FMT == WFMT_FP8 || FMT == WFMT_FP8_A16;         // fp32 128x128 block scales
+  static constexpr bool W4 = NV || FMT == WFMT_MXFP4_A16;     // E2M1 rows of 128 bytes per chunk (256 K)
+  static constexpr bool BF_X = FMT == WFMT_BF16 || NV || A16; // 16-bit tokens (bf16, or fp16 for NVFP4)
   static constexpr int CK = FMT == WFMT_BF16 ? 128 : (FMT == WFMT_MXFP4 ? 512 : 256);   // K per chunk
-  static constexpr int WB = NV ? 128 : 256;                   // weight bytes per row per chunk
+  static constexpr int WB = W4 ? 128 : 256;                   // weight bytes per row per chunk
   static constexpr int WSZ = 16 * WB;                         // one wave's rows of one matrix
   static constexpr int NWL = WSZ / 1024;                      // weight loads per wave and matrix
-  static constexpr int XB = (FMT == WFMT_MXFP4 || NV) ? 512 : 256;   // token bytes per chunk
+  static constexpr int XB = (FMT == WFMT_MXFP4 || NV || A16) ? 512 : 256;   // token bytes per chunk
   static constexpr int MB = 16 * NS;                          // tokens per m-block
   static constexpr int NXI = MB * XB / 1024 / NW;             // token loads per wave per chunk
   static constexpr int W_OFF = 0;
@@ -94,13 +110,13 @@ struct Cfg {
   static constexpr int XS_OFF = X_OFF + MB * XB;
   static constexpr int XS_BYTES = BF_X ? 0 : NW * 256;
   static constexpr int WS_OFF = XS_OFF + XS_BYTES;
-  static constexpr int WS_BYTES = FMT == WFMT_BF16 ? 0 : (FMT == WFMT_FP8 ? NW * 256 : NMAT * NW * 256);
+  static constexpr int WS_BYTES = FMT == WFMT_BF16 ? 0 : (F8S ? NW * 256 : NMAT * NW * 256);
   static constexpr int STAGE = WS_OFF + WS_BYTES;
-  // ring stages: NVFP4 with two stages fits more workgroups per CU
-  static constexpr int NST = (NV && NS <= 2) ? 2 : 3;
+  // ring stages: E2M1 rows with two stages fit more workgroups per CU
+  static constexpr int NST = (W4 && NS <= 2) ? 2 : 3;
   // loads per wave per chunk: weights, tokens, token scales, weight scales
   static constexpr int NI = NWL * NMAT + NXI + (BF_X ? 0 : 1) +
-                            (FMT == WFMT_BF16 ? 0 : (FMT == WFMT_FP8 ? 1 : NMAT));
+                            (FMT == WFMT_BF16 ? 0 : (F8S ? 1 : NMAT));
   static constexpr int NACC = NMAT * NS;
   static_assert(NXI >= 1 && NXI * NW * 1024 == MB * XB, "token chunk must split evenly over the waves");
   static_assert(FMT != WFMT_FP8 || 2 * MB <= NW * 64, "fp8 token scales: one dword per lane");
@@ -124,6 +140,25 @@ DEV int uni(int v) { return __builtin_amdgcn_readfirstlane(v); }
 DEV float silu_mul(float g, float u) { return g / (1.0f + expf(-g)) * u; }
 
 DEV i32x4_t lds16(const uint8_t* p) { return *(const i32x4_t*)p; }
+
+// Eight E4M3 codes (bytes of d0 then d1, element order) as bf16, exact.
+DEV bf16x8_t fp8x8_bf16(int d0, int d1) {
+  const bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((uint32_t)d0, 1.0f, false);
+  const bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((uint32_t)d0, 1.0f, true);
+  const bf16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((uint32_t)d1, 1.0f, false);
+  const bf16x2_t d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp8((uint32_t)d1, 1.0f, true);
+  return bf16x8_t{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
+
+// Eight E2M1 codes (nibbles of w, even element in the low nibble) times the
+// block scale s (a power of two) as bf16, exact.
+DEV bf16x8_t fp4x8_bf16(uint32_t w, float s) {
+  const bf16x2_t a = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 0);
+  const bf16x2_t b = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 1);
+  const bf16x2_t c = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 2);
+  const bf16x2_t d = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4(w, s, 3);
+  return bf16x8_t{a[0], a[1], b[0], b[1], c[0], c[1], d[0], d[1]};
+}
 
 struct Item {
   int slot, row0, nrows, n0;
@@ -222,18 +257,19 @@ DEV void decode_global(const WorkList* wl, const int32_t* counts, const int32_t*
 // or fp16 for NVFP4) or taken in grouped order; Xs holds the activation
 // scales of the 8-bit formats; soff0/soff1 the weight scales.
 // part: partial tiles [MAX_BLOCKS][2][NW][NACC][64] of the items cut by a
-// range boundary, finished by gemm_dec_fix.
+// range boundary, finished by gemm_dec_fix; part == nullptr: one workgroup
+// per item, and a grid smaller than the item count sets bit 1 of *err.
 template <int FMT, bool GATED, int NS>
 __global__ void __launch_bounds__(256, 1)
 gemm_dec(const WorkList* __restrict__ wl, const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
          const uint8_t* __restrict__ pool, size_t S, size_t woff0, size_t woff1, size_t soff0, size_t soff1,
          const uint8_t* __restrict__ X, const uint8_t* __restrict__ Xs, const int32_t* __restrict__ row_tok, int K,
-         int N, void* __restrict__ out, f32x4_t* __restrict__ part) {
+         int N, void* __restrict__ out, f32x4_t* __restrict__ part, int* __restrict__ err) {
   using C = Cfg<FMT, GATED, NS>;
   extern __shared__ __align__(16) uint8_t ring[];
   __shared__ int l_pref[257], l_slot[256], l_row0[256], l_cnt[256];
   // token row of each grouped row this workgroup touches (16-bit GEMM 1)
-  constexpr int ROWTAB = (FMT == WFMT_BF16 && GATED) ? 2048 : ((C::NV && GATED) ? 1024 : 1);
+  constexpr int ROWTAB = (FMT == WFMT_BF16 && GATED) ? 2048 : (((C::NV || C::A16) && GATED) ? 1024 : 1);
   __shared__ int l_rows[ROWTAB];
   const int wave = uni(threadIdx.x >> 6), lane = threadIdx.x & 63;
   const int lr = lane & 15, lg = lane >> 4;
@@ -256,7 +292,10 @@ gemm_dec(const WorkList* __restrict__ wl, const int32_t* __restrict__ counts, co
   if (U == 0) return;
   // part == nullptr: one workgroup per item (the grid covers every item),
   // so no item is cut and nothing needs summing afterwards
-  if (!part && U / KC > (long)gridDim.x) return;
+  if (!part && U / KC > (long)gridDim.x) {
+    if (blockIdx.x == 0 && threadIdx.x == 0) atomicOr(err, 2);   // items would be left unwritten
+    return;
+  }
   const long G = !part ? U / KC : (U < (long)gridDim.x ? U : (long)gridDim.x);
   long b = blockIdx.x;
   if (G == gridDim.x && (gridDim.x % N_XCD) == 0)       // XCD x takes ranges x*G/8 .. (x+1)*G/8 - 1
@@ -265,7 +304,7 @@ gemm_dec(const WorkList* __restrict__ wl, const int32_t* __restrict__ counts, co
   const long u0 = range_start(b, U, G), u1 = range_start(b + 1, U, G);
 
   // bytes of one weight row and of one token row
-  const int wrow = FMT == WFMT_BF16 ? K * 2 : (FMT == WFMT_FP8 ? K : K / 2);
+  const int wrow = FMT == WFMT_BF16 ? K * 2 : (C::F8S ? K : K / 2);
   const int xrow = C::BF_X ? K * 2 : K;
 
   // Items are visited in order: a cursor (m-block p, tile nt, active expert
@@ -320,11 +359,11 @@ gemm_dec(const WorkList* __restrict__ wl, const int32_t* __restrict__ counts, co
   // weight loads: instruction j covers rows 4j..4j+3 of the wave's 16; lane l
   // fetches piece (l&15) ^ row so that the lane-linear LDS placement is the
   // swizzled layout
-  // (NVFP4: instruction j covers rows 8j..8j+7, lane l piece (l&7) ^ (row&7))
+  // (E2M1 rows of 128 bytes: instruction j covers rows 8j..8j+7, lane l piece (l&7) ^ (row&7))
   uint32_t w_lane[4];
 #pragma unroll
   for (int j = 0; j < C::NWL; ++j) {
-    if (C::NV) {
+    if (C::W4) {
       const int r = 8 * j + (lane >> 3);
       w_lane[j] = (uint32_t)(16 * wave + r) * wrow + (((lane & 7) ^ (r & 7)) << 4);
     } else {
@@ -397,8 +436,8 @@ gemm_dec(const WorkList* __restrict__ wl, const int32_t* __restrict__ counts, co
       for (int j = 0; j < C::NWL; ++j) {
         uint32_t o = w_lane[j];
         if (FMT != WFMT_BF16 && wpart) {
-          const int r = C::NV ? 8 * j + (lane >> 3) : 4 * j + (lane >> 4);
-          const int p16 = (C::NV ? ((lane & 7) ^ (r & 7)) : ((lane & 15) ^ r)) << 4;
+          const int r = C::W4 ? 8 * j + (lane >> 3) : 4 * j + (lane >> 4);
+          const int p16 = (C::W4 ? ((lane & 7) ^ (r & 7)) : ((lane & 15) ^ r)) << 4;
           o = (uint32_t)(16 * wave + r) * wrow + (p16 < wrow - kc * C::WB ? p16 : 0);
         }
         dma16_nt(mat + o, sb + C::W_OFF + (m * NW + wave) * C::WSZ + j * 1024);
@@ -416,9 +455,9 @@ gemm_dec(const WorkList* __restrict__ wl, const int32_t* __restrict__ counts, co
       }
       dma16(xb + o, sb + C::X_OFF + (wave * C::NXI + j) * 1024);
     }
-    if (FMT == WFMT_FP8) {
+    if (C::F8S) {
       const int kb = K / 128;   // 128-K groups per row
-      {
+      if (FMT == WFMT_FP8) {
         // token scales: entry e = 64*wave + lane -> token e/2, half e%2 of the chunk
         const int e = wave * 64 + lane, t = e >> 1, h = e & 1;
         const int tt = t < ii.nrows ? t : 0;
@@ -439,6 +478,17 @@ gemm_dec(const WorkList* __restrict__ wl, const int32_t* __restrict__ counts, co
         // weight scales: lane -> row lane/4 of the wave's 16, 4 bytes (16 per row per chunk)
         const int r = lane >> 2, qd = lane & 3;
         const int g = min(kc * 16 + qd * 4, kb - 4);
+        dma4(wb + (m ? soff1 : soff0) + (size_t)(ii.n0 + 16 * wave + r) * kb + g,
+             sb + C::WS_OFF + (m * NW + wave) * 256);
+      }
+    } else if (FMT == WFMT_MXFP4_A16) {
+      const int kb = K / 32;    // 32-K blocks per row
+#pragma unroll
+      for (int m = 0; m < C::NMAT; ++m) {
+        // weight scales: 8 bytes per row per chunk; lane -> row (lane/2) % 16,
+        // bytes 4*(lane%2).. (lanes 32-63 repeat rows 0-15 into unused bytes)
+        const int r = (lane >> 1) & 15, qd = lane & 1;
+        const int g = min(kc * 8 + qd * 4, kb - 4);
         dma4(wb + (m ? soff1 : soff0) + (size_t)(ii.n0 + 16 * wave + r) * kb + g,
              sb + C::WS_OFF + (m * NW + wave) * 256);
       }
@@ -519,6 +569,58 @@ gemm_dec(const WorkList* __restrict__ wl, const int32_t* __restrict__ counts, co
           for (int m = 0; m < C::NMAT; ++m) {
             const f32x4_t pr = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(wa[m], xv, z4, 0, 0, 0, 127, 0, 127);
             acc[m * NS + ms] += pr * (ws[m] * xs);
+          }
+        }
+      }
+    } else if (C::A16) {
+      // 256 K per chunk in two 128-K halves (one fp8 scale block each), each
+      // half two pairs of MFMA steps; lane group lg of pair p takes K
+      // [64p + 16lg, +16): 8 values for each step of the pair
+      const bool full = kc * 256 + 256 <= K;
+#pragma unroll
+      for (int h = 0; h < 2; ++h) {
+        if (h == 1 && !full) break;
+        f32x4_t pa[C::NACC];                    // fp8: this block's sums, scaled below
+#pragma unroll
+        for (int q = 0; q < C::NACC; ++q) pa[q] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+        for (int pp = 0; pp < 2; ++pp) {
+          const int p = 2 * h + pp;
+          bf16x8_t wa0[C::NMAT], wa1[C::NMAT];
+#pragma unroll
+          for (int m = 0; m < C::NMAT; ++m) {
+            if (C::F8S) {
+              const i32x4_t v = lds16(sb + (m * NW + wave) * C::WSZ + lr * 256 + (((4 * p + lg) ^ lr) << 4));
+              wa0[m] = fp8x8_bf16(v[0], v[1]);
+              wa1[m] = fp8x8_bf16(v[2], v[3]);
+            } else {
+              const uint2 cw = *(const uint2*)(sb + (m * NW + wave) * C::WSZ + lr * 128 +
+                                                (((2 * p + (lg >> 1)) ^ (lr & 7)) << 4) + 8 * (lg & 1));
+              const float sc = e8m0_to_f32(sb[C::WS_OFF + (m * NW + wave) * 256 + lr * 8 + 2 * p + (lg >> 1)]);
+              wa0[m] = fp4x8_bf16(cw.x, sc);
+              wa1[m] = fp4x8_bf16(cw.y, sc);
+            }
+          }
+#pragma unroll
+          for (int ms = 0; ms < NS; ++ms) {
+            if (ms >= nms) break;
+            const uint8_t* xr = sb + C::X_OFF + (ms * 16 + lr) * C::XB;
+            const bf16x8_t x0 = __builtin_bit_cast(bf16x8_t, lds16(xr + (((8 * p + 2 * lg) ^ lr) << 4)));
+            const bf16x8_t x1 = __builtin_bit_cast(bf16x8_t, lds16(xr + (((8 * p + 2 * lg + 1) ^ lr) << 4)));
+#pragma unroll
+            for (int m = 0; m < C::NMAT; ++m) {
+              f32x4_t& d = C::F8S ? pa[m * NS + ms] : acc[m * NS + ms];
+              d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa0[m], x0, d, 0, 0, 0);
+              d = __builtin_amdgcn_mfma_f32_16x16x32_bf16(wa1[m], x1, d, 0, 0, 0);
+            }
+          }
+        }
+        if (C::F8S) {
+#pragma unroll
+          for (int m = 0; m < C::NMAT; ++m) {
+            const float ws = *(const float*)(sb + C::WS_OFF + wave * 256 + (2 * m + h) * 4);
+#pragma unroll
+            for (int ms = 0; ms < NS; ++ms) acc[m * NS + ms] += pa[m * NS + ms] * ws;
           }
         }
       }
@@ -732,7 +834,7 @@ template <int FMT, bool GATED, int NS>
 hipError_t launch_dec(int n_cu, const WorkList* wl, const int32_t* counts, const int32_t* offsets,
                       const uint8_t* pool, size_t S, size_t woff0, size_t woff1, size_t soff0, size_t soff1,
                       const void* X, const void* Xs, const int32_t* row_tok, int K, int N, void* out, f32x4_t* part,
-                      int fix, hipStream_t s) {
+                      size_t part_bytes, int fix, int* err, hipStream_t s) {
   using C = Cfg<FMT, GATED, NS>;
   static int per_cu = 0;     // resident workgroups per CU for this instance
   const size_t lds = (size_t)C::NST * C::STAGE;
@@ -747,15 +849,23 @@ hipError_t launch_dec(int n_cu, const WorkList* wl, const int32_t* counts, const
   }
   int grid = n_cu * per_cu;
   if (grid > MAX_BLOCKS) grid = MAX_BLOCKS - MAX_BLOCKS % N_XCD;
+  // the partial tiles of 2 items per workgroup must fit the caller's buffer
+  const size_t per_wg = (size_t)2 * NW * C::NACC * 64 * sizeof(f32x4_t);
+  if (fix >= 0 && (size_t)grid * per_wg > part_bytes) {
+    grid = (int)(part_bytes / per_wg);
+    if (grid >= N_XCD) grid -= grid % N_XCD;
+    if (grid < 1) return hipErrorInvalidValue;
+  }
   if (fix < 0)      // one workgroup per item: a grid of -fix workgroups, no partial tiles
     gemm_dec<FMT, GATED, NS><<<-fix, 256, lds, s>>>(wl, counts, offsets, pool, S, woff0, woff1, soff0, soff1,
                                                     (const uint8_t*)X, (const uint8_t*)Xs, row_tok, K, N, out,
-                                                    nullptr);
+                                                    nullptr, err);
   else if (fix)
     gemm_dec_fix<FMT, GATED, NS><<<grid, 256, 0, s>>>(wl, counts, offsets, pool, S, K, N, grid, out, part);
   else
     gemm_dec<FMT, GATED, NS><<<grid, 256, lds, s>>>(wl, counts, offsets, pool, S, woff0, woff1, soff0, soff1,
-                                                    (const uint8_t*)X, (const uint8_t*)Xs, row_tok, K, N, out, part);
+                                                    (const uint8_t*)X, (const uint8_t*)Xs, row_tok, K, N, out, part,
+                                                    err);
   return hipGetLastError();
 }
 
@@ -763,11 +873,11 @@ template <int FMT, bool GATED>
 hipError_t launch_ns(int ns, int n_cu, const WorkList* wl, const int32_t* counts, const int32_t* offsets,
                      const uint8_t* pool, size_t S, size_t woff0, size_t woff1, size_t soff0, size_t soff1,
                      const void* X, const void* Xs, const int32_t* row_tok, int K, int N, void* out, f32x4_t* part,
-                     int fix, hipStream_t s) {
-#define MOE_DEC_ARGS n_cu, wl, counts, offsets, pool, S, woff0, woff1, soff0, soff1, X, Xs, row_tok, K, N, out, part, fix, s
+                     size_t part_bytes, int fix, int* err, hipStream_t s) {
+#define MOE_DEC_ARGS n_cu, wl, counts, offsets, pool, S, woff0, woff1, soff0, soff1, X, Xs, row_tok, K, N, out, part, part_bytes, fix, err, s
   if (ns == 1) return launch_dec<FMT, GATED, 1>(MOE_DEC_ARGS);
   if (ns == 2) return launch_dec<FMT, GATED, 2>(MOE_DEC_ARGS);
-  if constexpr (FMT != WFMT_MXFP4) {
+  if constexpr (FMT != WFMT_MXFP4 && FMT != WFMT_FP8_A16) {     // 64-token blocks exceed LDS there
     if (ns == 4) return launch_dec<FMT, GATED, 4>(MOE_DEC_ARGS);
   }
 #undef MOE_DEC_ARGS
@@ -776,32 +886,41 @@ hipError_t launch_ns(int ns, int n_cu, const WorkList* wl, const int32_t* counts
 
 }  // namespace
 
-// Bytes of the partial-tile buffer.
+// Bytes of a partial-tile buffer that never limits the grid.
 extern "C" size_t moe_dec_part_bytes() { return (size_t)MAX_BLOCKS * 2 * NW * 8 * 64 * sizeof(f32x4_t); }
 // Largest tokens-per-m-block choice (16 * ns) for a weight format.
-extern "C" int moe_dec_max_ns(int fmt) { return fmt == WFMT_MXFP4 ? 2 : 4; }
+extern "C" int moe_dec_max_ns(int fmt) { return fmt == WFMT_MXFP4 || fmt == WFMT_FP8_A16 ? 2 : 4; }
 
 // ns: 16-token sub-tiles per m-block (1, 2 or 4; 1 or 2 for MXFP4); the work
 // list must have been built with m-blocks of 16*ns tokens.  N must be a
 // multiple of 64; K a multiple of 128.  For the 8-bit formats X holds the
 // quantised rows in grouped order (row_tok must be null).  The stream leaves
-// the items cut between workgroups as partial tiles in `part`; the same call
-// with fix = 1 (same arguments, next on the stream) adds and stores them.
+// the items cut between workgroups as partial tiles in `part` (part_bytes
+// long: a smaller buffer caps the grid at the workgroups whose tiles fit);
+// the same call with fix = 1 (same arguments, next on the stream) adds and
+// stores them.
 // fix = -n: one workgroup per item on a grid of n workgroups (n at least the
-// number of items), no partial tiles and no second call.
+// number of items, else bit 1 of *err is set and nothing is written), no
+// partial tiles and no second call.
 extern "C" hipError_t moe_launch_gemm_dec(int fmt, int gated, int ns, int n_cu, const WorkList* wl,
                                           const int32_t* counts, const int32_t* offsets, const uint8_t* pool,
                                           size_t S, size_t woff0, size_t woff1, size_t soff0, size_t soff1,
                                           const void* X, const void* Xs, const int32_t* row_tok, int K, int N,
-                                          void* out, void* part, int fix, hipStream_t s) {
-  if (N % ROWS || K % 128 || (fmt != WFMT_BF16 && fmt != WFMT_NVFP4 && row_tok)) return hipErrorInvalidValue;
+                                          void* out, void* part, size_t part_bytes, int fix, int* err,
+                                          hipStream_t s) {
+  const bool x16 = fmt == WFMT_BF16 || fmt == WFMT_NVFP4 || fmt == WFMT_FP8_A16 || fmt == WFMT_MXFP4_A16;
+  if (N % ROWS || K % 128 || (!x16 && row_tok)) return hipErrorInvalidValue;
   f32x4_t* p = (f32x4_t*)part;
   const int f = fix;
-#define MOE_DEC_ARGS ns, n_cu, wl, counts, offsets, pool, S, woff0, woff1, soff0, soff1, X, Xs, row_tok, K, N, out, p, f, s
+#define MOE_DEC_ARGS ns, n_cu, wl, counts, offsets, pool, S, woff0, woff1, soff0, soff1, X, Xs, row_tok, K, N, out, p, part_bytes, f, err, s
   if (fmt == WFMT_BF16) return gated ? launch_ns<WFMT_BF16, true>(MOE_DEC_ARGS) : launch_ns<WFMT_BF16, false>(MOE_DEC_ARGS);
   if (fmt == WFMT_FP8) return gated ? launch_ns<WFMT_FP8, true>(MOE_DEC_ARGS) : launch_ns<WFMT_FP8, false>(MOE_DEC_ARGS);
   if (fmt == WFMT_NVFP4)
     return gated ? launch_ns<WFMT_NVFP4, true>(MOE_DEC_ARGS) : launch_ns<WFMT_NVFP4, false>(MOE_DEC_ARGS);
+  if (fmt == WFMT_FP8_A16)
+    return gated ? launch_ns<WFMT_FP8_A16, true>(MOE_DEC_ARGS) : launch_ns<WFMT_FP8_A16, false>(MOE_DEC_ARGS);
+  if (fmt == WFMT_MXFP4_A16)
+    return gated ? launch_ns<WFMT_MXFP4_A16, true>(MOE_DEC_ARGS) : launch_ns<WFMT_MXFP4_A16, false>(MOE_DEC_ARGS);
   if (fmt != WFMT_MXFP4) return hipErrorInvalidValue;
   return gated ? launch_ns<WFMT_MXFP4, true>(MOE_DEC_ARGS) : launch_ns<WFMT_MXFP4, false>(MOE_DEC_ARGS);
 #undef MOE_DEC_ARGS

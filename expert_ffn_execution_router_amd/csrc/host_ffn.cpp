@@ -11,6 +11,7 @@
 // no intermediate rounding.  Experts are processed in ascending id order and
 // each output element is owned by one thread, so the result is deterministic.
 #include <atomic>
+#include <chrono>
 #include <cmath>
 #include <cstdint>
 #include <cstring>
@@ -156,6 +157,9 @@ struct HostPool {
   uint64_t gen = 0;
   int running = 0;
   bool stop = false;
+  // one job at a time: held from host_ffn_start to host_ffn_wait
+  std::mutex job_mu;
+  std::chrono::steady_clock::time_point t_start, t_done;
   // spin barrier for phases inside a job
   std::atomic<int> bar_count{0};
   std::atomic<int> bar_gen{0};
@@ -185,7 +189,10 @@ struct HostPool {
       f(id);
       {
         std::lock_guard<std::mutex> g(mu);
-        if (--running == 0) done_cv.notify_all();
+        if (--running == 0) {
+          t_done = std::chrono::steady_clock::now();
+          done_cv.notify_all();
+        }
       }
     }
   }
@@ -195,12 +202,15 @@ struct HostPool {
       job = std::move(f);
       running = n;
       ++gen;
+      t_start = std::chrono::steady_clock::now();
     }
     cv.notify_all();
   }
-  void wait() {
+  // duration of the finished job in ms
+  double wait() {
     std::unique_lock<std::mutex> g(mu);
     done_cv.wait(g, [&] { return running == 0; });
+    return std::chrono::duration<double, std::milli>(t_done - t_start).count();
   }
   void barrier() {
     const int g = bar_gen.load(std::memory_order_acquire);
@@ -317,11 +327,14 @@ HostFfnHandle* host_ffn_start(HostPool* P, const HostFfnShape& sh, const uint8_t
   W.nC = nC;
   W.out = out;
   HostFfnWork* wp = &W;
+  P->job_mu.lock();                 // released by host_ffn_wait on this thread
   P->start([P, wp](int id) { host_ffn_worker(P, wp, id); });
   return h;
 }
 
-void host_ffn_wait(HostPool* P, HostFfnHandle* h) {
-  P->wait();
+double host_ffn_wait(HostPool* P, HostFfnHandle* h) {
+  const double ms = P->wait();
   delete h;
+  P->job_mu.unlock();
+  return ms;
 }

@@ -97,6 +97,12 @@ class MoeRuntime:
         self._chk(B.moe_calibrate(self.ctx, ctypes.byref(bp), ctypes.byref(bh)))
         return bp.value, bh.value
 
+    def calibrate_ex(self, T=1):
+        """Bandwidth calibration with its breakdown (dict of moe_calibration)."""
+        m = B.moe_calibration()
+        self._chk(B.moe_calibrate_ex(self.ctx, T, ctypes.byref(m)))
+        return m.as_dict()
+
     def reset_cache(self, stream=None):
         self._chk(B.moe_reset_cache(self.ctx, self.stream_ptr(stream)))
 

@@ -145,23 +145,54 @@ int moe_set_activations(moe_ctx* ctx, int act);
 /* Miss policy and the bandwidths (GB/s) q* uses (section 2.5). */
 int moe_set_policy(moe_ctx* ctx, int policy, double B_P, double B_H);
 
-/* Startup calibration on the deployed shapes (section 2.5, section 3 Table 1):
- * B_P = pinned-host -> slot copy rate of whole experts, B_H = effective
- * weight-byte rate of the host FFN with the configured threads, both GB/s.
- * Uses the least recently used slots as copy targets and leaves them empty.
- * Synchronous. */
+/* Startup calibration on the deployed shapes (section 2.5, section 3 Table 1).
+ * B_P: rate of whole-expert copies pinned host pool -> slot (median of 5
+ * rounds of up to 8 copies from distinct pool rows into the highest slots,
+ * which are emptied first and left empty).  The host branch is timed as the
+ * decode path calls it: one expert, T tokens routed to it, the configured
+ * threads, weight bytes per second of the call; after a warm-up (at least
+ * 8 calls and 100 ms), 40 calls over (layer, expert) pairs spread over the
+ * pool, so no call finds its bytes in the host caches, first alone
+ * (host_alone) and then while a train of copies keeps the link busy
+ * (host_conc: calls that end inside the train).
+ * Section 2.5 splits the miss set so that the fills, at B_P, and the host
+ * branch, on the residual B_R = B_H - B_P, end together; B_R is measured
+ * here as host_conc (host_alone when fewer than 3 calls ran inside the
+ * train), and B_H = B_P + B_R.  All rates GB/s; medians with min and max.
+ * Synchronous.  INVAL for T outside [1, max_tokens]; HIP. */
+typedef struct {
+  double B_P, B_P_min, B_P_max;                     /* pinned -> slot copies */
+  double B_H;                                       /* B_P + B_R, the value q* uses */
+  double host_alone, host_alone_min, host_alone_max;
+  double host_conc, host_conc_min, host_conc_max;   /* with the link busy */
+  int n_copy, n_host_alone, n_host_conc;            /* timed repeats behind each median */
+} moe_calibration;
+int moe_calibrate_ex(moe_ctx* ctx, int T, moe_calibration* out);
+
+/* The same at T = 1 (single-stream decode), returning B_P and B_H. */
 int moe_calibrate(moe_ctx* ctx, double* B_P, double* B_H);
 
-/* Device int32 [L*E] residency table: slot of (l, e) or -1. */
+/* Device int32 [L*E] residency table: slot of (l, e) or -1.  Review section 2:
+ * every slot holds all tensors of one (layer, expert) pair and residency and
+ * lookup go by that logical id alone; section 2.6: the control kernel
+ * rewrites logical expert ids to physical slot ids.  Owned by the context
+ * (inside the workspace); valid until moe_destroy; NULL for a NULL ctx. */
 int32_t* moe_slot_table(moe_ctx* ctx);
 
 /* Empties the cache (every slot free, table -1) and clears the device error
  * flag; enqueued on stream. */
 int moe_reset_cache(moe_ctx* ctx, void* stream);
 
-/* Router: logits z = hidden router_w^T + bias (fp32), top-k by logit (larger
- * first, ties to the lower expert id), weights = softmax over the chosen
- * logits.  topk_ids int32 [T, k], topk_w fp32 [T, k] (device). */
+/* Router (gpts24, "MoE 模型为什么会造出一个 PCIe 带宽问题": a gate network
+ * picks a small subset of experts per incoming token; review section 1: each
+ * token activates k of E routed experts).  The pages give no gate formula;
+ * the reading taken: logits z = hidden router_w^T + bias (fp32), top-k by
+ * logit (larger first, ties to the lower expert id), weights = softmax over
+ * the chosen logits (the full softmax renormalised over the k).  hidden
+ * device bf16 [T, H]; router_w device fp32 [E, H]; router_bias device fp32
+ * [E] or NULL; topk_ids int32 [T, k], topk_w fp32 [T, k] (device,
+ * caller-owned).  Asynchronous on stream; INVAL for T outside [0,
+ * max_tokens], HIP on a launch failure. */
 int moe_route(moe_ctx* ctx, const void* hidden, const float* router_w, const float* router_bias, int T,
               int32_t* topk_ids, float* topk_w, void* stream);
 
@@ -192,7 +223,10 @@ int moe_route(moe_ctx* ctx, const void* hidden, const float* router_w, const flo
 int moe_quantize(int wfmt, int src_bf16, const void* src, int rows, int cols, const int32_t* row_map, uint8_t* q,
                  void* scale, void* stream);
 
-/* Same selection from given fp32 logits [T, E] (device), plus the grouping:
+/* Same selection from given fp32 logits [T, E] (device), plus the grouping
+ * that the grouped evaluation of the GPU set needs (review section 2.5:
+ * the GPU evaluates its experts as groups; section 2.6: the routed experts
+ * are de-duplicated on the device).  Test hook for bit-exact routing:
  * counts int32 [E], offsets int32 [E+1] (exclusive scan), perm_tok int32 [T*k]
  * (token of each grouped row: experts ascending, tokens ascending within an
  * expert), pos int32 [T, k] (grouped row of each choice).  All device. */
@@ -210,18 +244,31 @@ int moe_route_from_logits(moe_ctx* ctx, const float* logits, int T, int32_t* top
 int moe_plan(moe_ctx* ctx, int layer, const int32_t* topk_ids, int T, uint32_t* miss_mask_out,
              moe_plan_info* info, int32_t* fill_experts, int32_t* fill_slots, void* stream);
 
-/* Copies expert (layer, experts[i]) from the host pool into slots[i] on
- * copy_stream (n whole-expert DMAs of S bytes) and records the context's
- * fill event, which the next forward on any stream waits for. */
+/* Fill of the set F (review section 2.5: the misses chosen for the GPU are
+ * copied into their cache slots in one batch; section 2.6: one source /
+ * destination table for every bank).  Copies expert (layer, experts[i])
+ * from the host pool into slots[i] on copy_stream (n whole-expert DMAs of
+ * S bytes) and records the context's fill event, which the next forward
+ * on any stream waits for.  experts, slots: host int32 [n]; the residency
+ * table is NOT changed (moe_plan already rewrote it).  INVAL for a layer,
+ * expert or slot out of range; HIP on a copy failure. */
 int slot_pool_fill(moe_ctx* ctx, int layer, const int32_t* experts, const int32_t* slots, int n, void* copy_stream);
 
-/* LRU admission of the given experts of a layer (host int32 [n]): already
- * resident ones are refreshed, the others take the least recently used
- * slots and are copied from the host pool on copy_stream.  Blocks until the
- * admission plan is known (not until the copies end). */
+/* LRU admission (review section 2.4: one global LRU over every layer's
+ * experts; a hit refreshes the expert's recency, a miss installs it in place
+ * of the least recently needed one).  experts: host int32 [n] of this
+ * layer, n <= 8192: already resident ones are refreshed, the others take
+ * the least recently used slots and are copied from the host pool on
+ * copy_stream.  Blocks until the admission plan is known (not until the
+ * copies end).  NOSLOTS when fewer evictable slots than experts remain
+ * (the ones that fit are still installed); INVAL for bad ids. */
 int slot_pool_admit(moe_ctx* ctx, int layer, const int32_t* experts, int n, void* copy_stream);
 
-/* Drops the given experts of a layer (host int32 [n]) from the cache. */
+/* Eviction (review section 2.4: the LRU drops what the model needed least
+ * recently; section 2.7: the cache is reshaped under a new memory budget).
+ * Drops the given experts of a layer (host int32 [n], n <= 8192; absent
+ * ones are ignored) from the cache: their slots become free (stamp 0).
+ * Synchronous on the null stream; INVAL for bad ids. */
 int slot_pool_evict(moe_ctx* ctx, int layer, const int32_t* experts, int n);
 
 /* Rebuilds the expert cache under a new slot budget at a safe point (review
@@ -253,7 +300,10 @@ int moe_host_ffn(const moe_config* cfg, const void* host_pool, int layer, const 
                  const int32_t* topk_ids, const float* topk_w, int T, const uint32_t* miss_mask,
                  float* host_partial_out);
 
-/* The routed MoE layer forward on the GPU:
+/* The routed MoE layer forward on the GPU (review section 2.5: the GPU
+ * evaluates its set G = H u F as groups while the host computes C; the two
+ * partial sums are added, so the layer output is the plain MoE output;
+ * section 2: slot contents change speed, never the result):
  *   out[t] = bf16( sum_{j: e_tj not in mask} w_tj * FFN_e(hidden[t]) + host_partial[t] )
  * routing as moe_route; experts found through slot_table (device int32 [E],
  * this layer's row: slot or -1) in the context's slot pool; miss_mask
@@ -300,7 +350,8 @@ int moe_decode_layer_async(moe_ctx* ctx, int layer, const void* hidden, const fl
 /* Running totals of every plan of the context (device counters, summed by
  * the cache-control kernel): planning calls, routed distinct experts, hits,
  * misses m, fills q, host executions m - q, evictions of a resident expert;
- * host_ms: wall time of the asynchronous path's host-branch callbacks. */
+ * host_ms: time the host branches of both decode paths took on the thread
+ * pool (from the pool taking the job to its last worker finishing). */
 typedef struct moe_plan_totals {
   long long calls, n_unique, n_hit, m, q, n_host, n_evict;
   double host_ms;
@@ -326,7 +377,11 @@ int prefill_stream_layer(moe_ctx* ctx, int layer, const void* hidden, const floa
                          int double_buffer);
 
 /* Reads and clears the device error flag (synchronous): MOE_OK or
- * MOE_E_NOT_RESIDENT. */
+ * MOE_E_NOT_RESIDENT.  Review section 2.6: the control kernel maps every
+ * routed expert to a slot or to the host marker; a routed expert that a
+ * forward finds with neither (a caller that skipped the plan or evicted
+ * too early), or a small-batch GEMM launched with fewer workgroups than its
+ * items, sets the flag instead of reading a wrong slot. */
 int moe_check_device_error(moe_ctx* ctx);
 
 /* Per-stage GPU timing (the pages time stages by wall clock only; this hook

@@ -64,12 +64,20 @@ class Setup:
         x = synth.hidden(self.cfg, self.seed, T, tag)
         return x, torch.from_numpy(x.view(np.int16)).cuda()
 
+    def act_of(self, T):
+        """Activation rule of a call of T tokens: the large-batch kernels
+        quantise fp8 / MXFP4 activations (E4M3 per 128, MXFP8, or MXFP6 when
+        selected); the small-batch kernels take bf16 activations."""
+        if self.tiled(T):
+            return self.act
+        return "bf16" if self.cfg.fmt in (1, 2) else None
+
     def oracle(self, layer, x_bits, mode="mirrored", rows=None, T=None):
-        """T: tokens of the GPU call (default len(x_bits)); the MXFP6 variant
-        applies only where that call ran the large-batch GEMMs."""
+        """T: tokens of the GPU call (default len(x_bits)), which decides the
+        activation rule (act_of)."""
         xs = x_bits if rows is None else x_bits[rows]
         T = len(x_bits) if T is None else T
-        act = self.act if self.tiled(T) else None
+        act = self.act_of(T)
         return M.moe_layer(xs, self.R[layer], self.b[layer], self.cfg.k, self.weights(layer), fmt=self.cfg.fmt,
                            mode=mode, act=act)
 
@@ -96,9 +104,21 @@ def rel_err(got, ref, rows=None):
     return float(np.abs(got - ref).max() / denom) if denom > 0 else float(np.abs(got).max())
 
 
+def exact_bound(setup, T, e_q, tol):
+    """Bound on the error against the exact layer: the tolerance itself
+    wherever the activations stay 16-bit; with quantised activations (the
+    large-batch fp8 / MXFP4 kernels) the quantisation's own cost e_q (the
+    mirrored oracle's distance from the exact one, fp64, same inputs) plus
+    the tolerance."""
+    act = setup.act_of(T)
+    sixteen = act == "bf16" or (act is None and setup.cfg.fmt in (0, 3))
+    return tol if sixteen else e_q + tol
+
+
 def compare(setup, layer, x_bits, out_t, tol=None):
-    """Checks a GPU layer output against the mirrored oracle on tokens whose
-    top-k margin is >= MARGIN; returns (err_mirrored, err_exact, n_rows)."""
+    """Checks a GPU layer output against the mirrored oracle and the exact
+    oracle on tokens whose top-k margin is >= MARGIN; returns (err_mirrored,
+    err_exact, n_rows)."""
     ref = setup.oracle(layer, x_bits, "mirrored")
     ex = setup.oracle(layer, x_bits, "exact")
     rows = np.nonzero(ref["margin"] >= MARGIN)[0]
@@ -107,4 +127,6 @@ def compare(setup, layer, x_bits, out_t, tol=None):
     e_x = rel_err(got, ex["out"], rows)
     t = TOL[setup.cfg.fmt] if tol is None else tol
     assert e_m <= t, (e_m, e_x, len(rows))
+    e_q = rel_err(ref["out"], ex["out"], rows)
+    assert e_x <= exact_bound(setup, len(x_bits), e_q, t), (e_m, e_x, e_q, len(rows))
     return e_m, e_x, len(rows)

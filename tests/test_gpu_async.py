@@ -10,7 +10,7 @@ import torch
 from oracle import cache as OC
 from oracle import moe as M
 from expert_ffn_execution_router_amd import binding as B
-from gpu_util import MARGIN, TOL, Setup, bf16_to_np, compare, rel_err, shape
+from gpu_util import exact_bound, MARGIN, TOL, Setup, bf16_to_np, compare, rel_err, shape
 
 pytestmark = pytest.mark.gpu
 
@@ -41,11 +41,15 @@ def _device_ids(s, layer, xd):
 def _check_oracle(s, layer, x, out, host_set):
     """The mirrored oracle with the plan's host set evaluated exactly (the
     host branch keeps fp32 and the weights' exact values)."""
-    ref = M.moe_layer(x, s.R[layer], s.b[layer], s.cfg.k, s.weights(layer), fmt=s.cfg.fmt, mode="mirrored",
-                      host_set=host_set)
+    T = len(x)
+    ref = M.moe_layer(x, s.R[layer], s.b[layer], s.cfg.k, s.weights(layer), fmt=s.cfg.fmt, mode="both",
+                      host_set=host_set, act=s.act_of(T))
     rows = np.nonzero(ref["margin"] >= MARGIN)[0]
     assert len(rows) > 0
-    assert rel_err(bf16_to_np(out), ref["out"], rows) <= TOL[s.cfg.fmt]
+    got = bf16_to_np(out)
+    assert rel_err(got, ref["out"], rows) <= TOL[s.cfg.fmt]
+    e_q = rel_err(ref["out"], ref["out_exact"], rows)
+    assert rel_err(got, ref["out_exact"], rows) <= exact_bound(s, T, e_q, TOL[s.cfg.fmt])
 
 
 @pytest.mark.parametrize("fmt,n_slots,policy,T", [(0, 12, B.MOE_POLICY_HYBRID, 5), (0, 12, B.MOE_POLICY_OFFLOAD, 3),

@@ -247,9 +247,13 @@ def test_tiled_forward_overflow_rows(fmt, cap):
         s.R[0], s.b[0] = R, None
         xd = torch.from_numpy(bits.view(np.int16)).cuda()
         out = torch.empty(T, H, dtype=torch.bfloat16, device="cuda")
+        s.rt.profile_begin(64)
         s.rt.forward(0, xd, torch.from_numpy(R).cuda(), None, s.slot_row(0), out)
-        torch.cuda.synchronize()
+        prof = s.rt.profile_end()
         assert s.rt.check_device_error() == 0
+        # the overflow rows went through the small-batch kernel: one launch
+        # after each tiled GEMM
+        assert prof["tail"]["launches"] == 2, prof
         ids = torch.empty(T, k, dtype=torch.int32, device="cuda")
         w = torch.empty(T, k, dtype=torch.float32, device="cuda")
         s.rt.route(xd, torch.from_numpy(R).cuda(), None, ids, w)

@@ -92,3 +92,4 @@ def test_host_ffn_empty_set_is_zero(B):
     c = synth.CONFIGS[1]
     out, ref = _run_host(B, c, 8, 5, [], 2)
     assert not out.any() and not ref.any()
+
