@@ -102,6 +102,7 @@ SIGNATURES = {
     "moe_host_partial": (_i, [_vp, _i, _vp, _vp, _vp, _i, _vp, _vp]),
     "moe_host_ffn": (_i, [_P(moe_config), _vp, _i, _vp, _vp, _vp, _i, _vp, _vp]),
     "moe_layer_forward": (_i, [_vp, _i, _vp, _vp, _vp, _i, _vp, _vp, _vp, _vp, _vp]),
+    "moe_layer_forward_noalloc": (_i, [_P(moe_config), _vp, _vp, _vp, _vp, _vp, _i, _vp, _vp, _vp, _vp, _vp]),
     "moe_decode_layer": (_i, [_vp, _i, _vp, _vp, _vp, _i, _vp, _P(moe_plan_info), _vp, _vp]),
     "moe_decode_layer_async": (_i, [_vp, _i, _vp, _vp, _vp, _i, _vp, _vp, _vp]),
     "moe_plan_stats": (_i, [_vp, _P(moe_plan_totals), _i]),
@@ -177,6 +178,7 @@ slot_pool_evict = _fn("slot_pool_evict")
 moe_host_partial = _fn("moe_host_partial")
 moe_host_ffn = _fn("moe_host_ffn")
 moe_layer_forward = _fn("moe_layer_forward")
+moe_layer_forward_noalloc = _fn("moe_layer_forward_noalloc")
 moe_decode_layer = _fn("moe_decode_layer")
 moe_decode_layer_async = _fn("moe_decode_layer_async")
 moe_plan_stats = _fn("moe_plan_stats")

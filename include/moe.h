@@ -315,6 +315,31 @@ int moe_layer_forward(moe_ctx* ctx, int layer, const void* hidden, const float* 
                       int T, const int32_t* slot_table, const uint32_t* miss_mask, const float* host_partial,
                       void* out, void* stream);
 
+/* Allocation-free moe_layer_forward, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation.  No context: cfg gives the shape (L,
+ * n_slots, max_tokens and host_threads are ignored); slot_pool (device)
+ * holds experts in cfg's blob layout; slot_row (device int32 [E]) maps this
+ * layer's experts to slots (-1 = absent); the other arguments are those of
+ * moe_layer_forward, whose kernels it runs.  Every intermediate lives in one
+ * static device array of 40 MiB per GPU, held until the process ends;
+ * limits: T <= 64, and a shape whose forward buffers leave at least 4 MiB of
+ * the array for the small-batch GEMMs' partial tiles (every shape up to
+ * E = 256, k = 8, H = 6144, I = 2048 fits); otherwise MOE_E_UNSUPPORTED,
+ * before any device work.  Calls no allocator.  err_flag (device int, may be
+ * NULL): error bits are OR-ed into it (bit 0: a routed, unmasked expert
+ * without a slot, left out); the caller clears it.  The array keeps the last
+ * call's contents; a call writes every part of it that it reads before
+ * reading it, so nothing needs clearing between calls.  All calls on one
+ * GPU share the array: calls that overlap in time on one GPU (several
+ * streams, several host threads) race, so the caller orders them.
+ * Asynchronous on stream; errors INVAL, UNSUPPORTED, HIP (message in
+ * moe_last_error(NULL)). */
+int moe_layer_forward_noalloc(const moe_config* cfg, const void* slot_pool, const int32_t* slot_row,
+                              const void* hidden, const float* router_w, const float* router_bias, int T,
+                              const uint32_t* miss_mask, const float* host_partial, void* out, int* err_flag,
+                              void* stream);
+
 /* One decode-time layer through the cache (sections 2.4-2.6): route, plan
  * (host sync once), start the host branch on C, fill F on copy_stream,
  * grouped GPU evaluation of H u F on compute_stream, add the host partial.

@@ -93,3 +93,26 @@ def test_host_ffn_empty_set_is_zero(B):
     out, ref = _run_host(B, c, 8, 5, [], 2)
     assert not out.any() and not ref.any()
 
+
+def test_noalloc_forward_rejects_before_device_work(B):
+    """The allocation-free forward's limits are checked on the host before
+    any HIP call (so this runs without a GPU, and never launches a kernel):
+    T above 64, a shape whose forward buffers exceed its static scratch, a
+    bad shape, a missing argument."""
+    buf = (ctypes.c_uint8 * 64)()
+    p = ctypes.addressof(buf)
+    cfg = B.make_config(1, 8, 2, 256, 128, 0, 0, 64)
+    assert B.moe_layer_forward_noalloc(ctypes.byref(cfg), p, p, p, p, None, 65, None, None, p, None, None) \
+        == B.MOE_E_UNSUPPORTED
+    # Z alone would take 513 rows * 65536 * 2 bytes = 67 MB of the 40 MiB
+    huge = B.make_config(1, 256, 8, 65536, 8192, 0, 0, 64)
+    assert B.moe_layer_forward_noalloc(ctypes.byref(huge), p, p, p, p, None, 16, None, None, p, None, None) \
+        == B.MOE_E_UNSUPPORTED
+    assert "scratch" in B.last_error()
+    bad = B.make_config(1, 8, 2, 100, 128, 0, 0, 64)
+    assert B.moe_layer_forward_noalloc(ctypes.byref(bad), p, p, p, p, None, 16, None, None, p, None, None) \
+        == B.MOE_E_INVAL
+    assert B.moe_layer_forward_noalloc(None, p, p, p, p, None, 16, None, None, p, None, None) == B.MOE_E_INVAL
+    assert B.moe_layer_forward_noalloc(ctypes.byref(cfg), p, None, p, p, None, 16, None, None, p, None, None) \
+        == B.MOE_E_INVAL
+    assert B.moe_layer_forward_noalloc(ctypes.byref(cfg), p, p, p, p, None, 0, None, None, p, None, None) == 0
