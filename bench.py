@@ -72,6 +72,9 @@ def parse():
     ap.add_argument("--small-T", type=lambda v: [int(t) for t in v.split(",") if t], default=[1, 8, 32],
                     help="extra resident decode batch sizes timed on the same runtime (comma list, empty: none)")
     ap.add_argument("--e2e-T", type=int, default=1, help="tokens per step through the slot cache")
+    ap.add_argument("--e2e-Ts", type=lambda v: [int(t) for t in v.split(",") if t], default=[8, 32, 64],
+                    help="further batch sizes through the slot cache, short runs (comma list, empty: none)")
+    ap.add_argument("--e2e-T-steps", type=int, default=8, help="timed steps of each --e2e-Ts run")
     ap.add_argument("--e2e-warmup", type=int, default=16)
     ap.add_argument("--e2e-steps", type=int, default=32)
     ap.add_argument("--prefill-T", type=int, default=8192)
@@ -412,6 +415,58 @@ def phase_e2e(w: Workload):
     res["host_pred_over_measured"] = res["t_host_pred_us_per_layer"] / max(res["host_branch_us_per_layer"], 1e-9)
     res["device_cache_control"] = e2e_async(w, rc, hid, outs)
     log(json.dumps(res))
+    rc.close()
+    del rc
+    torch.cuda.empty_cache()
+    if args.e2e_Ts:
+        res["by_T"] = {str(t): e2e_at(w, t, bp, bh) for t in args.e2e_Ts}
+    return res
+
+
+def e2e_at(w: Workload, T, bp, bh):
+    """Decode at a larger batch through the same 40% cache (HYBRID with the
+    same calibrated bandwidths), cold start, a short run: --e2e-T-steps
+    timed steps after half as many warm-up steps, each on its own rows."""
+    import torch
+    import synth
+    from expert_ffn_execution_router_amd import binding as B
+    args, c = w.args, w.cfg
+    L = c.L
+    K = args.e2e_T_steps
+    W = max(1, K // 2)
+    keys = synth.decode_row_keys(c, args.seed + 2 + T, W + K, T)
+    hid = torch.from_numpy(synth.hidden_rows(c, keys.reshape(-1)).reshape(W + K, L, T, c.H).view(np.int16)).to(w.dev)
+    outs = torch.empty(L, T, c.H, dtype=torch.bfloat16, device=w.dev)
+    rc = w.runtime(c.n_slots, max(T, 64))
+    rc.set_policy(B.MOE_POLICY_HYBRID, bp, bh)
+    copy = torch.cuda.Stream()
+    infos = []
+    for s in range(W + K):
+        if s == W:
+            torch.cuda.synchronize()
+            rc.plan_stats(reset=True)
+            t0 = time.perf_counter()
+        for l in range(L):
+            info = rc.decode_layer(l, hid[s, l], w.R[l], w.bias[l], outs[l], copy_stream=copy)
+            if s >= W:
+                infos.append(info.as_dict())
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    tot = rc.plan_stats(reset=True)
+    assert rc.check_device_error() == 0
+    uq = sum(i["n_unique"] for i in infos)
+    n = len(infos)
+    res = {
+        "T": T, "warmup_steps": W, "steps": K, "ms_per_step": el / K * 1e3,
+        "moe_layer_tokens_per_s": K * L * T / el,
+        "hit_rate": sum(i["n_hit"] for i in infos) / max(uq, 1),
+        "unique_experts_per_layer": uq / n, "misses_per_layer": sum(i["m"] for i in infos) / n,
+        "fills_per_layer": sum(i["q"] for i in infos) / n, "host_per_layer": sum(i["n_host"] for i in infos) / n,
+        "t_fill_pred_us_per_layer": sum(i["t_fill_pred_us"] for i in infos) / n,
+        "t_host_pred_us_per_layer": sum(i["t_host_pred_us"] for i in infos) / n,
+        "host_branch_us_per_layer": tot["host_ms"] * 1e3 / n,
+    }
+    log(f"decode through the cache at T={T}: {json.dumps(res)}")
     rc.close()
     del rc
     torch.cuda.empty_cache()

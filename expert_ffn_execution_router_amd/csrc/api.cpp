@@ -1170,22 +1170,31 @@ int moe_calibrate_ex(moe_ctx* c, int T, moe_calibration* out) {
     lo = v.front();
     hi = v.back();
   };
-  // the host branch on one expert for T tokens (every token routed to it),
-  // as the decode path calls it; distinct (layer, expert) pairs spread over
-  // the pool, so no call reads bytes a previous one left in the host caches
+  // the host branch on a group of G = min(k, E) distinct experts of one
+  // layer, each with all T tokens routed to it: at T = 1 the job the decode
+  // path hands the host when all of a token's experts miss.  A single expert
+  // at T = 1 runs for tens of microseconds, where the pool's wake-up and the
+  // host's scheduling noise are a large share of the time.  Groups walk
+  // (layer, expert) pairs spread over the pool, so no call finds its bytes
+  // in the host caches.
+  const int G = std::min(g.k, g.E);
   std::vector<uint16_t> hid((size_t)T * g.H, 0x3f80);
   std::vector<int32_t> ids((size_t)T * g.k, -1);
   std::vector<float> w((size_t)T * g.k, 1.0f);
   std::vector<float> outv((size_t)T * g.H);
+  std::vector<int32_t> grp(G);
   int pair = 0;
   auto host_call = [&]() -> double {
     const int i = pair++;
-    const int l = (int)(((long)i * 5 + 1) % g.L), e = (int)(((long)i * 37 + 3) % g.E);
-    for (int t = 0; t < T; ++t) ids[(size_t)t * g.k] = e;
+    const int l = (int)(((long)i * 5 + 1) % g.L), e0 = (int)(((long)i * 37 + 3) % g.E);
+    for (int j = 0; j < G; ++j) grp[j] = (e0 + j) % g.E;
+    std::sort(grp.begin(), grp.end());
+    for (int t = 0; t < T; ++t)
+      for (int j = 0; j < G; ++j) ids[(size_t)t * g.k + j] = grp[j];
     HostFfnHandle* h = host_ffn_start(c->pool, host_shape(g, S), c->host_pool, l, T, hid.data(), ids.data(),
-                                      w.data(), &e, 1, outv.data());
+                                      w.data(), grp.data(), G, outv.data());
     const double ms = host_ffn_wait(c->pool, h);
-    return (double)S / (ms * 1e-3) / 1e9;
+    return (double)G * S / (ms * 1e-3) / 1e9;
   };
   // warm-up until the pool's threads run at speed: at least 8 calls and
   // 100 ms (right after a large pool fill the first tens of ms run up to a
@@ -1236,7 +1245,7 @@ int moe_calibrate_ex(moe_ctx* c, int T, moe_calibration* out) {
     // the host branch while the link copies: a train of copies long enough
     // to cover the host calls (about three times their expected time); only
     // calls that end before the train does count
-    const double host_s = (n_host + 1) * (double)S / (out->host_alone * 1e9);
+    const double host_s = (n_host + 1) * (double)G * S / (out->host_alone * 1e9);
     const double copy_s = (double)S / (out->B_P * 1e9);
     const int n_train = (int)std::min(512.0, std::max(4.0 * n_cp, std::ceil(3.0 * host_s / copy_s)));
     for (int i = 0; i < n_train; ++i) HIPCHK(c, copy(i));

@@ -10,12 +10,15 @@
 // dequantised exactly, g, u, a = silu(g)*u and the down projection in fp32),
 // no intermediate rounding.  Experts are processed in ascending id order and
 // each output element is owned by one thread, so the result is deterministic.
+#include <algorithm>
 #include <atomic>
 #include <chrono>
 #include <cmath>
 #include <cstdint>
+#include <cstdlib>
 #include <cstring>
 #include <thread>
+#include <type_traits>
 #include <vector>
 #include <immintrin.h>
 #include <mutex>
@@ -53,6 +56,54 @@ const Tables& tables() {
   return t;
 }
 
+// ---------------------------------------------------------------------------
+// Row kernels.  With AVX-512 a weight row of `cols` inputs meets up to 8
+// token vectors per pass: it is dequantised in registers and multiplied with
+// no intermediate buffer.  The AVX2 baseline decodes the row once into a
+// buffer and dots it with each vector.  Input vectors are stored in the row's
+// decode order: natural for bf16 and fp8; for the E2M1 formats, within every
+// 32 inputs the 16 even ones then the 16 odd ones (the order in which the low
+// and high nibbles of 16 bytes come out).
+// ---------------------------------------------------------------------------
+// Position of input i of a row in decode order.
+inline int arranged(int fmt, int i) {
+  if (fmt < 2) return i;
+  const int w = i & 31;
+  return (i & ~31) + ((w & 1) << 4) + (w >> 1);
+}
+
+// One dequantisation row: codes, its scales and the matrix scale.
+struct Row {
+  int fmt, cols;
+  const uint8_t* q;       // bf16 values, E4M3 codes, or packed E2M1 codes
+  const float* s8;        // fp8: the row's fp32 block scales, one per 128 inputs
+  const uint8_t* sb;      // mxfp4: E8M0 per 32 inputs; nvfp4: E4M3 per 16 inputs
+  float t;                // nvfp4: matrix scale
+};
+
+Row make_row(const HostFfnShape& sh, const uint8_t* blob, int mat, int r) {
+  const int cols = mat < 2 ? sh.H : sh.I;
+  const size_t n = (size_t)sh.H * sh.I;
+  Row w{sh.fmt, cols, nullptr, nullptr, nullptr, 1.0f};
+  if (sh.fmt == 0) {
+    w.q = blob + (mat * n + (size_t)r * cols) * 2;
+  } else if (sh.fmt == 1) {
+    w.q = blob + mat * n + (size_t)r * cols;
+    w.s8 = (const float*)(blob + 3 * n) + mat * (n / 16384) + (size_t)(r / 128) * (cols / 128);
+  } else {
+    w.q = blob + mat * (n / 2) + (size_t)r * (cols / 2);
+    if (sh.fmt == 3) {
+      w.sb = blob + 3 * (n / 2) + mat * (n / 16) + (size_t)r * (cols / 16);
+      std::memcpy(&w.t, blob + 3 * (n / 2) + 3 * (n / 16) + 4 * mat, 4);
+    } else {
+      w.sb = blob + 3 * (n / 2) + mat * (n / 32) + (size_t)r * (cols / 32);
+    }
+  }
+  return w;
+}
+
+// ---- AVX2 (the x86-64-v3 baseline): decode the row, then dot -----------
+
 // Eight E2M1 codes (one per byte of the low 8 bytes of c8) as floats times
 // s: magnitude from a register table, sign bit moved to bit 31.
 inline __m256 e2m1x8(__m128i c8, __m256 lut, __m256 s) {
@@ -60,19 +111,6 @@ inline __m256 e2m1x8(__m128i c8, __m256 lut, __m256 s) {
   const __m256 mag = _mm256_permutevar8x32_ps(lut, idx);               // low 3 bits select
   const __m256i sgn = _mm256_slli_epi32(_mm256_and_si256(idx, _mm256_set1_epi32(8)), 28);
   return _mm256_mul_ps(_mm256_xor_ps(mag, _mm256_castsi256_ps(sgn)), s);
-}
-
-// 16 packed bytes = 32 E2M1 codes (even element in the low nibble), in
-// element order, into dst[0..32): codes 0-15 times s0, 16-31 times s1.
-inline void e2m1x32(const uint8_t* p, __m256 lut, __m256 s0, __m256 s1, float* dst) {
-  const __m128i b = _mm_loadu_si128((const __m128i*)p);
-  const __m128i m = _mm_set1_epi8(0x0F);
-  const __m128i lo = _mm_and_si128(b, m), hi = _mm_and_si128(_mm_srli_epi16(b, 4), m);
-  const __m128i e0 = _mm_unpacklo_epi8(lo, hi), e1 = _mm_unpackhi_epi8(lo, hi);   // codes 0-15, 16-31
-  _mm256_storeu_ps(dst, e2m1x8(e0, lut, s0));
-  _mm256_storeu_ps(dst + 8, e2m1x8(_mm_srli_si128(e0, 8), lut, s0));
-  _mm256_storeu_ps(dst + 16, e2m1x8(e1, lut, s1));
-  _mm256_storeu_ps(dst + 24, e2m1x8(_mm_srli_si128(e1, 8), lut, s1));
 }
 
 // Eight E4M3FN codes as floats times s: the 7 magnitude bits placed at the
@@ -86,49 +124,46 @@ inline __m256 e4m3x8(const uint8_t* p, __m256 s120) {
   return _mm256_mul_ps(_mm256_castsi256_ps(_mm256_or_si256(mag, sgn)), s120);
 }
 
-// Dequantise row `r` of matrix `mat` (0 gate, 1 up, 2 down) into dst[cols]
-// (AVX2; cols is a multiple of 128 for every format the library accepts).
-void load_row(const HostFfnShape& sh, const uint8_t* blob, int mat, int r, float* dst) {
-  const int cols = mat < 2 ? sh.H : sh.I;
-  const size_t n = (size_t)sh.H * sh.I;
+// The row's values in decode order into dst[cols].
+void decode_row_avx2(const Row& w, float* dst) {
   const Tables& tb = tables();
-  if (sh.fmt == 0) {
-    const uint16_t* w = (const uint16_t*)blob + mat * n + (size_t)r * cols;
-    for (int c = 0; c < cols; c += 8) {
-      const __m256i v = _mm256_cvtepu16_epi32(_mm_loadu_si128((const __m128i*)(w + c)));
-      _mm256_storeu_ps(dst + c, _mm256_castsi256_ps(_mm256_slli_epi32(v, 16)));
+  if (w.fmt == 0) {
+    const uint16_t* v = (const uint16_t*)w.q;
+    for (int c = 0; c < w.cols; c += 8) {
+      const __m256i x = _mm256_cvtepu16_epi32(_mm_loadu_si128((const __m128i*)(v + c)));
+      _mm256_storeu_ps(dst + c, _mm256_castsi256_ps(_mm256_slli_epi32(x, 16)));
     }
-  } else if (sh.fmt == 1) {
-    const uint8_t* q = blob + mat * n + (size_t)r * cols;
-    const float* sc = (const float*)(blob + 3 * n) + mat * (n / 16384) + (size_t)(r / 128) * (cols / 128);
+  } else if (w.fmt == 1) {
     const float p120 = std::ldexp(1.0f, 120);
-    for (int b = 0; b < cols / 128; ++b) {
-      const __m256 s = _mm256_set1_ps(sc[b] * p120);      // exact: a power-of-two factor
-      for (int c = b * 128; c < b * 128 + 128; c += 8) _mm256_storeu_ps(dst + c, e4m3x8(q + c, s));
+    for (int b = 0; b < w.cols / 128; ++b) {
+      const __m256 s = _mm256_set1_ps(w.s8[b] * p120);      // exact: a power-of-two factor
+      for (int c = b * 128; c < b * 128 + 128; c += 8) _mm256_storeu_ps(dst + c, e4m3x8(w.q + c, s));
     }
   } else {
     // E2M1 magnitudes for codes 0..7
     const __m256 lut = _mm256_setr_ps(0.0f, 0.5f, 1.0f, 1.5f, 2.0f, 3.0f, 4.0f, 6.0f);
-    const uint8_t* p = blob + mat * (n / 2) + (size_t)r * (cols / 2);
-    if (sh.fmt == 3) {
-      // NVFP4: E4M3 block scale per 16 inputs and one fp32 scale per matrix
-      const uint8_t* sc = blob + 3 * (n / 2) + mat * (n / 16) + (size_t)r * (cols / 16);
-      float t;
-      std::memcpy(&t, blob + 3 * (n / 2) + 3 * (n / 16) + 4 * mat, 4);
-      for (int b = 0; b < cols / 32; ++b)
-        e2m1x32(p + b * 16, lut, _mm256_set1_ps(tb.e4m3[sc[2 * b]] * t), _mm256_set1_ps(tb.e4m3[sc[2 * b + 1]] * t),
-                dst + b * 32);
-    } else {
-      const uint8_t* sc = blob + 3 * (n / 2) + mat * (n / 32) + (size_t)r * (cols / 32);
-      for (int b = 0; b < cols / 32; ++b) {
-        const __m256 s = _mm256_set1_ps(tb.e8m0[sc[b]]);
-        e2m1x32(p + b * 16, lut, s, s, dst + b * 32);
+    const __m128i m4 = _mm_set1_epi8(0x0F);
+    for (int b = 0; b < w.cols / 32; ++b) {
+      // 16 bytes: low nibbles = the 16 even inputs, high nibbles = the 16 odd ones
+      const __m128i x = _mm_loadu_si128((const __m128i*)(w.q + b * 16));
+      const __m128i lo = _mm_and_si128(x, m4), hi = _mm_and_si128(_mm_srli_epi16(x, 4), m4);
+      __m256 s0, s1;     // scales of inputs 0-15 and 16-31 of the block
+      if (w.fmt == 3) {
+        s0 = _mm256_set1_ps(tb.e4m3[w.sb[2 * b]] * w.t);
+        s1 = _mm256_set1_ps(tb.e4m3[w.sb[2 * b + 1]] * w.t);
+      } else {
+        s0 = s1 = _mm256_set1_ps(tb.e8m0[w.sb[b]]);
       }
+      float* d = dst + b * 32;
+      _mm256_storeu_ps(d, e2m1x8(lo, lut, s0));                        // even inputs 0..14
+      _mm256_storeu_ps(d + 8, e2m1x8(_mm_srli_si128(lo, 8), lut, s1));  // even inputs 16..30
+      _mm256_storeu_ps(d + 16, e2m1x8(hi, lut, s0));
+      _mm256_storeu_ps(d + 24, e2m1x8(_mm_srli_si128(hi, 8), lut, s1));
     }
   }
 }
 
-inline float dot(const float* a, const float* b, int n) {
+inline float dot_avx2(const float* a, const float* b, int n) {
   // n is a multiple of 128 (checked shapes): four independent 8-wide sums
   __m256 s0 = _mm256_setzero_ps(), s1 = _mm256_setzero_ps(), s2 = _mm256_setzero_ps(), s3 = _mm256_setzero_ps();
   for (int i = 0; i < n; i += 32) {
@@ -141,6 +176,141 @@ inline float dot(const float* a, const float* b, int n) {
   const __m128 h = _mm_add_ps(_mm256_castps256_ps128(s), _mm256_extractf128_ps(s, 1));
   const __m128 q = _mm_add_ps(h, _mm_movehl_ps(h, h));
   return _mm_cvtss_f32(_mm_add_ss(q, _mm_shuffle_ps(q, q, 1)));
+}
+
+// ---- AVX-512 (runtime-selected): 16 values per instruction -------------
+#define AVX512 __attribute__((target("avx512f,avx512bw,avx512dq,avx512vl")))
+
+// Sixteen consecutive values of the row in decode order starting at input c
+// (c a multiple of 16), fp8 with its block scale s120 (2^120 folded in).
+AVX512 inline __m512 fp8x16(const uint8_t* q, __m512 s120) {
+  const __m512i v = _mm512_cvtepu8_epi32(_mm_loadu_si128((const __m128i*)q));
+  const __m512i mag = _mm512_slli_epi32(_mm512_and_si512(v, _mm512_set1_epi32(0x7F)), 20);
+  const __m512i sgn = _mm512_slli_epi32(_mm512_and_si512(v, _mm512_set1_epi32(0x80)), 24);
+  return _mm512_mul_ps(_mm512_castsi512_ps(_mm512_or_si512(mag, sgn)), s120);
+}
+
+// The 32 values of E2M1 block b (16 bytes at q + 16b) in decode order: lo =
+// even inputs, hi = odd inputs, times the block's scale vector s (MXFP4: one
+// value; NVFP4: lanes 0-7 for inputs 0-15, lanes 8-15 for inputs 16-31); the
+// 16-entry table holds every signed E2M1 value.
+AVX512 inline void fp4x32(const uint8_t* q, int b, __m512 lut, __m512 s, __m512& lo, __m512& hi) {
+  const __m512i v = _mm512_cvtepu8_epi32(_mm_loadu_si128((const __m128i*)(q + b * 16)));
+  lo = _mm512_mul_ps(_mm512_permutexvar_ps(v, lut), s);                          // index: low 4 bits
+  hi = _mm512_mul_ps(_mm512_permutexvar_ps(_mm512_srli_epi32(v, 4), lut), s);
+}
+
+// The scale vector of E2M1 block b of the row (see fp4x32).
+AVX512 inline __m512 fp4_scale(const float* e4m3, const float* e8m0, const uint8_t* sb, float t, bool nv, int b) {
+  if (nv) return _mm512_insertf32x8(_mm512_set1_ps(e4m3[sb[2 * b]] * t), _mm256_set1_ps(e4m3[sb[2 * b + 1]] * t), 1);
+  return _mm512_set1_ps(e8m0[sb[b]]);
+}
+
+// The E2M1 blocks of a row against N vectors (every invariant in a register).
+template <int N, bool NV>
+AVX512 inline void fp4_dots(const uint8_t* q, const uint8_t* sb, float t, int nb, __m512 lut, const Tables& tb,
+                            const float* const* x, __m512 (*acc)[2]) {
+  for (int b = 0; b < nb; ++b) {
+    __m512 lo, hi;
+    fp4x32(q, b, lut, fp4_scale(tb.e4m3, tb.e8m0, sb, t, NV, b), lo, hi);
+#pragma unroll
+    for (int j = 0; j < N; ++j) {
+      acc[j][0] = _mm512_fmadd_ps(lo, _mm512_loadu_ps(x[j] + b * 32), acc[j][0]);
+      acc[j][1] = _mm512_fmadd_ps(hi, _mm512_loadu_ps(x[j] + b * 32 + 16), acc[j][1]);
+    }
+  }
+}
+
+// res[j] = row . xs[j] for j < N <= 8, the row dequantised in registers;
+// two accumulators per vector (even and odd halves of a block), so no FMA
+// chain waits on the previous one.
+template <int N>
+AVX512 void row_dots_avx512(const Row& w, const float* const* xs, float* res) {
+  __m512 acc[N][2];
+#pragma unroll
+  for (int j = 0; j < N; ++j) acc[j][0] = acc[j][1] = _mm512_setzero_ps();
+  if (w.fmt == 0) {
+    const uint16_t* v = (const uint16_t*)w.q;
+    for (int c = 0; c < w.cols; c += 32) {
+      const __m512i x0 = _mm512_cvtepu16_epi32(_mm256_loadu_si256((const __m256i*)(v + c)));
+      const __m512i x1 = _mm512_cvtepu16_epi32(_mm256_loadu_si256((const __m256i*)(v + c + 16)));
+      const __m512 f0 = _mm512_castsi512_ps(_mm512_slli_epi32(x0, 16));
+      const __m512 f1 = _mm512_castsi512_ps(_mm512_slli_epi32(x1, 16));
+#pragma unroll
+      for (int j = 0; j < N; ++j) {
+        acc[j][0] = _mm512_fmadd_ps(f0, _mm512_loadu_ps(xs[j] + c), acc[j][0]);
+        acc[j][1] = _mm512_fmadd_ps(f1, _mm512_loadu_ps(xs[j] + c + 16), acc[j][1]);
+      }
+    }
+  } else if (w.fmt == 1) {
+    const float p120 = std::ldexp(1.0f, 120);
+    for (int b = 0; b < w.cols / 128; ++b) {
+      const __m512 s = _mm512_set1_ps(w.s8[b] * p120);
+#pragma unroll 2
+      for (int c = b * 128; c < b * 128 + 128; c += 32) {
+        const __m512 f0 = fp8x16(w.q + c, s), f1 = fp8x16(w.q + c + 16, s);
+#pragma unroll
+        for (int j = 0; j < N; ++j) {
+          acc[j][0] = _mm512_fmadd_ps(f0, _mm512_loadu_ps(xs[j] + c), acc[j][0]);
+          acc[j][1] = _mm512_fmadd_ps(f1, _mm512_loadu_ps(xs[j] + c + 16), acc[j][1]);
+        }
+      }
+    }
+  } else {
+    // every loop-invariant in a local, so nothing is reloaded per block
+    const Tables& tb = tables();
+    const __m512 lut = _mm512_loadu_ps(tb.e2m1);
+    const uint8_t* q = w.q;
+    const uint8_t* sb = w.sb;
+    const float t = w.t;
+    const int nb = w.cols / 32;
+    const bool nv = w.fmt == 3;
+    const float* x[N];
+#pragma unroll
+    for (int j = 0; j < N; ++j) x[j] = xs[j];
+    if (nv) fp4_dots<N, true>(q, sb, t, nb, lut, tb, x, acc);
+    else fp4_dots<N, false>(q, sb, t, nb, lut, tb, x, acc);
+  }
+#pragma unroll
+  for (int j = 0; j < N; ++j) res[j] = _mm512_reduce_add_ps(_mm512_add_ps(acc[j][0], acc[j][1]));
+}
+
+// AVX-512 when the host has it (MOE_HOST_ISA=avx2 forces the baseline).
+bool use_avx512() {
+  static const bool v = [] {
+    const char* e = std::getenv("MOE_HOST_ISA");
+    if (e && std::strcmp(e, "avx2") == 0) return false;
+    __builtin_cpu_init();
+    return __builtin_cpu_supports("avx512f") && __builtin_cpu_supports("avx512bw") &&
+           __builtin_cpu_supports("avx512dq") && __builtin_cpu_supports("avx512vl");
+  }();
+  return v;
+}
+
+// res[j] = row . xs[j], j < n: with AVX-512 fused in registers, up to 8
+// vectors per pass over the row (16 accumulators; the row's 2-4 KB stay in
+// L1 between passes); else the row decoded once into buf (cols floats) and
+// dotted with each vector.
+void row_dots(const Row& w, const float* const* xs, int n, float* res, float* buf) {
+  if (use_avx512()) {
+    for (int j0 = 0; j0 < n; j0 += 8) {
+      const float* const* x = xs + j0;
+      float* r = res + j0;
+      switch (std::min(8, n - j0)) {
+        case 1: row_dots_avx512<1>(w, x, r); break;
+        case 2: row_dots_avx512<2>(w, x, r); break;
+        case 3: row_dots_avx512<3>(w, x, r); break;
+        case 4: row_dots_avx512<4>(w, x, r); break;
+        case 5: row_dots_avx512<5>(w, x, r); break;
+        case 6: row_dots_avx512<6>(w, x, r); break;
+        case 7: row_dots_avx512<7>(w, x, r); break;
+        default: row_dots_avx512<8>(w, x, r); break;
+      }
+    }
+    return;
+  }
+  decode_row_avx2(w, buf);
+  for (int j = 0; j < n; ++j) res[j] = dot_avx2(buf, xs[j], w.cols);
 }
 
 }  // namespace
@@ -227,7 +397,14 @@ HostPool* host_pool_create(int nthreads) { return new HostPool(nthreads); }
 void host_pool_destroy(HostPool* p) { delete p; }
 int host_pool_threads(const HostPool* p) { return p->n; }
 
-// Body of the host FFN for worker `id` of `nt`.  Shared scratch lives in `ws`.
+// One expert of the job: its routed (token, choice) pairs, its inputs in
+// decode order and its SwiGLU activations.
+struct ExpertJob {
+  int e = 0;
+  std::vector<int> tok, jj;
+  std::vector<float> X, A;   // [ne][H], [ne][I], each row in decode order
+};
+
 struct HostFfnWork {
   HostFfnShape sh;
   const uint8_t* pool;
@@ -238,72 +415,108 @@ struct HostFfnWork {
   const int32_t* C;
   int nC;
   float* out;
-  // scratch
-  std::vector<int> tok, jj;
-  std::vector<float> X, A;   // [n_e, H], [n_e, I]
+  std::vector<ExpertJob> ex;
 };
 
+// Worker `id` of the pool.  Phases, separated by the pool's barrier:
+//   0: zero this worker's slice of out; token lists of experts id, id+nt, ...
+//   1: the routed tokens' hidden rows, widened exactly to fp32 in decode order
+//      (the (expert, token) pairs split evenly over the workers);
+//   2: gate and up rows of every expert (the (expert, row) pairs split evenly):
+//      a = silu(g) * u per routed token, stored in decode order;
+//   3: down rows: each worker owns an H range and takes the experts in
+//      ascending order, adding w * y to out (one writer per element, a fixed
+//      order: deterministic).
 static void host_ffn_worker(HostPool* P, HostFfnWork* W, int id) {
   const HostFfnShape& sh = W->sh;
-  const int nt = P->n, H = sh.H, I = sh.I, k = sh.k;
+  const int nt = P->n, H = sh.H, I = sh.I, k = sh.k, fmt = sh.fmt, nC = W->nC;
   const size_t S = sh.S;
-  std::vector<float> row((size_t)(H > I ? H : I)), row2((size_t)H);
-  // zero own slice of out
+  std::vector<float> buf((size_t)(H > I ? H : I));
   {
     const size_t tot = (size_t)W->T * H;
     const size_t a = tot * id / nt, b = tot * (id + 1) / nt;
     std::memset(W->out + a, 0, (b - a) * sizeof(float));
   }
+  for (int ci = id; ci < nC; ci += nt) {
+    ExpertJob& x = W->ex[ci];
+    x.e = W->C[ci];
+    x.tok.clear();
+    x.jj.clear();
+    for (int t = 0; t < W->T; ++t)
+      for (int j = 0; j < k; ++j)
+        if (W->ids[(size_t)t * k + j] == x.e) {
+          x.tok.push_back(t);
+          x.jj.push_back(j);
+        }
+    x.X.resize(x.tok.size() * (size_t)H);
+    x.A.resize(x.tok.size() * (size_t)I);
+  }
   P->barrier();
-  for (int ci = 0; ci < W->nC; ++ci) {
-    const int e = W->C[ci];
-    const uint8_t* blob = W->pool + ((size_t)W->layer * sh.E + e) * S;
-    if (id == 0) {
-      W->tok.clear();
-      W->jj.clear();
-      for (int t = 0; t < W->T; ++t)
-        for (int j = 0; j < k; ++j)
-          if (W->ids[(size_t)t * k + j] == e) { W->tok.push_back(t); W->jj.push_back(j); }
-      const int ne = (int)W->tok.size();
-      W->X.resize((size_t)ne * H);
-      W->A.resize((size_t)ne * I);
-      for (int r = 0; r < ne; ++r)
+  // phase 1: hidden rows
+  {
+    long tot = 0;
+    for (int ci = 0; ci < nC; ++ci) tot += (long)W->ex[ci].tok.size();
+    const long g0 = tot * id / nt, g1 = tot * (id + 1) / nt;
+    long base = 0;
+    for (int ci = 0; ci < nC && base < g1; ++ci) {
+      ExpertJob& x = W->ex[ci];
+      const long ne = (long)x.tok.size();
+      for (long r = std::max(g0 - base, 0L); r < ne && base + r < g1; ++r) {
+        const uint16_t* src = W->hidden + (size_t)x.tok[r] * H;
+        float* dst = x.X.data() + (size_t)r * H;
         for (int h = 0; h < H; ++h) {
-          const uint32_t u = (uint32_t)W->hidden[(size_t)W->tok[r] * H + h] << 16;
-          float f;
-          std::memcpy(&f, &u, 4);
-          W->X[(size_t)r * H + h] = f;
-        }
-    }
-    P->barrier();
-    const int ne = (int)W->tok.size();
-    if (ne > 0) {
-      // gate / up rows [i0, i1)
-      const int i0 = (int)((long)I * id / nt), i1 = (int)((long)I * (id + 1) / nt);
-      for (int i = i0; i < i1; ++i) {
-        load_row(sh, blob, 0, i, row.data());
-        load_row(sh, blob, 1, i, row2.data());
-        for (int r = 0; r < ne; ++r) {
-          const float* x = &W->X[(size_t)r * H];
-          const float g = dot(row.data(), x, H);
-          const float u = dot(row2.data(), x, H);
-          W->A[(size_t)r * I + i] = g / (1.0f + std::exp(-g)) * u;
+          const uint32_t u = (uint32_t)src[h] << 16;
+          std::memcpy(dst + arranged(fmt, h), &u, 4);
         }
       }
+      base += ne;
     }
-    P->barrier();
-    if (ne > 0) {
-      const int h0 = (int)((long)H * id / nt), h1 = (int)((long)H * (id + 1) / nt);
+  }
+  P->barrier();
+  // phase 2: gate and up rows
+  {
+    const long tot = (long)nC * I;
+    const long g0 = tot * id / nt, g1 = tot * (id + 1) / nt;
+    std::vector<const float*> xs;
+    std::vector<float> gv, uv;
+    for (long g = g0; g < g1; ++g) {
+      const int ci = (int)(g / I), i = (int)(g % I);
+      ExpertJob& x = W->ex[ci];
+      const int ne = (int)x.tok.size();
+      if (ne == 0) continue;
+      xs.resize(ne);
+      gv.resize(ne);
+      uv.resize(ne);
+      for (int r = 0; r < ne; ++r) xs[r] = x.X.data() + (size_t)r * H;
+      const uint8_t* blob = W->pool + ((size_t)W->layer * sh.E + x.e) * S;
+      row_dots(make_row(sh, blob, 0, i), xs.data(), ne, gv.data(), buf.data());
+      row_dots(make_row(sh, blob, 1, i), xs.data(), ne, uv.data(), buf.data());
+      const int ai = arranged(fmt, i);
+      for (int r = 0; r < ne; ++r) x.A[(size_t)r * I + ai] = gv[r] / (1.0f + std::exp(-gv[r])) * uv[r];
+    }
+  }
+  P->barrier();
+  // phase 3: down rows, this worker's H range, experts ascending
+  {
+    const int h0 = (int)((long)H * id / nt), h1 = (int)((long)H * (id + 1) / nt);
+    std::vector<const float*> as;
+    std::vector<float> yv;
+    for (int ci = 0; ci < nC; ++ci) {
+      ExpertJob& x = W->ex[ci];
+      const int ne = (int)x.tok.size();
+      if (ne == 0) continue;
+      as.resize(ne);
+      yv.resize(ne);
+      for (int r = 0; r < ne; ++r) as[r] = x.A.data() + (size_t)r * I;
+      const uint8_t* blob = W->pool + ((size_t)W->layer * sh.E + x.e) * S;
       for (int h = h0; h < h1; ++h) {
-        load_row(sh, blob, 2, h, row.data());
+        row_dots(make_row(sh, blob, 2, h), as.data(), ne, yv.data(), buf.data());
         for (int r = 0; r < ne; ++r) {
-          const float y = dot(row.data(), &W->A[(size_t)r * I], I);
-          const int t = W->tok[r];
-          W->out[(size_t)t * H + h] += W->w[(size_t)t * k + W->jj[r]] * y;
+          const int t = x.tok[r];
+          W->out[(size_t)t * H + h] += W->w[(size_t)t * k + x.jj[r]] * yv[r];
         }
       }
     }
-    P->barrier();
   }
 }
 
@@ -326,6 +539,7 @@ HostFfnHandle* host_ffn_start(HostPool* P, const HostFfnShape& sh, const uint8_t
   W.C = C;
   W.nC = nC;
   W.out = out;
+  W.ex.resize(nC > 0 ? nC : 0);
   HostFfnWork* wp = &W;
   P->job_mu.lock();                 // released by host_ffn_wait on this thread
   P->start([P, wp](int id) { host_ffn_worker(P, wp, id); });

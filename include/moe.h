@@ -149,10 +149,11 @@ int moe_set_policy(moe_ctx* ctx, int policy, double B_P, double B_H);
  * B_P: rate of whole-expert copies pinned host pool -> slot (median of 5
  * rounds of up to 8 copies from distinct pool rows into the highest slots,
  * which are emptied first and left empty).  The host branch is timed as the
- * decode path calls it: one expert, T tokens routed to it, the configured
- * threads, weight bytes per second of the call; after a warm-up (at least
- * 8 calls and 100 ms), 40 calls over (layer, expert) pairs spread over the
- * pool, so no call finds its bytes in the host caches, first alone
+ * decode path calls it, on min(k, E) distinct experts of one layer with all
+ * T tokens routed to each (at T = 1, a token whose k experts all miss), the
+ * configured threads, weight bytes per second of the call; after a warm-up
+ * (at least 8 calls and 100 ms), 40 calls over (layer, expert) groups
+ * spread over the pool, so no call finds its bytes in the host caches, first alone
  * (host_alone) and then while a train of copies keeps the link busy
  * (host_conc: calls that end inside the train).
  * Section 2.5 splits the miss set so that the fills, at B_P, and the host
