@@ -49,7 +49,7 @@ def build(jobs: int = 8) -> str:
     procs.append(["hipcc", *HIP_FLAGS, "-c", os.path.join(CSRC, "api.cpp"), "-o", api_obj])
     host_obj = os.path.join(BUILD, "host_ffn.o")
     objs.append(host_obj)
-    procs.append(["g++", "-O3", "-march=x86-64-v3", "-std=c++17", "-fPIC", "-Wall", "-pthread",
+    procs.append(["g++", "-O3", "-march=x86-64-v3", "-std=c++20", "-fPIC", "-Wall", "-pthread",
                   "-I" + CSRC, "-c", os.path.join(CSRC, "host_ffn.cpp"), "-o", host_obj])
     # compile in parallel
     running = []

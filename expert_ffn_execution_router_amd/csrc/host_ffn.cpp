@@ -22,8 +22,6 @@
 #include <vector>
 #include <immintrin.h>
 #include <mutex>
-#include <condition_variable>
-#include <functional>
 
 #include "host_ffn.h"
 
@@ -318,17 +316,46 @@ void row_dots(const Row& w, const float* const* xs, int n, float* res, float* bu
 // ---------------------------------------------------------------------------
 // resident thread pool with a phase barrier
 // ---------------------------------------------------------------------------
+struct HostFfnWork;
+static void host_ffn_worker(HostPool* P, const HostFfnWork* W, int id);
+
+// Buffers of one job, kept by the pool between jobs (the pool runs one job
+// at a time) so a job allocates nothing once they have grown to its size.
+struct HostScratch {
+  std::vector<int> slot;          // [E]: index in C of expert e, or -1
+  std::vector<int> begin;         // [nC + 1]: expert ci's pairs are [begin[ci], begin[ci+1])
+  std::vector<int> next;          // [nC]: next free pair of expert ci while bucketing
+  std::vector<int> tok, jj;       // per pair: token and choice, expert-major, tokens ascending
+  std::vector<float> X;           // [T][H]: hidden rows widened to fp32, decode order
+  std::vector<float> A;           // [pairs][I]: SwiGLU activations, decode order
+};
+
+struct HostFfnWork {
+  HostFfnShape sh;
+  const uint8_t* pool;
+  int layer, T;
+  const uint16_t* hidden;
+  const float* w;
+  const int32_t* C;
+  int nC;
+  float* out;
+  HostScratch* sc;
+};
+
+// Workers sleep on a generation word (a futex through std::atomic::wait, so
+// a start wakes them all at once with no lock to queue on); the last one to
+// finish stamps the end time and wakes the waiter.
 struct HostPool {
   int n;
   std::vector<std::thread> th;
-  std::mutex mu;
-  std::condition_variable cv, done_cv;
-  std::function<void(int)> job;
-  uint64_t gen = 0;
-  int running = 0;
-  bool stop = false;
+  std::atomic<uint32_t> gen{0};
+  std::atomic<uint32_t> done{1};
+  std::atomic<int> running{0};
+  std::atomic<bool> stop{false};
+  const HostFfnWork* work = nullptr;   // published by the release on gen
   // one job at a time: held from host_ffn_start to host_ffn_wait
   std::mutex job_mu;
+  HostScratch scratch;
   std::chrono::steady_clock::time_point t_start, t_done;
   // spin barrier for phases inside a job
   std::atomic<int> bar_count{0};
@@ -338,48 +365,38 @@ struct HostPool {
     for (int i = 0; i < n; ++i) th.emplace_back([this, i] { loop(i); });
   }
   ~HostPool() {
-    {
-      std::lock_guard<std::mutex> g(mu);
-      stop = true;
-    }
-    cv.notify_all();
+    stop.store(true, std::memory_order_release);
+    gen.fetch_add(1, std::memory_order_release);
+    gen.notify_all();
     for (auto& t : th) t.join();
   }
   void loop(int id) {
-    uint64_t seen = 0;
+    uint32_t seen = 0;
     for (;;) {
-      std::function<void(int)> f;
-      {
-        std::unique_lock<std::mutex> g(mu);
-        cv.wait(g, [&] { return stop || gen != seen; });
-        if (stop) return;
-        seen = gen;
-        f = job;
-      }
-      f(id);
-      {
-        std::lock_guard<std::mutex> g(mu);
-        if (--running == 0) {
-          t_done = std::chrono::steady_clock::now();
-          done_cv.notify_all();
-        }
+      gen.wait(seen, std::memory_order_acquire);
+      const uint32_t g = gen.load(std::memory_order_acquire);
+      if (g == seen) continue;                    // spurious wake
+      seen = g;
+      if (stop.load(std::memory_order_acquire)) return;
+      host_ffn_worker(this, work, id);
+      if (running.fetch_sub(1, std::memory_order_acq_rel) == 1) {
+        t_done = std::chrono::steady_clock::now();
+        done.store(1, std::memory_order_release);
+        done.notify_one();
       }
     }
   }
-  void start(std::function<void(int)> f) {
-    {
-      std::lock_guard<std::mutex> g(mu);
-      job = std::move(f);
-      running = n;
-      ++gen;
-      t_start = std::chrono::steady_clock::now();
-    }
-    cv.notify_all();
+  void start(const HostFfnWork* w) {
+    work = w;
+    running.store(n, std::memory_order_relaxed);
+    done.store(0, std::memory_order_relaxed);
+    t_start = std::chrono::steady_clock::now();
+    gen.fetch_add(1, std::memory_order_release);
+    gen.notify_all();
   }
   // duration of the finished job in ms
   double wait() {
-    std::unique_lock<std::mutex> g(mu);
-    done_cv.wait(g, [&] { return running == 0; });
+    while (done.load(std::memory_order_acquire) == 0) done.wait(0, std::memory_order_acquire);
     return std::chrono::duration<double, std::milli>(t_done - t_start).count();
   }
   void barrier() {
@@ -397,123 +414,76 @@ HostPool* host_pool_create(int nthreads) { return new HostPool(nthreads); }
 void host_pool_destroy(HostPool* p) { delete p; }
 int host_pool_threads(const HostPool* p) { return p->n; }
 
-// One expert of the job: its routed (token, choice) pairs, its inputs in
-// decode order and its SwiGLU activations.
-struct ExpertJob {
-  int e = 0;
-  std::vector<int> tok, jj;
-  std::vector<float> X, A;   // [ne][H], [ne][I], each row in decode order
-};
-
-struct HostFfnWork {
-  HostFfnShape sh;
-  const uint8_t* pool;
-  int layer, T;
-  const uint16_t* hidden;
-  const int32_t* ids;
-  const float* w;
-  const int32_t* C;
-  int nC;
-  float* out;
-  std::vector<ExpertJob> ex;
-};
-
-// Worker `id` of the pool.  Phases, separated by the pool's barrier:
-//   0: zero this worker's slice of out; token lists of experts id, id+nt, ...
-//   1: the routed tokens' hidden rows, widened exactly to fp32 in decode order
-//      (the (expert, token) pairs split evenly over the workers);
-//   2: gate and up rows of every expert (the (expert, row) pairs split evenly):
-//      a = silu(g) * u per routed token, stored in decode order;
+// Worker `id` of the pool.  The routed (expert, token) pairs are bucketed
+// by the caller.  Phases, separated by the pool's barrier:
+//   1: zero this worker's slice of out; its share of the T hidden rows,
+//      widened exactly to fp32 in decode order;
+//   2: gate and up rows of every expert (the (expert, row) pairs split
+//      evenly): a = silu(g) * u per routed token, stored in decode order;
 //   3: down rows: each worker owns an H range and takes the experts in
 //      ascending order, adding w * y to out (one writer per element, a fixed
 //      order: deterministic).
-static void host_ffn_worker(HostPool* P, HostFfnWork* W, int id) {
+static void host_ffn_worker(HostPool* P, const HostFfnWork* W, int id) {
   const HostFfnShape& sh = W->sh;
+  const HostScratch& sc = *W->sc;
   const int nt = P->n, H = sh.H, I = sh.I, k = sh.k, fmt = sh.fmt, nC = W->nC;
   const size_t S = sh.S;
-  std::vector<float> buf((size_t)(H > I ? H : I));
+  float* X = W->sc->X.data();
+  float* A = W->sc->A.data();
+  thread_local std::vector<float> rowbuf;         // AVX2 row buffer, grown once per thread
+  if (rowbuf.size() < (size_t)std::max(H, I)) rowbuf.resize((size_t)std::max(H, I));
+  float* buf = rowbuf.data();
+  const float* ptr[8];
+  float r0[8], r1[8];
   {
     const size_t tot = (size_t)W->T * H;
     const size_t a = tot * id / nt, b = tot * (id + 1) / nt;
     std::memset(W->out + a, 0, (b - a) * sizeof(float));
-  }
-  for (int ci = id; ci < nC; ci += nt) {
-    ExpertJob& x = W->ex[ci];
-    x.e = W->C[ci];
-    x.tok.clear();
-    x.jj.clear();
-    for (int t = 0; t < W->T; ++t)
-      for (int j = 0; j < k; ++j)
-        if (W->ids[(size_t)t * k + j] == x.e) {
-          x.tok.push_back(t);
-          x.jj.push_back(j);
-        }
-    x.X.resize(x.tok.size() * (size_t)H);
-    x.A.resize(x.tok.size() * (size_t)I);
-  }
-  P->barrier();
-  // phase 1: hidden rows
-  {
-    long tot = 0;
-    for (int ci = 0; ci < nC; ++ci) tot += (long)W->ex[ci].tok.size();
-    const long g0 = tot * id / nt, g1 = tot * (id + 1) / nt;
-    long base = 0;
-    for (int ci = 0; ci < nC && base < g1; ++ci) {
-      ExpertJob& x = W->ex[ci];
-      const long ne = (long)x.tok.size();
-      for (long r = std::max(g0 - base, 0L); r < ne && base + r < g1; ++r) {
-        const uint16_t* src = W->hidden + (size_t)x.tok[r] * H;
-        float* dst = x.X.data() + (size_t)r * H;
-        for (int h = 0; h < H; ++h) {
-          const uint32_t u = (uint32_t)src[h] << 16;
-          std::memcpy(dst + arranged(fmt, h), &u, 4);
-        }
-      }
-      base += ne;
+    for (size_t i = a; i < b; ++i) {
+      const size_t t = i / H;
+      const int h = (int)(i % H);
+      const uint32_t u = (uint32_t)W->hidden[i] << 16;
+      std::memcpy(X + t * H + arranged(fmt, h), &u, 4);
     }
   }
   P->barrier();
-  // phase 2: gate and up rows
+  // phase 2: gate and up rows, up to 8 tokens of an expert per row pass
   {
     const long tot = (long)nC * I;
     const long g0 = tot * id / nt, g1 = tot * (id + 1) / nt;
-    std::vector<const float*> xs;
-    std::vector<float> gv, uv;
     for (long g = g0; g < g1; ++g) {
       const int ci = (int)(g / I), i = (int)(g % I);
-      ExpertJob& x = W->ex[ci];
-      const int ne = (int)x.tok.size();
-      if (ne == 0) continue;
-      xs.resize(ne);
-      gv.resize(ne);
-      uv.resize(ne);
-      for (int r = 0; r < ne; ++r) xs[r] = x.X.data() + (size_t)r * H;
-      const uint8_t* blob = W->pool + ((size_t)W->layer * sh.E + x.e) * S;
-      row_dots(make_row(sh, blob, 0, i), xs.data(), ne, gv.data(), buf.data());
-      row_dots(make_row(sh, blob, 1, i), xs.data(), ne, uv.data(), buf.data());
+      const int p0 = sc.begin[ci], p1 = sc.begin[ci + 1];
+      if (p0 == p1) continue;
+      const uint8_t* blob = W->pool + ((size_t)W->layer * sh.E + W->C[ci]) * S;
+      const Row wg = make_row(sh, blob, 0, i), wu = make_row(sh, blob, 1, i);
       const int ai = arranged(fmt, i);
-      for (int r = 0; r < ne; ++r) x.A[(size_t)r * I + ai] = gv[r] / (1.0f + std::exp(-gv[r])) * uv[r];
+      for (int q0 = p0; q0 < p1; q0 += 8) {
+        const int ne = std::min(8, p1 - q0);
+        for (int r = 0; r < ne; ++r) ptr[r] = X + (size_t)sc.tok[q0 + r] * H;
+        row_dots(wg, ptr, ne, r0, buf);
+        row_dots(wu, ptr, ne, r1, buf);
+        for (int r = 0; r < ne; ++r) A[(size_t)(q0 + r) * I + ai] = r0[r] / (1.0f + std::exp(-r0[r])) * r1[r];
+      }
     }
   }
   P->barrier();
   // phase 3: down rows, this worker's H range, experts ascending
   {
     const int h0 = (int)((long)H * id / nt), h1 = (int)((long)H * (id + 1) / nt);
-    std::vector<const float*> as;
-    std::vector<float> yv;
     for (int ci = 0; ci < nC; ++ci) {
-      ExpertJob& x = W->ex[ci];
-      const int ne = (int)x.tok.size();
-      if (ne == 0) continue;
-      as.resize(ne);
-      yv.resize(ne);
-      for (int r = 0; r < ne; ++r) as[r] = x.A.data() + (size_t)r * I;
-      const uint8_t* blob = W->pool + ((size_t)W->layer * sh.E + x.e) * S;
-      for (int h = h0; h < h1; ++h) {
-        row_dots(make_row(sh, blob, 2, h), as.data(), ne, yv.data(), buf.data());
-        for (int r = 0; r < ne; ++r) {
-          const int t = x.tok[r];
-          W->out[(size_t)t * H + h] += W->w[(size_t)t * k + x.jj[r]] * yv[r];
+      const int p0 = sc.begin[ci], p1 = sc.begin[ci + 1];
+      if (p0 == p1) continue;
+      const uint8_t* blob = W->pool + ((size_t)W->layer * sh.E + W->C[ci]) * S;
+      for (int q0 = p0; q0 < p1; q0 += 8) {
+        const int ne = std::min(8, p1 - q0);
+        for (int r = 0; r < ne; ++r) ptr[r] = A + (size_t)(q0 + r) * I;
+        for (int h = h0; h < h1; ++h) {
+          row_dots(make_row(sh, blob, 2, h), ptr, ne, r0, buf);
+          for (int r = 0; r < ne; ++r) {
+            const int t = sc.tok[q0 + r];
+            W->out[(size_t)t * H + h] += W->w[(size_t)t * k + sc.jj[q0 + r]] * r0[r];
+          }
         }
       }
     }
@@ -527,6 +497,32 @@ struct HostFfnHandle {
 HostFfnHandle* host_ffn_start(HostPool* P, const HostFfnShape& sh, const uint8_t* pool, int layer, int T,
                               const uint16_t* hidden, const int32_t* ids, const float* w, const int32_t* C, int nC,
                               float* out) {
+  P->job_mu.lock();                 // released by host_ffn_wait on this thread
+  HostScratch& sc = P->scratch;
+  nC = nC > 0 ? nC : 0;
+  // bucket the routed pairs by expert: one pass over ids
+  sc.slot.assign((size_t)sh.E, -1);
+  for (int ci = 0; ci < nC; ++ci) sc.slot[C[ci]] = ci;
+  sc.begin.assign((size_t)nC + 1, 0);
+  for (int q = 0; q < T * sh.k; ++q) {
+    const int e = ids[q];
+    if (e >= 0 && e < sh.E && sc.slot[e] >= 0) ++sc.begin[sc.slot[e] + 1];
+  }
+  for (int ci = 0; ci < nC; ++ci) sc.begin[ci + 1] += sc.begin[ci];
+  const int np = sc.begin[nC];
+  sc.tok.resize((size_t)np);
+  sc.jj.resize((size_t)np);
+  sc.next.assign(sc.begin.begin(), sc.begin.end() - 1);
+  for (int t = 0; t < T; ++t)
+    for (int j = 0; j < sh.k; ++j) {
+      const int e = ids[(size_t)t * sh.k + j];
+      if (e < 0 || e >= sh.E || sc.slot[e] < 0) continue;
+      const int q = sc.next[sc.slot[e]]++;
+      sc.tok[q] = t;
+      sc.jj[q] = j;
+    }
+  if (sc.X.size() < (size_t)T * sh.H) sc.X.resize((size_t)T * sh.H);
+  if (sc.A.size() < (size_t)np * sh.I) sc.A.resize((size_t)np * sh.I);
   HostFfnHandle* h = new HostFfnHandle();
   HostFfnWork& W = h->work;
   W.sh = sh;
@@ -534,15 +530,12 @@ HostFfnHandle* host_ffn_start(HostPool* P, const HostFfnShape& sh, const uint8_t
   W.layer = layer;
   W.T = T;
   W.hidden = hidden;
-  W.ids = ids;
   W.w = w;
   W.C = C;
   W.nC = nC;
   W.out = out;
-  W.ex.resize(nC > 0 ? nC : 0);
-  HostFfnWork* wp = &W;
-  P->job_mu.lock();                 // released by host_ffn_wait on this thread
-  P->start([P, wp](int id) { host_ffn_worker(P, wp, id); });
+  W.sc = &sc;
+  P->start(&W);
   return h;
 }
 

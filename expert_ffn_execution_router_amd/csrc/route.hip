@@ -142,13 +142,11 @@ router_mfma_kernel(const uint16_t* __restrict__ x, const float* __restrict__ R, 
 // each winner's output position is its rank among the winners (descending
 // logit, ties to the lower expert id).  The gate weights are the softmax of
 // the winners, summed in output order.
-__global__ void __launch_bounds__(256)
-topk_kernel(const float* __restrict__ z, int T, int E, int k, int32_t* __restrict__ ids,
-            float* __restrict__ w) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int t = blockIdx.x * 4 + wave;
-  if (t >= T) return;
-  const float* zr = z + (size_t)t * E;
+// One wave: the k winners of logit row zr into ids_r / w_r (and, when
+// lds_r is not null, the ids into lds_r too).
+DEV void topk_row(const float* __restrict__ zr, int E, int k, int32_t* __restrict__ ids_r, float* __restrict__ w_r,
+                  int32_t* lds_r) {
+  const int lane = threadIdx.x & 63;
   const uint64_t below = (1ull << lane) - 1ull;
   float v[4];
   uint32_t key[4];
@@ -217,10 +215,19 @@ topk_kernel(const float* __restrict__ z, int T, int E, int k, int32_t* __restric
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     if (sel[i]) {
-      ids[(size_t)t * k + rank[i]] = lane + 64 * i;
-      w[(size_t)t * k + rank[i]] = expf(v[i] - top) / ssum;
+      ids_r[rank[i]] = lane + 64 * i;
+      w_r[rank[i]] = expf(v[i] - top) / ssum;
+      if (lds_r) lds_r[rank[i]] = lane + 64 * i;
     }
   }
+}
+
+__global__ void __launch_bounds__(256)
+topk_kernel(const float* __restrict__ z, int T, int E, int k, int32_t* __restrict__ ids,
+            float* __restrict__ w) {
+  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (t >= T) return;
+  topk_row(z + (size_t)t * E, E, k, ids + (size_t)t * k, w + (size_t)t * k, nullptr);
 }
 
 // ---------------------------------------------------------------------------
@@ -228,7 +235,8 @@ topk_kernel(const float* __restrict__ z, int T, int E, int k, int32_t* __restric
 // ---------------------------------------------------------------------------
 constexpr int GROUP_TOK = 256;   // tokens per grouping block
 
-// Exclusive scan of one value per thread over a 256-thread block.
+// Exclusive scan of one value per thread over the first 256 threads of the
+// block (threads past them, in larger blocks, pass 0 and get no result).
 __device__ int block_exclusive_scan256(int v, int* tmp /* >= 4 ints of LDS */, int* total) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   int incl = v;
@@ -237,10 +245,10 @@ __device__ int block_exclusive_scan256(int v, int* tmp /* >= 4 ints of LDS */, i
     const int o = __shfl_up(incl, off, 64);
     if (lane >= off) incl += o;
   }
-  if (lane == 63) tmp[wave] = incl;
+  if (lane == 63 && wave < 4) tmp[wave] = incl;
   __syncthreads();
   int base = 0;
-  for (int i = 0; i < wave; ++i) base += tmp[i];
+  for (int i = 0; i < wave && i < 4; ++i) base += tmp[i];
   *total = tmp[0] + tmp[1] + tmp[2] + tmp[3];
   __syncthreads();
   return base + incl - v;
@@ -359,6 +367,32 @@ group_single_kernel(const int32_t* __restrict__ ids, int T, int k, int E, const 
   scatter_block(ids, 0, T, k, E, base, bits, pos, perm_tok);
 }
 
+// T <= 16: top-k of every token (wave t takes token t) and the grouping of
+// group_single_kernel in one launch; the assignments pass through LDS.
+constexpr int TG_MAX_T = 16;
+__global__ void __launch_bounds__(1024)
+topk_group_kernel(const float* __restrict__ z, int T, int E, int k, int32_t* __restrict__ ids,
+                  float* __restrict__ w, const uint32_t* miss_mask, const int32_t* slot_row, int mb,
+                  int32_t* counts, int32_t* offsets, int32_t* __restrict__ pos, int32_t* __restrict__ perm_tok,
+                  WorkList* wl, int* err, TailSplit ts) {
+  __shared__ uint32_t bits[256 * 8];
+  __shared__ int base[256];
+  __shared__ int tmp[4];
+  __shared__ int32_t s_ids[TG_MAX_T * 8];
+  const int wave = threadIdx.x >> 6;
+  if (wave < T)
+    topk_row(z + (size_t)wave * E, E, k, ids + (size_t)wave * k, w + (size_t)wave * k, s_ids + wave * k);
+  __syncthreads();
+  mark_block(s_ids, 0, T, k, E, bits);
+  int cnt = 0;
+  if ((int)threadIdx.x < E)
+    for (int q = 0; q < 8; ++q) cnt += __popc(bits[threadIdx.x * 8 + q]);
+  finish_grouping(cnt, E, miss_mask, slot_row, counts, offsets, wl, mb, err, tmp, ts);
+  if ((int)threadIdx.x < E) base[threadIdx.x] = offsets[threadIdx.x];
+  __syncthreads();
+  scatter_block(s_ids, 0, T, k, E, base, bits, pos, perm_tok);
+}
+
 // General path, pass 1: per-block histograms hist[b][e].
 __global__ void __launch_bounds__(256)
 group_count_kernel(const int32_t* __restrict__ ids, int T, int k, int E, int32_t* __restrict__ hist) {
@@ -420,6 +454,19 @@ extern "C" hipError_t moe_launch_router(const uint16_t* x, const float* R, const
 
 extern "C" hipError_t moe_launch_topk(const float* z, int T, int E, int k, int32_t* ids, float* w, hipStream_t s) {
   topk_kernel<<<(T + 3) / 4, 256, 0, s>>>(z, T, E, k, ids, w);
+  return hipGetLastError();
+}
+
+// Top-k and grouping in one launch for T <= 16 (same outputs as
+// moe_launch_topk followed by moe_launch_group).
+extern "C" hipError_t moe_launch_topk_group(const float* z, int T, int E, int k, int32_t* ids, float* w,
+                                            const uint32_t* miss_mask, const int32_t* slot_row, int mb,
+                                            int32_t* counts, int32_t* offsets, int32_t* pos, int32_t* perm_tok,
+                                            WorkList* wl, int* err, hipStream_t s) {
+  if (T < 1 || T > TG_MAX_T || E > 256 || k > 8) return hipErrorInvalidValue;
+  const TailSplit ts{nullptr, nullptr, nullptr, nullptr, 1, 0};
+  topk_group_kernel<<<1, 1024, 0, s>>>(z, T, E, k, ids, w, miss_mask, slot_row, mb, counts, offsets, pos, perm_tok,
+                                       wl, err, ts);
   return hipGetLastError();
 }
 

@@ -155,7 +155,7 @@ int moe_set_policy(moe_ctx* ctx, int policy, double B_P, double B_H);
  * (at least 8 calls and 100 ms), 40 calls over (layer, expert) groups
  * spread over the pool, so no call finds its bytes in the host caches, first alone
  * (host_alone) and then while a train of copies keeps the link busy
- * (host_conc: calls that end inside the train).
+ * (host_conc: calls that end inside the second of two such trains).
  * Section 2.5 splits the miss set so that the fills, at B_P, and the host
  * branch, on the residual B_R = B_H - B_P, end together; B_R is measured
  * here as host_conc (host_alone when fewer than 3 calls ran inside the

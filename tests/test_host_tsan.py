@@ -16,7 +16,7 @@ CSRC = os.path.join(ROOT, "expert_ffn_execution_router_amd", "csrc")
 @pytest.mark.skipif(shutil.which("g++") is None, reason="needs g++")
 def test_host_pool_is_race_free_under_tsan(tmp_path):
     exe = str(tmp_path / "host_pool_stress")
-    cmd = ["g++", "-std=c++17", "-O1", "-g", "-fsanitize=thread", "-march=x86-64-v3", "-pthread", "-I" + CSRC,
+    cmd = ["g++", "-std=c++20", "-O1", "-g", "-fsanitize=thread", "-march=x86-64-v3", "-pthread", "-I" + CSRC,
            os.path.join(ROOT, "tests", "host_pool_stress.cpp"), os.path.join(CSRC, "host_ffn.cpp"), "-o", exe]
     subprocess.run(cmd, check=True, capture_output=True, text=True)
     env = dict(os.environ, TSAN_OPTIONS="halt_on_error=1 exitcode=66")

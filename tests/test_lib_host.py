@@ -74,14 +74,15 @@ def _run_host(B, cfg_s, seed, T, C, threads):
 
 
 @pytest.mark.parametrize("fmt", [0, 1, 2, 3])
-@pytest.mark.parametrize("threads", [1, 3])
-def test_host_ffn_matches_oracle(B, fmt, threads):
+@pytest.mark.parametrize("threads,T", [(1, 16), (3, 16), (5, 48)])
+def test_host_ffn_matches_oracle(B, fmt, threads, T):
+    """T=48 gives each host expert more than 8 tokens (several row passes)."""
     c = synth.CONFIGS[1]
     if fmt:
         c = dataclasses.replace(c, fmt=fmt, H=256, I=256)
     else:
         c = dataclasses.replace(c, fmt=fmt)
-    out, ref = _run_host(B, c, 7, 16, [0, 2, 3, 5], threads)
+    out, ref = _run_host(B, c, 7, T, [0, 2, 3, 5], threads)
     err = np.abs(out - ref).max() / np.abs(ref).max()
     assert err < 1e-5, err
     # tokens with no host expert get exactly zero
