@@ -19,9 +19,10 @@ full-layer double buffer (with the ablation without it).
 adds the optional ones: formats (fp8 / MXFP4 shapes), policies (miss rates
 of expert placements replayed over synthetic routing), elastic (cache
 rebuilds between decode steps), fallback (prefill with fewer than two
-layers of slots, and the prefill-to-decode hand-off) and mxfp4_serving (the
-MXFP4 shape's whole pool: a prefill chunk, then 512 decode steps through a
-25% cache);
+layers of slots, and the prefill-to-decode hand-off), mxfp4_serving (the
+MXFP4 shape's pool: a prefill chunk, then 512 decode steps through a 25%
+cache) and fp8_serving (the fp8 shape's pool: a 4096-token prefill chunk,
+then decode at T=1 and 32 through a 30% cache);
 --copy-probe only runs a 1 GiB device copy (calibrates the byte counters).
 """
 from __future__ import annotations
@@ -89,6 +90,9 @@ def parse():
     ap.add_argument("--policy-steps", type=int, default=256, help="decode steps counted by the policies phase")
     ap.add_argument("--serving-steps", type=int, default=512, help="decode steps of the mxfp4 serving phase")
     ap.add_argument("--serving-layers", type=int, default=11, help="layers of the mxfp4 serving phase's pool")
+    ap.add_argument("--fp8-serving-layers", type=int, default=6, help="layers of the fp8 serving phase's pool")
+    ap.add_argument("--fp8-serving-steps", type=int, default=256, help="T=1 decode steps of the fp8 serving phase "
+                    "(a quarter as many at T=32)")
     ap.add_argument("--copy-probe", action="store_true",
                     help="only copy 1 GiB device->device 3 times (calibrates HBM byte counters)")
     a = ap.parse_args()
@@ -749,29 +753,28 @@ def phase_fallback(w: Workload):
     return res
 
 
-def phase_mxfp4_serving(args):
-    """The MXFP4 shape end to end as its workload states it: E=256 top-8,
-    H=6144, I=2048, a slot cache of 25% of the pool; one 16384-token prefill
-    chunk through the full-layer double buffer, then 512 decode steps at T=1
-    (Zipf bias, 0.7 row reuse) through the cache with the q* split, one
-    captured graph per step.  --serving-layers of its 16 layers (the whole
-    82 GB pool is more than one process can pin here; per-layer work and the
-    cache fraction are unchanged)."""
+def serve(args, c, name, Tp, decode):
+    """One shape end to end as its workload states it: a Tp-token prefill
+    chunk through the full-layer double buffer, then decode steps through the
+    slot cache with the q* split on the bandwidths calibrated at startup, one
+    captured graph per step and batch size (decode: [(T, steps)], run in
+    order, each after 8 warm-up steps and on the cache the previous left)."""
     import torch
     import synth
     from expert_ffn_execution_router_amd import binding as B
     from expert_ffn_execution_router_amd.runtime import HostPool, MoeRuntime
-    c = synth.CONFIGS[5].with_layers(args.serving_layers)
     L, E, k, H, I, S = c.L, c.E, c.k, c.H, c.I, c.expert_bytes
     dev = torch.device("cuda:0")
     t0 = time.time()
     pool = HostPool(L * E * S)
     synth.fill_pool(pool.ptr, c, args.seed)
-    log(f"mxfp4 pool {L * E * S / 1e9:.1f} GB pinned and filled in {time.time() - t0:.1f}s")
+    log(f"{name} pool {L * E * S / 1e9:.1f} GB pinned and filled in {time.time() - t0:.1f}s")
     R = [torch.from_numpy(synth.router_weights(c, args.seed, l)).to(dev) for l in range(L)]
-    bias = [torch.from_numpy(synth.router_bias(c, args.seed, l)).to(dev) for l in range(L)]
-    Tp, K, W = 16384, args.serving_steps, 8
-    rt = MoeRuntime(L, E, k, H, I, c.fmt, c.n_slots, Tp, pool, host_threads=args.host_threads)
+    bias = [None if b is None else torch.from_numpy(b).to(dev)
+            for b in (synth.router_bias(c, args.seed, l) for l in range(L))]
+    W = 8
+    rt = MoeRuntime(L, E, k, H, I, c.fmt, c.n_slots, max([Tp] + [t for t, _ in decode]), pool,
+                    host_threads=args.host_threads)
     bp, bh = rt.calibrate()
     rt.set_policy(B.MOE_POLICY_HYBRID, bp, bh)
     rt.reset_cache()
@@ -786,42 +789,70 @@ def phase_mxfp4_serving(args):
     torch.cuda.synchronize()
     el_p = time.perf_counter() - t0
     del hp, out_p
-    keys = synth.decode_row_keys(c, args.seed, W + K, 1)
-    hid = torch.from_numpy(synth.hidden_rows(c, keys.reshape(-1)).reshape(W + K, L, 1, H).view(np.int16)).to(dev)
-    outs = torch.empty(L, 1, H, dtype=torch.bfloat16, device=dev)
-    xin = torch.empty_like(hid[0])
-    hs, cap = torch.cuda.Stream(), torch.cuda.Stream()
-    g = torch.cuda.CUDAGraph()
-    with torch.cuda.graph(g, stream=cap):
-        for l in range(L):
-            rt.decode_layer_async(l, xin[l], R[l], bias[l], outs[l], stream=cap, host_stream=hs)
-    for s_ in range(W):
-        xin.copy_(hid[s_])
-        g.replay()
-    torch.cuda.synchronize()
-    rt.plan_stats(reset=True)
-    t0 = time.perf_counter()
-    for s_ in range(K):
-        xin.copy_(hid[W + s_])
-        g.replay()
-    torch.cuda.synchronize()
-    el = time.perf_counter() - t0
-    st = rt.plan_stats()
-    assert rt.check_device_error() == 0
-    n = max(st["calls"], 1)
-    res = {"workload": f"mxfp4: {L} layers, E={E} top-{k}, H={H}, I={I}, {L * E * S / 1e9:.1f} GB pool, "
-                       f"{c.n_slots} slots (25%)",
+    res = {"workload": f"{name}: {L} layers, E={E} top-{k}, H={H}, I={I}, {L * E * S / 1e9:.1f} GB pool, "
+                       f"{c.n_slots} slots ({100.0 * c.n_slots / (L * E):.0f}%)",
            "prefill": {"T": Tp, "chunk_s": el_p, "tokens_per_s": Tp / el_p, "h2d_GBps": L * E * S / el_p / 1e9},
-           "decode": {"T": 1, "steps": K, "warmup": W, "ms_per_step": el / K * 1e3, "B_P_GBps": bp, "B_H_GBps": bh,
-                      "hit_rate": st["n_hit"] / max(st["n_unique"], 1), "misses_per_layer": st["m"] / n,
-                      "fills_per_layer": st["q"] / n, "host_per_layer": st["n_host"] / n,
-                      "host_branch_us_per_layer": st["host_ms"] * 1e3 / n}}
-    log(f"mxfp4 serving: {json.dumps(res)}")
+           "B_P_GBps": bp, "B_H_GBps": bh}
+    for T, K in decode:
+        keys = synth.decode_row_keys(c, args.seed + T, W + K, T)
+        hid = torch.from_numpy(synth.hidden_rows(c, keys.reshape(-1)).reshape(W + K, L, T, H).view(np.int16)).to(dev)
+        outs = torch.empty(L, T, H, dtype=torch.bfloat16, device=dev)
+        xin = torch.empty_like(hid[0])
+        hs, cap = torch.cuda.Stream(), torch.cuda.Stream()
+        g = torch.cuda.CUDAGraph()
+        with torch.cuda.graph(g, stream=cap):
+            for l in range(L):
+                rt.decode_layer_async(l, xin[l], R[l], bias[l], outs[l], stream=cap, host_stream=hs)
+        for s_ in range(W):
+            xin.copy_(hid[s_])
+            g.replay()
+        torch.cuda.synchronize()
+        rt.plan_stats(reset=True)
+        t0 = time.perf_counter()
+        for s_ in range(K):
+            xin.copy_(hid[W + s_])
+            g.replay()
+        torch.cuda.synchronize()
+        el = time.perf_counter() - t0
+        st = rt.plan_stats()
+        assert rt.check_device_error() == 0
+        n = max(st["calls"], 1)
+        res[f"decode_T{T}"] = {
+            "T": T, "steps": K, "warmup": W, "ms_per_step": el / K * 1e3,
+            "moe_layer_tokens_per_s": K * L * T / el,
+            "hit_rate": st["n_hit"] / max(st["n_unique"], 1), "misses_per_layer": st["m"] / n,
+            "fills_per_layer": st["q"] / n, "host_per_layer": st["n_host"] / n,
+            "host_branch_us_per_layer": st["host_ms"] * 1e3 / n}
+        log(f"{name} decode T={T}: {json.dumps(res[f'decode_T{T}'])}")
+        del g, hid, outs, xin
+    log(f"{name} serving: {json.dumps(res)}")
     rt.close()
-    del rt, g
+    del rt
     torch.cuda.empty_cache()
     pool.free()
     return res
+
+
+def phase_mxfp4_serving(args):
+    """The MXFP4 shape (E=256 top-8, H=6144, I=2048, a slot cache of 25% of
+    the pool): one 16384-token prefill chunk, then 512 decode steps at T=1
+    (Zipf bias, 0.7 row reuse).  --serving-layers of its 16 layers (the whole
+    82 GB pool is more than one process can pin here; per-layer work and the
+    cache fraction are unchanged)."""
+    import synth
+    c = synth.CONFIGS[5].with_layers(args.serving_layers)
+    return serve(args, c, "mxfp4", 16384, [(1, args.serving_steps)])
+
+
+def phase_fp8_serving(args):
+    """The fp8 shape (E=256 top-6, H=4096, I=2048, fp32 scale per 128x128
+    block, a slot cache of 30% of the pool): one 4096-token prefill chunk,
+    then decode at T=1 and T=32 through the cache.  --fp8-serving-layers of
+    its 43 layers (the 277 GB pool cannot be pinned by one process; per-layer
+    work and the cache fraction are unchanged)."""
+    import synth
+    c = synth.CONFIGS[4].with_layers(args.fp8_serving_layers)
+    return serve(args, c, "fp8_e4m3_b128", 4096, [(1, args.fp8_serving_steps), (32, args.fp8_serving_steps // 4)])
 
 
 def phase_formats(args):
@@ -1101,6 +1132,8 @@ def main():
         line["placement_miss_rates"] = phase_policies(args)
     if "mxfp4_serving" in args.phase_set:
         line["mxfp4_serving"] = phase_mxfp4_serving(args)
+    if "fp8_serving" in args.phase_set:
+        line["fp8_serving"] = phase_fp8_serving(args)
     print(json.dumps(line), flush=True)
     if w is not None:
         w.pool.free()

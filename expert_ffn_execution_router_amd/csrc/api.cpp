@@ -453,17 +453,24 @@ int forward_experts(moe_ctx* c, const void* hidden, int T, const int32_t* slot_r
       x16 = c->Xq;
     }
     // Equal ranges of the weight stream balance the bytes over every CU but
-    // cut items, whose partial tiles a second launch adds.  When every item
-    // (expert m-block x 64 weight rows) can have a workgroup of its own in
-    // one round (the m-blocks are at most T*k, and at most E plus T*k over
-    // the block size), the launch is bound by latency rather than by the
-    // stream, and one workgroup per item saves that second launch: at T=1 on
-    // the decode shape (8 experts: 96 gate/up items, 256 down items) the
-    // layer took 44 us instead of 51.
+    // cut items, whose partial tiles a second launch adds (6-8 us with its
+    // gap).  When every item (expert m-block x 64 weight rows) can have a
+    // workgroup of its own in one round (the m-blocks are at most T*k, and
+    // at most E plus T*k over the block size), one workgroup per item saves
+    // that launch, at the price of one workgroup streaming a whole item.
+    // That pays while an item takes at most ~30 us: measured one-workgroup
+    // rates per item, with the layer wall times at T=1 (split -> whole):
+    // bf16 512 KiB gate/up items ~32 GB/s (decode shape 51 -> 44 us), fp8
+    // ~18 GB/s (fp8 shape 67 -> 66 us), NVFP4 ~7.5 GB/s on 128 KiB items
+    // (52 -> 43 us), MXFP4 ~8 GB/s on 384 KiB items (78 -> 91 us: 47 us for
+    // the gate/up GEMM).
     const long mb_bound = std::min<long>((long)T * g.k, (long)g.E + (long)T * g.k / (16 * ns));
     const long it1 = mb_bound * (g.I / 64), it2 = mb_bound * (g.H / 64);
-    const int nc1 = it1 <= ncu ? (int)it1 : 0;
-    const int nc2 = it2 <= ncu ? (int)it2 : 0;
+    const double vb = g.wfmt == MOE_W_BF16 ? 2.0 : (g.wfmt == MOE_W_FP8_E4M3_B128 ? 1.0 : 0.5);   // bytes per weight
+    const double wg_GBps = g.wfmt == MOE_W_BF16 ? 32.0 : (g.wfmt == MOE_W_FP8_E4M3_B128 ? 18.0 : (g.wfmt == MOE_W_NVFP4 ? 7.5 : 8.0));
+    const double item1_us = 2.0 * 64 * g.H * vb / (wg_GBps * 1e3), item2_us = 64.0 * g.I * vb / (wg_GBps * 1e3);
+    const int nc1 = item1_us <= 30.0 && it1 <= ncu ? (int)it1 : 0;
+    const int nc2 = item2_us <= 30.0 && it2 <= ncu ? (int)it2 : 0;
     STAGE(c, MOE_STAGE_GEMM1, s,
           moe_launch_gemm_dec(dfmt, 1, ns, ncu, c->wl, c->counts, c->offsets, c->slot_pool, b.S, b.w[0], b.w[1],
                               b.s[0], b.s[1], x16, nullptr, c->perm_tok, g.H, g.I, c->A, c->part, c->part_bytes, -nc1,
