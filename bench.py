@@ -77,6 +77,8 @@ def parse():
                     help="further batch sizes through the slot cache, short runs (comma list, empty: none)")
     ap.add_argument("--e2e-T-steps", type=int, default=8, help="timed steps of each --e2e-Ts run")
     ap.add_argument("--e2e-warmup", type=int, default=16)
+    ap.add_argument("--high-hit-frac", type=float, default=0.9,
+                    help="cache fraction of the high-hit sync-vs-graph decode comparison (0: skip)")
     ap.add_argument("--e2e-steps", type=int, default=32)
     ap.add_argument("--prefill-T", type=int, default=8192)
     ap.add_argument("--prefill-Ts", type=lambda v: [int(t) for t in v.split(",") if t], default=[4096, 16384],
@@ -424,6 +426,71 @@ def phase_e2e(w: Workload):
     torch.cuda.empty_cache()
     if args.e2e_Ts:
         res["by_T"] = {str(t): e2e_at(w, t, bp, bh) for t in args.e2e_Ts}
+    if args.high_hit_frac > 0:
+        res["high_hit"] = e2e_high_hit(w, bp, bh, args.high_hit_frac)
+    return res
+
+
+def e2e_high_hit(w: Workload, bp, bh, frac):
+    """The synchronous decode layer (a host read of each layer's plan) against
+    the device-resident one (one captured graph per step, no host read) where
+    misses are rare: T=1 through a cache of `frac` of the pool, the same rows
+    and the same cold start for both, 64 warm-up and 32 timed steps."""
+    import torch
+    import synth
+    from expert_ffn_execution_router_amd import binding as B
+    args, c = w.args, w.cfg
+    L, T, W, K = c.L, 1, 64, 32
+    n_slots = int(frac * L * c.E)
+    keys = synth.decode_row_keys(c, args.seed + 3, W + K, T)
+    hid = torch.from_numpy(synth.hidden_rows(c, keys.reshape(-1)).reshape(W + K, L, T, c.H).view(np.int16)).to(w.dev)
+    outs = torch.empty(L, T, c.H, dtype=torch.bfloat16, device=w.dev)
+    rc = w.runtime(n_slots, 64)
+    rc.set_policy(B.MOE_POLICY_HYBRID, bp, bh)
+
+    def totals(t):
+        n = max(t["calls"], 1)
+        return {"hit_rate": t["n_hit"] / max(t["n_unique"], 1), "misses_per_layer": t["m"] / n,
+                "fills_per_layer": t["q"] / n, "host_per_layer": t["n_host"] / n}
+    copy = torch.cuda.Stream()
+    res = {"T": T, "n_slots": n_slots, "cache_frac": frac, "warmup_steps": W, "steps": K}
+    for s in range(W):
+        for l in range(L):
+            rc.decode_layer(l, hid[s, l], w.R[l], w.bias[l], outs[l], copy_stream=copy)
+    torch.cuda.synchronize()
+    rc.plan_stats(reset=True)
+    t0 = time.perf_counter()
+    for s in range(K):
+        for l in range(L):
+            rc.decode_layer(l, hid[W + s, l], w.R[l], w.bias[l], outs[l], copy_stream=copy)
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    res["sync"] = dict(ms_per_step=el / K * 1e3, **totals(rc.plan_stats(reset=True)))
+    hs, cap = torch.cuda.Stream(), torch.cuda.Stream()
+    xin = torch.empty_like(hid[0])
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g, stream=cap):
+        for l in range(L):
+            rc.decode_layer_async(l, xin[l], w.R[l], w.bias[l], outs[l], stream=cap, host_stream=hs)
+    rc.reset_cache()
+    torch.cuda.synchronize()
+    for s in range(W):
+        xin.copy_(hid[s])
+        g.replay()
+    torch.cuda.synchronize()
+    rc.plan_stats(reset=True)
+    t0 = time.perf_counter()
+    for s in range(K):
+        xin.copy_(hid[W + s])
+        g.replay()
+    torch.cuda.synchronize()
+    el = time.perf_counter() - t0
+    assert rc.check_device_error() == 0
+    res["graph"] = dict(ms_per_step=el / K * 1e3, **totals(rc.plan_stats(reset=True)))
+    log(f"high-hit decode: {json.dumps(res)}")
+    rc.close()
+    del rc, g
+    torch.cuda.empty_cache()
     return res
 
 
