@@ -15,7 +15,7 @@ CSRC = os.path.join(PKG, "csrc")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libmoe.so")
 
-HIP_SOURCES = ["route.hip", "gemm_dec.hip", "gemm_pf.hip", "gemm_pf8.hip", "combine.hip", "slots.hip",
+HIP_SOURCES = ["route.hip", "gemm_dec.hip", "gemm_pf.hip", "gemv.hip", "gemm_pf8.hip", "combine.hip", "slots.hip",
                "noalloc.hip"]
 # Per-source code-generation options (none at present).
 HIP_EXTRA = {}

@@ -91,6 +91,27 @@ def test_decode_config2_shape_T64():
         s.close()
 
 
+@pytest.mark.parametrize("T", [1, 3, 4, 8])
+def test_decode_config2_shape_small_T(T):
+    """The decode shape at the smallest batches (at most 4 tokens per expert:
+    the matrix-vector kernels; 8: the MFMA kernel), every item covered."""
+    print(f"decode config-2 shape T={T}", flush=True)
+    cfg = _fullsize(2, L=1)
+    s = Setup(cfg, seed=5, max_tokens=64, host_threads=8)
+    try:
+        s.admit_all(0)
+        keys = synth.decode_row_keys(cfg, 5, 1, T)
+        x = synth.hidden_rows(cfg, keys[0, 0])
+        xd = torch.from_numpy(x.view(np.int16)).cuda()
+        out = torch.empty(T, cfg.H, dtype=torch.bfloat16, device="cuda")
+        s.rt.forward(0, xd, s.R_d[0], s.b_d[0], s.slot_row(0), out)
+        torch.cuda.synchronize()
+        assert s.rt.check_device_error() == 0
+        _check_rows(s, 0, x, out)
+    finally:
+        s.close()
+
+
 @pytest.mark.timeout(400)
 @pytest.mark.parametrize("T", [2048, 4096, 8192, 16384])
 def test_prefill_config3_shape(T):
