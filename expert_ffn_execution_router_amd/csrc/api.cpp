@@ -41,9 +41,10 @@ size_t moe_dec_part_bytes();
 int moe_dec_max_ns(int fmt);
 int moe_pf_tile_tokens();
 int moe_gemv_max_tokens();
-hipError_t moe_launch_gemv(int gated, int grid, const WorkList* wl, const int32_t* counts, const int32_t* offsets,
-                           const uint8_t* pool, size_t S, size_t woff0, size_t woff1, const void* X,
-                           const int32_t* row_tok, int K, int N, void* out, hipStream_t s);
+hipError_t moe_launch_gemv(int fmt, int gated, int grid, const WorkList* wl, const int32_t* counts,
+                           const int32_t* offsets, const uint8_t* pool, size_t S, size_t woff0, size_t woff1,
+                           size_t soff0, size_t soff1, const void* X, const int32_t* row_tok, int K, int N, void* out,
+                           hipStream_t s);
 int moe_pf8_tile_tokens(int fmt, int small);
 hipError_t moe_launch_gemm_pf8(int fmt, int gated, int small, int n_cu, const WorkList* wl, const int32_t* counts,
                                const int32_t* offsets, const uint8_t* pool, size_t S, size_t woff0, size_t woff1,
@@ -447,17 +448,6 @@ int forward_experts(moe_ctx* c, const void* hidden, int T, const int32_t* slot_r
           moe_launch_gemm_pf(g.wfmt, 0, c->n_cu, c->wl, tile_counts, c->offsets, c->slot_pool, b.S, b.w[2], 0, c->A,
                              nullptr, g.I, g.H, c->Z, s));
     if ((rc = tail_gemm(0, c->A, nullptr, nullptr, c->Z))) return rc;
-  } else if (g.wfmt == MOE_W_BF16 && T <= moe_gemv_max_tokens()) {
-    // at most 4 tokens per expert: matrix-vector products, one weight load
-    // per weight, no partial tiles; grids sized by the bound on the active
-    // experts (min(T*k, E))
-    const long ne = std::min<long>((long)T * g.k, g.E);
-    STAGE(c, MOE_STAGE_GEMM1, s,
-          moe_launch_gemv(1, (int)(ne * (g.I / 8)), c->wl, c->counts, c->offsets, c->slot_pool, b.S, b.w[0], b.w[1],
-                          hidden, c->perm_tok, g.H, g.I, c->A, s));
-    STAGE(c, MOE_STAGE_GEMM2, s,
-          moe_launch_gemv(0, (int)(ne * (g.H / 16)), c->wl, c->counts, c->offsets, c->slot_pool, b.S, b.w[2], 0,
-                          c->A, nullptr, g.I, g.H, c->Z, s));
   } else {
     // 16-bit tokens gathered through perm_tok for GEMM 1 (bf16, or the
     // hidden rows converted to fp16 for NVFP4's fp16 MFMA), A in the same
@@ -466,6 +456,21 @@ int forward_experts(moe_ctx* c, const void* hidden, int T, const int32_t* slot_r
     if (g.wfmt == MOE_W_NVFP4) {
       STAGE(c, MOE_STAGE_QUANT_X, s, moe_launch_cvt_f16(hidden, (long)T * g.H, c->Xq, s));
       x16 = c->Xq;
+    }
+    if (T <= moe_gemv_max_tokens() && dfmt != WFMT_MXFP4_A16) {
+      // at most 4 tokens per expert: matrix-vector products, one weight
+      // load per weight, no partial tiles; grids sized by the bound on the
+      // active experts (min(T*k, E)).  Not for MXFP4: its 32 weights per
+      // lane and step meet four token loads each, and the T=1 layer of the
+      // MXFP4 shape took 91 us this way against 78 with the MFMA kernel.
+      const long ne = std::min<long>((long)T * g.k, g.E);
+      STAGE(c, MOE_STAGE_GEMM1, s,
+            moe_launch_gemv(dfmt, 1, (int)(ne * (g.I / 8)), c->wl, c->counts, c->offsets, c->slot_pool, b.S, b.w[0],
+                            b.w[1], b.s[0], b.s[1], x16, c->perm_tok, g.H, g.I, c->A, s));
+      STAGE(c, MOE_STAGE_GEMM2, s,
+            moe_launch_gemv(dfmt, 0, (int)(ne * (g.H / 16)), c->wl, c->counts, c->offsets, c->slot_pool, b.S, b.w[2],
+                            0, b.s[2], 0, c->A, nullptr, g.I, g.H, c->Z, s));
+      return MOE_OK;
     }
     // Equal ranges of the weight stream balance the bytes over every CU but
     // cut items, whose partial tiles a second launch adds (6-8 us with its

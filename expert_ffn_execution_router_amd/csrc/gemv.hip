@@ -1,25 +1,36 @@
 // Slot-indexed grouped expert GEMMs for the smallest batches (at most 4
-// tokens per expert), bf16 weights, as matrix-vector products on the
-// vector ALUs.
+// tokens per expert) as matrix-vector products on the vector ALUs, for
+// every weight format.
 //
 // Method (paper.oopus.info review of FreeToken, section 2.5: the GPU
 // evaluates every expert of G = H u F for the tokens routed to it; SwiGLU
 // expert): the same two GEMMs as the small-batch MFMA kernel,
-//   GEMM 1: A = silu(x W_gate^T) * (x W_up^T), rounded to bf16,
+//   GEMM 1: A = silu(x W_gate^T) * (x W_up^T), rounded to the A type,
 //   GEMM 2: Z = A W_down^T, rounded to bf16,
-// with fp32 products and sums.  With one to four tokens an expert's weight
-// rows are each used one to four times: the work is the weight stream.
-// The MFMA kernel moves every weight through LDS and multiplies 16-token
-// tiles that are almost all padding; here each weight is loaded once into
-// registers and multiplied by the token values it meets.
+// with exact fp32 products and fp32 sums, and the same rounding points as
+// that kernel: bf16 tokens and A for bf16, fp8 and MXFP4 weights; fp16
+// tokens (the hidden rows converted once per call) and fp16 A for NVFP4,
+// whose fp32 matrix scales multiply the sums (gate and up before the
+// SwiGLU, down before rounding Z).  With one to four tokens an expert's
+// weight rows are each used one to four times: the work is the weight
+// stream.  The MFMA kernel moves every weight through LDS and multiplies
+// 16-token tiles that are almost all padding; here each weight is loaded
+// once into registers, dequantised exactly and multiplied by the token
+// values it meets.
 //   * an item is (active expert, 16 weight rows): for GEMM 1 the gate and up
 //     rows of 8 features, for GEMM 2 16 output columns; one workgroup of
 //     4 waves per item, each wave 4 rows;
 //   * a row is read by 16 consecutive lanes, 16 bytes each per step, so one
 //     wave instruction covers four 256-byte row segments (the pattern that
-//     streams HBM fastest with the nontemporal hint); lane i takes the bytes
-//     [256 s + 16 i, +16) of its row at step s, and the same K range of
-//     each token row (cached: every item of the expert reads it);
+//     streams HBM fastest with the nontemporal hint); lane i takes bytes
+//     [256 s + 16 i, +16) of its row at step s: V = 8 (bf16), 16 (fp8) or
+//     32 (E2M1) weights, and the same V token values of each token row
+//     (cached: every item of the expert reads them);
+//   * scales: fp8 - the fp32 scale of the 128x128 block multiplies the
+//     lane's 16 products (all in one 128-K block); MXFP4 - the E8M0 scale
+//     of the lane's 32 weights (one block) goes into the conversion (a
+//     power of two: exact); NVFP4 - the E4M3 scales of the lane's two
+//     16-weight blocks multiply their products;
 //   * the 16 partial sums of a row are added across the lanes with four
 //     DPP moves (xor 1, xor 2, rotate 4, rotate 8 inside the 16-lane row);
 //     GEMM 1's up sums move to the gate lanes with one lane shuffle.
@@ -50,33 +61,74 @@ DEV float row16_sum(float v) {
   return dpp_add(v, 3);
 }
 
-// acc += the 8 products of weights w and tokens x (bf16 pairs, exact fp32
-// products, fp32 sums in element order).
-DEV float dot8(i32x4_t w, i32x4_t x, float acc) {
+DEV float silu_mul(float g, float u) { return g / (1.0f + expf(-g)) * u; }
+
+// Eight token values (bf16 or fp16 bits, element order) as fp32, exact.
+template <bool F16>
+DEV void tok8(i32x4_t x, float (&v)[8]) {
 #pragma unroll
   for (int q = 0; q < 4; ++q) {
-    const uint32_t a = (uint32_t)w[q], b = (uint32_t)x[q];
-    acc = fmaf(__uint_as_float(a << 16), __uint_as_float(b << 16), acc);
-    acc = fmaf(__uint_as_float(a & 0xffff0000u), __uint_as_float(b & 0xffff0000u), acc);
+    const uint32_t b = (uint32_t)x[q];
+    if (F16) {
+      const f16x2_t h = __builtin_bit_cast(f16x2_t, b);
+      v[2 * q] = (float)h[0];
+      v[2 * q + 1] = (float)h[1];
+    } else {
+      v[2 * q] = __uint_as_float(b << 16);
+      v[2 * q + 1] = __uint_as_float(b & 0xffff0000u);
+    }
   }
-  return acc;
 }
 
-DEV float silu_mul(float g, float u) { return g / (1.0f + expf(-g)) * u; }
+// acc += the 8 E2M1 weights of word w (two per byte, even element in the
+// low nibble; the conversion scaled by s, a power of two) times x.
+DEV float fp4_dot8(uint32_t w, float s, const float (&x)[8], float acc) {
+  // the byte selector must be a literal
+  const f32x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, s, 0);
+  const f32x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, s, 1);
+  const f32x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, s, 2);
+  const f32x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f32_fp4(w, s, 3);
+  acc = fmaf(p0[0], x[0], acc);
+  acc = fmaf(p0[1], x[1], acc);
+  acc = fmaf(p1[0], x[2], acc);
+  acc = fmaf(p1[1], x[3], acc);
+  acc = fmaf(p2[0], x[4], acc);
+  acc = fmaf(p2[1], x[5], acc);
+  acc = fmaf(p3[0], x[6], acc);
+  return fmaf(p3[1], x[7], acc);
+}
+
+// acc += the 4 E4M3 weights of word w (element order) times x[0..3].
+DEV float fp8_dot4(uint32_t w, const float* x, float acc) {
+  const f32x2_t lo = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, 1.0f, false);
+  const f32x2_t hi = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(w, 1.0f, true);
+  acc = fmaf(lo[0], x[0], acc);
+  acc = fmaf(lo[1], x[1], acc);
+  acc = fmaf(hi[0], x[2], acc);
+  return fmaf(hi[1], x[3], acc);
+}
 
 }  // namespace
 
-// GATED: out = A (bf16 [rows, N], N = I) from X = the hidden rows (bf16
-// [T, K]) gathered through row_tok, weights gate at woff0 and up at woff1.
-// Otherwise out = Z (bf16 [rows, N], N = H) from X = A in grouped order,
-// weights at woff0.  Rows of expert e are offsets[e] .. + counts[e] <= 4.
-// K % 128 == 0; N % 8 (gated) or 16.  The grid may exceed the items
-// (n_act * N / 8 or N / 16): the extra workgroups leave at once.
-template <bool GATED>
+// FMT: WFMT_BF16, WFMT_FP8_A16, WFMT_MXFP4_A16 or WFMT_NVFP4.  GATED:
+// out = A ([rows, N], N = I; fp16 for NVFP4, else bf16) from X = the token
+// rows ([T, K], fp16 for NVFP4, else bf16) gathered through row_tok, weights
+// gate at woff0 / soff0 and up at woff1 / soff1.  Otherwise out = Z (bf16
+// [rows, N], N = H) from X = A in grouped order, weights at woff0 / soff0.
+// Rows of expert e are offsets[e] .. + counts[e] <= 4.  K is a multiple of
+// the values in 16 bytes of a row (8, 16 or 32; a row's last 256-byte
+// segment may be partial: lanes past it contribute nothing); N % 8 (gated)
+// or 16.  The grid may exceed the items (n_act * N / 8 or N / 16): the extra
+// workgroups leave at once.
+template <int FMT, bool GATED>
 __global__ void __launch_bounds__(256)
-gemv_bf16(const WorkList* __restrict__ wl, const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
-          const uint8_t* __restrict__ pool, size_t S, size_t woff0, size_t woff1, const uint16_t* __restrict__ X,
-          const int32_t* __restrict__ row_tok, int K, int N, uint16_t* __restrict__ out) {
+gemv_dec(const WorkList* __restrict__ wl, const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
+         const uint8_t* __restrict__ pool, size_t S, size_t woff0, size_t woff1, size_t soff0, size_t soff1,
+         const uint16_t* __restrict__ X, const int32_t* __restrict__ row_tok, int K, int N, uint16_t* __restrict__ out) {
+  constexpr bool NV = FMT == WFMT_NVFP4;
+  constexpr bool W4 = NV || FMT == WFMT_MXFP4_A16;
+  constexpr int V = FMT == WFMT_BF16 ? 8 : (W4 ? 32 : 16);       // weights per lane and step
+  constexpr int WB2 = FMT == WFMT_BF16 ? 4 : (W4 ? 1 : 2);        // weight bytes per value, times 2
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int g = lane >> 4, li = lane & 15;
   const int per_e = GATED ? N / 8 : N / 16;          // items per expert
@@ -86,73 +138,166 @@ gemv_bf16(const WorkList* __restrict__ wl, const int32_t* __restrict__ counts, c
   const int e = wl->act_e[a];
   const uint8_t* blob = pool + (size_t)wl->act_slot[a] * S;
   const int row0 = offsets[e], cnt = min(counts[e], GV_MAXT);
-  // this lane group's weight row
-  int wrow, feat;
-  const uint8_t* wbase;
+  // this lane group's weight row: matrix m, row feat
+  int m, feat;
   if (GATED) {
     feat = blk * 8 + 2 * wave + (g & 1);
-    wbase = blob + ((g >> 1) ? woff1 : woff0);
-    wrow = feat;
+    m = g >> 1;
   } else {
     feat = blk * 16 + 4 * wave + g;
-    wbase = blob + woff0;
-    wrow = feat;
+    m = 0;
   }
-  const uint8_t* wr = wbase + (size_t)wrow * K * 2 + li * 16;
+  const size_t woff = m ? woff1 : woff0, soff = m ? soff1 : soff0;
+  const uint8_t* wr = blob + woff + (size_t)feat * K * WB2 / 2 + li * 16;
   const uint8_t* xr[GV_MAXT];
 #pragma unroll
   for (int t = 0; t < GV_MAXT; ++t) {
     const int r = row0 + min(t, cnt - 1);
     const int xrow = GATED ? row_tok[r] : r;
-    xr[t] = (const uint8_t*)X + (size_t)xrow * K * 2 + li * 16;
+    xr[t] = (const uint8_t*)X + (size_t)xrow * K * 2 + li * (2 * V);
   }
+  // the row's scales (per step: fp8 block scale, MXFP4 E8M0 byte, NVFP4 two E4M3 bytes)
+  const float* s8 = nullptr;
+  const uint8_t* sb = nullptr;
+  if (FMT == WFMT_FP8_A16) s8 = (const float*)(blob + soff) + (size_t)(feat / 128) * (K / 128);
+  if (W4) sb = blob + soff + (size_t)feat * (K / (NV ? 16 : 32));
   float acc[GV_MAXT] = {0.f, 0.f, 0.f, 0.f};
-  const int nstep = K / 128;                          // 256-byte segments per row
+  const int rowb = K * WB2 / 2;                      // weight bytes per row
+  const int nstep = (rowb + 255) / 256;              // 256-byte segments per row (the last may be partial)
+  const i32x4_t z4 = {0, 0, 0, 0};
   for (int s0 = 0; s0 < nstep; s0 += GV_BLK) {
     i32x4_t wv[GV_BLK];
+    float sc[GV_BLK][2];
+    bool ok[GV_BLK];
 #pragma unroll
-    for (int j = 0; j < GV_BLK; ++j)
-      if (s0 + j < nstep) wv[j] = ld16_nt(wr + (s0 + j) * 256);
+    for (int j = 0; j < GV_BLK; ++j) {
+      if (s0 + j >= nstep) break;
+      const int s = s0 + j;
+      ok[j] = s * 256 + 16 * li < rowb;              // this lane's 16 bytes lie in the row
+      sc[j][0] = sc[j][1] = 0.0f;
+      wv[j] = ok[j] ? ld16_nt(wr + s * 256) : z4;
+      if (!ok[j]) continue;
+      if (FMT == WFMT_FP8_A16) {
+        sc[j][0] = s8[(s * 256 + 16 * li) / 128];
+      } else if (FMT == WFMT_MXFP4_A16) {
+        sc[j][0] = e8m0_to_f32(sb[s * 16 + li]);
+      } else if (NV) {
+        const f32x2_t p = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(*(const uint16_t*)(sb + s * 32 + 2 * li), 1.0f,
+                                                                   false);
+        sc[j][0] = p[0];
+        sc[j][1] = p[1];
+      }
+    }
 #pragma unroll
     for (int t = 0; t < GV_MAXT; ++t) {
       if (t >= cnt) break;
 #pragma unroll
-      for (int j = 0; j < GV_BLK; ++j)
-        if (s0 + j < nstep) acc[t] = dot8(wv[j], ld16(xr[t] + (s0 + j) * 256), acc[t]);
+      for (int j = 0; j < GV_BLK; ++j) {
+        if (s0 + j >= nstep) break;
+        if (!ok[j]) continue;                         // past the row: contributes nothing
+        const uint8_t* xs = xr[t] + (s0 + j) * (32 * V);
+        if (FMT == WFMT_BF16) {
+          float xv[8];
+          tok8<false>(ld16(xs), xv);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            const uint32_t w = (uint32_t)wv[j][q];
+            acc[t] = fmaf(__uint_as_float(w << 16), xv[2 * q], acc[t]);
+            acc[t] = fmaf(__uint_as_float(w & 0xffff0000u), xv[2 * q + 1], acc[t]);
+          }
+        } else if (FMT == WFMT_FP8_A16) {
+          float p = 0.0f;
+#pragma unroll
+          for (int h = 0; h < 2; ++h) {
+            float xv[8];
+            tok8<false>(ld16(xs + 16 * h), xv);
+            p = fp8_dot4((uint32_t)wv[j][2 * h], xv, p);
+            p = fp8_dot4((uint32_t)wv[j][2 * h + 1], xv + 4, p);
+          }
+          acc[t] = fmaf(p, sc[j][0], acc[t]);
+        } else if (FMT == WFMT_MXFP4_A16) {
+#pragma unroll
+          for (int h = 0; h < 4; ++h) {
+            float xv[8];
+            tok8<false>(ld16(xs + 16 * h), xv);
+            acc[t] = fp4_dot8((uint32_t)wv[j][h], sc[j][0], xv, acc[t]);
+          }
+        } else {
+#pragma unroll
+          for (int b = 0; b < 2; ++b) {               // two 16-weight blocks, each with its scale
+            float p = 0.0f;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              float xv[8];
+              tok8<true>(ld16(xs + 32 * b + 16 * h), xv);
+              p = fp4_dot8((uint32_t)wv[j][2 * b + h], 1.0f, xv, p);
+            }
+            acc[t] = fmaf(p, sc[j][b], acc[t]);
+          }
+        }
+      }
     }
   }
 #pragma unroll
   for (int t = 0; t < GV_MAXT; ++t) acc[t] = row16_sum(acc[t]);
+  float ts = 1.0f, tsu = 1.0f;                        // NVFP4 matrix scales
+  if (NV) {
+    const size_t n = (size_t)K * N;
+    const float* tsc = (const float*)(blob + 3 * (n / 2) + 3 * (n / 16));
+    ts = GATED ? tsc[0] : tsc[2];
+    tsu = tsc[1];
+  }
   if (GATED) {
     // lane groups 0/1 hold the gate sums of features 2w, 2w+1; groups 2/3
     // the up sums of the same features, 32 lanes on
 #pragma unroll
     for (int t = 0; t < GV_MAXT; ++t) {
       const float u = __shfl_down(acc[t], 32, 64);
-      if (t < cnt && g < 2 && li == 0)
-        out[(size_t)(row0 + t) * N + feat] = f32_to_bf16_bits(silu_mul(acc[t], u));
+      if (t < cnt && g < 2 && li == 0) {
+        const float v = NV ? silu_mul(acc[t] * ts, u * tsu) : silu_mul(acc[t], u);
+        out[(size_t)(row0 + t) * N + feat] = NV ? (uint16_t)(pack_f16x2(v, 0.0f) & 0xffffu) : f32_to_bf16_bits(v);
+      }
     }
   } else {
 #pragma unroll
     for (int t = 0; t < GV_MAXT; ++t)
-      if (t < cnt && li == 0) out[(size_t)(row0 + t) * N + feat] = f32_to_bf16_bits(acc[t]);
+      if (t < cnt && li == 0) out[(size_t)(row0 + t) * N + feat] = f32_to_bf16_bits(NV ? acc[t] * ts : acc[t]);
   }
 }
 
-// grid: at least the items (active experts x N / 8 for GEMM 1, N / 16 for
-// GEMM 2); every expert must have at most 4 routed rows.
-extern "C" hipError_t moe_launch_gemv(int gated, int grid, const WorkList* wl, const int32_t* counts,
-                                      const int32_t* offsets, const uint8_t* pool, size_t S, size_t woff0,
-                                      size_t woff1, const void* X, const int32_t* row_tok, int K, int N, void* out,
-                                      hipStream_t s) {
-  if (grid < 1 || K % 128 || N % (gated ? 8 : 16) || (gated && !row_tok)) return hipErrorInvalidValue;
+namespace {
+template <int FMT>
+hipError_t launch_gemv(int gated, int grid, const WorkList* wl, const int32_t* counts, const int32_t* offsets,
+                       const uint8_t* pool, size_t S, size_t woff0, size_t woff1, size_t soff0, size_t soff1,
+                       const void* X, const int32_t* row_tok, int K, int N, void* out, hipStream_t s) {
   if (gated)
-    gemv_bf16<true><<<grid, 256, 0, s>>>(wl, counts, offsets, pool, S, woff0, woff1, (const uint16_t*)X, row_tok,
-                                         K, N, (uint16_t*)out);
+    gemv_dec<FMT, true><<<grid, 256, 0, s>>>(wl, counts, offsets, pool, S, woff0, woff1, soff0, soff1,
+                                             (const uint16_t*)X, row_tok, K, N, (uint16_t*)out);
   else
-    gemv_bf16<false><<<grid, 256, 0, s>>>(wl, counts, offsets, pool, S, woff0, woff1, (const uint16_t*)X, row_tok,
-                                          K, N, (uint16_t*)out);
+    gemv_dec<FMT, false><<<grid, 256, 0, s>>>(wl, counts, offsets, pool, S, woff0, woff1, soff0, soff1,
+                                              (const uint16_t*)X, row_tok, K, N, (uint16_t*)out);
   return hipGetLastError();
+}
+}  // namespace
+
+// fmt: WFMT_BF16, WFMT_FP8_A16, WFMT_MXFP4_A16 or WFMT_NVFP4.  grid: at
+// least the items (active experts x N / 8 for GEMM 1, N / 16 for GEMM 2);
+// every expert must have at most 4 routed rows.
+extern "C" hipError_t moe_launch_gemv(int fmt, int gated, int grid, const WorkList* wl, const int32_t* counts,
+                                      const int32_t* offsets, const uint8_t* pool, size_t S, size_t woff0,
+                                      size_t woff1, size_t soff0, size_t soff1, const void* X,
+                                      const int32_t* row_tok, int K, int N, void* out, hipStream_t s) {
+  const int kq = fmt == WFMT_BF16 ? 8 : (fmt == WFMT_FP8_A16 ? 16 : 32);   // K per 16 bytes of a row
+  if (grid < 1 || K % kq || N % (gated ? 8 : 16) || (gated && !row_tok)) return hipErrorInvalidValue;
+#define MOE_GV_ARGS gated, grid, wl, counts, offsets, pool, S, woff0, woff1, soff0, soff1, X, row_tok, K, N, out, s
+  switch (fmt) {
+    case WFMT_BF16: return launch_gemv<WFMT_BF16>(MOE_GV_ARGS);
+    case WFMT_FP8_A16: return launch_gemv<WFMT_FP8_A16>(MOE_GV_ARGS);
+    case WFMT_MXFP4_A16: return launch_gemv<WFMT_MXFP4_A16>(MOE_GV_ARGS);
+    case WFMT_NVFP4: return launch_gemv<WFMT_NVFP4>(MOE_GV_ARGS);
+    default: return hipErrorInvalidValue;
+  }
+#undef MOE_GV_ARGS
 }
 
 extern "C" int moe_gemv_max_tokens() { return GV_MAXT; }
