@@ -457,12 +457,10 @@ int forward_experts(moe_ctx* c, const void* hidden, int T, const int32_t* slot_r
       STAGE(c, MOE_STAGE_QUANT_X, s, moe_launch_cvt_f16(hidden, (long)T * g.H, c->Xq, s));
       x16 = c->Xq;
     }
-    if (T <= moe_gemv_max_tokens() && dfmt != WFMT_MXFP4_A16) {
+    if (T <= moe_gemv_max_tokens()) {
       // at most 4 tokens per expert: matrix-vector products, one weight
       // load per weight, no partial tiles; grids sized by the bound on the
-      // active experts (min(T*k, E)).  Not for MXFP4: its 32 weights per
-      // lane and step meet four token loads each, and the T=1 layer of the
-      // MXFP4 shape took 91 us this way against 78 with the MFMA kernel.
+      // active experts (min(T*k, E))
       const long ne = std::min<long>((long)T * g.k, g.E);
       STAGE(c, MOE_STAGE_GEMM1, s,
             moe_launch_gemv(dfmt, 1, (int)(ne * (g.I / 8)), c->wl, c->counts, c->offsets, c->slot_pool, b.S, b.w[0],

@@ -20,26 +20,28 @@
 //   * an item is (active expert, 16 weight rows): for GEMM 1 the gate and up
 //     rows of 8 features, for GEMM 2 16 output columns; one workgroup of
 //     4 waves per item, each wave 4 rows;
-//   * a row is read by 16 consecutive lanes, 16 bytes each per step, so one
-//     wave instruction covers four 256-byte row segments (the pattern that
-//     streams HBM fastest with the nontemporal hint); lane i takes bytes
-//     [256 s + 16 i, +16) of its row at step s: V = 8 (bf16), 16 (fp8) or
-//     32 (E2M1) weights, and the same V token values of each token row
-//     (cached: every item of the expert reads them);
+//   * at step s lane l takes bytes [1024 s + 16 l, +16) of each of its
+//     wave's four rows: V = 8 (bf16), 16 (fp8) or 32 (E2M1) weights per row,
+//     so one wave instruction reads 1 KiB of one row, four 256-byte
+//     segments with the nontemporal hint; the V token values of that K range
+//     are loaded once per token (cached: every item of the expert reads
+//     them) and serve all four rows;
 //   * scales: fp8 - the fp32 scale of the 128x128 block multiplies the
 //     lane's 16 products (all in one 128-K block); MXFP4 - the E8M0 scale
 //     of the lane's 32 weights (one block) goes into the conversion (a
 //     power of two: exact); NVFP4 - the E4M3 scales of the lane's two
 //     16-weight blocks multiply their products;
-//   * the 16 partial sums of a row are added across the lanes with four
-//     DPP moves (xor 1, xor 2, rotate 4, rotate 8 inside the 16-lane row);
-//     GEMM 1's up sums move to the gate lanes with one lane shuffle.
+//   * the 64 partial sums of a row are added across the lanes with four
+//     DPP moves inside each 16-lane row (xor 1, xor 2, rotate 4, rotate 8)
+//     and two lane shuffles across the rows; a wave's four rows of GEMM 1
+//     are the gate and up rows of two features, so the SwiGLU needs no
+//     exchange.
 #include "common.h"
 
 namespace {
 
 constexpr int GV_MAXT = 4;      // tokens per expert
-constexpr int GV_BLK = 8;       // 16-byte steps in flight per lane
+constexpr int GV_BLK = 2;       // steps in flight (a step: 16 bytes of each of the wave's 4 rows per lane)
 
 DEV float dpp_add(float v, int ctrl_sel) {
   int x = __float_as_int(v);
@@ -130,7 +132,6 @@ gemv_dec(const WorkList* __restrict__ wl, const int32_t* __restrict__ counts, co
   constexpr int V = FMT == WFMT_BF16 ? 8 : (W4 ? 32 : 16);       // weights per lane and step
   constexpr int WB2 = FMT == WFMT_BF16 ? 4 : (W4 ? 1 : 2);        // weight bytes per value, times 2
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int g = lane >> 4, li = lane & 15;
   const int per_e = GATED ? N / 8 : N / 16;          // items per expert
   const int it = blockIdx.x;
   if (it >= wl->n_act * per_e) return;
@@ -138,54 +139,59 @@ gemv_dec(const WorkList* __restrict__ wl, const int32_t* __restrict__ counts, co
   const int e = wl->act_e[a];
   const uint8_t* blob = pool + (size_t)wl->act_slot[a] * S;
   const int row0 = offsets[e], cnt = min(counts[e], GV_MAXT);
-  // this lane group's weight row: matrix m, row feat
-  int m, feat;
-  if (GATED) {
-    feat = blk * 8 + 2 * wave + (g & 1);
-    m = g >> 1;
-  } else {
-    feat = blk * 16 + 4 * wave + g;
-    m = 0;
+  const int rowb = K * WB2 / 2;                      // weight bytes per row
+  // the wave's four rows: GATED gate f0, gate f0+1, up f0, up f0+1
+  // (f0 = 8 blk + 2 wave); otherwise columns 16 blk + 4 wave + q
+  const uint8_t* wr[4];
+  const float* s8[4];
+  const uint8_t* sb[4];
+#pragma unroll
+  for (int q = 0; q < 4; ++q) {
+    const int feat = GATED ? blk * 8 + 2 * wave + (q & 1) : blk * 16 + 4 * wave + q;
+    const int m = GATED ? (q >> 1) : 0;
+    const size_t woff = m ? woff1 : woff0, soff = m ? soff1 : soff0;
+    wr[q] = blob + woff + (size_t)feat * rowb + lane * 16;
+    s8[q] = (const float*)(blob + soff) + (size_t)(feat / 128) * (K / 128);
+    sb[q] = blob + soff + (size_t)feat * (K / (NV ? 16 : 32));
   }
-  const size_t woff = m ? woff1 : woff0, soff = m ? soff1 : soff0;
-  const uint8_t* wr = blob + woff + (size_t)feat * K * WB2 / 2 + li * 16;
   const uint8_t* xr[GV_MAXT];
 #pragma unroll
   for (int t = 0; t < GV_MAXT; ++t) {
     const int r = row0 + min(t, cnt - 1);
     const int xrow = GATED ? row_tok[r] : r;
-    xr[t] = (const uint8_t*)X + (size_t)xrow * K * 2 + li * (2 * V);
+    xr[t] = (const uint8_t*)X + (size_t)xrow * K * 2 + lane * (2 * V);
   }
-  // the row's scales (per step: fp8 block scale, MXFP4 E8M0 byte, NVFP4 two E4M3 bytes)
-  const float* s8 = nullptr;
-  const uint8_t* sb = nullptr;
-  if (FMT == WFMT_FP8_A16) s8 = (const float*)(blob + soff) + (size_t)(feat / 128) * (K / 128);
-  if (W4) sb = blob + soff + (size_t)feat * (K / (NV ? 16 : 32));
-  float acc[GV_MAXT] = {0.f, 0.f, 0.f, 0.f};
-  const int rowb = K * WB2 / 2;                      // weight bytes per row
-  const int nstep = (rowb + 255) / 256;              // 256-byte segments per row (the last may be partial)
+  float acc[4][GV_MAXT];
+#pragma unroll
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int t = 0; t < GV_MAXT; ++t) acc[q][t] = 0.0f;
+  const int nstep = (rowb + 1023) / 1024;            // 1 KiB of each row per step (the last may be partial)
   const i32x4_t z4 = {0, 0, 0, 0};
   for (int s0 = 0; s0 < nstep; s0 += GV_BLK) {
-    i32x4_t wv[GV_BLK];
-    float sc[GV_BLK][2];
+    i32x4_t wv[GV_BLK][4];
+    float sc[GV_BLK][4][2];
     bool ok[GV_BLK];
 #pragma unroll
     for (int j = 0; j < GV_BLK; ++j) {
       if (s0 + j >= nstep) break;
       const int s = s0 + j;
-      ok[j] = s * 256 + 16 * li < rowb;              // this lane's 16 bytes lie in the row
-      sc[j][0] = sc[j][1] = 0.0f;
-      wv[j] = ok[j] ? ld16_nt(wr + s * 256) : z4;
-      if (!ok[j]) continue;
-      if (FMT == WFMT_FP8_A16) {
-        sc[j][0] = s8[(s * 256 + 16 * li) / 128];
-      } else if (FMT == WFMT_MXFP4_A16) {
-        sc[j][0] = e8m0_to_f32(sb[s * 16 + li]);
-      } else if (NV) {
-        const f32x2_t p = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(*(const uint16_t*)(sb + s * 32 + 2 * li), 1.0f,
-                                                                   false);
-        sc[j][0] = p[0];
-        sc[j][1] = p[1];
+      const int v0 = V * (64 * s + lane);            // first value of the lane's 16 bytes
+      ok[j] = 1024 * s + 16 * lane < rowb;           // they lie in the row
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        sc[j][q][0] = sc[j][q][1] = 0.0f;
+        wv[j][q] = ok[j] ? ld16_nt(wr[q] + 1024 * s) : z4;
+        if (!ok[j]) continue;
+        if (FMT == WFMT_FP8_A16) {
+          sc[j][q][0] = s8[q][v0 / 128];
+        } else if (FMT == WFMT_MXFP4_A16) {
+          sc[j][q][0] = e8m0_to_f32(sb[q][v0 / 32]);
+        } else if (NV) {
+          const f32x2_t p = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(*(const uint16_t*)(sb[q] + v0 / 16), 1.0f, false);
+          sc[j][q][0] = p[0];
+          sc[j][q][1] = p[1];
+        }
       }
     }
 #pragma unroll
@@ -195,51 +201,63 @@ gemv_dec(const WorkList* __restrict__ wl, const int32_t* __restrict__ counts, co
       for (int j = 0; j < GV_BLK; ++j) {
         if (s0 + j >= nstep) break;
         if (!ok[j]) continue;                         // past the row: contributes nothing
-        const uint8_t* xs = xr[t] + (s0 + j) * (32 * V);
+        const uint8_t* xs = xr[t] + (s0 + j) * (128 * V);
         if (FMT == WFMT_BF16) {
           float xv[8];
           tok8<false>(ld16(xs), xv);
 #pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            const uint32_t w = (uint32_t)wv[j][q];
-            acc[t] = fmaf(__uint_as_float(w << 16), xv[2 * q], acc[t]);
-            acc[t] = fmaf(__uint_as_float(w & 0xffff0000u), xv[2 * q + 1], acc[t]);
-          }
+          for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+              const uint32_t w = (uint32_t)wv[j][q][c];
+              acc[q][t] = fmaf(__uint_as_float(w << 16), xv[2 * c], acc[q][t]);
+              acc[q][t] = fmaf(__uint_as_float(w & 0xffff0000u), xv[2 * c + 1], acc[q][t]);
+            }
         } else if (FMT == WFMT_FP8_A16) {
-          float p = 0.0f;
+          float xv[2][8];
+          tok8<false>(ld16(xs), xv[0]);
+          tok8<false>(ld16(xs + 16), xv[1]);
 #pragma unroll
-          for (int h = 0; h < 2; ++h) {
-            float xv[8];
-            tok8<false>(ld16(xs + 16 * h), xv);
-            p = fp8_dot4((uint32_t)wv[j][2 * h], xv, p);
-            p = fp8_dot4((uint32_t)wv[j][2 * h + 1], xv + 4, p);
-          }
-          acc[t] = fmaf(p, sc[j][0], acc[t]);
-        } else if (FMT == WFMT_MXFP4_A16) {
-#pragma unroll
-          for (int h = 0; h < 4; ++h) {
-            float xv[8];
-            tok8<false>(ld16(xs + 16 * h), xv);
-            acc[t] = fp4_dot8((uint32_t)wv[j][h], sc[j][0], xv, acc[t]);
-          }
-        } else {
-#pragma unroll
-          for (int b = 0; b < 2; ++b) {               // two 16-weight blocks, each with its scale
+          for (int q = 0; q < 4; ++q) {
             float p = 0.0f;
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
-              float xv[8];
-              tok8<true>(ld16(xs + 32 * b + 16 * h), xv);
-              p = fp4_dot8((uint32_t)wv[j][2 * b + h], 1.0f, xv, p);
+              p = fp8_dot4((uint32_t)wv[j][q][2 * h], xv[h], p);
+              p = fp8_dot4((uint32_t)wv[j][q][2 * h + 1], xv[h] + 4, p);
             }
-            acc[t] = fmaf(p, sc[j][b], acc[t]);
+            acc[q][t] = fmaf(p, sc[j][q][0], acc[q][t]);
+          }
+        } else {
+          float xv[4][8];
+#pragma unroll
+          for (int h = 0; h < 4; ++h) tok8<NV>(ld16(xs + 16 * h), xv[h]);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            if (NV) {
+#pragma unroll
+              for (int bb = 0; bb < 2; ++bb) {        // two 16-weight blocks, each with its scale
+                float p = fp4_dot8((uint32_t)wv[j][q][2 * bb], 1.0f, xv[2 * bb], 0.0f);
+                p = fp4_dot8((uint32_t)wv[j][q][2 * bb + 1], 1.0f, xv[2 * bb + 1], p);
+                acc[q][t] = fmaf(p, sc[j][q][bb], acc[q][t]);
+              }
+            } else {
+#pragma unroll
+              for (int h = 0; h < 4; ++h) acc[q][t] = fp4_dot8((uint32_t)wv[j][q][h], sc[j][q][0], xv[h], acc[q][t]);
+            }
           }
         }
       }
     }
   }
+  // sums over the 64 lanes: the 16 of each DPP row, then across the rows
 #pragma unroll
-  for (int t = 0; t < GV_MAXT; ++t) acc[t] = row16_sum(acc[t]);
+  for (int q = 0; q < 4; ++q)
+#pragma unroll
+    for (int t = 0; t < GV_MAXT; ++t) {
+      float v = row16_sum(acc[q][t]);
+      v += __shfl_xor(v, 16, 64);
+      acc[q][t] = v + __shfl_xor(v, 32, 64);
+    }
   float ts = 1.0f, tsu = 1.0f;                        // NVFP4 matrix scales
   if (NV) {
     const size_t n = (size_t)K * N;
@@ -247,21 +265,22 @@ gemv_dec(const WorkList* __restrict__ wl, const int32_t* __restrict__ counts, co
     ts = GATED ? tsc[0] : tsc[2];
     tsu = tsc[1];
   }
-  if (GATED) {
-    // lane groups 0/1 hold the gate sums of features 2w, 2w+1; groups 2/3
-    // the up sums of the same features, 32 lanes on
+  if (lane != 0) return;
 #pragma unroll
-    for (int t = 0; t < GV_MAXT; ++t) {
-      const float u = __shfl_down(acc[t], 32, 64);
-      if (t < cnt && g < 2 && li == 0) {
-        const float v = NV ? silu_mul(acc[t] * ts, u * tsu) : silu_mul(acc[t], u);
-        out[(size_t)(row0 + t) * N + feat] = NV ? (uint16_t)(pack_f16x2(v, 0.0f) & 0xffffu) : f32_to_bf16_bits(v);
+  for (int t = 0; t < GV_MAXT; ++t) {
+    if (t >= cnt) break;
+    if (GATED) {
+#pragma unroll
+      for (int c = 0; c < 2; ++c) {
+        const float v = NV ? silu_mul(acc[c][t] * ts, acc[2 + c][t] * tsu) : silu_mul(acc[c][t], acc[2 + c][t]);
+        out[(size_t)(row0 + t) * N + blk * 8 + 2 * wave + c] =
+            NV ? (uint16_t)(pack_f16x2(v, 0.0f) & 0xffffu) : f32_to_bf16_bits(v);
       }
-    }
-  } else {
+    } else {
 #pragma unroll
-    for (int t = 0; t < GV_MAXT; ++t)
-      if (t < cnt && li == 0) out[(size_t)(row0 + t) * N + feat] = f32_to_bf16_bits(NV ? acc[t] * ts : acc[t]);
+      for (int q = 0; q < 4; ++q)
+        out[(size_t)(row0 + t) * N + blk * 16 + 4 * wave + q] = f32_to_bf16_bits(NV ? acc[q][t] * ts : acc[q][t]);
+    }
   }
 }
 
