@@ -41,7 +41,7 @@ size_t moe_dec_part_bytes();
 int moe_dec_max_ns(int fmt);
 int moe_pf_tile_tokens();
 int moe_gemv_max_tokens();
-hipError_t moe_launch_gemv(int fmt, int gated, int grid, const WorkList* wl, const int32_t* counts,
+hipError_t moe_launch_gemv(int fmt, int max_rows, int gated, int grid, const WorkList* wl, const int32_t* counts,
                            const int32_t* offsets, const uint8_t* pool, size_t S, size_t woff0, size_t woff1,
                            size_t soff0, size_t soff1, const void* X, const int32_t* row_tok, int K, int N, void* out,
                            hipStream_t s);
@@ -458,15 +458,15 @@ int forward_experts(moe_ctx* c, const void* hidden, int T, const int32_t* slot_r
       x16 = c->Xq;
     }
     if (T <= moe_gemv_max_tokens()) {
-      // at most 4 tokens per expert: matrix-vector products, one weight
+      // at most 8 tokens per expert: matrix-vector products, one weight
       // load per weight, no partial tiles; grids sized by the bound on the
       // active experts (min(T*k, E))
       const long ne = std::min<long>((long)T * g.k, g.E);
       STAGE(c, MOE_STAGE_GEMM1, s,
-            moe_launch_gemv(dfmt, 1, (int)(ne * (g.I / 8)), c->wl, c->counts, c->offsets, c->slot_pool, b.S, b.w[0],
+            moe_launch_gemv(dfmt, T, 1, (int)(ne * (g.I / 8)), c->wl, c->counts, c->offsets, c->slot_pool, b.S, b.w[0],
                             b.w[1], b.s[0], b.s[1], x16, c->perm_tok, g.H, g.I, c->A, s));
       STAGE(c, MOE_STAGE_GEMM2, s,
-            moe_launch_gemv(dfmt, 0, (int)(ne * (g.H / 16)), c->wl, c->counts, c->offsets, c->slot_pool, b.S, b.w[2],
+            moe_launch_gemv(dfmt, T, 0, (int)(ne * (g.H / 16)), c->wl, c->counts, c->offsets, c->slot_pool, b.S, b.w[2],
                             0, b.s[2], 0, c->A, nullptr, g.I, g.H, c->Z, s));
       return MOE_OK;
     }

@@ -1,4 +1,4 @@
-// Slot-indexed grouped expert GEMMs for the smallest batches (at most 4
+// Slot-indexed grouped expert GEMMs for the smallest batches (at most 8
 // tokens per expert) as matrix-vector products on the vector ALUs, for
 // every weight format.
 //
@@ -11,12 +11,12 @@
 // that kernel: bf16 tokens and A for bf16, fp8 and MXFP4 weights; fp16
 // tokens (the hidden rows converted once per call) and fp16 A for NVFP4,
 // whose fp32 matrix scales multiply the sums (gate and up before the
-// SwiGLU, down before rounding Z).  With one to four tokens an expert's
-// weight rows are each used one to four times: the work is the weight
+// SwiGLU, down before rounding Z).  With one to eight tokens an expert's
+// weight rows are each used one to eight times: the work is the weight
 // stream.  The MFMA kernel moves every weight through LDS and multiplies
 // 16-token tiles that are almost all padding; here each weight is loaded
 // once into registers, dequantised exactly and multiplied by the token
-// values it meets.
+// values it meets (one to eight token rows).
 //   * an item is (active expert, 16 weight rows): for GEMM 1 the gate and up
 //     rows of 8 features, for GEMM 2 16 output columns; one workgroup of
 //     4 waves per item, each wave 4 rows;
@@ -40,7 +40,7 @@
 
 namespace {
 
-constexpr int GV_MAXT = 4;      // tokens per expert
+constexpr int GV_MAXT = 8;      // tokens per expert (instances for 4 and 8)
 constexpr int GV_BLK = 2;       // steps in flight (a step: 16 bytes of each of the wave's 4 rows per lane)
 
 DEV float dpp_add(float v, int ctrl_sel) {
@@ -117,12 +117,12 @@ DEV float fp8_dot4(uint32_t w, const float* x, float acc) {
 // rows ([T, K], fp16 for NVFP4, else bf16) gathered through row_tok, weights
 // gate at woff0 / soff0 and up at woff1 / soff1.  Otherwise out = Z (bf16
 // [rows, N], N = H) from X = A in grouped order, weights at woff0 / soff0.
-// Rows of expert e are offsets[e] .. + counts[e] <= 4.  K is a multiple of
+// Rows of expert e are offsets[e] .. + counts[e] <= MT (4 or 8).  K is a multiple of
 // the values in 16 bytes of a row (8, 16 or 32; a row's last 256-byte
 // segment may be partial: lanes past it contribute nothing); N % 8 (gated)
 // or 16.  The grid may exceed the items (n_act * N / 8 or N / 16): the extra
 // workgroups leave at once.
-template <int FMT, bool GATED>
+template <int FMT, bool GATED, int MT>
 __global__ void __launch_bounds__(256)
 gemv_dec(const WorkList* __restrict__ wl, const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
          const uint8_t* __restrict__ pool, size_t S, size_t woff0, size_t woff1, size_t soff0, size_t soff1,
@@ -138,7 +138,7 @@ gemv_dec(const WorkList* __restrict__ wl, const int32_t* __restrict__ counts, co
   const int a = it / per_e, blk = it - a * per_e;
   const int e = wl->act_e[a];
   const uint8_t* blob = pool + (size_t)wl->act_slot[a] * S;
-  const int row0 = offsets[e], cnt = min(counts[e], GV_MAXT);
+  const int row0 = offsets[e], cnt = min(counts[e], MT);
   const int rowb = K * WB2 / 2;                      // weight bytes per row
   // the wave's four rows: GATED gate f0, gate f0+1, up f0, up f0+1
   // (f0 = 8 blk + 2 wave); otherwise columns 16 blk + 4 wave + q
@@ -154,18 +154,18 @@ gemv_dec(const WorkList* __restrict__ wl, const int32_t* __restrict__ counts, co
     s8[q] = (const float*)(blob + soff) + (size_t)(feat / 128) * (K / 128);
     sb[q] = blob + soff + (size_t)feat * (K / (NV ? 16 : 32));
   }
-  const uint8_t* xr[GV_MAXT];
+  const uint8_t* xr[MT];
 #pragma unroll
-  for (int t = 0; t < GV_MAXT; ++t) {
+  for (int t = 0; t < MT; ++t) {
     const int r = row0 + min(t, cnt - 1);
     const int xrow = GATED ? row_tok[r] : r;
     xr[t] = (const uint8_t*)X + (size_t)xrow * K * 2 + lane * (2 * V);
   }
-  float acc[4][GV_MAXT];
+  float acc[4][MT];
 #pragma unroll
   for (int q = 0; q < 4; ++q)
 #pragma unroll
-    for (int t = 0; t < GV_MAXT; ++t) acc[q][t] = 0.0f;
+    for (int t = 0; t < MT; ++t) acc[q][t] = 0.0f;
   const int nstep = (rowb + 1023) / 1024;            // 1 KiB of each row per step (the last may be partial)
   const i32x4_t z4 = {0, 0, 0, 0};
   for (int s0 = 0; s0 < nstep; s0 += GV_BLK) {
@@ -195,7 +195,7 @@ gemv_dec(const WorkList* __restrict__ wl, const int32_t* __restrict__ counts, co
       }
     }
 #pragma unroll
-    for (int t = 0; t < GV_MAXT; ++t) {
+    for (int t = 0; t < MT; ++t) {
       if (t >= cnt) break;
 #pragma unroll
       for (int j = 0; j < GV_BLK; ++j) {
@@ -253,7 +253,7 @@ gemv_dec(const WorkList* __restrict__ wl, const int32_t* __restrict__ counts, co
 #pragma unroll
   for (int q = 0; q < 4; ++q)
 #pragma unroll
-    for (int t = 0; t < GV_MAXT; ++t) {
+    for (int t = 0; t < MT; ++t) {
       float v = row16_sum(acc[q][t]);
       v += __shfl_xor(v, 16, 64);
       acc[q][t] = v + __shfl_xor(v, 32, 64);
@@ -267,7 +267,7 @@ gemv_dec(const WorkList* __restrict__ wl, const int32_t* __restrict__ counts, co
   }
   if (lane != 0) return;
 #pragma unroll
-  for (int t = 0; t < GV_MAXT; ++t) {
+  for (int t = 0; t < MT; ++t) {
     if (t >= cnt) break;
     if (GATED) {
 #pragma unroll
@@ -285,30 +285,45 @@ gemv_dec(const WorkList* __restrict__ wl, const int32_t* __restrict__ counts, co
 }
 
 namespace {
-template <int FMT>
-hipError_t launch_gemv(int gated, int grid, const WorkList* wl, const int32_t* counts, const int32_t* offsets,
-                       const uint8_t* pool, size_t S, size_t woff0, size_t woff1, size_t soff0, size_t soff1,
-                       const void* X, const int32_t* row_tok, int K, int N, void* out, hipStream_t s) {
+template <int FMT, int MT>
+hipError_t launch_gemv_mt(int gated, int grid, const WorkList* wl, const int32_t* counts, const int32_t* offsets,
+                          const uint8_t* pool, size_t S, size_t woff0, size_t woff1, size_t soff0, size_t soff1,
+                          const void* X, const int32_t* row_tok, int K, int N, void* out, hipStream_t s) {
   if (gated)
-    gemv_dec<FMT, true><<<grid, 256, 0, s>>>(wl, counts, offsets, pool, S, woff0, woff1, soff0, soff1,
-                                             (const uint16_t*)X, row_tok, K, N, (uint16_t*)out);
+    gemv_dec<FMT, true, MT><<<grid, 256, 0, s>>>(wl, counts, offsets, pool, S, woff0, woff1, soff0, soff1,
+                                                 (const uint16_t*)X, row_tok, K, N, (uint16_t*)out);
   else
-    gemv_dec<FMT, false><<<grid, 256, 0, s>>>(wl, counts, offsets, pool, S, woff0, woff1, soff0, soff1,
-                                              (const uint16_t*)X, row_tok, K, N, (uint16_t*)out);
+    gemv_dec<FMT, false, MT><<<grid, 256, 0, s>>>(wl, counts, offsets, pool, S, woff0, woff1, soff0, soff1,
+                                                  (const uint16_t*)X, row_tok, K, N, (uint16_t*)out);
   return hipGetLastError();
+}
+
+// Four tokens' accumulators keep more waves per SIMD than eight: the
+// 4-token instance serves every batch it can.
+template <int FMT>
+hipError_t launch_gemv(int max_rows, int gated, int grid, const WorkList* wl, const int32_t* counts,
+                       const int32_t* offsets, const uint8_t* pool, size_t S, size_t woff0, size_t woff1, size_t soff0,
+                       size_t soff1, const void* X, const int32_t* row_tok, int K, int N, void* out, hipStream_t s) {
+  if (max_rows <= 4)
+    return launch_gemv_mt<FMT, 4>(gated, grid, wl, counts, offsets, pool, S, woff0, woff1, soff0, soff1, X, row_tok,
+                                  K, N, out, s);
+  return launch_gemv_mt<FMT, 8>(gated, grid, wl, counts, offsets, pool, S, woff0, woff1, soff0, soff1, X, row_tok,
+                                K, N, out, s);
 }
 }  // namespace
 
 // fmt: WFMT_BF16, WFMT_FP8_A16, WFMT_MXFP4_A16 or WFMT_NVFP4.  grid: at
 // least the items (active experts x N / 8 for GEMM 1, N / 16 for GEMM 2);
-// every expert must have at most 4 routed rows.
-extern "C" hipError_t moe_launch_gemv(int fmt, int gated, int grid, const WorkList* wl, const int32_t* counts,
+// max_rows: a bound on the routed rows of any expert (at most 8; the batch
+// size bounds it).
+extern "C" hipError_t moe_launch_gemv(int fmt, int max_rows, int gated, int grid, const WorkList* wl, const int32_t* counts,
                                       const int32_t* offsets, const uint8_t* pool, size_t S, size_t woff0,
                                       size_t woff1, size_t soff0, size_t soff1, const void* X,
                                       const int32_t* row_tok, int K, int N, void* out, hipStream_t s) {
   const int kq = fmt == WFMT_BF16 ? 8 : (fmt == WFMT_FP8_A16 ? 16 : 32);   // K per 16 bytes of a row
-  if (grid < 1 || K % kq || N % (gated ? 8 : 16) || (gated && !row_tok)) return hipErrorInvalidValue;
-#define MOE_GV_ARGS gated, grid, wl, counts, offsets, pool, S, woff0, woff1, soff0, soff1, X, row_tok, K, N, out, s
+  if (grid < 1 || max_rows < 1 || max_rows > GV_MAXT || K % kq || N % (gated ? 8 : 16) || (gated && !row_tok))
+    return hipErrorInvalidValue;
+#define MOE_GV_ARGS max_rows, gated, grid, wl, counts, offsets, pool, S, woff0, woff1, soff0, soff1, X, row_tok, K, N, out, s
   switch (fmt) {
     case WFMT_BF16: return launch_gemv<WFMT_BF16>(MOE_GV_ARGS);
     case WFMT_FP8_A16: return launch_gemv<WFMT_FP8_A16>(MOE_GV_ARGS);

@@ -91,7 +91,7 @@ def test_decode_config2_shape_T64():
         s.close()
 
 
-@pytest.mark.parametrize("T", [1, 3, 4, 8])
+@pytest.mark.parametrize("T", [1, 3, 4, 8, 16])
 def test_decode_config2_shape_small_T(T):
     """The decode shape at the smallest batches (at most 4 tokens per expert:
     the matrix-vector kernels; 8: the MFMA kernel), every item covered."""
