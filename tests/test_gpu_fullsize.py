@@ -93,8 +93,8 @@ def test_decode_config2_shape_T64():
 
 @pytest.mark.parametrize("T", [1, 3, 4, 8, 16])
 def test_decode_config2_shape_small_T(T):
-    """The decode shape at the smallest batches (at most 4 tokens per expert:
-    the matrix-vector kernels; 8: the MFMA kernel), every item covered."""
+    """The decode shape at the smallest batches (up to 8 tokens: the
+    matrix-vector kernels; 16: the MFMA kernel), every item covered."""
     print(f"decode config-2 shape T={T}", flush=True)
     cfg = _fullsize(2, L=1)
     s = Setup(cfg, seed=5, max_tokens=64, host_threads=8)
