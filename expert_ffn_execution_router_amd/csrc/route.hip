@@ -465,7 +465,10 @@ extern "C" hipError_t moe_launch_topk_group(const float* z, int T, int E, int k,
                                             WorkList* wl, int* err, hipStream_t s) {
   if (T < 1 || T > TG_MAX_T || E > 256 || k > 8) return hipErrorInvalidValue;
   const TailSplit ts{nullptr, nullptr, nullptr, nullptr, 1, 0};
-  topk_group_kernel<<<1, 1024, 0, s>>>(z, T, E, k, ids, w, miss_mask, slot_row, mb, counts, offsets, pos, perm_tok,
+  // one wave per token, at least the four waves the grouping needs (fewer
+  // waves make its barriers cheaper)
+  topk_group_kernel<<<1, 64 * (T < 4 ? 4 : T), 0, s>>>(z, T, E, k, ids, w, miss_mask, slot_row, mb, counts, offsets,
+                                                       pos, perm_tok,
                                        wl, err, ts);
   return hipGetLastError();
 }
