@@ -41,6 +41,11 @@ size_t moe_dec_part_bytes();
 int moe_dec_max_ns(int fmt);
 int moe_pf_tile_tokens();
 int moe_gemv_max_tokens();
+hipError_t moe_launch_gemv_down_combine(int fmt, const int32_t* ids, const float* w, const int32_t* pos,
+                                        const uint32_t* miss_mask, const int32_t* slot_row, const uint8_t* pool,
+                                        size_t S, size_t woff, size_t soff, const void* A, int T, int k, int K, int N,
+                                        const float* hp, const int32_t* hp_count, void* out, float* out_f32,
+                                        hipStream_t s);
 hipError_t moe_launch_gemv(int fmt, int max_rows, int gated, int grid, const WorkList* wl, const int32_t* counts,
                            const int32_t* offsets, const uint8_t* pool, size_t S, size_t woff0, size_t woff1,
                            size_t soff0, size_t soff1, const void* X, const int32_t* row_tok, int K, int N, void* out,
@@ -244,6 +249,8 @@ struct moe_ctx {
   // optional per-stage timing (moe_profile_begin / moe_profile_end)
   bool prof_on = false;
   unsigned prof_mask = 0;               // stages timed (bit per MOE_STAGE_*)
+  // the last forward left its down GEMM to the combine (matrix-vector path): its format
+  int down_fused = -1;
   bool fills_pending = false;           // fill_evt recorded since the last wait on it
   std::vector<hipEvent_t> prof_ev;      // 2 per record
   std::vector<int> prof_stage;
@@ -354,8 +361,9 @@ HostFfnShape host_shape(const moe_config& c, size_t S) { return HostFfnShape{c.w
 constexpr int FUSED_TOPK_T = 16;
 
 int forward_experts(moe_ctx* c, const void* hidden, int T, const int32_t* slot_row, const uint32_t* mask,
-                    hipStream_t s, bool fused_topk = false) {
+                    hipStream_t s, bool fused_topk = false, bool fuse_down = false) {
   const moe_config& g = c->cfg;
+  c->down_fused = -1;
   if (c->fills_pending) {                 // weights copied by slot_pool_* / the decode plan
     HIPCHK(c, hipStreamWaitEvent(s, c->fill_evt, 0));
     c->fills_pending = false;
@@ -465,6 +473,10 @@ int forward_experts(moe_ctx* c, const void* hidden, int T, const int32_t* slot_r
       STAGE(c, MOE_STAGE_GEMM1, s,
             moe_launch_gemv(dfmt, T, 1, (int)(ne * (g.I / 8)), c->wl, c->counts, c->offsets, c->slot_pool, b.S, b.w[0],
                             b.w[1], b.s[0], b.s[1], x16, c->perm_tok, g.H, g.I, c->A, s));
+      if (fuse_down && g.k <= 8) {      // the combine runs the down GEMM (one launch fewer)
+        c->down_fused = dfmt;
+        return MOE_OK;
+      }
       STAGE(c, MOE_STAGE_GEMM2, s,
             moe_launch_gemv(dfmt, T, 0, (int)(ne * (g.H / 16)), c->wl, c->counts, c->offsets, c->slot_pool, b.S, b.w[2],
                             0, b.s[2], 0, c->A, nullptr, g.I, g.H, c->Z, s));
@@ -520,6 +532,15 @@ int route_only(moe_ctx* c, const void* hidden, const float* R, const float* bias
 
 int combine(moe_ctx* c, const uint32_t* mask, const int32_t* row, const float* hp, int T, void* out, hipStream_t s,
             const int32_t* hp_count = nullptr, float* out_f32 = nullptr) {
+  if (c->down_fused >= 0) {
+    const int f = c->down_fused;
+    c->down_fused = -1;
+    const BlobLayout& b = c->bl;
+    STAGE(c, MOE_STAGE_COMBINE, s,
+          moe_launch_gemv_down_combine(f, c->ids, c->w, c->pos, mask, row, c->slot_pool, b.S, b.w[2], b.s[2], c->A, T,
+                                       c->cfg.k, c->cfg.I, c->cfg.H, hp, hp_count, out, out_f32, s));
+    return MOE_OK;
+  }
   STAGE(c, MOE_STAGE_COMBINE, s,
         moe_launch_combine(c->Z, c->ids, c->w, c->pos, mask, row, hp, hp_count, T, c->cfg.k, c->cfg.H,
                            (uint16_t*)out, out_f32, s));
@@ -961,7 +982,7 @@ int moe_layer_forward(moe_ctx* c, int layer, const void* hidden, const float* R,
   const bool fz = T <= FUSED_TOPK_T;
   rc = route_only(c, hidden, R, bias, T, s, !fz);
   if (rc) return rc;
-  rc = forward_experts(c, hidden, T, slot_row, miss_mask, s, fz);
+  rc = forward_experts(c, hidden, T, slot_row, miss_mask, s, fz, true);
   if (rc) return rc;
   return combine(c, miss_mask, slot_row, host_partial, T, out, s);
 }
@@ -994,7 +1015,7 @@ int moe_fwd_on_ws(const moe_config* cfg, int max_T, uint8_t* ws, size_t part_byt
   c.part_bytes = part_bytes;
   const bool fz = T <= FUSED_TOPK_T;
   int rc = route_only(&c, hidden, R, bias, T, s, !fz);
-  if (!rc) rc = forward_experts(&c, hidden, T, slot_row, miss_mask, s, fz);
+  if (!rc) rc = forward_experts(&c, hidden, T, slot_row, miss_mask, s, fz, true);
   if (!rc) rc = combine(&c, miss_mask, slot_row, hp, T, out, s);
   if (rc && msg) *msg = "a kernel launch of the forward failed";
   return rc;

@@ -284,6 +284,166 @@ gemv_dec(const WorkList* __restrict__ wl, const int32_t* __restrict__ counts, co
   }
 }
 
+// The down GEMM and the weighted combine in one launch, for the resident
+// forward at the smallest batches: workgroup (4 output columns h0..h0+3,
+// token t), wave j = the token's choice j.  Wave j computes the 4 columns of
+// Z for (t, j) exactly as gemv_dec does for that row (same lane layout,
+// steps and sums, the NVFP4 down scale on the sum, rounded to bf16); wave
+// 0 then adds w_tj * z_j over j = 0..7 in order, choices that ran on the
+// host (miss_mask) or past k adding zero, then the host partial, as the
+// combine kernel does:
+//   out[t, h] = bf16( sum_j w_tj z_tj[h] + host_partial[t, h] ).
+// out_f32 (optional): the unrounded sum instead.  A: the GEMM 1 output in
+// grouped order (row pos[t, j]); K = I, N = H, N % 4 == 0.
+template <int FMT>
+__global__ void __launch_bounds__(512)
+gemv_down_combine(const int32_t* __restrict__ ids, const float* __restrict__ w, const int32_t* __restrict__ pos,
+                  const uint32_t* __restrict__ miss_mask, const int32_t* __restrict__ slot_row,
+                  const uint8_t* __restrict__ pool, size_t S, size_t woff, size_t soff,
+                  const uint16_t* __restrict__ A, int k, int K, int N, const float* hp,
+                  const int32_t* __restrict__ hp_count, uint16_t* __restrict__ out, float* out_f32) {
+  constexpr bool NV = FMT == WFMT_NVFP4;
+  constexpr bool W4 = NV || FMT == WFMT_MXFP4_A16;
+  constexpr int V = FMT == WFMT_BF16 ? 8 : (W4 ? 32 : 16);
+  constexpr int WB2 = FMT == WFMT_BF16 ? 4 : (W4 ? 1 : 2);
+  __shared__ float zs[8][4];
+  __shared__ int us[8];
+  const int j = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int h0 = blockIdx.x * 4, t = blockIdx.y;
+  const size_t a = (size_t)t * k + j;
+  const int e = ids[a];
+  const bool host = miss_mask && ((miss_mask[e >> 5] >> (e & 31)) & 1u);   // computed by the host
+  const int slot = slot_row[e];
+  const bool use = !host && slot >= 0;                                    // not resident: error flagged elsewhere
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  if (use) {
+    const uint8_t* blob = pool + (size_t)slot * S;
+    const int rowb = K * WB2 / 2;
+    const uint8_t* wr[4];
+    const float* s8[4];
+    const uint8_t* sb[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int feat = h0 + q;
+      wr[q] = blob + woff + (size_t)feat * rowb + lane * 16;
+      s8[q] = (const float*)(blob + soff) + (size_t)(feat / 128) * (K / 128);
+      sb[q] = blob + soff + (size_t)feat * (K / (NV ? 16 : 32));
+    }
+    const uint8_t* xr = (const uint8_t*)A + (size_t)pos[a] * K * 2 + lane * (2 * V);
+    const int nstep = (rowb + 1023) / 1024;
+    const i32x4_t z4 = {0, 0, 0, 0};
+    for (int s0 = 0; s0 < nstep; s0 += GV_BLK) {
+      i32x4_t wv[GV_BLK][4];
+      float sc[GV_BLK][4][2];
+      bool ok[GV_BLK];
+#pragma unroll
+      for (int jj = 0; jj < GV_BLK; ++jj) {
+        if (s0 + jj >= nstep) break;
+        const int st = s0 + jj;
+        const int v0 = V * (64 * st + lane);
+        ok[jj] = 1024 * st + 16 * lane < rowb;
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          sc[jj][q][0] = sc[jj][q][1] = 0.0f;
+          wv[jj][q] = ok[jj] ? ld16_nt(wr[q] + 1024 * st) : z4;
+          if (!ok[jj]) continue;
+          if (FMT == WFMT_FP8_A16) {
+            sc[jj][q][0] = s8[q][v0 / 128];
+          } else if (FMT == WFMT_MXFP4_A16) {
+            sc[jj][q][0] = e8m0_to_f32(sb[q][v0 / 32]);
+          } else if (NV) {
+            const f32x2_t p = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(*(const uint16_t*)(sb[q] + v0 / 16), 1.0f, false);
+            sc[jj][q][0] = p[0];
+            sc[jj][q][1] = p[1];
+          }
+        }
+      }
+#pragma unroll
+      for (int jj = 0; jj < GV_BLK; ++jj) {
+        if (s0 + jj >= nstep) break;
+        if (!ok[jj]) continue;
+        const uint8_t* xs = xr + (s0 + jj) * (128 * V);
+        if (FMT == WFMT_BF16) {
+          float xv[8];
+          tok8<false>(ld16(xs), xv);
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+#pragma unroll
+            for (int c = 0; c < 4; ++c) {
+              const uint32_t wq = (uint32_t)wv[jj][q][c];
+              acc[q] = fmaf(__uint_as_float(wq << 16), xv[2 * c], acc[q]);
+              acc[q] = fmaf(__uint_as_float(wq & 0xffff0000u), xv[2 * c + 1], acc[q]);
+            }
+        } else if (FMT == WFMT_FP8_A16) {
+          float xv[2][8];
+          tok8<false>(ld16(xs), xv[0]);
+          tok8<false>(ld16(xs + 16), xv[1]);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            float p = 0.0f;
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+              p = fp8_dot4((uint32_t)wv[jj][q][2 * h], xv[h], p);
+              p = fp8_dot4((uint32_t)wv[jj][q][2 * h + 1], xv[h] + 4, p);
+            }
+            acc[q] = fmaf(p, sc[jj][q][0], acc[q]);
+          }
+        } else {
+          float xv[4][8];
+#pragma unroll
+          for (int h = 0; h < 4; ++h) tok8<NV>(ld16(xs + 16 * h), xv[h]);
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            if (NV) {
+#pragma unroll
+              for (int bb = 0; bb < 2; ++bb) {
+                float p = fp4_dot8((uint32_t)wv[jj][q][2 * bb], 1.0f, xv[2 * bb], 0.0f);
+                p = fp4_dot8((uint32_t)wv[jj][q][2 * bb + 1], 1.0f, xv[2 * bb + 1], p);
+                acc[q] = fmaf(p, sc[jj][q][bb], acc[q]);
+              }
+            } else {
+#pragma unroll
+              for (int h = 0; h < 4; ++h) acc[q] = fp4_dot8((uint32_t)wv[jj][q][h], sc[jj][q][0], xv[h], acc[q]);
+            }
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      float v = row16_sum(acc[q]);
+      v += __shfl_xor(v, 16, 64);
+      acc[q] = v + __shfl_xor(v, 32, 64);
+    }
+    if (NV) {
+      const size_t n = (size_t)K * N;
+      const float ts = ((const float*)(blob + 3 * (n / 2) + 3 * (n / 16)))[2];
+#pragma unroll
+      for (int q = 0; q < 4; ++q) acc[q] *= ts;
+    }
+  }
+  if (lane < 4) {
+    float zq = acc[0];
+#pragma unroll
+    for (int q = 1; q < 4; ++q) zq = lane == q ? acc[q] : zq;
+    zs[j][lane] = use ? bf16_bits_to_f32(f32_to_bf16_bits(zq)) : 0.0f;
+  }
+  if (lane == 0) us[j] = use ? 1 : 0;
+  __syncthreads();
+  if (j != 0 || lane >= 4) return;
+  float o = 0.0f;
+#pragma unroll
+  for (int jj = 0; jj < 8; ++jj) {
+    const bool u = jj < k && us[jj < k ? jj : 0];
+    const float lo = jj < k ? w[(size_t)t * k + jj] * zs[jj < k ? jj : 0][lane] : 0.0f;
+    o += u ? lo : 0.0f;
+  }
+  const int h = h0 + lane;
+  if (hp && (!hp_count || *hp_count > 0)) o += hp[(size_t)t * N + h];
+  if (out_f32) out_f32[(size_t)t * N + h] = o;
+  else out[(size_t)t * N + h] = f32_to_bf16_bits(o);
+}
+
 namespace {
 template <int FMT, int MT>
 hipError_t launch_gemv_mt(int gated, int grid, const WorkList* wl, const int32_t* counts, const int32_t* offsets,
@@ -332,6 +492,29 @@ extern "C" hipError_t moe_launch_gemv(int fmt, int max_rows, int gated, int grid
     default: return hipErrorInvalidValue;
   }
 #undef MOE_GV_ARGS
+}
+
+// The down GEMM of a matrix-vector forward fused with the combine (see
+// gemv_down_combine): fmt as moe_launch_gemv; k <= 8; N % 4 == 0.
+extern "C" hipError_t moe_launch_gemv_down_combine(int fmt, const int32_t* ids, const float* w, const int32_t* pos,
+                                                   const uint32_t* miss_mask, const int32_t* slot_row,
+                                                   const uint8_t* pool, size_t S, size_t woff, size_t soff,
+                                                   const void* A, int T, int k, int K, int N, const float* hp,
+                                                   const int32_t* hp_count, void* out, float* out_f32, hipStream_t s) {
+  const int kq = fmt == WFMT_BF16 ? 8 : (fmt == WFMT_FP8_A16 ? 16 : 32);
+  if (T < 1 || k < 1 || k > 8 || N % 4 || K % kq) return hipErrorInvalidValue;
+  const dim3 grid(N / 4, T);
+#define MOE_DC_ARGS ids, w, pos, miss_mask, slot_row, pool, S, woff, soff, (const uint16_t*)A, k, K, N, hp, hp_count, \
+                    (uint16_t*)out, out_f32
+  switch (fmt) {
+    case WFMT_BF16: gemv_down_combine<WFMT_BF16><<<grid, 64 * k, 0, s>>>(MOE_DC_ARGS); break;
+    case WFMT_FP8_A16: gemv_down_combine<WFMT_FP8_A16><<<grid, 64 * k, 0, s>>>(MOE_DC_ARGS); break;
+    case WFMT_MXFP4_A16: gemv_down_combine<WFMT_MXFP4_A16><<<grid, 64 * k, 0, s>>>(MOE_DC_ARGS); break;
+    case WFMT_NVFP4: gemv_down_combine<WFMT_NVFP4><<<grid, 64 * k, 0, s>>>(MOE_DC_ARGS); break;
+    default: return hipErrorInvalidValue;
+  }
+#undef MOE_DC_ARGS
+  return hipGetLastError();
 }
 
 extern "C" int moe_gemv_max_tokens() { return GV_MAXT; }

@@ -125,12 +125,13 @@ def test_not_resident_expert_raises_flag(setups):
     assert s.rt.check_device_error() == 0          # the flag was cleared
 
 
-def test_host_partial_is_added_exactly(setups):
+@pytest.mark.parametrize("name,T", [("bf16_tiny", 16), ("bf16_tiny", 3), ("nvfp4_small", 2), ("fp8_small", 4)])
+def test_host_partial_is_added_exactly(setups, name, T):
     """out(mask, host_partial) == out(all on GPU) up to the rounding of the
     host-computed experts: with the mask covering experts {0,1} and the host
-    partial taken from the oracle, the result stays within tolerance."""
-    s = _get(setups, "bf16_tiny")
-    T = 16
+    partial taken from the oracle, the result stays within tolerance (T <= 8:
+    the down GEMM and the combine in one launch)."""
+    s = _get(setups, name)
     x, xd = s.hidden(T, tag=7)
     ref = s.oracle(0, x, "exact")
     from oracle import moe as M
