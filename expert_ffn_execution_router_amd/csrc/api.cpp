@@ -473,7 +473,7 @@ int forward_experts(moe_ctx* c, const void* hidden, int T, const int32_t* slot_r
       STAGE(c, MOE_STAGE_GEMM1, s,
             moe_launch_gemv(dfmt, T, 1, (int)(ne * (g.I / 8)), c->wl, c->counts, c->offsets, c->slot_pool, b.S, b.w[0],
                             b.w[1], b.s[0], b.s[1], x16, c->perm_tok, g.H, g.I, c->A, s));
-      if (fuse_down && g.k <= 8) {      // the combine runs the down GEMM (one launch fewer)
+      if (fuse_down && T <= 8 && g.k <= 8) {      // the combine runs the down GEMM (one launch fewer)
         c->down_fused = dfmt;
         return MOE_OK;
       }

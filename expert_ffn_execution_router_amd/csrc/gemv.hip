@@ -138,148 +138,154 @@ gemv_dec(const WorkList* __restrict__ wl, const int32_t* __restrict__ counts, co
   const int a = it / per_e, blk = it - a * per_e;
   const int e = wl->act_e[a];
   const uint8_t* blob = pool + (size_t)wl->act_slot[a] * S;
-  const int row0 = offsets[e], cnt = min(counts[e], MT);
   const int rowb = K * WB2 / 2;                      // weight bytes per row
-  // the wave's four rows: GATED gate f0, gate f0+1, up f0, up f0+1
-  // (f0 = 8 blk + 2 wave); otherwise columns 16 blk + 4 wave + q
-  const uint8_t* wr[4];
-  const float* s8[4];
-  const uint8_t* sb[4];
-#pragma unroll
-  for (int q = 0; q < 4; ++q) {
-    const int feat = GATED ? blk * 8 + 2 * wave + (q & 1) : blk * 16 + 4 * wave + q;
-    const int m = GATED ? (q >> 1) : 0;
-    const size_t woff = m ? woff1 : woff0, soff = m ? soff1 : soff0;
-    wr[q] = blob + woff + (size_t)feat * rowb + lane * 16;
-    s8[q] = (const float*)(blob + soff) + (size_t)(feat / 128) * (K / 128);
-    sb[q] = blob + soff + (size_t)feat * (K / (NV ? 16 : 32));
-  }
-  const uint8_t* xr[MT];
-#pragma unroll
-  for (int t = 0; t < MT; ++t) {
-    const int r = row0 + min(t, cnt - 1);
-    const int xrow = GATED ? row_tok[r] : r;
-    xr[t] = (const uint8_t*)X + (size_t)xrow * K * 2 + lane * (2 * V);
-  }
-  float acc[4][MT];
-#pragma unroll
-  for (int q = 0; q < 4; ++q)
-#pragma unroll
-    for (int t = 0; t < MT; ++t) acc[q][t] = 0.0f;
-  const int nstep = (rowb + 1023) / 1024;            // 1 KiB of each row per step (the last may be partial)
-  const i32x4_t z4 = {0, 0, 0, 0};
-  for (int s0 = 0; s0 < nstep; s0 += GV_BLK) {
-    i32x4_t wv[GV_BLK][4];
-    float sc[GV_BLK][4][2];
-    bool ok[GV_BLK];
-#pragma unroll
-    for (int j = 0; j < GV_BLK; ++j) {
-      if (s0 + j >= nstep) break;
-      const int s = s0 + j;
-      const int v0 = V * (64 * s + lane);            // first value of the lane's 16 bytes
-      ok[j] = 1024 * s + 16 * lane < rowb;           // they lie in the row
-#pragma unroll
-      for (int q = 0; q < 4; ++q) {
-        sc[j][q][0] = sc[j][q][1] = 0.0f;
-        wv[j][q] = ok[j] ? ld16_nt(wr[q] + 1024 * s) : z4;
-        if (!ok[j]) continue;
-        if (FMT == WFMT_FP8_A16) {
-          sc[j][q][0] = s8[q][v0 / 128];
-        } else if (FMT == WFMT_MXFP4_A16) {
-          sc[j][q][0] = e8m0_to_f32(sb[q][v0 / 32]);
-        } else if (NV) {
-          const f32x2_t p = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(*(const uint16_t*)(sb[q] + v0 / 16), 1.0f, false);
-          sc[j][q][0] = p[0];
-          sc[j][q][1] = p[1];
-        }
-      }
+  const int rbase = offsets[e], ctot = counts[e];
+  // the expert's rows in chunks of MT (the batch bounds them by MT; a chunk
+  // loop keeps the kernel correct for any count)
+  for (int tc = 0; tc < ctot; tc += MT) {
+    const int row0 = rbase + tc, cnt = min(MT, ctot - tc);
+    // the wave's four rows: GATED gate f0, gate f0+1, up f0, up f0+1
+    // (f0 = 8 blk + 2 wave); otherwise columns 16 blk + 4 wave + q
+    const uint8_t* wr[4];
+    const float* s8[4];
+    const uint8_t* sb[4];
+  #pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int feat = GATED ? blk * 8 + 2 * wave + (q & 1) : blk * 16 + 4 * wave + q;
+      const int m = GATED ? (q >> 1) : 0;
+      const size_t woff = m ? woff1 : woff0, soff = m ? soff1 : soff0;
+      wr[q] = blob + woff + (size_t)feat * rowb + lane * 16;
+      s8[q] = (const float*)(blob + soff) + (size_t)(feat / 128) * (K / 128);
+      sb[q] = blob + soff + (size_t)feat * (K / (NV ? 16 : 32));
     }
-#pragma unroll
+    const uint8_t* xr[MT];
+  #pragma unroll
     for (int t = 0; t < MT; ++t) {
-      if (t >= cnt) break;
-#pragma unroll
+      const int r = row0 + min(t, cnt - 1);
+      const int xrow = GATED ? row_tok[r] : r;
+      xr[t] = (const uint8_t*)X + (size_t)xrow * K * 2 + lane * (2 * V);
+    }
+    float acc[4][MT];
+  #pragma unroll
+    for (int q = 0; q < 4; ++q)
+  #pragma unroll
+      for (int t = 0; t < MT; ++t) acc[q][t] = 0.0f;
+    const int nstep = (rowb + 1023) / 1024;            // 1 KiB of each row per step (the last may be partial)
+    const i32x4_t z4 = {0, 0, 0, 0};
+    for (int s0 = 0; s0 < nstep; s0 += GV_BLK) {
+      i32x4_t wv[GV_BLK][4];
+      float sc[GV_BLK][4][2];
+      bool ok[GV_BLK];
+  #pragma unroll
       for (int j = 0; j < GV_BLK; ++j) {
         if (s0 + j >= nstep) break;
-        if (!ok[j]) continue;                         // past the row: contributes nothing
-        const uint8_t* xs = xr[t] + (s0 + j) * (128 * V);
-        if (FMT == WFMT_BF16) {
-          float xv[8];
-          tok8<false>(ld16(xs), xv);
-#pragma unroll
-          for (int q = 0; q < 4; ++q)
-#pragma unroll
-            for (int c = 0; c < 4; ++c) {
-              const uint32_t w = (uint32_t)wv[j][q][c];
-              acc[q][t] = fmaf(__uint_as_float(w << 16), xv[2 * c], acc[q][t]);
-              acc[q][t] = fmaf(__uint_as_float(w & 0xffff0000u), xv[2 * c + 1], acc[q][t]);
-            }
-        } else if (FMT == WFMT_FP8_A16) {
-          float xv[2][8];
-          tok8<false>(ld16(xs), xv[0]);
-          tok8<false>(ld16(xs + 16), xv[1]);
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            float p = 0.0f;
-#pragma unroll
-            for (int h = 0; h < 2; ++h) {
-              p = fp8_dot4((uint32_t)wv[j][q][2 * h], xv[h], p);
-              p = fp8_dot4((uint32_t)wv[j][q][2 * h + 1], xv[h] + 4, p);
-            }
-            acc[q][t] = fmaf(p, sc[j][q][0], acc[q][t]);
+        const int s = s0 + j;
+        const int v0 = V * (64 * s + lane);            // first value of the lane's 16 bytes
+        ok[j] = 1024 * s + 16 * lane < rowb;           // they lie in the row
+  #pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          sc[j][q][0] = sc[j][q][1] = 0.0f;
+          wv[j][q] = ok[j] ? ld16_nt(wr[q] + 1024 * s) : z4;
+          if (!ok[j]) continue;
+          if (FMT == WFMT_FP8_A16) {
+            sc[j][q][0] = s8[q][v0 / 128];
+          } else if (FMT == WFMT_MXFP4_A16) {
+            sc[j][q][0] = e8m0_to_f32(sb[q][v0 / 32]);
+          } else if (NV) {
+            const f32x2_t p = __builtin_amdgcn_cvt_scalef32_pk_f32_fp8(*(const uint16_t*)(sb[q] + v0 / 16), 1.0f, false);
+            sc[j][q][0] = p[0];
+            sc[j][q][1] = p[1];
           }
-        } else {
-          float xv[4][8];
-#pragma unroll
-          for (int h = 0; h < 4; ++h) tok8<NV>(ld16(xs + 16 * h), xv[h]);
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            if (NV) {
-#pragma unroll
-              for (int bb = 0; bb < 2; ++bb) {        // two 16-weight blocks, each with its scale
-                float p = fp4_dot8((uint32_t)wv[j][q][2 * bb], 1.0f, xv[2 * bb], 0.0f);
-                p = fp4_dot8((uint32_t)wv[j][q][2 * bb + 1], 1.0f, xv[2 * bb + 1], p);
-                acc[q][t] = fmaf(p, sc[j][q][bb], acc[q][t]);
+        }
+      }
+  #pragma unroll
+      for (int t = 0; t < MT; ++t) {
+        if (t >= cnt) break;
+  #pragma unroll
+        for (int j = 0; j < GV_BLK; ++j) {
+          if (s0 + j >= nstep) break;
+          if (!ok[j]) continue;                         // past the row: contributes nothing
+          const uint8_t* xs = xr[t] + (s0 + j) * (128 * V);
+          if (FMT == WFMT_BF16) {
+            float xv[8];
+            tok8<false>(ld16(xs), xv);
+  #pragma unroll
+            for (int q = 0; q < 4; ++q)
+  #pragma unroll
+              for (int c = 0; c < 4; ++c) {
+                const uint32_t w = (uint32_t)wv[j][q][c];
+                acc[q][t] = fmaf(__uint_as_float(w << 16), xv[2 * c], acc[q][t]);
+                acc[q][t] = fmaf(__uint_as_float(w & 0xffff0000u), xv[2 * c + 1], acc[q][t]);
               }
-            } else {
-#pragma unroll
-              for (int h = 0; h < 4; ++h) acc[q][t] = fp4_dot8((uint32_t)wv[j][q][h], sc[j][q][0], xv[h], acc[q][t]);
+          } else if (FMT == WFMT_FP8_A16) {
+            float xv[2][8];
+            tok8<false>(ld16(xs), xv[0]);
+            tok8<false>(ld16(xs + 16), xv[1]);
+  #pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              float p = 0.0f;
+  #pragma unroll
+              for (int h = 0; h < 2; ++h) {
+                p = fp8_dot4((uint32_t)wv[j][q][2 * h], xv[h], p);
+                p = fp8_dot4((uint32_t)wv[j][q][2 * h + 1], xv[h] + 4, p);
+              }
+              acc[q][t] = fmaf(p, sc[j][q][0], acc[q][t]);
+            }
+          } else {
+            float xv[4][8];
+  #pragma unroll
+            for (int h = 0; h < 4; ++h) tok8<NV>(ld16(xs + 16 * h), xv[h]);
+  #pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              if (NV) {
+  #pragma unroll
+                for (int bb = 0; bb < 2; ++bb) {        // two 16-weight blocks, each with its scale
+                  float p = fp4_dot8((uint32_t)wv[j][q][2 * bb], 1.0f, xv[2 * bb], 0.0f);
+                  p = fp4_dot8((uint32_t)wv[j][q][2 * bb + 1], 1.0f, xv[2 * bb + 1], p);
+                  acc[q][t] = fmaf(p, sc[j][q][bb], acc[q][t]);
+                }
+              } else {
+  #pragma unroll
+                for (int h = 0; h < 4; ++h) acc[q][t] = fp4_dot8((uint32_t)wv[j][q][h], sc[j][q][0], xv[h], acc[q][t]);
+              }
             }
           }
         }
       }
     }
-  }
-  // sums over the 64 lanes: the 16 of each DPP row, then across the rows
-#pragma unroll
-  for (int q = 0; q < 4; ++q)
-#pragma unroll
-    for (int t = 0; t < MT; ++t) {
-      float v = row16_sum(acc[q][t]);
-      v += __shfl_xor(v, 16, 64);
-      acc[q][t] = v + __shfl_xor(v, 32, 64);
-    }
-  float ts = 1.0f, tsu = 1.0f;                        // NVFP4 matrix scales
-  if (NV) {
-    const size_t n = (size_t)K * N;
-    const float* tsc = (const float*)(blob + 3 * (n / 2) + 3 * (n / 16));
-    ts = GATED ? tsc[0] : tsc[2];
-    tsu = tsc[1];
-  }
-  if (lane != 0) return;
-#pragma unroll
-  for (int t = 0; t < MT; ++t) {
-    if (t >= cnt) break;
-    if (GATED) {
-#pragma unroll
-      for (int c = 0; c < 2; ++c) {
-        const float v = NV ? silu_mul(acc[c][t] * ts, acc[2 + c][t] * tsu) : silu_mul(acc[c][t], acc[2 + c][t]);
-        out[(size_t)(row0 + t) * N + blk * 8 + 2 * wave + c] =
-            NV ? (uint16_t)(pack_f16x2(v, 0.0f) & 0xffffu) : f32_to_bf16_bits(v);
+    // sums over the 64 lanes: the 16 of each DPP row, then across the rows
+  #pragma unroll
+    for (int q = 0; q < 4; ++q)
+  #pragma unroll
+      for (int t = 0; t < MT; ++t) {
+        float v = row16_sum(acc[q][t]);
+        v += __shfl_xor(v, 16, 64);
+        acc[q][t] = v + __shfl_xor(v, 32, 64);
       }
-    } else {
-#pragma unroll
-      for (int q = 0; q < 4; ++q)
-        out[(size_t)(row0 + t) * N + blk * 16 + 4 * wave + q] = f32_to_bf16_bits(NV ? acc[q][t] * ts : acc[q][t]);
+    float ts = 1.0f, tsu = 1.0f;                        // NVFP4 matrix scales
+    if (NV) {
+      const size_t n = (size_t)K * N;
+      const float* tsc = (const float*)(blob + 3 * (n / 2) + 3 * (n / 16));
+      ts = GATED ? tsc[0] : tsc[2];
+      tsu = tsc[1];
+    }
+    if (lane == 0) {
+  #pragma unroll
+    for (int t = 0; t < MT; ++t) {
+      if (t >= cnt) break;
+      if (GATED) {
+  #pragma unroll
+        for (int c = 0; c < 2; ++c) {
+          const float v = NV ? silu_mul(acc[c][t] * ts, acc[2 + c][t] * tsu) : silu_mul(acc[c][t], acc[2 + c][t]);
+          out[(size_t)(row0 + t) * N + blk * 8 + 2 * wave + c] =
+              NV ? (uint16_t)(pack_f16x2(v, 0.0f) & 0xffffu) : f32_to_bf16_bits(v);
+        }
+      } else {
+  #pragma unroll
+        for (int q = 0; q < 4; ++q)
+          out[(size_t)(row0 + t) * N + blk * 16 + 4 * wave + q] = f32_to_bf16_bits(NV ? acc[q][t] * ts : acc[q][t]);
+      }
+    }
     }
   }
 }
