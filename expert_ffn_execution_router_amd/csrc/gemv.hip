@@ -149,7 +149,7 @@ gemv_dec(const WorkList* __restrict__ wl, const int32_t* __restrict__ counts, co
     const uint8_t* wr[4];
     const float* s8[4];
     const uint8_t* sb[4];
-  #pragma unroll
+#pragma unroll
     for (int q = 0; q < 4; ++q) {
       const int feat = GATED ? blk * 8 + 2 * wave + (q & 1) : blk * 16 + 4 * wave + q;
       const int m = GATED ? (q >> 1) : 0;
@@ -159,16 +159,16 @@ gemv_dec(const WorkList* __restrict__ wl, const int32_t* __restrict__ counts, co
       sb[q] = blob + soff + (size_t)feat * (K / (NV ? 16 : 32));
     }
     const uint8_t* xr[MT];
-  #pragma unroll
+#pragma unroll
     for (int t = 0; t < MT; ++t) {
       const int r = row0 + min(t, cnt - 1);
       const int xrow = GATED ? row_tok[r] : r;
       xr[t] = (const uint8_t*)X + (size_t)xrow * K * 2 + lane * (2 * V);
     }
     float acc[4][MT];
-  #pragma unroll
+#pragma unroll
     for (int q = 0; q < 4; ++q)
-  #pragma unroll
+#pragma unroll
       for (int t = 0; t < MT; ++t) acc[q][t] = 0.0f;
     const int nstep = (rowb + 1023) / 1024;            // 1 KiB of each row per step (the last may be partial)
     const i32x4_t z4 = {0, 0, 0, 0};
@@ -176,13 +176,13 @@ gemv_dec(const WorkList* __restrict__ wl, const int32_t* __restrict__ counts, co
       i32x4_t wv[GV_BLK][4];
       float sc[GV_BLK][4][2];
       bool ok[GV_BLK];
-  #pragma unroll
+#pragma unroll
       for (int j = 0; j < GV_BLK; ++j) {
         if (s0 + j >= nstep) break;
         const int s = s0 + j;
         const int v0 = V * (64 * s + lane);            // first value of the lane's 16 bytes
         ok[j] = 1024 * s + 16 * lane < rowb;           // they lie in the row
-  #pragma unroll
+#pragma unroll
         for (int q = 0; q < 4; ++q) {
           sc[j][q][0] = sc[j][q][1] = 0.0f;
           wv[j][q] = ok[j] ? ld16_nt(wr[q] + 1024 * s) : z4;
@@ -198,10 +198,10 @@ gemv_dec(const WorkList* __restrict__ wl, const int32_t* __restrict__ counts, co
           }
         }
       }
-  #pragma unroll
+#pragma unroll
       for (int t = 0; t < MT; ++t) {
         if (t >= cnt) break;
-  #pragma unroll
+#pragma unroll
         for (int j = 0; j < GV_BLK; ++j) {
           if (s0 + j >= nstep) break;
           if (!ok[j]) continue;                         // past the row: contributes nothing
@@ -209,9 +209,9 @@ gemv_dec(const WorkList* __restrict__ wl, const int32_t* __restrict__ counts, co
           if (FMT == WFMT_BF16) {
             float xv[8];
             tok8<false>(ld16(xs), xv);
-  #pragma unroll
+#pragma unroll
             for (int q = 0; q < 4; ++q)
-  #pragma unroll
+#pragma unroll
               for (int c = 0; c < 4; ++c) {
                 const uint32_t w = (uint32_t)wv[j][q][c];
                 acc[q][t] = fmaf(__uint_as_float(w << 16), xv[2 * c], acc[q][t]);
@@ -221,10 +221,10 @@ gemv_dec(const WorkList* __restrict__ wl, const int32_t* __restrict__ counts, co
             float xv[2][8];
             tok8<false>(ld16(xs), xv[0]);
             tok8<false>(ld16(xs + 16), xv[1]);
-  #pragma unroll
+#pragma unroll
             for (int q = 0; q < 4; ++q) {
               float p = 0.0f;
-  #pragma unroll
+#pragma unroll
               for (int h = 0; h < 2; ++h) {
                 p = fp8_dot4((uint32_t)wv[j][q][2 * h], xv[h], p);
                 p = fp8_dot4((uint32_t)wv[j][q][2 * h + 1], xv[h] + 4, p);
@@ -233,19 +233,19 @@ gemv_dec(const WorkList* __restrict__ wl, const int32_t* __restrict__ counts, co
             }
           } else {
             float xv[4][8];
-  #pragma unroll
+#pragma unroll
             for (int h = 0; h < 4; ++h) tok8<NV>(ld16(xs + 16 * h), xv[h]);
-  #pragma unroll
+#pragma unroll
             for (int q = 0; q < 4; ++q) {
               if (NV) {
-  #pragma unroll
+#pragma unroll
                 for (int bb = 0; bb < 2; ++bb) {        // two 16-weight blocks, each with its scale
                   float p = fp4_dot8((uint32_t)wv[j][q][2 * bb], 1.0f, xv[2 * bb], 0.0f);
                   p = fp4_dot8((uint32_t)wv[j][q][2 * bb + 1], 1.0f, xv[2 * bb + 1], p);
                   acc[q][t] = fmaf(p, sc[j][q][bb], acc[q][t]);
                 }
               } else {
-  #pragma unroll
+#pragma unroll
                 for (int h = 0; h < 4; ++h) acc[q][t] = fp4_dot8((uint32_t)wv[j][q][h], sc[j][q][0], xv[h], acc[q][t]);
               }
             }
@@ -254,9 +254,9 @@ gemv_dec(const WorkList* __restrict__ wl, const int32_t* __restrict__ counts, co
       }
     }
     // sums over the 64 lanes: the 16 of each DPP row, then across the rows
-  #pragma unroll
+#pragma unroll
     for (int q = 0; q < 4; ++q)
-  #pragma unroll
+#pragma unroll
       for (int t = 0; t < MT; ++t) {
         float v = row16_sum(acc[q][t]);
         v += __shfl_xor(v, 16, 64);
@@ -270,22 +270,22 @@ gemv_dec(const WorkList* __restrict__ wl, const int32_t* __restrict__ counts, co
       tsu = tsc[1];
     }
     if (lane == 0) {
-  #pragma unroll
-    for (int t = 0; t < MT; ++t) {
-      if (t >= cnt) break;
-      if (GATED) {
-  #pragma unroll
-        for (int c = 0; c < 2; ++c) {
-          const float v = NV ? silu_mul(acc[c][t] * ts, acc[2 + c][t] * tsu) : silu_mul(acc[c][t], acc[2 + c][t]);
-          out[(size_t)(row0 + t) * N + blk * 8 + 2 * wave + c] =
-              NV ? (uint16_t)(pack_f16x2(v, 0.0f) & 0xffffu) : f32_to_bf16_bits(v);
+#pragma unroll
+      for (int t = 0; t < MT; ++t) {
+        if (t >= cnt) break;
+        if (GATED) {
+#pragma unroll
+          for (int c = 0; c < 2; ++c) {
+            const float v = NV ? silu_mul(acc[c][t] * ts, acc[2 + c][t] * tsu) : silu_mul(acc[c][t], acc[2 + c][t]);
+            out[(size_t)(row0 + t) * N + blk * 8 + 2 * wave + c] =
+                NV ? (uint16_t)(pack_f16x2(v, 0.0f) & 0xffffu) : f32_to_bf16_bits(v);
+          }
+        } else {
+#pragma unroll
+          for (int q = 0; q < 4; ++q)
+            out[(size_t)(row0 + t) * N + blk * 16 + 4 * wave + q] = f32_to_bf16_bits(NV ? acc[q][t] * ts : acc[q][t]);
         }
-      } else {
-  #pragma unroll
-        for (int q = 0; q < 4; ++q)
-          out[(size_t)(row0 + t) * N + blk * 16 + 4 * wave + q] = f32_to_bf16_bits(NV ? acc[q][t] * ts : acc[q][t]);
       }
-    }
     }
   }
 }
