@@ -23,13 +23,10 @@
 // row T-1 and are not stored; chunks past H re-read the last one and are
 // weighted by zero), so no branch splits the batch.  H % 256 == 0.
 constexpr int RT_TOK = 4;
-__global__ void __launch_bounds__(256)
-router_small_kernel(const uint16_t* __restrict__ x, const float* __restrict__ R,
-                    const float* __restrict__ bias, int T, int E, int H, float* __restrict__ z) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int e = blockIdx.x * 4 + wave;
-  if (e >= E) return;
-  const int t0 = blockIdx.y * RT_TOK;
+// One wave: the logits of expert e for tokens t0 .. t0 + RT_TOK - 1.
+DEV void router_wave(const uint16_t* __restrict__ x, const float* __restrict__ R, const float* __restrict__ bias,
+                     int T, int E, int H, float* __restrict__ z, int e, int t0) {
+  const int lane = threadIdx.x & 63;
   const float* r = R + (size_t)e * H;
   const uint16_t* xr[RT_TOK];
 #pragma unroll
@@ -69,6 +66,14 @@ router_small_kernel(const uint16_t* __restrict__ x, const float* __restrict__ R,
     const float v = wave_sum(acc[i]);
     if (lane == 0 && t0 + i < T) z[(size_t)(t0 + i) * E + e] = v + b;
   }
+}
+
+__global__ void __launch_bounds__(256)
+router_small_kernel(const uint16_t* __restrict__ x, const float* __restrict__ R,
+                    const float* __restrict__ bias, int T, int E, int H, float* __restrict__ z) {
+  const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (e >= E) return;
+  router_wave(x, R, bias, T, E, H, z, e, blockIdx.y * RT_TOK);
 }
 
 // Large batches on fp32 MFMA: 64 tokens x 64 experts per workgroup, each wave
@@ -137,97 +142,150 @@ router_mfma_kernel(const uint16_t* __restrict__ x, const float* __restrict__ R, 
 // One wave per token (E <= 256: lane l holds experts l, l+64, l+128, l+192).
 // Selection works on an order-preserving 32-bit key of each logit (-0 taken
 // as +0, so equal logits have equal keys): the k-th largest key is found by
-// bisection on its bits with wave ballots (no data crosses lanes), the k
-// winners are the keys above it plus the lowest-numbered experts at it, and
-// each winner's output position is its rank among the winners (descending
-// logit, ties to the lower expert id).  The gate weights are the softmax of
-// the winners, summed in output order.
-// One wave: the k winners of logit row zr into ids_r / w_r (and, when
-// lds_r is not null, the ids into lds_r too).
-DEV void topk_row(const float* __restrict__ zr, int E, int k, int32_t* __restrict__ ids_r, float* __restrict__ w_r,
-                  int32_t* lds_r) {
+// bisection on its bits with wave ballots (one compare per expert slot and
+// step, the counts in scalar registers), the k winners are the keys above it
+// plus the lowest-numbered experts at it, and each winner's output position
+// is its rank among the winners (descending logit, ties to the lower expert
+// id), counted by lanes 0..k-1 over the k winners staged in LDS.  The gate
+// weights are the softmax of the winners, summed in output order.
+
+// Per-wave LDS of topk_row: the winners in expert order, then in output order
+// (16-byte aligned arrays of 8, read as two 16-byte vectors).
+struct __attribute__((aligned(16))) TopkScratch {
+  uint32_t key[8];
+  int32_t e[8];
+  float v[8];
+  int32_t oe[8];
+  float ov[8];
+};
+
+// LDS written by some lanes of a wave and read by others afterwards: a wave's
+// LDS operations complete in order, so the compiler only has to keep them in
+// program order.
+DEV void wave_lds_order() { __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront"); }
+
+// One wave, NS = ceil(E / 64) expert slots per lane (a compile-time count,
+// so the bisection loop has no branches besides its own).  k <= 8.
+template <int NS>
+DEV void topk_row_ns(const float* __restrict__ zr, int E, int k, int32_t* __restrict__ ids_r,
+                     float* __restrict__ w_r, int32_t* lds_r, TopkScratch* sc) {
   const int lane = threadIdx.x & 63;
   const uint64_t below = (1ull << lane) - 1ull;
+  constexpr int ns = NS;
   float v[4];
   uint32_t key[4];
-  bool valid[4];
+  uint64_t vm[4];                               // lanes whose slot i holds an expert
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const int e = lane + 64 * i;
-    valid[i] = e < E;
-    const float x = zr[min(e, E - 1)];           // unconditional load; entries past E are not valid
-    v[i] = x == 0.0f ? 0.0f : x;
-    const uint32_t u = __float_as_uint(v[i]);
-    key[i] = (u >> 31) ? ~u : (u | 0x80000000u);
+    v[i] = 0.0f;
+    key[i] = 0u;
+    vm[i] = 0ull;
+    if (i < ns) {
+      const int e = lane + 64 * i;
+      const float x = zr[min(e, E - 1)];         // clamped load; entries past E are masked out
+      v[i] = x == 0.0f ? 0.0f : x;
+      const uint32_t u = __float_as_uint(v[i]);
+      key[i] = (u >> 31) ? ~u : (u | 0x80000000u);
+      vm[i] = __builtin_amdgcn_ballot_w64(e < E);
+    }
   }
   // the k-th largest key
   uint32_t kth = 0;
+#pragma unroll 8
   for (int b = 31; b >= 0; --b) {
     const uint32_t cand = kth | (1u << b);
     int cnt = 0;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) cnt += __popcll(__ballot(valid[i] && key[i] >= cand));
+    for (int i = 0; i < 4; ++i)
+      if (i < ns) cnt += __popcll(__builtin_amdgcn_ballot_w64(key[i] >= cand) & vm[i]);
     if (cnt >= k) kth = cand;
   }
   // winners: keys above kth, then the lowest-numbered experts at kth
-  int n_gt = 0;
-#pragma unroll
-  for (int i = 0; i < 4; ++i) n_gt += __popcll(__ballot(valid[i] && key[i] > kth));
-  const int need = k - n_gt;
-  bool sel[4];
-  int eq_before = 0;                            // experts at kth with a lower id (slots before i, then lanes)
+  // (expert ids ascend with the slot, then the lane)
+  uint64_t selm[4];
+  int need = k;
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
-    const bool eq = valid[i] && key[i] == kth;
-    const uint64_t m = __ballot(eq);
-    sel[i] = (valid[i] && key[i] > kth) || (eq && eq_before + __popcll(m & below) < need);
-    eq_before += __popcll(m);
+    selm[i] = i < ns ? __builtin_amdgcn_ballot_w64(key[i] > kth) & vm[i] : 0ull;
+    need -= __popcll(selm[i]);
   }
-  // rank of each winner among the winners
-  int rank[4] = {0, 0, 0, 0};
 #pragma unroll
-  for (int i2 = 0; i2 < 4; ++i2) {
-    uint64_t m = __ballot(sel[i2]);
-    while (m) {
-      const int L = __builtin_ctzll(m);
-      m &= m - 1;
-      const uint32_t uk = (uint32_t)__builtin_amdgcn_readlane((int)key[i2], L);   // winner (L, i2)
-      const int ue = L + 64 * i2;
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int e = lane + 64 * i;
-        rank[i] += (sel[i] && (uk > key[i] || (uk == key[i] && ue < e))) ? 1 : 0;
-      }
+  for (int i = 0; i < 4; ++i) {
+    uint64_t m = i < ns ? __builtin_amdgcn_ballot_w64(key[i] == kth) & vm[i] : 0ull;
+    for (; need > 0 && m; --need) {
+      const uint64_t lo = m & (~m + 1ull);
+      selm[i] |= lo;
+      m ^= lo;
     }
   }
+  // the winners in expert order
+  int at = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if ((selm[i] >> lane) & 1ull) {
+      const int p = at + __popcll(selm[i] & below);
+      sc->key[p] = key[i];
+      sc->e[p] = lane + 64 * i;
+      sc->v[p] = v[i];
+    }
+    at += __popcll(selm[i]);
+  }
+  wave_lds_order();
+  // lane j < k: winner j's output position (all 8 entries read at once;
+  // those past k are ignored)
+  if (lane < k) {
+    const uint32_t kj = sc->key[lane];
+    const int ej = sc->e[lane];
+    uint32_t kq[8];
+    int eq[8];
+    __builtin_memcpy(kq, sc->key, sizeof(kq));       // two 16-byte LDS reads each
+    __builtin_memcpy(eq, sc->e, sizeof(eq));
+    int r = 0;
+#pragma unroll
+    for (int q = 0; q < 8; ++q)
+      r += (int)(q < k) & ((int)(kq[q] > kj) | ((int)(kq[q] == kj) & (int)(eq[q] < ej)));
+    sc->oe[r] = ej;
+    sc->ov[r] = sc->v[lane];
+  }
+  wave_lds_order();
   // softmax over the winners in output order (the first is the largest)
-  float top = 0.0f, ssum = 0.0f;
-  for (int j = 0; j < k; ++j) {
-    float vj = 0.0f;
+  if (lane < k) {
+    float ov[8];
+    __builtin_memcpy(ov, sc->ov, sizeof(ov));
+    const float top = ov[0];
+    float ssum = 0.0f;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const uint64_t m = __ballot(sel[i] && rank[i] == j);
-      if (m) vj = __int_as_float(__builtin_amdgcn_readlane(__float_as_int(v[i]), __builtin_ctzll(m)));
+    for (int q = 0; q < 8; ++q) {
+      const float eq = expf(ov[q] - top);
+      ssum += q < k ? eq : 0.0f;
     }
-    if (j == 0) top = vj;
-    ssum += expf(vj - top);
+    const int ej = sc->oe[lane];
+    ids_r[lane] = ej;
+    w_r[lane] = expf(sc->ov[lane] - top) / ssum;
+    if (lds_r) lds_r[lane] = ej;
   }
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    if (sel[i]) {
-      ids_r[rank[i]] = lane + 64 * i;
-      w_r[rank[i]] = expf(v[i] - top) / ssum;
-      if (lds_r) lds_r[rank[i]] = lane + 64 * i;
-    }
+}
+
+// One wave: the k winners of logit row zr into ids_r / w_r (and, when
+// lds_r is not null, the ids into lds_r too).  sc: this wave's scratch.
+DEV void topk_row(const float* __restrict__ zr, int E, int k, int32_t* __restrict__ ids_r, float* __restrict__ w_r,
+                  int32_t* lds_r, TopkScratch* sc) {
+  switch ((E + 63) >> 6) {
+    case 1: topk_row_ns<1>(zr, E, k, ids_r, w_r, lds_r, sc); break;
+    case 2: topk_row_ns<2>(zr, E, k, ids_r, w_r, lds_r, sc); break;
+    case 3: topk_row_ns<3>(zr, E, k, ids_r, w_r, lds_r, sc); break;
+    default: topk_row_ns<4>(zr, E, k, ids_r, w_r, lds_r, sc); break;
   }
 }
 
 __global__ void __launch_bounds__(256)
 topk_kernel(const float* __restrict__ z, int T, int E, int k, int32_t* __restrict__ ids,
             float* __restrict__ w) {
-  const int t = blockIdx.x * 4 + (threadIdx.x >> 6);
+  __shared__ TopkScratch sc[4];
+  const int wave = threadIdx.x >> 6;
+  const int t = blockIdx.x * 4 + wave;
   if (t >= T) return;
-  topk_row(z + (size_t)t * E, E, k, ids + (size_t)t * k, w + (size_t)t * k, nullptr);
+  topk_row(z + (size_t)t * E, E, k, ids + (size_t)t * k, w + (size_t)t * k, nullptr, sc + wave);
 }
 
 // ---------------------------------------------------------------------------
@@ -235,59 +293,100 @@ topk_kernel(const float* __restrict__ z, int T, int E, int k, int32_t* __restric
 // ---------------------------------------------------------------------------
 constexpr int GROUP_TOK = 256;   // tokens per grouping block
 
-// Exclusive scan of one value per thread over the first 256 threads of the
-// block (threads past them, in larger blocks, pass 0 and get no result).
-__device__ int block_exclusive_scan256(int v, int* tmp /* >= 4 ints of LDS */, int* total) {
+// Inclusive sum over the wave's lanes in lane order (DPP: shifts by 1, 2, 4
+// and 8 within each row of 16 lanes, then rows 1 and 3 add lane 15's total
+// of the row before, and rows 2 and 3 lane 31's total of rows 0-1).
+DEV int wave_incl_sum(int v) {
+  v += __builtin_amdgcn_update_dpp(0, v, 0x111, 0xf, 0xf, false);   // row_shr:1
+  v += __builtin_amdgcn_update_dpp(0, v, 0x112, 0xf, 0xf, false);   // row_shr:2
+  v += __builtin_amdgcn_update_dpp(0, v, 0x114, 0xf, 0xf, false);   // row_shr:4
+  v += __builtin_amdgcn_update_dpp(0, v, 0x118, 0xf, 0xf, false);   // row_shr:8
+  v += __builtin_amdgcn_update_dpp(0, v, 0x142, 0xa, 0xf, false);   // row_bcast:15
+  v += __builtin_amdgcn_update_dpp(0, v, 0x143, 0xc, 0xf, false);   // row_bcast:31
+  return v;
+}
+
+struct Scan3 {
+  int a, b, c;
+};
+
+// Exclusive scans of three values per thread over the first 256 threads of
+// the block (threads past them, in larger blocks, pass 0 and get no
+// result); *tot: the three totals.  Every thread of the block calls it.
+__device__ Scan3 block_exclusive_scan256_x3(int a, int b, int c, int* tmp /* >= 12 ints of LDS */, Scan3* tot) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  int incl = v;
-#pragma unroll
-  for (int off = 1; off < 64; off <<= 1) {
-    const int o = __shfl_up(incl, off, 64);
-    if (lane >= off) incl += o;
+  const int ia = wave_incl_sum(a), ib = wave_incl_sum(b), ic = wave_incl_sum(c);
+  if (lane == 63 && wave < 4) {
+    tmp[wave] = ia;
+    tmp[4 + wave] = ib;
+    tmp[8 + wave] = ic;
   }
-  if (lane == 63 && wave < 4) tmp[wave] = incl;
   __syncthreads();
-  int base = 0;
-  for (int i = 0; i < wave && i < 4; ++i) base += tmp[i];
-  *total = tmp[0] + tmp[1] + tmp[2] + tmp[3];
+  Scan3 base{0, 0, 0};
+  for (int i = 0; i < wave && i < 4; ++i) {
+    base.a += tmp[i];
+    base.b += tmp[4 + i];
+    base.c += tmp[8 + i];
+  }
+  tot->a = tmp[0] + tmp[1] + tmp[2] + tmp[3];
+  tot->b = tmp[4] + tmp[5] + tmp[6] + tmp[7];
+  tot->c = tmp[8] + tmp[9] + tmp[10] + tmp[11];
   __syncthreads();
-  return base + incl - v;
+  return Scan3{base.a + ia - a, base.b + ib - b, base.c + ic - c};
+}
+
+// What the grouping needs of expert e = threadIdx.x besides its count: the
+// miss-mask word holding its bit (0 without a mask) and its slot (0 without
+// a table: grouping only).  Loaded at a kernel's start, so the loads overlap
+// the work before the count is known.
+struct ExpertMeta {
+  uint32_t mword;
+  int slot;
+};
+
+DEV ExpertMeta expert_meta(int E, const uint32_t* miss_mask, const int32_t* slot_row) {
+  const int e = threadIdx.x;
+  ExpertMeta m{0u, 0};
+  if (e < E) {
+    if (miss_mask) m.mword = miss_mask[e >> 5];
+    if (slot_row) m.slot = slot_row[e];
+  }
+  return m;
 }
 
 // From per-expert counts (thread e holds counts[e]), write offsets, the list
 // of experts that run on the GPU (routed, not in the host miss mask) with
 // their slots and m-block prefix.  A routed, unmasked expert without a slot
-// raises the device error flag and is skipped.
-__device__ void finish_grouping(int cnt, int E, const uint32_t* miss_mask, const int32_t* slot_row,
-                                int32_t* counts, int32_t* offsets, WorkList* wl, int mb, int* err,
-                                int* tmp, const TailSplit& ts) {
+// raises the device error flag and is skipped.  Returns thread e's offset
+// (the first grouped row of expert e).
+__device__ int finish_grouping(int cnt, int E, ExpertMeta em, int32_t* counts, int32_t* offsets, WorkList* wl,
+                               int mb, int* err, int* tmp /* >= 12 ints of LDS */, const TailSplit& ts) {
   const int e = threadIdx.x;
   const int c = e < E ? cnt : 0;
-  int total;
-  const int off = block_exclusive_scan256(c, tmp, &total);
-  if (e < E) { counts[e] = c; offsets[e] = off; }
-  if (e == 0) offsets[E] = total;
   bool act = false;
   int slot = -1;
   if (e < E && c > 0) {
-    const bool masked = miss_mask && ((miss_mask[e >> 5] >> (e & 31)) & 1u);
+    const bool masked = (em.mword >> (e & 31)) & 1u;
     if (!masked) {
-      slot = slot_row ? slot_row[e] : 0;     // no table: grouping only
+      slot = em.slot;
       if (slot < 0) atomicOr(err, 1);
       else act = true;
     }
   }
-  int nact;
-  const int a = block_exclusive_scan256(act ? 1 : 0, tmp, &nact);
   int nb = act ? (c + mb - 1) / mb : 0;
+  Scan3 tot;
+  // offsets, active-expert positions and m-block prefixes in one pass
+  const Scan3 x = block_exclusive_scan256_x3(c, act ? 1 : 0, nb, tmp, &tot);
+  const int off = x.a, a = x.b, nact = tot.b;
+  int pb = x.c, nmblk = tot.c;
   // overflow rows of a last tile of at most tau rows go to the tail list
   // when that removes a round of the tiled grid and the tail items are few
   int tl = 0;
   if (ts.wl) {
     const bool cand = nb >= 2 && c - (nb - 1) * mb <= ts.tau;
-    int n0, ncand;
-    (void)block_exclusive_scan256(nb, tmp, &n0);
-    (void)block_exclusive_scan256(cand ? 1 : 0, tmp, &ncand);
+    Scan3 t2;
+    (void)block_exclusive_scan256_x3(cand ? 1 : 0, 0, 0, tmp, &t2);
+    const int n0 = tot.c, ncand = t2.a;
     const long it0 = (long)n0 * ts.ntiles, it1 = (long)(n0 - ncand) * ts.ntiles;
     const bool split = ncand > 0 && (it1 + ts.n_cu - 1) / ts.n_cu < (it0 + ts.n_cu - 1) / ts.n_cu &&
                        (long)ncand * ts.ntiles * 4 <= ts.n_cu;
@@ -295,25 +394,25 @@ __device__ void finish_grouping(int cnt, int E, const uint32_t* miss_mask, const
       --nb;
       tl = c - nb * mb;
     }
-  }
-  int nmblk;
-  const int pb = block_exclusive_scan256(nb, tmp, &nmblk);
-  if (act) { wl->act_e[a] = e; wl->act_slot[a] = slot; wl->mblk_prefix[a] = pb; }
-  if (e == 0) {
-    wl->n_act = nact; wl->n_mblk = nmblk; wl->mb = mb; wl->mblk_prefix[nact] = nmblk;
-  }
-  if (ts.wl) {
-    if (e < E) { ts.mcounts[e] = c - tl; ts.tcounts[e] = tl; ts.toffsets[e] = off + c - tl; }
-    int ntact;
-    const int ta = block_exclusive_scan256(tl > 0 ? 1 : 0, tmp, &ntact);
     const int tnb = tl > 0 ? (tl + ts.mb - 1) / ts.mb : 0;
-    int tnm;
-    const int tpb = block_exclusive_scan256(tnb, tmp, &tnm);
+    Scan3 t3;
+    const Scan3 y = block_exclusive_scan256_x3(nb, tl > 0 ? 1 : 0, tnb, tmp, &t3);
+    pb = y.a;
+    nmblk = t3.a;
+    const int ta = y.b, tpb = y.c, ntact = t3.b, tnm = t3.c;
+    if (e < E) { ts.mcounts[e] = c - tl; ts.tcounts[e] = tl; ts.toffsets[e] = off + c - tl; }
     if (tl > 0) { ts.wl->act_e[ta] = e; ts.wl->act_slot[ta] = slot; ts.wl->mblk_prefix[ta] = tpb; }
     if (e == 0) {
       ts.wl->n_act = ntact; ts.wl->n_mblk = tnm; ts.wl->mb = ts.mb; ts.wl->mblk_prefix[ntact] = tnm;
     }
   }
+  if (e < E) { counts[e] = c; offsets[e] = off; }
+  if (e == 0) offsets[E] = tot.a;
+  if (act) { wl->act_e[a] = e; wl->act_slot[a] = slot; wl->mblk_prefix[a] = pb; }
+  if (e == 0) {
+    wl->n_act = nact; wl->n_mblk = nmblk; wl->mb = mb; wl->mblk_prefix[nact] = nmblk;
+  }
+  return off;
 }
 
 // Stable scatter of one block of tokens given per-expert bases for the block.
@@ -348,6 +447,41 @@ __device__ void mark_block(const int32_t* __restrict__ ids, int t0, int T, int k
   __syncthreads();
 }
 
+// One block of T <= 256 tokens, one (token, choice) pair per thread and
+// pass: presence bits (token t -> bit t & 31 of word t >> 5 of each of its
+// experts' rows; bits is LDS [E][8] of which the first ceil(T / 32) words of
+// a row are used) and the stable scatter that reads them.
+DEV void mark_pairs(const int32_t* ids, int T, int k, int E, uint32_t* bits) {
+  const int nw = (T + 31) >> 5;
+  for (int i = threadIdx.x; i < E * nw; i += blockDim.x) bits[(i / nw) * 8 + i % nw] = 0u;
+  __syncthreads();
+  for (int p = threadIdx.x; p < T * k; p += blockDim.x) {
+    const int t = p / k;
+    atomicOr(&bits[ids[p] * 8 + (t >> 5)], 1u << (t & 31));
+  }
+  __syncthreads();
+}
+
+DEV int count_pairs(const uint32_t* bits, int T, int E) {
+  const int e = threadIdx.x, nw = (T + 31) >> 5;
+  int c = 0;
+  if (e < E)
+    for (int q = 0; q < nw; ++q) c += __popc(bits[e * 8 + q]);
+  return c;
+}
+
+DEV void scatter_pairs(const int32_t* ids, int T, int k, const int* base, const uint32_t* bits,
+                       int32_t* __restrict__ pos, int32_t* __restrict__ perm_tok) {
+  for (int p = threadIdx.x; p < T * k; p += blockDim.x) {
+    const int t = p / k, e = ids[p], wi = t >> 5;
+    int r = __popc(bits[e * 8 + wi] & ((1u << (t & 31)) - 1u));
+    for (int q = 0; q < wi; ++q) r += __popc(bits[e * 8 + q]);
+    const int d = base[e] + r;
+    pos[p] = d;
+    perm_tok[d] = t;
+  }
+}
+
 // T <= 256: histogram, scan, work list and scatter in one workgroup.
 __global__ void __launch_bounds__(256)
 group_single_kernel(const int32_t* __restrict__ ids, int T, int k, int E, const uint32_t* miss_mask,
@@ -356,41 +490,49 @@ group_single_kernel(const int32_t* __restrict__ ids, int T, int k, int E, const 
                     TailSplit ts) {
   __shared__ uint32_t bits[256 * 8];
   __shared__ int base[256];
-  __shared__ int tmp[4];
-  mark_block(ids, 0, T, k, E, bits);
-  int cnt = 0;
-  if ((int)threadIdx.x < E)
-    for (int q = 0; q < 8; ++q) cnt += __popc(bits[threadIdx.x * 8 + q]);
-  finish_grouping(cnt, E, miss_mask, slot_row, counts, offsets, wl, mb, err, tmp, ts);
-  if ((int)threadIdx.x < E) base[threadIdx.x] = offsets[threadIdx.x];
+  __shared__ int tmp[12];
+  const ExpertMeta em = expert_meta(E, miss_mask, slot_row);
+  mark_pairs(ids, T, k, E, bits);
+  const int off = finish_grouping(count_pairs(bits, T, E), E, em, counts, offsets, wl, mb, err, tmp, ts);
+  if ((int)threadIdx.x < E) base[threadIdx.x] = off;
   __syncthreads();
-  scatter_block(ids, 0, T, k, E, base, bits, pos, perm_tok);
+  scatter_pairs(ids, T, k, base, bits, pos, perm_tok);
 }
 
 // T <= 16: top-k of every token (wave t takes token t) and the grouping of
 // group_single_kernel in one launch; the assignments pass through LDS.
 constexpr int TG_MAX_T = 16;
+
+// The grouping of T <= 256 tokens whose k choices each sit in LDS (s_ids,
+// written before a barrier), by the first 256 threads of the workgroup.
+DEV void group_from_lds(const int32_t* s_ids, int T, int k, int E, ExpertMeta em, int mb, int32_t* counts,
+                        int32_t* offsets, int32_t* __restrict__ pos, int32_t* __restrict__ perm_tok, WorkList* wl,
+                        int* err, uint32_t* bits, int* base, int* tmp) {
+  const TailSplit ts{nullptr, nullptr, nullptr, nullptr, 1, 0};
+  mark_pairs(s_ids, T, k, E, bits);
+  const int off = finish_grouping(count_pairs(bits, T, E), E, em, counts, offsets, wl, mb, err, tmp, ts);
+  if ((int)threadIdx.x < E) base[threadIdx.x] = off;
+  __syncthreads();
+  scatter_pairs(s_ids, T, k, base, bits, pos, perm_tok);
+}
+
 __global__ void __launch_bounds__(1024)
 topk_group_kernel(const float* __restrict__ z, int T, int E, int k, int32_t* __restrict__ ids,
                   float* __restrict__ w, const uint32_t* miss_mask, const int32_t* slot_row, int mb,
                   int32_t* counts, int32_t* offsets, int32_t* __restrict__ pos, int32_t* __restrict__ perm_tok,
-                  WorkList* wl, int* err, TailSplit ts) {
+                  WorkList* wl, int* err) {
   __shared__ uint32_t bits[256 * 8];
   __shared__ int base[256];
-  __shared__ int tmp[4];
+  __shared__ int tmp[12];
   __shared__ int32_t s_ids[TG_MAX_T * 8];
+  __shared__ TopkScratch sc[TG_MAX_T];
+  const ExpertMeta em = expert_meta(E, miss_mask, slot_row);
   const int wave = threadIdx.x >> 6;
   if (wave < T)
-    topk_row(z + (size_t)wave * E, E, k, ids + (size_t)wave * k, w + (size_t)wave * k, s_ids + wave * k);
+    topk_row(z + (size_t)wave * E, E, k, ids + (size_t)wave * k, w + (size_t)wave * k, s_ids + wave * k,
+             sc + wave);
   __syncthreads();
-  mark_block(s_ids, 0, T, k, E, bits);
-  int cnt = 0;
-  if ((int)threadIdx.x < E)
-    for (int q = 0; q < 8; ++q) cnt += __popc(bits[threadIdx.x * 8 + q]);
-  finish_grouping(cnt, E, miss_mask, slot_row, counts, offsets, wl, mb, err, tmp, ts);
-  if ((int)threadIdx.x < E) base[threadIdx.x] = offsets[threadIdx.x];
-  __syncthreads();
-  scatter_block(s_ids, 0, T, k, E, base, bits, pos, perm_tok);
+  group_from_lds(s_ids, T, k, E, em, mb, counts, offsets, pos, perm_tok, wl, err, bits, base, tmp);
 }
 
 // General path, pass 1: per-block histograms hist[b][e].
@@ -412,14 +554,15 @@ __global__ void __launch_bounds__(256)
 group_scan_kernel(int nblk, int E, const uint32_t* miss_mask, const int32_t* slot_row, int mb,
                   int32_t* __restrict__ hist, int32_t* counts, int32_t* offsets, WorkList* wl, int* err,
                   TailSplit ts) {
-  __shared__ int tmp[4];
+  __shared__ int tmp[12];
   const int e = threadIdx.x;
+  const ExpertMeta em = expert_meta(E, miss_mask, slot_row);
   int cnt = 0;
   if (e < E)
     for (int b = 0; b < nblk; ++b) cnt += hist[(size_t)b * E + e];
-  finish_grouping(cnt, E, miss_mask, slot_row, counts, offsets, wl, mb, err, tmp, ts);
+  const int off = finish_grouping(cnt, E, em, counts, offsets, wl, mb, err, tmp, ts);
   if (e < E) {
-    int run = offsets[e];
+    int run = off;
     for (int b = 0; b < nblk; ++b) {
       const int h = hist[(size_t)b * E + e];
       hist[(size_t)b * E + e] = run;
@@ -464,12 +607,10 @@ extern "C" hipError_t moe_launch_topk_group(const float* z, int T, int E, int k,
                                             int32_t* counts, int32_t* offsets, int32_t* pos, int32_t* perm_tok,
                                             WorkList* wl, int* err, hipStream_t s) {
   if (T < 1 || T > TG_MAX_T || E > 256 || k > 8) return hipErrorInvalidValue;
-  const TailSplit ts{nullptr, nullptr, nullptr, nullptr, 1, 0};
   // one wave per token, at least the four waves the grouping needs (fewer
   // waves make its barriers cheaper)
   topk_group_kernel<<<1, 64 * (T < 4 ? 4 : T), 0, s>>>(z, T, E, k, ids, w, miss_mask, slot_row, mb, counts, offsets,
-                                                       pos, perm_tok,
-                                       wl, err, ts);
+                                                       pos, perm_tok, wl, err);
   return hipGetLastError();
 }
 

@@ -10,7 +10,7 @@ from gpu_util import Setup, compare, shape
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("T", [1, 64, 300])
+@pytest.mark.parametrize("T", [1, 5, 64, 300])
 def test_graph_replay_matches_eager(T):
     print(f"graph replay T={T}", flush=True)
     cfg = shape(1, L=2, E=32, k=4, H=1024, I=384)

@@ -33,7 +33,9 @@ def test_noalloc_matches_forward(fmt, base, kw):
     s = Setup(cfg, seed=11, max_tokens=64)
     try:
         s.admit_all(0)
-        for T in (64, 23):                  # two calls in a row, the second smaller
+        # calls in a row, each smaller (the last ones through the
+        # matrix-vector kernels)
+        for T in (64, 23, 8, 3, 1):
             _, x = s.hidden(T, tag=T)
             ref = torch.empty(T, cfg.H, dtype=torch.bfloat16, device="cuda")
             got = torch.full((T, cfg.H), 7.0, dtype=torch.bfloat16, device="cuda")
@@ -48,22 +50,23 @@ def test_noalloc_matches_forward(fmt, base, kw):
         s.close()
 
 
-def test_noalloc_error_flag():
+@pytest.mark.parametrize("T", [16, 4])
+def test_noalloc_error_flag(T):
     """A routed expert without a slot (the test's own shape, its own slot
     pool): left out, bit 0 of the caller's flag set, the output zero."""
-    print("noalloc error flag", flush=True)
+    print(f"noalloc error flag T={T}", flush=True)
     cfg = shape(1)
     s = Setup(cfg, seed=12, max_tokens=64)
     try:
         s.admit_all(0)
-        _, x = s.hidden(16)
-        out = torch.full((16, cfg.H), 3.0, dtype=torch.bfloat16, device="cuda")
+        _, x = s.hidden(T)
+        out = torch.full((T, cfg.H), 3.0, dtype=torch.bfloat16, device="cuda")
         row = s.slot_row(0).clone()
         row[:] = -1
         err = torch.zeros(1, dtype=torch.int32, device="cuda")
         cfgc = B.make_config(cfg.L, cfg.E, cfg.k, cfg.H, cfg.I, cfg.fmt, 0, 64, 0)
         rc = B.moe_layer_forward_noalloc(ctypes.byref(cfgc), s.rt.slots.data_ptr(), row.data_ptr(), x.data_ptr(),
-                                         s.R_d[0].data_ptr(), None, 16, None, None, out.data_ptr(), err.data_ptr(),
+                                         s.R_d[0].data_ptr(), None, T, None, None, out.data_ptr(), err.data_ptr(),
                                          torch.cuda.current_stream().cuda_stream)
         assert rc == 0
         torch.cuda.synchronize()
