@@ -27,7 +27,7 @@ hipError_t moe_launch_topk(const float* z, int T, int E, int k, int32_t* ids, fl
 hipError_t moe_launch_topk_group(const float* z, int T, int E, int k, int32_t* ids, float* w,
                                  const uint32_t* miss_mask, const int32_t* slot_row, int mb, int32_t* counts,
                                  int32_t* offsets, int32_t* pos, int32_t* perm_tok, WorkList* wl, int* err,
-                                 hipStream_t s);
+                                 int32_t* pslot, hipStream_t s);
 hipError_t moe_launch_group(const int32_t* ids, int T, int k, int E, const uint32_t* miss_mask,
                             const int32_t* slot_row, int mb, int32_t* counts, int32_t* offsets, int32_t* pos,
                             int32_t* perm_tok, int32_t* hist, WorkList* wl, int* err, const TailSplit* tail,
@@ -41,11 +41,10 @@ size_t moe_dec_part_bytes();
 int moe_dec_max_ns(int fmt);
 int moe_pf_tile_tokens();
 int moe_gemv_max_tokens();
-hipError_t moe_launch_gemv_down_combine(int fmt, const int32_t* ids, const float* w, const int32_t* pos,
-                                        const uint32_t* miss_mask, const int32_t* slot_row, const uint8_t* pool,
-                                        size_t S, size_t woff, size_t soff, const void* A, int T, int k, int K, int N,
-                                        const float* hp, const int32_t* hp_count, void* out, float* out_f32,
-                                        hipStream_t s);
+hipError_t moe_launch_gemv_down_combine(int fmt, const int32_t* pslot, const float* w, const int32_t* pos,
+                                        const uint8_t* pool, size_t S, size_t woff, size_t soff, const void* A, int T,
+                                        int k, int K, int N, const float* hp, const int32_t* hp_count, void* out,
+                                        float* out_f32, hipStream_t s);
 hipError_t moe_launch_gemv(int fmt, int max_rows, int gated, int grid, const WorkList* wl, const int32_t* counts,
                            const int32_t* offsets, const uint8_t* pool, size_t S, size_t woff0, size_t woff1,
                            size_t soff0, size_t soff1, const void* X, const int32_t* row_tok, int K, int N, void* out,
@@ -118,7 +117,7 @@ BlobLayout blob_layout(const moe_config& c) {
 
 // Workspace carving (all offsets 256-byte aligned).
 struct WsLayout {
-  size_t slot_table, owner, last_use, ctl, err, logits, ids, w, pos, perm_tok, counts, offsets, hist, wl, wl_tail,
+  size_t slot_table, owner, last_use, ctl, err, logits, ids, w, pos, pslot, perm_tok, counts, offsets, hist, wl, wl_tail,
       tail_rows, mask, plan, A,
       Aq, As, Z, Xq, Xs, hp, part, total;
 };
@@ -147,6 +146,7 @@ WsLayout ws_layout(const moe_config& c, bool fwd_only = false, size_t part_bytes
   L.ids = take(R * 4);
   L.w = take(R * 4);
   L.pos = take(R * 4);
+  L.pslot = take(R * 4);
   L.perm_tok = take((R + moe_pf_tile_tokens()) * 4);   // + one tile of slack: the prefill GEMM reads whole blocks
   L.counts = take((size_t)c.E * 4);
   L.offsets = take((size_t)(c.E + 1) * 4);
@@ -203,6 +203,7 @@ struct moe_ctx {
   int32_t* ids;
   float* w;
   int32_t* pos;
+  int32_t* pslot;           // per routed pair: its expert's GPU slot, -1 if not on the GPU (fused grouping)
   int32_t* perm_tok;
   int32_t* counts;
   int32_t* offsets;
@@ -273,6 +274,7 @@ void carve(moe_ctx* c, uint8_t* w, bool fwd_only) {
   c->ids = (int32_t*)(w + L.ids);
   c->w = (float*)(w + L.w);
   c->pos = (int32_t*)(w + L.pos);
+  c->pslot = (int32_t*)(w + L.pslot);
   c->perm_tok = (int32_t*)(w + L.perm_tok);
   c->counts = (int32_t*)(w + L.counts);
   c->offsets = (int32_t*)(w + L.offsets);
@@ -401,7 +403,7 @@ int forward_experts(moe_ctx* c, const void* hidden, int T, const int32_t* slot_r
     if (tiled || T > FUSED_TOPK_T) return fail(c, MOE_E_INVAL, "fused top-k and grouping needs a small batch");
     STAGE(c, MOE_STAGE_GROUP, s,
           moe_launch_topk_group(c->logits, T, g.E, g.k, c->ids, c->w, mask, slot_row, 16 * ns, c->counts,
-                                c->offsets, c->pos, c->perm_tok, c->wl, c->err, s));
+                                c->offsets, c->pos, c->perm_tok, c->wl, c->err, c->pslot, s));
   } else {
     STAGE(c, MOE_STAGE_GROUP, s,
           moe_launch_group(c->ids, T, g.k, g.E, mask, slot_row, tiled ? tile_mb : 16 * ns, c->counts,
@@ -473,7 +475,9 @@ int forward_experts(moe_ctx* c, const void* hidden, int T, const int32_t* slot_r
       STAGE(c, MOE_STAGE_GEMM1, s,
             moe_launch_gemv(dfmt, T, 1, (int)(ne * (g.I / 8)), c->wl, c->counts, c->offsets, c->slot_pool, b.S, b.w[0],
                             b.w[1], b.s[0], b.s[1], x16, c->perm_tok, g.H, g.I, c->A, s));
-      if (fuse_down && T <= 8 && g.k <= 8) {      // the combine runs the down GEMM (one launch fewer)
+      // the combine runs the down GEMM (one launch fewer); it reads the
+      // per-pair slots the fused top-k/grouping writes
+      if (fuse_down && fused_topk && T <= 8 && g.k <= 8) {
         c->down_fused = dfmt;
         return MOE_OK;
       }
@@ -537,7 +541,7 @@ int combine(moe_ctx* c, const uint32_t* mask, const int32_t* row, const float* h
     c->down_fused = -1;
     const BlobLayout& b = c->bl;
     STAGE(c, MOE_STAGE_COMBINE, s,
-          moe_launch_gemv_down_combine(f, c->ids, c->w, c->pos, mask, row, c->slot_pool, b.S, b.w[2], b.s[2], c->A, T,
+          moe_launch_gemv_down_combine(f, c->pslot, c->w, c->pos, c->slot_pool, b.S, b.w[2], b.s[2], c->A, T,
                                        c->cfg.k, c->cfg.I, c->cfg.H, hp, hp_count, out, out_f32, s));
     return MOE_OK;
   }

@@ -134,10 +134,13 @@ gemv_dec(const WorkList* __restrict__ wl, const int32_t* __restrict__ counts, co
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int per_e = GATED ? N / 8 : N / 16;          // items per expert
   const int it = blockIdx.x;
-  if (it >= wl->n_act * per_e) return;
   const int a = it / per_e, blk = it - a * per_e;
-  const int e = wl->act_e[a];
-  const uint8_t* blob = pool + (size_t)wl->act_slot[a] * S;
+  // the item's work-list entries are read beside the count (entries past
+  // n_act are not used), so the weight addresses wait for one load
+  const int ac = min(a, 255);
+  const int nact = wl->n_act, e = wl->act_e[ac], slot = wl->act_slot[ac];
+  if (a >= nact) return;
+  const uint8_t* blob = pool + (size_t)slot * S;
   const int rowb = K * WB2 / 2;                      // weight bytes per row
   const int rbase = offsets[e], ctot = counts[e];
   // the expert's rows in chunks of MT (the batch bounds them by MT; a chunk
@@ -296,15 +299,16 @@ gemv_dec(const WorkList* __restrict__ wl, const int32_t* __restrict__ counts, co
 // Z for (t, j) exactly as gemv_dec does for that row (same lane layout,
 // steps and sums, the NVFP4 down scale on the sum, rounded to bf16); wave
 // 0 then adds w_tj * z_j over j = 0..7 in order, choices that ran on the
-// host (miss_mask) or past k adding zero, then the host partial, as the
-// combine kernel does:
+// host or past k adding zero, then the host partial, as the combine kernel
+// does:
 //   out[t, h] = bf16( sum_j w_tj z_tj[h] + host_partial[t, h] ).
 // out_f32 (optional): the unrounded sum instead.  A: the GEMM 1 output in
-// grouped order (row pos[t, j]); K = I, N = H, N % 4 == 0.
+// grouped order (row pos[t, j]); pslot[t, j]: the slot of choice j's expert,
+// -1 where it did not run on the GPU (the fused top-k/grouping writes it);
+// K = I, N = H, N % 4 == 0.
 template <int FMT>
 __global__ void __launch_bounds__(512)
-gemv_down_combine(const int32_t* __restrict__ ids, const float* __restrict__ w, const int32_t* __restrict__ pos,
-                  const uint32_t* __restrict__ miss_mask, const int32_t* __restrict__ slot_row,
+gemv_down_combine(const int32_t* __restrict__ pslot, const float* __restrict__ w, const int32_t* __restrict__ pos,
                   const uint8_t* __restrict__ pool, size_t S, size_t woff, size_t soff,
                   const uint16_t* __restrict__ A, int k, int K, int N, const float* hp,
                   const int32_t* __restrict__ hp_count, uint16_t* __restrict__ out, float* out_f32) {
@@ -317,10 +321,8 @@ gemv_down_combine(const int32_t* __restrict__ ids, const float* __restrict__ w, 
   const int j = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int h0 = blockIdx.x * 4, t = blockIdx.y;
   const size_t a = (size_t)t * k + j;
-  const int e = ids[a];
-  const bool host = miss_mask && ((miss_mask[e >> 5] >> (e & 31)) & 1u);   // computed by the host
-  const int slot = slot_row[e];
-  const bool use = !host && slot >= 0;                                    // not resident: error flagged elsewhere
+  const int slot = pslot[a];        // -1: computed by the host, or not resident (error flagged by the grouping)
+  const bool use = slot >= 0;
   float acc[4] = {0.f, 0.f, 0.f, 0.f};
   if (use) {
     const uint8_t* blob = pool + (size_t)slot * S;
@@ -502,15 +504,14 @@ extern "C" hipError_t moe_launch_gemv(int fmt, int max_rows, int gated, int grid
 
 // The down GEMM of a matrix-vector forward fused with the combine (see
 // gemv_down_combine): fmt as moe_launch_gemv; k <= 8; N % 4 == 0.
-extern "C" hipError_t moe_launch_gemv_down_combine(int fmt, const int32_t* ids, const float* w, const int32_t* pos,
-                                                   const uint32_t* miss_mask, const int32_t* slot_row,
+extern "C" hipError_t moe_launch_gemv_down_combine(int fmt, const int32_t* pslot, const float* w, const int32_t* pos,
                                                    const uint8_t* pool, size_t S, size_t woff, size_t soff,
                                                    const void* A, int T, int k, int K, int N, const float* hp,
                                                    const int32_t* hp_count, void* out, float* out_f32, hipStream_t s) {
   const int kq = fmt == WFMT_BF16 ? 8 : (fmt == WFMT_FP8_A16 ? 16 : 32);
   if (T < 1 || k < 1 || k > 8 || N % 4 || K % kq) return hipErrorInvalidValue;
   const dim3 grid(N / 4, T);
-#define MOE_DC_ARGS ids, w, pos, miss_mask, slot_row, pool, S, woff, soff, (const uint16_t*)A, k, K, N, hp, hp_count, \
+#define MOE_DC_ARGS pslot, w, pos, pool, S, woff, soff, (const uint16_t*)A, k, K, N, hp, hp_count, \
                     (uint16_t*)out, out_f32
   switch (fmt) {
     case WFMT_BF16: gemv_down_combine<WFMT_BF16><<<grid, 64 * k, 0, s>>>(MOE_DC_ARGS); break;

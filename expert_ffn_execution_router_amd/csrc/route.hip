@@ -358,9 +358,11 @@ DEV ExpertMeta expert_meta(int E, const uint32_t* miss_mask, const int32_t* slot
 // of experts that run on the GPU (routed, not in the host miss mask) with
 // their slots and m-block prefix.  A routed, unmasked expert without a slot
 // raises the device error flag and is skipped.  Returns thread e's offset
-// (the first grouped row of expert e).
+// (the first grouped row of expert e); *gslot (may be null): its slot if it
+// runs on the GPU, else -1.
 __device__ int finish_grouping(int cnt, int E, ExpertMeta em, int32_t* counts, int32_t* offsets, WorkList* wl,
-                               int mb, int* err, int* tmp /* >= 12 ints of LDS */, const TailSplit& ts) {
+                               int mb, int* err, int* tmp /* >= 12 ints of LDS */, const TailSplit& ts,
+                               int* gslot = nullptr) {
   const int e = threadIdx.x;
   const int c = e < E ? cnt : 0;
   bool act = false;
@@ -412,6 +414,7 @@ __device__ int finish_grouping(int cnt, int E, ExpertMeta em, int32_t* counts, i
   if (e == 0) {
     wl->n_act = nact; wl->n_mblk = nmblk; wl->mb = mb; wl->mblk_prefix[nact] = nmblk;
   }
+  if (gslot) *gslot = act ? slot : -1;
   return off;
 }
 
@@ -470,8 +473,11 @@ DEV int count_pairs(const uint32_t* bits, int T, int E) {
   return c;
 }
 
+// pslot (may be null): per pair, the slot its expert runs from on the GPU,
+// -1 where it does not (host-run or without a slot); gslot: those per expert.
 DEV void scatter_pairs(const int32_t* ids, int T, int k, const int* base, const uint32_t* bits,
-                       int32_t* __restrict__ pos, int32_t* __restrict__ perm_tok) {
+                       int32_t* __restrict__ pos, int32_t* __restrict__ perm_tok, const int* gslot = nullptr,
+                       int32_t* __restrict__ pslot = nullptr) {
   for (int p = threadIdx.x; p < T * k; p += blockDim.x) {
     const int t = p / k, e = ids[p], wi = t >> 5;
     int r = __popc(bits[e * 8 + wi] & ((1u << (t & 31)) - 1u));
@@ -479,6 +485,7 @@ DEV void scatter_pairs(const int32_t* ids, int T, int k, const int* base, const 
     const int d = base[e] + r;
     pos[p] = d;
     perm_tok[d] = t;
+    if (pslot) pslot[p] = gslot[e];
   }
 }
 
@@ -507,22 +514,27 @@ constexpr int TG_MAX_T = 16;
 // written before a barrier), by the first 256 threads of the workgroup.
 DEV void group_from_lds(const int32_t* s_ids, int T, int k, int E, ExpertMeta em, int mb, int32_t* counts,
                         int32_t* offsets, int32_t* __restrict__ pos, int32_t* __restrict__ perm_tok, WorkList* wl,
-                        int* err, uint32_t* bits, int* base, int* tmp) {
+                        int* err, int32_t* pslot, uint32_t* bits, int* base, int* gslot, int* tmp) {
   const TailSplit ts{nullptr, nullptr, nullptr, nullptr, 1, 0};
   mark_pairs(s_ids, T, k, E, bits);
-  const int off = finish_grouping(count_pairs(bits, T, E), E, em, counts, offsets, wl, mb, err, tmp, ts);
-  if ((int)threadIdx.x < E) base[threadIdx.x] = off;
+  int gs;
+  const int off = finish_grouping(count_pairs(bits, T, E), E, em, counts, offsets, wl, mb, err, tmp, ts, &gs);
+  if ((int)threadIdx.x < E) {
+    base[threadIdx.x] = off;
+    gslot[threadIdx.x] = gs;
+  }
   __syncthreads();
-  scatter_pairs(s_ids, T, k, base, bits, pos, perm_tok);
+  scatter_pairs(s_ids, T, k, base, bits, pos, perm_tok, gslot, pslot);
 }
 
 __global__ void __launch_bounds__(1024)
 topk_group_kernel(const float* __restrict__ z, int T, int E, int k, int32_t* __restrict__ ids,
                   float* __restrict__ w, const uint32_t* miss_mask, const int32_t* slot_row, int mb,
                   int32_t* counts, int32_t* offsets, int32_t* __restrict__ pos, int32_t* __restrict__ perm_tok,
-                  WorkList* wl, int* err) {
+                  WorkList* wl, int* err, int32_t* pslot) {
   __shared__ uint32_t bits[256 * 8];
   __shared__ int base[256];
+  __shared__ int gslot[256];
   __shared__ int tmp[12];
   __shared__ int32_t s_ids[TG_MAX_T * 8];
   __shared__ TopkScratch sc[TG_MAX_T];
@@ -532,7 +544,7 @@ topk_group_kernel(const float* __restrict__ z, int T, int E, int k, int32_t* __r
     topk_row(z + (size_t)wave * E, E, k, ids + (size_t)wave * k, w + (size_t)wave * k, s_ids + wave * k,
              sc + wave);
   __syncthreads();
-  group_from_lds(s_ids, T, k, E, em, mb, counts, offsets, pos, perm_tok, wl, err, bits, base, tmp);
+  group_from_lds(s_ids, T, k, E, em, mb, counts, offsets, pos, perm_tok, wl, err, pslot, bits, base, gslot, tmp);
 }
 
 // General path, pass 1: per-block histograms hist[b][e].
@@ -602,15 +614,17 @@ extern "C" hipError_t moe_launch_topk(const float* z, int T, int E, int k, int32
 
 // Top-k and grouping in one launch for T <= 16 (same outputs as
 // moe_launch_topk followed by moe_launch_group).
+// pslot (may be null): [T * k], per (token, choice) the slot its expert runs
+// from on the GPU, -1 where it does not.
 extern "C" hipError_t moe_launch_topk_group(const float* z, int T, int E, int k, int32_t* ids, float* w,
                                             const uint32_t* miss_mask, const int32_t* slot_row, int mb,
                                             int32_t* counts, int32_t* offsets, int32_t* pos, int32_t* perm_tok,
-                                            WorkList* wl, int* err, hipStream_t s) {
+                                            WorkList* wl, int* err, int32_t* pslot, hipStream_t s) {
   if (T < 1 || T > TG_MAX_T || E > 256 || k > 8) return hipErrorInvalidValue;
   // one wave per token, at least the four waves the grouping needs (fewer
   // waves make its barriers cheaper)
   topk_group_kernel<<<1, 64 * (T < 4 ? 4 : T), 0, s>>>(z, T, E, k, ids, w, miss_mask, slot_row, mb, counts, offsets,
-                                                       pos, perm_tok, wl, err);
+                                                       pos, perm_tok, wl, err, pslot);
   return hipGetLastError();
 }
 
