@@ -16,7 +16,8 @@
 // ---------------------------------------------------------------------------
 
 // Small batches: one wave per (expert, 4 tokens), grid (E/4, T/4) so that
-// every CU takes part.  A lane covers 4 consecutive elements of each
+// every CU takes part (8 tokens per wave, so that each expert row is read by
+// half as many workgroups, ran the 32- and 64-token router 2 us slower).  A lane covers 4 consecutive elements of each
 // 256-element chunk of H and issues the loads of 8 chunks (2048 elements) at
 // once, so a wave waits for memory once per 2048 elements instead of once
 // per chunk.  Loads and sums are unconditional (token rows past T re-read

@@ -44,7 +44,7 @@ def _get(setups, name):
 
 
 @pytest.mark.parametrize("name", list(CASES))
-@pytest.mark.parametrize("T", [1, 2, 4, 8, 16, 100, 300, 1000])
+@pytest.mark.parametrize("T", [1, 2, 4, 8, 16, 40, 100, 300, 1000])
 def test_forward_matches_oracle(setups, name, T):
     print(f"forward {name} T={T}", flush=True)
     s = _get(setups, name)
