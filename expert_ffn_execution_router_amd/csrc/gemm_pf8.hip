@@ -49,6 +49,13 @@
 //     group g is the 24 bytes of K [32g, 32g+32), one 16-byte and one 8-byte
 //     aligned read (x6_off16, x6_off8), and E2M1 x E2M3 issues at the 6/4-bit
 //     rate (1.7x the E2M1 x E4M3 rate, measured);
+//   * E2M1 weights: the E8M0 scales are stored by row (K/32 bytes a row), so
+//     one chunk's 4 bytes of each of 256 rows are 256 separate requests; the
+//     weight waves load them 16 bytes a row (four chunks) at the first chunk
+//     of each group of four into one of two group buffers outside the stage
+//     ring (a group's buffer is reused two groups later, after the chunk
+//     barriers), and only chunks past the last whole group of an item load
+//     their 4 bytes with the chunk;
 //   * few tokens per expert (a weight stream more than a GEMM): tiles of 128
 //     tokens and three LDS stages, so two chunks are in flight while one is
 //     multiplied; the wait before a chunk counts only loads (the ones this
@@ -93,6 +100,9 @@ struct QCfg {
   static constexpr int WS_OFF = XS_OFF + XS_BYTES;
   static constexpr int WS_BYTES = W4 ? Q_BN * 4 : 256;
   static constexpr int STAGE = WS_OFF + WS_BYTES;
+  // E2M1 weights: two group buffers of 16 scale bytes (four chunks) per row
+  static constexpr int GB_BYTES = W4 ? 2 * Q_BN * 16 : 0;
+  static constexpr int LDS = NST * STAGE + GB_BYTES;
 };
 
 struct QItem {
@@ -132,7 +142,7 @@ gemm_pf_q8(const WorkList* __restrict__ wl, const int32_t* __restrict__ counts,
            size_t woff1, size_t soff0, size_t soff1, const uint8_t* __restrict__ X, const uint8_t* __restrict__ Xs,
            int xcap, int K, int N, void* __restrict__ out, int trash_row) {
   using C = QCfg<FMT, VAR>;
-  static_assert(C::NST * C::STAGE + 4200 <= 160 * 1024, "LDS budget");
+  static_assert(C::LDS + 4200 <= 160 * 1024, "LDS budget");
   extern __shared__ __align__(16) uint8_t lds[];
   __shared__ int l_pref[257], l_slot[256], l_row0[256], l_cnt[256];
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
@@ -256,7 +266,8 @@ gemm_pf_q8(const WorkList* __restrict__ wl, const int32_t* __restrict__ counts,
       }
     }
   };
-  int iss_it = it0, iss_c = 0;
+  int iss_it = it0, iss_c = 0, iss_g = -1;
+  lds_u8_t* const gb = (lds_u8_t*)lds + C::NST * C::STAGE;    // scale group buffers (E2M1 weights)
   {
     QItem t;
     decode(iss_it, t);
@@ -297,8 +308,16 @@ gemm_pf_q8(const WorkList* __restrict__ wl, const int32_t* __restrict__ counts,
       for (int q = 0; q < C::WLOADS; ++q) dma16(wb_ + src[q], sb + C::W_OFF + (wv * C::WLOADS + q) * 1024);
       n = C::WLOADS;
       if (C::W4) {
-        dma4(wbase + ws_src + kc * 4, sb + C::WS_OFF + wv * 256);
-        ++n;
+        if ((kc & ~3) + 4 <= nchunk) {                     // in a whole group of four chunks
+          if ((kc & 3) == 0) {                             // its first: the group's 16 bytes a row
+            ++iss_g;
+            dma16(wbase + ws_src + kc * 4, gb + (iss_g & 1) * (Q_BN * 16) + wv * 1024);
+            ++n;
+          }
+        } else {
+          dma4(wbase + ws_src + kc * 4, sb + C::WS_OFF + wv * 256);
+          ++n;
+        }
       } else if (wv == 0) {
         dma4(wbase + ws_src + kc * 4, sb + C::WS_OFF);
         ++n;
@@ -332,7 +351,9 @@ gemm_pf_q8(const WorkList* __restrict__ wl, const int32_t* __restrict__ counts,
 #pragma unroll
     for (int j = 0; j < C::SUB; ++j) acc[i][j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
 
-  auto compute = [&](const uint8_t* sb) __attribute__((always_inline)) {
+  // wsb / wss: the E2M1 weight scales of the chunk, row r's byte for lane
+  // group g at wsb[r * wss + g]
+  auto compute = [&](const uint8_t* sb, const uint8_t* wsb, int wss) __attribute__((always_inline)) {
     i32x8_t wa[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -347,7 +368,7 @@ gemm_pf_q8(const WorkList* __restrict__ wl, const int32_t* __restrict__ counts,
     if (C::X6) {
       int wsc[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) wsc[i] = sb[C::WS_OFF + (wrow + 16 * i) * 4 + lg];
+      for (int i = 0; i < 4; ++i) wsc[i] = wsb[(wrow + 16 * i) * wss + lg];
       const uint8_t* rb = sb + C::T_OFF + trow * X6_ROWB;
       const int o16 = x6_off16(lg), o8 = x6_off8(lg);
 #pragma unroll
@@ -364,7 +385,7 @@ gemm_pf_q8(const WorkList* __restrict__ wl, const int32_t* __restrict__ counts,
     } else if (C::W4) {
       int wsc[4];
 #pragma unroll
-      for (int i = 0; i < 4; ++i) wsc[i] = sb[C::WS_OFF + (wrow + 16 * i) * 4 + lg];
+      for (int i = 0; i < 4; ++i) wsc[i] = wsb[(wrow + 16 * i) * wss + lg];
 #pragma unroll
       for (int j = 0; j < C::SUB; ++j) {
         const i32x4_t lo = lds16(sb + x_rd[0] + j * 16 * 128);
@@ -444,7 +465,7 @@ gemm_pf_q8(const WorkList* __restrict__ wl, const int32_t* __restrict__ counts,
   decode(it0, ct);
   QItem done{};
   bool pending = false;
-  int c = 0, stage = 0;
+  int c = 0, stage = 0, cg = -1;
   for (long v = 0; v < n_units; ++v) {
     if (C::NST == 3 && v + 1 < n_units) {
       switch (last_n) {                         // this wave's loads of unit v have landed
@@ -479,7 +500,15 @@ gemm_pf_q8(const WorkList* __restrict__ wl, const int32_t* __restrict__ counts,
     } else {
       if (v + 2 < n_units) last_n = issue(stage == 0 ? 2 : stage - 1);
     }
-    if (ct.nrows > wm * C::HALF) compute(lds + stage * C::STAGE);
+    const uint8_t* sbv = lds + stage * C::STAGE;
+    const uint8_t* wsb = sbv + C::WS_OFF;
+    int wss = 4;
+    if (C::W4 && (c & ~3) + 4 <= nchunk) {
+      if ((c & 3) == 0) ++cg;
+      wsb = lds + C::NST * C::STAGE + (cg & 1) * (Q_BN * 16) + (c & 3) * 4;
+      wss = 16;
+    }
+    if (ct.nrows > wm * C::HALF) compute(sbv, wsb, wss);
     stage = stage + 1 == C::NST ? 0 : stage + 1;
     if (++c == nchunk) {
       done = ct;
@@ -492,7 +521,7 @@ gemm_pf_q8(const WorkList* __restrict__ wl, const int32_t* __restrict__ counts,
 }
 
 template <int FMT, int VAR>
-static size_t lds_of() { return (size_t)QCfg<FMT, VAR>::NST * QCfg<FMT, VAR>::STAGE; }
+static size_t lds_of() { return (size_t)QCfg<FMT, VAR>::LDS; }
 
 extern "C" size_t moe_pf8_lds_bytes(int fmt, int small) {
   if (fmt == WFMT_MXFP4_A6) return small ? lds_of<WFMT_MXFP4_A6, 1>() : lds_of<WFMT_MXFP4_A6, 0>();
