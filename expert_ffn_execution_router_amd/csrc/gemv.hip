@@ -40,7 +40,7 @@
 
 namespace {
 
-constexpr int GV_MAXT = 8;      // tokens per expert (instances for 4 and 8)
+constexpr int GV_MAXT = 8;      // tokens per expert (instances for 1, 2, 4 and 8)
 constexpr int GV_BLK = 2;       // steps in flight (a step: 16 bytes of each of the wave's 4 rows per lane)
 
 DEV float dpp_add(float v, int ctrl_sel) {
@@ -117,13 +117,16 @@ DEV float fp8_dot4(uint32_t w, const float* x, float acc) {
 // rows ([T, K], fp16 for NVFP4, else bf16) gathered through row_tok, weights
 // gate at woff0 / soff0 and up at woff1 / soff1.  Otherwise out = Z (bf16
 // [rows, N], N = H) from X = A in grouped order, weights at woff0 / soff0.
-// Rows of expert e are offsets[e] .. + counts[e] <= MT (4 or 8).  K is a multiple of
+// Rows of expert e are offsets[e] .. + counts[e], MT (1, 2, 4 or 8) at a time.
+// The one-token instance is held to four waves per SIMD (128 registers: the
+// grids of the fp8 and MXFP4 shapes need more than one round of workgroups,
+// and residency decides their speed).  K is a multiple of
 // the values in 16 bytes of a row (8, 16 or 32; a row's last 256-byte
 // segment may be partial: lanes past it contribute nothing); N % 8 (gated)
 // or 16.  The grid may exceed the items (n_act * N / 8 or N / 16): the extra
 // workgroups leave at once.
 template <int FMT, bool GATED, int MT>
-__global__ void __launch_bounds__(256)
+__global__ void __launch_bounds__(256, MT == 1 ? 4 : 1)
 gemv_dec(const WorkList* __restrict__ wl, const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
          const uint8_t* __restrict__ pool, size_t S, size_t woff0, size_t woff1, size_t soff0, size_t soff1,
          const uint16_t* __restrict__ X, const int32_t* __restrict__ row_tok, int K, int N, uint16_t* __restrict__ out) {
@@ -305,9 +308,10 @@ gemv_dec(const WorkList* __restrict__ wl, const int32_t* __restrict__ counts, co
 // out_f32 (optional): the unrounded sum instead.  A: the GEMM 1 output in
 // grouped order (row pos[t, j]); pslot[t, j]: the slot of choice j's expert,
 // -1 where it did not run on the GPU (the fused top-k/grouping writes it);
-// K = I, N = H, N % 4 == 0.
+// K = I, N = H, N % 4 == 0.  Held to four waves per SIMD (two workgroups
+// per CU; MXFP4 spills a few registers there and still runs as fast).
 template <int FMT>
-__global__ void __launch_bounds__(512)
+__global__ void __launch_bounds__(512, 4)
 gemv_down_combine(const int32_t* __restrict__ pslot, const float* __restrict__ w, const int32_t* __restrict__ pos,
                   const uint8_t* __restrict__ pool, size_t S, size_t woff, size_t soff,
                   const uint16_t* __restrict__ A, int k, int K, int N, const float* hp,
@@ -466,17 +470,18 @@ hipError_t launch_gemv_mt(int gated, int grid, const WorkList* wl, const int32_t
   return hipGetLastError();
 }
 
-// Four tokens' accumulators keep more waves per SIMD than eight: the
-// 4-token instance serves every batch it can.
+// Fewer tokens' accumulators keep more waves per SIMD: each batch takes the
+// smallest instance that holds its largest expert's rows.
 template <int FMT>
 hipError_t launch_gemv(int max_rows, int gated, int grid, const WorkList* wl, const int32_t* counts,
                        const int32_t* offsets, const uint8_t* pool, size_t S, size_t woff0, size_t woff1, size_t soff0,
                        size_t soff1, const void* X, const int32_t* row_tok, int K, int N, void* out, hipStream_t s) {
-  if (max_rows <= 4)
-    return launch_gemv_mt<FMT, 4>(gated, grid, wl, counts, offsets, pool, S, woff0, woff1, soff0, soff1, X, row_tok,
-                                  K, N, out, s);
-  return launch_gemv_mt<FMT, 8>(gated, grid, wl, counts, offsets, pool, S, woff0, woff1, soff0, soff1, X, row_tok,
-                                K, N, out, s);
+#define MOE_GVM_ARGS gated, grid, wl, counts, offsets, pool, S, woff0, woff1, soff0, soff1, X, row_tok, K, N, out, s
+  if (max_rows == 1) return launch_gemv_mt<FMT, 1>(MOE_GVM_ARGS);
+  if (max_rows == 2) return launch_gemv_mt<FMT, 2>(MOE_GVM_ARGS);
+  if (max_rows <= 4) return launch_gemv_mt<FMT, 4>(MOE_GVM_ARGS);
+  return launch_gemv_mt<FMT, 8>(MOE_GVM_ARGS);
+#undef MOE_GVM_ARGS
 }
 }  // namespace
 
