@@ -21,7 +21,7 @@ combine_kernel(const uint16_t* __restrict__ Z, const int32_t* __restrict__ ids, 
                const int32_t* __restrict__ slot_row, const float* hp, const int32_t* __restrict__ hp_count, int T,
                int k, int H, uint16_t* __restrict__ out, float* out_f32) {
   const int t = blockIdx.y;
-  const int h = (blockIdx.x * 256 + threadIdx.x) * 8;
+  const int h = (blockIdx.x * blockDim.x + threadIdx.x) * 8;
   if (t >= T || h >= H) return;
   float acc[8];
 #pragma unroll
@@ -247,8 +247,9 @@ extern "C" hipError_t moe_launch_combine(const uint16_t* Z, const int32_t* ids, 
                                          const int32_t* hp_count, int T, int k, int H, uint16_t* out,
                                          float* out_f32, hipStream_t s) {
   if (T == 0) return hipSuccess;
-  dim3 g((H / 8 + 255) / 256, T);
-  combine_kernel<<<g, 256, 0, s>>>(Z, ids, w, pos, miss_mask, slot_row, hp, hp_count, T, k, H, out, out_f32);
+  // one wave per workgroup: a token's H/8 threads spread over H/512 CUs
+  dim3 g((H / 8 + 63) / 64, T);
+  combine_kernel<<<g, 64, 0, s>>>(Z, ids, w, pos, miss_mask, slot_row, hp, hp_count, T, k, H, out, out_f32);
   return hipGetLastError();
 }
 

@@ -285,7 +285,7 @@ topk_kernel(const float* __restrict__ z, int T, int E, int k, int32_t* __restric
             float* __restrict__ w) {
   __shared__ TopkScratch sc[4];
   const int wave = threadIdx.x >> 6;
-  const int t = blockIdx.x * 4 + wave;
+  const int t = blockIdx.x * (blockDim.x >> 6) + wave;
   if (t >= T) return;
   topk_row(z + (size_t)t * E, E, k, ids + (size_t)t * k, w + (size_t)t * k, nullptr, sc + wave);
 }
@@ -615,7 +615,8 @@ extern "C" hipError_t moe_launch_router(const uint16_t* x, const float* R, const
 }
 
 extern "C" hipError_t moe_launch_topk(const float* z, int T, int E, int k, int32_t* ids, float* w, hipStream_t s) {
-  topk_kernel<<<(T + 3) / 4, 256, 0, s>>>(z, T, E, k, ids, w);
+  // one wave (token) per workgroup
+  topk_kernel<<<T, 64, 0, s>>>(z, T, E, k, ids, w);
   return hipGetLastError();
 }
 
