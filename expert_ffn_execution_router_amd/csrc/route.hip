@@ -529,6 +529,90 @@ DEV void group_from_lds(const int32_t* s_ids, int T, int k, int E, ExpertMeta em
   scatter_pairs(s_ids, T, k, base, bits, pos, perm_tok, gslot, pslot);
 }
 
+// The grouping of group_from_lds by wave 0 alone, for at most 64 routed
+// pairs (T * k <= 64, so T <= 32 and one presence word per expert): lane p
+// takes pair p for the marking and the scatter, and experts lane + 64i for
+// the counts; the three scans run over the wave (DPP) in expert order, slot
+// by slot, so no workgroup barrier is needed.  Same outputs as
+// group_from_lds.  bits / off / gsl: LDS [E] each.
+
+// The mask words and slots of experts lane + 64i (0 / 0 without a mask or
+// table), loaded at the kernel's start so they overlap the top-k.
+struct WaveMeta {
+  uint32_t mw[4];
+  int sl[4];
+};
+
+DEV WaveMeta wave_meta(int E, const uint32_t* miss_mask, const int32_t* slot_row) {
+  const int lane = threadIdx.x & 63;
+  WaveMeta m;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int e = lane + 64 * i;
+    m.mw[i] = 0u;
+    m.sl[i] = 0;
+    if (e < E) {
+      if (miss_mask) m.mw[i] = miss_mask[e >> 5];
+      if (slot_row) m.sl[i] = slot_row[e];
+    }
+  }
+  return m;
+}
+
+DEV void group_wave(const int32_t* s_ids, int T, int k, int E, const WaveMeta& wm, int mb, int32_t* counts,
+                    int32_t* offsets, int32_t* __restrict__ pos, int32_t* __restrict__ perm_tok, WorkList* wl,
+                    int* err, int32_t* pslot, uint32_t* bits, int* off, int* gsl) {
+  const int lane = threadIdx.x & 63;
+  const int P = T * k, ns = (E + 63) >> 6;
+  const uint32_t* mw = wm.mw;
+  const int* sl = wm.sl;
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+    if (i < ns && lane + 64 * i < E) bits[lane + 64 * i] = 0u;
+  wave_lds_order();
+  const int pe = lane < P ? s_ids[lane] : 0, pt = lane < P ? lane / k : 0;
+  if (lane < P) atomicOr(&bits[pe], 1u << pt);
+  wave_lds_order();
+  int c_off = 0, c_act = 0, c_blk = 0;         // totals of the slots before i
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    if (i >= ns) break;
+    const int e = lane + 64 * i;
+    const int c = e < E ? __popc(bits[e]) : 0;
+    bool act = false;
+    int slot = -1;
+    if (c > 0 && !((mw[i] >> (e & 31)) & 1u)) {
+      slot = sl[i];
+      if (slot < 0) atomicOr(err, 1);
+      else act = true;
+    }
+    const int nb = act ? (c + mb - 1) / mb : 0;
+    const int io = wave_incl_sum(c), ia = wave_incl_sum(act ? 1 : 0), ib = wave_incl_sum(nb);
+    const int o = c_off + io - c, a = c_act + ia - (act ? 1 : 0), pb = c_blk + ib - nb;
+    if (e < E) {
+      counts[e] = c;
+      offsets[e] = o;
+      off[e] = o;
+      gsl[e] = act ? slot : -1;
+    }
+    if (act) { wl->act_e[a] = e; wl->act_slot[a] = slot; wl->mblk_prefix[a] = pb; }
+    c_off += __builtin_amdgcn_readlane(io, 63);
+    c_act += __builtin_amdgcn_readlane(ia, 63);
+    c_blk += __builtin_amdgcn_readlane(ib, 63);
+  }
+  if (lane == 0) {
+    offsets[E] = c_off;
+    wl->n_act = c_act; wl->n_mblk = c_blk; wl->mb = mb; wl->mblk_prefix[c_act] = c_blk;
+  }
+  wave_lds_order();
+  if (lane < P) {
+    const int d = off[pe] + __popc(bits[pe] & ((1u << pt) - 1u));
+    pos[lane] = d;
+    perm_tok[d] = pt;
+    if (pslot) pslot[lane] = gsl[pe];
+  }
+}
+
 __global__ void __launch_bounds__(1024)
 topk_group_kernel(const float* __restrict__ z, int T, int E, int k, int32_t* __restrict__ ids,
                   float* __restrict__ w, const uint32_t* miss_mask, const int32_t* slot_row, int mb,
@@ -540,8 +624,19 @@ topk_group_kernel(const float* __restrict__ z, int T, int E, int k, int32_t* __r
   __shared__ int tmp[12];
   __shared__ int32_t s_ids[TG_MAX_T * 8];
   __shared__ TopkScratch sc[TG_MAX_T];
-  const ExpertMeta em = expert_meta(E, miss_mask, slot_row);
   const int wave = threadIdx.x >> 6;
+  if (T * k <= 64) {               // one wave groups the at most 64 pairs
+    WaveMeta wm{};
+    if (wave == 0) wm = wave_meta(E, miss_mask, slot_row);
+    if (wave < T)
+      topk_row(z + (size_t)wave * E, E, k, ids + (size_t)wave * k, w + (size_t)wave * k, s_ids + wave * k,
+               sc + wave);
+    __syncthreads();
+    if (wave == 0)
+      group_wave(s_ids, T, k, E, wm, mb, counts, offsets, pos, perm_tok, wl, err, pslot, bits, base, gslot);
+    return;
+  }
+  const ExpertMeta em = expert_meta(E, miss_mask, slot_row);
   if (wave < T)
     topk_row(z + (size_t)wave * E, E, k, ids + (size_t)wave * k, w + (size_t)wave * k, s_ids + wave * k,
              sc + wave);
