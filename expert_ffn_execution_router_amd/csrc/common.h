@@ -58,6 +58,26 @@ struct WorkList {
   int mblk_prefix[257];
 };
 
+// A gate/up matrix-vector launch that routes its one token itself (T = 1):
+// every workgroup picks its expert from the router logits, and workgroup 0
+// also writes the routing and grouping outputs (ids, w, counts, offsets,
+// pos, perm_tok, the work list, per-pair slots) for the launches after it.
+struct GemvRoute {
+  const float* z;                 // logits [E]
+  int E, k, mb;
+  const uint32_t* miss_mask;      // may be null
+  const int32_t* slot_row;        // may be null: grouping only
+  int32_t* ids;
+  float* w;
+  int32_t* counts;
+  int32_t* offsets;
+  int32_t* pos;
+  int32_t* perm_tok;
+  WorkList* wl;
+  int* err;
+  int32_t* pslot;
+};
+
 // Optional split of the large-batch work: an expert whose last m-tile would
 // hold at most tau rows keeps one tile fewer, its main rows (mcounts) going
 // to the tiled kernels through the main work list and the overflow rows

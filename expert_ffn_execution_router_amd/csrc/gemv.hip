@@ -36,7 +36,7 @@
 //     and two lane shuffles across the rows; a wave's four rows of GEMM 1
 //     are the gate and up rows of two features, so the SwiGLU needs no
 //     exchange.
-#include "common.h"
+#include "route_dev.h"
 
 namespace {
 
@@ -125,11 +125,19 @@ DEV float fp8_dot4(uint32_t w, const float* x, float acc) {
 // segment may be partial: lanes past it contribute nothing); N % 8 (gated)
 // or 16.  The grid may exceed the items (n_act * N / 8 or N / 16): the extra
 // workgroups leave at once.
-template <int FMT, bool GATED, int MT>
+// ROUTE (GATED, MT = 1, one token): the item's expert is the a-th of the
+// token's winners that run on the GPU (expert order), picked by wave 0 from
+// the logits (rt.z) with the top-k selection of topk_row, its grouped row
+// the number of winners with a lower id; workgroup 0 also writes the routing
+// and grouping outputs at the end (topk_row and group_wave).  wl, counts,
+// offsets and row_tok are not read.
+template <int FMT, bool GATED, int MT, bool ROUTE = false>
 __global__ void __launch_bounds__(256, MT == 1 ? 4 : 1)
 gemv_dec(const WorkList* __restrict__ wl, const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
          const uint8_t* __restrict__ pool, size_t S, size_t woff0, size_t woff1, size_t soff0, size_t soff1,
-         const uint16_t* __restrict__ X, const int32_t* __restrict__ row_tok, int K, int N, uint16_t* __restrict__ out) {
+         const uint16_t* __restrict__ X, const int32_t* __restrict__ row_tok, int K, int N, uint16_t* __restrict__ out,
+         GemvRoute rt = GemvRoute{}) {
+  static_assert(!ROUTE || (GATED && MT == 1), "self-routed launches: gate/up, one token");
   constexpr bool NV = FMT == WFMT_NVFP4;
   constexpr bool W4 = NV || FMT == WFMT_MXFP4_A16;
   constexpr int V = FMT == WFMT_BF16 ? 8 : (W4 ? 32 : 16);       // weights per lane and step
@@ -138,14 +146,54 @@ gemv_dec(const WorkList* __restrict__ wl, const int32_t* __restrict__ counts, co
   const int per_e = GATED ? N / 8 : N / 16;          // items per expert
   const int it = blockIdx.x;
   const int a = it / per_e, blk = it - a * per_e;
-  // the item's work-list entries are read beside the count (entries past
-  // n_act are not used), so the weight addresses wait for one load
-  const int ac = min(a, 255);
-  const int nact = wl->n_act, e = wl->act_e[ac], slot = wl->act_slot[ac];
-  if (a >= nact) return;
+  int slot, rbase, ctot;
+  if constexpr (ROUTE) {
+    __shared__ int s_pick[3];                        // slot, grouped row, found
+    if (wave == 0) {
+      const WaveMeta wm = wave_meta(rt.E, rt.miss_mask, rt.slot_row);
+      uint64_t selm[4];
+      topk_select(rt.z, rt.E, rt.k, selm);
+      int n_act = 0, n_sel = 0, p_slot = 0, p_row = 0, found = 0;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int ee = lane + 64 * i;
+        const bool act = ((selm[i] >> lane) & 1ull) && !((wm.mw[i] >> (ee & 31)) & 1u) && wm.sl[i] >= 0;
+        const uint64_t am = __builtin_amdgcn_ballot_w64(act);
+        const int n = __popcll(am);
+        if (!found && a < n_act + n) {
+          uint64_t m = am;
+          for (int q = 0; q < a - n_act; ++q) m &= m - 1ull;
+          const int L = __builtin_ctzll(m);
+          p_slot = __builtin_amdgcn_readlane(wm.sl[i], L);
+          p_row = n_sel + __popcll(selm[i] & ((1ull << L) - 1ull));
+          found = 1;
+        }
+        n_act += n;
+        n_sel += __popcll(selm[i]);
+      }
+      if (lane == 0) {
+        s_pick[0] = p_slot;
+        s_pick[1] = p_row;
+        s_pick[2] = found;
+      }
+    }
+    __syncthreads();
+    if (!s_pick[2] && blockIdx.x != 0) return;
+    slot = s_pick[2] ? s_pick[0] : 0;
+    rbase = s_pick[1];
+    ctot = s_pick[2];                                // one row, or none (workgroup 0 still routes)
+  } else {
+    // the item's work-list entries are read beside the count (entries past
+    // n_act are not used), so the weight addresses wait for one load
+    const int ac = min(a, 255);
+    const int nact = wl->n_act, e = wl->act_e[ac];
+    slot = wl->act_slot[ac];
+    if (a >= nact) return;
+    rbase = offsets[e];
+    ctot = counts[e];
+  }
   const uint8_t* blob = pool + (size_t)slot * S;
   const int rowb = K * WB2 / 2;                      // weight bytes per row
-  const int rbase = offsets[e], ctot = counts[e];
   // the expert's rows in chunks of MT (the batch bounds them by MT; a chunk
   // loop keeps the kernel correct for any count)
   for (int tc = 0; tc < ctot; tc += MT) {
@@ -168,7 +216,7 @@ gemv_dec(const WorkList* __restrict__ wl, const int32_t* __restrict__ counts, co
 #pragma unroll
     for (int t = 0; t < MT; ++t) {
       const int r = row0 + min(t, cnt - 1);
-      const int xrow = GATED ? row_tok[r] : r;
+      const int xrow = ROUTE ? 0 : (GATED ? row_tok[r] : r);
       xr[t] = (const uint8_t*)X + (size_t)xrow * K * 2 + lane * (2 * V);
     }
     float acc[4][MT];
@@ -292,6 +340,20 @@ gemv_dec(const WorkList* __restrict__ wl, const int32_t* __restrict__ counts, co
             out[(size_t)(row0 + t) * N + blk * 16 + 4 * wave + q] = f32_to_bf16_bits(NV ? acc[q][t] * ts : acc[q][t]);
         }
       }
+    }
+  }
+  if constexpr (ROUTE) {
+    // workgroup 0: the token's routing and grouping for the launches after this one
+    if (blockIdx.x == 0 && wave == 0) {
+      __shared__ TopkScratch r_sc;
+      __shared__ int32_t r_ids[8];
+      __shared__ uint32_t r_bits[256];
+      __shared__ int r_off[256], r_gsl[256];
+      const WaveMeta wm = wave_meta(rt.E, rt.miss_mask, rt.slot_row);
+      topk_row(rt.z, rt.E, rt.k, rt.ids, rt.w, r_ids, &r_sc);
+      wave_lds_order();
+      group_wave(r_ids, 1, rt.k, rt.E, wm, rt.mb, rt.counts, rt.offsets, rt.pos, rt.perm_tok, rt.wl, rt.err,
+                 rt.pslot, r_bits, r_off, r_gsl);
     }
   }
 }
@@ -457,6 +519,15 @@ gemv_down_combine(const int32_t* __restrict__ pslot, const float* __restrict__ w
 }
 
 namespace {
+template <int FMT>
+hipError_t launch_gemv_routed(int grid, const GemvRoute& rt, const uint8_t* pool, size_t S, size_t woff0,
+                              size_t woff1, size_t soff0, size_t soff1, const void* X, int K, int N, void* out,
+                              hipStream_t s) {
+  gemv_dec<FMT, true, 1, true><<<grid, 256, 0, s>>>(nullptr, nullptr, nullptr, pool, S, woff0, woff1, soff0, soff1,
+                                                    (const uint16_t*)X, nullptr, K, N, (uint16_t*)out, rt);
+  return hipGetLastError();
+}
+
 template <int FMT, int MT>
 hipError_t launch_gemv_mt(int gated, int grid, const WorkList* wl, const int32_t* counts, const int32_t* offsets,
                           const uint8_t* pool, size_t S, size_t woff0, size_t woff1, size_t soff0, size_t soff1,
@@ -530,3 +601,24 @@ extern "C" hipError_t moe_launch_gemv_down_combine(int fmt, const int32_t* pslot
 }
 
 extern "C" int moe_gemv_max_tokens() { return GV_MAXT; }
+
+// The gate/up matrix-vector launch of a one-token batch that routes for
+// itself (GemvRoute): grid at least min(k, E) * N / 8 workgroups (the
+// experts that run on the GPU are at most k); X holds the token's row (bf16,
+// or fp16 for NVFP4).
+extern "C" hipError_t moe_launch_gemv_routed(int fmt, int grid, const GemvRoute* rt, const uint8_t* pool, size_t S,
+                                             size_t woff0, size_t woff1, size_t soff0, size_t soff1, const void* X,
+                                             int K, int N, void* out, hipStream_t s) {
+  const int kq = fmt == WFMT_BF16 ? 8 : (fmt == WFMT_FP8_A16 ? 16 : 32);
+  if (!rt || grid < 1 || K % kq || N % 8 || rt->E < 1 || rt->E > 256 || rt->k < 1 || rt->k > 8 || rt->k > rt->E)
+    return hipErrorInvalidValue;
+#define MOE_GR_ARGS grid, *rt, pool, S, woff0, woff1, soff0, soff1, X, K, N, out, s
+  switch (fmt) {
+    case WFMT_BF16: return launch_gemv_routed<WFMT_BF16>(MOE_GR_ARGS);
+    case WFMT_FP8_A16: return launch_gemv_routed<WFMT_FP8_A16>(MOE_GR_ARGS);
+    case WFMT_MXFP4_A16: return launch_gemv_routed<WFMT_MXFP4_A16>(MOE_GR_ARGS);
+    case WFMT_NVFP4: return launch_gemv_routed<WFMT_NVFP4>(MOE_GR_ARGS);
+    default: return hipErrorInvalidValue;
+  }
+#undef MOE_GR_ARGS
+}
