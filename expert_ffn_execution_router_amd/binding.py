@@ -46,7 +46,8 @@ class moe_plan_totals(ctypes.Structure):
 class moe_calibration(ctypes.Structure):
     _fields_ = [(f, ctypes.c_double) for f in ("B_P", "B_P_min", "B_P_max", "B_H", "host_alone", "host_alone_min",
                                                "host_alone_max", "host_conc", "host_conc_min", "host_conc_max")] + \
-        [(f, ctypes.c_int) for f in ("n_copy", "n_host_alone", "n_host_conc")]
+        [(f, ctypes.c_int) for f in ("n_copy", "n_host_alone", "n_host_conc")] + \
+        [(f, ctypes.c_double) for f in ("host_alone_1", "host_conc_1", "host_t0_us", "B_R")]
 
     def as_dict(self):
         return {f: getattr(self, f) for f, _ in self._fields_}

@@ -238,6 +238,7 @@ struct moe_ctx {
   // policy
   int policy = MOE_POLICY_OFFLOAD;
   double BP = 1.0, BH = 1.0;
+  double host_t0_us = 0.0;              // per-call time of the host branch (calibrated)
   int act = MOE_ACT_DEFAULT;              // MXFP4's large-batch activation format
   // asynchronous decode: host-branch callback arguments, one per (layer, T),
   // alive until moe_destroy because captured graphs keep their addresses
@@ -357,6 +358,10 @@ int nthreads_of(const moe_config& c) {
 }
 
 HostFfnShape host_shape(const moe_config& c, size_t S) { return HostFfnShape{c.wfmt, c.E, c.k, c.H, c.I, S}; }
+
+// Idle time before each timed host-branch call of the calibration: about a
+// small-batch decode layer's GPU work ahead of its host branch.
+constexpr int kHostIdleGapUs = 200;
 
 
 // Grouping, quantisation and both grouped GEMMs for a routed batch (ids/w in
@@ -600,7 +605,8 @@ void fill_info(moe_ctx* c, moe_plan_info* info) {
   const double S = (double)c->bl.S;
   info->t_fill_pred_us = p.q * S / (c->BP * 1e9) * 1e6;
   const double BR = c->BH - c->BP;
-  info->t_host_pred_us = p.n_host == 0 ? 0.0 : (BR > 0 ? p.n_host * S / (BR * 1e9) * 1e6 : INFINITY);
+  info->t_host_pred_us =
+      p.n_host == 0 ? 0.0 : (BR > 0 ? c->host_t0_us + p.n_host * S / (BR * 1e9) * 1e6 : INFINITY);
 }
 
 int issue_fills(moe_ctx* c, int layer, const int* experts, const int* slots, int n, hipStream_t copy) {
@@ -1278,11 +1284,10 @@ int moe_calibrate_ex(moe_ctx* c, int T, moe_calibration* out) {
   };
   // the host branch on a group of G = min(k, E) distinct experts of one
   // layer, each with all T tokens routed to it: at T = 1 the job the decode
-  // path hands the host when all of a token's experts miss.  A single expert
-  // at T = 1 runs for tens of microseconds, where the pool's wake-up and the
-  // host's scheduling noise are a large share of the time.  Groups walk
-  // (layer, expert) pairs spread over the pool, so no call finds its bytes
-  // in the host caches.
+  // path hands the host when all of a token's experts miss; and on a single
+  // expert, the smallest job.  The two sizes alternate, so both see the same
+  // host conditions.  Groups walk (layer, expert) pairs spread over the
+  // pool, so no call finds its bytes in the host caches.
   const int G = std::min(g.k, g.E);
   std::vector<uint16_t> hid((size_t)T * g.H, 0x3f80);
   std::vector<int32_t> ids((size_t)T * g.k, -1);
@@ -1290,31 +1295,46 @@ int moe_calibrate_ex(moe_ctx* c, int T, moe_calibration* out) {
   std::vector<float> outv((size_t)T * g.H);
   std::vector<int32_t> grp(G);
   int pair = 0;
-  auto host_call = [&]() -> double {
+  auto host_call = [&](int n) -> double {      // weight bytes per second of one call on n experts
     const int i = pair++;
     const int l = (int)(((long)i * 5 + 1) % g.L), e0 = (int)(((long)i * 37 + 3) % g.E);
-    for (int j = 0; j < G; ++j) grp[j] = (e0 + j) % g.E;
-    std::sort(grp.begin(), grp.end());
+    for (int j = 0; j < n; ++j) grp[j] = (e0 + j) % g.E;
+    std::sort(grp.begin(), grp.begin() + n);
+    std::fill(ids.begin(), ids.end(), -1);
     for (int t = 0; t < T; ++t)
-      for (int j = 0; j < G; ++j) ids[(size_t)t * g.k + j] = grp[j];
+      for (int j = 0; j < n; ++j) ids[(size_t)t * g.k + j] = grp[j];
     HostFfnHandle* h = host_ffn_start(c->pool, host_shape(g, S), c->host_pool, l, T, hid.data(), ids.data(),
-                                      w.data(), grp.data(), G, outv.data());
+                                      w.data(), grp.data(), n, outv.data());
     const double ms = host_ffn_wait(c->pool, h);
-    return (double)G * S / (ms * 1e-3) / 1e9;
+    return (double)n * S / (ms * 1e-3) / 1e9;
+  };
+  // The decode path calls the host branch once per layer, after the pool
+  // has idled through the layer's routing and planning; each timed call
+  // follows an idle gap of that order, so the workers' wake-up from idle is
+  // part of what is timed.
+  const auto idle_gap = std::chrono::microseconds(kHostIdleGapUs);
+  auto gapped_call = [&](int n) {
+    std::this_thread::sleep_for(idle_gap);
+    return host_call(n);
   };
   // warm-up until the pool's threads run at speed: at least 8 calls and
   // 100 ms (right after a large pool fill the first tens of ms run up to a
-  // third slower); then 40 timed calls (single calls vary by tens of
-  // percent on a shared host, so the median needs many)
+  // third slower); then 40 timed calls of each size (single calls vary by
+  // tens of percent on a shared host, so the medians need many)
   const int n_host = 40;
   {
     const auto w0 = std::chrono::steady_clock::now();
     for (int i = 0; i < 8 || std::chrono::steady_clock::now() - w0 < std::chrono::milliseconds(100); ++i)
-      (void)host_call();
+      (void)host_call(G);
   }
-  std::vector<double> alone;
-  for (int i = 0; i < n_host; ++i) alone.push_back(host_call());
+  std::vector<double> alone, alone1;
+  for (int i = 0; i < n_host; ++i) {
+    alone.push_back(gapped_call(G));
+    alone1.push_back(gapped_call(1));
+  }
+  double lo1, hi1;
   summarise(alone, out->host_alone, out->host_alone_min, out->host_alone_max);
+  summarise(alone1, out->host_alone_1, lo1, hi1);
   out->n_host_alone = (int)alone.size();
 
   // B_P: whole-expert copies from distinct host rows into the highest slots
@@ -1354,32 +1374,52 @@ int moe_calibrate_ex(moe_ctx* c, int T, moe_calibration* out) {
     // warms the concurrent regime and is not counted (measured once per
     // calibration, the concurrent rate of a process's first calibration ran
     // up to a fifth below that of its second).
-    const double host_s = (n_host + 1) * (double)G * S / (out->host_alone * 1e9);
+    const double host_s = (n_host + 1) * ((double)G * S / (out->host_alone * 1e9) + (double)S / (out->host_alone_1 * 1e9) +
+                                          2e-6 * kHostIdleGapUs);
     const double copy_s = (double)S / (out->B_P * 1e9);
-    const int n_train = (int)std::min(512.0, std::max(4.0 * n_cp, std::ceil(3.0 * host_s / copy_s)));
-    std::vector<double> conc;
+    const int n_train = (int)std::min(1024.0, std::max(4.0 * n_cp, std::ceil(3.0 * host_s / copy_s)));
+    std::vector<double> conc, conc1;
     for (int rep = 0; rep < 2; ++rep) {
       for (int i = 0; i < n_train; ++i) HIPCHK(c, copy(i));
       HIPCHK(c, hipEventRecord(t1, cs));
       for (int i = 0; i < n_host + 1; ++i) {
         if (hipEventQuery(t1) != hipErrorNotReady) break;
-        const double r = host_call();
+        const double r = gapped_call(G);
         if (hipEventQuery(t1) != hipErrorNotReady) break;   // the train ended during the call
-        if (i > 0 && rep == 1) conc.push_back(r);
+        const double r1 = gapped_call(1);
+        if (hipEventQuery(t1) != hipErrorNotReady) break;
+        if (i > 0 && rep == 1) {
+          conc.push_back(r);
+          conc1.push_back(r1);
+        }
       }
       HIPCHK(c, hipEventSynchronize(t1));
     }
     summarise(conc, out->host_conc, out->host_conc_min, out->host_conc_max);
+    summarise(conc1, out->host_conc_1, lo1, hi1);
     out->n_host_conc = (int)conc.size();
     (void)hipEventDestroy(t0);
     (void)hipEventDestroy(t1);
     (void)hipStreamDestroy(cs);
   }
-  // the residual bandwidth the q* split gives the host branch (review
-  // section 2.5: B_R = B_H - B_P): measured directly with the link busy when
-  // enough calls ran inside the copy train, else the standalone rate
-  const double BR = out->n_host_conc >= 3 ? out->host_conc : out->host_alone;
+  // t(n) = t0 + n S / B_R through the medians at n = 1 and n = G (review
+  // section 2.5: B_R = B_H - B_P is the rate the host branch adds); with the
+  // link busy when at least 3 pairs of calls ran inside the copy train,
+  // else alone.  A single size (G = 1), or medians whose line has no
+  // positive intercept, leave t0 = 0 and B_R the rate at G.
+  const bool conc_ok = out->n_host_conc >= 3;
+  const double rG = conc_ok ? out->host_conc : out->host_alone, r1 = conc_ok ? out->host_conc_1 : out->host_alone_1;
+  const double msG = (double)G * S / (rG * 1e9) * 1e3, ms1 = (double)S / (r1 * 1e9) * 1e3;
+  double BR = rG, t0_us = 0.0;
+  const double tau = G > 1 ? (msG - ms1) / (G - 1) : 0.0;   // ms per further expert
+  if (G > 1 && tau > 0 && ms1 > tau) {
+    BR = (double)S / (tau * 1e-3) / 1e9;
+    t0_us = (ms1 - tau) * 1e3;
+  }
+  out->B_R = BR;
+  out->host_t0_us = t0_us;
   out->B_H = out->B_P + BR;
+  c->host_t0_us = t0_us;
   return MOE_OK;
 }
 

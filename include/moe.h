@@ -104,7 +104,7 @@ typedef struct {
   int q;               /* filled over the link (F) */
   int n_host;          /* executed on the host (C = m - q) */
   int n_evict;         /* occupied slots overwritten */
-  double t_fill_pred_us, t_host_pred_us;  /* qS/B_P and (m-q)S/(B_H-B_P) */
+  double t_fill_pred_us, t_host_pred_us;  /* qS/B_P and t0 + (m-q)S/(B_H-B_P) (t0 = 0 when m = q) */
 } moe_plan_info;
 
 /* Bytes of one expert blob S for the configuration (layout above). */
@@ -156,17 +156,28 @@ int moe_set_policy(moe_ctx* ctx, int policy, double B_P, double B_H);
  * spread over the pool, so no call finds its bytes in the host caches, first alone
  * (host_alone) and then while a train of copies keeps the link busy
  * (host_conc: calls that end inside the second of two such trains).
- * Section 2.5 splits the miss set so that the fills, at B_P, and the host
- * branch, on the residual B_R = B_H - B_P, end together; B_R is measured
- * here as host_conc (host_alone when fewer than 3 calls ran inside the
- * train), and B_H = B_P + B_R.  All rates GB/s; medians with min and max.
- * Synchronous.  INVAL for T outside [1, max_tokens]; HIP. */
+ * Single-expert calls (host_alone_1, host_conc_1) are timed beside them, in
+ * alternation: a call on n experts takes t0 + n S / B_R, where t0 is the
+ * pool's per-call cost (waking the workers, the phase barriers) and B_R the
+ * rate at which further experts stream; the two medians fix both.  Section
+ * 2.5 splits the miss set so that the fills, at B_P, and the host branch, on
+ * the residual B_R = B_H - B_P, end together; B_R is that marginal rate, from
+ * the calls made with the link busy (alone when fewer than 3 calls of each
+ * size ran inside the train), and B_H = B_P + B_R.  t0 shifts the balance by
+ * t0 B_P B_R / (S (B_P + B_R)) experts (about 0.2 on the decode shape), below
+ * the rounding of q*, so q* keeps the closed form; moe_plan_info's host-time
+ * prediction adds t0 to every layer that has a host set.  All rates GB/s;
+ * medians with min and max.  Synchronous.  INVAL for T outside [1,
+ * max_tokens]; HIP. */
 typedef struct {
   double B_P, B_P_min, B_P_max;                     /* pinned -> slot copies */
   double B_H;                                       /* B_P + B_R, the value q* uses */
   double host_alone, host_alone_min, host_alone_max;
   double host_conc, host_conc_min, host_conc_max;   /* with the link busy */
   int n_copy, n_host_alone, n_host_conc;            /* timed repeats behind each median */
+  double host_alone_1, host_conc_1;                 /* single-expert calls, medians */
+  double host_t0_us;                                /* per-call time t0 of the host branch */
+  double B_R;                                       /* marginal host rate, B_H - B_P */
 } moe_calibration;
 int moe_calibrate_ex(moe_ctx* ctx, int T, moe_calibration* out);
 

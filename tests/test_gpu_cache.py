@@ -273,8 +273,19 @@ def test_calibrate_reproducible_on_deployed_shape():
             assert m["n_copy"] == 5 and m["n_host_alone"] == 40
             assert m["B_P_min"] <= m["B_P"] <= m["B_P_max"]
             assert m["host_alone_min"] <= m["host_alone"] <= m["host_alone_max"]
-            br = m["host_conc"] if m["n_host_conc"] >= 3 else m["host_alone"]
-            assert m["B_H"] == pytest.approx(m["B_P"] + br)
+            assert m["B_H"] == pytest.approx(m["B_P"] + m["B_R"])
+            # t(n) = t0 + n S / B_R passes through the medians of the calls on
+            # 1 and k experts (the series the split uses)
+            conc = m["n_host_conc"] >= 3
+            r1, rk = (m["host_conc_1"], m["host_conc"]) if conc else (m["host_alone_1"], m["host_alone"])
+            S = s.rt.S
+            t1, tk = S / (r1 * 1e3), cfg.k * S / (rk * 1e3)          # us
+            if m["host_t0_us"] > 0:
+                assert m["host_t0_us"] + S / (m["B_R"] * 1e3) == pytest.approx(t1, rel=1e-9)
+                assert m["host_t0_us"] + cfg.k * S / (m["B_R"] * 1e3) == pytest.approx(tk, rel=1e-9)
+            else:
+                assert m["B_R"] == pytest.approx(rk)
+            assert m["B_R"] >= rk * (1 - 1e-9)         # further experts stream at least as fast as whole calls
         # the calibration's outputs (what q* uses) agree; the standalone host
         # rate is a reported diagnostic
         assert abs(a["B_P"] - b["B_P"]) <= 0.15 * max(a["B_P"], b["B_P"])
