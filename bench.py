@@ -89,6 +89,7 @@ def parse():
                     help="host FFN pool threads: the 16 host cores of one GPU's share less two, for the calling "
                          "thread (it launches, copies and synchronises while the pool runs) and the HIP runtime's")
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of one graph per step")
+    ap.add_argument("--format-shapes", default="fp8,mxfp4,nvfp4", help="shapes of the formats phase")
     ap.add_argument("--format-layers", type=int, default=4,
                     help="layers of the fp8 and MXFP4 pools in the formats phase")
     ap.add_argument("--policy-steps", type=int, default=256, help="decode steps counted by the policies phase")
@@ -937,8 +938,11 @@ def phase_formats(args):
     out = {}
     dev = torch.device("cuda:0")
     import dataclasses
+    shapes = set(args.format_shapes.split(","))
     for cid, dec_T, pf_T, pf_bound in ((4, (1, 32), 4096, "hbm"), (5, (1,), 16384, "mfma"),
-                                       (6, (1, 32, 64), 8192, "hbm")):
+                                       (6, (1, 32, 64), 8192, "mfma")):
+        if {4: "fp8", 5: "mxfp4", 6: "nvfp4"}[cid] not in shapes:
+            continue
         if cid == 6:       # the decode shape with NVFP4 experts (the pages' laptop build of that model)
             c = dataclasses.replace(synth.CONFIGS[2], name="decode_nvfp4", fmt=synth.FMT_NVFP4)
             c = c.with_layers(args.format_layers)
@@ -1006,12 +1010,17 @@ def phase_formats(args):
         hp = torch.from_numpy(synth.hidden(c, args.seed, pf_T, 7).view(np.int16)).to(dev)
         op = torch.empty(pf_T, H, dtype=torch.bfloat16, device=dev)
 
+        # the NVFP4 experts sit on the decode shape, whose router bias is the
+        # decode workload's Zipf prior; its prefill batch takes the prefill
+        # shape's unbiased routing (nearly every expert ~512 rows at 8192)
+        pbias = [None] * L if cid == 6 else bias
+
         def prefill_pass(key, kernel, peak):
-            rt.forward(0, hp, R[0], bias[0], rows[0], op)
+            rt.forward(0, hp, R[0], pbias[0], rows[0], op)
             torch.cuda.synchronize()
             rt.profile_begin(L * 16 + 16)
             for l in range(L):
-                rt.forward(l, hp, R[l], bias[l], rows[l], op)
+                rt.forward(l, hp, R[l], pbias[l], rows[l], op)
             prof = profile_end(rt)
             torch.cuda.synchronize()
             assert rt.check_device_error() == 0
@@ -1028,8 +1037,8 @@ def phase_formats(args):
             log(f"{name} {key}: {json.dumps(res[key])}")
 
         peak = {4: FP8_PEAK, 5: FP4_PEAK, 6: BF16_PEAK}[cid]
-        prefill_pass(f"prefill_T{pf_T}", "gemm_dec (weight stream, NVFP4 dequantised to fp16 in registers)"
-                     if cid == 6 else "gemm_pf_q8 (LDS-tiled scaled-MFMA grouped GEMM)", peak)
+        prefill_pass(f"prefill_T{pf_T}", "gemm_pf16 (LDS-tiled fp16-MFMA grouped GEMM, NVFP4 dequantised in "
+                     "registers)" if cid == 6 else "gemm_pf_q8 (LDS-tiled scaled-MFMA grouped GEMM)", peak)
         if cid == 5:     # MXFP6 activations: E2M1 x E2M3 at the 6/4-bit MFMA rate
             from expert_ffn_execution_router_amd import binding as B
             rt.set_activations(B.MOE_ACT_MXFP6)

@@ -59,7 +59,8 @@ hipError_t moe_launch_gemm_pf8(int fmt, int gated, int small, int n_cu, const Wo
                                int N, void* out, int trash_row, hipStream_t s);
 hipError_t moe_launch_gemm_pf(int fmt, int gated, int grid, const WorkList* wl, const int32_t* counts,
                               const int32_t* offsets, const uint8_t* pool, size_t S, size_t woff0, size_t woff1,
-                              const void* X, const int32_t* row_tok, int K, int N, void* out, hipStream_t s);
+                              size_t soff0, size_t soff1, const void* X, const int32_t* row_tok, int K, int N,
+                              void* out, hipStream_t s);
 hipError_t moe_launch_combine(const uint16_t* Z, const int32_t* ids, const float* w, const int32_t* pos,
                               const uint32_t* miss_mask, const int32_t* slot_row, const float* hp,
                               const int32_t* hp_count, int T, int k, int H, uint16_t* out, float* out_f32,
@@ -379,12 +380,12 @@ int forward_experts(moe_ctx* c, const void* hidden, int T, const int32_t* slot_r
     c->fills_pending = false;
   }
   // many tokens per expert: LDS-tiled MFMA kernels; otherwise weight streaming
-  // (NVFP4 has no large-batch kernel: its weights stream at every size)
-  const bool tiled = T > 64 && (long)T * g.k >= 48L * g.E && g.wfmt != MOE_W_NVFP4;
+  const bool tiled = T > 64 && (long)T * g.k >= 48L * g.E;
+  const bool tiled16 = g.wfmt == MOE_W_BF16 || g.wfmt == MOE_W_NVFP4;   // 16-bit tokens in the tiled kernels
   // 8-bit formats with few tokens per expert (at most 160 on average): the
   // 128-token, three-stage variant (a weight stream more than a GEMM)
   const int small8 = (long)T * g.k <= 160L * g.E ? 1 : 0;
-  const int tile_mb = g.wfmt == MOE_W_BF16 ? moe_pf_tile_tokens() : moe_pf8_tile_tokens(g.wfmt, small8);
+  const int tile_mb = tiled16 ? moe_pf_tile_tokens() : moe_pf8_tile_tokens(g.wfmt, small8);
   // weight streaming with 16-bit activations: fp8 and MXFP4 weights are
   // dequantised to bf16 in registers (the small-batch kernels are bound by
   // the weight bytes, so unrounded activations cost nothing)
@@ -451,7 +452,7 @@ int forward_experts(moe_ctx* c, const void* hidden, int T, const int32_t* slot_r
                               0, -(max_split * (N / 64)), c->err, s));
     return MOE_OK;
   };
-  if (tiled && g.wfmt != MOE_W_BF16) {
+  if (tiled && !tiled16) {
     const int trash = g.max_tokens * g.k;       // the spare row of A and Z
     // activations quantised straight into grouped order (row p <- token perm_tok[p])
     STAGE(c, MOE_STAGE_QUANT_X, s,
@@ -468,14 +469,20 @@ int forward_experts(moe_ctx* c, const void* hidden, int T, const int32_t* slot_r
                               b.s[2], 0, c->Aq, c->As, trash, g.I, g.H, c->Z, trash, s));
     if ((rc = tail_gemm(0, c->Aq, c->As, nullptr, c->Z))) return rc;
   } else if (tiled) {
+    // bf16 tokens, or for NVFP4 the hidden rows converted to fp16 (A in fp16)
+    const void* x16 = hidden;
+    if (g.wfmt == MOE_W_NVFP4) {
+      STAGE(c, MOE_STAGE_QUANT_X, s, moe_launch_cvt_f16(hidden, (long)T * g.H, c->Xq, s));
+      x16 = c->Xq;
+    }
     STAGE(c, MOE_STAGE_GEMM1, s,
           moe_launch_gemm_pf(g.wfmt, 1, c->n_cu, c->wl, tile_counts, c->offsets, c->slot_pool, b.S, b.w[0],
-                             b.w[1], hidden, c->perm_tok, g.H, g.I, c->A, s));
-    int rc = tail_gemm(1, hidden, nullptr, c->perm_tok, c->A);
+                             b.w[1], b.s[0], b.s[1], x16, c->perm_tok, g.H, g.I, c->A, s));
+    int rc = tail_gemm(1, x16, nullptr, c->perm_tok, c->A);
     if (rc) return rc;
     STAGE(c, MOE_STAGE_GEMM2, s,
-          moe_launch_gemm_pf(g.wfmt, 0, c->n_cu, c->wl, tile_counts, c->offsets, c->slot_pool, b.S, b.w[2], 0, c->A,
-                             nullptr, g.I, g.H, c->Z, s));
+          moe_launch_gemm_pf(g.wfmt, 0, c->n_cu, c->wl, tile_counts, c->offsets, c->slot_pool, b.S, b.w[2], 0,
+                             b.s[2], 0, c->A, nullptr, g.I, g.H, c->Z, s));
     if ((rc = tail_gemm(0, c->A, nullptr, nullptr, c->Z))) return rc;
   } else {
     // 16-bit tokens gathered through perm_tok for GEMM 1 (bf16, or the

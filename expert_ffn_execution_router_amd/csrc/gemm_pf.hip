@@ -42,6 +42,17 @@
 //     and a wave whose 144-token half holds no routed token skips its MFMAs;
 //   * the grid is persistent over the device work list, so the host never
 //     reads the routing.
+// NVFP4 experts (E2M1 codes, an E4M3 scale per 16 inputs of a row, an fp32
+// scale per matrix) run through the same kernel with fp16 tokens (the hidden
+// rows converted to fp16 once per call; A written in fp16): a chunk's weight
+// rows are 32 bytes of codes and 4 scale bytes, loaded as they are stored
+// (9 KiB a chunk against 32 KiB of bf16 weights), and each wave dequantises
+// its operand in registers, element times block scale, exact in fp16 (a
+// scaled fp4 -> fp16 pair conversion and a packed fp16 multiply per two
+// weights), for v_mfma_f32_16x16x32_f16; the matrix scales multiply the
+// fp32 sums in the epilogue (gate and up before SwiGLU, down on Z).  The
+// weight operand's 16-byte halves are swapped on rows 8-15 of every 16, so
+// the 64 lanes' dword reads of 16 rows hit 64 distinct banks.
 #include "common.h"
 
 namespace {
@@ -53,6 +64,11 @@ constexpr int PF_BN = 256;    // weight rows per tile
 constexpr int PF_BK = 64;     // K per chunk
 constexpr int PF_ROWB = PF_BK * 2;                    // bytes per LDS row (128)
 constexpr int PF_STAGE = (PF_BM + PF_BN) * PF_ROWB;    // 68 KiB per stage
+// NVFP4 stage: token rows as above, then 32 code bytes and 4 scale bytes per weight row
+constexpr int PF_NV_CODEB = PF_BK / 2;                 // 32
+constexpr int PF_NV_CODE_OFF = PF_BM * PF_ROWB;        // 36 KiB
+constexpr int PF_NV_SC_OFF = PF_NV_CODE_OFF + PF_BN * PF_NV_CODEB;
+constexpr int PF_NV_STAGE = PF_NV_SC_OFF + PF_BN * 4;  // 45 KiB
 constexpr int PF_NSTAGE = 2;
 constexpr int PF_WAVES = 8;
 constexpr int PF_TLOADS = PF_BM / 8 / (PF_WAVES / 2);   // 8-row token blocks per loading wave (9)
@@ -63,24 +79,30 @@ constexpr int N_XCD = 8;
 // byte offset of (row, 16-byte piece) in a stage
 DEV int swz(int row, int piece) { return row * PF_ROWB + ((piece ^ ((row >> 1) & 7)) << 4); }
 
+typedef __attribute__((address_space(4))) float cst_f32_t;   // constant memory: scalar loads
+
 struct PfItem {
   int slot, row0, nrows, f0;
 };
 
 }  // namespace
 
-// GATED: out = A (bf16 [rows, N]) with N = I features, weights gate at woff0
-// and up at woff1 ([N, K] each).  Otherwise out = Z (bf16 [rows, N]) with
-// weights at woff0 ([N, K]).  X rows are gathered through row_tok (GEMM 1) or
+// GATED: out = A ([rows, N], bf16; NVFP4: fp16) with N = I features,
+// weights gate at woff0 and up at woff1 ([N, K] each).  Otherwise out = Z
+// (bf16 [rows, N]) with weights at woff0 ([N, K]).  NV: the weights are
+// NVFP4 codes ([N, K/2] bytes) with their E4M3 block scales at soff0 /
+// soff1 ([N, K/16] bytes) and the three matrices' fp32 scales after the
+// block scales; X is fp16.  X rows are gathered through row_tok (GEMM 1) or
 // taken in grouped order.  K % 64 == 0; N % 128 (gated) or 256 (not gated).
 // row_tok is read in 8-entry blocks up to 287 entries past a tile's first
 // row, so it must hold 288 entries of slack after the last routed row.
-template <bool GATED>
+template <bool GATED, bool NV>
 __global__ void __launch_bounds__(64 * PF_WAVES, 1)
-gemm_pf_bf16(const WorkList* __restrict__ wl, const int32_t* __restrict__ counts,
-             const int32_t* __restrict__ offsets, const uint8_t* __restrict__ pool, size_t S, size_t woff0,
-             size_t woff1, const uint16_t* __restrict__ X, const int32_t* __restrict__ row_tok, int K, int N,
-             uint16_t* __restrict__ out) {
+gemm_pf16(const WorkList* __restrict__ wl, const int32_t* __restrict__ counts, const int32_t* __restrict__ offsets,
+          const uint8_t* __restrict__ pool, size_t S, size_t woff0, size_t woff1, size_t soff0, size_t soff1,
+          const uint16_t* __restrict__ X, const int32_t* __restrict__ row_tok, int K, int N,
+          uint16_t* __restrict__ out) {
+  constexpr int STG = NV ? PF_NV_STAGE : PF_STAGE;
   extern __shared__ __align__(16) uint8_t lds[];
   __shared__ int l_pref[257], l_slot[256], l_row0[256], l_cnt[256];
   const int tid = threadIdx.x, wave = __builtin_amdgcn_readfirstlane(tid >> 6), lane = tid & 63;
@@ -175,6 +197,25 @@ gemm_pf_bf16(const WorkList* __restrict__ wl, const int32_t* __restrict__ counts
           xrow = v;
         }
         src[q] = (uint32_t)xrow * (uint32_t)(K * 2) + piece * 16;
+      } else if (NV) {
+        // q 0, 1: code rows 32 (2 (wave - 4) + q) + lane/2, 16-byte half
+        // lane & 1, swapped on rows 8-15 of every 16; q 2: the scale dword
+        // of row 64 (wave - 4) + lane
+        const int wq = wave - PF_WAVES / 2;
+        if (q < 3) {
+          const int wr = q < 2 ? (2 * wq + q) * 32 + (lane >> 1) : 64 * wq + lane;
+          size_t f, base;
+          if (GATED) {
+            const int h = wr >> 6, g = (wr >> 5) & 1, j = wr & 31;
+            f = (size_t)(t.f0 + h * 32 + j);
+            base = q < 2 ? (g ? woff1 : woff0) : (g ? soff1 : soff0);
+          } else {
+            f = (size_t)(t.f0 + wr);
+            base = q < 2 ? woff0 : soff0;
+          }
+          src[q] = q < 2 ? (uint32_t)(base + f * (K / 2)) + (((lane & 1) ^ ((wr >> 3) & 1)) << 4)
+                         : (uint32_t)(base + f * (K / 16));
+        }
       } else if (q < PF_WLOADS) {
         const int wr = srow - PF_BM;                              // weight tile row 0..255
         if (GATED) {
@@ -203,14 +244,24 @@ gemm_pf_bf16(const WorkList* __restrict__ wl, const int32_t* __restrict__ counts
       decode(iss_it, t);
       set_sources(t);
     }
-    const uint8_t* base = sbase + iss_c * (PF_BK * 2);
-    ++iss_c;
-    lds_u8_t* dst = (lds_u8_t*)lds + stage * PF_STAGE + blk0 * 1024;
+    const int cc = iss_c++;
+    const uint8_t* base = sbase + cc * (PF_BK * 2);
+    lds_u8_t* dst = (lds_u8_t*)lds + stage * STG + blk0 * 1024;
     if (wtok) {
 #pragma unroll
       for (int q = 0; q < PF_TLOADS; ++q)
         if (blk0 + q < tok_blocks)            // blocks past the tile's rows are skipped
           __builtin_amdgcn_global_load_lds((gbl_void_t*)(base + src[q]), (lds_void_t*)(dst + q * 1024), 16, 0, 0);
+    } else if (NV) {
+      const int wq = wave - PF_WAVES / 2;
+      lds_u8_t* st = (lds_u8_t*)lds + stage * STG;
+      const uint8_t* cb = sbase + cc * PF_NV_CODEB;
+#pragma unroll
+      for (int q = 0; q < 2; ++q)
+        __builtin_amdgcn_global_load_lds((gbl_void_t*)(cb + src[q]),
+                                         (lds_void_t*)(st + PF_NV_CODE_OFF + (2 * wq + q) * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds((gbl_void_t*)(sbase + cc * 4 + src[2]),
+                                       (lds_void_t*)(st + PF_NV_SC_OFF + wq * 256), 4, 0, 0);
     } else {
 #pragma unroll
       for (int q = 0; q < PF_WLOADS; ++q)
@@ -233,6 +284,18 @@ gemm_pf_bf16(const WorkList* __restrict__ wl, const int32_t* __restrict__ counts
   // epilogue: lane holds weight rows 4*lg..+3 of each 16-row sub-tile i for
   // token column lr of each 16-token sub-tile j
   auto store_item = [&](const PfItem& t) {
+    // NVFP4: the matrices' fp32 scales (gate and up, or down), after the
+    // three matrices' codes and block scales
+    // (scalar loads through the constant address space: a vector load here
+    // would leave its destination registers pending across the loop, and
+    // the wait for them would also wait for the next chunk's loads)
+    float ts0 = 1.0f, ts1 = 1.0f;
+    if (NV) {
+      const size_t n = (size_t)K * N;
+      const cst_f32_t* ts = (const cst_f32_t*)(pool + (size_t)t.slot * S + 3 * (n / 2) + 3 * (n / 16));
+      ts0 = GATED ? ts[0] : ts[2];
+      ts1 = GATED ? ts[1] : 1.0f;
+    }
 #pragma unroll
     for (int j = 0; j < PF_SUB; ++j) {
       const int r = wm * PF_HALF + j * 16 + lr;
@@ -245,12 +308,12 @@ gemm_pf_bf16(const WorkList* __restrict__ wl, const int32_t* __restrict__ counts
           float v[4];
 #pragma unroll
           for (int q = 0; q < 4; ++q) {
-            const float g = acc[i][j][q], u = acc[2 + i][j][q];
-            v[q] = g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;   // rounded to bf16 below
+            const float g = acc[i][j][q] * ts0, u = acc[2 + i][j][q] * ts1;
+            v[q] = g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;   // rounded to bf16 (fp16) below
           }
           uint2 pk;
-          pk.x = pack_bf16x2(v[0], v[1]);
-          pk.y = pack_bf16x2(v[2], v[3]);
+          pk.x = NV ? pack_f16x2(v[0], v[1]) : pack_bf16x2(v[0], v[1]);
+          pk.y = NV ? pack_f16x2(v[2], v[3]) : pack_bf16x2(v[2], v[3]);
           st8(orow + f, pk);
         }
       } else {
@@ -258,8 +321,8 @@ gemm_pf_bf16(const WorkList* __restrict__ wl, const int32_t* __restrict__ counts
         for (int i = 0; i < 4; ++i) {
           const int f = t.f0 + wn * 64 + i * 16 + lg * 4;
           uint2 pk;
-          pk.x = pack_bf16x2(acc[i][j][0], acc[i][j][1]);
-          pk.y = pack_bf16x2(acc[i][j][2], acc[i][j][3]);
+          pk.x = pack_bf16x2(acc[i][j][0] * ts0, acc[i][j][1] * ts0);
+          pk.y = pack_bf16x2(acc[i][j][2] * ts0, acc[i][j][3] * ts0);
           st8(orow + f, pk);
         }
       }
@@ -292,8 +355,40 @@ gemm_pf_bf16(const WorkList* __restrict__ wl, const int32_t* __restrict__ counts
       pending = false;
     }
     if (v + PF_NSTAGE - 1 < n_units) issue(stage == 0 ? PF_NSTAGE - 1 : stage - 1);
-    const uint8_t* cur = lds + stage * PF_STAGE;
-    if (ct.nrows > wm * PF_HALF) {              // this wave's token half holds a routed token
+    const uint8_t* cur = lds + stage * STG;
+    if (NV && ct.nrows > wm * PF_HALF) {
+      // the four scale bytes (16-input groups 0-3 of the chunk) of row lr of each sub-tile
+      uint32_t scd[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) scd[i] = *(const uint32_t*)(cur + PF_NV_SC_OFF + (wn * 64 + i * 16 + lr) * 4);
+#pragma unroll
+      for (int ks = 0; ks < 2; ++ks) {
+        f16x8_t bx[PF_SUB], aw[4];
+#pragma unroll
+        for (int j = 0; j < PF_SUB; ++j)
+          bx[j] = __builtin_bit_cast(f16x8_t, *(const i32x4_t*)(cur + xoff[ks] + j * 2048));
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          // lane (row lr, group lg): K [32 ks + 8 lg, +8) = code bytes 16 ks + 4 lg of the row, in group 2 ks + lg/2
+          const uint32_t cw = *(const uint32_t*)(cur + PF_NV_CODE_OFF + (wn * 64 + i * 16 + lr) * PF_NV_CODEB +
+                                                 ((ks ^ ((lr >> 3) & 1)) << 4) + 4 * lg);
+          const int scb = (int)(scd[i] >> (8 * (2 * ks + (lg >> 1))));
+          const _Float16 sh = (_Float16)__builtin_amdgcn_cvt_f32_fp8(scb, 0);   // E4M3 is exact in fp16
+          const f16x2_t s2 = {sh, sh};
+          i32x4_t w4;
+          w4[0] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 1.0f, 0) * s2);
+          w4[1] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 1.0f, 1) * s2);
+          w4[2] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 1.0f, 2) * s2);
+          w4[3] = __builtin_bit_cast(int, __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(cw, 1.0f, 3) * s2);
+          aw[i] = __builtin_bit_cast(f16x8_t, w4);
+        }
+#pragma unroll
+        for (int i = 0; i < 4; ++i)
+#pragma unroll
+          for (int j = 0; j < PF_SUB; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_16x16x32_f16(aw[i], bx[j], acc[i][j], 0, 0, 0);
+      }
+    } else if (!NV && ct.nrows > wm * PF_HALF) {   // this wave's token half holds a routed token
 #pragma unroll
       for (int ks = 0; ks < 2; ++ks) {
         bf16x8_t bx[PF_SUB], aw[4];
@@ -320,32 +415,41 @@ gemm_pf_bf16(const WorkList* __restrict__ wl, const int32_t* __restrict__ counts
   if (pending) store_item(done);
 }
 
-extern "C" size_t moe_pf_lds_bytes() { return PF_NSTAGE * PF_STAGE; }
 extern "C" int moe_pf_tile_tokens() { return PF_BM; }
 
-// n_cu: CUs (one workgroup each).
-extern "C" hipError_t moe_launch_gemm_pf(int fmt, int gated, int n_cu, const WorkList* wl, const int32_t* counts,
-                                         const int32_t* offsets, const uint8_t* pool, size_t S, size_t woff0,
-                                         size_t woff1, const void* X, const int32_t* row_tok, int K, int N, void* out,
-                                         hipStream_t s) {
-  const int grid = n_cu;
-  if (fmt != WFMT_BF16 || K % PF_BK || N % (gated ? PF_BN / 2 : PF_BN)) return hipErrorInvalidValue;
-  const size_t lds = PF_NSTAGE * PF_STAGE;
+template <bool GATED, bool NV>
+static hipError_t launch_pf16(int grid, const WorkList* wl, const int32_t* counts, const int32_t* offsets,
+                              const uint8_t* pool, size_t S, size_t woff0, size_t woff1, size_t soff0, size_t soff1,
+                              const void* X, const int32_t* row_tok, int K, int N, void* out, hipStream_t s) {
+  const size_t lds = PF_NSTAGE * (NV ? PF_NV_STAGE : PF_STAGE);
   static bool attr = false;
   if (!attr) {
-    hipError_t e = hipFuncSetAttribute((const void*)gemm_pf_bf16<true>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                                       (int)lds);
-    if (e == hipSuccess)
-      e = hipFuncSetAttribute((const void*)gemm_pf_bf16<false>, hipFuncAttributeMaxDynamicSharedMemorySize,
-                              (int)lds);
+    const hipError_t e =
+        hipFuncSetAttribute((const void*)gemm_pf16<GATED, NV>, hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
     if (e != hipSuccess) return e;
     attr = true;
   }
-  if (gated)
-    gemm_pf_bf16<true><<<grid, 64 * PF_WAVES, lds, s>>>(wl, counts, offsets, pool, S, woff0, woff1, (const uint16_t*)X, row_tok,
-                                              K, N, (uint16_t*)out);
-  else
-    gemm_pf_bf16<false><<<grid, 64 * PF_WAVES, lds, s>>>(wl, counts, offsets, pool, S, woff0, woff1, (const uint16_t*)X,
-                                               row_tok, K, N, (uint16_t*)out);
+  gemm_pf16<GATED, NV><<<grid, 64 * PF_WAVES, lds, s>>>(wl, counts, offsets, pool, S, woff0, woff1, soff0, soff1,
+                                                         (const uint16_t*)X, row_tok, K, N, (uint16_t*)out);
   return hipGetLastError();
+}
+
+// fmt: WFMT_BF16 (X bf16, out bf16) or WFMT_NVFP4 (X fp16; GEMM 1 writes A
+// in fp16, GEMM 2 Z in bf16); soff0 / soff1: NVFP4 block-scale offsets.
+// n_cu: CUs (one workgroup each).
+extern "C" hipError_t moe_launch_gemm_pf(int fmt, int gated, int n_cu, const WorkList* wl, const int32_t* counts,
+                                         const int32_t* offsets, const uint8_t* pool, size_t S, size_t woff0,
+                                         size_t woff1, size_t soff0, size_t soff1, const void* X,
+                                         const int32_t* row_tok, int K, int N, void* out, hipStream_t s) {
+  if ((fmt != WFMT_BF16 && fmt != WFMT_NVFP4) || K % PF_BK || N % (gated ? PF_BN / 2 : PF_BN))
+    return hipErrorInvalidValue;
+  if (fmt == WFMT_NVFP4)
+    return gated ? launch_pf16<true, true>(n_cu, wl, counts, offsets, pool, S, woff0, woff1, soff0, soff1, X,
+                                           row_tok, K, N, out, s)
+                 : launch_pf16<false, true>(n_cu, wl, counts, offsets, pool, S, woff0, 0, soff0, 0, X, row_tok, K,
+                                            N, out, s);
+  return gated ? launch_pf16<true, false>(n_cu, wl, counts, offsets, pool, S, woff0, woff1, 0, 0, X, row_tok, K, N,
+                                          out, s)
+               : launch_pf16<false, false>(n_cu, wl, counts, offsets, pool, S, woff0, 0, 0, 0, X, row_tok, K, N, out,
+                                           s);
 }

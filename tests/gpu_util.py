@@ -49,7 +49,7 @@ class Setup:
     def tiled(self, T):
         """Whether a forward of T tokens runs the large-batch GEMMs."""
         c = self.cfg
-        return T > 64 and T * c.k >= 48 * c.E and c.fmt != 3
+        return T > 64 and T * c.k >= 48 * c.E
 
     def weights(self, layer):
         def get(e):

@@ -161,7 +161,7 @@ def edge_counts(cap):
 
 
 @pytest.mark.parametrize("fmt,cap,act", [(0, 288, None), (1, 256, None), (2, 288, None), (1, 128, None),
-                                         (2, 128, None), (2, 288, "mxfp6"), (2, 128, "mxfp6")])
+                                         (2, 128, None), (2, 288, "mxfp6"), (2, 128, "mxfp6"), (3, 288, None)])
 def test_tiled_forward_tile_edges(fmt, cap, act):
     """Routing forced to edge_counts by a one-hot router: token t's hidden row
     holds 4 at its first expert's dimension and 3 at its second's (noise
@@ -211,7 +211,7 @@ def test_tiled_forward_tile_edges(fmt, cap, act):
         s.close()
 
 
-@pytest.mark.parametrize("fmt,cap", [(0, 288), (1, 256), (2, 288)])
+@pytest.mark.parametrize("fmt,cap", [(0, 288), (1, 256), (2, 288), (3, 288)])
 def test_tiled_forward_overflow_rows(fmt, cap):
     """Routing that makes the large-batch kernels send overflow rows to the
     small-batch kernel: every one of E=256 experts fills one m-tile of cap

@@ -197,16 +197,19 @@ def test_mxfp4_config5_shape_mxfp6(T):
         s.close()
 
 
-@pytest.mark.parametrize("T", [1, 64, 1024])
+@pytest.mark.timeout(400)
+@pytest.mark.parametrize("T", [1, 64, 1024, 8192])
 def test_nvfp4_decode_shape(T):
     """The decode shape with NVFP4 experts at the sizes the formats bench
-    times (T=1 and 64) and a large batch through the same weight stream."""
+    times (T=1 and 64 through the weight stream, 8192 through the tiled
+    kernel) and a batch of 1024 (tiled, ~64 rows per expert)."""
     import dataclasses
     print(f"nvfp4 decode shape T={T}", flush=True)
     cfg = dataclasses.replace(_fullsize(2, L=1), fmt=synth.FMT_NVFP4)
     s = Setup(cfg, seed=4, max_tokens=max(T, 64), host_threads=8)
     try:
         s.admit_all(0)
+        assert s.tiled(T) == (T >= 1024)
         x, xd = s.hidden(T, tag=T)
         out = torch.empty(T, cfg.H, dtype=torch.bfloat16, device="cuda")
         s.rt.forward(0, xd, s.R_d[0], s.b_d[0], s.slot_row(0), out)
