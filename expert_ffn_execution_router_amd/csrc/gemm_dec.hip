@@ -200,9 +200,12 @@ DEV void activate(const f32x4_t* acc, f32x4_t* val, float s0 = 1.0f, float s1 = 
 
 // NVFP4: the fp32 scales of an expert's matrices, after its block scales
 // (gate, up, down); n = K * N elements per matrix.
+// Scalar loads through the constant address space: a vector load would
+// make the epilogue wait for every load in flight (the next chunks' too).
+typedef __attribute__((address_space(4))) float cst_f32_t;
 DEV void nv_tensor_scales(const uint8_t* pool, size_t S, int slot, int K, int N, bool gated, float& s0, float& s1) {
   const size_t n = (size_t)K * N;
-  const float* t = (const float*)(pool + (size_t)slot * S + 3 * (n / 2) + 3 * (n / 16));
+  const cst_f32_t* t = (const cst_f32_t*)(pool + (size_t)slot * S + 3 * (n / 2) + 3 * (n / 16));
   s0 = gated ? t[0] : t[2];
   s1 = gated ? t[1] : 1.0f;
 }
@@ -594,11 +597,15 @@ gemm_dec(const WorkList* __restrict__ wl, const int32_t* __restrict__ counts, co
               wa0[m] = fp8x8_bf16(v[0], v[1]);
               wa1[m] = fp8x8_bf16(v[2], v[3]);
             } else {
-              const uint2 cw = *(const uint2*)(sb + (m * NW + wave) * C::WSZ + lr * 128 +
-                                                (((2 * p + (lg >> 1)) ^ (lr & 7)) << 4) + 8 * (lg & 1));
+              // two dword reads: the compiler cannot tell an 8-byte LDS read
+              // from the stages the direct loads are filling and would wait
+              // for every load in flight before it
+              const uint8_t* cp = sb + (m * NW + wave) * C::WSZ + lr * 128 +
+                                  (((2 * p + (lg >> 1)) ^ (lr & 7)) << 4) + 8 * (lg & 1);
+              const uint32_t c0 = *(const uint32_t*)cp, c1 = *(const uint32_t*)(cp + 4);
               const float sc = e8m0_to_f32(sb[C::WS_OFF + (m * NW + wave) * 256 + lr * 8 + 2 * p + (lg >> 1)]);
-              wa0[m] = fp4x8_bf16(cw.x, sc);
-              wa1[m] = fp4x8_bf16(cw.y, sc);
+              wa0[m] = fp4x8_bf16(c0, sc);
+              wa1[m] = fp4x8_bf16(c1, sc);
             }
           }
 #pragma unroll

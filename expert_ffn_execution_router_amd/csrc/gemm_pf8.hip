@@ -375,8 +375,12 @@ gemm_pf_q8(const WorkList* __restrict__ wl, const int32_t* __restrict__ counts,
       for (int j = 0; j < C::SUB; ++j) {
         const uint8_t* p = rb + j * 16 * X6_ROWB;
         const i32x4_t a = lds16(p + o16);
-        const uint2 b = *(const uint2*)(p + o8);
-        const i32x8_t xv = i32x8_t{a[0], a[1], a[2], a[3], (int)b.x, (int)b.y, 0, 0};
+        // two dword reads, not one 8-byte read: the compiler cannot tell an
+        // 8-byte LDS read from the stage the direct loads are filling and
+        // puts a wait for every outstanding load (the next chunk's too)
+        // before it
+        const int b0 = *(const int*)(p + o8), b1 = *(const int*)(p + o8 + 4);
+        const i32x8_t xv = i32x8_t{a[0], a[1], a[2], a[3], b0, b1, 0, 0};
         const int xsc = sb[xs_at(trow + 16 * j) + lg];
 #pragma unroll
         for (int i = 0; i < 4; ++i)
