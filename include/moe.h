@@ -157,7 +157,9 @@ int moe_set_policy(moe_ctx* ctx, int policy, double B_P, double B_H);
  * (host_alone) and then while a train of copies keeps the link busy
  * (host_conc: calls that end inside the second of two such trains).
  * Single-expert calls (host_alone_1, host_conc_1) are timed beside them, in
- * alternation: a call on n experts takes t0 + n S / B_R, where t0 is the
+ * alternation, each call after a 200 us idle gap (the decode path wakes the
+ * pool once per layer, after the layer's GPU work has left it idle): a
+ * call on n experts takes t0 + n S / B_R, where t0 is the
  * pool's per-call cost (waking the workers, the phase barriers) and B_R the
  * rate at which further experts stream; the two medians fix both.  Section
  * 2.5 splits the miss set so that the fills, at B_P, and the host branch, on
