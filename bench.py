@@ -85,9 +85,10 @@ def parse():
                     help="further prefill chunk sizes timed with and without the second buffer (comma list)")
     ap.add_argument("--prefill-runs", type=int, default=2, help="double-buffered chunks timed (best is kept)")
     ap.add_argument("--cpu-layers", type=int, default=20, help="decode layers the oracle times (~0.5 s each)")
-    ap.add_argument("--host-threads", type=int, default=14,
-                    help="host FFN pool threads: the 16 host cores of one GPU's share less two, for the calling "
-                         "thread (it launches, copies and synchronises while the pool runs) and the HIP runtime's")
+    ap.add_argument("--host-threads", type=int, default=13,
+                    help="host FFN pool threads: the 16 host cores of one GPU's share less three, for the calling "
+                         "thread (it launches, copies and synchronises while the pool runs) and the HIP runtime's "
+                         "(the pool's workers poll for their next job between jobs)")
     ap.add_argument("--eager", action="store_true", help="time eager launches instead of one graph per step")
     ap.add_argument("--format-shapes", default="fp8,mxfp4,nvfp4", help="shapes of the formats phase")
     ap.add_argument("--format-layers", type=int, default=4,

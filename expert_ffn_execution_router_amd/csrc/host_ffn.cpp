@@ -17,6 +17,7 @@
 #include <cstdint>
 #include <cstdlib>
 #include <cstring>
+#include <immintrin.h>
 #include <thread>
 #include <type_traits>
 #include <vector>
@@ -344,7 +345,27 @@ struct HostFfnWork {
 
 // Workers sleep on a generation word (a futex through std::atomic::wait, so
 // a start wakes them all at once with no lock to queue on); the last one to
-// finish stamps the end time and wakes the waiter.
+// finish stamps the end time and wakes the waiter.  Before sleeping, a
+// worker polls the word for kSpinUs: the decode path starts one job per
+// layer, a few hundred microseconds apart, and a worker woken from the futex
+// starts tens of microseconds late (the last of 14 up to ~100 us on a busy
+// host) while the job's phase barriers wait for every worker.  (The caller
+// sleeps on the end of its job: polling there took a core from the workers
+// for the whole job, and jobs of many experts ran up to half again longer.)
+constexpr int kSpinUs = 500;
+
+// Polls pred() with a pause between reads until it holds or `us`
+// microseconds have passed; returns whether it held.
+template <class P>
+static bool spin_until(P pred, int us) {
+  const auto t_end = std::chrono::steady_clock::now() + std::chrono::microseconds(us);
+  for (int i = 0;; ++i) {
+    if (pred()) return true;
+    _mm_pause();
+    if ((i & 63) == 63 && std::chrono::steady_clock::now() >= t_end) return pred();
+  }
+}
+
 struct HostPool {
   int n;
   std::vector<std::thread> th;
@@ -373,7 +394,8 @@ struct HostPool {
   void loop(int id) {
     uint32_t seen = 0;
     for (;;) {
-      gen.wait(seen, std::memory_order_acquire);
+      if (!spin_until([&] { return gen.load(std::memory_order_acquire) != seen; }, kSpinUs))
+        gen.wait(seen, std::memory_order_acquire);
       const uint32_t g = gen.load(std::memory_order_acquire);
       if (g == seen) continue;                    // spurious wake
       seen = g;
