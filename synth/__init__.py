@@ -4,7 +4,7 @@ This module only draws numbers and lays them out; it contains none of the
 MoE layer's arithmetic.  Both the HIP library's callers and the oracle's
 callers take their inputs from here, so the two sides read identical bytes.
 
-The five workload shapes follow the configurations the spec names
+The five workload shapes are the benchmark configurations of this layer
 (tiny, decode-shaped, prefill-shaped, large-pool fp8, MXFP4); the value
 distributions are: expert weights N(0, 0.02) stored in the pool format,
 activations N(0, 1) as bf16, router weights N(0, 0.1) fp32.
