@@ -16,7 +16,8 @@ never the value), and one 8192-token prefill chunk streamed through the
 full-layer double buffer (with the ablation without it).
 
 --phases selects a subset (decode, e2e, prefill, cpu) for profiling runs, or
-adds the optional ones: formats (fp8 / MXFP4 shapes), policies (miss rates
+adds the optional ones: formats (fp8 / MXFP4 / NVFP4 shapes, a subset with
+--format-shapes), policies (miss rates
 of expert placements replayed over synthetic routing), elastic (cache
 rebuilds between decode steps), fallback (prefill with fewer than two
 layers of slots, and the prefill-to-decode hand-off), mxfp4_serving (the
