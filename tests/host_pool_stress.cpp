@@ -1,8 +1,12 @@
 // Two host threads share one host FFN thread pool, as the library's
 // synchronous decode calls and the HIP host callbacks of an asynchronous step
 // do: each submits jobs back to back; the pool must run them one at a time
-// and every result must equal the same job run alone.  Built with
+// and every result must equal the same job run alone.  Then one thread
+// submits jobs after idle gaps shorter and longer than the workers' polling
+// window (workers still polling, just asleep, long asleep).  Built with
 // ThreadSanitizer by tests/test_host_tsan.py; prints "ok" on success.
+#include <algorithm>
+#include <chrono>
 #include <cstdint>
 #include <cstdio>
 #include <cstring>
@@ -76,10 +80,24 @@ int main() {
   std::thread t2([&] { run(b, 1); });
   t1.join();
   t2.join();
+  // one thread again, with idle gaps on both sides of the workers' polling
+  // window before each job, so a job finds the workers polling, just gone
+  // to sleep, or long asleep
+  std::vector<Job> c = ref_a;
+  for (auto& j : c) std::fill(j.out.begin(), j.out.end(), 0.f);
+  const int gaps_us[] = {0, 100, 450, 550, 1500, 3000};
+  for (int i = 0; i < n_jobs; ++i) {
+    std::this_thread::sleep_for(std::chrono::microseconds(gaps_us[i % 6]));
+    Job& j = c[i];
+    HostFfnHandle* h = host_ffn_start(P, sh, pool.data(), 0, T, j.hidden.data(), j.ids.data(), j.w.data(),
+                                      j.C.data(), (int)j.C.size(), j.out.data());
+    (void)host_ffn_wait(P, h);
+  }
   host_pool_destroy(P);
   for (int i = 0; i < n_jobs; ++i)
     if (std::memcmp(a[i].out.data(), ref_a[i].out.data(), a[i].out.size() * 4) ||
-        std::memcmp(b[i].out.data(), ref_b[i].out.data(), b[i].out.size() * 4)) {
+        std::memcmp(b[i].out.data(), ref_b[i].out.data(), b[i].out.size() * 4) ||
+        std::memcmp(c[i].out.data(), ref_a[i].out.data(), c[i].out.size() * 4)) {
       std::printf("mismatch in job %d\n", i);
       return 1;
     }

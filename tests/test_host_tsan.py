@@ -1,7 +1,8 @@
 """ThreadSanitizer run of the host FFN thread pool (the host branch's
 resident pool): two threads submit jobs to one pool at once, as a
-synchronous decode call and a HIP host callback can; no data race may be
-reported and every result must equal the job run alone.  Host code only,
+synchronous decode call and a HIP host callback can, then one thread submits
+jobs after idle gaps on both sides of the workers' polling window; no data
+race may be reported and every result must equal the job run alone.  Host code only,
 compiled here with g++ (no GPU code is involved)."""
 import os
 import shutil
